@@ -1,0 +1,31 @@
+"""Reference oracle for batched lossless draft verification and the prefix scheduler.
+
+TEST INFRASTRUCTURE ONLY.  Plain, slow, float64 CPU code written from the
+pages' statement of the method.  It shares no code with the HIP library and
+imports nothing from it.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it; the product path never
+does.
+
+Modules
+-------
+verify    speculative-sampling verification (temperature softmax, accept test,
+          first-reject scan, residual / bonus inverse-CDF draw) and its greedy
+          (temperature 0) limit.
+schedule  confidence-scheduled verification depth (CumProd survival, greedy
+          throughput-improving prefix extension under a token budget).
+
+Every function is pinned by a ``-m "not gpu"`` test (tests/test_oracle_pins.py)
+against what the pages and the mathematics fix; none is "parity unpinned".
+"""
+
+from .verify import (  # noqa: F401
+    bf16_bits_to_f64,
+    target_probs,
+    accept_draft,
+    residual,
+    inverse_cdf,
+    verify,
+    verify_greedy,
+    row_is_bad,
+)
+from .schedule import survival, schedule, schedule_value, brute_force  # noqa: F401
