@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Throughput of batched lossless draft verification on one MI355X.
+
+A step is one spec_verify call over the block-diffusion workload: B=64 requests,
+gamma=15 draft positions, V=129280, bf16 target logits, T=1 (every request
+verifies all 15 drafts, so a step verifies 960 draft positions).  Inputs are
+seeded synthetic arrays resident in HBM before the timed region; several
+independent copies rotate so that HBM, not the 256 MB last-level cache, serves
+the reads.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+KERNEL_SRC = os.path.join(ROOT, "lossless_draft_verification_verify_amd", "csrc", "verify_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_block_verify.json")
+
+
+def algorithmic_bytes(B, G, V, lens, n_rej, esize=2):
+    """Bytes the method must move per call: every read target row once, one
+    fp32 draft row per rejecting request, the per-position gathers (token id,
+    q(x), uniform) and the per-request final uniform and outputs."""
+    lens = np.asarray(lens, np.int64)
+    rows = int((lens + 1).sum())
+    return rows * V * esize + n_rej * V * 4 + int(lens.sum()) * 12 + B * (4 + 4 + 4 * (G + 1))
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def _oracle_slice(args):
+    import oracle
+    lo, hi = args
+    w = _CPU_W
+    sl = slice(lo, hi)
+    t0 = time.perf_counter()
+    oracle.verify(w["logits"][sl], w["draft_probs"][sl], w["draft_tokens"][sl], w["uniforms"][sl],
+                  np.float32(w["T"]))
+    return time.perf_counter() - t0
+
+
+_CPU_W = None
+
+
+def cpu_baseline(w, workers, reqs):
+    """Time the float64 oracle on host cores over the first `reqs` requests."""
+    global _CPU_W
+    import multiprocessing as mp
+    _CPU_W = w
+    chunk = max(1, reqs // workers)
+    parts = [(i, min(reqs, i + chunk)) for i in range(0, reqs, chunk)]
+    ctx = mp.get_context("fork")                 # before any GPU initialisation
+    t0 = time.perf_counter()
+    with ctx.Pool(processes=min(workers, len(parts))) as pool:
+        busy = pool.map(_oracle_slice, parts)
+    wall = time.perf_counter() - t0
+    positions = reqs * w["G"]
+    return {"value": positions / wall, "unit": "verified draft positions/s", "cores": min(workers, len(parts)),
+            "kind": "oracle",
+            "sample": f"{reqs} of {w['B']} requests of the same workload (all {w['G']} positions each), "
+                      f"float64 numpy oracle, {len(parts)} slices in a process pool; wall {wall:.2f} s, "
+                      f"summed worker time {sum(busy):.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated in HBM")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=0)
+    ap.add_argument("--cpu-requests", type=int, default=64)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(requests shard across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    w = W.block()
+    B, G, V = w["B"], w["G"], w["V"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
+        cpu = cpu_baseline(w, workers, min(args.cpu_requests, B))
+
+    import torch
+    import lossless_draft_verification_verify_amd as sv
+    sv.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    z0 = torch.from_numpy(w["logits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    q0 = torch.from_numpy(w["draft_probs"]).to(dev)
+    x0 = torch.from_numpy(w["draft_tokens"]).to(dev)
+    u0 = torch.from_numpy(w["uniforms"]).to(dev)
+    sets = [(z0, q0, x0, u0)] + [(z0.clone(), q0.clone(), x0.clone(), u0.clone()) for _ in range(args.sets - 1)]
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty(B, G + 1, dtype=torch.int32, device=dev)
+
+    # outputs of one call fix the data-dependent byte count (rejecting requests)
+    sv.verify(*sets[0], 1.0, out_accepted=acc, out_tokens=tok)
+    torch.cuda.synchronize()
+    a = acc.cpu().numpy()
+    lens = np.full(B, G)
+    n_rej = int((a < lens).sum())
+    algo = algorithmic_bytes(B, G, V, lens, n_rej)
+
+    for i in range(args.warmup):
+        sv.verify(*sets[i % len(sets)], 1.0, out_accepted=acc, out_tokens=tok)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    stream = torch.cuda.current_stream(dev)       # the stream spec_verify launches on
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        sv.verify(*sets[i % len(sets)], 1.0, out_accepted=acc, out_tokens=tok)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per = np.array([s.elapsed_time(e) for s, e in ev])          # ms per launch
+    ms_step = total_ms / K
+    kern_ms = float(per.mean())
+    positions = int(lens.sum())
+    value = positions / (ms_step * 1e-3)
+    achieved = algo / (kern_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+    out = {
+        "metric": "verified draft positions/sec and achieved HBM GB/s (% peak), B=64 gamma=15 V=129k",
+        "value": round(value, 1),
+        "unit": "verified draft positions/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "block-diffusion draft verification: B=64, gamma=15, V=129280, bf16 logits "
+                               "(Zipf(1.1) over a per-row permutation), fp32 draft probabilities, T=1",
+                   "B": B, "gamma": G, "V": V, "temperature": 1.0, "logits": "bf16", "rotating_sets": len(sets),
+                   "verified_positions_per_step": positions, "rejecting_requests": n_rej},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "k_verify_sampled (one fused launch per step)",
+                     "algorithmic_bytes_per_launch": algo,
+                     "launch_ms_mean": round(kern_ms, 5),
+                     "launch_ms_p10_p50_p90": [round(float(np.percentile(per, p)), 5) for p in (10, 50, 90)]},
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) batched lossless draft
+ * verification library, libspecverify.so.
+ *
+ * Two operations:
+ *
+ *   spec_verify    speculative-sampling verification of a batch of draft
+ *                  blocks against the target's logits.
+ *   spec_schedule  confidence-scheduled verification depth: how many drafts
+ *                  of each request to verify under a batch token budget.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensors are row-major and contiguous.  Pointers named "device" point
+ *   to memory on the current HIP device; host pointers are never read.
+ * - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
+ *   stream).  Calls are asynchronous: they validate their arguments on the
+ *   host, enqueue kernels on `stream` and return.  Outputs are valid once the
+ *   caller has synchronised the stream.  No call allocates or frees memory,
+ *   synchronises, or keeps state between calls; every call may be captured
+ *   into a HIP graph.
+ * - Host-checkable errors (null pointers, bad sizes, bad temperature, bad
+ *   dtype, misalignment, small workspace) return a status before anything is
+ *   enqueued, and every output is left untouched.  A failed kernel launch
+ *   returns SPEC_ERR_DEVICE.
+ * - Data errors found on the device do not stop the batch: the affected
+ *   request's outputs are set to -1 and the other requests are processed.
+ * - The caller owns every buffer.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPEC_OK = 0,
+    SPEC_ERR_NULL_POINTER = 1,        /* a required pointer is NULL                     */
+    SPEC_ERR_BAD_SHAPE = 2,           /* B, G, V, table or budget out of range           */
+    SPEC_ERR_BAD_TEMPERATURE = 3,     /* temperature < 0, not finite, or too small       */
+    SPEC_ERR_BAD_DTYPE = 4,           /* unknown dtype code                              */
+    SPEC_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < the *_workspace_bytes query   */
+    SPEC_ERR_UNSUPPORTED = 6,         /* valid but beyond this build's limits            */
+    SPEC_ERR_DEVICE = 7,              /* HIP error while querying the device or launching */
+    SPEC_ERR_MISALIGNED = 8           /* a pointer is not aligned to its element type /
+                                         the workspace is not 256-byte aligned           */
+} spec_status_t;
+
+typedef enum { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 } spec_dtype_t;
+
+/* A hipStream_t, passed opaquely so that this header needs no HIP include. */
+typedef void *spec_stream_t;
+
+/* Limits of this build. */
+#define SPEC_MAX_DRAFTS 255           /* G <= 255                                        */
+#define SPEC_MAX_VOCAB (1 << 30)      /* V <= 2^30                                       */
+#define SPEC_MAX_SCHEDULE_CANDIDATES 4096 /* B * G <= 4096 for spec_schedule              */
+
+/*
+ * Optional diagnostics of spec_verify (for parity checks; they cost extra
+ * stores, keep them NULL on a timed path).  Each pointer may be NULL.  All
+ * device pointers.  Entries that a request does not compute are set to NaN;
+ * for a request with a data error every entry is NaN.
+ *
+ *   target_lse [B, G+1]  m_k/T + ln S_k of each read target row k <= len_b
+ *   p_draft    [B, G]    p_k(x_k), the target probability of draft k, k < len_b
+ *   q_draft    [B, G]    q_k(x_k) as read from draft_probs, k < len_b
+ *   resid_mass [B]       R = sum_v max(p_j(v) - q_j(v), 0) at the rejection
+ *                        row j; -1 when every verified draft was accepted
+ *
+ * Temperature 0 writes none of them.
+ */
+typedef struct {
+    float *target_lse;
+    float *p_draft;
+    float *q_draft;
+    float *resid_mass;
+} spec_verify_diag_t;
+
+/*
+ * Bytes of device workspace spec_verify needs for this shape (0 on invalid
+ * arguments).  The same workspace serves every shape whose query is not larger.
+ *
+ * The workspace holds per-row partial reductions, per-request decisions and
+ * per-request arrival counters.  It must be zero-filled once before its first
+ * use (e.g. allocated with a zeroing allocator); every completed call leaves it
+ * zero-filled again, so it can be reused by later calls without clearing.
+ * Calls that share one workspace must not overlap in time (use one workspace
+ * per stream).
+ */
+size_t spec_verify_workspace_bytes(int32_t B, int32_t G, int32_t V, spec_dtype_t target_dtype);
+
+/*
+ * spec_verify -- batched lossless speculative-sampling verification.
+ *
+ * Operation ("breaking down dspark and its lineage", sections "Speculative
+ * decoding basics: drafting and verification" and "Preserving the target
+ * distribution during verification"; "UraionSpec", section "Speculative
+ * Decoding", Eq. (acceptance); "AngelSpec", sections 1 and 4.1):
+ * for request b with verify length n = len_b,
+ *   p_k = softmax(z[b,k,:] / T) for target rows k = 0..n (row k is the target's
+ *         distribution after k accepted drafts; row n supplies the bonus token);
+ *   draft k < n is accepted iff u[b,k] < p_k(x_k) / q[b,k,x_k]  (if
+ *         q[b,k,x_k] <= 0: accepted iff p_k(x_k) > 0);
+ *   j = the first rejected k, or n if none;
+ *   if j < n the final token is drawn from r = max(p_j - q[b,j,:], 0),
+ *   else from r = p_n;  y = min{v : sum_{w<=v} r(w) > u[b,G] * sum_w r(w)}
+ *   (if r sums to zero, p_j is used; if no index qualifies, the largest v
+ *   with r(v) > 0);
+ *   out_accepted[b] = j;  out_tokens[b,:] = x[b,0..j-1], y, then -1.
+ * Temperature 0 is the greedy limit: a_k = lowest index of the maximum of
+ * row k (exact comparison); draft k is accepted iff x_k == a_k; y = a_j.
+ *
+ * Arguments (all device pointers unless stated):
+ *   target_logits  [B, G+1, V] of target_dtype (F32 or BF16).  Only rows
+ *                  k <= len_b of each request are read.
+ *   draft_probs    [B, G, V] float, the distribution each draft token was
+ *                  sampled from; used as given.  May be NULL if T == 0 or G == 0.
+ *   draft_tokens   [B, G] int32 in [0, V).  May be NULL if G == 0.
+ *   uniforms       [B, G+1] float in [0, 1): u[b,k], k < G, decides draft k;
+ *                  u[b,G] is the final draw.  May be NULL if T == 0.
+ *   verify_len     [B] int32 in [0, G], or NULL meaning G for every request.
+ *   B >= 1, 0 <= G <= SPEC_MAX_DRAFTS, 1 <= V <= SPEC_MAX_VOCAB.
+ *   temperature    T == 0 (greedy) or 2^-126 <= T < inf.
+ *   out_accepted   [B] int32: accepted drafts j in [0, len_b]; -1 = data error.
+ *   out_tokens     [B, G+1] int32.
+ *   diag           host pointer to a spec_verify_diag_t, or NULL.
+ *   workspace      device, 256-byte aligned, zero-filled before first use, at
+ *                  least spec_verify_workspace_bytes(B, G, V, target_dtype).
+ *
+ * Data errors (outputs of that request all -1): len_b outside [0, G]; a draft
+ * token outside [0, V) at a verified position; a read target row that holds a
+ * NaN, whose maximum is +inf, or which is entirely -inf.
+ */
+spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype,
+                          const float *draft_probs, const int32_t *draft_tokens,
+                          const float *uniforms, const int32_t *verify_len,
+                          int32_t B, int32_t G, int32_t V, float temperature,
+                          int32_t *out_accepted, int32_t *out_tokens,
+                          const spec_verify_diag_t *diag,
+                          void *workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/* Bytes of device workspace spec_schedule needs (currently 0: it works in LDS). */
+size_t spec_schedule_workspace_bytes(int32_t B, int32_t G);
+
+/*
+ * spec_schedule -- confidence-scheduled verification depth.
+ *
+ * Operation ("AngelSpec", section 4.2, Eq. 19-21 and the tie rule after them;
+ * "UraionSpec", section "Hardware-Aware Prefix Scheduler", Algorithm 1;
+ * "breaking down dspark and its lineage", section "Verify smarter, not longer"),
+ * in float64:
+ *   s[b,k] = prod_{t=0..k} c[b,t]  (survival of draft k+1);
+ *   candidates (b,k) with s[b,k] > eps, ordered by s descending, then k
+ *   ascending, then b ascending;
+ *   len = 0, T = B, tau = B, best = tau / cost[T];
+ *   for each candidate in order: skip it unless len_b == k; stop if
+ *   T + 1 > token_budget; theta = (tau + s[b,k]) / cost[T+1]; if theta > best
+ *   keep it (len_b = k+1, T += 1, tau += s[b,k], best = theta), else stop.
+ * The result is bit-identical to that sequential loop in float64.
+ *
+ * Arguments (device pointers unless stated):
+ *   confidence          [B, G] float, per-draft acceptance estimates in [0, 1].
+ *   cost_table          [table_len] float, cost of one verification step with
+ *                       T positions, T = 0..table_len-1 (1/steps-per-second);
+ *                       entries T = B..token_budget must be positive.
+ *   B >= 1, G >= 0, B*G <= SPEC_MAX_SCHEDULE_CANDIDATES,
+ *   B <= token_budget < table_len, eps finite.
+ *   out_verify_len      [B] int32 in [0, G]: feed to spec_verify's verify_len.
+ *   out_total_tokens    [1] int32: T = sum_b (len_b + 1).
+ *   out_expected_tokens [1] float: tau = B + sum of kept survivals, or NULL.
+ *   workspace           may be NULL when spec_schedule_workspace_bytes is 0.
+ */
+spec_status_t spec_schedule(const float *confidence, const float *cost_table, int32_t table_len,
+                            int32_t B, int32_t G, int32_t token_budget, float eps,
+                            int32_t *out_verify_len, int32_t *out_total_tokens,
+                            float *out_expected_tokens,
+                            void *workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *spec_status_string(spec_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

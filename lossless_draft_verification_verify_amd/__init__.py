@@ -1,0 +1,142 @@
+"""Batched lossless draft verification and confidence-scheduled depth on MI355X.
+
+Thin PyTorch-facing binding of libspecverify.so (C ABI in include/spec_verify.h).
+It only checks tensor metadata, passes device pointers and the current HIP
+stream, and keeps one zero-filled workspace per (device, stream).  Every step of
+the computation runs in the library's HIP kernels; there is no fallback.
+
+    acc, tok = verify(target_logits, draft_probs, draft_tokens, uniforms, temperature)
+    vlen, T, tau = schedule(confidence, cost_table, token_budget)
+    acc, tok = verify(..., verify_len=vlen)
+"""
+
+import torch
+
+from . import _capi
+from ._capi import SpecError, SPEC_DTYPE_BF16, SPEC_DTYPE_F32  # noqa: F401
+
+__all__ = ["verify", "schedule", "verify_workspace_bytes", "SpecError", "load"]
+
+_workspaces = {}
+
+
+def load():
+    """Load the native library (raises ImportError if it is not built)."""
+    return _capi.load()
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return SPEC_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return SPEC_DTYPE_F32
+    raise TypeError(f"target_logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t, dtype, device, name):
+    if t is None:
+        return 0
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def verify_workspace_bytes(B, G, V, dtype=torch.bfloat16):
+    code = SPEC_DTYPE_BF16 if dtype == torch.bfloat16 else SPEC_DTYPE_F32
+    return _capi.verify_workspace_bytes(B, G, V, code)
+
+
+def _workspace(device, stream_handle, nbytes):
+    key = (device.index, stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        # zero-filled once; every completed call leaves it zero-filled
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def verify(target_logits, draft_probs, draft_tokens, uniforms, temperature, verify_len=None, *,
+           out_accepted=None, out_tokens=None, diag=False, workspace=None):
+    """Verify a batch of draft blocks on the current stream of target_logits' device.
+
+    target_logits [B, G+1, V] bf16/fp32; draft_probs [B, G, V] fp32 (None at T=0);
+    draft_tokens [B, G] int32; uniforms [B, G+1] fp32 (None at T=0);
+    verify_len [B] int32 or None.  Returns (accepted [B], tokens [B, G+1]) int32,
+    plus a dict of diagnostics when diag=True.  Asynchronous like any kernel.
+    """
+    z = target_logits
+    if not isinstance(z, torch.Tensor) or z.dim() != 3:
+        raise ValueError("target_logits must be a [B, G+1, V] tensor")
+    dev = z.device
+    if dev.type != "cuda":
+        raise ValueError("target_logits must be on a GPU")
+    B, G1, V = z.shape
+    G = G1 - 1
+    code = _dtype_code(z)
+    T = float(temperature)
+    i32, f32 = torch.int32, torch.float32
+    if out_accepted is None:
+        out_accepted = torch.empty(B, dtype=i32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty(B, G1, dtype=i32, device=dev)
+    for t, shape, name in ((draft_probs, (B, G, V), "draft_probs"), (draft_tokens, (B, G), "draft_tokens"),
+                           (uniforms, (B, G1), "uniforms"), (verify_len, (B,), "verify_len"),
+                           (out_accepted, (B,), "out_accepted"), (out_tokens, (B, G1), "out_tokens")):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    d = None
+    dg = None
+    if diag:
+        dg = {"target_lse": torch.empty(B, G1, dtype=f32, device=dev),
+              "p_draft": torch.empty(B, G, dtype=f32, device=dev),
+              "q_draft": torch.empty(B, G, dtype=f32, device=dev),
+              "resid_mass": torch.empty(B, dtype=f32, device=dev)}
+        d = _capi.DiagT(*(dg[k].data_ptr() for k in ("target_lse", "p_draft", "q_draft", "resid_mass")))
+    nbytes = _capi.verify_workspace_bytes(B, G, V, code)
+    ws = workspace if workspace is not None else _workspace(dev, stream, nbytes)
+    st = _capi.spec_verify(
+        z.data_ptr(), code, _ptr(draft_probs, f32, dev, "draft_probs"), _ptr(draft_tokens, i32, dev, "draft_tokens"),
+        _ptr(uniforms, f32, dev, "uniforms"), _ptr(verify_len, i32, dev, "verify_len"), B, G, V, T,
+        _ptr(out_accepted, i32, dev, "out_accepted"), _ptr(out_tokens, i32, dev, "out_tokens"), d,
+        ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    if st != _capi.SPEC_OK:
+        raise SpecError(st, "spec_verify")
+    if diag:
+        return out_accepted, out_tokens, dg
+    return out_accepted, out_tokens
+
+
+def schedule(confidence, cost_table, token_budget, eps=0.0, *, out_verify_len=None, out_total=None,
+             out_expected=None):
+    """Choose per-request verify lengths.  Returns (verify_len [B], T [1], tau [1]) device tensors."""
+    c = confidence
+    if not isinstance(c, torch.Tensor) or c.dim() != 2:
+        raise ValueError("confidence must be a [B, G] tensor")
+    dev = c.device
+    B, G = c.shape
+    i32, f32 = torch.int32, torch.float32
+    if cost_table.dim() != 1:
+        raise ValueError("cost_table must be 1-D")
+    L = cost_table.shape[0]
+    if out_verify_len is None:
+        out_verify_len = torch.empty(B, dtype=i32, device=dev)
+    if out_total is None:
+        out_total = torch.empty(1, dtype=i32, device=dev)
+    if out_expected is None:
+        out_expected = torch.empty(1, dtype=f32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = _capi.spec_schedule(_ptr(c, f32, dev, "confidence"), _ptr(cost_table, f32, dev, "cost_table"), L, B, G,
+                             int(token_budget), float(eps), _ptr(out_verify_len, i32, dev, "out_verify_len"),
+                             _ptr(out_total, i32, dev, "out_total"), _ptr(out_expected, f32, dev, "out_expected"),
+                             0, 0, stream)
+    if st != _capi.SPEC_OK:
+        raise SpecError(st, "spec_schedule")
+    return out_verify_len, out_total, out_expected

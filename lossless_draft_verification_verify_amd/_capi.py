@@ -1,0 +1,105 @@
+"""ctypes prototypes of libspecverify.so (the C ABI declared in include/spec_verify.h).
+
+Argument marshalling only.  Loading fails loudly when the library has not been
+built; there is no fallback implementation.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SPEC_OK = 0
+STATUS_NAMES = {
+    0: "SPEC_OK",
+    1: "SPEC_ERR_NULL_POINTER",
+    2: "SPEC_ERR_BAD_SHAPE",
+    3: "SPEC_ERR_BAD_TEMPERATURE",
+    4: "SPEC_ERR_BAD_DTYPE",
+    5: "SPEC_ERR_WORKSPACE_TOO_SMALL",
+    6: "SPEC_ERR_UNSUPPORTED",
+    7: "SPEC_ERR_DEVICE",
+    8: "SPEC_ERR_MISALIGNED",
+}
+SPEC_DTYPE_F32 = 0
+SPEC_DTYPE_BF16 = 1
+
+# Every symbol the header declares.
+EXPORTS = (
+    "spec_verify_workspace_bytes",
+    "spec_verify",
+    "spec_schedule_workspace_bytes",
+    "spec_schedule",
+    "spec_status_string",
+)
+
+
+class DiagT(ctypes.Structure):
+    _fields_ = [
+        ("target_lse", ctypes.c_void_p),
+        ("p_draft", ctypes.c_void_p),
+        ("q_draft", ctypes.c_void_p),
+        ("resid_mass", ctypes.c_void_p),
+    ]
+
+
+class SpecError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+
+def load():
+    """Load libspecverify.so (once).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m lossless_draft_verification_verify_amd.build` "
+            "or __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    lib.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, ctypes.c_int]
+    lib.spec_verify_workspace_bytes.restype = sz
+    lib.spec_verify.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp,
+                                ctypes.POINTER(DiagT), vp, sz, vp]
+    lib.spec_verify.restype = ctypes.c_int
+    lib.spec_schedule_workspace_bytes.argtypes = [i32, i32]
+    lib.spec_schedule_workspace_bytes.restype = sz
+    lib.spec_schedule.argtypes = [vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
+    lib.spec_schedule.restype = ctypes.c_int
+    lib.spec_status_string.argtypes = [ctypes.c_int]
+    lib.spec_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load().spec_status_string(int(status)).decode()
+
+
+def verify_workspace_bytes(B, G, V, dtype_code):
+    return int(load().spec_verify_workspace_bytes(B, G, V, dtype_code))
+
+
+def schedule_workspace_bytes(B, G):
+    return int(load().spec_schedule_workspace_bytes(B, G))
+
+
+def spec_verify(logits, dtype_code, q, x, u, vlen, B, G, V, T, out_acc, out_tok, diag, ws, ws_bytes, stream):
+    """Raw call; pointers are ints (0 = NULL), `diag` a DiagT or None.  Returns the status."""
+    d = ctypes.byref(diag) if diag is not None else None
+    return int(load().spec_verify(logits or None, dtype_code, q or None, x or None, u or None, vlen or None,
+                                  B, G, V, ctypes.c_float(T), out_acc or None, out_tok or None, d,
+                                  ws or None, ws_bytes, stream or None))
+
+
+def spec_schedule(conf, cost, table_len, B, G, budget, eps, out_len, out_T, out_tau, ws, ws_bytes, stream):
+    return int(load().spec_schedule(conf or None, cost or None, table_len, B, G, budget, ctypes.c_float(eps),
+                                    out_len or None, out_T or None, out_tau or None, ws or None, ws_bytes,
+                                    stream or None))

@@ -1,0 +1,214 @@
+// Host side of the C ABI: argument validation (before any HIP call), launch
+// planning from the device's resident capacity, and kernel launches.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "spec_verify.h"
+#include "sv_plan.h"
+
+namespace {
+
+using sv::Layout;
+
+int esize_of(int dt) {
+    if (dt == SPEC_DTYPE_F32) return 4;
+    if (dt == SPEC_DTYPE_BF16) return 2;
+    return 0;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape limits of the verify launch: grid size and 32-bit element offsets
+// inside a row stay representable.
+spec_status_t check_verify_shape(int64_t B, int64_t G, int64_t V, int es) {
+    if (B < 1 || G < 0 || V < 1) return SPEC_ERR_BAD_SHAPE;
+    if (G > SPEC_MAX_DRAFTS || V > SPEC_MAX_VOCAB) return SPEC_ERR_UNSUPPORTED;
+    const int64_t nc1 = (V + sv::chunk_elems(es) - 1) / sv::chunk_elems(es);
+    const int64_t ntiles = (V + sv::kTile - 1) / sv::kTile;
+    const int64_t items = B * ((G + 1) * nc1 + ntiles);
+    if (items >= (int64_t(1) << 31)) return SPEC_ERR_UNSUPPORTED;
+    if (B * (G + 1) > (int64_t(1) << 40) / V) return SPEC_ERR_UNSUPPORTED;
+    return SPEC_OK;
+}
+
+struct DeviceInfo {
+    bool ready = false;
+    int cus = 0;
+    int occ[2][2][2] = {};   // [esize==2][aligned_z][aligned_q] blocks per CU, 0 = unknown
+};
+std::mutex g_mu;
+DeviceInfo g_dev[128];
+
+// Resident workgroups of the sampled kernel on this device; -1 on error.
+long resident_capacity(int dev, bool az, bool aq, int es) {
+    if (dev < 0 || dev >= 128) return -1;
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceInfo &d = g_dev[dev];
+    if (!d.ready) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return -1;
+        d.cus = cus;
+        d.ready = true;
+    }
+    int &o = d.occ[es == 2][az][aq];
+    if (o == 0) {
+        int n = 0;
+        if (sv::verify_sampled_occupancy(az, aq, es, &n) != 0 || n <= 0) return -1;
+        o = n;
+    }
+    return long(o) * d.cus;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *spec_status_string(spec_status_t s) {
+    switch (s) {
+    case SPEC_OK: return "ok";
+    case SPEC_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case SPEC_ERR_BAD_SHAPE: return "shape, table, budget or eps out of range";
+    case SPEC_ERR_BAD_TEMPERATURE: return "temperature must be 0 or a finite value >= 2^-126";
+    case SPEC_ERR_BAD_DTYPE: return "unknown dtype";
+    case SPEC_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the workspace-size query";
+    case SPEC_ERR_UNSUPPORTED: return "shape beyond this build's limits";
+    case SPEC_ERR_DEVICE: return "HIP error while querying the device or launching";
+    case SPEC_ERR_MISALIGNED: return "pointer misaligned for its element type (workspace: 256 bytes)";
+    }
+    return "unknown status";
+}
+
+size_t spec_verify_workspace_bytes(int32_t B, int32_t G, int32_t V, spec_dtype_t dt) {
+    const int es = esize_of(int(dt));
+    if (es == 0 || check_verify_shape(B, G, V, es) != SPEC_OK) return 0;
+    return sv::make_layout(B, G, V, es).total;
+}
+
+spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, const float *draft_probs,
+                          const int32_t *draft_tokens, const float *uniforms, const int32_t *verify_len,
+                          int32_t B, int32_t G, int32_t V, float temperature, int32_t *out_accepted,
+                          int32_t *out_tokens, const spec_verify_diag_t *diag, void *workspace,
+                          size_t workspace_bytes, spec_stream_t stream) {
+    // ---- host-checkable errors, before anything touches the device
+    const int es = esize_of(int(target_dtype));
+    if (es == 0) return SPEC_ERR_BAD_DTYPE;
+    const spec_status_t sh = check_verify_shape(B, G, V, es);
+    if (sh != SPEC_OK) return sh;
+    const float T = temperature;
+    if (!std::isfinite(T) || T < 0.0f || (T > 0.0f && T < 1.17549435e-38f)) return SPEC_ERR_BAD_TEMPERATURE;
+    const bool sampled = T > 0.0f;
+    if (!target_logits || !out_accepted || !out_tokens) return SPEC_ERR_NULL_POINTER;
+    if (G > 0 && !draft_tokens) return SPEC_ERR_NULL_POINTER;
+    if (sampled && G > 0 && !draft_probs) return SPEC_ERR_NULL_POINTER;
+    if (sampled && !uniforms) return SPEC_ERR_NULL_POINTER;
+    if (!aligned(target_logits, es) || !aligned(draft_probs, 4) || !aligned(draft_tokens, 4) ||
+        !aligned(uniforms, 4) || !aligned(verify_len, 4) || !aligned(out_accepted, 4) ||
+        !aligned(out_tokens, 4))
+        return SPEC_ERR_MISALIGNED;
+    spec_verify_diag_t dg = {nullptr, nullptr, nullptr, nullptr};
+    if (diag && sampled) dg = *diag;
+    if (!aligned(dg.target_lse, 4) || !aligned(dg.p_draft, 4) || !aligned(dg.q_draft, 4) ||
+        !aligned(dg.resid_mass, 4))
+        return SPEC_ERR_MISALIGNED;
+    const Layout lay = sv::make_layout(B, G, V, es);
+    if (!workspace) return SPEC_ERR_NULL_POINTER;
+    if (!aligned(workspace, 256)) return SPEC_ERR_MISALIGNED;
+    if (workspace_bytes < lay.total) return SPEC_ERR_WORKSPACE_TOO_SMALL;
+
+    // ---- launch plan
+    sv::VerifyArgs a = {};
+    a.logits = target_logits;
+    a.q = draft_probs;
+    a.x = draft_tokens;
+    a.u = uniforms;
+    a.vlen = verify_len;
+    a.out_acc = out_accepted;
+    a.out_tok = out_tokens;
+    a.d_lse = dg.target_lse;
+    a.d_p = dg.p_draft;
+    a.d_q = dg.q_draft;
+    a.d_r = dg.resid_mass;
+    a.ws = static_cast<unsigned char *>(workspace);
+    a.lay = lay;
+    a.B = B;
+    a.G = G;
+    a.V = V;
+    a.T = T;
+    a.c32 = sampled ? float(1.4426950408889634 / double(T)) : 0.0f;
+    a.ch1 = sv::chunk_elems(es);
+    a.nc1 = (V + a.ch1 - 1) / a.ch1;
+    a.ntiles = (V + sv::kTile - 1) / sv::kTile;
+    a.spin_limit = 1u << 22;
+    const bool az = aligned(target_logits, 16) && (size_t(V) * es) % 16 == 0;
+    const bool aq = aligned(draft_probs, 16) && V % 4 == 0;
+    const long g1 = long(G + 1) * a.nc1;
+
+    if (!sampled) {
+        const long grid = long(B) * g1;
+        return sv::launch_verify_greedy(a, az, es, int(grid), stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+    }
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SPEC_ERR_DEVICE;
+    const long cap = resident_capacity(dev, az, aq, es);
+    if (cap <= 0) return SPEC_ERR_DEVICE;
+    // Draw workgroups that may wait must stay below half of the resident capacity.
+    const long half = cap / 2;
+    long nc2 = half / B;
+    if (nc2 < 1) nc2 = 1;
+    if (nc2 > a.ntiles) nc2 = a.ntiles;
+    a.tpw = int((a.ntiles + nc2 - 1) / nc2);
+    a.nc2 = (a.ntiles + a.tpw - 1) / a.tpw;
+    const bool fused = long(B) * a.nc2 <= half;
+    if (fused) {
+        long lag = (cap + g1 - 1) / g1 + 1;
+        if (lag > B) lag = B;
+        a.lag = int(lag);
+        a.mode = 0;
+        const long grid = long(B) * (g1 + a.nc2);
+        return sv::launch_verify_sampled(a, az, aq, es, int(grid), stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+    }
+    a.lag = B;
+    a.mode = 1;
+    if (sv::launch_verify_sampled(a, az, aq, es, int(long(B) * g1), stream) != 0) return SPEC_ERR_DEVICE;
+    a.mode = 2;
+    return sv::launch_verify_sampled(a, az, aq, es, int(long(B) * a.nc2), stream) == 0 ? SPEC_OK
+                                                                                       : SPEC_ERR_DEVICE;
+}
+
+size_t spec_schedule_workspace_bytes(int32_t, int32_t) { return 0; }
+
+spec_status_t spec_schedule(const float *confidence, const float *cost_table, int32_t table_len, int32_t B,
+                            int32_t G, int32_t token_budget, float eps, int32_t *out_verify_len,
+                            int32_t *out_total_tokens, float *out_expected_tokens, void *workspace,
+                            size_t workspace_bytes, spec_stream_t stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (B < 1 || G < 0 || table_len < 1) return SPEC_ERR_BAD_SHAPE;
+    if (int64_t(B) * G > SPEC_MAX_SCHEDULE_CANDIDATES || B > SPEC_MAX_SCHEDULE_CANDIDATES)
+        return SPEC_ERR_UNSUPPORTED;
+    if (token_budget < B || token_budget >= table_len) return SPEC_ERR_BAD_SHAPE;
+    if (!std::isfinite(eps)) return SPEC_ERR_BAD_SHAPE;
+    if ((G > 0 && !confidence) || !cost_table || !out_verify_len || !out_total_tokens) return SPEC_ERR_NULL_POINTER;
+    if (!aligned(confidence, 4) || !aligned(cost_table, 4) || !aligned(out_verify_len, 4) ||
+        !aligned(out_total_tokens, 4) || !aligned(out_expected_tokens, 4))
+        return SPEC_ERR_MISALIGNED;
+    sv::ScheduleArgs a = {};
+    a.conf = confidence;
+    a.cost = cost_table;
+    a.B = B;
+    a.G = G;
+    a.budget = token_budget;
+    a.eps = eps;
+    a.out_len = out_verify_len;
+    a.out_T = out_total_tokens;
+    a.out_tau = out_expected_tokens;
+    return sv::launch_schedule(a, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads, exports every function include/spec_verify.h declares, sizes
+its workspace, and rejects bad arguments with a status before touching the
+device (argument errors are caught before any HIP call, so these run on a
+machine without a GPU).  Pointers below are fake, never dereferenced.
+"""
+
+import os
+import re
+
+import pytest
+
+from lossless_draft_verification_verify_amd import _capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+# Fake, suitably aligned device addresses (never dereferenced by host validation).
+P = 0x7F0000000000
+Z, Q, X, U, VL, OA, OT, WS = (P + i * 0x100000 for i in range(8))
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = _capi.load()
+    declared = header_functions()
+    assert set(declared) == set(_capi.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(9):
+        s = _capi.status_string(code)
+        assert isinstance(s, str) and s and s != "unknown status"
+    assert _capi.status_string(99) == "unknown status"
+
+
+def test_workspace_query():
+    w = _capi.verify_workspace_bytes(64, 15, 129280, _capi.SPEC_DTYPE_BF16)
+    # counters 3*256 + partials 64*16*8 chunks*8 B + decisions + tile masses 64*16*16 B
+    assert w == 3 * 256 + 65536 + 2048 + 16384
+    assert _capi.verify_workspace_bytes(64, 15, 129280, _capi.SPEC_DTYPE_F32) >= w
+    assert _capi.verify_workspace_bytes(0, 15, 100, 1) == 0
+    assert _capi.verify_workspace_bytes(1, -1, 100, 1) == 0
+    assert _capi.verify_workspace_bytes(1, 1, 100, 7) == 0
+    assert _capi.verify_workspace_bytes(1, 256, 100, 1) == 0
+    assert _capi.schedule_workspace_bytes(64, 15) == 0
+
+
+def _verify(**kw):
+    args = dict(logits=Z, dtype_code=1, q=Q, x=X, u=U, vlen=0, B=4, G=3, V=1000, T=1.0, out_acc=OA,
+                out_tok=OT, diag=None, ws=WS, ws_bytes=1 << 20, stream=0)
+    args.update(kw)
+    return _capi.spec_verify(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype_code=5), 4),
+    (dict(B=0), 2), (dict(G=-1), 2), (dict(V=0), 2),
+    (dict(G=256), 6), (dict(V=(1 << 30) + 1), 6),
+    (dict(T=-0.5), 3), (dict(T=float("nan")), 3), (dict(T=float("inf")), 3), (dict(T=1e-39), 3),
+    (dict(logits=0), 1), (dict(out_acc=0), 1), (dict(out_tok=0), 1), (dict(x=0), 1),
+    (dict(q=0), 1), (dict(u=0), 1), (dict(ws=0), 1),
+    (dict(logits=Z + 1), 8), (dict(q=Q + 2), 8), (dict(x=X + 2), 8), (dict(vlen=VL + 1), 8),
+    (dict(ws=WS + 16), 8), (dict(logits=Z + 2, dtype_code=0), 8),
+    (dict(ws_bytes=100), 5),
+])
+def test_verify_rejects_bad_arguments(kw, status):
+    assert _verify(**kw) == status
+
+
+def test_verify_nullable_inputs_follow_the_mode():
+    # T == 0: q and u may be NULL; G == 0: q and x may be NULL.  These pass
+    # validation, so they must fail later only for lack of a device: check
+    # just that they are not reported as NULL pointers.
+    assert _verify(T=0.0, q=0, u=0, ws_bytes=100) == 5
+    assert _verify(G=0, q=0, x=0, ws_bytes=100) == 5
+
+
+def test_verify_diag_alignment_checked():
+    d = _capi.DiagT(P + 2, 0, 0, 0)
+    assert _verify(diag=d) == 8
+
+
+def _sched(**kw):
+    args = dict(conf=Q, cost=U, table_len=513, B=4, G=15, budget=512, eps=0.0, out_len=OA, out_T=OT,
+                out_tau=X, ws=0, ws_bytes=0, stream=0)
+    args.update(kw)
+    return _capi.spec_schedule(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 2), (dict(G=-1), 2), (dict(table_len=0), 2),
+    (dict(budget=3), 2), (dict(budget=513), 2), (dict(eps=float("nan")), 2),
+    (dict(B=300, G=15, budget=400), 6), (dict(B=5000, G=0, budget=5000, table_len=6000), 6),
+    (dict(conf=0), 1), (dict(cost=0), 1), (dict(out_len=0), 1), (dict(out_T=0), 1),
+    (dict(conf=Q + 1), 8), (dict(out_tau=X + 2), 8),
+])
+def test_schedule_rejects_bad_arguments(kw, status):
+    assert _sched(**kw) == status

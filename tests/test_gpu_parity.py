@@ -1,0 +1,296 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Same seeded inputs on both sides (workloads.py).  Sizes are small enough for
+the oracle to finish in seconds while spanning several row chunks, several
+final-draw tiles and ragged tails; the full-size workloads run too.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import lossless_draft_verification_verify_amd as sv
+from parity_util import compare, run_gpu, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sv.load()
+    yield
+
+
+def check(w, verify_len=None, diag=True):
+    say(f"[parity] {w['name']} B={w['B']} G={w['G']} V={w['V']} T={w['T']} dtype={w['dtype']}")
+    g = run_gpu(w, diag=diag)
+    o = run_oracle(w, verify_len)
+    rep = compare(w, g, o, verify_len, check_diag=diag)
+    say("   ", rep)
+    return g, o, rep
+
+
+# ------------------------------------------------------------ page example
+
+def test_page_example_grid():
+    """Worked example p=(0.5,0.3,0.2), q=(0.4,0.5,0.1): every x, a grid of (u0, u1)."""
+    base = W.page_example()
+    M0, M1 = 50, 20
+    u0 = (np.arange(M0) + 0.5) / M0
+    u1 = (np.arange(M1) + 0.5) / M1
+    xs, us = [], []
+    for x in range(3):
+        for a in u0:
+            for b in u1:
+                xs.append([x])
+                us.append([a, b])
+    N = len(xs)
+    w = W.Workload(base)
+    w.update(B=N, logits=np.repeat(base["logits"], N, 0), draft_probs=np.repeat(base["draft_probs"], N, 0),
+             draft_tokens=np.array(xs, np.int32), uniforms=np.array(us, np.float32))
+    g, o, rep = check(w)
+    # acceptance mass and first-token law of the page: 0.8 and (0.5, 0.3, 0.2)
+    q = base["draft_probs"][0, 0].astype(np.float64)
+    acc = g["accepted"].reshape(3, -1)
+    first = g["tokens"][:, 0].reshape(3, -1)
+    mass = sum(q[x] * np.mean(acc[x] == 1) for x in range(3))
+    law = sum(q[x] * np.bincount(first[x], minlength=3) / first.shape[1] for x in range(3))
+    assert abs(mass - 0.8) < 1e-6
+    np.testing.assert_allclose(law, [0.5, 0.3, 0.2], atol=1e-6)
+
+
+# ------------------------------------------------------------ configs
+
+def test_tiny_fp32():
+    for seed in range(6):
+        check(W.tiny(seed=1235 + seed))
+
+
+def test_mtp_bf16():
+    check(W.mtp())
+
+
+def test_block_reduced_ragged():
+    # V not a multiple of the row chunk (16384) or the draw tile (8192)
+    check(W.block(B=8, G=15, V=20000))
+    check(W.block(B=5, G=6, V=40961, seed=77))
+
+
+def test_block_full_size():
+    g, o, rep = check(W.block())
+    assert rep["requests"] == 64
+
+
+def test_greedy_full_size_bit_exact():
+    w = W.greedy()
+    say("[parity] greedy full")
+    g = run_gpu(w)
+    o = run_oracle(w)
+    np.testing.assert_array_equal(g["accepted"], o["accepted"])
+    np.testing.assert_array_equal(g["tokens"], o["tokens"])
+    say("    accepted mean", g["accepted"].mean())
+
+
+def test_greedy_ties_and_sizes():
+    g0 = np.random.default_rng(3)
+    for (B, G, V) in [(16, 7, 1024), (9, 3, 1023), (4, 5, 16385), (3, 2, 50001)]:
+        z = np.round(g0.normal(0, 1, size=(B, G + 1, V)) * 2) / 2          # many exact ties
+        bits = W.f32_to_bf16_bits(z.astype(np.float32))
+        zf = W.bf16_bits_to_f32(bits).astype(np.float64)
+        a = zf.argmax(2)
+        x = np.where(g0.random((B, G)) < 0.8, a[:, :G], g0.integers(0, V, (B, G))).astype(np.int32)
+        w = W.Workload(name=f"greedy_ties_{V}", B=B, G=G, V=V, T=0.0, dtype="bf16", logits=bits,
+                       draft_probs=None, draft_tokens=x, uniforms=None, verify_len=None)
+        say(f"[parity] {w['name']}")
+        g = run_gpu(w)
+        o = run_oracle(w)
+        np.testing.assert_array_equal(g["accepted"], o["accepted"])
+        np.testing.assert_array_equal(g["tokens"], o["tokens"])
+        # fp32 logits, same ties
+        w2 = W.Workload(w)
+        w2.update(dtype="f32", logits=zf.astype(np.float32), name=f"greedy_ties_f32_{V}")
+        g = run_gpu(w2)
+        o = run_oracle(w2)
+        np.testing.assert_array_equal(g["accepted"], o["accepted"])
+        np.testing.assert_array_equal(g["tokens"], o["tokens"])
+
+
+# ------------------------------------------------------------ scheduling
+
+@pytest.mark.parametrize("B", [4, 16, 64])
+def test_scheduled_end_to_end(B):
+    w = W.scheduled(B)
+    say(f"[parity] scheduled B={B}")
+    c = torch.from_numpy(w["confidence"]).cuda()
+    cost = torch.from_numpy(w["cost_table"]).cuda()
+    vl, T, tau = sv.schedule(c, cost, w["budget"])
+    torch.cuda.synchronize()
+    lens_o, T_o, tau_o = oracle.schedule(w["confidence"], w["cost_table"], w["budget"])
+    np.testing.assert_array_equal(vl.cpu().numpy(), lens_o)
+    assert int(T.item()) == T_o
+    assert abs(float(tau.item()) - tau_o) <= 1e-6 * tau_o
+    say(f"    T={T_o} tau={tau_o:.4f} lens={lens_o.tolist()[:16]}")
+    # verify with the device-resident lengths
+    w["verify_len"] = lens_o
+    g = run_gpu(w, verify_len=vl)
+    o = run_oracle(w, lens_o)
+    say("   ", compare(w, g, o, lens_o))
+
+
+def test_schedule_random_against_oracle():
+    g0 = np.random.default_rng(11)
+    for trial in range(30):
+        B = int(g0.integers(1, 70))
+        G = int(g0.integers(0, 17))
+        conf = (1 / (1 + np.exp(-g0.normal(1.0, 1.5, size=(B, G))))).astype(np.float32)
+        if trial % 5 == 1:
+            conf[g0.random((B, G)) < 0.2] = 0.0
+        if trial % 5 == 2:
+            conf = np.round(conf * 4) / 4                      # many exact ties
+        if trial % 7 == 3:
+            conf = (conf * 1.6).astype(np.float32)             # > 1: non-contiguous skips
+        L = int(B * (G + 1) + int(g0.integers(1, 40)))
+        a, b = 1.0, float(g0.choice([0.0, 0.001, 0.02, 0.2]))
+        cost = (a + b * np.arange(L)).astype(np.float32)
+        if trial % 4 == 3:
+            cost = (a + b * np.arange(L) + 0.3 * np.sqrt(np.arange(L))).astype(np.float32)
+        budget = int(g0.integers(B, L))
+        eps = float(g0.choice([0.0, 0.01]))
+        vl, T, tau = sv.schedule(torch.from_numpy(conf).cuda(), torch.from_numpy(cost).cuda(), budget, eps)
+        torch.cuda.synchronize()
+        lo, To, tauo = oracle.schedule(conf, cost, budget, eps)
+        np.testing.assert_array_equal(vl.cpu().numpy(), lo, err_msg=f"trial {trial}")
+        assert int(T.item()) == To, trial
+        assert abs(float(tau.item()) - np.float32(tauo)) <= 1e-6 * max(1.0, tauo), trial
+
+
+# ------------------------------------------------------------ edge cases
+
+def _rand_workload(name, B, G, V, T=1.0, dtype="bf16", seed=0, zscale=2.0):
+    g0 = np.random.default_rng(seed)
+    z = (zscale * g0.normal(size=(B, G + 1, V))).astype(np.float32)
+    if dtype == "bf16":
+        bits = W.f32_to_bf16_bits(z)
+        zf = W.bf16_bits_to_f32(bits)
+        logits = bits
+    else:
+        zf = z
+        logits = z
+    d = zf[:, :G].astype(np.float64) + 0.7 * g0.normal(size=(B, G, V))
+    q = np.exp((d - d.max(2, keepdims=True)) / T)
+    q = (q / q.sum(2, keepdims=True)).astype(np.float32)
+    x = np.array([[g0.choice(V, p=q[b, k] / q[b, k].astype(np.float64).sum()) for k in range(G)]
+                  for b in range(B)], np.int32).reshape(B, G)
+    u = g0.random((B, G + 1), dtype=np.float32)
+    return W.Workload(name=name, B=B, G=G, V=V, T=T, dtype=dtype, logits=logits, draft_probs=q,
+                      draft_tokens=x, uniforms=u, verify_len=None)
+
+
+def test_gamma_zero_plain_sampling():
+    w = _rand_workload("gamma0", 50, 0, 3000, seed=1)
+    check(w)
+
+
+def test_verify_len_mixed():
+    w = _rand_workload("vlen", 40, 6, 5000, seed=2)
+    w["verify_len"] = np.random.default_rng(2).integers(0, 7, size=40).astype(np.int32)
+    check(w)
+
+
+def test_unaligned_vocab_sizes():
+    for V, dt in [(1023, "bf16"), (1023, "f32"), (129281, "bf16"), (8193, "f32"), (7, "bf16")]:
+        check(_rand_workload(f"V{V}_{dt}", 6, 4, V, dtype=dt, seed=V))
+
+
+def test_q_equal_p_accepts_all():
+    B, G, V = 12, 5, 4096
+    z = np.zeros((B, G + 1, V), np.float32)                  # uniform rows: p = 1/V exactly
+    q = np.full((B, G, V), 1.0 / V, np.float32)
+    g0 = np.random.default_rng(4)
+    w = W.Workload(name="q_eq_p", B=B, G=G, V=V, T=1.0, dtype="f32", logits=z, draft_probs=q,
+                   draft_tokens=g0.integers(0, V, (B, G)).astype(np.int32),
+                   uniforms=g0.random((B, G + 1), dtype=np.float32), verify_len=None)
+    g, o, rep = check(w)
+    assert np.all(g["accepted"] == G)
+
+
+def test_onehot_draft_zero_target_mass_and_masked_vocab():
+    B, G, V = 10, 3, 2048
+    g0 = np.random.default_rng(5)
+    z = g0.normal(0, 2, size=(B, G + 1, V)).astype(np.float32)
+    z[:, :, 1000:1500] = -np.inf                             # masked vocabulary
+    x = np.full((B, G), 1200, np.int32)                     # draft a masked token
+    q = np.zeros((B, G, V), np.float32)
+    q[:, :, 1200] = 1.0                                     # one-hot draft
+    w = W.Workload(name="onehot_masked", B=B, G=G, V=V, T=1.0, dtype="f32", logits=z, draft_probs=q,
+                   draft_tokens=x, uniforms=g0.random((B, G + 1), dtype=np.float32), verify_len=None)
+    g, o, rep = check(w)
+    assert np.all(g["accepted"] == 0)
+    assert np.all((g["tokens"][:, 0] < 1000) | (g["tokens"][:, 0] >= 1500))
+
+
+def test_extreme_uniforms():
+    w = _rand_workload("u_extremes", 32, 4, 3000, seed=6)
+    u = w["uniforms"]
+    u[:16] = 0.0
+    u[16:] = np.float32(np.nextafter(np.float32(1), np.float32(0)))
+    check(w)
+
+
+def test_low_temperature_and_peaked_rows():
+    check(_rand_workload("lowT", 16, 4, 6000, T=0.05, seed=7))
+    check(_rand_workload("peaked", 16, 4, 6000, T=1.0, seed=8, zscale=12.0))
+
+
+def test_data_errors():
+    w = _rand_workload("errors", 8, 3, 1500, dtype="f32", seed=9)
+    z = w["logits"]
+    z[1, 2, 7] = np.nan                      # NaN in a read row
+    z[2, 0, 3] = np.inf                      # +inf maximum
+    z[3, 1, :] = -np.inf                     # all -inf
+    w["draft_tokens"][4, 1] = 1500           # out of range
+    w["draft_tokens"][5, 0] = -3
+    vl = np.array([3, 3, 3, 3, 3, 3, 4, 1], np.int32)   # request 6: verify_len > G
+    z[7, 3, :] = np.nan                      # beyond verify_len=1: never read
+    w["verify_len"] = vl
+    g, o, rep = check(w)
+    assert g["accepted"].tolist()[:7] == [g["accepted"][0], -1, -1, -1, -1, -1, -1]
+    assert g["accepted"][7] >= 0
+
+
+def test_split_launch_path():
+    # Many requests: the draw pass runs as a second launch.
+    check(_rand_workload("split", 700, 1, 300, seed=10))
+
+
+def test_workspace_reuse_and_determinism():
+    w1 = W.block(B=8, G=15, V=20000, seed=5)
+    w2 = _rand_workload("small", 3, 2, 100, seed=12)
+    r1 = run_gpu(w1)
+    run_gpu(w2)
+    r3 = run_gpu(w1)
+    for k in ("accepted", "tokens", "p_draft", "lse", "resid_mass"):
+        np.testing.assert_array_equal(np.nan_to_num(r1[k], nan=-7.0), np.nan_to_num(r3[k], nan=-7.0))
+
+
+def test_workspace_left_zero():
+    w = W.block(B=4, G=3, V=9000, seed=3)
+    z, q, x, u, vl = to_device(w)
+    nbytes = sv.verify_workspace_bytes(4, 3, 9000)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sv.verify(z, q, x, u, 1.0, workspace=ws)
+    sv.verify(z, None, x, None, 0.0, workspace=ws)
+    torch.cuda.synchronize()
+    counters = ws[: 3 * 256].cpu().numpy()
+    assert not counters.any()
