@@ -56,6 +56,7 @@ typedef enum { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 } spec_dtype_t;
 typedef void *spec_stream_t;
 
 /* Limits of this build. */
+#define SPEC_MAX_BATCH 65536          /* B <= 65536 for spec_verify                      */
 #define SPEC_MAX_DRAFTS 255           /* G <= 255                                        */
 #define SPEC_MAX_VOCAB (1 << 30)      /* V <= 2^30                                       */
 #define SPEC_MAX_SCHEDULE_CANDIDATES 4096 /* B * G <= 4096 for spec_schedule              */
@@ -85,12 +86,13 @@ typedef struct {
  * Bytes of device workspace spec_verify needs for this shape (0 on invalid
  * arguments).  The same workspace serves every shape whose query is not larger.
  *
- * The workspace holds per-row partial reductions, per-request decisions and
- * per-request arrival counters.  It must be zero-filled once before its first
- * use (e.g. allocated with a zeroing allocator); every completed call leaves it
- * zero-filled again, so it can be reused by later calls without clearing.
- * Calls that share one workspace must not overlap in time (use one workspace
- * per stream).
+ * The workspace starts with a fixed 1 MiB region of per-request counters and
+ * flags (the same offsets for every shape), followed by per-row partial
+ * reductions, per-request decisions and per-tile masses.  It must be
+ * zero-filled once before its first use (e.g. allocated with a zeroing
+ * allocator); every completed call leaves the counter region zero again, so
+ * one workspace can serve later calls of any shape without clearing.  Calls
+ * that share one workspace must not overlap in time (use one per stream).
  */
 size_t spec_verify_workspace_bytes(int32_t B, int32_t G, int32_t V, spec_dtype_t target_dtype);
 
@@ -124,7 +126,7 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t G, int32_t V, spec_dtype_t
  *   uniforms       [B, G+1] float in [0, 1): u[b,k], k < G, decides draft k;
  *                  u[b,G] is the final draw.  May be NULL if T == 0.
  *   verify_len     [B] int32 in [0, G], or NULL meaning G for every request.
- *   B >= 1, 0 <= G <= SPEC_MAX_DRAFTS, 1 <= V <= SPEC_MAX_VOCAB.
+ *   1 <= B <= SPEC_MAX_BATCH, 0 <= G <= SPEC_MAX_DRAFTS, 1 <= V <= SPEC_MAX_VOCAB.
  *   temperature    T == 0 (greedy) or 2^-126 <= T < inf.
  *   out_accepted   [B] int32: accepted drafts j in [0, len_b]; -1 = data error.
  *   out_tokens     [B, G+1] int32.

@@ -10,6 +10,8 @@
 #include "spec_verify.h"
 #include "sv_plan.h"
 
+static_assert(SPEC_MAX_BATCH == sv::kMaxBatch, "batch limit matches the counter region");
+
 namespace {
 
 using sv::Layout;
@@ -26,7 +28,7 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // inside a row stay representable.
 spec_status_t check_verify_shape(int64_t B, int64_t G, int64_t V, int es) {
     if (B < 1 || G < 0 || V < 1) return SPEC_ERR_BAD_SHAPE;
-    if (G > SPEC_MAX_DRAFTS || V > SPEC_MAX_VOCAB) return SPEC_ERR_UNSUPPORTED;
+    if (B > SPEC_MAX_BATCH || G > SPEC_MAX_DRAFTS || V > SPEC_MAX_VOCAB) return SPEC_ERR_UNSUPPORTED;
     const int64_t nc1 = (V + sv::chunk_elems(es) - 1) / sv::chunk_elems(es);
     const int64_t ntiles = (V + sv::kTile - 1) / sv::kTile;
     const int64_t items = B * ((G + 1) * nc1 + ntiles);

@@ -19,8 +19,17 @@ constexpr unsigned kFlagError = 2;  // request has a data error; outputs already
 // Elements per row-pass chunk: 256 threads x 8 loads x 16 bytes.
 inline int chunk_elems(int esize) { return kWG * kVecPerThread * (16 / esize); }
 
+// Workspace layout.  The first kCounterBytes hold one 16-byte slot of
+// counters per request, {row-pass arrivals, decision flag, draw-pass
+// arrivals, unused}, at the same offsets for every shape: these must start at
+// zero and every completed call leaves them at zero, so one zero-filled
+// workspace stays valid across calls of any shape.  Everything after them is
+// written before it is read within a call.
+constexpr int kMaxBatch = 65536;
+constexpr size_t kSlotBytes = 16;
+constexpr size_t kCounterBytes = size_t(kMaxBatch) * kSlotBytes;
+
 struct Layout {
-    size_t ctr1, flag, ctr2;   // [B] uint32 each: row-pass arrivals, decision flag, draw-pass arrivals
     size_t part;               // [B*(G+1)*nc1] 8 bytes: (max, sum) or (max, argmax)
     size_t dec;                // [B] Decision
     size_t mass;               // [B*ntiles] 2 doubles: (residual mass, target mass) per tile
@@ -33,10 +42,7 @@ inline Layout make_layout(int64_t B, int64_t G, int64_t V, int esize) {
     const int64_t nc1 = (V + chunk_elems(esize) - 1) / chunk_elems(esize);
     const int64_t ntiles = (V + kTile - 1) / kTile;
     Layout L;
-    size_t o = 0;
-    L.ctr1 = o; o += align256(size_t(B) * 4);
-    L.flag = o; o += align256(size_t(B) * 4);
-    L.ctr2 = o; o += align256(size_t(B) * 4);
+    size_t o = kCounterBytes;
     L.part = o; o += align256(size_t(B) * size_t(G + 1) * size_t(nc1) * 8);
     L.dec = o;  o += align256(size_t(B) * 32);
     L.mass = o; o += align256(size_t(B) * size_t(ntiles) * 16);
@@ -48,7 +54,7 @@ inline Layout make_layout(int64_t B, int64_t G, int64_t V, int esize) {
 // row pass, read by the final-draw workgroups.
 struct Decision {
     int32_t j;        // accepted drafts
-    int32_t row;      // target row of the final draw (j, or len when all accepted)
+    int32_t row;      // target row of the final draw: always j (j = len when all accepted)
     int32_t resid;    // 1: draw from max(p_j - q_j, 0); 0: draw from p_row
     int32_t pad;
     float m;          // row maximum (logit units)

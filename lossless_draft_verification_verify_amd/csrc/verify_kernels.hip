@@ -191,8 +191,10 @@ __device__ void write_error(const VerifyArgs &a, int b, bool diag) {
     if (threadIdx.x == 0 && a.d_r) a.d_r[b] = qnan;
 }
 
-__device__ __forceinline__ unsigned *ws_u32(const VerifyArgs &a, size_t off) {
-    return reinterpret_cast<unsigned *>(a.ws + off);
+// Per-request counter slot at a fixed offset: [0] row-pass arrivals,
+// [1] decision flag, [2] draw-pass arrivals.
+__device__ __forceinline__ unsigned *slot(const VerifyArgs &a, int b) {
+    return reinterpret_cast<unsigned *>(a.ws + size_t(b) * kSlotBytes);
 }
 
 // ------------------------------------------------------------- row pass
@@ -354,7 +356,7 @@ __device__ void decide_sampled(const VerifyArgs &a, int b, int n, Smem &sh) {
         if (a.d_q) a.d_q[size_t(b) * a.G + k] = qx;
     }
     __syncthreads();
-    unsigned *flag = ws_u32(a, a.lay.flag) + b;
+    unsigned *flag = slot(a, b) + 1;
     const bool diag = a.d_lse || a.d_p || a.d_q || a.d_r;
     if (sh.bad) {
         write_error(a, b, diag);
@@ -585,8 +587,8 @@ __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, cons
 // One draw workgroup: tiles [w*tpw, (w+1)*tpw) of request b's draw row.
 template <int ES, bool ALZ, bool ALQ>
 __device__ void draw_item(const VerifyArgs &a, int b, int w, Smem &sh) {
-    unsigned *flag = ws_u32(a, a.lay.flag) + b;
-    unsigned *ctr2 = ws_u32(a, a.lay.ctr2) + b;
+    unsigned *flag = slot(a, b) + 1;
+    unsigned *ctr2 = slot(a, b) + 2;
     if (threadIdx.x == 0) {
         unsigned f;
         uint32_t spins = 0;
@@ -608,6 +610,13 @@ __device__ void draw_item(const VerifyArgs &a, int b, int w, Smem &sh) {
         return;
     }
     const Decision d = reinterpret_cast<const Decision *>(a.ws + a.lay.dec)[b];
+    if (d.j < 0 || d.j > a.G || d.row != d.j || (d.resid != 0 && d.j >= a.G)) {
+        // Not a record this call wrote (workspace not zero-filled before its
+        // first use): report the request instead of following it.
+        write_error(a, b, false);
+        if (arrive_last(ctr2, unsigned(a.nc2), sh) && threadIdx.x == 0) *flag = 0u;
+        return;
+    }
     const bool resid = d.resid != 0;
     const int G1 = a.G + 1;
     const void *zrow = static_cast<const char *>(a.logits) + (size_t(b) * G1 + d.row) * size_t(a.V) * ES;
@@ -668,7 +677,7 @@ __global__ __launch_bounds__(kWG) void k_verify_sampled(VerifyArgs a) {
             __syncthreads();
             if (threadIdx.x == 0) {
                 __threadfence();
-                __hip_atomic_store(ws_u32(a, a.lay.flag) + b, kFlagError, __ATOMIC_RELEASE,
+                __hip_atomic_store(slot(a, b) + 1, kFlagError, __ATOMIC_RELEASE,
                                    __HIP_MEMORY_SCOPE_AGENT);
             }
         }
@@ -683,7 +692,7 @@ __global__ __launch_bounds__(kWG) void k_verify_sampled(VerifyArgs a) {
     wg_reduce_ms(m, s, a.c32, sh);
     if (threadIdx.x == 0)
         reinterpret_cast<float2 *>(a.ws + a.lay.part)[(size_t(b) * G1 + k) * a.nc1 + c] = make_float2(m, s);
-    if (arrive_last(ws_u32(a, a.lay.ctr1) + b, unsigned((n + 1) * a.nc1), sh)) decide_sampled<ES>(a, b, n, sh);
+    if (arrive_last(slot(a, b) + 0, unsigned((n + 1) * a.nc1), sh)) decide_sampled<ES>(a, b, n, sh);
 }
 
 template <int ES, bool AL>
@@ -708,7 +717,7 @@ __global__ __launch_bounds__(kWG) void k_verify_greedy(VerifyArgs a) {
     if (threadIdx.x == 0)
         reinterpret_cast<int2 *>(a.ws + a.lay.part)[(size_t(b) * G1 + k) * a.nc1 + c] =
             make_int2(__float_as_int(best), nan ? kNanIdx : bi);
-    if (arrive_last(ws_u32(a, a.lay.ctr1) + b, unsigned((n + 1) * a.nc1), sh)) decide_greedy(a, b, n, sh);
+    if (arrive_last(slot(a, b) + 0, unsigned((n + 1) * a.nc1), sh)) decide_greedy(a, b, n, sh);
 }
 
 template <int ES, bool ALZ, bool ALQ>

@@ -44,8 +44,10 @@ def test_status_strings():
 
 def test_workspace_query():
     w = _capi.verify_workspace_bytes(64, 15, 129280, _capi.SPEC_DTYPE_BF16)
-    # counters 3*256 + partials 64*16*8 chunks*8 B + decisions + tile masses 64*16*16 B
-    assert w == 3 * 256 + 65536 + 2048 + 16384
+    # fixed 1 MiB counter region + partials 64*16*8 chunks*8 B + decisions + tile masses 64*16*16 B
+    assert w == (1 << 20) + 65536 + 2048 + 16384
+    # the counter region does not move with the shape
+    assert _capi.verify_workspace_bytes(1, 0, 1, _capi.SPEC_DTYPE_BF16) == (1 << 20) + 3 * 256
     assert _capi.verify_workspace_bytes(64, 15, 129280, _capi.SPEC_DTYPE_F32) >= w
     assert _capi.verify_workspace_bytes(0, 15, 100, 1) == 0
     assert _capi.verify_workspace_bytes(1, -1, 100, 1) == 0
@@ -64,7 +66,7 @@ def _verify(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype_code=5), 4),
     (dict(B=0), 2), (dict(G=-1), 2), (dict(V=0), 2),
-    (dict(G=256), 6), (dict(V=(1 << 30) + 1), 6),
+    (dict(G=256), 6), (dict(V=(1 << 30) + 1), 6), (dict(B=65537, V=10), 6),
     (dict(T=-0.5), 3), (dict(T=float("nan")), 3), (dict(T=float("inf")), 3), (dict(T=1e-39), 3),
     (dict(logits=0), 1), (dict(out_acc=0), 1), (dict(out_tok=0), 1), (dict(x=0), 1),
     (dict(q=0), 1), (dict(u=0), 1), (dict(ws=0), 1),

@@ -269,9 +269,12 @@ def test_data_errors():
     assert g["accepted"][7] >= 0
 
 
-def test_split_launch_path():
-    # Many requests: the draw pass runs as a second launch.
-    check(_rand_workload("split", 700, 1, 300, seed=10))
+def test_many_requests_fused_and_split_launch():
+    # 700 requests still fit one fused launch (all draw items after all row
+    # items); 1500 exceed half the resident capacity, so the draw pass runs as
+    # a second launch.
+    check(_rand_workload("many_fused", 700, 1, 300, seed=10))
+    check(_rand_workload("many_split", 1500, 1, 64, seed=13))
 
 
 def test_workspace_reuse_and_determinism():
@@ -292,5 +295,27 @@ def test_workspace_left_zero():
     sv.verify(z, q, x, u, 1.0, workspace=ws)
     sv.verify(z, None, x, None, 0.0, workspace=ws)
     torch.cuda.synchronize()
-    counters = ws[: 3 * 256].cpu().numpy()
+    counters = ws[: 1 << 20].cpu().numpy()
     assert not counters.any()
+
+
+def test_workspace_shared_across_shapes():
+    """One workspace for calls whose shapes (and so data layouts) differ.
+
+    Regression: the counters once sat at offsets that moved with B, so a larger
+    batch read an earlier call's partial sums as counters.  They now sit at
+    fixed offsets in a region no data ever occupies.
+    """
+    big = W.block(B=64, G=15, V=20000, seed=21)
+    wide = _rand_workload("wide", 700, 1, 300, seed=22)
+    need = max(sv.verify_workspace_bytes(64, 15, 20000), sv.verify_workspace_bytes(700, 1, 300))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for w in (big, wide, big, wide):
+        z, q, x, u, vl = to_device(w)
+        say(f"[parity] shared workspace {w['name']} B={w['B']}")
+        acc, tok = sv.verify(z, q, x, u, float(w["T"]), workspace=ws)
+        torch.cuda.synchronize()
+        o = run_oracle(w)
+        g = {"accepted": acc.cpu().numpy().astype(np.int64), "tokens": tok.cpu().numpy().astype(np.int64)}
+        compare(w, g, o, check_diag=False)
+    assert not ws[: 1 << 20].cpu().numpy().any()
