@@ -86,13 +86,13 @@ typedef struct {
  * Bytes of device workspace spec_verify needs for this shape (0 on invalid
  * arguments).  The same workspace serves every shape whose query is not larger.
  *
- * The workspace starts with a fixed 1 MiB region of per-request counters and
- * flags (the same offsets for every shape), followed by per-row partial
- * reductions, per-request decisions and per-tile masses.  It must be
- * zero-filled once before its first use (e.g. allocated with a zeroing
- * allocator); every completed call leaves the counter region zero again, so
- * one workspace can serve later calls of any shape without clearing.  Calls
- * that share one workspace must not overlap in time (use one per stream).
+ * The workspace holds a fixed 1 MiB region of per-request counters (the same
+ * offsets for every shape), the per-row chunk partials and the per-request
+ * sub-tile masses.  It must be zero-filled once before its first use (e.g.
+ * allocated with a zeroing allocator); every completed call leaves it
+ * zero-filled again, so one workspace can serve later calls of any shape
+ * without clearing.  Calls that share one workspace must not overlap in time
+ * (use one per stream).
  */
 size_t spec_verify_workspace_bytes(int32_t B, int32_t G, int32_t V, spec_dtype_t target_dtype);
 

@@ -30,8 +30,8 @@ spec_status_t check_verify_shape(int64_t B, int64_t G, int64_t V, int es) {
     if (B < 1 || G < 0 || V < 1) return SPEC_ERR_BAD_SHAPE;
     if (B > SPEC_MAX_BATCH || G > SPEC_MAX_DRAFTS || V > SPEC_MAX_VOCAB) return SPEC_ERR_UNSUPPORTED;
     const int64_t nc1 = (V + sv::chunk_elems(es) - 1) / sv::chunk_elems(es);
-    const int64_t ntiles = (V + sv::kTile - 1) / sv::kTile;
-    const int64_t items = B * ((G + 1) * nc1 + ntiles);
+    const int64_t nsub = (V + sv::kSub - 1) / sv::kSub;
+    const int64_t items = B * ((G + 1) * nc1 + nsub);
     if (items >= (int64_t(1) << 31)) return SPEC_ERR_UNSUPPORTED;
     if (B * (G + 1) > (int64_t(1) << 40) / V) return SPEC_ERR_UNSUPPORTED;
     return SPEC_OK;
@@ -40,13 +40,13 @@ spec_status_t check_verify_shape(int64_t B, int64_t G, int64_t V, int es) {
 struct DeviceInfo {
     bool ready = false;
     int cus = 0;
-    int occ[2][2][2] = {};   // [esize==2][aligned_z][aligned_q] blocks per CU, 0 = unknown
+    int occ[2][2][2][2] = {};   // [sampled][esize==2][aligned_z][aligned_q] blocks per CU, 0 = unknown
 };
 std::mutex g_mu;
 DeviceInfo g_dev[128];
 
-// Resident workgroups of the sampled kernel on this device; -1 on error.
-long resident_capacity(int dev, bool az, bool aq, int es) {
+// Resident workgroups of the verify kernel on this device; -1 on error.
+long resident_capacity(int dev, bool sampled, bool az, bool aq, int es) {
     if (dev < 0 || dev >= 128) return -1;
     std::lock_guard<std::mutex> lock(g_mu);
     DeviceInfo &d = g_dev[dev];
@@ -57,10 +57,10 @@ long resident_capacity(int dev, bool az, bool aq, int es) {
         d.cus = cus;
         d.ready = true;
     }
-    int &o = d.occ[es == 2][az][aq];
+    int &o = d.occ[sampled][es == 2][az][aq];
     if (o == 0) {
         int n = 0;
-        if (sv::verify_sampled_occupancy(az, aq, es, &n) != 0 || n <= 0) return -1;
+        if (sv::verify_occupancy(sampled, az, aq, es, &n) != 0 || n <= 0) return -1;
         o = n;
     }
     return long(o) * d.cus;
@@ -144,43 +144,42 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
     a.c32 = sampled ? float(1.4426950408889634 / double(T)) : 0.0f;
     a.ch1 = sv::chunk_elems(es);
     a.nc1 = (V + a.ch1 - 1) / a.ch1;
-    a.ntiles = (V + sv::kTile - 1) / sv::kTile;
-    a.spin_limit = 1u << 22;
+    a.nsub = (V + sv::kSub - 1) / sv::kSub;
+    a.spin_limit = 1u << 20;
     const bool az = aligned(target_logits, 16) && (size_t(V) * es) % 16 == 0;
     const bool aq = aligned(draft_probs, 16) && V % 4 == 0;
     const long g1 = long(G + 1) * a.nc1;
 
-    if (!sampled) {
-        const long grid = long(B) * g1;
-        return sv::launch_verify_greedy(a, az, es, int(grid), stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
-    }
-
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SPEC_ERR_DEVICE;
-    const long cap = resident_capacity(dev, az, aq, es);
+    const long cap = resident_capacity(dev, sampled, az, aq, es);
     if (cap <= 0) return SPEC_ERR_DEVICE;
-    // Draw workgroups that may wait must stay below half of the resident capacity.
+    // Request items wait for row items; there must stay fewer of them than half
+    // of the resident capacity for one launch, else two launches.
     const long half = cap / 2;
-    long nc2 = half / B;
-    if (nc2 < 1) nc2 = 1;
-    if (nc2 > a.ntiles) nc2 = a.ntiles;
-    a.tpw = int((a.ntiles + nc2 - 1) / nc2);
-    a.nc2 = (a.ntiles + a.tpw - 1) / a.tpw;
-    const bool fused = long(B) * a.nc2 <= half;
-    if (fused) {
-        long lag = (cap + g1 - 1) / g1 + 1;
-        if (lag > B) lag = B;
-        a.lag = int(lag);
-        a.mode = 0;
-        const long grid = long(B) * (g1 + a.nc2);
-        return sv::launch_verify_sampled(a, az, aq, es, int(grid), stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+    if (sampled) {
+        long nc2 = half / B;
+        if (nc2 < 1) nc2 = 1;
+        if (nc2 > a.nsub) nc2 = a.nsub;
+        a.spw = int((a.nsub + nc2 - 1) / nc2);
+        a.spw = (a.spw + sv::kSubBatch - 1) / sv::kSubBatch * sv::kSubBatch;   // whole batches
+        a.nc2 = (a.nsub + a.spw - 1) / a.spw;
+    } else {
+        a.nc2 = 1;
+        a.spw = 0;
     }
-    a.lag = B;
+    auto launch = [&](long grid) {
+        return sampled ? sv::launch_verify_sampled(a, az, aq, es, int(grid), stream)
+                       : sv::launch_verify_greedy(a, az, es, int(grid), stream);
+    };
+    if (long(B) * a.nc2 <= half) {
+        a.mode = 0;
+        return launch(long(B) * (g1 + a.nc2)) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+    }
     a.mode = 1;
-    if (sv::launch_verify_sampled(a, az, aq, es, int(long(B) * g1), stream) != 0) return SPEC_ERR_DEVICE;
+    if (launch(long(B) * g1) != 0) return SPEC_ERR_DEVICE;
     a.mode = 2;
-    return sv::launch_verify_sampled(a, az, aq, es, int(long(B) * a.nc2), stream) == 0 ? SPEC_OK
-                                                                                       : SPEC_ERR_DEVICE;
+    return launch(long(B) * a.nc2) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
 }
 
 size_t spec_schedule_workspace_bytes(int32_t, int32_t) { return 0; }

@@ -9,30 +9,32 @@ namespace sv {
 
 constexpr int kWG = 256;            // threads per workgroup: 4 wave64s
 constexpr int kVecPerThread = 8;    // 16-byte loads in flight per thread in the row pass
-constexpr int kRun = 32;            // contiguous elements per thread in the final-draw pass
-constexpr int kTile = kWG * kRun;   // elements per final-draw tile (8192)
+constexpr int kSubPerThread = 8;    // contiguous elements per thread in a draw sub-tile
+constexpr int kSub = kWG * kSubPerThread;   // elements per draw sub-tile (2048)
+constexpr int kSubBatch = 2;        // sub-tiles loaded together by a draw workgroup
+constexpr int kStage = 256;         // sub-tile masses staged in LDS at a time
 constexpr int kNanIdx = -2;         // greedy partial: chunk holds a NaN
-
-constexpr unsigned kFlagReady = 1;  // decision record valid
-constexpr unsigned kFlagError = 2;  // request has a data error; outputs already written
 
 // Elements per row-pass chunk: 256 threads x 8 loads x 16 bytes.
 inline int chunk_elems(int esize) { return kWG * kVecPerThread * (16 / esize); }
 
-// Workspace layout.  The first kCounterBytes hold one 16-byte slot of
-// counters per request, {row-pass arrivals, decision flag, draw-pass
-// arrivals, unused}, at the same offsets for every shape: these must start at
-// zero and every completed call leaves them at zero, so one zero-filled
-// workspace stays valid across calls of any shape.  Everything after them is
-// written before it is read within a call.
+// Workspace.  Between calls every byte the kernels use is zero: each slot is
+// reset by the last workgroup that reads it, so one zero-filled workspace stays
+// valid across calls of any shape.
+//   counters [kMaxBatch] 16-byte slots at fixed offsets: word 2 counts the
+//            request's draw workgroups;
+//   part     [B*(G+1)*nc1] u64 chunk partials, bit 63 set once written
+//            (sampled: low = max bits, high = sum bits | 1<<31;
+//             greedy:  low = max bits, high = (argmax + 2) | 1<<31);
+//   mass     [B*nsub] 2 u64: fp64 (residual mass, target mass) per sub-tile.
 constexpr int kMaxBatch = 65536;
 constexpr size_t kSlotBytes = 16;
 constexpr size_t kCounterBytes = size_t(kMaxBatch) * kSlotBytes;
+constexpr uint32_t kValid = 0x80000000u;
 
 struct Layout {
-    size_t part;               // [B*(G+1)*nc1] 8 bytes: (max, sum) or (max, argmax)
-    size_t dec;                // [B] Decision
-    size_t mass;               // [B*ntiles] 2 doubles: (residual mass, target mass) per tile
+    size_t part;
+    size_t mass;
     size_t total;
 };
 
@@ -40,28 +42,14 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline Layout make_layout(int64_t B, int64_t G, int64_t V, int esize) {
     const int64_t nc1 = (V + chunk_elems(esize) - 1) / chunk_elems(esize);
-    const int64_t ntiles = (V + kTile - 1) / kTile;
+    const int64_t nsub = (V + kSub - 1) / kSub;
     Layout L;
     size_t o = kCounterBytes;
     L.part = o; o += align256(size_t(B) * size_t(G + 1) * size_t(nc1) * 8);
-    L.dec = o;  o += align256(size_t(B) * 32);
-    L.mass = o; o += align256(size_t(B) * size_t(ntiles) * 16);
+    L.mass = o; o += align256(size_t(B) * size_t(nsub) * 16);
     L.total = o;
     return L;
 }
-
-// Per-request decision written by the workgroup that finishes the request's
-// row pass, read by the final-draw workgroups.
-struct Decision {
-    int32_t j;        // accepted drafts
-    int32_t row;      // target row of the final draw: always j (j = len when all accepted)
-    int32_t resid;    // 1: draw from max(p_j - q_j, 0); 0: draw from p_row
-    int32_t pad;
-    float m;          // row maximum (logit units)
-    float inv_s;      // 1 / S of that row, fp32
-    double s;         // S of that row, fp64
-};
-static_assert(sizeof(Decision) == 32, "Decision is 32 bytes");
 
 struct VerifyArgs {
     const void *logits;
@@ -76,12 +64,11 @@ struct VerifyArgs {
     Layout lay;
     int32_t B, G, V;
     float T;          // temperature
-    float c32;        // log2(e) / T, the fp32 exponent scale of the row pass
+    float c32;        // log2(e) / T, the fp32 exponent scale
     int32_t nc1, ch1; // row-pass chunks per row, elements per chunk
-    int32_t ntiles;   // final-draw tiles per row
-    int32_t nc2, tpw; // final-draw workgroups per request, tiles per workgroup
-    int32_t lag;      // requests between a request's row pass and its draw items
-    int32_t mode;     // 0: one fused launch; 1: row pass only; 2: draw pass only
+    int32_t nsub;     // draw sub-tiles per row
+    int32_t nc2, spw; // draw workgroups per request, sub-tiles per workgroup
+    int32_t mode;     // 0: one launch (row items, then request items); 1: row items only; 2: request items only
     uint32_t spin_limit;
 };
 
@@ -89,7 +76,7 @@ struct VerifyArgs {
 int launch_verify_sampled(const VerifyArgs &a, bool aligned_z, bool aligned_q, int esize,
                           int grid, void *stream);
 int launch_verify_greedy(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
-int verify_sampled_occupancy(bool aligned_z, bool aligned_q, int esize, int *blocks_per_cu);
+int verify_occupancy(bool sampled, bool aligned_z, bool aligned_q, int esize, int *blocks_per_cu);
 
 struct ScheduleArgs {
     const float *conf;

@@ -12,34 +12,35 @@
 // How it maps to the chip
 // -----------------------
 // The work is a bandwidth-bound streaming reduction (no contraction, so no
-// MFMA).  One launch handles the whole batch:
+// MFMA).  One launch handles the whole batch, in two kinds of workgroup:
 //
-//   row-pass items   one workgroup per (request, row, chunk of the vocabulary):
-//                    8 x 16-byte loads in flight per thread, held in registers,
-//                    chunk maximum, then sum of 2^((z - m) * log2(e)/T); wave
-//                    butterflies and LDS merge (max, sum) pairs.  The
-//                    workgroup that finishes a request's last chunk (arrival
-//                    counter) merges that request's chunk partials in fp64,
-//                    runs the accept tests and the first-reject scan, writes
-//                    the accepted prefix, and publishes a decision record.
-//   draw items       a few workgroups per request, placed in the grid `lag`
-//                    requests behind the request's row-pass items, wait for its
-//                    decision, stream the one row the final token is drawn from
-//                    (target row, plus the draft row on a rejection) in tiles of
-//                    8192, and write per-tile masses; the last one to arrive
-//                    locates the tile holding u * R by an fp64 prefix over tiles
-//                    and re-scans only that tile to find the token.
+//   row items      one per (request, row, 16384-element chunk): 8 x 16-byte
+//                  loads in flight per thread, the chunk maximum, then the sum
+//                  of 2^((z - m) * log2(e)/T), merged across the workgroup by
+//                  wave butterflies and LDS.  The (max, sum) partial goes out as
+//                  one coherent 64-bit store tagged valid; the workgroup then
+//                  exits.  No counters, no waits.
+//   request items  nc2 per request, placed after every row item in the grid.
+//                  Each polls its request's chunk partials until all are valid,
+//                  merges them per row in fp64, runs the accept tests (the
+//                  draft-token gathers were issued before the poll) and finds
+//                  the first rejection; then streams its share of the one row
+//                  the final token is drawn from (target row, plus the draft row
+//                  on a rejection) in sub-tiles of 2048, writing fp64 sub-tile
+//                  masses.  The last of the request's nc2 workgroups to arrive
+//                  locates u * R by a prefix over sub-tile masses, re-scans that
+//                  one sub-tile, writes the token, and zeroes every workspace
+//                  word the request used.
 //
-// The draw items of request b only wait for row-pass items that precede them
-// in the grid, and the host keeps the number of draw workgroups below half the
-// device's resident capacity, so the waits always end (they are also bounded).
-// When that bound cannot be met the host uses two launches (row pass, then
-// draw pass) instead.  All counters are reset by their last user, so a zeroed
-// workspace stays zeroed after every call.
+// Request items only wait for row items, which precede them in the grid and
+// never wait, and the host keeps the request items below half the device's
+// resident capacity (else it launches the two kinds separately), so every
+// wait ends; the waits are also bounded.
 //
-// Determinism: no floating-point atomics; reductions run in a fixed order;
-// the per-tile masses and the re-scan use the same code, so the tile the draw
-// lands in is found exactly.  The library is compiled with -ffp-contract=off.
+// Determinism: no floating-point atomics; every reduction has a fixed order;
+// the sub-tile masses and the final re-scan run the same code, so the sub-tile
+// the draw lands in is found exactly.  The library is compiled with
+// -ffp-contract=off.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -54,7 +55,7 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 // Native 2^x (v_exp_f32).  Arguments here are <= 0; results below the fp32
-// normal range flush to zero, which is far below every tolerance.
+// normal range flush to zero, far below every tolerance.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int ES>
@@ -66,18 +67,43 @@ __device__ __forceinline__ float load_elem(const void *base, size_t i) {
     }
 }
 
+// ------------------------------------------------ cross-workgroup publication
+//
+// Words one workgroup hands to another are written with coherent device-scope
+// stores and read with coherent device-scope loads (no whole-cache write-back
+// or invalidation, which a generic device-scope fence performs on every L2).
+// A chunk partial carries its own valid bit, so it needs no ordering at all.
+// Sub-tile masses are ordered before the arrival that publishes them by
+// waiting for the stores to complete.
+__device__ __forceinline__ void st_coherent(void *p, uint64_t v) {
+    __hip_atomic_store(static_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_coherent(const void *p) {
+    return __hip_atomic_load(static_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stores_complete() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);          // vmcnt = expcnt = lgkmcnt = 0
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float(uint32_t(v)); }
+__device__ __forceinline__ uint32_t hi_u(uint64_t v) { return uint32_t(v >> 32); }
+__device__ __forceinline__ bool valid(uint64_t v) { return (hi_u(v) & kValid) != 0u; }
+
 struct __align__(16) Smem {
     union {
-        float ms[8];                      // (max, sum) per wave
+        float ms[8];                              // (max, sum) per wave
         struct { float v[4]; int i[4]; int nan[4]; } am;   // argmax per wave
-        double sc[8];                     // scan totals per wave
+        double sc[4][2 * kSubBatch];              // scan totals per wave
     } r;
-    double S[kWG];                        // fp64 row sums (decision)
-    float M[kWG];                         // row maxima (decision)
-    int A[kWG];                           // greedy row argmax (decision)
-    int jmin, bad, last, flag;
-    double base, target, total, R;
-    int tstar, mode, t1, y;
+    double S[kWG];                                // fp64 row sums
+    float M[kWG];                                 // row maxima
+    int A[kWG];                                   // greedy row argmax
+    double mr[kStage], mp[kStage];                // staged sub-tile masses
+    double tot[2 * kSubBatch];
+    int jmin, bad, last;
+    int sstar, mode, t1, y;
+    double base, target, R;
 };
 
 // ---------------------------------------------------------------- reductions
@@ -131,48 +157,70 @@ __device__ void wg_reduce_am(float &v, int &i, int &nan, Smem &sh) {
     }
 }
 
-// Exclusive prefix over the 256 threads in fp64, fixed association.
-// Returns the exclusive prefix; `total` = inclusive prefix of the last thread,
-// computed as (its exclusive prefix + its value), the same way every caller's
-// inclusive value is formed.
-__device__ double wg_excl_scan(double v, double &total, Smem &sh) {
+// Exclusive prefix over the 256 threads of NS fp64 values at once.  Each value
+// goes through the same fixed sequence of additions whatever NS is.  Writes
+// the exclusive prefix to excl[]; the inclusive prefix of a thread is defined
+// as excl + v, and total[] is that of the last thread.
+template <int NS>
+__device__ void wg_excl_scan(const double (&v)[NS], double (&excl)[NS], double (&total)[NS], Smem &sh) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    double x = v;
+    double x[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) x[i] = v[i];
     for (int d = 1; d < 64; d <<= 1) {
-        const double y = __shfl_up(x, d);
-        if (lane >= d) x = x + y;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const double y = __shfl_up(x[i], d);
+            if (lane >= d) x[i] = x[i] + y;
+        }
     }
-    double xprev = __shfl_up(x, 1);
-    if (lane == 0) xprev = 0.0;
+    double xprev[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) xprev[i] = __shfl_up(x[i], 1);
     __syncthreads();
-    if (lane == 63) sh.r.sc[w] = x;
+    if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) sh.r.sc[w][i] = x[i];
+    }
     __syncthreads();
-    double wbase = 0.0;
-    for (int i = 0; i < w; ++i) wbase = wbase + sh.r.sc[i];
-    const double excl = (lane == 0) ? wbase : wbase + xprev;
-    if (threadIdx.x == kWG - 1) sh.total = excl + v;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        double wbase = 0.0;
+        for (int k = 0; k < w; ++k) wbase = wbase + sh.r.sc[k][i];
+        excl[i] = (lane == 0) ? wbase : wbase + xprev[i];
+        if (threadIdx.x == kWG - 1) sh.tot[i] = excl[i] + v[i];
+    }
     __syncthreads();
-    total = sh.total;
-    return excl;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) total[i] = sh.tot[i];
 }
 
 // ------------------------------------------------------------- arrivals
 
+// Every thread's published stores complete, then one counted arrival.
 // Returns true in every thread of the workgroup that arrives last; that
-// workgroup resets the counter and acquires the other workgroups' writes.
+// workgroup resets the counter.
 __device__ bool arrive_last(unsigned *ctr, unsigned target, Smem &sh) {
+    stores_complete();
     __syncthreads();
     if (threadIdx.x == 0) {
-        __threadfence();
-        const unsigned old = atomicAdd(ctr, 1u);
+        const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int last = (old + 1 == target);
-        if (last) *ctr = 0u;
+        if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sh.last = last;
     }
     __syncthreads();
-    const bool last = sh.last != 0;
-    if (last) __threadfence();
-    return last;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    return sh.last != 0;
+}
+
+// Draw-workgroup counter of request b (fixed offset for every shape).
+__device__ __forceinline__ unsigned *draw_counter(const VerifyArgs &a, int b) {
+    return reinterpret_cast<unsigned *>(a.ws + size_t(b) * kSlotBytes) + 2;
+}
+
+__device__ __forceinline__ uint64_t *partials(const VerifyArgs &a, int b) {
+    return reinterpret_cast<uint64_t *>(a.ws + a.lay.part) + size_t(b) * (a.G + 1) * a.nc1;
 }
 
 __device__ void write_error(const VerifyArgs &a, int b, bool diag) {
@@ -191,13 +239,32 @@ __device__ void write_error(const VerifyArgs &a, int b, bool diag) {
     if (threadIdx.x == 0 && a.d_r) a.d_r[b] = qnan;
 }
 
-// Per-request counter slot at a fixed offset: [0] row-pass arrivals,
-// [1] decision flag, [2] draw-pass arrivals.
-__device__ __forceinline__ unsigned *slot(const VerifyArgs &a, int b) {
-    return reinterpret_cast<unsigned *>(a.ws + size_t(b) * kSlotBytes);
+// Zero the request's chunk partials (rows 0..n) and sub-tile masses.
+__device__ void reset_request(const VerifyArgs &a, int b, int n, bool masses) {
+    uint64_t *part = partials(a, b);
+    const int np = (n + 1) * a.nc1;
+    for (int i = threadIdx.x; i < np; i += kWG) st_coherent(part + i, 0ull);
+    if (masses) {
+        uint64_t *mass = reinterpret_cast<uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
+        for (int i = threadIdx.x; i < 2 * a.nsub; i += kWG) st_coherent(mass + i, 0ull);
+    }
 }
 
-// ------------------------------------------------------------- row pass
+// Wait until the chunk partials of rows 0..n are all written.  False if the
+// bounded wait expired.
+__device__ bool wait_partials(const VerifyArgs &a, int b, int n) {
+    const uint64_t *part = partials(a, b);
+    const int np = (n + 1) * a.nc1;
+    for (uint32_t spins = 0;; ++spins) {
+        bool ready = true;
+        for (int i = threadIdx.x; i < np; i += kWG) ready = ready && valid(ld_coherent(part + i));
+        if (__syncthreads_and(ready)) return true;
+        if (spins >= a.spin_limit) return false;
+        __builtin_amdgcn_s_sleep(4);
+    }
+}
+
+// ------------------------------------------------------------- row items
 
 // (max, sum of 2^((z-max)*c)) over elements [beg, end) of one row, per thread.
 template <int ES, bool AL>
@@ -316,260 +383,294 @@ __device__ void chunk_argmax(const void *row, int beg, int end, float &best, int
     }
 }
 
-// ---------------------------------------------------------- decisions
+__device__ __forceinline__ int verify_len(const VerifyArgs &a, int b) { return a.vlen ? a.vlen[b] : a.G; }
 
-// Workgroup that completed request b's row pass (T > 0).
+template <int ES, bool AL>
+__device__ void row_item_sampled(const VerifyArgs &a, int b, int local, Smem &sh) {
+    const int k = local / a.nc1, c = local - k * a.nc1;
+    const int n = verify_len(a, b);
+    if (n < 0 || n > a.G || k > n) return;
+    const void *row = static_cast<const char *>(a.logits) + (size_t(b) * (a.G + 1) + k) * size_t(a.V) * ES;
+    const int beg = c * a.ch1, end = min(a.V, beg + a.ch1);
+    float m, s;
+    chunk_ms<ES, AL>(row, beg, end, a.c32, m, s);
+    wg_reduce_ms(m, s, a.c32, sh);
+    if (threadIdx.x == 0)
+        st_coherent(partials(a, b) + size_t(k) * a.nc1 + c,
+                    uint64_t(__float_as_uint(m)) | (uint64_t(__float_as_uint(s) | kValid) << 32));
+}
+
+template <int ES, bool AL>
+__device__ void row_item_greedy(const VerifyArgs &a, int b, int local, Smem &sh) {
+    const int k = local / a.nc1, c = local - k * a.nc1;
+    const int n = verify_len(a, b);
+    if (n < 0 || n > a.G || k > n) return;
+    const void *row = static_cast<const char *>(a.logits) + (size_t(b) * (a.G + 1) + k) * size_t(a.V) * ES;
+    const int beg = c * a.ch1, end = min(a.V, beg + a.ch1);
+    float best;
+    int bi, nan;
+    chunk_argmax<ES, AL>(row, beg, end, best, bi, nan);
+    wg_reduce_am(best, bi, nan, sh);
+    if (threadIdx.x == 0)
+        st_coherent(partials(a, b) + size_t(k) * a.nc1 + c,
+                    uint64_t(__float_as_uint(best)) | (uint64_t(uint32_t((nan ? kNanIdx : bi) + 2) | kValid) << 32));
+}
+
+// ---------------------------------------------------------- draw sub-tiles
+
+__device__ __forceinline__ void draw_term(float z, float q, float m, float c, float inv_s, bool resid,
+                                          float &r, float &p) {
+    const float e = exp2_fast((z - m) * c);
+    p = e * inv_s;
+    r = resid ? fmaxf(p - q, 0.0f) : p;
+}
+
+// One thread's 8 contiguous elements of sub-tile `sub` of a draw row: the
+// residual (or target) mass `rs` and the target mass `ps`, fp64 in index order.
+template <int ES, bool ALZ, bool ALQ>
+__device__ void sub_sums(const void *zrow, const float *qrow, int V, int sub, float m, float c, float inv_s,
+                         bool resid, double &rs, double &ps) {
+    rs = 0.0; ps = 0.0;
+    const int e0 = sub * kSub + int(threadIdx.x) * kSubPerThread;
+    if (e0 >= V) return;
+    float z[kSubPerThread], q[kSubPerThread];
+    if (ALZ && (!resid || ALQ) && e0 + kSubPerThread <= V) {
+        const uint4 *zp = reinterpret_cast<const uint4 *>(static_cast<const char *>(zrow) + size_t(e0) * ES);
+        if constexpr (ES == 2) {
+            const uint4 w = zp[0];
+            z[0] = bf16_lo(w.x); z[1] = bf16_hi(w.x); z[2] = bf16_lo(w.y); z[3] = bf16_hi(w.y);
+            z[4] = bf16_lo(w.z); z[5] = bf16_hi(w.z); z[6] = bf16_lo(w.w); z[7] = bf16_hi(w.w);
+        } else {
+            const uint4 w0 = zp[0], w1 = zp[1];
+            z[0] = __uint_as_float(w0.x); z[1] = __uint_as_float(w0.y);
+            z[2] = __uint_as_float(w0.z); z[3] = __uint_as_float(w0.w);
+            z[4] = __uint_as_float(w1.x); z[5] = __uint_as_float(w1.y);
+            z[6] = __uint_as_float(w1.z); z[7] = __uint_as_float(w1.w);
+        }
+        if (resid) {
+            const uint4 *qp = reinterpret_cast<const uint4 *>(qrow + e0);
+            const uint4 w0 = qp[0], w1 = qp[1];
+            q[0] = __uint_as_float(w0.x); q[1] = __uint_as_float(w0.y);
+            q[2] = __uint_as_float(w0.z); q[3] = __uint_as_float(w0.w);
+            q[4] = __uint_as_float(w1.x); q[5] = __uint_as_float(w1.y);
+            q[6] = __uint_as_float(w1.z); q[7] = __uint_as_float(w1.w);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kSubPerThread; ++i) q[i] = 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < kSubPerThread; ++i) {
+            float r, p;
+            draw_term(z[i], q[i], m, c, inv_s, resid, r, p);
+            rs = rs + double(r);
+            ps = ps + double(p);
+        }
+    } else {
+        const int e1 = min(V, e0 + kSubPerThread);
+        for (int e = e0; e < e1; ++e) {
+            float r, p;
+            const float qv = resid ? qrow[e] : 0.0f;
+            draw_term(load_elem<ES>(zrow, size_t(e)), qv, m, c, inv_s, resid, r, p);
+            rs = rs + double(r);
+            ps = ps + double(p);
+        }
+    }
+}
+
+// ------------------------------------------------------------- request items
+
+// Per-request decision, computed identically by each of the request's workgroups.
+struct Decision {
+    int n, j;
+    bool resid;
+    float m, inv_s;
+};
+
+// Poll and merge the request's rows, run the accept tests.  Returns false
+// (outputs already reported) on a data error or an expired wait.
 template <int ES>
-__device__ void decide_sampled(const VerifyArgs &a, int b, int n, Smem &sh) {
-    const int G1 = a.G + 1;
-    const float2 *part = reinterpret_cast<const float2 *>(a.ws + a.lay.part) + size_t(b) * G1 * a.nc1;
+__device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, Smem &sh) {
+    const int G = a.G, G1 = G + 1;
+    const bool diag = a.d_lse || a.d_p || a.d_q || a.d_r;
+    const int n = verify_len(a, b);
+    d.n = n;
+    if (n < 0 || n > G) {
+        if (w == 0) write_error(a, b, diag);
+        return false;
+    }
+    // Gathers of the drafted positions do not depend on the row pass: issue first.
+    const int k = threadIdx.x;
+    int xk = 0;
+    float zx = 0.0f, qx = 0.0f, uk = 0.0f;
+    bool xbad = false;
+    if (k < n) {
+        xk = a.x[size_t(b) * G + k];
+        xbad = xk < 0 || xk >= a.V;
+        if (!xbad) {
+            zx = load_elem<ES>(a.logits, (size_t(b) * G1 + k) * size_t(a.V) + size_t(xk));
+            qx = a.q[(size_t(b) * G + k) * size_t(a.V) + size_t(xk)];
+        }
+        uk = a.u[size_t(b) * G1 + k];
+    }
+    if (threadIdx.x == 0) { sh.jmin = n; sh.bad = 0; }
+    if (!wait_partials(a, b, n)) {
+        if (w == 0) write_error(a, b, diag);
+        return false;
+    }
+    // Merge each row's chunk partials in fp64 (thread r owns row r).
     const double c64 = double(a.c32);
     const double T64 = double(a.T);
-    if (threadIdx.x == 0) { sh.jmin = n; sh.bad = 0; }
-    __syncthreads();
+    const uint64_t *part = partials(a, b);
     for (int r = threadIdx.x; r <= n; r += kWG) {
-        const float2 *pp = part + size_t(r) * a.nc1;
+        const uint64_t *pp = part + size_t(r) * a.nc1;
         float M = neg_inf();
-        for (int c = 0; c < a.nc1; ++c) M = fmaxf(M, pp[c].x);
+        for (int c = 0; c < a.nc1; ++c) M = fmaxf(M, lo_f(ld_coherent(pp + c)));
         double S = 0.0;
         for (int c = 0; c < a.nc1; ++c) {
-            const float2 v = pp[c];
-            if (v.x == neg_inf() && v.y == 0.0f) continue;          // empty chunk
-            S = S + double(v.y) * exp2((double(v.x) - double(M)) * c64);
+            const uint64_t v = ld_coherent(pp + c);
+            const float vm = lo_f(v), vs = __uint_as_float(hi_u(v) & ~kValid);
+            if (vm == neg_inf() && vs == 0.0f) continue;            // empty chunk
+            S = S + double(vs) * exp2((double(vm) - double(M)) * c64);
         }
-        const bool bad = !(S > 0.0 && S < INFINITY) || !(M > neg_inf() && M < INFINITY);
-        if (bad) atomicOr(&sh.bad, 1);
+        if (!(S > 0.0 && S < INFINITY) || !(M > neg_inf() && M < INFINITY)) atomicOr(&sh.bad, 1);
         sh.M[r] = M;
         sh.S[r] = S;
     }
     __syncthreads();
-    for (int k = threadIdx.x; k < n; k += kWG) {
-        const int xk = a.x[size_t(b) * a.G + k];
-        if (xk < 0 || xk >= a.V) { atomicOr(&sh.bad, 1); continue; }
-        const float zx = load_elem<ES>(a.logits, (size_t(b) * G1 + k) * size_t(a.V) + size_t(xk));
-        const float qx = a.q[(size_t(b) * a.G + k) * size_t(a.V) + size_t(xk)];
-        const double u = double(a.u[size_t(b) * G1 + k]);
-        const double p = exp((double(zx) - double(sh.M[k])) / T64) / sh.S[k];
-        const bool acc = (qx > 0.0f) ? (u < p / double(qx)) : (p > 0.0);
-        if (!acc) atomicMin(&sh.jmin, k);
-        if (a.d_p) a.d_p[size_t(b) * a.G + k] = float(p);
-        if (a.d_q) a.d_q[size_t(b) * a.G + k] = qx;
+    if (k < n) {
+        if (xbad) {
+            atomicOr(&sh.bad, 1);
+        } else {
+            const double p = exp((double(zx) - double(sh.M[k])) / T64) / sh.S[k];
+            const bool acc = (qx > 0.0f) ? (double(uk) < p / double(qx)) : (p > 0.0);
+            if (!acc) atomicMin(&sh.jmin, k);
+            if (w == 0) {
+                if (a.d_p) a.d_p[size_t(b) * G + k] = float(p);
+                if (a.d_q) a.d_q[size_t(b) * G + k] = qx;
+            }
+        }
     }
     __syncthreads();
-    unsigned *flag = slot(a, b) + 1;
-    const bool diag = a.d_lse || a.d_p || a.d_q || a.d_r;
     if (sh.bad) {
-        write_error(a, b, diag);
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            __threadfence();
-            __hip_atomic_store(flag, kFlagError, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        return;
+        if (w == 0) write_error(a, b, diag);
+        return false;
     }
     const int j = sh.jmin;
-    const float qnan = __builtin_nanf("");
-    for (int t = threadIdx.x; t < G1; t += kWG) {
-        if (t < j) a.out_tok[size_t(b) * G1 + t] = a.x[size_t(b) * a.G + t];
-        else if (t > j) a.out_tok[size_t(b) * G1 + t] = -1;
-        if (a.d_lse) a.d_lse[size_t(b) * G1 + t] = (t <= n) ? float(double(sh.M[t]) / T64 + log(sh.S[t])) : qnan;
-        if (t >= n && t < a.G) {
-            if (a.d_p) a.d_p[size_t(b) * a.G + t] = qnan;
-            if (a.d_q) a.d_q[size_t(b) * a.G + t] = qnan;
-        }
-    }
-    if (threadIdx.x == 0) {
-        a.out_acc[b] = j;
-        const int row = (j < n) ? j : n;
-        Decision d;
-        d.j = j;
-        d.row = row;
-        d.resid = (j < n) ? 1 : 0;
-        d.pad = 0;
-        d.m = sh.M[row];
-        d.s = sh.S[row];
-        d.inv_s = float(1.0 / sh.S[row]);
-        reinterpret_cast<Decision *>(a.ws + a.lay.dec)[b] = d;
-        __threadfence();
-        __hip_atomic_store(flag, kFlagReady, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    }
-}
-
-// Workgroup that completed request b's row pass (T == 0).
-__device__ void decide_greedy(const VerifyArgs &a, int b, int n, Smem &sh) {
-    const int G1 = a.G + 1;
-    const int2 *part = reinterpret_cast<const int2 *>(a.ws + a.lay.part) + size_t(b) * G1 * a.nc1;
-    if (threadIdx.x == 0) { sh.jmin = n; sh.bad = 0; }
-    __syncthreads();
-    for (int r = threadIdx.x; r <= n; r += kWG) {
-        const int2 *pp = part + size_t(r) * a.nc1;
-        float best = neg_inf();
-        int bi = -1, nan = 0;
-        for (int c = 0; c < a.nc1; ++c) {               // ascending chunks: first maximum wins
-            const int2 v = pp[c];
-            if (v.y == kNanIdx) { nan = 1; continue; }
-            merge_am(best, bi, __int_as_float(v.x), v.y);
-        }
-        if (nan || bi < 0 || best == __builtin_inff()) atomicOr(&sh.bad, 1);
-        sh.A[r] = bi;
-    }
-    __syncthreads();
-    for (int k = threadIdx.x; k < n; k += kWG) {
-        const int xk = a.x[size_t(b) * a.G + k];
-        if (xk < 0 || xk >= a.V) { atomicOr(&sh.bad, 1); continue; }
-        if (xk != sh.A[k]) atomicMin(&sh.jmin, k);
-    }
-    __syncthreads();
-    if (sh.bad) { write_error(a, b, false); return; }
-    const int j = sh.jmin;
-    for (int t = threadIdx.x; t < G1; t += kWG) {
-        int v = -1;
-        if (t < j) v = a.x[size_t(b) * a.G + t];
-        else if (t == j) v = sh.A[j];
-        a.out_tok[size_t(b) * G1 + t] = v;
-    }
-    if (threadIdx.x == 0) a.out_acc[b] = j;
-}
-
-// ---------------------------------------------------------- final draw
-
-__device__ __forceinline__ void draw_term(float z, float q, const Decision &d, float c, bool resid,
-                                          float &r, float &p) {
-    const float e = exp2_fast((z - d.m) * c);
-    p = e * d.inv_s;
-    r = resid ? fmaxf(p - q, 0.0f) : p;
-}
-
-// Sums over one thread's run [e0, e0 + kRun) of a draw row: residual (or
-// target) mass `rs` and target mass `ps`, accumulated in fp64 in index order.
-template <int ES, bool ALZ, bool ALQ>
-__device__ void run_sums(const void *zrow, const float *qrow, int V, int e0, const Decision &d,
-                         float c, bool resid, double &rs, double &ps) {
-    rs = 0.0; ps = 0.0;
-    if (e0 >= V) return;
-    const bool vec = ALZ && (!resid || ALQ) && (e0 + kRun <= V);
-    if (vec) {
-        float z[kRun], q[kRun];
-        const uint4 *zp = reinterpret_cast<const uint4 *>(static_cast<const char *>(zrow) + size_t(e0) * ES);
-        if constexpr (ES == 2) {
-#pragma unroll
-            for (int i = 0; i < kRun / 8; ++i) {
-                const uint4 w = zp[i];
-                z[8 * i + 0] = bf16_lo(w.x); z[8 * i + 1] = bf16_hi(w.x);
-                z[8 * i + 2] = bf16_lo(w.y); z[8 * i + 3] = bf16_hi(w.y);
-                z[8 * i + 4] = bf16_lo(w.z); z[8 * i + 5] = bf16_hi(w.z);
-                z[8 * i + 6] = bf16_lo(w.w); z[8 * i + 7] = bf16_hi(w.w);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < kRun / 4; ++i) {
-                const uint4 w = zp[i];
-                z[4 * i + 0] = __uint_as_float(w.x); z[4 * i + 1] = __uint_as_float(w.y);
-                z[4 * i + 2] = __uint_as_float(w.z); z[4 * i + 3] = __uint_as_float(w.w);
+    d.j = j;
+    d.resid = j < n;
+    d.m = sh.M[j];
+    d.inv_s = float(1.0 / sh.S[j]);
+    if (w == 0) {
+        const float qnan = __builtin_nanf("");
+        for (int t = threadIdx.x; t < G1; t += kWG) {
+            if (t < j) a.out_tok[size_t(b) * G1 + t] = a.x[size_t(b) * G + t];
+            else if (t > j) a.out_tok[size_t(b) * G1 + t] = -1;
+            if (a.d_lse) a.d_lse[size_t(b) * G1 + t] = (t <= n) ? float(double(sh.M[t]) / T64 + log(sh.S[t])) : qnan;
+            if (t >= n && t < G) {
+                if (a.d_p) a.d_p[size_t(b) * G + t] = qnan;
+                if (a.d_q) a.d_q[size_t(b) * G + t] = qnan;
             }
         }
-        if (resid) {
-            const uint4 *qp = reinterpret_cast<const uint4 *>(qrow + e0);
-#pragma unroll
-            for (int i = 0; i < kRun / 4; ++i) {
-                const uint4 w = qp[i];
-                q[4 * i + 0] = __uint_as_float(w.x); q[4 * i + 1] = __uint_as_float(w.y);
-                q[4 * i + 2] = __uint_as_float(w.z); q[4 * i + 3] = __uint_as_float(w.w);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < kRun; ++i) q[i] = 0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < kRun; ++i) {
-            float r, p;
-            draw_term(z[i], q[i], d, c, resid, r, p);
-            rs = rs + double(r);
-            ps = ps + double(p);
-        }
-    } else {
-        const int e1 = min(V, e0 + kRun);
-        for (int e = e0; e < e1; ++e) {
-            float r, p;
-            draw_term(load_elem<ES>(zrow, size_t(e)), resid ? qrow[e] : 0.0f, d, c, resid, r, p);
-            rs = rs + double(r);
-            ps = ps + double(p);
-        }
+        if (threadIdx.x == 0) a.out_acc[b] = j;
     }
+    return true;
 }
 
 // Last draw workgroup of request b: locate u * R and write the token.
 template <int ES, bool ALZ, bool ALQ>
-__device__ void final_select(const VerifyArgs &a, int b, const Decision &d, const void *zrow,
-                             const float *qrow, Smem &sh) {
+__device__ void final_select(const VerifyArgs &a, int b, const Decision &d, const void *zrow, const float *qrow,
+                             Smem &sh) {
     const int G1 = a.G + 1;
-    const double2 *mass = reinterpret_cast<const double2 *>(a.ws + a.lay.mass) + size_t(b) * a.ntiles;
-    bool resid = d.resid != 0;
-    if (threadIdx.x == 0) {
-        double R = 0.0, Rp = 0.0;
-        for (int t = 0; t < a.ntiles; ++t) { const double2 m = mass[t]; R = R + m.x; Rp = Rp + m.y; }
-        int mode = resid ? 1 : 0;                       // 1: residual terms, 0: target terms
-        if (resid && !(R > 0.0)) mode = 0;              // zero residual: draw from p_j
-        const double total = mode ? R : (resid ? Rp : R);
-        const double target = double(a.u[size_t(b) * G1 + a.G]) * total;
-        double P = 0.0;
-        int tstar = -1;
-        for (int t = 0; t < a.ntiles; ++t) {
-            const double2 m = mass[t];
-            const double mt = mode ? m.x : (resid ? m.y : m.x);
-            const double P1 = P + mt;
-            if (P1 > target) { tstar = t; break; }
-            P = P1;
+    const bool resid = d.resid;
+    const uint64_t *mass = reinterpret_cast<const uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
+    // Pass 1: totals, in sub-tile order.  mode 1 draws from the residual, mode 0 from p.
+    double R = 0.0, Rp = 0.0;
+    int last_r = -1, last_p = -1;
+    for (int blk = 0; blk < a.nsub; blk += kStage) {
+        const int cnt = min(kStage, a.nsub - blk);
+        __syncthreads();
+        if (int(threadIdx.x) < cnt) {
+            sh.mr[threadIdx.x] = __longlong_as_double(ld_coherent(mass + 2 * (blk + threadIdx.x)));
+            sh.mp[threadIdx.x] = __longlong_as_double(ld_coherent(mass + 2 * (blk + threadIdx.x) + 1));
         }
-        int lastpos = 0;
-        if (tstar < 0) {                                 // u * R at or beyond the top
-            lastpos = 1;
-            for (int t = a.ntiles - 1; t >= 0; --t) {
-                const double2 m = mass[t];
-                const double mt = mode ? m.x : (resid ? m.y : m.x);
-                if (mt > 0.0) { tstar = t; break; }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int i = 0; i < cnt; ++i) {
+                R = R + sh.mr[i];
+                Rp = Rp + sh.mp[i];
+                if (sh.mr[i] > 0.0) last_r = blk + i;
+                if (sh.mp[i] > 0.0) last_p = blk + i;
             }
-            if (tstar < 0) tstar = 0;
         }
-        sh.mode = mode | (lastpos << 1);
-        sh.tstar = tstar;
-        sh.base = P;
-        sh.target = target;
+    }
+    if (threadIdx.x == 0) {
+        const int mode = (resid && R > 0.0) ? 1 : 0;
+        const double total = mode ? R : (resid ? Rp : R);
+        sh.mode = mode;
+        sh.target = double(a.u[size_t(b) * G1 + a.G]) * total;
         sh.R = R;
+        sh.sstar = -1;
+        sh.base = 0.0;
         sh.t1 = kWG;
         sh.y = -1;
+        // kept for the no-crossing fallback below
+        sh.jmin = (mode || !resid) ? last_r : last_p;
     }
     __syncthreads();
-    const int mode = sh.mode & 1, lastpos = sh.mode >> 1;
-    const int tstar = sh.tstar;
-    const double base = sh.base, target = sh.target, R = sh.R;
-    const bool use_resid = resid && mode;
-    const int e0 = tstar * kTile + threadIdx.x * kRun;
+    const int mode = sh.mode;
+    const bool use_r = resid && mode;          // else: terms are p (bonus draw or zero-residual fallback)
+    const bool from_m = mode || !resid;        // which mass array holds those terms' sums
+    // Pass 2: the first sub-tile whose running sum exceeds the target.
+    double P = 0.0;
+    for (int blk = 0; blk < a.nsub; blk += kStage) {
+        const int cnt = min(kStage, a.nsub - blk);
+        if (a.nsub > kStage) {
+            __syncthreads();
+            if (int(threadIdx.x) < cnt) {
+                sh.mr[threadIdx.x] = __longlong_as_double(ld_coherent(mass + 2 * (blk + threadIdx.x)));
+                sh.mp[threadIdx.x] = __longlong_as_double(ld_coherent(mass + 2 * (blk + threadIdx.x) + 1));
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int i = 0; i < cnt; ++i) {
+                const double P1 = P + (from_m ? sh.mr[i] : sh.mp[i]);
+                if (P1 > sh.target) { sh.sstar = blk + i; sh.base = P; break; }
+                P = P1;
+            }
+        }
+        __syncthreads();
+        if (sh.sstar >= 0) break;
+    }
+    const int lastpos = (sh.sstar < 0) ? 1 : 0;         // u * R at or beyond the top
+    const int sstar = lastpos ? max(0, sh.jmin) : sh.sstar;
+    const double base = sh.base, target = sh.target;
     double rs, ps;
-    run_sums<ES, ALZ, ALQ>(zrow, qrow, a.V, e0, d, a.c32, resid, rs, ps);
-    const double mine = use_resid ? rs : (resid ? ps : rs);
-    double tile_total;
-    const double excl = wg_excl_scan(mine, tile_total, sh);
-    const int e1 = min(a.V, e0 + kRun);
+    sub_sums<ES, ALZ, ALQ>(zrow, qrow, a.V, sstar, d.m, a.c32, d.inv_s, resid, rs, ps);
+    const double v1[1] = {use_r ? rs : ps};
+    double ex[1], tot[1];
+    wg_excl_scan<1>(v1, ex, tot, sh);
+    const int e0 = sstar * kSub + int(threadIdx.x) * kSubPerThread;
+    const int e1 = min(a.V, e0 + kSubPerThread);
     if (lastpos) {
         int lp = -1;
         for (int e = e0; e < e1; ++e) {
             float r, p;
-            draw_term(load_elem<ES>(zrow, size_t(e)), resid ? qrow[e] : 0.0f, d, a.c32, resid, r, p);
-            if ((use_resid ? r : p) > 0.0f) lp = e;
+            draw_term(load_elem<ES>(zrow, size_t(e)), resid ? qrow[e] : 0.0f, d.m, a.c32, d.inv_s, resid, r, p);
+            if ((use_r ? r : p) > 0.0f) lp = e;
         }
         atomicMax(&sh.y, lp);
         __syncthreads();
     } else {
-        if (base + (excl + mine) > target) atomicMin(&sh.t1, int(threadIdx.x));
+        if (base + (ex[0] + v1[0]) > target) atomicMin(&sh.t1, int(threadIdx.x));
         __syncthreads();
         if (int(threadIdx.x) == sh.t1) {
-            double acc = base + excl;
+            double acc = base + ex[0];
             int y = -1, lp = -1;
             for (int e = e0; e < e1; ++e) {
                 float r, p;
-                draw_term(load_elem<ES>(zrow, size_t(e)), resid ? qrow[e] : 0.0f, d, a.c32, resid, r, p);
-                const float t = use_resid ? r : p;
+                draw_term(load_elem<ES>(zrow, size_t(e)), resid ? qrow[e] : 0.0f, d.m, a.c32, d.inv_s, resid, r, p);
+                const float t = use_r ? r : p;
                 if (t > 0.0f) lp = e;
                 acc = acc + double(t);
                 if (acc > target) { y = e; break; }
@@ -580,144 +681,125 @@ __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, cons
     }
     if (threadIdx.x == 0) {
         a.out_tok[size_t(b) * G1 + d.j] = sh.y;
-        if (a.d_r) a.d_r[b] = resid ? float(R) : -1.0f;
+        if (a.d_r) a.d_r[b] = resid ? float(sh.R) : -1.0f;
     }
 }
 
-// One draw workgroup: tiles [w*tpw, (w+1)*tpw) of request b's draw row.
 template <int ES, bool ALZ, bool ALQ>
-__device__ void draw_item(const VerifyArgs &a, int b, int w, Smem &sh) {
-    unsigned *flag = slot(a, b) + 1;
-    unsigned *ctr2 = slot(a, b) + 2;
-    if (threadIdx.x == 0) {
-        unsigned f;
-        uint32_t spins = 0;
-        while ((f = __hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)) == 0u) {
-            if (++spins > a.spin_limit) break;
-            __builtin_amdgcn_s_sleep(2);
+__device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh) {
+    Decision d;
+    if (!decide<ES>(a, b, w, d, sh)) {
+        // Data error or expired wait: outputs are reported.  The last of the
+        // request's workgroups clears what the row items wrote.
+        if (d.n >= 0 && d.n <= a.G && arrive_last(draw_counter(a, b), unsigned(a.nc2), sh)) {
+            if (wait_partials(a, b, d.n)) reset_request(a, b, d.n, false);
         }
-        sh.flag = int(f);
+        return;
+    }
+    const int G1 = a.G + 1;
+    const void *zrow = static_cast<const char *>(a.logits) + (size_t(b) * G1 + d.j) * size_t(a.V) * ES;
+    const float *qrow = d.resid ? a.q + (size_t(b) * a.G + d.j) * size_t(a.V) : nullptr;
+    uint64_t *mass = reinterpret_cast<uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
+    const int s_end = min(a.nsub, (w + 1) * a.spw);
+    for (int s0 = w * a.spw; s0 < s_end; s0 += kSubBatch) {
+        double v[2 * kSubBatch], ex[2 * kSubBatch], tot[2 * kSubBatch];
+#pragma unroll
+        for (int i = 0; i < kSubBatch; ++i) {
+            double rs = 0.0, ps = 0.0;
+            if (s0 + i < s_end) sub_sums<ES, ALZ, ALQ>(zrow, qrow, a.V, s0 + i, d.m, a.c32, d.inv_s, d.resid, rs, ps);
+            v[i] = rs;
+            v[kSubBatch + i] = ps;
+        }
+        wg_excl_scan<2 * kSubBatch>(v, ex, tot, sh);
+        if (int(threadIdx.x) < kSubBatch && s0 + int(threadIdx.x) < s_end) {
+            const int i = threadIdx.x;
+            st_coherent(mass + 2 * (s0 + i), uint64_t(__double_as_longlong(tot[i])));
+            st_coherent(mass + 2 * (s0 + i) + 1, uint64_t(__double_as_longlong(tot[kSubBatch + i])));
+        }
+    }
+    if (arrive_last(draw_counter(a, b), unsigned(a.nc2), sh)) {
+        final_select<ES, ALZ, ALQ>(a, b, d, zrow, qrow, sh);
+        reset_request(a, b, d.n, true);
+    }
+}
+
+// One workgroup per request (T == 0).
+__device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
+    const int G = a.G, G1 = G + 1;
+    const int n = verify_len(a, b);
+    if (n < 0 || n > G) { write_error(a, b, false); return; }
+    const int k = threadIdx.x;
+    int xk = 0;
+    if (k < n) xk = a.x[size_t(b) * G + k];
+    if (threadIdx.x == 0) { sh.jmin = n; sh.bad = 0; }
+    if (!wait_partials(a, b, n)) { write_error(a, b, false); return; }
+    const uint64_t *part = partials(a, b);
+    for (int r = threadIdx.x; r <= n; r += kWG) {
+        const uint64_t *pp = part + size_t(r) * a.nc1;
+        float best = neg_inf();
+        int bi = -1, nan = 0;
+        for (int c = 0; c < a.nc1; ++c) {               // ascending chunks: first maximum wins
+            const uint64_t v = ld_coherent(pp + c);
+            const int vi = int(hi_u(v) & ~kValid) - 2;
+            if (vi == kNanIdx) { nan = 1; continue; }
+            merge_am(best, bi, lo_f(v), vi);
+        }
+        if (nan || bi < 0 || best == __builtin_inff()) atomicOr(&sh.bad, 1);
+        sh.A[r] = bi;
     }
     __syncthreads();
-    unsigned f = unsigned(sh.flag);
-    if (f == 0u) {                                   // bounded wait expired: report, do not arrive
+    if (k < n) {
+        if (xk < 0 || xk >= a.V) atomicOr(&sh.bad, 1);
+        else if (xk != sh.A[k]) atomicMin(&sh.jmin, k);
+    }
+    __syncthreads();
+    if (sh.bad) {
         write_error(a, b, false);
-        return;
+    } else {
+        const int j = sh.jmin;
+        for (int t = threadIdx.x; t < G1; t += kWG) {
+            int v = -1;
+            if (t < j) v = a.x[size_t(b) * G + t];
+            else if (t == j) v = sh.A[j];
+            a.out_tok[size_t(b) * G1 + t] = v;
+        }
+        if (threadIdx.x == 0) a.out_acc[b] = j;
     }
-    f = __hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    if (f == kFlagError) {
-        if (arrive_last(ctr2, unsigned(a.nc2), sh) && threadIdx.x == 0) *flag = 0u;
-        return;
-    }
-    const Decision d = reinterpret_cast<const Decision *>(a.ws + a.lay.dec)[b];
-    if (d.j < 0 || d.j > a.G || d.row != d.j || (d.resid != 0 && d.j >= a.G)) {
-        // Not a record this call wrote (workspace not zero-filled before its
-        // first use): report the request instead of following it.
-        write_error(a, b, false);
-        if (arrive_last(ctr2, unsigned(a.nc2), sh) && threadIdx.x == 0) *flag = 0u;
-        return;
-    }
-    const bool resid = d.resid != 0;
-    const int G1 = a.G + 1;
-    const void *zrow = static_cast<const char *>(a.logits) + (size_t(b) * G1 + d.row) * size_t(a.V) * ES;
-    const float *qrow = resid ? a.q + (size_t(b) * a.G + d.j) * size_t(a.V) : nullptr;
-    double2 *mass = reinterpret_cast<double2 *>(a.ws + a.lay.mass) + size_t(b) * a.ntiles;
-    const int t_end = min(a.ntiles, (w + 1) * a.tpw);
-    for (int t = w * a.tpw; t < t_end; ++t) {
-        double rs, ps, rtot, ptot;
-        run_sums<ES, ALZ, ALQ>(zrow, qrow, a.V, t * kTile + threadIdx.x * kRun, d, a.c32, resid, rs, ps);
-        wg_excl_scan(rs, rtot, sh);
-        if (resid) wg_excl_scan(ps, ptot, sh);
-        else ptot = rtot;
-        if (threadIdx.x == 0) mass[t] = make_double2(rtot, ptot);
-    }
-    if (arrive_last(ctr2, unsigned(a.nc2), sh)) {
-        final_select<ES, ALZ, ALQ>(a, b, d, zrow, qrow, sh);
-        __syncthreads();
-        if (threadIdx.x == 0) *flag = 0u;
-    }
+    __syncthreads();
+    reset_request(a, b, n, false);
 }
 
 // ------------------------------------------------------------- kernels
 
-__device__ __forceinline__ void map_item(const VerifyArgs &a, int i, int &phase, int &b, int &local) {
-    const int g1 = (a.G + 1) * a.nc1, g2 = a.nc2;
-    if (a.mode == 1) { phase = 1; b = i / g1; local = i - b * g1; return; }
-    if (a.mode == 2) { phase = 2; b = i / g2; local = i - b * g2; return; }
-    const int L = a.lag;
-    const long head = long(L) * g1;
-    if (i < head) { phase = 1; b = int(i / g1); local = int(i - long(b) * g1); return; }
-    const long i2 = i - head;
-    const int seg = g1 + g2;
-    const long nseg = long(a.B - L);
-    if (i2 < nseg * seg) {
-        const long s = i2 / seg;
-        const int r = int(i2 - s * seg);
-        if (r < g1) { phase = 1; b = L + int(s); local = r; }
-        else { phase = 2; b = int(s); local = r - g1; }
-        return;
+// Grid: row items first (b-major, then row, then chunk), then request items.
+__device__ __forceinline__ bool map_item(const VerifyArgs &a, int i, int per_req, int &b, int &local) {
+    const int g1 = (a.G + 1) * a.nc1;
+    const long rows = long(a.B) * g1;
+    if (a.mode == 2 || (a.mode == 0 && i >= rows)) {
+        const long r = (a.mode == 2) ? i : i - rows;
+        b = int(r / per_req);
+        local = int(r - long(b) * per_req);
+        return false;
     }
-    const long t = i2 - nseg * seg;
-    phase = 2;
-    b = (a.B - L) + int(t / g2);
-    local = int(t % g2);
+    b = i / g1;
+    local = i - b * g1;
+    return true;
 }
 
 template <int ES, bool ALZ, bool ALQ>
 __global__ __launch_bounds__(kWG) void k_verify_sampled(VerifyArgs a) {
     __shared__ Smem sh;
-    int phase, b, local;
-    map_item(a, int(blockIdx.x), phase, b, local);
-    if (phase == 2) { draw_item<ES, ALZ, ALQ>(a, b, local, sh); return; }
-    const int k = local / a.nc1, c = local - k * a.nc1;
-    const int n = a.vlen ? a.vlen[b] : a.G;
-    if (n < 0 || n > a.G) {
-        if (k == 0 && c == 0) {
-            write_error(a, b, a.d_lse || a.d_p || a.d_q || a.d_r);
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                __threadfence();
-                __hip_atomic_store(slot(a, b) + 1, kFlagError, __ATOMIC_RELEASE,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        return;
-    }
-    if (k > n) return;
-    const int G1 = a.G + 1;
-    const void *row = static_cast<const char *>(a.logits) + (size_t(b) * G1 + k) * size_t(a.V) * ES;
-    const int beg = c * a.ch1, end = min(a.V, beg + a.ch1);
-    float m, s;
-    chunk_ms<ES, ALZ>(row, beg, end, a.c32, m, s);
-    wg_reduce_ms(m, s, a.c32, sh);
-    if (threadIdx.x == 0)
-        reinterpret_cast<float2 *>(a.ws + a.lay.part)[(size_t(b) * G1 + k) * a.nc1 + c] = make_float2(m, s);
-    if (arrive_last(slot(a, b) + 0, unsigned((n + 1) * a.nc1), sh)) decide_sampled<ES>(a, b, n, sh);
+    int b, local;
+    if (map_item(a, int(blockIdx.x), a.nc2, b, local)) row_item_sampled<ES, ALZ>(a, b, local, sh);
+    else request_item_sampled<ES, ALZ, ALQ>(a, b, local, sh);
 }
 
 template <int ES, bool AL>
 __global__ __launch_bounds__(kWG) void k_verify_greedy(VerifyArgs a) {
     __shared__ Smem sh;
-    const int g1 = (a.G + 1) * a.nc1;
-    const int b = int(blockIdx.x) / g1, local = int(blockIdx.x) - b * g1;
-    const int k = local / a.nc1, c = local - k * a.nc1;
-    const int n = a.vlen ? a.vlen[b] : a.G;
-    if (n < 0 || n > a.G) {
-        if (k == 0 && c == 0) write_error(a, b, false);
-        return;
-    }
-    if (k > n) return;
-    const int G1 = a.G + 1;
-    const void *row = static_cast<const char *>(a.logits) + (size_t(b) * G1 + k) * size_t(a.V) * ES;
-    const int beg = c * a.ch1, end = min(a.V, beg + a.ch1);
-    float best;
-    int bi, nan;
-    chunk_argmax<ES, AL>(row, beg, end, best, bi, nan);
-    wg_reduce_am(best, bi, nan, sh);
-    if (threadIdx.x == 0)
-        reinterpret_cast<int2 *>(a.ws + a.lay.part)[(size_t(b) * G1 + k) * a.nc1 + c] =
-            make_int2(__float_as_int(best), nan ? kNanIdx : bi);
-    if (arrive_last(slot(a, b) + 0, unsigned((n + 1) * a.nc1), sh)) decide_greedy(a, b, n, sh);
+    int b, local;
+    if (map_item(a, int(blockIdx.x), 1, b, local)) row_item_greedy<ES, AL>(a, b, local, sh);
+    else request_item_greedy(a, b, sh);
 }
 
 template <int ES, bool ALZ, bool ALQ>
@@ -732,9 +814,9 @@ int launch_g(const VerifyArgs &a, int grid, hipStream_t st) {
     return int(hipGetLastError());
 }
 
-template <int ES, bool ALZ, bool ALQ>
-int occ_s(int *n) {
-    return int(hipOccupancyMaxActiveBlocksPerMultiprocessor(n, k_verify_sampled<ES, ALZ, ALQ>, kWG, 0));
+template <typename K>
+int occ(K kernel, int *n) {
+    return int(hipOccupancyMaxActiveBlocksPerMultiprocessor(n, kernel, kWG, 0));
 }
 
 }  // namespace
@@ -757,15 +839,19 @@ int launch_verify_greedy(const VerifyArgs &a, bool az, int esize, int grid, void
     return az ? launch_g<4, true>(a, grid, st) : launch_g<4, false>(a, grid, st);
 }
 
-int verify_sampled_occupancy(bool az, bool aq, int esize, int *n) {
-    if (esize == 2) {
-        if (az && aq) return occ_s<2, true, true>(n);
-        if (az) return occ_s<2, true, false>(n);
-        return occ_s<2, false, false>(n);
+int verify_occupancy(bool sampled, bool az, bool aq, int esize, int *n) {
+    if (!sampled) {
+        if (esize == 2) return az ? occ(k_verify_greedy<2, true>, n) : occ(k_verify_greedy<2, false>, n);
+        return az ? occ(k_verify_greedy<4, true>, n) : occ(k_verify_greedy<4, false>, n);
     }
-    if (az && aq) return occ_s<4, true, true>(n);
-    if (az) return occ_s<4, true, false>(n);
-    return occ_s<4, false, false>(n);
+    if (esize == 2) {
+        if (az && aq) return occ(k_verify_sampled<2, true, true>, n);
+        if (az) return occ(k_verify_sampled<2, true, false>, n);
+        return occ(k_verify_sampled<2, false, false>, n);
+    }
+    if (az && aq) return occ(k_verify_sampled<4, true, true>, n);
+    if (az) return occ(k_verify_sampled<4, true, false>, n);
+    return occ(k_verify_sampled<4, false, false>, n);
 }
 
 }  // namespace sv

@@ -295,8 +295,8 @@ def test_workspace_left_zero():
     sv.verify(z, q, x, u, 1.0, workspace=ws)
     sv.verify(z, None, x, None, 0.0, workspace=ws)
     torch.cuda.synchronize()
-    counters = ws[: 1 << 20].cpu().numpy()
-    assert not counters.any()
+    # every word a call uses is zero again afterwards
+    assert not ws.cpu().numpy().any()
 
 
 def test_workspace_shared_across_shapes():
@@ -318,4 +318,4 @@ def test_workspace_shared_across_shapes():
         o = run_oracle(w)
         g = {"accepted": acc.cpu().numpy().astype(np.int64), "tokens": tok.cpu().numpy().astype(np.int64)}
         compare(w, g, o, check_diag=False)
-    assert not ws[: 1 << 20].cpu().numpy().any()
+    assert not ws.cpu().numpy().any()
