@@ -31,7 +31,7 @@ spec_status_t check_verify_shape(int64_t B, int64_t G, int64_t V, int es) {
     if (B > SPEC_MAX_BATCH || G > SPEC_MAX_DRAFTS || V > SPEC_MAX_VOCAB) return SPEC_ERR_UNSUPPORTED;
     const int64_t nc1 = (V + sv::chunk_elems(es) - 1) / sv::chunk_elems(es);
     const int64_t nsub = (V + sv::kSub - 1) / sv::kSub;
-    const int64_t items = B * ((G + 1) * nc1 + nsub);
+    const int64_t items = B * ((G + 1) * nc1 + nsub + 1);
     if (items >= (int64_t(1) << 31)) return SPEC_ERR_UNSUPPORTED;
     if (B * (G + 1) > (int64_t(1) << 40) / V) return SPEC_ERR_UNSUPPORTED;
     return SPEC_OK;
@@ -154,11 +154,12 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
     if (hipGetDevice(&dev) != hipSuccess) return SPEC_ERR_DEVICE;
     const long cap = resident_capacity(dev, sampled, az, aq, es);
     if (cap <= 0) return SPEC_ERR_DEVICE;
-    // Request items wait for row items; there must stay fewer of them than half
-    // of the resident capacity for one launch, else two launches.
+    // Request and cleanup items wait for row items (and cleanup items for
+    // request items).  One launch holds all of them only while the waiting
+    // items stay below half the resident capacity; otherwise three launches.
     const long half = cap / 2;
     if (sampled) {
-        long nc2 = half / B;
+        long nc2 = (half - B) / B;
         if (nc2 < 1) nc2 = 1;
         if (nc2 > a.nsub) nc2 = a.nsub;
         a.spw = int((a.nsub + nc2 - 1) / nc2);
@@ -168,18 +169,31 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
         a.nc2 = 1;
         a.spw = 0;
     }
+    // Request items go in after the row waves that are resident when they are
+    // dispatched plus two more, so most decisions are ready when they start.
+    const long wave = long(B) * a.nc1;
+    long k0 = (cap + wave - 1) / wave + 2;
+    if (k0 > G + 1) k0 = G + 1;
+    a.k0 = int(k0);
     auto launch = [&](long grid) {
         return sampled ? sv::launch_verify_sampled(a, az, aq, es, int(grid), stream)
                        : sv::launch_verify_greedy(a, az, es, int(grid), stream);
     };
-    if (long(B) * a.nc2 <= half) {
+    const long reqs = long(B) * a.nc2;
+    if (reqs + B <= half) {
         a.mode = 0;
-        return launch(long(B) * (g1 + a.nc2)) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+        if (launch(long(B) * g1 + reqs + B) != 0) return SPEC_ERR_DEVICE;
+    } else {
+        a.mode = 1;
+        if (launch(long(B) * g1) != 0) return SPEC_ERR_DEVICE;
+        a.mode = 2;
+        if (launch(reqs) != 0) return SPEC_ERR_DEVICE;
+        a.mode = 3;
+        if (launch(B) != 0) return SPEC_ERR_DEVICE;
     }
-    a.mode = 1;
-    if (launch(long(B) * g1) != 0) return SPEC_ERR_DEVICE;
-    a.mode = 2;
-    return launch(long(B) * a.nc2) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+    if (sampled && (a.d_lse || a.d_p || a.d_q || a.d_r))
+        return sv::launch_verify_diag(a, es, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+    return SPEC_OK;
 }
 
 size_t spec_schedule_workspace_bytes(int32_t, int32_t) { return 0; }

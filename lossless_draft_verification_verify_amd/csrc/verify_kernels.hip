@@ -86,6 +86,14 @@ __device__ __forceinline__ void stores_complete() {
     __builtin_amdgcn_s_waitcnt(0);          // vmcnt = expcnt = lgkmcnt = 0
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+// Output words that a later workgroup may overwrite are written through to
+// the coherence point, so the last write in time is the one that lands.
+__device__ __forceinline__ void st_out(int32_t *p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_out(float *p, float v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float(uint32_t(v)); }
 __device__ __forceinline__ uint32_t hi_u(uint64_t v) { return uint32_t(v >> 32); }
 __device__ __forceinline__ bool valid(uint64_t v) { return (hi_u(v) & kValid) != 0u; }
@@ -101,7 +109,7 @@ struct __align__(16) Smem {
     int A[kWG];                                   // greedy row argmax
     double mr[kStage], mp[kStage];                // staged sub-tile masses
     double tot[2 * kSubBatch];
-    int jmin, bad, last;
+    int jmin, bad, badrow, last, flagv;
     int sstar, mode, t1, y;
     double base, target, R;
 };
@@ -223,31 +231,12 @@ __device__ __forceinline__ uint64_t *partials(const VerifyArgs &a, int b) {
     return reinterpret_cast<uint64_t *>(a.ws + a.lay.part) + size_t(b) * (a.G + 1) * a.nc1;
 }
 
-__device__ void write_error(const VerifyArgs &a, int b, bool diag) {
+// A request with a data error: every output word -1 (diagnostics become NaN
+// in the diagnostics kernel, which checks out_accepted).
+__device__ void write_error(const VerifyArgs &a, int b) {
     const int G1 = a.G + 1;
-    for (int t = threadIdx.x; t < G1; t += kWG) a.out_tok[size_t(b) * G1 + t] = -1;
-    if (threadIdx.x == 0) a.out_acc[b] = -1;
-    if (!diag) return;
-    const float qnan = __builtin_nanf("");
-    for (int t = threadIdx.x; t < G1; t += kWG) {
-        if (a.d_lse) a.d_lse[size_t(b) * G1 + t] = qnan;
-        if (t < a.G) {
-            if (a.d_p) a.d_p[size_t(b) * a.G + t] = qnan;
-            if (a.d_q) a.d_q[size_t(b) * a.G + t] = qnan;
-        }
-    }
-    if (threadIdx.x == 0 && a.d_r) a.d_r[b] = qnan;
-}
-
-// Zero the request's chunk partials (rows 0..n) and sub-tile masses.
-__device__ void reset_request(const VerifyArgs &a, int b, int n, bool masses) {
-    uint64_t *part = partials(a, b);
-    const int np = (n + 1) * a.nc1;
-    for (int i = threadIdx.x; i < np; i += kWG) st_coherent(part + i, 0ull);
-    if (masses) {
-        uint64_t *mass = reinterpret_cast<uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
-        for (int i = threadIdx.x; i < 2 * a.nsub; i += kWG) st_coherent(mass + i, 0ull);
-    }
+    for (int t = threadIdx.x; t < G1; t += kWG) st_out(a.out_tok + size_t(b) * G1 + t, -1);
+    if (threadIdx.x == 0) st_out(a.out_acc + b, -1);
 }
 
 // Wait until the chunk partials of rows 0..n are all written.  False if the
@@ -486,19 +475,55 @@ struct Decision {
     float m, inv_s;
 };
 
-// Poll and merge the request's rows, run the accept tests.  Returns false
-// (outputs already reported) on a data error or an expired wait.
-template <int ES>
-__device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, Smem &sh) {
+enum { kDecided = 0, kReported = 1, kNoRequest = 2 };
+
+// Row r's chunk partials (sampled): fp64 merge into sh.M[r], sh.S[r]; flags a bad row.
+__device__ void merge_row_sampled(const VerifyArgs &a, const uint64_t *pp, int r, Smem &sh) {
+    const double c64 = double(a.c32);
+    float M = neg_inf();
+    for (int c = 0; c < a.nc1; ++c) M = fmaxf(M, lo_f(ld_coherent(pp + c)));
+    double S = 0.0;
+    for (int c = 0; c < a.nc1; ++c) {
+        const uint64_t v = ld_coherent(pp + c);
+        const float vm = lo_f(v), vs = __uint_as_float(hi_u(v) & ~kValid);
+        if (vm == neg_inf() && vs == 0.0f) continue;            // empty chunk
+        S = S + double(vs) * exp2((double(vm) - double(M)) * c64);
+    }
+    if (!(S > 0.0 && S < INFINITY) || !(M > neg_inf() && M < INFINITY)) atomicMin(&sh.badrow, r);
+    sh.M[r] = M;
+    sh.S[r] = S;
+}
+
+// Row r's chunk partials (greedy): lowest index of the maximum into sh.A[r].
+__device__ void merge_row_greedy(const VerifyArgs &a, const uint64_t *pp, int r, Smem &sh) {
+    float best = neg_inf();
+    int bi = -1, nan = 0;
+    for (int c = 0; c < a.nc1; ++c) {               // ascending chunks: first maximum wins
+        const uint64_t v = ld_coherent(pp + c);
+        const int vi = int(hi_u(v) & ~kValid) - 2;
+        if (vi == kNanIdx) { nan = 1; continue; }
+        merge_am(best, bi, lo_f(v), vi);
+    }
+    if (nan || bi < 0 || best == __builtin_inff()) atomicMin(&sh.badrow, r);
+    sh.A[r] = bi;
+}
+
+// Find the request's first rejection, merging rows in order as their chunk
+// partials arrive: the decision needs rows 0..j only, so it is final as soon as
+// a rejection is found among the rows merged so far (or all n+1 rows are in).
+// A bad row counts here only if it comes no later than the first rejection,
+// so every workgroup of the request reaches the same conclusion; bad rows
+// after it are reported by the cleanup item.
+template <bool SAMPLED, int ES>
+__device__ int decide(const VerifyArgs &a, int b, int w, Decision &d, Smem &sh) {
     const int G = a.G, G1 = G + 1;
-    const bool diag = a.d_lse || a.d_p || a.d_q || a.d_r;
     const int n = verify_len(a, b);
     d.n = n;
     if (n < 0 || n > G) {
-        if (w == 0) write_error(a, b, diag);
-        return false;
+        if (w == 0) write_error(a, b);
+        return kNoRequest;
     }
-    // Gathers of the drafted positions do not depend on the row pass: issue first.
+    // Per-position inputs do not depend on the row pass: issue them first.
     const int k = threadIdx.x;
     int xk = 0;
     float zx = 0.0f, qx = 0.0f, uk = 0.0f;
@@ -506,74 +531,91 @@ __device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, Smem &sh)
     if (k < n) {
         xk = a.x[size_t(b) * G + k];
         xbad = xk < 0 || xk >= a.V;
-        if (!xbad) {
-            zx = load_elem<ES>(a.logits, (size_t(b) * G1 + k) * size_t(a.V) + size_t(xk));
-            qx = a.q[(size_t(b) * G + k) * size_t(a.V) + size_t(xk)];
+        if (SAMPLED) {
+            if (!xbad) {
+                zx = load_elem<ES>(a.logits, (size_t(b) * G1 + k) * size_t(a.V) + size_t(xk));
+                qx = a.q[(size_t(b) * G + k) * size_t(a.V) + size_t(xk)];
+            }
+            uk = a.u[size_t(b) * G1 + k];
         }
-        uk = a.u[size_t(b) * G1 + k];
     }
-    if (threadIdx.x == 0) { sh.jmin = n; sh.bad = 0; }
-    if (!wait_partials(a, b, n)) {
-        if (w == 0) write_error(a, b, diag);
-        return false;
+    if (threadIdx.x == 0) { sh.jmin = n; sh.badrow = 0x7fffffff; }
+    if (__syncthreads_or(xbad)) {
+        if (w == 0) write_error(a, b);
+        return kReported;
     }
-    // Merge each row's chunk partials in fp64 (thread r owns row r).
-    const double c64 = double(a.c32);
-    const double T64 = double(a.T);
     const uint64_t *part = partials(a, b);
-    for (int r = threadIdx.x; r <= n; r += kWG) {
-        const uint64_t *pp = part + size_t(r) * a.nc1;
-        float M = neg_inf();
-        for (int c = 0; c < a.nc1; ++c) M = fmaxf(M, lo_f(ld_coherent(pp + c)));
-        double S = 0.0;
-        for (int c = 0; c < a.nc1; ++c) {
-            const uint64_t v = ld_coherent(pp + c);
-            const float vm = lo_f(v), vs = __uint_as_float(hi_u(v) & ~kValid);
-            if (vm == neg_inf() && vs == 0.0f) continue;            // empty chunk
-            S = S + double(vs) * exp2((double(vm) - double(M)) * c64);
+    const double T64 = double(a.T);
+    int next = 0;                                  // rows [0, next) are merged and tested
+    for (uint32_t spins = 0;;) {
+        if (threadIdx.x == 0) sh.t1 = n + 1;
+        __syncthreads();
+        const int r = next + int(threadIdx.x);
+        if (r <= n) {
+            bool rv = true;
+            for (int c = 0; c < a.nc1; ++c) rv = rv && valid(ld_coherent(part + size_t(r) * a.nc1 + c));
+            if (!rv) atomicMin(&sh.t1, r);
         }
-        if (!(S > 0.0 && S < INFINITY) || !(M > neg_inf() && M < INFINITY)) atomicOr(&sh.bad, 1);
-        sh.M[r] = M;
-        sh.S[r] = S;
-    }
-    __syncthreads();
-    if (k < n) {
-        if (xbad) {
-            atomicOr(&sh.bad, 1);
-        } else {
-            const double p = exp((double(zx) - double(sh.M[k])) / T64) / sh.S[k];
-            const bool acc = (qx > 0.0f) ? (double(uk) < p / double(qx)) : (p > 0.0);
-            if (!acc) atomicMin(&sh.jmin, k);
-            if (w == 0) {
-                if (a.d_p) a.d_p[size_t(b) * G + k] = float(p);
-                if (a.d_q) a.d_q[size_t(b) * G + k] = qx;
+        __syncthreads();
+        const int p = sh.t1;                       // rows [next, p) are all written
+        if (r < p) {
+            if (SAMPLED) merge_row_sampled(a, part + size_t(r) * a.nc1, r, sh);
+            else merge_row_greedy(a, part + size_t(r) * a.nc1, r, sh);
+        }
+        __syncthreads();
+        if (k >= next && k < p && k < n) {
+            if (SAMPLED) {
+                const double pk = exp((double(zx) - double(sh.M[k])) / T64) / sh.S[k];
+                const bool acc = (qx > 0.0f) ? (double(uk) < pk / double(qx)) : (pk > 0.0);
+                if (!acc) atomicMin(&sh.jmin, k);
+            } else if (xk != sh.A[k]) {
+                atomicMin(&sh.jmin, k);
             }
         }
-    }
-    __syncthreads();
-    if (sh.bad) {
-        if (w == 0) write_error(a, b, diag);
-        return false;
+        __syncthreads();
+        const int jm = sh.jmin, br = sh.badrow;
+        if (br < p && br <= jm) {                  // a bad row before (or at) the first rejection
+            if (w == 0) write_error(a, b);
+            return kReported;
+        }
+        if (jm < p) break;                         // rejection among merged rows, or all rows merged
+        if (p > next) { next = p; continue; }
+        if (++spins > a.spin_limit) {
+            if (w == 0) write_error(a, b);
+            return kReported;
+        }
+        __builtin_amdgcn_s_sleep(4);
     }
     const int j = sh.jmin;
     d.j = j;
     d.resid = j < n;
-    d.m = sh.M[j];
-    d.inv_s = float(1.0 / sh.S[j]);
-    if (w == 0) {
-        const float qnan = __builtin_nanf("");
-        for (int t = threadIdx.x; t < G1; t += kWG) {
-            if (t < j) a.out_tok[size_t(b) * G1 + t] = a.x[size_t(b) * G + t];
-            else if (t > j) a.out_tok[size_t(b) * G1 + t] = -1;
-            if (a.d_lse) a.d_lse[size_t(b) * G1 + t] = (t <= n) ? float(double(sh.M[t]) / T64 + log(sh.S[t])) : qnan;
-            if (t >= n && t < G) {
-                if (a.d_p) a.d_p[size_t(b) * G + t] = qnan;
-                if (a.d_q) a.d_q[size_t(b) * G + t] = qnan;
-            }
-        }
-        if (threadIdx.x == 0) a.out_acc[b] = j;
+    if (SAMPLED) {
+        d.m = sh.M[j];
+        d.inv_s = float(1.0 / sh.S[j]);
     }
-    return true;
+    if (w == 0) {
+        for (int t = threadIdx.x; t < G1; t += kWG) {
+            int v = -1;
+            if (t < j) v = a.x[size_t(b) * G + t];
+            else if (t == j && !SAMPLED) v = sh.A[j];
+            if (t != j || !SAMPLED) st_out(a.out_tok + size_t(b) * G1 + t, v);
+        }
+        if (threadIdx.x == 0) st_out(a.out_acc + b, j);
+    }
+    return kDecided;
+}
+
+__device__ __forceinline__ unsigned *done_flag(const VerifyArgs &a, int b) {
+    return reinterpret_cast<unsigned *>(a.ws + size_t(b) * kSlotBytes) + 1;
+}
+
+constexpr unsigned kDoneOk = 1, kDoneError = 2;
+
+// Outputs of request b are final (after every store that wrote them completed).
+__device__ void publish_done(const VerifyArgs &a, int b, unsigned v) {
+    stores_complete();
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(done_flag(a, b), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Last draw workgroup of request b: locate u * R and write the token.
@@ -613,8 +655,7 @@ __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, cons
         sh.base = 0.0;
         sh.t1 = kWG;
         sh.y = -1;
-        // kept for the no-crossing fallback below
-        sh.jmin = (mode || !resid) ? last_r : last_p;
+        sh.jmin = (mode || !resid) ? last_r : last_p;   // for the no-crossing fallback
     }
     __syncthreads();
     const int mode = sh.mode;
@@ -680,20 +721,18 @@ __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, cons
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        a.out_tok[size_t(b) * G1 + d.j] = sh.y;
-        if (a.d_r) a.d_r[b] = resid ? float(sh.R) : -1.0f;
+        st_out(a.out_tok + size_t(b) * G1 + d.j, sh.y);
+        if (a.d_r) st_out(a.d_r + b, resid ? float(sh.R) : -1.0f);
     }
 }
 
 template <int ES, bool ALZ, bool ALQ>
 __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh) {
     Decision d;
-    if (!decide<ES>(a, b, w, d, sh)) {
-        // Data error or expired wait: outputs are reported.  The last of the
-        // request's workgroups clears what the row items wrote.
-        if (d.n >= 0 && d.n <= a.G && arrive_last(draw_counter(a, b), unsigned(a.nc2), sh)) {
-            if (wait_partials(a, b, d.n)) reset_request(a, b, d.n, false);
-        }
+    const int st = decide<true, ES>(a, b, w, d, sh);
+    if (st == kNoRequest) return;
+    if (st == kReported) {
+        if (arrive_last(draw_counter(a, b), unsigned(a.nc2), sh)) publish_done(a, b, kDoneError);
         return;
     }
     const int G1 = a.G + 1;
@@ -719,87 +758,153 @@ __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh
     }
     if (arrive_last(draw_counter(a, b), unsigned(a.nc2), sh)) {
         final_select<ES, ALZ, ALQ>(a, b, d, zrow, qrow, sh);
-        reset_request(a, b, d.n, true);
+        uint64_t *m = reinterpret_cast<uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
+        for (int i = threadIdx.x; i < 2 * a.nsub; i += kWG) st_coherent(m + i, 0ull);
+        publish_done(a, b, kDoneOk);
     }
 }
 
-// One workgroup per request (T == 0).
+// One workgroup per request (T == 0): the emitted token is the argmax of row j.
+template <int ES>
 __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
+    Decision d;
+    const int st = decide<false, ES>(a, b, 0, d, sh);
+    if (st == kNoRequest) return;
+    publish_done(a, b, st == kDecided ? kDoneOk : kDoneError);
+}
+
+// Last workgroup of request b (placed at the end of the grid): waits for the
+// outputs to be final and for every read row's partials, reports a data error
+// in a row after the decision, writes the diagnostics, and zeroes the
+// request's partials and flag.
+template <bool SAMPLED, int ES>
+__device__ void cleanup_item(const VerifyArgs &a, int b, Smem &sh) {
     const int G = a.G, G1 = G + 1;
     const int n = verify_len(a, b);
-    if (n < 0 || n > G) { write_error(a, b, false); return; }
-    const int k = threadIdx.x;
-    int xk = 0;
-    if (k < n) xk = a.x[size_t(b) * G + k];
-    if (threadIdx.x == 0) { sh.jmin = n; sh.bad = 0; }
-    if (!wait_partials(a, b, n)) { write_error(a, b, false); return; }
+    if (n < 0 || n > G) return;
+    const bool diag = SAMPLED && (a.d_lse || a.d_p || a.d_q);
+    unsigned *flag = done_flag(a, b);
+    if (threadIdx.x == 0) {
+        unsigned f = 0;
+        for (uint32_t spins = 0; (f = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0u;
+             ++spins) {
+            if (spins >= a.spin_limit) break;
+            __builtin_amdgcn_s_sleep(4);
+        }
+        sh.flagv = int(f);
+        sh.badrow = 0x7fffffff;
+    }
+    __syncthreads();
+    const unsigned fv = unsigned(sh.flagv);
+    if (fv == 0u || !wait_partials(a, b, n)) { write_error(a, b); return; }
     const uint64_t *part = partials(a, b);
     for (int r = threadIdx.x; r <= n; r += kWG) {
-        const uint64_t *pp = part + size_t(r) * a.nc1;
-        float best = neg_inf();
-        int bi = -1, nan = 0;
-        for (int c = 0; c < a.nc1; ++c) {               // ascending chunks: first maximum wins
-            const uint64_t v = ld_coherent(pp + c);
-            const int vi = int(hi_u(v) & ~kValid) - 2;
-            if (vi == kNanIdx) { nan = 1; continue; }
-            merge_am(best, bi, lo_f(v), vi);
+        if (SAMPLED) merge_row_sampled(a, part + size_t(r) * a.nc1, r, sh);
+        else merge_row_greedy(a, part + size_t(r) * a.nc1, r, sh);
+    }
+    __syncthreads();
+    const bool bad = sh.badrow <= n || fv == kDoneError;
+    if (bad) {
+        write_error(a, b);
+    } else if (diag) {
+        char *rs = reinterpret_cast<char *>(a.ws + a.lay.rowstat) + size_t(b) * G1 * 16;
+        for (int t = threadIdx.x; t <= n; t += kWG) {
+            *reinterpret_cast<float *>(rs + size_t(t) * 16) = sh.M[t];
+            *reinterpret_cast<double *>(rs + size_t(t) * 16 + 8) = sh.S[t];
         }
-        if (nan || bi < 0 || best == __builtin_inff()) atomicOr(&sh.bad, 1);
-        sh.A[r] = bi;
     }
     __syncthreads();
-    if (k < n) {
-        if (xk < 0 || xk >= a.V) atomicOr(&sh.bad, 1);
-        else if (xk != sh.A[k]) atomicMin(&sh.jmin, k);
-    }
-    __syncthreads();
-    if (sh.bad) {
-        write_error(a, b, false);
-    } else {
-        const int j = sh.jmin;
-        for (int t = threadIdx.x; t < G1; t += kWG) {
-            int v = -1;
-            if (t < j) v = a.x[size_t(b) * G + t];
-            else if (t == j) v = sh.A[j];
-            a.out_tok[size_t(b) * G1 + t] = v;
-        }
-        if (threadIdx.x == 0) a.out_acc[b] = j;
-    }
-    __syncthreads();
-    reset_request(a, b, n, false);
+    for (int i = threadIdx.x; i < (n + 1) * a.nc1; i += kWG) st_coherent(partials(a, b) + i, 0ull);
+    if (threadIdx.x == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------- kernels
 
-// Grid: row items first (b-major, then row, then chunk), then request items.
-__device__ __forceinline__ bool map_item(const VerifyArgs &a, int i, int per_req, int &b, int &local) {
-    const int g1 = (a.G + 1) * a.nc1;
-    const long rows = long(a.B) * g1;
-    if (a.mode == 2 || (a.mode == 0 && i >= rows)) {
-        const long r = (a.mode == 2) ? i : i - rows;
-        b = int(r / per_req);
-        local = int(r - long(b) * per_req);
-        return false;
+enum { kRowItem = 0, kRequestItem = 1, kCleanupItem = 2 };
+
+// Grid order: row waves 0..k0-1 (wave k = row k of every request, request-major
+// then chunk), the request items, row waves k0..G, then one cleanup item per
+// request.  Row k of every request is streamed before row k+1, so most
+// decisions (which need rows 0..j) are ready while later rows still stream.
+__device__ __forceinline__ int map_item(const VerifyArgs &a, int i, int per_req, int &b, int &local) {
+    const long W = long(a.B) * a.nc1;                 // one row wave
+    const long rows = long(a.G + 1) * W;
+    const long reqs = long(a.B) * per_req;
+    long ri;                                          // index among row items
+    if (a.mode == 1) {
+        ri = i;
+    } else if (a.mode == 2) {
+        b = i / per_req; local = i - b * per_req; return kRequestItem;
+    } else if (a.mode == 3) {
+        b = i; local = 0; return kCleanupItem;
+    } else {
+        const long head = long(a.k0) * W;
+        if (i < head) ri = i;
+        else if (i < head + reqs) { const long r = i - head; b = int(r / per_req); local = int(r - long(b) * per_req); return kRequestItem; }
+        else if (i < rows + reqs) ri = i - reqs;
+        else { b = int(i - rows - reqs); local = 0; return kCleanupItem; }
     }
-    b = i / g1;
-    local = i - b * g1;
-    return true;
+    const int k = int(ri / W);
+    const int rem = int(ri - long(k) * W);
+    b = rem / a.nc1;
+    local = k * a.nc1 + (rem - b * a.nc1);            // row-item local index: k * nc1 + c
+    return kRowItem;
 }
 
 template <int ES, bool ALZ, bool ALQ>
 __global__ __launch_bounds__(kWG) void k_verify_sampled(VerifyArgs a) {
     __shared__ Smem sh;
     int b, local;
-    if (map_item(a, int(blockIdx.x), a.nc2, b, local)) row_item_sampled<ES, ALZ>(a, b, local, sh);
-    else request_item_sampled<ES, ALZ, ALQ>(a, b, local, sh);
+    const int kind = map_item(a, int(blockIdx.x), a.nc2, b, local);
+    if (kind == kRowItem) row_item_sampled<ES, ALZ>(a, b, local, sh);
+    else if (kind == kRequestItem) request_item_sampled<ES, ALZ, ALQ>(a, b, local, sh);
+    else cleanup_item<true, ES>(a, b, sh);
 }
 
 template <int ES, bool AL>
 __global__ __launch_bounds__(kWG) void k_verify_greedy(VerifyArgs a) {
     __shared__ Smem sh;
     int b, local;
-    if (map_item(a, int(blockIdx.x), 1, b, local)) row_item_greedy<ES, AL>(a, b, local, sh);
-    else request_item_greedy(a, b, sh);
+    const int kind = map_item(a, int(blockIdx.x), 1, b, local);
+    if (kind == kRowItem) row_item_greedy<ES, AL>(a, b, local, sh);
+    else if (kind == kRequestItem) request_item_greedy<ES>(a, b, sh);
+    else cleanup_item<false, ES>(a, b, sh);
+}
+
+// Diagnostics (parity checks only): per request, from the row statistics the
+// cleanup item stored; NaN for rows not read and for requests with an error.
+template <int ES>
+__global__ __launch_bounds__(kWG) void k_verify_diag(VerifyArgs a) {
+    const int b = blockIdx.x;
+    const int G = a.G, G1 = G + 1;
+    const float qnan = __builtin_nanf("");
+    const bool bad = a.out_acc[b] < 0;
+    const int n = bad ? -1 : verify_len(a, b);
+    char *rs = reinterpret_cast<char *>(a.ws + a.lay.rowstat) + size_t(b) * G1 * 16;
+    const double T64 = double(a.T);
+    for (int t = threadIdx.x; t < G1; t += kWG) {
+        float lse = qnan, pv = qnan, qv = qnan;
+        if (t <= n) {
+            const float M = *reinterpret_cast<const float *>(rs + size_t(t) * 16);
+            const double S = *reinterpret_cast<const double *>(rs + size_t(t) * 16 + 8);
+            // last reader: leave the workspace zero-filled
+            *reinterpret_cast<uint64_t *>(rs + size_t(t) * 16) = 0ull;
+            *reinterpret_cast<uint64_t *>(rs + size_t(t) * 16 + 8) = 0ull;
+            lse = float(double(M) / T64 + log(S));
+            if (t < n) {
+                const int xt = a.x[size_t(b) * G + t];
+                const float zt = load_elem<ES>(a.logits, (size_t(b) * G1 + t) * size_t(a.V) + size_t(xt));
+                qv = a.q[(size_t(b) * G + t) * size_t(a.V) + size_t(xt)];
+                pv = float(exp((double(zt) - double(M)) / T64) / S);
+            }
+        }
+        if (a.d_lse) a.d_lse[size_t(b) * G1 + t] = lse;
+        if (t < G) {
+            if (a.d_p) a.d_p[size_t(b) * G + t] = pv;
+            if (a.d_q) a.d_q[size_t(b) * G + t] = qv;
+        }
+    }
+    if (threadIdx.x == 0 && bad && a.d_r) a.d_r[b] = qnan;
 }
 
 template <int ES, bool ALZ, bool ALQ>
@@ -837,6 +942,13 @@ int launch_verify_greedy(const VerifyArgs &a, bool az, int esize, int grid, void
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (esize == 2) return az ? launch_g<2, true>(a, grid, st) : launch_g<2, false>(a, grid, st);
     return az ? launch_g<4, true>(a, grid, st) : launch_g<4, false>(a, grid, st);
+}
+
+int launch_verify_diag(const VerifyArgs &a, int esize, void *stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (esize == 2) hipLaunchKernelGGL(k_verify_diag<2>, dim3(a.B), dim3(kWG), 0, st, a);
+    else hipLaunchKernelGGL(k_verify_diag<4>, dim3(a.B), dim3(kWG), 0, st, a);
+    return int(hipGetLastError());
 }
 
 int verify_occupancy(bool sampled, bool az, bool aq, int esize, int *n) {

@@ -294,6 +294,7 @@ def test_workspace_left_zero():
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     sv.verify(z, q, x, u, 1.0, workspace=ws)
     sv.verify(z, None, x, None, 0.0, workspace=ws)
+    sv.verify(z, q, x, u, 1.0, workspace=ws, diag=True)
     torch.cuda.synchronize()
     # every word a call uses is zero again afterwards
     assert not ws.cpu().numpy().any()
