@@ -31,7 +31,7 @@ spec_status_t check_verify_shape(int64_t B, int64_t G, int64_t V, int es) {
     if (B > SPEC_MAX_BATCH || G > SPEC_MAX_DRAFTS || V > SPEC_MAX_VOCAB) return SPEC_ERR_UNSUPPORTED;
     const int64_t nc1 = (V + sv::chunk_elems(es) - 1) / sv::chunk_elems(es);
     const int64_t nsub = (V + sv::kSub - 1) / sv::kSub;
-    const int64_t items = B * ((G + 1) * nc1 + nsub + 1);
+    const int64_t items = B * ((G + 1) * nc1 + nsub);
     if (items >= (int64_t(1) << 31)) return SPEC_ERR_UNSUPPORTED;
     if (B * (G + 1) > (int64_t(1) << 40) / V) return SPEC_ERR_UNSUPPORTED;
     return SPEC_OK;
@@ -40,13 +40,13 @@ spec_status_t check_verify_shape(int64_t B, int64_t G, int64_t V, int es) {
 struct DeviceInfo {
     bool ready = false;
     int cus = 0;
-    int occ[2][2][2][2] = {};   // [sampled][esize==2][aligned_z][aligned_q] blocks per CU, 0 = unknown
+    int occ[2][2] = {};   // [esize==2][aligned_z] greedy-kernel blocks per CU, 0 = unknown
 };
 std::mutex g_mu;
 DeviceInfo g_dev[128];
 
-// Resident workgroups of the verify kernel on this device; -1 on error.
-long resident_capacity(int dev, bool sampled, bool az, bool aq, int es) {
+// Resident workgroups of the greedy verify kernel on this device; -1 on error.
+long resident_capacity(int dev, bool az, int es) {
     if (dev < 0 || dev >= 128) return -1;
     std::lock_guard<std::mutex> lock(g_mu);
     DeviceInfo &d = g_dev[dev];
@@ -57,10 +57,10 @@ long resident_capacity(int dev, bool sampled, bool az, bool aq, int es) {
         d.cus = cus;
         d.ready = true;
     }
-    int &o = d.occ[sampled][es == 2][az][aq];
+    int &o = d.occ[es == 2][az];
     if (o == 0) {
         int n = 0;
-        if (sv::verify_occupancy(sampled, az, aq, es, &n) != 0 || n <= 0) return -1;
+        if (sv::greedy_occupancy(az, es, &n) != 0 || n <= 0) return -1;
         o = n;
     }
     return long(o) * d.cus;
@@ -150,50 +150,29 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
     const bool aq = aligned(draft_probs, 16) && V % 4 == 0;
     const long g1 = long(G + 1) * a.nc1;
 
+    if (sampled) {
+        // Row pass, then request pass: nothing waits, each launch sized freely.
+        a.spw = sv::kSubBatch;
+        a.nc2 = (a.nsub + a.spw - 1) / a.spw;
+        if (sv::launch_rows_sampled(a, az, es, int(long(B) * g1), stream) != 0) return SPEC_ERR_DEVICE;
+        return sv::launch_requests_sampled(a, az, aq, es, int(long(B) * a.nc2), stream) == 0 ? SPEC_OK
+                                                                                            : SPEC_ERR_DEVICE;
+    }
+    // Greedy: the per-request items are cheap and wait for their rows, so they
+    // share the row launch while they stay below half the resident capacity.
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SPEC_ERR_DEVICE;
-    const long cap = resident_capacity(dev, sampled, az, aq, es);
+    const long cap = resident_capacity(dev, az, es);
     if (cap <= 0) return SPEC_ERR_DEVICE;
-    // Request and cleanup items wait for row items (and cleanup items for
-    // request items).  One launch holds all of them only while the waiting
-    // items stay below half the resident capacity; otherwise three launches.
-    const long half = cap / 2;
-    if (sampled) {
-        long nc2 = (half - B) / B;
-        if (nc2 < 1) nc2 = 1;
-        if (nc2 > a.nsub) nc2 = a.nsub;
-        a.spw = int((a.nsub + nc2 - 1) / nc2);
-        a.spw = (a.spw + sv::kSubBatch - 1) / sv::kSubBatch * sv::kSubBatch;   // whole batches
-        a.nc2 = (a.nsub + a.spw - 1) / a.spw;
-    } else {
-        a.nc2 = 1;
-        a.spw = 0;
-    }
-    // Request items go in after the row waves that are resident when they are
-    // dispatched plus two more, so most decisions are ready when they start.
-    const long wave = long(B) * a.nc1;
-    long k0 = (cap + wave - 1) / wave + 2;
-    if (k0 > G + 1) k0 = G + 1;
-    a.k0 = int(k0);
-    auto launch = [&](long grid) {
-        return sampled ? sv::launch_verify_sampled(a, az, aq, es, int(grid), stream)
-                       : sv::launch_verify_greedy(a, az, es, int(grid), stream);
-    };
-    const long reqs = long(B) * a.nc2;
-    if (reqs + B <= half) {
+    a.nc2 = 1;
+    if (long(B) <= cap / 2) {
         a.mode = 0;
-        if (launch(long(B) * g1 + reqs + B) != 0) return SPEC_ERR_DEVICE;
-    } else {
-        a.mode = 1;
-        if (launch(long(B) * g1) != 0) return SPEC_ERR_DEVICE;
-        a.mode = 2;
-        if (launch(reqs) != 0) return SPEC_ERR_DEVICE;
-        a.mode = 3;
-        if (launch(B) != 0) return SPEC_ERR_DEVICE;
+        return sv::launch_verify_greedy(a, az, es, int(long(B) * g1 + B), stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
     }
-    if (sampled && (a.d_lse || a.d_p || a.d_q || a.d_r))
-        return sv::launch_verify_diag(a, es, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
-    return SPEC_OK;
+    a.mode = 1;
+    if (sv::launch_verify_greedy(a, az, es, int(long(B) * g1), stream) != 0) return SPEC_ERR_DEVICE;
+    a.mode = 2;
+    return sv::launch_verify_greedy(a, az, es, B, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
 }
 
 size_t spec_schedule_workspace_bytes(int32_t, int32_t) { return 0; }

@@ -21,14 +21,13 @@ inline int chunk_elems(int esize) { return kWG * kVecPerThread * (16 / esize); }
 // Workspace.  Between calls every byte the kernels use is zero: each slot is
 // reset by the last workgroup that reads it, so one zero-filled workspace stays
 // valid across calls of any shape.
-//   counters [kMaxBatch] 16-byte slots at fixed offsets: word 1 flags the
-//            request's outputs as final, word 2 counts its draw workgroups;
+//   counters [kMaxBatch] 16-byte slots at fixed offsets: word 2 counts the
+//            request's workgroups of the request pass;
 //   part     [B*(G+1)*nc1] u64 chunk partials, bit 63 set once written
 //            (sampled: low = max bits, high = sum bits | 1<<31;
 //             greedy:  low = max bits, high = (argmax + 2) | 1<<31);
-//   mass     [B*nsub] 2 u64: fp64 (residual mass, target mass) per sub-tile;
-//   rowstat  [B*(G+1)] (float max, fp64 sum) per read row, written only when
-//            diagnostics are requested and read by the diagnostics kernel.
+//   mass     [B*nsub] 2 u64: fp64 (residual mass, target mass) per sub-tile.
+
 constexpr int kMaxBatch = 65536;
 constexpr size_t kSlotBytes = 16;
 constexpr size_t kCounterBytes = size_t(kMaxBatch) * kSlotBytes;
@@ -37,7 +36,6 @@ constexpr uint32_t kValid = 0x80000000u;
 struct Layout {
     size_t part;
     size_t mass;
-    size_t rowstat;
     size_t total;
 };
 
@@ -50,7 +48,6 @@ inline Layout make_layout(int64_t B, int64_t G, int64_t V, int esize) {
     size_t o = kCounterBytes;
     L.part = o; o += align256(size_t(B) * size_t(G + 1) * size_t(nc1) * 8);
     L.mass = o; o += align256(size_t(B) * size_t(nsub) * 16);
-    L.rowstat = o; o += align256(size_t(B) * size_t(G + 1) * 16);
     L.total = o;
     return L;
 }
@@ -71,18 +68,17 @@ struct VerifyArgs {
     float c32;        // log2(e) / T, the fp32 exponent scale
     int32_t nc1, ch1; // row-pass chunks per row, elements per chunk
     int32_t nsub;     // draw sub-tiles per row
-    int32_t nc2, spw; // draw workgroups per request, sub-tiles per workgroup
-    int32_t k0;       // row waves placed before the request items
-    int32_t mode;     // 0: one launch of everything; 1: row items; 2: request items; 3: cleanup items
+    int32_t nc2, spw; // request workgroups per request, sub-tiles per workgroup
+    int32_t mode;     // greedy kernel: 0 row items then request items; 1 row items only; 2 request items only
     uint32_t spin_limit;
 };
 
 // Launchers (verify_kernels.hip).  Return a hipError_t as int.
-int launch_verify_sampled(const VerifyArgs &a, bool aligned_z, bool aligned_q, int esize,
-                          int grid, void *stream);
+int launch_rows_sampled(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
+int launch_requests_sampled(const VerifyArgs &a, bool aligned_z, bool aligned_q, int esize, int grid,
+                            void *stream);
 int launch_verify_greedy(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
-int verify_occupancy(bool sampled, bool aligned_z, bool aligned_q, int esize, int *blocks_per_cu);
-int launch_verify_diag(const VerifyArgs &a, int esize, void *stream);
+int greedy_occupancy(bool aligned_z, int esize, int *blocks_per_cu);
 
 struct ScheduleArgs {
     const float *conf;

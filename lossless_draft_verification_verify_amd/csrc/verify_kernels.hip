@@ -12,30 +12,35 @@
 // How it maps to the chip
 // -----------------------
 // The work is a bandwidth-bound streaming reduction (no contraction, so no
-// MFMA).  One launch handles the whole batch, in two kinds of workgroup:
+// MFMA).  Temperature > 0 runs as two launches on the caller's stream:
 //
-//   row items      one per (request, row, 16384-element chunk): 8 x 16-byte
-//                  loads in flight per thread, the chunk maximum, then the sum
-//                  of 2^((z - m) * log2(e)/T), merged across the workgroup by
-//                  wave butterflies and LDS.  The (max, sum) partial goes out as
-//                  one coherent 64-bit store tagged valid; the workgroup then
-//                  exits.  No counters, no waits.
-//   request items  nc2 per request, placed after every row item in the grid.
-//                  Each polls its request's chunk partials until all are valid,
-//                  merges them per row in fp64, runs the accept tests (the
-//                  draft-token gathers were issued before the poll) and finds
-//                  the first rejection; then streams its share of the one row
-//                  the final token is drawn from (target row, plus the draft row
-//                  on a rejection) in sub-tiles of 2048, writing fp64 sub-tile
-//                  masses.  The last of the request's nc2 workgroups to arrive
-//                  locates u * R by a prefix over sub-tile masses, re-scans that
-//                  one sub-tile, writes the token, and zeroes every workspace
-//                  word the request used.
+//   row pass       one workgroup per (request, row, 16384-element chunk):
+//                  8 x 16-byte loads in flight per thread, the chunk maximum,
+//                  then the sum of 2^((z - m) * log2(e)/T), merged across the
+//                  workgroup by wave butterflies and LDS; the (max, sum)
+//                  partial is one 64-bit store.  Nothing else, so the kernel
+//                  keeps few registers and full occupancy.
+//   request pass   nc2 workgroups per request, one per pair of 2048-element
+//                  sub-tiles of the draw row.  Each merges the request's chunk
+//                  partials per row in fp64, runs the accept tests and finds the
+//                  first rejection j (every workgroup of the request computes
+//                  the same result), then streams its sub-tiles of the one row
+//                  the final token is drawn from (target row j, plus draft row j
+//                  on a rejection) and writes fp64 sub-tile masses.  The last of
+//                  the request's workgroups to arrive (a counter) locates u * R
+//                  by a prefix over the masses, re-scans that one sub-tile,
+//                  writes the token, and zeroes every workspace word the
+//                  request used.
 //
-// Request items only wait for row items, which precede them in the grid and
-// never wait, and the host keeps the request items below half the device's
-// resident capacity (else it launches the two kinds separately), so every
-// wait ends; the waits are also bounded.
+// Nothing waits on anything inside a launch except the arrival counter, so
+// there are no spin loops on this path.  Temperature 0 (argmax) is one launch:
+// row items, then one item per request that polls its rows' partials (bounded
+// wait) — the host keeps those below half the resident capacity, else it
+// splits them into a second launch.
+//
+// Words handed between workgroups of one launch (sub-tile masses, the greedy
+// partials) use coherent device-scope stores and loads instead of device-scope
+// fences, which on this chip write back or invalidate the whole L2.
 //
 // Determinism: no floating-point atomics; every reduction has a fixed order;
 // the sub-tile masses and the final re-scan run the same code, so the sub-tile
@@ -57,6 +62,33 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // Native 2^x (v_exp_f32).  Arguments here are <= 0; results below the fp32
 // normal range flush to zero, far below every tolerance.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max(a, b, c) in one instruction, without the NaN canonicalisation fmaxf
+// needs: a NaN in the data reaches the row sum through its exp2 term anyway.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ bool finitef(float x) { return x > -__builtin_inff() && x < __builtin_inff(); }
+
+// Sums are taken in scaled units y = z * c (c = log2(e)/T) against a
+// reference R = fl(m * c) for the maximum m of the elements summed:
+// 2^(fma(z, c, -R)) rounds only the difference, which is near 0 for the
+// terms that dominate.  When R overflows (huge logits or a tiny T) the
+// reference falls back to m itself: 2^((z - m) * c).
+// Factor that rescales a sum taken against reference m1 to reference m0 >= m1.
+__device__ __forceinline__ float rescale(float m1, float m0, float c) {
+    if (m1 == -__builtin_inff()) return 0.0f;
+    const float r1 = m1 * c, r0 = m0 * c;
+    return (finitef(r1) && finitef(r0)) ? __builtin_amdgcn_exp2f(r1 - r0) : __builtin_amdgcn_exp2f((m1 - m0) * c);
+}
+__device__ __forceinline__ double rescale_d(float m1, float m0, float c) {
+    if (m1 == -__builtin_inff()) return 0.0;
+    const float r1 = m1 * c, r0 = m0 * c;
+    return (finitef(r1) && finitef(r0)) ? exp2(double(r1) - double(r0))
+                                        : exp2((double(m1) - double(m0)) * double(c));
+}
 
 template <int ES>
 __device__ __forceinline__ float load_elem(const void *base, size_t i) {
@@ -109,19 +141,20 @@ struct __align__(16) Smem {
     int A[kWG];                                   // greedy row argmax
     double mr[kStage], mp[kStage];                // staged sub-tile masses
     double tot[2 * kSubBatch];
-    int jmin, bad, badrow, last, flagv;
+    int jmin, bad, last;
     int sstar, mode, t1, y;
     double base, target, R;
 };
 
 // ---------------------------------------------------------------- reductions
 
-// Merge two (max, sum) partials of the same row; sums are relative to their max.
+// Merge two (max, sum) partials of the same row; each sum is taken against
+// its own max (see rescale).
 __device__ __forceinline__ void merge_ms(float &m, float &s, float m2, float s2, float c) {
     const float M = fmaxf(m, m2);
     if (M == neg_inf()) { m = M; s = s + s2; return; }
-    const float a = (m == neg_inf()) ? 0.0f * s : s * exp2_fast((m - M) * c);
-    const float b = (m2 == neg_inf()) ? 0.0f * s2 : s2 * exp2_fast((m2 - M) * c);
+    const float a = (m == neg_inf()) ? 0.0f * s : s * rescale(m, M, c);
+    const float b = (m2 == neg_inf()) ? 0.0f * s2 : s2 * rescale(m2, M, c);
     m = M;
     s = a + b;
 }
@@ -246,7 +279,7 @@ __device__ bool wait_partials(const VerifyArgs &a, int b, int n) {
     const int np = (n + 1) * a.nc1;
     for (uint32_t spins = 0;; ++spins) {
         bool ready = true;
-        for (int i = threadIdx.x; i < np; i += kWG) ready = ready && valid(ld_coherent(part + i));
+        for (int i = threadIdx.x; i < np; i += kWG) ready &= valid(ld_coherent(part + i));   // no short circuit: loads overlap
         if (__syncthreads_and(ready)) return true;
         if (spins >= a.spin_limit) return false;
         __builtin_amdgcn_s_sleep(4);
@@ -274,12 +307,19 @@ __device__ void chunk_ms(const void *row, int beg, int end, float c, float &m_ou
 #pragma unroll
         for (int i = 0; i < kVecPerThread; ++i) {
             const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+            if constexpr (ES == 2) {
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                if constexpr (ES == 2) m = fmaxf(m, fmaxf(bf16_lo(w[d]), bf16_hi(w[d])));
-                else m = fmaxf(m, __uint_as_float(w[d]));
+                for (int d = 0; d < 4; ++d) m = max3(m, bf16_lo(w[d]), bf16_hi(w[d]));
+            } else {
+                m = max3(m, __uint_as_float(w[0]), __uint_as_float(w[1]));
+                m = max3(m, __uint_as_float(w[2]), __uint_as_float(w[3]));
             }
         }
+        // Keep only the raw words live between the two passes (re-converting a
+        // bf16 is one instruction; holding 64 converted floats costs occupancy).
+#pragma unroll
+        for (int i = 0; i < kVecPerThread; ++i)
+            asm volatile("" : "+v"(r[i].x), "+v"(r[i].y), "+v"(r[i].z), "+v"(r[i].w));
         float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
         if (m == neg_inf()) {
             // Every element is -inf or NaN (fmaxf drops NaN): keep a NaN visible.
@@ -295,24 +335,39 @@ __device__ void chunk_ms(const void *row, int beg, int end, float c, float &m_ou
                     }
                 }
             }
-        } else {
+        } else if (finitef(m * c)) {
+            const float nR = -(m * c);
 #pragma unroll
             for (int i = 0; i < kVecPerThread; ++i) {
                 const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
                 if constexpr (ES == 2) {
-                    s0 = s0 + exp2_fast((bf16_lo(w[0]) - m) * c);
-                    s1 = s1 + exp2_fast((bf16_hi(w[0]) - m) * c);
-                    s2 = s2 + exp2_fast((bf16_lo(w[1]) - m) * c);
-                    s3 = s3 + exp2_fast((bf16_hi(w[1]) - m) * c);
-                    s0 = s0 + exp2_fast((bf16_lo(w[2]) - m) * c);
-                    s1 = s1 + exp2_fast((bf16_hi(w[2]) - m) * c);
-                    s2 = s2 + exp2_fast((bf16_lo(w[3]) - m) * c);
-                    s3 = s3 + exp2_fast((bf16_hi(w[3]) - m) * c);
+                    s0 = s0 + exp2_fast(__builtin_fmaf(bf16_lo(w[0]), c, nR));
+                    s1 = s1 + exp2_fast(__builtin_fmaf(bf16_hi(w[0]), c, nR));
+                    s2 = s2 + exp2_fast(__builtin_fmaf(bf16_lo(w[1]), c, nR));
+                    s3 = s3 + exp2_fast(__builtin_fmaf(bf16_hi(w[1]), c, nR));
+                    s0 = s0 + exp2_fast(__builtin_fmaf(bf16_lo(w[2]), c, nR));
+                    s1 = s1 + exp2_fast(__builtin_fmaf(bf16_hi(w[2]), c, nR));
+                    s2 = s2 + exp2_fast(__builtin_fmaf(bf16_lo(w[3]), c, nR));
+                    s3 = s3 + exp2_fast(__builtin_fmaf(bf16_hi(w[3]), c, nR));
                 } else {
-                    s0 = s0 + exp2_fast((__uint_as_float(w[0]) - m) * c);
-                    s1 = s1 + exp2_fast((__uint_as_float(w[1]) - m) * c);
-                    s2 = s2 + exp2_fast((__uint_as_float(w[2]) - m) * c);
-                    s3 = s3 + exp2_fast((__uint_as_float(w[3]) - m) * c);
+                    s0 = s0 + exp2_fast(__builtin_fmaf(__uint_as_float(w[0]), c, nR));
+                    s1 = s1 + exp2_fast(__builtin_fmaf(__uint_as_float(w[1]), c, nR));
+                    s2 = s2 + exp2_fast(__builtin_fmaf(__uint_as_float(w[2]), c, nR));
+                    s3 = s3 + exp2_fast(__builtin_fmaf(__uint_as_float(w[3]), c, nR));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kVecPerThread; ++i) {
+                const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    if constexpr (ES == 2) {
+                        s0 = s0 + exp2_fast((bf16_lo(w[d]) - m) * c);
+                        s1 = s1 + exp2_fast((bf16_hi(w[d]) - m) * c);
+                    } else {
+                        s0 = s0 + exp2_fast((__uint_as_float(w[d]) - m) * c);
+                    }
                 }
             }
         }
@@ -321,9 +376,13 @@ __device__ void chunk_ms(const void *row, int beg, int end, float c, float &m_ou
         float s = 0.0f;
         for (int e = beg + threadIdx.x; e < end; e += kWG) {
             const float v = load_elem<ES>(row, size_t(e));
-            if (v > m) { s = s * exp2_fast((m - v) * c); m = v; }
-            if (m != neg_inf()) s = s + exp2_fast((v - m) * c);
-            else if (v != v) s = v;                       // NaN among -inf: keep it visible
+            if (v > m) { s = s * rescale(m, v, c); m = v; }
+            if (m != neg_inf()) {
+                const float R = m * c;
+                s = s + (finitef(R) ? exp2_fast(__builtin_fmaf(v, c, -R)) : exp2_fast((v - m) * c));
+            } else if (v != v) {
+                s = v;                                    // NaN among -inf: keep it visible
+            }
         }
         s_out = s;
     }
@@ -407,9 +466,12 @@ __device__ void row_item_greedy(const VerifyArgs &a, int b, int local, Smem &sh)
 
 // ---------------------------------------------------------- draw sub-tiles
 
+// Target probability and residual of one element of the draw row; m is the
+// row maximum (reference as in the row pass: fl(m * c) when finite).
 __device__ __forceinline__ void draw_term(float z, float q, float m, float c, float inv_s, bool resid,
                                           float &r, float &p) {
-    const float e = exp2_fast((z - m) * c);
+    const float R = m * c;
+    const float e = finitef(R) ? exp2_fast(__builtin_fmaf(z, c, -R)) : exp2_fast((z - m) * c);
     p = e * inv_s;
     r = resid ? fmaxf(p - q, 0.0f) : p;
 }
@@ -475,21 +537,24 @@ struct Decision {
     float m, inv_s;
 };
 
-enum { kDecided = 0, kReported = 1, kNoRequest = 2 };
-
-// Row r's chunk partials (sampled): fp64 merge into sh.M[r], sh.S[r]; flags a bad row.
+// Merge row r's chunk partials into sh.M[r] (max) and sh.S[r] (fp64 sum);
+// marks the request bad for a bad row or a partial that was never written.
 __device__ void merge_row_sampled(const VerifyArgs &a, const uint64_t *pp, int r, Smem &sh) {
-    const double c64 = double(a.c32);
     float M = neg_inf();
-    for (int c = 0; c < a.nc1; ++c) M = fmaxf(M, lo_f(ld_coherent(pp + c)));
+    bool ok = true;
+    for (int c = 0; c < a.nc1; ++c) {
+        const uint64_t v = pp[c];
+        ok &= valid(v);
+        M = fmaxf(M, lo_f(v));
+    }
     double S = 0.0;
     for (int c = 0; c < a.nc1; ++c) {
-        const uint64_t v = ld_coherent(pp + c);
+        const uint64_t v = pp[c];
         const float vm = lo_f(v), vs = __uint_as_float(hi_u(v) & ~kValid);
         if (vm == neg_inf() && vs == 0.0f) continue;            // empty chunk
-        S = S + double(vs) * exp2((double(vm) - double(M)) * c64);
+        S = S + double(vs) * rescale_d(vm, M, a.c32);
     }
-    if (!(S > 0.0 && S < INFINITY) || !(M > neg_inf() && M < INFINITY)) atomicMin(&sh.badrow, r);
+    if (!ok || !(S > 0.0 && S < INFINITY) || !(M > neg_inf() && M < INFINITY)) atomicOr(&sh.bad, 1);
     sh.M[r] = M;
     sh.S[r] = S;
 }
@@ -498,32 +563,45 @@ __device__ void merge_row_sampled(const VerifyArgs &a, const uint64_t *pp, int r
 __device__ void merge_row_greedy(const VerifyArgs &a, const uint64_t *pp, int r, Smem &sh) {
     float best = neg_inf();
     int bi = -1, nan = 0;
+    bool ok = true;
     for (int c = 0; c < a.nc1; ++c) {               // ascending chunks: first maximum wins
         const uint64_t v = ld_coherent(pp + c);
+        ok &= valid(v);
         const int vi = int(hi_u(v) & ~kValid) - 2;
         if (vi == kNanIdx) { nan = 1; continue; }
         merge_am(best, bi, lo_f(v), vi);
     }
-    if (nan || bi < 0 || best == __builtin_inff()) atomicMin(&sh.badrow, r);
+    if (!ok || nan || bi < 0 || best == __builtin_inff()) atomicOr(&sh.bad, 1);
     sh.A[r] = bi;
 }
 
-// Find the request's first rejection, merging rows in order as their chunk
-// partials arrive: the decision needs rows 0..j only, so it is final as soon as
-// a rejection is found among the rows merged so far (or all n+1 rows are in).
-// A bad row counts here only if it comes no later than the first rejection,
-// so every workgroup of the request reaches the same conclusion; bad rows
-// after it are reported by the cleanup item.
-template <bool SAMPLED, int ES>
-__device__ int decide(const VerifyArgs &a, int b, int w, Decision &d, Smem &sh) {
+// Unnormalised target probability 2^(z*c - R) of a value z in a row with
+// maximum m, in fp64, against the same reference the row sum S used.
+__device__ __forceinline__ double target_prob(float z, float m, float c) {
+    const float R = m * c;
+    return finitef(R) ? exp2(double(z) * double(c) - double(R)) : exp2((double(z) - double(m)) * double(c));
+}
+// log-sum-exp of the row at temperature T: ln sum_v e^(z_v/T) = R ln 2 + ln S.
+__device__ __forceinline__ double row_lse(float m, double S, float c, double T) {
+    const float R = m * c;
+    return finitef(R) ? double(R) * 0.69314718055994530942 + log(S) : double(m) / T + log(S);
+}
+
+// All chunk partials of the request are complete (written by the previous
+// launch): merge every row, run the accept tests, find the first rejection.
+// Returns false (outputs reported by workgroup 0) for a data error or an
+// invalid verify length (then *arrive is false: no workgroup counts itself).
+template <int ES>
+__device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, bool &arrive, Smem &sh) {
     const int G = a.G, G1 = G + 1;
     const int n = verify_len(a, b);
     d.n = n;
+    arrive = false;
     if (n < 0 || n > G) {
         if (w == 0) write_error(a, b);
-        return kNoRequest;
+        return false;
     }
-    // Per-position inputs do not depend on the row pass: issue them first.
+    arrive = true;
     const int k = threadIdx.x;
     int xk = 0;
     float zx = 0.0f, qx = 0.0f, uk = 0.0f;
@@ -531,94 +609,70 @@ __device__ int decide(const VerifyArgs &a, int b, int w, Decision &d, Smem &sh) 
     if (k < n) {
         xk = a.x[size_t(b) * G + k];
         xbad = xk < 0 || xk >= a.V;
-        if (SAMPLED) {
-            if (!xbad) {
-                zx = load_elem<ES>(a.logits, (size_t(b) * G1 + k) * size_t(a.V) + size_t(xk));
-                qx = a.q[(size_t(b) * G + k) * size_t(a.V) + size_t(xk)];
-            }
-            uk = a.u[size_t(b) * G1 + k];
+        if (!xbad) {
+            zx = load_elem<ES>(a.logits, (size_t(b) * G1 + k) * size_t(a.V) + size_t(xk));
+            qx = a.q[(size_t(b) * G + k) * size_t(a.V) + size_t(xk)];
         }
+        uk = a.u[size_t(b) * G1 + k];
     }
-    if (threadIdx.x == 0) { sh.jmin = n; sh.badrow = 0x7fffffff; }
-    if (__syncthreads_or(xbad)) {
-        if (w == 0) write_error(a, b);
-        return kReported;
-    }
+    if (threadIdx.x == 0) { sh.jmin = n; sh.bad = 0; }
+    __syncthreads();
     const uint64_t *part = partials(a, b);
-    const double T64 = double(a.T);
-    int next = 0;                                  // rows [0, next) are merged and tested
-    for (uint32_t spins = 0;;) {
-        if (threadIdx.x == 0) sh.t1 = n + 1;
-        __syncthreads();
-        const int r = next + int(threadIdx.x);
-        if (r <= n) {
-            bool rv = true;
-            for (int c = 0; c < a.nc1; ++c) rv = rv && valid(ld_coherent(part + size_t(r) * a.nc1 + c));
-            if (!rv) atomicMin(&sh.t1, r);
-        }
-        __syncthreads();
-        const int p = sh.t1;                       // rows [next, p) are all written
-        if (r < p) {
-            if (SAMPLED) merge_row_sampled(a, part + size_t(r) * a.nc1, r, sh);
-            else merge_row_greedy(a, part + size_t(r) * a.nc1, r, sh);
-        }
-        __syncthreads();
-        if (k >= next && k < p && k < n) {
-            if (SAMPLED) {
-                const double pk = exp((double(zx) - double(sh.M[k])) / T64) / sh.S[k];
-                const bool acc = (qx > 0.0f) ? (double(uk) < pk / double(qx)) : (pk > 0.0);
-                if (!acc) atomicMin(&sh.jmin, k);
-            } else if (xk != sh.A[k]) {
-                atomicMin(&sh.jmin, k);
-            }
-        }
-        __syncthreads();
-        const int jm = sh.jmin, br = sh.badrow;
-        if (br < p && br <= jm) {                  // a bad row before (or at) the first rejection
-            if (w == 0) write_error(a, b);
-            return kReported;
-        }
-        if (jm < p) break;                         // rejection among merged rows, or all rows merged
-        if (p > next) { next = p; continue; }
-        if (++spins > a.spin_limit) {
-            if (w == 0) write_error(a, b);
-            return kReported;
-        }
-        __builtin_amdgcn_s_sleep(4);
+    for (int r = threadIdx.x; r <= n; r += kWG) merge_row_sampled(a, part + size_t(r) * a.nc1, r, sh);
+    if (xbad) atomicOr(&sh.bad, 1);
+    __syncthreads();
+    if (k < n && !xbad) {
+        const double pk = target_prob(zx, sh.M[k], a.c32) / sh.S[k];
+        const bool acc = (qx > 0.0f) ? (double(uk) < pk / double(qx)) : (pk > 0.0);
+        if (!acc) atomicMin(&sh.jmin, k);
+    }
+    __syncthreads();
+    if (sh.bad) {
+        if (w == 0) write_error(a, b);
+        return false;
     }
     const int j = sh.jmin;
     d.j = j;
     d.resid = j < n;
-    if (SAMPLED) {
-        d.m = sh.M[j];
-        d.inv_s = float(1.0 / sh.S[j]);
-    }
+    d.m = sh.M[j];
+    d.inv_s = float(1.0 / sh.S[j]);
     if (w == 0) {
         for (int t = threadIdx.x; t < G1; t += kWG) {
-            int v = -1;
-            if (t < j) v = a.x[size_t(b) * G + t];
-            else if (t == j && !SAMPLED) v = sh.A[j];
-            if (t != j || !SAMPLED) st_out(a.out_tok + size_t(b) * G1 + t, v);
+            if (t < j) a.out_tok[size_t(b) * G1 + t] = a.x[size_t(b) * G + t];
+            else if (t > j) a.out_tok[size_t(b) * G1 + t] = -1;
         }
-        if (threadIdx.x == 0) st_out(a.out_acc + b, j);
+        if (threadIdx.x == 0) a.out_acc[b] = j;
     }
-    return kDecided;
+    return true;
 }
 
-__device__ __forceinline__ unsigned *done_flag(const VerifyArgs &a, int b) {
-    return reinterpret_cast<unsigned *>(a.ws + size_t(b) * kSlotBytes) + 1;
+// Diagnostics of request b (only when requested), from the merged rows.
+template <int ES>
+__device__ void write_diag(const VerifyArgs &a, int b, bool ok, int n, Smem &sh) {
+    const int G = a.G, G1 = G + 1;
+    const float qnan = __builtin_nanf("");
+    const double T64 = double(a.T);
+    for (int t = threadIdx.x; t < G1; t += kWG) {
+        float lse = qnan, pv = qnan, qv = qnan;
+        if (ok && t <= n) {
+            lse = float(row_lse(sh.M[t], sh.S[t], a.c32, T64));
+            if (t < n) {
+                const int xt = a.x[size_t(b) * G + t];
+                const float zt = load_elem<ES>(a.logits, (size_t(b) * G1 + t) * size_t(a.V) + size_t(xt));
+                qv = a.q[(size_t(b) * G + t) * size_t(a.V) + size_t(xt)];
+                pv = float(target_prob(zt, sh.M[t], a.c32) / sh.S[t]);
+            }
+        }
+        if (a.d_lse) a.d_lse[size_t(b) * G1 + t] = lse;
+        if (t < G) {
+            if (a.d_p) a.d_p[size_t(b) * G + t] = pv;
+            if (a.d_q) a.d_q[size_t(b) * G + t] = qv;
+        }
+    }
+    if (!ok && threadIdx.x == 0 && a.d_r) a.d_r[b] = qnan;
 }
 
-constexpr unsigned kDoneOk = 1, kDoneError = 2;
-
-// Outputs of request b are final (after every store that wrote them completed).
-__device__ void publish_done(const VerifyArgs &a, int b, unsigned v) {
-    stores_complete();
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_store(done_flag(a, b), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Last draw workgroup of request b: locate u * R and write the token.
+// Last workgroup of request b: locate u * R and write the token.
 template <int ES, bool ALZ, bool ALQ>
 __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, const void *zrow, const float *qrow,
                              Smem &sh) {
@@ -721,202 +775,127 @@ __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, cons
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        st_out(a.out_tok + size_t(b) * G1 + d.j, sh.y);
-        if (a.d_r) st_out(a.d_r + b, resid ? float(sh.R) : -1.0f);
+        a.out_tok[size_t(b) * G1 + d.j] = sh.y;
+        if (a.d_r) a.d_r[b] = resid ? float(sh.R) : -1.0f;
     }
 }
 
+// Request pass (after the row pass has completed): workgroup w of request b
+// decides the request, streams sub-tiles [w*spw, (w+1)*spw) of the draw row,
+// and the last of the request's nc2 workgroups selects the token and zeroes
+// the request's partials and masses.
 template <int ES, bool ALZ, bool ALQ>
 __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh) {
     Decision d;
-    const int st = decide<true, ES>(a, b, w, d, sh);
-    if (st == kNoRequest) return;
-    if (st == kReported) {
-        if (arrive_last(draw_counter(a, b), unsigned(a.nc2), sh)) publish_done(a, b, kDoneError);
-        return;
-    }
+    bool arrive;
+    const bool ok = decide<ES>(a, b, w, d, arrive, sh);
+    if (!arrive) return;
     const int G1 = a.G + 1;
-    const void *zrow = static_cast<const char *>(a.logits) + (size_t(b) * G1 + d.j) * size_t(a.V) * ES;
-    const float *qrow = d.resid ? a.q + (size_t(b) * a.G + d.j) * size_t(a.V) : nullptr;
-    uint64_t *mass = reinterpret_cast<uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
-    const int s_end = min(a.nsub, (w + 1) * a.spw);
-    for (int s0 = w * a.spw; s0 < s_end; s0 += kSubBatch) {
-        double v[2 * kSubBatch], ex[2 * kSubBatch], tot[2 * kSubBatch];
+    const bool diag = a.d_lse || a.d_p || a.d_q || a.d_r;
+    const void *zrow = nullptr;
+    const float *qrow = nullptr;
+    if (ok) {
+        zrow = static_cast<const char *>(a.logits) + (size_t(b) * G1 + d.j) * size_t(a.V) * ES;
+        qrow = d.resid ? a.q + (size_t(b) * a.G + d.j) * size_t(a.V) : nullptr;
+        uint64_t *mass = reinterpret_cast<uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
+        const int s_end = min(a.nsub, (w + 1) * a.spw);
+        for (int s0 = w * a.spw; s0 < s_end; s0 += kSubBatch) {
+            double v[2 * kSubBatch], ex[2 * kSubBatch], tot[2 * kSubBatch];
 #pragma unroll
-        for (int i = 0; i < kSubBatch; ++i) {
-            double rs = 0.0, ps = 0.0;
-            if (s0 + i < s_end) sub_sums<ES, ALZ, ALQ>(zrow, qrow, a.V, s0 + i, d.m, a.c32, d.inv_s, d.resid, rs, ps);
-            v[i] = rs;
-            v[kSubBatch + i] = ps;
-        }
-        wg_excl_scan<2 * kSubBatch>(v, ex, tot, sh);
-        if (int(threadIdx.x) < kSubBatch && s0 + int(threadIdx.x) < s_end) {
-            const int i = threadIdx.x;
-            st_coherent(mass + 2 * (s0 + i), uint64_t(__double_as_longlong(tot[i])));
-            st_coherent(mass + 2 * (s0 + i) + 1, uint64_t(__double_as_longlong(tot[kSubBatch + i])));
+            for (int i = 0; i < kSubBatch; ++i) {
+                double rs = 0.0, ps = 0.0;
+                if (s0 + i < s_end) sub_sums<ES, ALZ, ALQ>(zrow, qrow, a.V, s0 + i, d.m, a.c32, d.inv_s, d.resid, rs, ps);
+                v[i] = rs;
+                v[kSubBatch + i] = ps;
+            }
+            wg_excl_scan<2 * kSubBatch>(v, ex, tot, sh);
+            if (int(threadIdx.x) < kSubBatch && s0 + int(threadIdx.x) < s_end) {
+                const int i = threadIdx.x;
+                st_coherent(mass + 2 * (s0 + i), uint64_t(__double_as_longlong(tot[i])));
+                st_coherent(mass + 2 * (s0 + i) + 1, uint64_t(__double_as_longlong(tot[kSubBatch + i])));
+            }
         }
     }
-    if (arrive_last(draw_counter(a, b), unsigned(a.nc2), sh)) {
+    if (!arrive_last(draw_counter(a, b), unsigned(a.nc2), sh)) return;
+    if (ok) {
         final_select<ES, ALZ, ALQ>(a, b, d, zrow, qrow, sh);
         uint64_t *m = reinterpret_cast<uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
         for (int i = threadIdx.x; i < 2 * a.nsub; i += kWG) st_coherent(m + i, 0ull);
-        publish_done(a, b, kDoneOk);
     }
+    if (diag) write_diag<ES>(a, b, ok, d.n, sh);
+    uint64_t *part = partials(a, b);
+    for (int i = threadIdx.x; i < (d.n + 1) * a.nc1; i += kWG) part[i] = 0ull;
 }
 
-// One workgroup per request (T == 0): the emitted token is the argmax of row j.
-template <int ES>
+// One workgroup per request (T == 0), after the request's row items: waits
+// for every read row, emits the argmax match, and zeroes the partials.
 __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
-    Decision d;
-    const int st = decide<false, ES>(a, b, 0, d, sh);
-    if (st == kNoRequest) return;
-    publish_done(a, b, st == kDecided ? kDoneOk : kDoneError);
-}
-
-// Last workgroup of request b (placed at the end of the grid): waits for the
-// outputs to be final and for every read row's partials, reports a data error
-// in a row after the decision, writes the diagnostics, and zeroes the
-// request's partials and flag.
-template <bool SAMPLED, int ES>
-__device__ void cleanup_item(const VerifyArgs &a, int b, Smem &sh) {
     const int G = a.G, G1 = G + 1;
     const int n = verify_len(a, b);
-    if (n < 0 || n > G) return;
-    const bool diag = SAMPLED && (a.d_lse || a.d_p || a.d_q);
-    unsigned *flag = done_flag(a, b);
-    if (threadIdx.x == 0) {
-        unsigned f = 0;
-        for (uint32_t spins = 0; (f = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0u;
-             ++spins) {
-            if (spins >= a.spin_limit) break;
-            __builtin_amdgcn_s_sleep(4);
-        }
-        sh.flagv = int(f);
-        sh.badrow = 0x7fffffff;
-    }
-    __syncthreads();
-    const unsigned fv = unsigned(sh.flagv);
-    if (fv == 0u || !wait_partials(a, b, n)) { write_error(a, b); return; }
+    if (n < 0 || n > G) { write_error(a, b); return; }
+    const int k = threadIdx.x;
+    int xk = 0;
+    if (k < n) xk = a.x[size_t(b) * G + k];
+    if (threadIdx.x == 0) { sh.jmin = n; sh.bad = 0; }
+    if (!wait_partials(a, b, n)) { write_error(a, b); return; }
     const uint64_t *part = partials(a, b);
-    for (int r = threadIdx.x; r <= n; r += kWG) {
-        if (SAMPLED) merge_row_sampled(a, part + size_t(r) * a.nc1, r, sh);
-        else merge_row_greedy(a, part + size_t(r) * a.nc1, r, sh);
+    for (int r = threadIdx.x; r <= n; r += kWG) merge_row_greedy(a, part + size_t(r) * a.nc1, r, sh);
+    __syncthreads();
+    if (k < n) {
+        if (xk < 0 || xk >= a.V) atomicOr(&sh.bad, 1);
+        else if (xk != sh.A[k]) atomicMin(&sh.jmin, k);
     }
     __syncthreads();
-    const bool bad = sh.badrow <= n || fv == kDoneError;
-    if (bad) {
+    if (sh.bad) {
         write_error(a, b);
-    } else if (diag) {
-        char *rs = reinterpret_cast<char *>(a.ws + a.lay.rowstat) + size_t(b) * G1 * 16;
-        for (int t = threadIdx.x; t <= n; t += kWG) {
-            *reinterpret_cast<float *>(rs + size_t(t) * 16) = sh.M[t];
-            *reinterpret_cast<double *>(rs + size_t(t) * 16 + 8) = sh.S[t];
+    } else {
+        const int j = sh.jmin;
+        for (int t = threadIdx.x; t < G1; t += kWG) {
+            int v = -1;
+            if (t < j) v = a.x[size_t(b) * G + t];
+            else if (t == j) v = sh.A[j];
+            a.out_tok[size_t(b) * G1 + t] = v;
         }
+        if (threadIdx.x == 0) a.out_acc[b] = j;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < (n + 1) * a.nc1; i += kWG) st_coherent(partials(a, b) + i, 0ull);
-    if (threadIdx.x == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t *pw = partials(a, b);
+    for (int i = threadIdx.x; i < (n + 1) * a.nc1; i += kWG) st_coherent(pw + i, 0ull);
 }
 
 // ------------------------------------------------------------- kernels
 
-enum { kRowItem = 0, kRequestItem = 1, kCleanupItem = 2 };
-
-// Grid order: row waves 0..k0-1 (wave k = row k of every request, request-major
-// then chunk), the request items, row waves k0..G, then one cleanup item per
-// request.  Row k of every request is streamed before row k+1, so most
-// decisions (which need rows 0..j) are ready while later rows still stream.
-__device__ __forceinline__ int map_item(const VerifyArgs &a, int i, int per_req, int &b, int &local) {
-    const long W = long(a.B) * a.nc1;                 // one row wave
-    const long rows = long(a.G + 1) * W;
-    const long reqs = long(a.B) * per_req;
-    long ri;                                          // index among row items
-    if (a.mode == 1) {
-        ri = i;
-    } else if (a.mode == 2) {
-        b = i / per_req; local = i - b * per_req; return kRequestItem;
-    } else if (a.mode == 3) {
-        b = i; local = 0; return kCleanupItem;
-    } else {
-        const long head = long(a.k0) * W;
-        if (i < head) ri = i;
-        else if (i < head + reqs) { const long r = i - head; b = int(r / per_req); local = int(r - long(b) * per_req); return kRequestItem; }
-        else if (i < rows + reqs) ri = i - reqs;
-        else { b = int(i - rows - reqs); local = 0; return kCleanupItem; }
-    }
-    const int k = int(ri / W);
-    const int rem = int(ri - long(k) * W);
-    b = rem / a.nc1;
-    local = k * a.nc1 + (rem - b * a.nc1);            // row-item local index: k * nc1 + c
-    return kRowItem;
-}
-
-template <int ES, bool ALZ, bool ALQ>
-__global__ __launch_bounds__(kWG) void k_verify_sampled(VerifyArgs a) {
+// Row pass of a sampled verify: one workgroup per (request, row, chunk).
+template <int ES, bool AL>
+__global__ __launch_bounds__(kWG) void k_rows_sampled(VerifyArgs a) {
     __shared__ Smem sh;
-    int b, local;
-    const int kind = map_item(a, int(blockIdx.x), a.nc2, b, local);
-    if (kind == kRowItem) row_item_sampled<ES, ALZ>(a, b, local, sh);
-    else if (kind == kRequestItem) request_item_sampled<ES, ALZ, ALQ>(a, b, local, sh);
-    else cleanup_item<true, ES>(a, b, sh);
+    const int g1 = (a.G + 1) * a.nc1;
+    const int b = int(blockIdx.x) / g1;
+    row_item_sampled<ES, AL>(a, b, int(blockIdx.x) - b * g1, sh);
 }
 
+// Request pass of a sampled verify: nc2 workgroups per request.
+template <int ES, bool ALZ, bool ALQ>
+__global__ __launch_bounds__(kWG) void k_requests_sampled(VerifyArgs a) {
+    __shared__ Smem sh;
+    const int b = int(blockIdx.x) / a.nc2;
+    request_item_sampled<ES, ALZ, ALQ>(a, b, int(blockIdx.x) - b * a.nc2, sh);
+}
+
+// Greedy verify: row items (request-major), then one request item per
+// request (mode 0); or only the row items (mode 1) / request items (mode 2).
 template <int ES, bool AL>
 __global__ __launch_bounds__(kWG) void k_verify_greedy(VerifyArgs a) {
     __shared__ Smem sh;
-    int b, local;
-    const int kind = map_item(a, int(blockIdx.x), 1, b, local);
-    if (kind == kRowItem) row_item_greedy<ES, AL>(a, b, local, sh);
-    else if (kind == kRequestItem) request_item_greedy<ES>(a, b, sh);
-    else cleanup_item<false, ES>(a, b, sh);
-}
-
-// Diagnostics (parity checks only): per request, from the row statistics the
-// cleanup item stored; NaN for rows not read and for requests with an error.
-template <int ES>
-__global__ __launch_bounds__(kWG) void k_verify_diag(VerifyArgs a) {
-    const int b = blockIdx.x;
-    const int G = a.G, G1 = G + 1;
-    const float qnan = __builtin_nanf("");
-    const bool bad = a.out_acc[b] < 0;
-    const int n = bad ? -1 : verify_len(a, b);
-    char *rs = reinterpret_cast<char *>(a.ws + a.lay.rowstat) + size_t(b) * G1 * 16;
-    const double T64 = double(a.T);
-    for (int t = threadIdx.x; t < G1; t += kWG) {
-        float lse = qnan, pv = qnan, qv = qnan;
-        if (t <= n) {
-            const float M = *reinterpret_cast<const float *>(rs + size_t(t) * 16);
-            const double S = *reinterpret_cast<const double *>(rs + size_t(t) * 16 + 8);
-            // last reader: leave the workspace zero-filled
-            *reinterpret_cast<uint64_t *>(rs + size_t(t) * 16) = 0ull;
-            *reinterpret_cast<uint64_t *>(rs + size_t(t) * 16 + 8) = 0ull;
-            lse = float(double(M) / T64 + log(S));
-            if (t < n) {
-                const int xt = a.x[size_t(b) * G + t];
-                const float zt = load_elem<ES>(a.logits, (size_t(b) * G1 + t) * size_t(a.V) + size_t(xt));
-                qv = a.q[(size_t(b) * G + t) * size_t(a.V) + size_t(xt)];
-                pv = float(exp((double(zt) - double(M)) / T64) / S);
-            }
-        }
-        if (a.d_lse) a.d_lse[size_t(b) * G1 + t] = lse;
-        if (t < G) {
-            if (a.d_p) a.d_p[size_t(b) * G + t] = pv;
-            if (a.d_q) a.d_q[size_t(b) * G + t] = qv;
-        }
+    const int g1 = (a.G + 1) * a.nc1;
+    const long rows = long(a.B) * g1;
+    const long i = blockIdx.x;
+    if (a.mode == 2 || (a.mode == 0 && i >= rows)) {
+        request_item_greedy(a, int(a.mode == 2 ? i : i - rows), sh);
+    } else {
+        const int b = int(i / g1);
+        row_item_greedy<ES, AL>(a, b, int(i - long(b) * g1), sh);
     }
-    if (threadIdx.x == 0 && bad && a.d_r) a.d_r[b] = qnan;
-}
-
-template <int ES, bool ALZ, bool ALQ>
-int launch_s(const VerifyArgs &a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((k_verify_sampled<ES, ALZ, ALQ>), dim3(grid), dim3(kWG), 0, st, a);
-    return int(hipGetLastError());
-}
-
-template <int ES, bool AL>
-int launch_g(const VerifyArgs &a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((k_verify_greedy<ES, AL>), dim3(grid), dim3(kWG), 0, st, a);
-    return int(hipGetLastError());
 }
 
 template <typename K>
@@ -926,44 +905,47 @@ int occ(K kernel, int *n) {
 
 }  // namespace
 
-int launch_verify_sampled(const VerifyArgs &a, bool az, bool aq, int esize, int grid, void *stream) {
+int launch_rows_sampled(const VerifyArgs &a, bool az, int esize, int grid, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (esize == 2) {
-        if (az && aq) return launch_s<2, true, true>(a, grid, st);
-        if (az) return launch_s<2, true, false>(a, grid, st);
-        return launch_s<2, false, false>(a, grid, st);
+        if (az) hipLaunchKernelGGL((k_rows_sampled<2, true>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_rows_sampled<2, false>), dim3(grid), dim3(kWG), 0, st, a);
+    } else {
+        if (az) hipLaunchKernelGGL((k_rows_sampled<4, true>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_rows_sampled<4, false>), dim3(grid), dim3(kWG), 0, st, a);
     }
-    if (az && aq) return launch_s<4, true, true>(a, grid, st);
-    if (az) return launch_s<4, true, false>(a, grid, st);
-    return launch_s<4, false, false>(a, grid, st);
+    return int(hipGetLastError());
+}
+
+int launch_requests_sampled(const VerifyArgs &a, bool az, bool aq, int esize, int grid, void *stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (esize == 2) {
+        if (az && aq) hipLaunchKernelGGL((k_requests_sampled<2, true, true>), dim3(grid), dim3(kWG), 0, st, a);
+        else if (az) hipLaunchKernelGGL((k_requests_sampled<2, true, false>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_requests_sampled<2, false, false>), dim3(grid), dim3(kWG), 0, st, a);
+    } else {
+        if (az && aq) hipLaunchKernelGGL((k_requests_sampled<4, true, true>), dim3(grid), dim3(kWG), 0, st, a);
+        else if (az) hipLaunchKernelGGL((k_requests_sampled<4, true, false>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_requests_sampled<4, false, false>), dim3(grid), dim3(kWG), 0, st, a);
+    }
+    return int(hipGetLastError());
 }
 
 int launch_verify_greedy(const VerifyArgs &a, bool az, int esize, int grid, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (esize == 2) return az ? launch_g<2, true>(a, grid, st) : launch_g<2, false>(a, grid, st);
-    return az ? launch_g<4, true>(a, grid, st) : launch_g<4, false>(a, grid, st);
-}
-
-int launch_verify_diag(const VerifyArgs &a, int esize, void *stream) {
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (esize == 2) hipLaunchKernelGGL(k_verify_diag<2>, dim3(a.B), dim3(kWG), 0, st, a);
-    else hipLaunchKernelGGL(k_verify_diag<4>, dim3(a.B), dim3(kWG), 0, st, a);
+    if (esize == 2) {
+        if (az) hipLaunchKernelGGL((k_verify_greedy<2, true>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_verify_greedy<2, false>), dim3(grid), dim3(kWG), 0, st, a);
+    } else {
+        if (az) hipLaunchKernelGGL((k_verify_greedy<4, true>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_verify_greedy<4, false>), dim3(grid), dim3(kWG), 0, st, a);
+    }
     return int(hipGetLastError());
 }
 
-int verify_occupancy(bool sampled, bool az, bool aq, int esize, int *n) {
-    if (!sampled) {
-        if (esize == 2) return az ? occ(k_verify_greedy<2, true>, n) : occ(k_verify_greedy<2, false>, n);
-        return az ? occ(k_verify_greedy<4, true>, n) : occ(k_verify_greedy<4, false>, n);
-    }
-    if (esize == 2) {
-        if (az && aq) return occ(k_verify_sampled<2, true, true>, n);
-        if (az) return occ(k_verify_sampled<2, true, false>, n);
-        return occ(k_verify_sampled<2, false, false>, n);
-    }
-    if (az && aq) return occ(k_verify_sampled<4, true, true>, n);
-    if (az) return occ(k_verify_sampled<4, true, false>, n);
-    return occ(k_verify_sampled<4, false, false>, n);
+int greedy_occupancy(bool az, int esize, int *n) {
+    if (esize == 2) return az ? occ(k_verify_greedy<2, true>, n) : occ(k_verify_greedy<2, false>, n);
+    return az ? occ(k_verify_greedy<4, true>, n) : occ(k_verify_greedy<4, false>, n);
 }
 
 }  // namespace sv
