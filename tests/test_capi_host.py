@@ -45,10 +45,9 @@ def test_status_strings():
 def test_workspace_query():
     w = _capi.verify_workspace_bytes(64, 15, 129280, _capi.SPEC_DTYPE_BF16)
     # fixed 1 MiB counter region + partials 64*16 rows*8 chunks*8 B + masses 64*64 sub-tiles*16 B
-    # + row statistics 64*16 rows*16 B
-    assert w == (1 << 20) + 65536 + 65536 + 16384
+    assert w == (1 << 20) + 65536 + 65536
     # the counter region does not move with the shape
-    assert _capi.verify_workspace_bytes(1, 0, 1, _capi.SPEC_DTYPE_BF16) == (1 << 20) + 3 * 256
+    assert _capi.verify_workspace_bytes(1, 0, 1, _capi.SPEC_DTYPE_BF16) == (1 << 20) + 2 * 256
     assert _capi.verify_workspace_bytes(64, 15, 129280, _capi.SPEC_DTYPE_F32) >= w
     assert _capi.verify_workspace_bytes(0, 15, 100, 1) == 0
     assert _capi.verify_workspace_bytes(1, -1, 100, 1) == 0
