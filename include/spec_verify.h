@@ -62,10 +62,12 @@ typedef void *spec_stream_t;
 #define SPEC_MAX_SCHEDULE_CANDIDATES 4096 /* B * G <= 4096 for spec_schedule              */
 
 /*
- * Optional diagnostics of spec_verify (for parity checks; they cost extra
- * stores, keep them NULL on a timed path).  Each pointer may be NULL.  All
- * device pointers.  Entries that a request does not compute are set to NaN;
- * for a request with a data error every entry is NaN.
+ * Optional diagnostics of spec_verify.  Each field may be NULL.
+ *
+ * The four arrays are for parity checks (they cost extra stores; keep them
+ * NULL on a timed path).  Device pointers.  Entries that a request does not
+ * compute are set to NaN; for a request with a data error every entry is NaN.
+ * Temperature 0 writes none of them.
  *
  *   target_lse [B, G+1]  m_k/T + ln S_k of each read target row k <= len_b
  *   p_draft    [B, G]    p_k(x_k), the target probability of draft k, k < len_b
@@ -73,13 +75,18 @@ typedef void *spec_stream_t;
  *   resid_mass [B]       R = sum_v max(p_j(v) - q_j(v), 0) at the rejection
  *                        row j; -1 when every verified draft was accepted
  *
- * Temperature 0 writes none of them.
+ * row_pass_event is a hipEvent_t (opaque) created by the caller, for timing:
+ * spec_verify records it on `stream` right after the launch of the pass over
+ * the target rows (T > 0 always; T == 0 after the row launch when the call is
+ * split in two launches, else after its single launch).  It costs one event
+ * record and no extra memory traffic.
  */
 typedef struct {
     float *target_lse;
     float *p_draft;
     float *q_draft;
     float *resid_mass;
+    void *row_pass_event;
 } spec_verify_diag_t;
 
 /*

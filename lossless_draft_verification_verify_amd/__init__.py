@@ -63,13 +63,16 @@ def _workspace(device, stream_handle, nbytes):
 
 
 def verify(target_logits, draft_probs, draft_tokens, uniforms, temperature, verify_len=None, *,
-           out_accepted=None, out_tokens=None, diag=False, workspace=None):
+           out_accepted=None, out_tokens=None, diag=False, workspace=None, row_pass_event=None):
     """Verify a batch of draft blocks on the current stream of target_logits' device.
 
     target_logits [B, G+1, V] bf16/fp32; draft_probs [B, G, V] fp32 (None at T=0);
     draft_tokens [B, G] int32; uniforms [B, G+1] fp32 (None at T=0);
     verify_len [B] int32 or None.  Returns (accepted [B], tokens [B, G+1]) int32,
     plus a dict of diagnostics when diag=True.  Asynchronous like any kernel.
+    row_pass_event: a torch.cuda.Event, or a raw hipEvent_t handle (int), that
+    the library records right after the launch of the row pass (for timing
+    that kernel alone).
     """
     z = target_logits
     if not isinstance(z, torch.Tensor) or z.dim() != 3:
@@ -94,12 +97,21 @@ def verify(target_logits, draft_probs, draft_tokens, uniforms, temperature, veri
     stream = torch.cuda.current_stream(dev).cuda_stream
     d = None
     dg = None
+    ev = 0
+    if isinstance(row_pass_event, int):
+        ev = row_pass_event
+    elif row_pass_event is not None:
+        if row_pass_event.cuda_event == 0:          # torch creates the event on its first record
+            row_pass_event.record(torch.cuda.current_stream(dev))
+        ev = row_pass_event.cuda_event
     if diag:
         dg = {"target_lse": torch.empty(B, G1, dtype=f32, device=dev),
               "p_draft": torch.empty(B, G, dtype=f32, device=dev),
               "q_draft": torch.empty(B, G, dtype=f32, device=dev),
               "resid_mass": torch.empty(B, dtype=f32, device=dev)}
-        d = _capi.DiagT(*(dg[k].data_ptr() for k in ("target_lse", "p_draft", "q_draft", "resid_mass")))
+        d = _capi.DiagT(*(dg[k].data_ptr() for k in ("target_lse", "p_draft", "q_draft", "resid_mass")), ev)
+    elif ev:
+        d = _capi.DiagT(0, 0, 0, 0, ev)
     nbytes = _capi.verify_workspace_bytes(B, G, V, code)
     ws = workspace if workspace is not None else _workspace(dev, stream, nbytes)
     st = _capi.spec_verify(

@@ -41,6 +41,7 @@ class DiagT(ctypes.Structure):
         ("p_draft", ctypes.c_void_p),
         ("q_draft", ctypes.c_void_p),
         ("resid_mass", ctypes.c_void_p),
+        ("row_pass_event", ctypes.c_void_p),
     ]
 
 

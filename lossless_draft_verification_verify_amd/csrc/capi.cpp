@@ -31,7 +31,7 @@ spec_status_t check_verify_shape(int64_t B, int64_t G, int64_t V, int es) {
     if (B > SPEC_MAX_BATCH || G > SPEC_MAX_DRAFTS || V > SPEC_MAX_VOCAB) return SPEC_ERR_UNSUPPORTED;
     const int64_t nc1 = (V + sv::chunk_elems(es) - 1) / sv::chunk_elems(es);
     const int64_t nsub = (V + sv::kSub - 1) / sv::kSub;
-    const int64_t items = B * ((G + 1) * nc1 + nsub);
+    const int64_t items = B * ((G + 1) * nc1 + nsub);   // row waves + request workgroups
     if (items >= (int64_t(1) << 31)) return SPEC_ERR_UNSUPPORTED;
     if (B * (G + 1) > (int64_t(1) << 40) / V) return SPEC_ERR_UNSUPPORTED;
     return SPEC_OK;
@@ -112,7 +112,8 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
         !aligned(uniforms, 4) || !aligned(verify_len, 4) || !aligned(out_accepted, 4) ||
         !aligned(out_tokens, 4))
         return SPEC_ERR_MISALIGNED;
-    spec_verify_diag_t dg = {nullptr, nullptr, nullptr, nullptr};
+    spec_verify_diag_t dg = {nullptr, nullptr, nullptr, nullptr, nullptr};
+    hipEvent_t row_event = diag ? static_cast<hipEvent_t>(diag->row_pass_event) : nullptr;
     if (diag && sampled) dg = *diag;
     if (!aligned(dg.target_lse, 4) || !aligned(dg.p_draft, 4) || !aligned(dg.q_draft, 4) ||
         !aligned(dg.resid_mass, 4))
@@ -148,13 +149,15 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
     a.spin_limit = 1u << 20;
     const bool az = aligned(target_logits, 16) && (size_t(V) * es) % 16 == 0;
     const bool aq = aligned(draft_probs, 16) && V % 4 == 0;
-    const long g1 = long(G + 1) * a.nc1;
+    const long row_wgs = (long(B) * (G + 1) * a.nc1 + sv::kWaves - 1) / sv::kWaves;   // one wave per chunk
 
     if (sampled) {
         // Row pass, then request pass: nothing waits, each launch sized freely.
         a.spw = sv::kSubBatch;
         a.nc2 = (a.nsub + a.spw - 1) / a.spw;
-        if (sv::launch_rows_sampled(a, az, es, int(long(B) * g1), stream) != 0) return SPEC_ERR_DEVICE;
+        if (sv::launch_rows_sampled(a, az, es, int(row_wgs), stream) != 0) return SPEC_ERR_DEVICE;
+        if (row_event && hipEventRecord(row_event, static_cast<hipStream_t>(stream)) != hipSuccess)
+            return SPEC_ERR_DEVICE;
         return sv::launch_requests_sampled(a, az, aq, es, int(long(B) * a.nc2), stream) == 0 ? SPEC_OK
                                                                                             : SPEC_ERR_DEVICE;
     }
@@ -167,10 +170,15 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
     a.nc2 = 1;
     if (long(B) <= cap / 2) {
         a.mode = 0;
-        return sv::launch_verify_greedy(a, az, es, int(long(B) * g1 + B), stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+        if (sv::launch_verify_greedy(a, az, es, int(row_wgs + B), stream) != 0) return SPEC_ERR_DEVICE;
+        if (row_event && hipEventRecord(row_event, static_cast<hipStream_t>(stream)) != hipSuccess)
+            return SPEC_ERR_DEVICE;
+        return SPEC_OK;
     }
     a.mode = 1;
-    if (sv::launch_verify_greedy(a, az, es, int(long(B) * g1), stream) != 0) return SPEC_ERR_DEVICE;
+    if (sv::launch_verify_greedy(a, az, es, int(row_wgs), stream) != 0) return SPEC_ERR_DEVICE;
+    if (row_event && hipEventRecord(row_event, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return SPEC_ERR_DEVICE;
     a.mode = 2;
     return sv::launch_verify_greedy(a, az, es, B, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
 }

@@ -8,15 +8,16 @@
 namespace sv {
 
 constexpr int kWG = 256;            // threads per workgroup: 4 wave64s
-constexpr int kVecPerThread = 8;    // 16-byte loads in flight per thread in the row pass
+constexpr int kWaves = kWG / 64;    // waves per workgroup
+constexpr int kRowVec = 4;          // 16-byte loads per lane of a row-pass chunk
 constexpr int kSubPerThread = 8;    // contiguous elements per thread in a draw sub-tile
 constexpr int kSub = kWG * kSubPerThread;   // elements per draw sub-tile (2048)
 constexpr int kSubBatch = 2;        // sub-tiles loaded together by a draw workgroup
-constexpr int kStage = 256;         // sub-tile masses staged in LDS at a time
 constexpr int kNanIdx = -2;         // greedy partial: chunk holds a NaN
 
-// Elements per row-pass chunk: 256 threads x 8 loads x 16 bytes.
-inline int chunk_elems(int esize) { return kWG * kVecPerThread * (16 / esize); }
+// Elements per row-pass chunk, the unit of one wave: 64 lanes x 4 loads x 16
+// bytes (2048 bf16 or 1024 fp32 values).
+inline int chunk_elems(int esize) { return 64 * kRowVec * (16 / esize); }
 
 // Workspace.  Between calls every byte the kernels use is zero: each slot is
 // reset by the last workgroup that reads it, so one zero-filled workspace stays
@@ -26,7 +27,11 @@ inline int chunk_elems(int esize) { return kWG * kVecPerThread * (16 / esize); }
 //   part     [B*(G+1)*nc1] u64 chunk partials, bit 63 set once written
 //            (sampled: low = max bits, high = sum bits | 1<<31;
 //             greedy:  low = max bits, high = (argmax + 2) | 1<<31);
-//   mass     [B*nsub] 2 u64: fp64 (residual mass, target mass) per sub-tile.
+//   mass     [B*nsub] 2 u64: fp64 (residual mass, target mass) per sub-tile;
+//   gx       [B*G] u64: the row pass's gather of draft k (sampled only):
+//            low = fp32 bits of z[b,k,x_k], high = bits of q[b,k,x_k];
+//   zero     256 bytes never written: the draft row a bonus draw reads in
+//            place of q (so the draw loads need no branch).
 
 constexpr int kMaxBatch = 65536;
 constexpr size_t kSlotBytes = 16;
@@ -34,8 +39,10 @@ constexpr size_t kCounterBytes = size_t(kMaxBatch) * kSlotBytes;
 constexpr uint32_t kValid = 0x80000000u;
 
 struct Layout {
+    size_t zero;
     size_t part;
     size_t mass;
+    size_t gx;
     size_t total;
 };
 
@@ -46,8 +53,10 @@ inline Layout make_layout(int64_t B, int64_t G, int64_t V, int esize) {
     const int64_t nsub = (V + kSub - 1) / kSub;
     Layout L;
     size_t o = kCounterBytes;
+    L.zero = o; o += 256;
     L.part = o; o += align256(size_t(B) * size_t(G + 1) * size_t(nc1) * 8);
     L.mass = o; o += align256(size_t(B) * size_t(nsub) * 16);
+    L.gx = o; o += align256(size_t(B) * size_t(G) * 8);
     L.total = o;
     return L;
 }
@@ -66,7 +75,7 @@ struct VerifyArgs {
     int32_t B, G, V;
     float T;          // temperature
     float c32;        // log2(e) / T, the fp32 exponent scale
-    int32_t nc1, ch1; // row-pass chunks per row, elements per chunk
+    int32_t nc1, ch1; // row-pass chunks (waves) per row, elements per chunk
     int32_t nsub;     // draw sub-tiles per row
     int32_t nc2, spw; // request workgroups per request, sub-tiles per workgroup
     int32_t mode;     // greedy kernel: 0 row items then request items; 1 row items only; 2 request items only

@@ -14,40 +14,43 @@
 // The work is a bandwidth-bound streaming reduction (no contraction, so no
 // MFMA).  Temperature > 0 runs as two launches on the caller's stream:
 //
-//   row pass       one workgroup per (request, row, 16384-element chunk):
-//                  8 x 16-byte loads in flight per thread, the chunk maximum,
-//                  then the sum of 2^((z - m) * log2(e)/T), merged across the
-//                  workgroup by wave butterflies and LDS; the (max, sum)
-//                  partial is one 64-bit store.  Nothing else, so the kernel
-//                  keeps few registers and full occupancy.
+//   row pass       one wave per (request, row, 2048-element chunk): four
+//                  16-byte streaming loads per lane, the chunk maximum, then
+//                  the sum of 2^((z - m) * log2(e)/T), both reduced across the
+//                  wave with DPP (no LDS, no barrier); lane 0 stores the
+//                  (max, sum) partial as one 64-bit word.  The wave whose chunk
+//                  holds draft token x_k also records z(x_k) and q(x_k), so the
+//                  request pass has no dependent gathers.
 //   request pass   nc2 workgroups per request, one per pair of 2048-element
 //                  sub-tiles of the draw row.  Each merges the request's chunk
-//                  partials per row in fp64, runs the accept tests and finds the
-//                  first rejection j (every workgroup of the request computes
-//                  the same result), then streams its sub-tiles of the one row
-//                  the final token is drawn from (target row j, plus draft row j
-//                  on a rejection) and writes fp64 sub-tile masses.  The last of
-//                  the request's workgroups to arrive (a counter) locates u * R
-//                  by a prefix over the masses, re-scans that one sub-tile,
-//                  writes the token, and zeroes every workspace word the
-//                  request used.
+//                  partials per row (16 lanes per row, fp64 sums), runs the
+//                  accept tests and finds the first rejection j (every
+//                  workgroup of the request computes the same result), then
+//                  streams its sub-tiles of the one row the final token is drawn
+//                  from (target row j, plus draft row j on a rejection) and
+//                  writes fp64 sub-tile masses.  The last of the request's
+//                  workgroups to arrive (a counter) locates u * R by a parallel
+//                  prefix over the masses, re-scans that one sub-tile, writes
+//                  the token, and zeroes every workspace word the request used.
 //
 // Nothing waits on anything inside a launch except the arrival counter, so
 // there are no spin loops on this path.  Temperature 0 (argmax) is one launch:
-// row items, then one item per request that polls its rows' partials (bounded
-// wait) — the host keeps those below half the resident capacity, else it
-// splits them into a second launch.
+// row waves, then one workgroup per request that polls its rows' partials
+// (bounded wait) — the host keeps those below half the resident capacity, else
+// it splits them into a second launch.
 //
 // Words handed between workgroups of one launch (sub-tile masses, the greedy
 // partials) use coherent device-scope stores and loads instead of device-scope
 // fences, which on this chip write back or invalidate the whole L2.
 //
-// Determinism: no floating-point atomics; every reduction has a fixed order;
-// the sub-tile masses and the final re-scan run the same code, so the sub-tile
-// the draw lands in is found exactly.  The library is compiled with
+// Determinism: no floating-point atomics; every reduction has a fixed order.
+// A sub-tile mass is the butterfly sum of its wave totals, which is bitwise the
+// total of the prefix scan the final re-scan runs over the same terms, so the
+// sub-tile the draw lands in is located exactly.  The library is compiled with
 // -ffp-contract=off.
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -81,13 +84,7 @@ __device__ __forceinline__ bool finitef(float x) { return x > -__builtin_inff() 
 __device__ __forceinline__ float rescale(float m1, float m0, float c) {
     if (m1 == -__builtin_inff()) return 0.0f;
     const float r1 = m1 * c, r0 = m0 * c;
-    return (finitef(r1) && finitef(r0)) ? __builtin_amdgcn_exp2f(r1 - r0) : __builtin_amdgcn_exp2f((m1 - m0) * c);
-}
-__device__ __forceinline__ double rescale_d(float m1, float m0, float c) {
-    if (m1 == -__builtin_inff()) return 0.0;
-    const float r1 = m1 * c, r0 = m0 * c;
-    return (finitef(r1) && finitef(r0)) ? exp2(double(r1) - double(r0))
-                                        : exp2((double(m1) - double(m0)) * double(c));
+    return (finitef(r1) && finitef(r0)) ? exp2_fast(r1 - r0) : exp2_fast((m1 - m0) * c);
 }
 
 template <int ES>
@@ -99,14 +96,22 @@ __device__ __forceinline__ float load_elem(const void *base, size_t i) {
     }
 }
 
+// Streaming 16-byte load: the logits are read once, so keep them from
+// displacing the cached workspace and draft rows.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
 // ------------------------------------------------ cross-workgroup publication
 //
-// Words one workgroup hands to another are written with coherent device-scope
-// stores and read with coherent device-scope loads (no whole-cache write-back
-// or invalidation, which a generic device-scope fence performs on every L2).
-// A chunk partial carries its own valid bit, so it needs no ordering at all.
-// Sub-tile masses are ordered before the arrival that publishes them by
-// waiting for the stores to complete.
+// Words one workgroup hands to another inside a launch are written with
+// coherent device-scope stores and read with coherent device-scope loads (no
+// whole-cache write-back or invalidation, which a generic device-scope fence
+// performs on every L2).  A greedy chunk partial carries its own valid bit, so
+// it needs no ordering at all.  Sub-tile masses are ordered before the arrival
+// that publishes them by waiting for the stores to complete.
 __device__ __forceinline__ void st_coherent(void *p, uint64_t v) {
     __hip_atomic_store(static_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -123,57 +128,111 @@ __device__ __forceinline__ void stores_complete() {
 __device__ __forceinline__ void st_out(int32_t *p, int32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_out(float *p, float v) {
-    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float(uint32_t(v)); }
 __device__ __forceinline__ uint32_t hi_u(uint64_t v) { return uint32_t(v >> 32); }
 __device__ __forceinline__ bool valid(uint64_t v) { return (hi_u(v) & kValid) != 0u; }
 
+// ---------------------------------------------------------- DPP reductions
+//
+// Inside a row of 16 lanes: exchange with lane ^ 1, lane ^ 2 (quad
+// permutes), then the half-row and row mirrors.  Every step is own + partner
+// with a commutative operation, so all 16 lanes end with bitwise the same
+// value.  Across the wave the four row results are read with readlane.
+constexpr int kXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kHalfMirror = 0x141;
+constexpr int kMirror = 0x140;
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+constexpr int kWaveShr1 = 0x138;
+
+// DPP move; lanes whose source is out of range, or whose row is masked off,
+// read 0.
+template <int C, int RM = 0xF> __device__ __forceinline__ int dpp_i(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, C, RM, 0xF, true);
+}
+template <int C> __device__ __forceinline__ float dpp_f(float x) { return __int_as_float(dpp_i<C>(__float_as_int(x))); }
+template <int C, int RM = 0xF> __device__ __forceinline__ double dpp_d(double x) {
+    const uint64_t v = uint64_t(__double_as_longlong(x));
+    const uint32_t lo = uint32_t(dpp_i<C, RM>(int(uint32_t(v)))), hi = uint32_t(dpp_i<C, RM>(int(uint32_t(v >> 32))));
+    return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+}
+__device__ __forceinline__ int lane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ __forceinline__ float lane_f(float x, int l) { return __int_as_float(lane_i(__float_as_int(x), l)); }
+__device__ __forceinline__ double lane_d(double x, int l) {
+    const uint64_t v = uint64_t(__double_as_longlong(x));
+    const uint32_t lo = uint32_t(lane_i(int(uint32_t(v)), l)), hi = uint32_t(lane_i(int(uint32_t(v >> 32)), l));
+    return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+}
+
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<kXor1>(x));
+    x = fmaxf(x, dpp_f<kXor2>(x));
+    x = fmaxf(x, dpp_f<kHalfMirror>(x));
+    return fmaxf(x, dpp_f<kMirror>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x = x + dpp_f<kXor1>(x);
+    x = x + dpp_f<kXor2>(x);
+    x = x + dpp_f<kHalfMirror>(x);
+    return x + dpp_f<kMirror>(x);
+}
+__device__ __forceinline__ double row16_sum_d(double x) {
+    x = x + dpp_d<kXor1>(x);
+    x = x + dpp_d<kXor2>(x);
+    x = x + dpp_d<kHalfMirror>(x);
+    return x + dpp_d<kMirror>(x);
+}
+__device__ __forceinline__ int row16_and(int x) {
+    x = x & dpp_i<kXor1>(x);
+    x = x & dpp_i<kXor2>(x);
+    x = x & dpp_i<kHalfMirror>(x);
+    return x & dpp_i<kMirror>(x);
+}
+// Whole-wave results, uniform across the wave.
+__device__ __forceinline__ float wave_max(float x) {
+    x = row16_max(x);
+    return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x = row16_sum(x);
+    return (lane_f(x, 0) + lane_f(x, 16)) + (lane_f(x, 32) + lane_f(x, 48));
+}
+// The butterfly sum; by commutativity it is bitwise the value wave_scan_d
+// leaves in lane 63.
+__device__ __forceinline__ double wave_sum_d(double x) {
+    x = row16_sum_d(x);
+    return (lane_d(x, 0) + lane_d(x, 16)) + (lane_d(x, 32) + lane_d(x, 48));
+}
+// Inclusive prefix across the wave: own + lane - d for d = 1, 2, 4, 8 inside
+// each row of 16, then row 0's total into row 1 and row 2's into row 3, then
+// the first two rows' total into rows 2 and 3.  (Adding a 0 where a lane has
+// no partner leaves it unchanged.)  At lane 63 this is the same tree as
+// wave_sum_d's: ((r3 + r2) + (r1 + r0)) with each row total t15 + t7-style.
+__device__ __forceinline__ double wave_scan_d(double x) {
+    x = x + dpp_d<kRowShr1>(x);
+    x = x + dpp_d<kRowShr2>(x);
+    x = x + dpp_d<kRowShr4>(x);
+    x = x + dpp_d<kRowShr8>(x);
+    x = x + dpp_d<kRowBcast15, 0xA>(x);
+    x = x + dpp_d<kRowBcast31, 0xC>(x);
+    return x;
+}
+
 struct __align__(16) Smem {
     union {
-        float ms[8];                              // (max, sum) per wave
-        struct { float v[4]; int i[4]; int nan[4]; } am;   // argmax per wave
-        double sc[4][2 * kSubBatch];              // scan totals per wave
+        double sc[kWaves][2];                     // scan: wave totals
+        double wt[kWaves][2 * kSubBatch];         // draw: wave totals of the sub-tile masses
     } r;
     double S[kWG];                                // fp64 row sums
     float M[kWG];                                 // row maxima
     int A[kWG];                                   // greedy row argmax
-    double mr[kStage], mp[kStage];                // staged sub-tile masses
-    double tot[2 * kSubBatch];
-    int jmin, bad, last;
-    int sstar, mode, t1, y;
-    double base, target, R;
+    int last;
+    int q[6][kWaves];                             // per-wave results of ballot searches
+    double base, R, Rp;
 };
 
-// ---------------------------------------------------------------- reductions
-
-// Merge two (max, sum) partials of the same row; each sum is taken against
-// its own max (see rescale).
-__device__ __forceinline__ void merge_ms(float &m, float &s, float m2, float s2, float c) {
-    const float M = fmaxf(m, m2);
-    if (M == neg_inf()) { m = M; s = s + s2; return; }
-    const float a = (m == neg_inf()) ? 0.0f * s : s * rescale(m, M, c);
-    const float b = (m2 == neg_inf()) ? 0.0f * s2 : s2 * rescale(m2, M, c);
-    m = M;
-    s = a + b;
-}
-
-// Result valid in thread 0.
-__device__ void wg_reduce_ms(float &m, float &s, float c, Smem &sh) {
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float m2 = __shfl_xor(m, off);
-        const float s2 = __shfl_xor(s, off);
-        merge_ms(m, s, m2, s2, c);
-    }
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (lane == 0) { sh.r.ms[2 * w] = m; sh.r.ms[2 * w + 1] = s; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        m = sh.r.ms[0]; s = sh.r.ms[1];
-        for (int i = 1; i < 4; ++i) merge_ms(m, s, sh.r.ms[2 * i], sh.r.ms[2 * i + 1], c);
-    }
-}
+// ---------------------------------------------------------------- merges
 
 // (value, index) with the larger value; equal values keep the lower index; index < 0 = none.
 __device__ __forceinline__ void merge_am(float &v, int &i, float v2, int i2) {
@@ -181,43 +240,66 @@ __device__ __forceinline__ void merge_am(float &v, int &i, float v2, int i2) {
     if (i < 0 || v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
 
-__device__ void wg_reduce_am(float &v, int &i, int &nan, Smem &sh) {
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float v2 = __shfl_xor(v, off);
-        const int i2 = __shfl_xor(i, off);
-        const int n2 = __shfl_xor(nan, off);
-        merge_am(v, i, v2, i2);
-        nan |= n2;
+template <int C> __device__ __forceinline__ void am_step(float &v, int &i, int &nan) {
+    const float v2 = dpp_f<C>(v);
+    const int i2 = dpp_i<C>(i);
+    nan |= dpp_i<C>(nan);
+    merge_am(v, i, v2, i2);
+}
+__device__ __forceinline__ void row16_argmax(float &v, int &i, int &nan) {
+    am_step<kXor1>(v, i, nan);
+    am_step<kXor2>(v, i, nan);
+    am_step<kHalfMirror>(v, i, nan);
+    am_step<kMirror>(v, i, nan);
+}
+__device__ __forceinline__ void wave_argmax(float &v, int &i, int &nan) {
+    row16_argmax(v, i, nan);
+    float bv = lane_f(v, 0);
+    int bi = lane_i(i, 0), bn = lane_i(nan, 0);
+    for (int r = 16; r < 64; r += 16) {
+        merge_am(bv, bi, lane_f(v, r), lane_i(i, r));
+        bn |= lane_i(nan, r);
     }
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (lane == 0) { sh.r.am.v[w] = v; sh.r.am.i[w] = i; sh.r.am.nan[w] = nan; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        v = sh.r.am.v[0]; i = sh.r.am.i[0]; nan = sh.r.am.nan[0];
-        for (int k = 1; k < 4; ++k) { merge_am(v, i, sh.r.am.v[k], sh.r.am.i[k]); nan |= sh.r.am.nan[k]; }
-    }
+    v = bv; i = bi; nan = bn;
 }
 
-// Exclusive prefix over the 256 threads of NS fp64 values at once.  Each value
-// goes through the same fixed sequence of additions whatever NS is.  Writes
-// the exclusive prefix to excl[]; the inclusive prefix of a thread is defined
-// as excl + v, and total[] is that of the last thread.
+// Ballot searches over the workgroup's threads.  Each wave reduces its
+// ballot (first or last set lane); lane 0 posts the wave's result in slot q
+// of sh.q; after the caller's barrier, wg_first / wg_last combine the four.
+// (A shared-memory atomic here would become a loop over the active lanes.)
+__device__ __forceinline__ void post_first(bool pred, int q, Smem &sh) {
+    const uint64_t m = __ballot(pred);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) sh.q[q][w] = m ? w * 64 + __builtin_ctzll(m) : INT_MAX;
+}
+__device__ __forceinline__ void post_last(bool pred, int q, Smem &sh) {
+    const uint64_t m = __ballot(pred);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) sh.q[q][w] = m ? w * 64 + 63 - __builtin_clzll(m) : -1;
+}
+// Lowest thread with the posted predicate (INT_MAX if none) / highest (-1).
+__device__ __forceinline__ int wg_first(int q, const Smem &sh) {
+    return min(min(sh.q[q][0], sh.q[q][1]), min(sh.q[q][2], sh.q[q][3]));
+}
+__device__ __forceinline__ int wg_last(int q, const Smem &sh) {
+    return max(max(sh.q[q][0], sh.q[q][1]), max(sh.q[q][2], sh.q[q][3]));
+}
+
+// Inclusive prefix over the 256 threads of NS fp64 values at once: the DPP
+// wave prefix x, then the wave totals W (x of lane 63) added in wave order
+// (wbase).  incl = wbase + x; excl = the previous thread's incl (wbase for
+// lane 0); total = incl of the last thread = ((W0 + W1) + W2) + W3, which is
+// what a sum of the four wave_sum_d results in that order gives.
 template <int NS>
-__device__ void wg_excl_scan(const double (&v)[NS], double (&excl)[NS], double (&total)[NS], Smem &sh) {
+__device__ void wg_scan(const double (&v)[NS], double (&excl)[NS], double (&incl)[NS], double (&total)[NS],
+                        Smem &sh) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    double x[NS];
+    double x[NS], xp[NS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) x[i] = v[i];
-    for (int d = 1; d < 64; d <<= 1) {
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-            const double y = __shfl_up(x[i], d);
-            if (lane >= d) x[i] = x[i] + y;
-        }
+    for (int i = 0; i < NS; ++i) {
+        x[i] = wave_scan_d(v[i]);
+        xp[i] = dpp_d<kWaveShr1>(x[i]);          // lane - 1's prefix (0 in lane 0)
     }
-    double xprev[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) xprev[i] = __shfl_up(x[i], 1);
     __syncthreads();
     if (lane == 63) {
 #pragma unroll
@@ -226,17 +308,15 @@ __device__ void wg_excl_scan(const double (&v)[NS], double (&excl)[NS], double (
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-        double wbase = 0.0;
-        for (int k = 0; k < w; ++k) wbase = wbase + sh.r.sc[k][i];
-        excl[i] = (lane == 0) ? wbase : wbase + xprev[i];
-        if (threadIdx.x == kWG - 1) sh.tot[i] = excl[i] + v[i];
+        double wb = 0.0;
+        for (int k = 0; k < w; ++k) wb = wb + sh.r.sc[k][i];
+        incl[i] = wb + x[i];
+        excl[i] = (lane == 0) ? wb : wb + xp[i];
+        total[i] = ((sh.r.sc[0][i] + sh.r.sc[1][i]) + sh.r.sc[2][i]) + sh.r.sc[3][i];
     }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NS; ++i) total[i] = sh.tot[i];
 }
 
-// ------------------------------------------------------------- arrivals
+// ------------------------------------------------------------- workspace
 
 // Every thread's published stores complete, then one counted arrival.
 // Returns true in every thread of the workgroup that arrives last; that
@@ -259,13 +339,17 @@ __device__ bool arrive_last(unsigned *ctr, unsigned target, Smem &sh) {
 __device__ __forceinline__ unsigned *draw_counter(const VerifyArgs &a, int b) {
     return reinterpret_cast<unsigned *>(a.ws + size_t(b) * kSlotBytes) + 2;
 }
-
 __device__ __forceinline__ uint64_t *partials(const VerifyArgs &a, int b) {
     return reinterpret_cast<uint64_t *>(a.ws + a.lay.part) + size_t(b) * (a.G + 1) * a.nc1;
 }
+__device__ __forceinline__ uint64_t *masses(const VerifyArgs &a, int b) {
+    return reinterpret_cast<uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
+}
+__device__ __forceinline__ uint64_t *gathered(const VerifyArgs &a, int b) {
+    return reinterpret_cast<uint64_t *>(a.ws + a.lay.gx) + size_t(b) * a.G;
+}
 
-// A request with a data error: every output word -1 (diagnostics become NaN
-// in the diagnostics kernel, which checks out_accepted).
+// A request with a data error: every output word -1 (diagnostics NaN).
 __device__ void write_error(const VerifyArgs &a, int b) {
     const int G1 = a.G + 1;
     for (int t = threadIdx.x; t < G1; t += kWG) st_out(a.out_tok + size_t(b) * G1 + t, -1);
@@ -286,181 +370,153 @@ __device__ bool wait_partials(const VerifyArgs &a, int b, int n) {
     }
 }
 
-// ------------------------------------------------------------- row items
-
-// (max, sum of 2^((z-max)*c)) over elements [beg, end) of one row, per thread.
-template <int ES, bool AL>
-__device__ void chunk_ms(const void *row, int beg, int end, float c, float &m_out, float &s_out) {
-    float m = neg_inf();
-    if constexpr (AL) {
-        constexpr int EPV = 16 / ES;
-        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const char *>(row) + size_t(beg) * ES);
-        const int nvec = (end - beg) / EPV;
-        constexpr uint32_t fill = (ES == 2) ? 0xff80ff80u : 0xff800000u;   // -inf
-        uint4 r[kVecPerThread];
-#pragma unroll
-        for (int i = 0; i < kVecPerThread; ++i) {
-            const int v = threadIdx.x + i * kWG;
-            if (v < nvec) r[i] = p[v];
-            else r[i] = make_uint4(fill, fill, fill, fill);
-        }
-#pragma unroll
-        for (int i = 0; i < kVecPerThread; ++i) {
-            const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-            if constexpr (ES == 2) {
-#pragma unroll
-                for (int d = 0; d < 4; ++d) m = max3(m, bf16_lo(w[d]), bf16_hi(w[d]));
-            } else {
-                m = max3(m, __uint_as_float(w[0]), __uint_as_float(w[1]));
-                m = max3(m, __uint_as_float(w[2]), __uint_as_float(w[3]));
-            }
-        }
-        // Keep only the raw words live between the two passes (re-converting a
-        // bf16 is one instruction; holding 64 converted floats costs occupancy).
-#pragma unroll
-        for (int i = 0; i < kVecPerThread; ++i)
-            asm volatile("" : "+v"(r[i].x), "+v"(r[i].y), "+v"(r[i].z), "+v"(r[i].w));
-        float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-        if (m == neg_inf()) {
-            // Every element is -inf or NaN (fmaxf drops NaN): keep a NaN visible.
-#pragma unroll
-            for (int i = 0; i < kVecPerThread; ++i) {
-                const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    if constexpr (ES == 2) {
-                        if (bf16_lo(w[d]) != bf16_lo(w[d]) || bf16_hi(w[d]) != bf16_hi(w[d])) s0 = __builtin_nanf("");
-                    } else {
-                        if (__uint_as_float(w[d]) != __uint_as_float(w[d])) s0 = __builtin_nanf("");
-                    }
-                }
-            }
-        } else if (finitef(m * c)) {
-            const float nR = -(m * c);
-#pragma unroll
-            for (int i = 0; i < kVecPerThread; ++i) {
-                const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-                if constexpr (ES == 2) {
-                    s0 = s0 + exp2_fast(__builtin_fmaf(bf16_lo(w[0]), c, nR));
-                    s1 = s1 + exp2_fast(__builtin_fmaf(bf16_hi(w[0]), c, nR));
-                    s2 = s2 + exp2_fast(__builtin_fmaf(bf16_lo(w[1]), c, nR));
-                    s3 = s3 + exp2_fast(__builtin_fmaf(bf16_hi(w[1]), c, nR));
-                    s0 = s0 + exp2_fast(__builtin_fmaf(bf16_lo(w[2]), c, nR));
-                    s1 = s1 + exp2_fast(__builtin_fmaf(bf16_hi(w[2]), c, nR));
-                    s2 = s2 + exp2_fast(__builtin_fmaf(bf16_lo(w[3]), c, nR));
-                    s3 = s3 + exp2_fast(__builtin_fmaf(bf16_hi(w[3]), c, nR));
-                } else {
-                    s0 = s0 + exp2_fast(__builtin_fmaf(__uint_as_float(w[0]), c, nR));
-                    s1 = s1 + exp2_fast(__builtin_fmaf(__uint_as_float(w[1]), c, nR));
-                    s2 = s2 + exp2_fast(__builtin_fmaf(__uint_as_float(w[2]), c, nR));
-                    s3 = s3 + exp2_fast(__builtin_fmaf(__uint_as_float(w[3]), c, nR));
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < kVecPerThread; ++i) {
-                const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    if constexpr (ES == 2) {
-                        s0 = s0 + exp2_fast((bf16_lo(w[d]) - m) * c);
-                        s1 = s1 + exp2_fast((bf16_hi(w[d]) - m) * c);
-                    } else {
-                        s0 = s0 + exp2_fast((__uint_as_float(w[d]) - m) * c);
-                    }
-                }
-            }
-        }
-        s_out = (s0 + s1) + (s2 + s3);
-    } else {
-        float s = 0.0f;
-        for (int e = beg + threadIdx.x; e < end; e += kWG) {
-            const float v = load_elem<ES>(row, size_t(e));
-            if (v > m) { s = s * rescale(m, v, c); m = v; }
-            if (m != neg_inf()) {
-                const float R = m * c;
-                s = s + (finitef(R) ? exp2_fast(__builtin_fmaf(v, c, -R)) : exp2_fast((v - m) * c));
-            } else if (v != v) {
-                s = v;                                    // NaN among -inf: keep it visible
-            }
-        }
-        s_out = s;
-    }
-    m_out = m;
-}
-
-// (max, lowest index of max, any NaN) over [beg, end), per thread, ascending order.
-template <int ES, bool AL>
-__device__ void chunk_argmax(const void *row, int beg, int end, float &best, int &bi, int &nan) {
-    best = neg_inf(); bi = -1; nan = 0;
-    if constexpr (AL) {
-        constexpr int EPV = 16 / ES;
-        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const char *>(row) + size_t(beg) * ES);
-        const int nvec = (end - beg) / EPV;
-        constexpr uint32_t fill = (ES == 2) ? 0xff80ff80u : 0xff800000u;   // -inf
-        uint4 r[kVecPerThread];
-#pragma unroll
-        for (int i = 0; i < kVecPerThread; ++i) {
-            const int v = threadIdx.x + i * kWG;
-            r[i] = (v < nvec) ? p[v] : make_uint4(fill, fill, fill, fill);
-        }
-#pragma unroll
-        for (int i = 0; i < kVecPerThread; ++i) {
-            const int e0 = beg + (threadIdx.x + i * kWG) * EPV;
-            const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                if constexpr (ES == 2) {
-                    const float lo = bf16_lo(w[d]), hi = bf16_hi(w[d]);
-                    nan |= (lo != lo) | (hi != hi);
-                    if (lo > best) { best = lo; bi = e0 + 2 * d; }
-                    if (hi > best) { best = hi; bi = e0 + 2 * d + 1; }
-                } else {
-                    const float f = __uint_as_float(w[d]);
-                    nan |= (f != f);
-                    if (f > best) { best = f; bi = e0 + d; }
-                }
-            }
-        }
-    } else {
-        for (int e = beg + threadIdx.x; e < end; e += kWG) {
-            const float v = load_elem<ES>(row, size_t(e));
-            nan |= (v != v);
-            if (v > best) { best = v; bi = e; }
-        }
-    }
-}
-
 __device__ __forceinline__ int verify_len(const VerifyArgs &a, int b) { return a.vlen ? a.vlen[b] : a.G; }
 
+// ------------------------------------------------------------- row waves
+
+template <int ES> constexpr int kEPL = kRowVec * (16 / ES);   // elements per lane of a chunk
+
+// Lane `lane`'s values of the chunk that starts at element beg of a row of V
+// elements; positions past the row end read as -inf.  Aligned rows use four
+// 16-byte loads per lane (vector v = lane + 64 i); others one element per load
+// (element beg + lane + 64 i).
 template <int ES, bool AL>
-__device__ void row_item_sampled(const VerifyArgs &a, int b, int local, Smem &sh) {
-    const int k = local / a.nc1, c = local - k * a.nc1;
-    const int n = verify_len(a, b);
-    if (n < 0 || n > a.G || k > n) return;
-    const void *row = static_cast<const char *>(a.logits) + (size_t(b) * (a.G + 1) + k) * size_t(a.V) * ES;
-    const int beg = c * a.ch1, end = min(a.V, beg + a.ch1);
-    float m, s;
-    chunk_ms<ES, AL>(row, beg, end, a.c32, m, s);
-    wg_reduce_ms(m, s, a.c32, sh);
-    if (threadIdx.x == 0)
-        st_coherent(partials(a, b) + size_t(k) * a.nc1 + c,
-                    uint64_t(__float_as_uint(m)) | (uint64_t(__float_as_uint(s) | kValid) << 32));
+__device__ __forceinline__ void load_chunk(const void *row, int beg, int V, int lane, float (&f)[kEPL<ES>]) {
+    if constexpr (AL) {
+        constexpr int EPV = 16 / ES;
+        constexpr uint32_t fill = (ES == 2) ? 0xff80ff80u : 0xff800000u;   // -inf
+        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const char *>(row) + size_t(beg) * ES);
+        const int nvec = (V - beg) / EPV;
+        uint4 r[kRowVec];
+        if (nvec >= 64 * kRowVec) {
+#pragma unroll
+            for (int i = 0; i < kRowVec; ++i) r[i] = ld_stream(p + lane + 64 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kRowVec; ++i) {
+                const int v = lane + 64 * i;
+                r[i] = (v < nvec) ? ld_stream(p + v) : make_uint4(fill, fill, fill, fill);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kRowVec; ++i) {
+            if constexpr (ES == 2) {
+                f[8 * i + 0] = bf16_lo(r[i].x); f[8 * i + 1] = bf16_hi(r[i].x);
+                f[8 * i + 2] = bf16_lo(r[i].y); f[8 * i + 3] = bf16_hi(r[i].y);
+                f[8 * i + 4] = bf16_lo(r[i].z); f[8 * i + 5] = bf16_hi(r[i].z);
+                f[8 * i + 6] = bf16_lo(r[i].w); f[8 * i + 7] = bf16_hi(r[i].w);
+            } else {
+                f[4 * i + 0] = __uint_as_float(r[i].x); f[4 * i + 1] = __uint_as_float(r[i].y);
+                f[4 * i + 2] = __uint_as_float(r[i].z); f[4 * i + 3] = __uint_as_float(r[i].w);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kEPL<ES>; ++i) {
+            const int e = beg + lane + 64 * i;
+            f[i] = (e < V) ? load_elem<ES>(row, size_t(e)) : neg_inf();
+        }
+    }
+}
+// Row index of f[i] in load_chunk's layout (ascending in i for a fixed lane).
+template <int ES, bool AL>
+__device__ __forceinline__ int chunk_index(int beg, int lane, int i) {
+    constexpr int EPV = 16 / ES;
+    return AL ? beg + (lane + 64 * (i / EPV)) * EPV + (i % EPV) : beg + lane + 64 * i;
 }
 
+// Row-pass job -> (request, row, chunk); false if that row is not read.
+struct RowJob {
+    int b, k, c, n;
+};
+__device__ __forceinline__ bool row_job(const VerifyArgs &a, int job, RowJob &j) {
+    const int per = (a.G + 1) * a.nc1;
+    j.b = job / per;
+    const int local = job - j.b * per;
+    j.k = local / a.nc1;
+    j.c = local - j.k * a.nc1;
+    j.n = verify_len(a, j.b);
+    return j.n >= 0 && j.n <= a.G && j.k <= j.n;
+}
+
+// Sampled row pass, one wave: (max, sum of 2^((z - max) * c)) of its chunk.
 template <int ES, bool AL>
-__device__ void row_item_greedy(const VerifyArgs &a, int b, int local, Smem &sh) {
-    const int k = local / a.nc1, c = local - k * a.nc1;
-    const int n = verify_len(a, b);
-    if (n < 0 || n > a.G || k > n) return;
-    const void *row = static_cast<const char *>(a.logits) + (size_t(b) * (a.G + 1) + k) * size_t(a.V) * ES;
-    const int beg = c * a.ch1, end = min(a.V, beg + a.ch1);
-    float best;
-    int bi, nan;
-    chunk_argmax<ES, AL>(row, beg, end, best, bi, nan);
-    wg_reduce_am(best, bi, nan, sh);
-    if (threadIdx.x == 0)
-        st_coherent(partials(a, b) + size_t(k) * a.nc1 + c,
+__device__ void row_wave_sampled(const VerifyArgs &a, int job, int lane) {
+    RowJob jb;
+    if (!row_job(a, job, jb)) return;
+    constexpr int EPL = kEPL<ES>;
+    const int G1 = a.G + 1;
+    const void *row = static_cast<const char *>(a.logits) + (size_t(jb.b) * G1 + jb.k) * size_t(a.V) * ES;
+    const int beg = jb.c * a.ch1;
+    float f[EPL];
+    load_chunk<ES, AL>(row, beg, a.V, lane, f);
+    // The chunk holding draft token x_k gathers z(x_k) and q(x_k) for the
+    // request pass's accept test (an x_k out of range is never gathered).
+    const int xk = (jb.k < jb.n) ? a.x[size_t(jb.b) * a.G + jb.k] : -1;
+    const bool gather = xk >= beg && xk < beg + a.ch1 && xk < a.V;
+    float gz = 0.0f, gq = 0.0f;
+    if (gather && lane == 0) {
+        gz = load_elem<ES>(row, size_t(xk));
+        gq = a.q[(size_t(jb.b) * a.G + jb.k) * size_t(a.V) + size_t(xk)];
+    }
+    const float c = a.c32;
+    float m = f[0];
+#pragma unroll
+    for (int i = 1; i + 1 < EPL; i += 2) m = max3(m, f[i], f[i + 1]);
+    m = fmaxf(m, f[EPL - 1]);
+    const float M = wave_max(m);
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    if (M == neg_inf()) {
+        // Every element is -inf or NaN (the maximum drops NaN): keep a NaN visible.
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (f[i] != f[i]) s0 = __builtin_nanf("");
+    } else if (finitef(M * c)) {
+        const float nR = -(M * c);
+#pragma unroll
+        for (int i = 0; i < EPL; i += 4) {
+            s0 = s0 + exp2_fast(__builtin_fmaf(f[i + 0], c, nR));
+            s1 = s1 + exp2_fast(__builtin_fmaf(f[i + 1], c, nR));
+            s2 = s2 + exp2_fast(__builtin_fmaf(f[i + 2], c, nR));
+            s3 = s3 + exp2_fast(__builtin_fmaf(f[i + 3], c, nR));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL; i += 4) {
+            s0 = s0 + exp2_fast((f[i + 0] - M) * c);
+            s1 = s1 + exp2_fast((f[i + 1] - M) * c);
+            s2 = s2 + exp2_fast((f[i + 2] - M) * c);
+            s3 = s3 + exp2_fast((f[i + 3] - M) * c);
+        }
+    }
+    const float S = wave_sum((s0 + s1) + (s2 + s3));
+    if (lane == 0) {
+        partials(a, jb.b)[size_t(jb.k) * a.nc1 + jb.c] =
+            uint64_t(__float_as_uint(M)) | (uint64_t(__float_as_uint(S) | kValid) << 32);
+        if (gather)
+            gathered(a, jb.b)[jb.k] = uint64_t(__float_as_uint(gz)) | (uint64_t(__float_as_uint(gq)) << 32);
+    }
+}
+
+// Greedy row pass, one wave: (max, lowest index of the max, any NaN) of its chunk.
+template <int ES, bool AL>
+__device__ void row_wave_greedy(const VerifyArgs &a, int job, int lane) {
+    RowJob jb;
+    if (!row_job(a, job, jb)) return;
+    const void *row = static_cast<const char *>(a.logits) + (size_t(jb.b) * (a.G + 1) + jb.k) * size_t(a.V) * ES;
+    const int beg = jb.c * a.ch1;
+    float f[kEPL<ES>];
+    load_chunk<ES, AL>(row, beg, a.V, lane, f);
+    float best = neg_inf();
+    int bi = -1, nan = 0;
+#pragma unroll
+    for (int i = 0; i < kEPL<ES>; ++i) {
+        nan |= int(f[i] != f[i]);
+        if (f[i] > best) { best = f[i]; bi = chunk_index<ES, AL>(beg, lane, i); }
+    }
+    wave_argmax(best, bi, nan);
+    if (lane == 0)
+        st_coherent(partials(a, jb.b) + size_t(jb.k) * a.nc1 + jb.c,
                     uint64_t(__float_as_uint(best)) | (uint64_t(uint32_t((nan ? kNanIdx : bi) + 2) | kValid) << 32));
 }
 
@@ -477,53 +533,60 @@ __device__ __forceinline__ void draw_term(float z, float q, float m, float c, fl
 }
 
 // One thread's 8 contiguous elements of sub-tile `sub` of a draw row: the
-// residual (or target) mass `rs` and the target mass `ps`, fp64 in index order.
+// residual (or target) mass `rs` and the target mass `ps`, fp64 in index
+// order, and the terms t (residual if use_r, else target; 0 past the row end).
+// qrow is the draft row (resid) or a block of zeros (bonus draw), so the z
+// and q loads are all issued before any is waited for.  The mass pass and the
+// final re-scan both call this, so their sums agree bitwise.
 template <int ES, bool ALZ, bool ALQ>
-__device__ void sub_sums(const void *zrow, const float *qrow, int V, int sub, float m, float c, float inv_s,
-                         bool resid, double &rs, double &ps) {
+__device__ __forceinline__ void sub_tile(const void *zrow, const float *qrow, int V, int sub, float m, float c,
+                                         float inv_s, bool resid, bool use_r, float (&t)[kSubPerThread],
+                                         double &rs, double &ps) {
     rs = 0.0; ps = 0.0;
+#pragma unroll
+    for (int i = 0; i < kSubPerThread; ++i) t[i] = 0.0f;
     const int e0 = sub * kSub + int(threadIdx.x) * kSubPerThread;
     if (e0 >= V) return;
+    const int qo = resid ? e0 : 0;          // the zero block is read from its start
     float z[kSubPerThread], q[kSubPerThread];
     if (ALZ && (!resid || ALQ) && e0 + kSubPerThread <= V) {
         const uint4 *zp = reinterpret_cast<const uint4 *>(static_cast<const char *>(zrow) + size_t(e0) * ES);
+        const uint4 *qp = reinterpret_cast<const uint4 *>(qrow + qo);
+        uint4 zw[ES == 2 ? 1 : 2];
+        zw[0] = zp[0];
+        if constexpr (ES == 4) zw[1] = zp[1];
+        const uint4 q0 = qp[0], q1 = qp[1];
         if constexpr (ES == 2) {
-            const uint4 w = zp[0];
-            z[0] = bf16_lo(w.x); z[1] = bf16_hi(w.x); z[2] = bf16_lo(w.y); z[3] = bf16_hi(w.y);
-            z[4] = bf16_lo(w.z); z[5] = bf16_hi(w.z); z[6] = bf16_lo(w.w); z[7] = bf16_hi(w.w);
+            z[0] = bf16_lo(zw[0].x); z[1] = bf16_hi(zw[0].x); z[2] = bf16_lo(zw[0].y); z[3] = bf16_hi(zw[0].y);
+            z[4] = bf16_lo(zw[0].z); z[5] = bf16_hi(zw[0].z); z[6] = bf16_lo(zw[0].w); z[7] = bf16_hi(zw[0].w);
         } else {
-            const uint4 w0 = zp[0], w1 = zp[1];
-            z[0] = __uint_as_float(w0.x); z[1] = __uint_as_float(w0.y);
-            z[2] = __uint_as_float(w0.z); z[3] = __uint_as_float(w0.w);
-            z[4] = __uint_as_float(w1.x); z[5] = __uint_as_float(w1.y);
-            z[6] = __uint_as_float(w1.z); z[7] = __uint_as_float(w1.w);
+            z[0] = __uint_as_float(zw[0].x); z[1] = __uint_as_float(zw[0].y);
+            z[2] = __uint_as_float(zw[0].z); z[3] = __uint_as_float(zw[0].w);
+            z[4] = __uint_as_float(zw[1].x); z[5] = __uint_as_float(zw[1].y);
+            z[6] = __uint_as_float(zw[1].z); z[7] = __uint_as_float(zw[1].w);
         }
-        if (resid) {
-            const uint4 *qp = reinterpret_cast<const uint4 *>(qrow + e0);
-            const uint4 w0 = qp[0], w1 = qp[1];
-            q[0] = __uint_as_float(w0.x); q[1] = __uint_as_float(w0.y);
-            q[2] = __uint_as_float(w0.z); q[3] = __uint_as_float(w0.w);
-            q[4] = __uint_as_float(w1.x); q[5] = __uint_as_float(w1.y);
-            q[6] = __uint_as_float(w1.z); q[7] = __uint_as_float(w1.w);
-        } else {
-#pragma unroll
-            for (int i = 0; i < kSubPerThread; ++i) q[i] = 0.0f;
-        }
+        q[0] = __uint_as_float(q0.x); q[1] = __uint_as_float(q0.y);
+        q[2] = __uint_as_float(q0.z); q[3] = __uint_as_float(q0.w);
+        q[4] = __uint_as_float(q1.x); q[5] = __uint_as_float(q1.y);
+        q[6] = __uint_as_float(q1.z); q[7] = __uint_as_float(q1.w);
+    } else {
+        // Element loads at clamped indices (all in bounds, all issued at once);
+        // positions past the row end are dropped below.
 #pragma unroll
         for (int i = 0; i < kSubPerThread; ++i) {
+            const int e = min(e0 + i, V - 1);
+            z[i] = load_elem<ES>(zrow, size_t(e));
+            q[i] = qrow[resid ? e : 0];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kSubPerThread; ++i) {
+        if (e0 + i < V) {
             float r, p;
             draw_term(z[i], q[i], m, c, inv_s, resid, r, p);
             rs = rs + double(r);
             ps = ps + double(p);
-        }
-    } else {
-        const int e1 = min(V, e0 + kSubPerThread);
-        for (int e = e0; e < e1; ++e) {
-            float r, p;
-            const float qv = resid ? qrow[e] : 0.0f;
-            draw_term(load_elem<ES>(zrow, size_t(e)), qv, m, c, inv_s, resid, r, p);
-            rs = rs + double(r);
-            ps = ps + double(p);
+            t[i] = use_r ? r : p;
         }
     }
 }
@@ -535,44 +598,98 @@ struct Decision {
     int n, j;
     bool resid;
     float m, inv_s;
+    float u_final;    // u[b, G], the final draw's uniform
 };
 
-// Merge row r's chunk partials into sh.M[r] (max) and sh.S[r] (fp64 sum);
-// marks the request bad for a bad row or a partial that was never written.
-__device__ void merge_row_sampled(const VerifyArgs &a, const uint64_t *pp, int r, Smem &sh) {
-    float M = neg_inf();
-    bool ok = true;
-    for (int c = 0; c < a.nc1; ++c) {
-        const uint64_t v = pp[c];
-        ok &= valid(v);
-        M = fmaxf(M, lo_f(v));
+// Merge each read row's chunk partials into sh.M[r] (max) and sh.S[r] (fp64
+// sum against the reference of sh.M[r]): 16 lanes per row, each lane's
+// partials rescaled once, then a fixed 16-lane tree.  Returns true in some
+// thread if a read row is bad or has a partial that was never written.  Rows
+// up to G are loaded whatever n is, so these loads need not wait for the
+// verify length.
+__device__ bool merge_rows_sampled(const VerifyArgs &a, int b, int n, Smem &sh) {
+    bool bad = false;
+    constexpr int kRegs = 4;   // partials held per lane when nc1 <= 64
+    const uint64_t *part = partials(a, b);
+    const int l = threadIdx.x & 15, g = threadIdx.x >> 4;
+    const float c = a.c32;
+    const uint64_t empty = uint64_t(0xff800000u) | (uint64_t(kValid) << 32);   // (-inf, 0), written
+    for (int r0 = 0; r0 <= a.G; r0 += kWG / 16) {
+        const int r = r0 + g;
+        const bool live = r <= a.G;
+        const uint64_t *pp = part + size_t(live ? r : 0) * a.nc1;
+        float M = neg_inf();
+        double S = 0.0;
+        int ok = 1;
+        if (a.nc1 <= 16 * kRegs) {
+            uint64_t v[kRegs];
+#pragma unroll
+            for (int i = 0; i < kRegs; ++i) {
+                const int cc = l + 16 * i;
+                v[i] = (live && cc < a.nc1) ? pp[cc] : empty;
+            }
+#pragma unroll
+            for (int i = 0; i < kRegs; ++i) {
+                ok &= int(valid(v[i]));
+                M = fmaxf(M, lo_f(v[i]));
+            }
+            M = row16_max(M);
+#pragma unroll
+            for (int i = 0; i < kRegs; ++i)
+                S = S + double(__uint_as_float(hi_u(v[i]) & ~kValid)) * double(rescale(lo_f(v[i]), M, c));
+        } else {
+            if (live)
+                for (int cc = l; cc < a.nc1; cc += 16) {
+                    const uint64_t v = pp[cc];
+                    ok &= int(valid(v));
+                    M = fmaxf(M, lo_f(v));
+                }
+            M = row16_max(M);
+            if (live)
+                for (int cc = l; cc < a.nc1; cc += 16) {
+                    const uint64_t v = pp[cc];
+                    S = S + double(__uint_as_float(hi_u(v) & ~kValid)) * double(rescale(lo_f(v), M, c));
+                }
+        }
+        S = row16_sum_d(S);
+        ok = row16_and(ok);
+        if (l == 0 && r <= n) {
+            bad |= !ok || !(S > 0.0 && S < INFINITY) || !(M > neg_inf() && M < __builtin_inff());
+            sh.M[r] = M;
+            sh.S[r] = S;
+        }
     }
-    double S = 0.0;
-    for (int c = 0; c < a.nc1; ++c) {
-        const uint64_t v = pp[c];
-        const float vm = lo_f(v), vs = __uint_as_float(hi_u(v) & ~kValid);
-        if (vm == neg_inf() && vs == 0.0f) continue;            // empty chunk
-        S = S + double(vs) * rescale_d(vm, M, a.c32);
-    }
-    if (!ok || !(S > 0.0 && S < INFINITY) || !(M > neg_inf() && M < INFINITY)) atomicOr(&sh.bad, 1);
-    sh.M[r] = M;
-    sh.S[r] = S;
+    return bad;
 }
 
-// Row r's chunk partials (greedy): lowest index of the maximum into sh.A[r].
-__device__ void merge_row_greedy(const VerifyArgs &a, const uint64_t *pp, int r, Smem &sh) {
-    float best = neg_inf();
-    int bi = -1, nan = 0;
-    bool ok = true;
-    for (int c = 0; c < a.nc1; ++c) {               // ascending chunks: first maximum wins
-        const uint64_t v = ld_coherent(pp + c);
-        ok &= valid(v);
-        const int vi = int(hi_u(v) & ~kValid) - 2;
-        if (vi == kNanIdx) { nan = 1; continue; }
-        merge_am(best, bi, lo_f(v), vi);
+// Rows 0..n's chunk partials (greedy): lowest index of the maximum into
+// sh.A[r].  Returns true in some thread if a row is bad or incomplete.
+__device__ bool merge_rows_greedy(const VerifyArgs &a, int b, int n, Smem &sh) {
+    bool bad = false;
+    const uint64_t *part = partials(a, b);
+    const int l = threadIdx.x & 15, g = threadIdx.x >> 4;
+    for (int r0 = 0; r0 <= n; r0 += kWG / 16) {
+        const int r = r0 + g;
+        float best = neg_inf();
+        int bi = -1, nan = 0, ok = 1;
+        if (r <= n) {
+            const uint64_t *pp = part + size_t(r) * a.nc1;
+            for (int cc = l; cc < a.nc1; cc += 16) {
+                const uint64_t v = ld_coherent(pp + cc);
+                ok &= int(valid(v));
+                const int vi = int(hi_u(v) & ~kValid) - 2;
+                if (vi == kNanIdx) nan = 1;
+                else merge_am(best, bi, lo_f(v), vi);
+            }
+        }
+        row16_argmax(best, bi, nan);
+        ok = row16_and(ok);
+        if (l == 0 && r <= n) {
+            bad |= !ok || nan || bi < 0 || best == __builtin_inff();
+            sh.A[r] = bi;
+        }
     }
-    if (!ok || nan || bi < 0 || best == __builtin_inff()) atomicOr(&sh.bad, 1);
-    sh.A[r] = bi;
+    return bad;
 }
 
 // Unnormalised target probability 2^(z*c - R) of a value z in a row with
@@ -587,14 +704,32 @@ __device__ __forceinline__ double row_lse(float m, double S, float c, double T) 
     return finitef(R) ? double(R) * 0.69314718055994530942 + log(S) : double(m) / T + log(S);
 }
 
-// All chunk partials of the request are complete (written by the previous
-// launch): merge every row, run the accept tests, find the first rejection.
-// Returns false (outputs reported by workgroup 0) for a data error or an
-// invalid verify length (then *arrive is false: no workgroup counts itself).
+// All chunk partials and gathers of the request are complete (written by the
+// previous launch): merge every row, run the accept tests, find the first
+// rejection.  Returns false (outputs reported by workgroup 0) for a data error
+// or an invalid verify length (then *arrive is false: no workgroup counts
+// itself).  Every load is issued before the first barrier (a barrier waits for
+// outstanding loads), so the whole decision costs one memory round trip.
 template <int ES>
 __device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, bool &arrive, Smem &sh) {
     const int G = a.G, G1 = G + 1;
+    const int k = threadIdx.x;
     const int n = verify_len(a, b);
+    int xk = 0;
+    uint64_t gk = 0;
+    float uk = 0.0f;
+    if (k < G) {
+        xk = a.x[size_t(b) * G + k];
+        gk = gathered(a, b)[k];
+        uk = a.u[size_t(b) * G1 + k];
+    }
+    d.u_final = a.u[size_t(b) * G1 + G];
+    bool bad = merge_rows_sampled(a, b, n, sh);
+    // Keep the uses of the per-draft loads below the partials' loads (the
+    // compiler would otherwise wait for them before issuing the partials).
+    asm volatile("" : "+v"(xk), "+v"(uk), "+v"(gk));
+    bad |= k < n && (xk < 0 || xk >= a.V);
+    const bool any_bad = __syncthreads_or(bad);
     d.n = n;
     arrive = false;
     if (n < 0 || n > G) {
@@ -602,36 +737,21 @@ __device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, bool &arr
         return false;
     }
     arrive = true;
-    const int k = threadIdx.x;
-    int xk = 0;
-    float zx = 0.0f, qx = 0.0f, uk = 0.0f;
-    bool xbad = false;
-    if (k < n) {
-        xk = a.x[size_t(b) * G + k];
-        xbad = xk < 0 || xk >= a.V;
-        if (!xbad) {
-            zx = load_elem<ES>(a.logits, (size_t(b) * G1 + k) * size_t(a.V) + size_t(xk));
-            qx = a.q[(size_t(b) * G + k) * size_t(a.V) + size_t(xk)];
-        }
-        uk = a.u[size_t(b) * G1 + k];
-    }
-    if (threadIdx.x == 0) { sh.jmin = n; sh.bad = 0; }
-    __syncthreads();
-    const uint64_t *part = partials(a, b);
-    for (int r = threadIdx.x; r <= n; r += kWG) merge_row_sampled(a, part + size_t(r) * a.nc1, r, sh);
-    if (xbad) atomicOr(&sh.bad, 1);
-    __syncthreads();
-    if (k < n && !xbad) {
-        const double pk = target_prob(zx, sh.M[k], a.c32) / sh.S[k];
-        const bool acc = (qx > 0.0f) ? (double(uk) < pk / double(qx)) : (pk > 0.0);
-        if (!acc) atomicMin(&sh.jmin, k);
-    }
-    __syncthreads();
-    if (sh.bad) {
+    if (any_bad) {
         if (w == 0) write_error(a, b);
         return false;
     }
-    const int j = sh.jmin;
+    bool rej = false;
+    if (k < n) {
+        const float zx = lo_f(gk), qx = __uint_as_float(hi_u(gk));
+        const double pk = target_prob(zx, sh.M[k], a.c32) / sh.S[k];
+        const bool acc = (qx > 0.0f) ? (double(uk) < pk / double(qx)) : (pk > 0.0);
+        rej = !acc;
+    }
+    post_first(rej, 0, sh);
+    __syncthreads();
+    const int jf = wg_first(0, sh);
+    const int j = (jf == INT_MAX) ? n : jf;
     d.j = j;
     d.resid = j < n;
     d.m = sh.M[j];
@@ -673,117 +793,122 @@ __device__ void write_diag(const VerifyArgs &a, int b, bool ok, int n, Smem &sh)
 }
 
 // Last workgroup of request b: locate u * R and write the token.
+//
+// The draw follows the inverse-CDF definition: y is the first index whose
+// running sum of terms exceeds u times their total.  Sums are hierarchical
+// (sub-tile masses, then 8-element thread sums, then the elements), so the
+// search takes the first sub-tile, then the first thread, then the first
+// element whose running sum passes the target, each level restricted to
+// positive mass.  Where rounding between the levels leaves no crossing, the
+// last positive term before the target is taken, which differs from the exact
+// draw only when u * R lies within rounding of a cumulative sum.
 template <int ES, bool ALZ, bool ALQ>
 __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, const void *zrow, const float *qrow,
                              Smem &sh) {
     const int G1 = a.G + 1;
     const bool resid = d.resid;
-    const uint64_t *mass = reinterpret_cast<const uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
-    // Pass 1: totals, in sub-tile order.  mode 1 draws from the residual, mode 0 from p.
+    const uint64_t *mass = masses(a, b);
+    const int nsub = a.nsub;
+    // Pass 1: totals of both mass arrays (residual, target), and the last
+    // sub-tile of each with positive mass.  With at most kWG sub-tiles (every
+    // vocabulary up to 2^19) the masses stay in registers for pass 2.
+    const bool one = nsub <= kWG;
+    double v[2] = {0.0, 0.0}, ex[2] = {0.0, 0.0}, in[2], tot[2];
     double R = 0.0, Rp = 0.0;
-    int last_r = -1, last_p = -1;
-    for (int blk = 0; blk < a.nsub; blk += kStage) {
-        const int cnt = min(kStage, a.nsub - blk);
-        __syncthreads();
-        if (int(threadIdx.x) < cnt) {
-            sh.mr[threadIdx.x] = __longlong_as_double(ld_coherent(mass + 2 * (blk + threadIdx.x)));
-            sh.mp[threadIdx.x] = __longlong_as_double(ld_coherent(mass + 2 * (blk + threadIdx.x) + 1));
+    int lr = -1, lp_s = -1;
+    for (int blk = 0; blk < nsub; blk += kWG) {
+        const int s = blk + int(threadIdx.x);
+        v[0] = 0.0; v[1] = 0.0;
+        if (s < nsub) {
+            v[0] = __longlong_as_double((long long)ld_coherent(mass + 2 * s));
+            v[1] = __longlong_as_double((long long)ld_coherent(mass + 2 * s + 1));
         }
+        wg_scan<2>(v, ex, in, tot, sh);
+        post_last(v[0] > 0.0, 1, sh);
+        post_last(v[1] > 0.0, 2, sh);
         __syncthreads();
-        if (threadIdx.x == 0) {
-            for (int i = 0; i < cnt; ++i) {
-                R = R + sh.mr[i];
-                Rp = Rp + sh.mp[i];
-                if (sh.mr[i] > 0.0) last_r = blk + i;
-                if (sh.mp[i] > 0.0) last_p = blk + i;
-            }
-        }
+        if (wg_last(1, sh) >= 0) lr = blk + wg_last(1, sh);
+        if (wg_last(2, sh) >= 0) lp_s = blk + wg_last(2, sh);
+        R = R + tot[0];
+        Rp = Rp + tot[1];
     }
-    if (threadIdx.x == 0) {
-        const int mode = (resid && R > 0.0) ? 1 : 0;
-        const double total = mode ? R : (resid ? Rp : R);
-        sh.mode = mode;
-        sh.target = double(a.u[size_t(b) * G1 + a.G]) * total;
-        sh.R = R;
-        sh.sstar = -1;
-        sh.base = 0.0;
-        sh.t1 = kWG;
-        sh.y = -1;
-        sh.jmin = (mode || !resid) ? last_r : last_p;   // for the no-crossing fallback
+    // The draw is from the residual when it has mass; a rejection whose
+    // residual is zero draws from p_j, a bonus draw from p_n (whose residual
+    // terms are p itself).
+    const bool use_r = resid && R > 0.0;
+    const int sel = (resid && !use_r) ? 1 : 0;
+    const double target = double(d.u_final) * (sel ? Rp : R);
+    // Pass 2: the first sub-tile s with positive mass and base(s) + mass(s) > target.
+    int sstar = INT_MAX;
+    if (one) {
+        const int s = int(threadIdx.x);
+        const double vs = sel ? v[1] : v[0], bs = sel ? ex[1] : ex[0];
+        post_first(s < nsub && vs > 0.0 && bs + vs > target, 3, sh);
+        __syncthreads();
+        sstar = wg_first(3, sh);
+        if (s == sstar) sh.base = bs;
+    } else {
+        double P = 0.0;
+        for (int blk = 0; blk < nsub; blk += kWG) {
+            const int s = blk + int(threadIdx.x);
+            double w1[1] = {0.0}, ex1[1], in1[1], tot1[1];
+            if (s < nsub) w1[0] = __longlong_as_double((long long)ld_coherent(mass + 2 * s + sel));
+            wg_scan<1>(w1, ex1, in1, tot1, sh);
+            const double bs = P + ex1[0];
+            post_first(s < nsub && w1[0] > 0.0 && bs + w1[0] > target, 3, sh);
+            __syncthreads();
+            const int f = wg_first(3, sh);
+            if (f != INT_MAX) {
+                sstar = blk + f;
+                if (s == sstar) sh.base = bs;
+                break;
+            }
+            P = P + tot1[0];
+        }
     }
     __syncthreads();
-    const int mode = sh.mode;
-    const bool use_r = resid && mode;          // else: terms are p (bonus draw or zero-residual fallback)
-    const bool from_m = mode || !resid;        // which mass array holds those terms' sums
-    // Pass 2: the first sub-tile whose running sum exceeds the target.
-    double P = 0.0;
-    for (int blk = 0; blk < a.nsub; blk += kStage) {
-        const int cnt = min(kStage, a.nsub - blk);
-        if (a.nsub > kStage) {
-            __syncthreads();
-            if (int(threadIdx.x) < cnt) {
-                sh.mr[threadIdx.x] = __longlong_as_double(ld_coherent(mass + 2 * (blk + threadIdx.x)));
-                sh.mp[threadIdx.x] = __longlong_as_double(ld_coherent(mass + 2 * (blk + threadIdx.x) + 1));
-            }
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            for (int i = 0; i < cnt; ++i) {
-                const double P1 = P + (from_m ? sh.mr[i] : sh.mp[i]);
-                if (P1 > sh.target) { sh.sstar = blk + i; sh.base = P; break; }
-                P = P1;
-            }
-        }
-        __syncthreads();
-        if (sh.sstar >= 0) break;
-    }
-    const int lastpos = (sh.sstar < 0) ? 1 : 0;         // u * R at or beyond the top
-    const int sstar = lastpos ? max(0, sh.jmin) : sh.sstar;
-    const double base = sh.base, target = sh.target;
+    const bool lastpos = sstar == INT_MAX;         // u * R at or beyond the top: last positive term
+    if (lastpos) sstar = max(0, sel ? lp_s : lr);
+    const double base = lastpos ? 0.0 : sh.base;
+    float t[kSubPerThread];
     double rs, ps;
-    sub_sums<ES, ALZ, ALQ>(zrow, qrow, a.V, sstar, d.m, a.c32, d.inv_s, resid, rs, ps);
-    const double v1[1] = {use_r ? rs : ps};
-    double ex[1], tot[1];
-    wg_excl_scan<1>(v1, ex, tot, sh);
+    sub_tile<ES, ALZ, ALQ>(zrow, qrow, a.V, sstar, d.m, a.c32, d.inv_s, resid, use_r, t, rs, ps);
+    const double v1[1] = {sel ? ps : rs};
+    double ex1[1], in1[1], tot1[1];
+    wg_scan<1>(v1, ex1, in1, tot1, sh);
     const int e0 = sstar * kSub + int(threadIdx.x) * kSubPerThread;
-    const int e1 = min(a.V, e0 + kSubPerThread);
-    if (lastpos) {
-        int lp = -1;
-        for (int e = e0; e < e1; ++e) {
-            float r, p;
-            draw_term(load_elem<ES>(zrow, size_t(e)), resid ? qrow[e] : 0.0f, d.m, a.c32, d.inv_s, resid, r, p);
-            if ((use_r ? r : p) > 0.0f) lp = e;
+    int lp = -1;
+#pragma unroll
+    for (int i = 0; i < kSubPerThread; ++i)
+        if (t[i] > 0.0f) lp = e0 + i;
+    post_last(v1[0] > 0.0, 4, sh);
+    post_first(v1[0] > 0.0 && !lastpos && base + in1[0] > target, 5, sh);
+    __syncthreads();
+    const int t1 = wg_first(5, sh), tl = wg_last(4, sh);
+    // The thread holding the draw writes it.
+    int y = -2;
+    if (t1 == INT_MAX) {
+        if (int(threadIdx.x) == max(tl, 0)) y = lp;   // tl < 0 cannot happen: p(argmax) >= 1/V
+    } else if (int(threadIdx.x) == t1) {
+        double acc = base + ex1[0];
+        int yc = -1;
+#pragma unroll
+        for (int i = 0; i < kSubPerThread; ++i) {
+            acc = acc + double(t[i]);
+            if (yc < 0 && t[i] > 0.0f && acc > target) yc = e0 + i;
         }
-        atomicMax(&sh.y, lp);
-        __syncthreads();
-    } else {
-        if (base + (ex[0] + v1[0]) > target) atomicMin(&sh.t1, int(threadIdx.x));
-        __syncthreads();
-        if (int(threadIdx.x) == sh.t1) {
-            double acc = base + ex[0];
-            int y = -1, lp = -1;
-            for (int e = e0; e < e1; ++e) {
-                float r, p;
-                draw_term(load_elem<ES>(zrow, size_t(e)), resid ? qrow[e] : 0.0f, d.m, a.c32, d.inv_s, resid, r, p);
-                const float t = use_r ? r : p;
-                if (t > 0.0f) lp = e;
-                acc = acc + double(t);
-                if (acc > target) { y = e; break; }
-            }
-            sh.y = (y >= 0) ? y : lp;
-        }
-        __syncthreads();
+        y = (yc >= 0) ? yc : lp;
     }
-    if (threadIdx.x == 0) {
-        a.out_tok[size_t(b) * G1 + d.j] = sh.y;
-        if (a.d_r) a.d_r[b] = resid ? float(sh.R) : -1.0f;
+    if (y != -2) {
+        a.out_tok[size_t(b) * G1 + d.j] = y;
+        if (a.d_r) a.d_r[b] = resid ? float(R) : -1.0f;
     }
 }
 
 // Request pass (after the row pass has completed): workgroup w of request b
 // decides the request, streams sub-tiles [w*spw, (w+1)*spw) of the draw row,
 // and the last of the request's nc2 workgroups selects the token and zeroes
-// the request's partials and masses.
+// the request's partials, gathers and masses.
 template <int ES, bool ALZ, bool ALQ>
 __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh) {
     Decision d;
@@ -791,43 +916,59 @@ __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh
     const bool ok = decide<ES>(a, b, w, d, arrive, sh);
     if (!arrive) return;
     const int G1 = a.G + 1;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const bool diag = a.d_lse || a.d_p || a.d_q || a.d_r;
     const void *zrow = nullptr;
     const float *qrow = nullptr;
+    uint64_t *mass = masses(a, b);
     if (ok) {
         zrow = static_cast<const char *>(a.logits) + (size_t(b) * G1 + d.j) * size_t(a.V) * ES;
-        qrow = d.resid ? a.q + (size_t(b) * a.G + d.j) * size_t(a.V) : nullptr;
-        uint64_t *mass = reinterpret_cast<uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
+        qrow = d.resid ? a.q + (size_t(b) * a.G + d.j) * size_t(a.V)
+                       : reinterpret_cast<const float *>(a.ws + a.lay.zero);
         const int s_end = min(a.nsub, (w + 1) * a.spw);
         for (int s0 = w * a.spw; s0 < s_end; s0 += kSubBatch) {
-            double v[2 * kSubBatch], ex[2 * kSubBatch], tot[2 * kSubBatch];
+            double rs[kSubBatch], ps[kSubBatch];
 #pragma unroll
             for (int i = 0; i < kSubBatch; ++i) {
-                double rs = 0.0, ps = 0.0;
-                if (s0 + i < s_end) sub_sums<ES, ALZ, ALQ>(zrow, qrow, a.V, s0 + i, d.m, a.c32, d.inv_s, d.resid, rs, ps);
-                v[i] = rs;
-                v[kSubBatch + i] = ps;
+                float t[kSubPerThread];
+                rs[i] = 0.0; ps[i] = 0.0;
+                if (s0 + i < s_end)
+                    sub_tile<ES, ALZ, ALQ>(zrow, qrow, a.V, s0 + i, d.m, a.c32, d.inv_s, d.resid, true, t, rs[i], ps[i]);
             }
-            wg_excl_scan<2 * kSubBatch>(v, ex, tot, sh);
-            if (int(threadIdx.x) < kSubBatch && s0 + int(threadIdx.x) < s_end) {
-                const int i = threadIdx.x;
-                st_coherent(mass + 2 * (s0 + i), uint64_t(__double_as_longlong(tot[i])));
-                st_coherent(mass + 2 * (s0 + i) + 1, uint64_t(__double_as_longlong(tot[kSubBatch + i])));
+#pragma unroll
+            for (int i = 0; i < kSubBatch; ++i) {
+                rs[i] = wave_sum_d(rs[i]);
+                ps[i] = wave_sum_d(ps[i]);
+            }
+            __syncthreads();
+            if (lane == 0) {
+#pragma unroll
+                for (int i = 0; i < kSubBatch; ++i) {
+                    sh.r.wt[wv][i] = rs[i];
+                    sh.r.wt[wv][kSubBatch + i] = ps[i];
+                }
+            }
+            __syncthreads();
+            if (int(threadIdx.x) < 2 * kSubBatch) {
+                const int q = threadIdx.x, i = q % kSubBatch, which = q / kSubBatch;   // which: 0 residual, 1 target
+                const double m4 = ((sh.r.wt[0][q] + sh.r.wt[1][q]) + sh.r.wt[2][q]) + sh.r.wt[3][q];
+                if (s0 + i < s_end) st_coherent(mass + 2 * (s0 + i) + which, uint64_t(__double_as_longlong(m4)));
             }
         }
     }
     if (!arrive_last(draw_counter(a, b), unsigned(a.nc2), sh)) return;
     if (ok) {
         final_select<ES, ALZ, ALQ>(a, b, d, zrow, qrow, sh);
-        uint64_t *m = reinterpret_cast<uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
-        for (int i = threadIdx.x; i < 2 * a.nsub; i += kWG) st_coherent(m + i, 0ull);
+        for (int i = threadIdx.x; i < 2 * a.nsub; i += kWG) st_coherent(mass + i, 0ull);
     }
     if (diag) write_diag<ES>(a, b, ok, d.n, sh);
     uint64_t *part = partials(a, b);
     for (int i = threadIdx.x; i < (d.n + 1) * a.nc1; i += kWG) part[i] = 0ull;
+    uint64_t *gx = gathered(a, b);
+    for (int i = threadIdx.x; i < d.n; i += kWG) gx[i] = 0ull;
 }
 
-// One workgroup per request (T == 0), after the request's row items: waits
+// One workgroup per request (T == 0), after the request's row waves: waits
 // for every read row, emits the argmax match, and zeroes the partials.
 __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
     const int G = a.G, G1 = G + 1;
@@ -836,20 +977,16 @@ __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
     const int k = threadIdx.x;
     int xk = 0;
     if (k < n) xk = a.x[size_t(b) * G + k];
-    if (threadIdx.x == 0) { sh.jmin = n; sh.bad = 0; }
     if (!wait_partials(a, b, n)) { write_error(a, b); return; }
-    const uint64_t *part = partials(a, b);
-    for (int r = threadIdx.x; r <= n; r += kWG) merge_row_greedy(a, part + size_t(r) * a.nc1, r, sh);
-    __syncthreads();
-    if (k < n) {
-        if (xk < 0 || xk >= a.V) atomicOr(&sh.bad, 1);
-        else if (xk != sh.A[k]) atomicMin(&sh.jmin, k);
-    }
-    __syncthreads();
-    if (sh.bad) {
+    bool bad = merge_rows_greedy(a, b, n, sh);
+    bad |= k < n && (xk < 0 || xk >= a.V);
+    if (__syncthreads_or(bad)) {
         write_error(a, b);
     } else {
-        const int j = sh.jmin;
+        post_first(k < n && xk != sh.A[k], 0, sh);
+        __syncthreads();
+        const int jf = wg_first(0, sh);
+        const int j = (jf == INT_MAX) ? n : jf;
         for (int t = threadIdx.x; t < G1; t += kWG) {
             int v = -1;
             if (t < j) v = a.x[size_t(b) * G + t];
@@ -865,36 +1002,38 @@ __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
 
 // ------------------------------------------------------------- kernels
 
-// Row pass of a sampled verify: one workgroup per (request, row, chunk).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6); }
+__device__ __forceinline__ int row_jobs(const VerifyArgs &a) { return a.B * (a.G + 1) * a.nc1; }
+
+// Row pass of a sampled verify: one wave per (request, row, chunk).
 template <int ES, bool AL>
 __global__ __launch_bounds__(kWG) void k_rows_sampled(VerifyArgs a) {
-    __shared__ Smem sh;
-    const int g1 = (a.G + 1) * a.nc1;
-    const int b = int(blockIdx.x) / g1;
-    row_item_sampled<ES, AL>(a, b, int(blockIdx.x) - b * g1, sh);
+    const int job = int(blockIdx.x) * kWaves + wave_id();
+    if (job < row_jobs(a)) row_wave_sampled<ES, AL>(a, job, int(threadIdx.x) & 63);
 }
 
 // Request pass of a sampled verify: nc2 workgroups per request.
 template <int ES, bool ALZ, bool ALQ>
-__global__ __launch_bounds__(kWG) void k_requests_sampled(VerifyArgs a) {
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_requests_sampled(VerifyArgs a) {
     __shared__ Smem sh;
     const int b = int(blockIdx.x) / a.nc2;
     request_item_sampled<ES, ALZ, ALQ>(a, b, int(blockIdx.x) - b * a.nc2, sh);
 }
 
-// Greedy verify: row items (request-major), then one request item per
-// request (mode 0); or only the row items (mode 1) / request items (mode 2).
+// Greedy verify: row workgroups (4 row waves each, request-major), then one
+// request workgroup per request (mode 0); or only the row workgroups (mode 1)
+// / request workgroups (mode 2).
 template <int ES, bool AL>
 __global__ __launch_bounds__(kWG) void k_verify_greedy(VerifyArgs a) {
     __shared__ Smem sh;
-    const int g1 = (a.G + 1) * a.nc1;
-    const long rows = long(a.B) * g1;
-    const long i = blockIdx.x;
-    if (a.mode == 2 || (a.mode == 0 && i >= rows)) {
-        request_item_greedy(a, int(a.mode == 2 ? i : i - rows), sh);
+    const int jobs = row_jobs(a);
+    const int row_wgs = (jobs + kWaves - 1) / kWaves;
+    const int i = blockIdx.x;
+    if (a.mode == 2 || (a.mode == 0 && i >= row_wgs)) {
+        request_item_greedy(a, a.mode == 2 ? i : i - row_wgs, sh);
     } else {
-        const int b = int(i / g1);
-        row_item_greedy<ES, AL>(a, b, int(i - long(b) * g1), sh);
+        const int job = i * kWaves + wave_id();
+        if (job < jobs) row_wave_greedy<ES, AL>(a, job, int(threadIdx.x) & 63);
     }
 }
 
