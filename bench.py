@@ -27,7 +27,7 @@ import workloads as W  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 KERNEL_SRC = os.path.join(ROOT, "lossless_draft_verification_verify_amd", "csrc", "verify_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_block_verify.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_rows_sampled_block_traffic.md")
 
 
 def algorithmic_bytes(B, G, V, lens, n_rej, esize=2):
@@ -53,16 +53,22 @@ def kernel_sha():
 
 
 def measured_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+    """HBM bytes per launch of the row pass from the committed rocprofv3
+    counter runs (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known
+    size), if they were taken on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            lines = f.read().splitlines()
+    except OSError:
         return None
-    if t.get("kernel_sha") != kernel_sha():
+    kv = {}
+    for line in lines:
+        key, sep, val = line.strip().partition(": ")
+        if sep and key in ("kernel_sha", "kernel", "bytes_per_launch"):
+            kv[key] = val.strip()
+    if kv.get("kernel_sha") != kernel_sha() or "bytes_per_launch" not in kv:
         return None
-    return t.get("bytes_per_launch")
+    return int(kv["bytes_per_launch"])
 
 
 class HipEvents:
@@ -141,20 +147,44 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated in HBM")
+    ap.add_argument("--workload", choices=("block", "greedy", "scheduled"), default="block",
+                    help="block: B=64 gamma=15 V=129280 T=1 (default); greedy: B=64 gamma=7 "
+                         "V=152064 T=0; scheduled: spec_schedule then spec_verify, gamma=15 V=129280")
+    ap.add_argument("--batch", type=int, default=64, help="B of the scheduled workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=0)
     ap.add_argument("--cpu-requests", type=int, default=64)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 20 plain device-to-device copies of MIB MiB (a known-size kernel "
+                         "for scaling the HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(requests shard across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    w = W.block()
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 20}), flush=True)
+        return
+
+    if args.workload == "block":
+        w = W.block()
+    elif args.workload == "greedy":
+        w = W.greedy()
+    else:
+        w = W.scheduled(args.batch)
     B, G, V = w["B"], w["G"], w["V"]
+    T = float(w["T"])
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "block":
         workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
         cpu = cpu_baseline(w, workers, min(args.cpu_requests, B))
 
@@ -165,25 +195,46 @@ def main():
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
 
+    def to_dev(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
     z0 = torch.from_numpy(w["logits"].view(np.int16)).to(dev).view(torch.bfloat16)
-    q0 = torch.from_numpy(w["draft_probs"]).to(dev)
-    x0 = torch.from_numpy(w["draft_tokens"]).to(dev)
-    u0 = torch.from_numpy(w["uniforms"]).to(dev)
-    sets = [(z0, q0, x0, u0)] + [(z0.clone(), q0.clone(), x0.clone(), u0.clone()) for _ in range(args.sets - 1)]
+    q0, x0, u0 = to_dev(w["draft_probs"]), to_dev(w["draft_tokens"]), to_dev(w["uniforms"])
+    clone = (lambda t: None if t is None else t.clone())
+    sets = [(z0, q0, x0, u0)] + [tuple(clone(t) for t in (z0, q0, x0, u0)) for _ in range(args.sets - 1)]
     acc = torch.empty(B, dtype=torch.int32, device=dev)
     tok = torch.empty(B, G + 1, dtype=torch.int32, device=dev)
+    sched = None
+    if args.workload == "scheduled":
+        conf, cost = to_dev(w["confidence"]), to_dev(w["cost_table"])
+        vlen = torch.empty(B, dtype=torch.int32, device=dev)
+        tot = torch.empty(1, dtype=torch.int32, device=dev)
+        tau = torch.empty(1, dtype=torch.float32, device=dev)
+        sched = (conf, cost, w["budget"], vlen, tot, tau)
 
-    # outputs of one call fix the data-dependent byte count (rejecting requests)
-    sv.verify(*sets[0], 1.0, out_accepted=acc, out_tokens=tok)
+    def step(i, row_event=None):
+        zz, qq, xx, uu = sets[i % len(sets)]
+        vl = None
+        if sched is not None:
+            conf, cost, budget, vlen, tot, tau = sched
+            sv.schedule(conf, cost, budget, out_verify_len=vlen, out_total=tot, out_expected=tau)
+            vl = vlen
+        sv.verify(zz, qq, xx, uu, T, vl, out_accepted=acc, out_tokens=tok, row_pass_event=row_event)
+
+    # outputs of one call fix the data-dependent counts (verify lengths, rejecting requests)
+    step(0)
     torch.cuda.synchronize()
     a = acc.cpu().numpy()
-    lens = np.full(B, G)
-    n_rej = int((a < lens).sum())
-    algo = algorithmic_bytes(B, G, V, lens, n_rej)
-    row_algo = row_pass_bytes(V, lens)
+    lens = sched[3].cpu().numpy().astype(np.int64) if sched is not None else np.full(B, G)
+    n_rej = int((a < lens).sum()) if T > 0 else 0
+    esize = 2
+    algo = algorithmic_bytes(B, G, V, lens, n_rej, esize)
+    if T == 0:                                   # no q rows, no uniforms
+        algo = int((lens + 1).sum()) * V * esize + int(lens.sum()) * 4 + B * (4 + 4 * (G + 1))
+    row_algo = row_pass_bytes(V, lens, esize)
 
     for i in range(args.warmup):
-        sv.verify(*sets[i % len(sets)], 1.0, out_accepted=acc, out_tokens=tok)
+        step(i)
     torch.cuda.synchronize()
 
     K = args.steps
@@ -196,7 +247,7 @@ def main():
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(K):
-        sv.verify(*sets[i % len(sets)], 1.0, out_accepted=acc, out_tokens=tok)
+        step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -207,20 +258,30 @@ def main():
     torch.cuda.synchronize()
     for i in range(K):
         hev.record(3 * i, sh)
-        sv.verify(*sets[i % len(sets)], 1.0, out_accepted=acc, out_tokens=tok,
-                  row_pass_event=hev.ev[3 * i + 1])
+        step(i, row_event=hev.ev[3 * i + 1])
         hev.record(3 * i + 2, sh)
     torch.cuda.synchronize()
     call = np.array([hev.ms(3 * i, 3 * i + 2) for i in range(K)])      # ms per call
-    rows_ms = np.array([hev.ms(3 * i, 3 * i + 1) for i in range(K)])   # ms of the row pass
-    req_ms = np.array([hev.ms(3 * i + 1, 3 * i + 2) for i in range(K)])  # ms of the request pass
+    rows_ms = np.array([hev.ms(3 * i, 3 * i + 1) for i in range(K)])   # ms up to the row-pass event
+    req_ms = np.array([hev.ms(3 * i + 1, 3 * i + 2) for i in range(K)])  # ms after it
     hev.close()
     ms_step = total_ms / K
     kern_ms = float(rows_ms.mean())
     positions = int(lens.sum())
     value = positions / (ms_step * 1e-3)
     achieved = row_algo / (kern_ms * 1e-3) / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic() if args.workload == "block" else None
+    if args.workload == "block":
+        desc = ("block-diffusion draft verification: B=64, gamma=15, V=129280, bf16 logits "
+                "(Zipf(1.1) over a per-row permutation), fp32 draft probabilities, T=1")
+        kname = "k_rows_sampled (row pass: max and exp-sum of every read target row)"
+    elif args.workload == "greedy":
+        desc = "greedy draft verification: B=64, gamma=7, V=152064, bf16 logits N(0,4), T=0"
+        kname = "k_verify_greedy (one launch: argmax row waves, then one workgroup per request)"
+    else:
+        desc = (f"confidence-scheduled verification: spec_schedule (token budget {w['budget']}, "
+                f"cost 1 + 0.02 T) then spec_verify, B={B}, gamma=15, V=129280, bf16, T=1")
+        kname = "spec_schedule + k_rows_sampled (time up to the row-pass event includes the scheduler)"
     out = {
         "metric": "verified draft positions/sec and achieved HBM GB/s (% peak), B=64 gamma=15 V=129k",
         "value": round(value, 1),
@@ -234,14 +295,13 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "block-diffusion draft verification: B=64, gamma=15, V=129280, bf16 logits "
-                               "(Zipf(1.1) over a per-row permutation), fp32 draft probabilities, T=1",
-                   "B": B, "gamma": G, "V": V, "temperature": 1.0, "logits": "bf16", "rotating_sets": len(sets),
-                   "verified_positions_per_step": positions, "rejecting_requests": n_rej},
+        "config": {"workload": desc, "B": B, "gamma": G, "V": V, "temperature": T, "logits": "bf16",
+                   "rotating_sets": len(sets), "verified_positions_per_step": positions,
+                   "rejecting_requests": n_rej},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "k_rows_sampled (row pass: max and exp-sum of every read target row)",
+                     "kernel": kname,
                      "algorithmic_bytes_per_launch": row_algo,
                      "launch_ms_mean": round(kern_ms, 5),
                      "launch_ms_p10_p50_p90": [round(float(np.percentile(rows_ms, p)), 5) for p in (10, 50, 90)]},
@@ -249,7 +309,7 @@ def main():
                  "achieved_GBps": round(algo / (ms_step * 1e-3) / 1e9, 1),
                  "frac": round(algo / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                  "ms_p10_p50_p90": [round(float(np.percentile(call, p)), 5) for p in (10, 50, 90)],
-                 "request_pass_ms_mean": round(float(req_ms.mean()), 5)},
+                 "after_row_pass_ms_mean": round(float(req_ms.mean()), 5)},
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }

@@ -10,18 +10,23 @@
 // The result is bit-identical to the sequential float64 loop: the survival
 // products and the running sum tau are formed in exactly that loop's order;
 // only the independent parts (sorting, the theta comparisons, the length
-// tally) run in parallel.
+// tally) run in parallel.  The work is a chain of dependent steps on one
+// workgroup, so the design minimises round trips and serial steps:
 //
-//   1. one thread per request: fp64 CumProd; detect whether survival is
-//      non-increasing along the request (always true for c in [0, 1]);
-//   2. bitonic sort of (s, k, b) keys in LDS, candidates first;
-//   3. contiguity: a candidate can be kept only if all shallower positions of
-//      its request are candidates placed before it (true for every candidate
-//      when survival is non-increasing);
-//   4. one wave forms tau_m = B + s_(0) + ... + s_(m-1) sequentially over the
-//      kept-able candidates (at most budget - B of them can be kept);
-//   5. all threads test theta_{m+1} > theta_m and T <= budget in parallel; the
-//      first failure m* ends the scan; lengths are tallied from the first m*.
+//   1. every confidence and every cost entry the scan can reach is loaded into
+//      LDS at once (one memory round trip);
+//   2. one thread per request: fp64 CumProd in place; detect whether survival
+//      is non-increasing along each request (always true for c in [0, 1]);
+//   3. bitonic sort of (s, k*B + b) keys in LDS, candidates first (the key's
+//      second half orders equal survivals by k, then b, with no division);
+//   4. contiguity (only when some survival increases): a candidate can be kept
+//      only if all shallower positions of its request are candidates placed
+//      before it;
+//   5. one wave walks the sorted candidates 64 at a time: tau is extended in
+//      candidate order, lane by lane, then the 64 tests theta_{m+1} > theta_m
+//      run at once; the walk stops at the block holding the first failure
+//      (or at the budget), so it visits only about m* + 64 candidates;
+//   6. lengths are tallied from the first m* candidates.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -32,91 +37,174 @@
 namespace sv {
 namespace {
 
-constexpr int kSchedThreads = 1024;
+constexpr int kMaxThreads = 1024;
 constexpr int kMaxCand = 4096;
+constexpr int kRegSort = 1024;     // at most this many slots: one per thread, sorted in registers
+constexpr int kPad = 0x7fffffff;
 
 struct SchedSmem {
-    double key[kMaxCand];      // survival (sort key), then tau_m
-    int id[kMaxCand];          // b * G + k, or INT_MAX for padding
-    int pos[kMaxCand];         // sorted position of each candidate id (or -1)
+    double key[kMaxCand];      // confidence, then survival (slot = b * G + k), then sorted survival
+    int id[kMaxCand];          // k * B + b, or kPad for padding / non-candidates
+    int pos[kMaxCand];         // sorted position of each candidate (slot b * G + k), or -1
     int len[kMaxCand];         // per request kept length (B <= kMaxCand)
-    int nonincr, ncand, nvalid, mstar;
+    float cost[kMaxCand + 1];  // cost[B + m] for m = 0..min(B*G, budget - B)
+    double xk[2][kRegSort];    // register sort: exchange buffers for strides >= 64
+    int xi[2][kRegSort];
+    int nvalid, mstar;
+    double taustar;            // tau_{m*}
 };
 
-// Order: larger survival first; equal survival -> smaller k, then smaller b.
-__device__ __forceinline__ bool before(double s1, int id1, double s2, int id2, int G, int B) {
-    if (s1 != s2) return s1 > s2;
-    if (id1 == id2) return false;
-    if (id2 == 0x7fffffff) return true;
-    if (id1 == 0x7fffffff) return false;
-    const int k1 = id1 % G, k2 = id2 % G;
-    if (k1 != k2) return k1 < k2;
-    return id1 / G < id2 / G;
+// Order: larger survival first; equal survival -> smaller k, then smaller b
+// (the id k * B + b compares in exactly that order; padding sorts last).
+__device__ __forceinline__ bool before(double s1, int id1, double s2, int id2) {
+    return s1 > s2 || (s1 == s2 && id1 < id2);
 }
 
-__global__ __launch_bounds__(kSchedThreads) void k_schedule(ScheduleArgs a) {
+__device__ __forceinline__ double lane_d(double x, int l) {
+    const uint64_t v = uint64_t(__double_as_longlong(x));
+    const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), l));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), l));
+    return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+}
+
+// Sorting slot i of Np: its survival when it is a candidate, else -inf padding.
+__device__ __forceinline__ void slot_key(const SchedSmem &sh, int i, int N, int B, int G, double eps, double &s,
+                                         int &id) {
+    s = -__builtin_inf();
+    id = kPad;
+    if (i < N && sh.key[i] > eps) {
+        const int b = i / G, k = i - b * G;
+        s = sh.key[i];
+        id = k * B + b;
+    }
+}
+
+// One block of the grid; blockDim.x = max(64, Np) when Np <= kRegSort (the
+// register sort), else kMaxThreads.
+__global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
     __shared__ SchedSmem sh;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, nth = blockDim.x;
     const int B = a.B, G = a.G, N = B * G;
     const double eps = double(a.eps);
-    if (tid == 0) { sh.nonincr = 1; sh.ncand = 0; sh.mstar = 0x7fffffff; }
-    __syncthreads();
-
-    // 1. survival, sequential product per request.
-    for (int b = tid; b < B; b += kSchedThreads) {
-        double acc = 1.0, prev = 1.0;
-        bool ok = true;
-        for (int k = 0; k < G; ++k) {
-            acc = acc * double(a.conf[size_t(b) * G + k]);
-            if (k > 0 && !(acc <= prev)) ok = false;
-            prev = acc;
-            sh.key[b * G + k] = acc;
-        }
-        sh.len[b] = 0;
-        if (!ok) atomicAnd(&sh.nonincr, 0);
-    }
-    __syncthreads();
-
-    // 2. bitonic sort of candidates; non-candidates become -inf padding.
+    const int mt_max = min(N, a.budget - B);          // kept drafts never exceed this
     int Np = 1;
     while (Np < N) Np <<= 1;
-    for (int i = tid; i < Np; i += kSchedThreads) {
-        if (i < N && sh.key[i] > eps) {
-            sh.id[i] = i;
-        } else {
-            sh.key[i] = -__builtin_inf();
-            sh.id[i] = 0x7fffffff;
-        }
-    }
+
+    // 1. every input the scan can read, in one round trip.
+    for (int i = tid; i < N; i += nth) sh.key[i] = double(a.conf[i]);
+    for (int i = tid; i <= mt_max; i += nth) sh.cost[i] = a.cost[B + i];
     __syncthreads();
-    for (int size = 2; size <= Np; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = tid; t < Np / 2; t += kSchedThreads) {
-                const int lo = 2 * t - (t & (stride - 1));
-                const int hi = lo + stride;
-                const bool up = ((lo & size) == 0);         // this block sorts "before" first
-                const double s1 = sh.key[lo], s2 = sh.key[hi];
-                const int i1 = sh.id[lo], i2 = sh.id[hi];
-                const bool swap = up ? before(s2, i2, s1, i1, G, B) : before(s1, i1, s2, i2, G, B);
-                if (swap) { sh.key[lo] = s2; sh.key[hi] = s1; sh.id[lo] = i2; sh.id[hi] = i1; }
+
+    // 2. survival, sequential product per request, in place (LDS reads issued
+    //    together for up to 16 drafts).
+    bool mono = true;
+    for (int b = tid; b < B; b += nth) {
+        double acc = 1.0, prev = 1.0;
+        if (G <= 16) {
+            double c[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) c[k] = (k < G) ? sh.key[b * G + k] : 1.0;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                if (k < G) {
+                    acc = acc * c[k];
+                    if (k > 0 && !(acc <= prev)) mono = false;
+                    prev = acc;
+                    sh.key[b * G + k] = acc;
+                }
             }
-            __syncthreads();
+        } else {
+            for (int k = 0; k < G; ++k) {
+                acc = acc * sh.key[b * G + k];
+                if (k > 0 && !(acc <= prev)) mono = false;
+                prev = acc;
+                sh.key[b * G + k] = acc;
+            }
         }
+        sh.len[b] = 0;
+    }
+    const bool nonincr = __syncthreads_and(mono);
+
+    // 3. sort the candidates (s desc, k asc, b asc); padding last.
+    int ncand;
+    if (Np <= kRegSort) {
+        // One slot per thread, bitonic network in registers: partners closer
+        // than a wave exchange by shuffles, farther ones through LDS (two
+        // buffers, so one barrier per stage).
+        double s;
+        int id;
+        slot_key(sh, tid, N, B, G, eps, s, id);
+        int buf = 0;
+        for (int size = 2; size <= Np; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                double s2;
+                int id2;
+                if (stride < 64) {
+                    s2 = __shfl_xor(s, stride);
+                    id2 = __shfl_xor(id, stride);
+                } else {
+                    sh.xk[buf][tid] = s;
+                    sh.xi[buf][tid] = id;
+                    __syncthreads();
+                    s2 = sh.xk[buf][tid ^ stride];
+                    id2 = sh.xi[buf][tid ^ stride];
+                    buf ^= 1;
+                }
+                const bool keep_first = ((tid & stride) == 0) == ((tid & size) == 0);
+                const bool mine_first = before(s, id, s2, id2);
+                if (keep_first != mine_first) { s = s2; id = id2; }
+            }
+        }
+        ncand = __syncthreads_count(tid < Np && id != kPad);
+        if (tid < Np) { sh.key[tid] = s; sh.id[tid] = id; }
+        __syncthreads();
+    } else {
+        for (int i = tid; i < Np; i += nth) {
+            double v;
+            int id;
+            slot_key(sh, i, N, B, G, eps, v, id);
+            sh.key[i] = v;          // slot i is read only by its own thread here
+            sh.id[i] = id;
+        }
+        __syncthreads();
+        for (int size = 2; size <= Np; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int t = tid; t < Np / 2; t += nth) {
+                    const int lo = 2 * t - (t & (stride - 1));
+                    const int hi = lo + stride;
+                    const bool up = ((lo & size) == 0);         // this block sorts "before" first
+                    const double s1 = sh.key[lo], s2 = sh.key[hi];
+                    const int i1 = sh.id[lo], i2 = sh.id[hi];
+                    const bool swap = up ? before(s2, i2, s1, i1) : before(s1, i1, s2, i2);
+                    if (swap) { sh.key[lo] = s2; sh.key[hi] = s1; sh.id[lo] = i2; sh.id[hi] = i1; }
+                }
+                __syncthreads();
+            }
+        }
+        // Candidates (finite survival) sort before the -inf padding: count the prefix.
+        if (tid == 0) {
+            int lo = 0, hi = Np;                              // first padding slot
+            while (lo < hi) { const int mid = (lo + hi) >> 1; if (sh.id[mid] != kPad) lo = mid + 1; else hi = mid; }
+            sh.nvalid = lo;
+        }
+        __syncthreads();
+        ncand = sh.nvalid;
+        __syncthreads();
     }
 
-    // 3. candidates and contiguity.
-    for (int i = tid; i < N; i += kSchedThreads) sh.pos[i] = -1;
-    __syncthreads();
-    for (int p = tid; p < Np; p += kSchedThreads) {
-        const int id = sh.id[p];
-        if (id != 0x7fffffff) { sh.pos[id] = p; atomicAdd(&sh.ncand, 1); }
-    }
-    __syncthreads();
-    const int ncand = sh.ncand;
-    if (!sh.nonincr) {
-        for (int p = tid; p < ncand; p += kSchedThreads) {
+    // 4. contiguity: only when some survival increases along a request.
+    if (!nonincr) {
+        for (int i = tid; i < N; i += nth) sh.pos[i] = -1;
+        __syncthreads();
+        for (int p = tid; p < ncand; p += nth) {
             const int id = sh.id[p];
-            const int b = id / G, k = id - b * G;
+            const int k = id / B, b = id - k * B;
+            sh.pos[b * G + k] = p;
+        }
+        __syncthreads();
+        for (int p = tid; p < ncand; p += nth) {
+            const int id = sh.id[p];
+            const int k = id / B, b = id - k * B;
             bool valid = true;
             int prevp = -1;
             for (int kk = 0; kk <= k; ++kk) {
@@ -144,56 +232,67 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(ScheduleArgs a) {
             if (tid == 0) sh.nvalid = w;
         }
         __syncthreads();
-    } else {
-        if (tid == 0) sh.nvalid = ncand;
-        __syncthreads();
+        ncand = sh.nvalid;
     }
-    const int nvalid = sh.nvalid;
+    const int mt = min(ncand, mt_max);                // at most budget - B can be kept
 
-    // 4. tau_m for m = 0..mt, sequential fp64 in candidate order (key[m] = s_(m)).
-    const int mt = min(nvalid, a.budget - B);        // at most budget - B can be kept
-    __shared__ double tau[kMaxCand + 1];
+    // 5. walk the sorted candidates; m* = first m with !(theta_{m+1} > theta_m).
+    //    tau_m = B + s_(0) + ... + s_(m-1) in candidate order; theta_m = tau_m / cost[B + m].
     if (tid < 64) {
         double t = double(B);
-        if (tid == 0) tau[0] = t;
+        if (mt == 0 && lane == 0) { sh.mstar = 0; sh.taustar = t; }
         for (int base = 0; base < mt; base += 64) {
-            const double v = (base + tid < mt) ? sh.key[base + tid] : 0.0;
+            const int m = base + lane;
+            const double sm = (m < mt) ? sh.key[m] : 0.0;
+            double tau0 = 0.0, tau1 = 0.0;
             const int cnt = min(64, mt - base);
-            for (int i = 0; i < cnt; ++i) {
-                const double si = __shfl(v, i);
-                t = t + si;
-                if (tid == 0) tau[base + i + 1] = t;
+#pragma unroll
+            for (int j = 0; j < 64; ++j) {
+                if (j < cnt) {
+                    if (lane == j) tau0 = t;
+                    t = t + lane_d(sm, j);
+                    if (lane == j) tau1 = t;
+                }
             }
+            bool fail = false;
+            if (m < mt) {
+                const double th0 = tau0 / double(sh.cost[m]);
+                const double th1 = tau1 / double(sh.cost[m + 1]);
+                fail = !(th1 > th0);
+            }
+            const unsigned long long f = __ballot(fail);
+            if (f) {
+                const int first = __builtin_ctzll(f);
+                if (lane == first) { sh.mstar = base + first; sh.taustar = tau0; }
+                break;
+            }
+            if (base + 64 >= mt && lane == 0) { sh.mstar = mt; sh.taustar = t; }   // no failure up to mt
         }
     }
     __syncthreads();
+    const int mstar = sh.mstar;
 
-    // 5. first failure of "theta improves" (the budget caps m at mt).
-    for (int m = tid; m < mt; m += kSchedThreads) {
-        const int T = B + m;
-        const double th0 = tau[m] / double(a.cost[T]);
-        const double th1 = tau[m + 1] / double(a.cost[T + 1]);
-        if (!(th1 > th0)) atomicMin(&sh.mstar, m);
-    }
-    __syncthreads();
-    const int mstar = min(sh.mstar, mt);
-    for (int m = tid; m < mstar; m += kSchedThreads) {
+    // 6. lengths from the first m* candidates, tau_{m*} for the caller.
+    for (int m = tid; m < mstar; m += nth) {
         const int id = sh.id[m];
-        const int b = id / G, k = id - b * G;
+        const int k = id / B, b = id - k * B;
         atomicMax(&sh.len[b], k + 1);
     }
     __syncthreads();
-    for (int b = tid; b < B; b += kSchedThreads) a.out_len[b] = sh.len[b];
+    for (int b = tid; b < B; b += nth) a.out_len[b] = sh.len[b];
     if (tid == 0) {
         a.out_T[0] = B + mstar;
-        if (a.out_tau) a.out_tau[0] = float(tau[mstar]);
+        if (a.out_tau) a.out_tau[0] = float(sh.taustar);
     }
 }
 
 }  // namespace
 
 int launch_schedule(const ScheduleArgs &a, void *stream) {
-    hipLaunchKernelGGL(k_schedule, dim3(1), dim3(kSchedThreads), 0, static_cast<hipStream_t>(stream), a);
+    int Np = 1;
+    while (Np < a.B * a.G) Np <<= 1;
+    const int threads = (Np <= kRegSort) ? (Np < 64 ? 64 : Np) : kMaxThreads;
+    hipLaunchKernelGGL(k_schedule, dim3(1), dim3(threads), 0, static_cast<hipStream_t>(stream), a);
     return int(hipGetLastError());
 }
 

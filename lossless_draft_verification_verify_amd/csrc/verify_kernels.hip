@@ -361,6 +361,14 @@ __device__ void write_error(const VerifyArgs &a, int b) {
 __device__ bool wait_partials(const VerifyArgs &a, int b, int n) {
     const uint64_t *part = partials(a, b);
     const int np = (n + 1) * a.nc1;
+    // One lane first waits for the request's last-dispatched row wave (row n,
+    // last chunk), so the workgroup does not flood memory with polls while the
+    // row pass is still streaming; then every partial is checked.
+    if (threadIdx.x == 0) {
+        for (uint32_t spins = 0; spins < a.spin_limit && !valid(ld_coherent(part + np - 1)); ++spins)
+            __builtin_amdgcn_s_sleep(8);
+    }
+    __syncthreads();
     for (uint32_t spins = 0;; ++spins) {
         bool ready = true;
         for (int i = threadIdx.x; i < np; i += kWG) ready &= valid(ld_coherent(part + i));   // no short circuit: loads overlap

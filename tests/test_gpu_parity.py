@@ -175,6 +175,27 @@ def test_schedule_random_against_oracle():
         assert abs(float(tau.item()) - np.float32(tauo)) <= 1e-6 * max(1.0, tauo), trial
 
 
+@pytest.mark.parametrize("B,G,slope,extra", [
+    (256, 16, 0.0, 130),       # 4096 candidates; theta always improves: the budget stops the walk
+    (64, 15, 0.001, 400),      # the walk crosses several 64-candidate blocks before theta stops it
+    (4096, 1, 0.0005, 3000),   # one draft per request, 4096 requests
+    (1, 255, 0.002, 255),      # one request, the deepest block
+    (3, 0, 0.02, 2),           # no drafts at all
+    (64, 15, 5.0, 50),         # steep cost: nothing is worth verifying
+])
+def test_schedule_large_and_block_boundaries(B, G, slope, extra):
+    g0 = np.random.default_rng(B * 1000 + G)
+    conf = (1 / (1 + np.exp(-g0.normal(2.0, 1.0, size=(B, G))))).astype(np.float32)
+    budget = min(B + extra, B * (G + 1))
+    cost = (1.0 + slope * np.arange(budget + 2)).astype(np.float32)
+    vl, T, tau = sv.schedule(torch.from_numpy(conf).cuda(), torch.from_numpy(cost).cuda(), budget)
+    torch.cuda.synchronize()
+    lo, To, tauo = oracle.schedule(conf, cost, budget)
+    np.testing.assert_array_equal(vl.cpu().numpy(), lo)
+    assert int(T.item()) == To
+    assert abs(float(tau.item()) - np.float32(tauo)) <= 1e-6 * max(1.0, tauo)
+
+
 # ------------------------------------------------------------ edge cases
 
 def _rand_workload(name, B, G, V, T=1.0, dtype="bf16", seed=0, zscale=2.0):
