@@ -121,24 +121,26 @@ def _oracle_slice(args):
 _CPU_W = None
 
 
-def cpu_baseline(w, workers, reqs):
-    """Time the float64 oracle on host cores over the first `reqs` requests."""
+def cpu_baseline(w, workers, reqs, reps=6):
+    """Time the float64 oracle on host cores: the first `reqs` requests of the
+    workload, verified `reps` times over (about 10 s of summed CPU work)."""
     global _CPU_W
     import multiprocessing as mp
     _CPU_W = w
     chunk = max(1, reqs // workers)
-    parts = [(i, min(reqs, i + chunk)) for i in range(0, reqs, chunk)]
+    parts = [(i, min(reqs, i + chunk)) for i in range(0, reqs, chunk)] * reps
+    procs = min(workers, len(parts))
     ctx = mp.get_context("fork")                 # before any GPU initialisation
     t0 = time.perf_counter()
-    with ctx.Pool(processes=min(workers, len(parts))) as pool:
+    with ctx.Pool(processes=procs) as pool:
         busy = pool.map(_oracle_slice, parts)
     wall = time.perf_counter() - t0
-    positions = reqs * w["G"]
-    return {"value": positions / wall, "unit": "verified draft positions/s", "cores": min(workers, len(parts)),
+    positions = reqs * w["G"] * reps
+    return {"value": positions / wall, "unit": "verified draft positions/s", "cores": procs,
             "kind": "oracle",
             "sample": f"{reqs} of {w['B']} requests of the same workload (all {w['G']} positions each), "
-                      f"float64 numpy oracle, {len(parts)} slices in a process pool; wall {wall:.2f} s, "
-                      f"summed worker time {sum(busy):.2f} s"}
+                      f"verified {reps} times over by the float64 numpy oracle in {len(parts)} slices "
+                      f"over a {procs}-process pool; wall {wall:.2f} s, summed worker time {sum(busy):.2f} s"}
 
 
 def main():
