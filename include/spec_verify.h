@@ -153,6 +153,15 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype,
                           const spec_verify_diag_t *diag,
                           void *workspace, size_t workspace_bytes, spec_stream_t stream);
 
+/*
+ * Number of kernel launches spec_verify makes for this shape on the current
+ * device, with 16-byte-aligned target_logits: 2 for T > 0 (the pass over the
+ * target rows, then the per-request pass); for T == 0, 1 when the per-request
+ * work shares the row launch and 2 when it runs as a second launch.  -1 on
+ * invalid arguments or a failed device query.  Host-only; enqueues nothing.
+ */
+int32_t spec_verify_launches(int32_t B, int32_t G, int32_t V, spec_dtype_t target_dtype, float temperature);
+
 /* Bytes of device workspace spec_schedule needs (currently 0: it works in LDS). */
 size_t spec_schedule_workspace_bytes(int32_t B, int32_t G);
 

@@ -29,6 +29,7 @@ SPEC_DTYPE_BF16 = 1
 EXPORTS = (
     "spec_verify_workspace_bytes",
     "spec_verify",
+    "spec_verify_launches",
     "spec_schedule_workspace_bytes",
     "spec_schedule",
     "spec_status_string",
@@ -70,6 +71,8 @@ def load():
     lib.spec_verify.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp,
                                 ctypes.POINTER(DiagT), vp, sz, vp]
     lib.spec_verify.restype = ctypes.c_int
+    lib.spec_verify_launches.argtypes = [i32, i32, i32, ctypes.c_int, f32]
+    lib.spec_verify_launches.restype = i32
     lib.spec_schedule_workspace_bytes.argtypes = [i32, i32]
     lib.spec_schedule_workspace_bytes.restype = sz
     lib.spec_schedule.argtypes = [vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
@@ -86,6 +89,10 @@ def status_string(status):
 
 def verify_workspace_bytes(B, G, V, dtype_code):
     return int(load().spec_verify_workspace_bytes(B, G, V, dtype_code))
+
+
+def verify_launches(B, G, V, dtype_code, T):
+    return int(load().spec_verify_launches(B, G, V, dtype_code, ctypes.c_float(T)))
 
 
 def schedule_workspace_bytes(B, G):

@@ -66,6 +66,15 @@ long resident_capacity(int dev, bool az, int es) {
     return long(o) * d.cus;
 }
 
+// Greedy launch plan: whether the per-request workgroups share the row
+// launch (they wait for their rows, so they stay below half the resident
+// capacity).  -1 on a device query failure.
+int greedy_one_launch(int dev, bool az, int es, long B) {
+    const long cap = resident_capacity(dev, az, es);
+    if (cap <= 0) return -1;
+    return B <= cap / 2;
+}
+
 }  // namespace
 
 extern "C" {
@@ -165,10 +174,10 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
     // share the row launch while they stay below half the resident capacity.
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SPEC_ERR_DEVICE;
-    const long cap = resident_capacity(dev, az, es);
-    if (cap <= 0) return SPEC_ERR_DEVICE;
+    const int one = greedy_one_launch(dev, az, es, B);
+    if (one < 0) return SPEC_ERR_DEVICE;
     a.nc2 = 1;
-    if (long(B) <= cap / 2) {
+    if (one) {
         a.mode = 0;
         if (sv::launch_verify_greedy(a, az, es, int(row_wgs + B), stream) != 0) return SPEC_ERR_DEVICE;
         if (row_event && hipEventRecord(row_event, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -181,6 +190,17 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
         return SPEC_ERR_DEVICE;
     a.mode = 2;
     return sv::launch_verify_greedy(a, az, es, B, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+}
+
+int32_t spec_verify_launches(int32_t B, int32_t G, int32_t V, spec_dtype_t dt, float temperature) {
+    const int es = esize_of(int(dt));
+    if (es == 0 || check_verify_shape(B, G, V, es) != SPEC_OK) return -1;
+    if (!std::isfinite(temperature) || temperature < 0.0f) return -1;
+    if (temperature > 0.0f) return 2;                 // row pass, then request pass
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    const int one = greedy_one_launch(dev, (size_t(V) * es) % 16 == 0, es, B);
+    return one < 0 ? -1 : (one ? 1 : 2);
 }
 
 size_t spec_schedule_workspace_bytes(int32_t, int32_t) { return 0; }

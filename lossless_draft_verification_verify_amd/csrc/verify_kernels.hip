@@ -706,11 +706,6 @@ __device__ __forceinline__ double target_prob(float z, float m, float c) {
     const float R = m * c;
     return finitef(R) ? exp2(double(z) * double(c) - double(R)) : exp2((double(z) - double(m)) * double(c));
 }
-// log-sum-exp of the row at temperature T: ln sum_v e^(z_v/T) = R ln 2 + ln S.
-__device__ __forceinline__ double row_lse(float m, double S, float c, double T) {
-    const float R = m * c;
-    return finitef(R) ? double(R) * 0.69314718055994530942 + log(S) : double(m) / T + log(S);
-}
 
 // All chunk partials and gathers of the request are complete (written by the
 // previous launch): merge every row, run the accept tests, find the first
@@ -774,21 +769,24 @@ __device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, bool &arr
     return true;
 }
 
-// Diagnostics of request b (only when requested), from the merged rows.
+// Diagnostics of request b (only when requested), from the merged rows.  In
+// fp32 (their tolerance is far above fp32 rounding), so this path costs the
+// kernel no registers beyond the hot path's.
 template <int ES>
 __device__ void write_diag(const VerifyArgs &a, int b, bool ok, int n, Smem &sh) {
     const int G = a.G, G1 = G + 1;
     const float qnan = __builtin_nanf("");
-    const double T64 = double(a.T);
     for (int t = threadIdx.x; t < G1; t += kWG) {
         float lse = qnan, pv = qnan, qv = qnan;
         if (ok && t <= n) {
-            lse = float(row_lse(sh.M[t], sh.S[t], a.c32, T64));
+            const float m = sh.M[t], S = float(sh.S[t]), R = m * a.c32;
+            lse = finitef(R) ? R * 0.6931471805599453f + logf(S) : m / a.T + logf(S);
             if (t < n) {
                 const int xt = a.x[size_t(b) * G + t];
                 const float zt = load_elem<ES>(a.logits, (size_t(b) * G1 + t) * size_t(a.V) + size_t(xt));
                 qv = a.q[(size_t(b) * G + t) * size_t(a.V) + size_t(xt)];
-                pv = float(target_prob(zt, sh.M[t], a.c32) / sh.S[t]);
+                const float e = finitef(R) ? exp2_fast(__builtin_fmaf(zt, a.c32, -R)) : exp2_fast((zt - m) * a.c32);
+                pv = e / S;
             }
         }
         if (a.d_lse) a.d_lse[size_t(b) * G1 + t] = lse;

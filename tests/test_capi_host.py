@@ -57,6 +57,15 @@ def test_workspace_query():
     assert _capi.schedule_workspace_bytes(64, 15) == 0
 
 
+def test_verify_launches_rejects_bad_arguments():
+    # Invalid shapes, dtype or temperature give -1 before any device query.
+    assert _capi.verify_launches(0, 15, 100, 1, 1.0) == -1
+    assert _capi.verify_launches(1, 256, 100, 1, 1.0) == -1
+    assert _capi.verify_launches(1, 3, 100, 7, 1.0) == -1
+    assert _capi.verify_launches(1, 3, 100, 1, -1.0) == -1
+    assert _capi.verify_launches(1, 3, 100, 1, float("nan")) == -1
+
+
 def _verify(**kw):
     args = dict(logits=Z, dtype_code=1, q=Q, x=X, u=U, vlen=0, B=4, G=3, V=1000, T=1.0, out_acc=OA,
                 out_tok=OT, diag=None, ws=WS, ws_bytes=1 << 20, stream=0)

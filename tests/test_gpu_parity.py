@@ -298,6 +298,15 @@ def test_many_requests_fused_and_split_launch():
     check(_rand_workload("many_split", 1500, 1, 64, seed=13))
 
 
+def test_launch_plan_query():
+    from lossless_draft_verification_verify_amd import _capi
+    torch.cuda.init()
+    assert _capi.verify_launches(64, 15, 129280, _capi.SPEC_DTYPE_BF16, 1.0) == 2
+    assert _capi.verify_launches(64, 7, 152064, _capi.SPEC_DTYPE_BF16, 0.0) == 1
+    # far more requests than half the resident workgroups: the greedy call splits
+    assert _capi.verify_launches(60000, 1, 64, _capi.SPEC_DTYPE_BF16, 0.0) == 2
+
+
 def test_workspace_reuse_and_determinism():
     w1 = W.block(B=8, G=15, V=20000, seed=5)
     w2 = _rand_workload("small", 3, 2, 100, seed=12)
