@@ -189,7 +189,17 @@ __device__ __forceinline__ int row16_and(int x) {
     x = x & dpp_i<kHalfMirror>(x);
     return x & dpp_i<kMirror>(x);
 }
+__device__ __forceinline__ int row16_min_i(int x) {
+    x = min(x, dpp_i<kXor1>(x));
+    x = min(x, dpp_i<kXor2>(x));
+    x = min(x, dpp_i<kHalfMirror>(x));
+    return min(x, dpp_i<kMirror>(x));
+}
 // Whole-wave results, uniform across the wave.
+__device__ __forceinline__ int wave_min_i(int x) {
+    x = row16_min_i(x);
+    return min(min(lane_i(x, 0), lane_i(x, 16)), min(lane_i(x, 32), lane_i(x, 48)));
+}
 __device__ __forceinline__ float wave_max(float x) {
     x = row16_max(x);
     return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
@@ -251,16 +261,6 @@ __device__ __forceinline__ void row16_argmax(float &v, int &i, int &nan) {
     am_step<kXor2>(v, i, nan);
     am_step<kHalfMirror>(v, i, nan);
     am_step<kMirror>(v, i, nan);
-}
-__device__ __forceinline__ void wave_argmax(float &v, int &i, int &nan) {
-    row16_argmax(v, i, nan);
-    float bv = lane_f(v, 0);
-    int bi = lane_i(i, 0), bn = lane_i(nan, 0);
-    for (int r = 16; r < 64; r += 16) {
-        merge_am(bv, bi, lane_f(v, r), lane_i(i, r));
-        bn |= lane_i(nan, r);
-    }
-    v = bv; i = bi; nan = bn;
 }
 
 // Ballot searches over the workgroup's threads.  Each wave reduces its
@@ -356,29 +356,13 @@ __device__ void write_error(const VerifyArgs &a, int b) {
     if (threadIdx.x == 0) st_out(a.out_acc + b, -1);
 }
 
-// Wait until the chunk partials of rows 0..n are all written.  False if the
-// bounded wait expired.
-__device__ bool wait_partials(const VerifyArgs &a, int b, int n) {
-    const uint64_t *part = partials(a, b);
-    const int np = (n + 1) * a.nc1;
-    // One lane first waits for the request's last-dispatched row wave (row n,
-    // last chunk), so the workgroup does not flood memory with polls while the
-    // row pass is still streaming; then every partial is checked.
-    if (threadIdx.x == 0) {
-        for (uint32_t spins = 0; spins < a.spin_limit && !valid(ld_coherent(part + np - 1)); ++spins)
-            __builtin_amdgcn_s_sleep(8);
-    }
-    __syncthreads();
-    for (uint32_t spins = 0;; ++spins) {
-        bool ready = true;
-        for (int i = threadIdx.x; i < np; i += kWG) ready &= valid(ld_coherent(part + i));   // no short circuit: loads overlap
-        if (__syncthreads_and(ready)) return true;
-        if (spins >= a.spin_limit) return false;
-        __builtin_amdgcn_s_sleep(4);
-    }
+// Inputs no kernel writes, read through the constant address space so that
+// uniform reads stay scalar loads even after the kernel's own stores.
+typedef const __attribute__((address_space(4))) int32_t ci32;
+__device__ __forceinline__ int32_t ld_const(const int32_t *p, size_t i) {
+    return reinterpret_cast<ci32 *>(reinterpret_cast<uintptr_t>(p))[i];
 }
-
-__device__ __forceinline__ int verify_len(const VerifyArgs &a, int b) { return a.vlen ? a.vlen[b] : a.G; }
+__device__ __forceinline__ int verify_len(const VerifyArgs &a, int b) { return a.vlen ? ld_const(a.vlen, b) : a.G; }
 
 // ------------------------------------------------------------- row waves
 
@@ -460,7 +444,7 @@ __device__ void row_wave_sampled(const VerifyArgs &a, int job, int lane) {
     load_chunk<ES, AL>(row, beg, a.V, lane, f);
     // The chunk holding draft token x_k gathers z(x_k) and q(x_k) for the
     // request pass's accept test (an x_k out of range is never gathered).
-    const int xk = (jb.k < jb.n) ? a.x[size_t(jb.b) * a.G + jb.k] : -1;
+    const int xk = (jb.k < jb.n) ? ld_const(a.x, size_t(jb.b) * a.G + jb.k) : -1;
     const bool gather = xk >= beg && xk < beg + a.ch1 && xk < a.V;
     float gz = 0.0f, gq = 0.0f;
     if (gather && lane == 0) {
@@ -506,26 +490,41 @@ __device__ void row_wave_sampled(const VerifyArgs &a, int job, int lane) {
     }
 }
 
-// Greedy row pass, one wave: (max, lowest index of the max, any NaN) of its chunk.
+// Greedy row pass, one wave: (max, lowest index of the max, any NaN) of its
+// chunk.  The maximum comes first (v_max3, which drops NaN); a NaN anywhere
+// shows in a running fp32 sum of the chunk (which also turns NaN when +inf
+// meets -inf, a row whose maximum is +inf and so bad anyway); then each lane
+// finds its lowest position holding the maximum and the wave takes the lowest
+// such index.  An all -inf chunk has no argmax (index -1).
 template <int ES, bool AL>
 __device__ void row_wave_greedy(const VerifyArgs &a, int job, int lane) {
     RowJob jb;
     if (!row_job(a, job, jb)) return;
+    constexpr int EPL = kEPL<ES>;
     const void *row = static_cast<const char *>(a.logits) + (size_t(jb.b) * (a.G + 1) + jb.k) * size_t(a.V) * ES;
     const int beg = jb.c * a.ch1;
-    float f[kEPL<ES>];
+    float f[EPL];
     load_chunk<ES, AL>(row, beg, a.V, lane, f);
-    float best = neg_inf();
-    int bi = -1, nan = 0;
+    float m = f[0];
 #pragma unroll
-    for (int i = 0; i < kEPL<ES>; ++i) {
-        nan |= int(f[i] != f[i]);
-        if (f[i] > best) { best = f[i]; bi = chunk_index<ES, AL>(beg, lane, i); }
+    for (int i = 1; i + 1 < EPL; i += 2) m = max3(m, f[i], f[i + 1]);
+    m = fmaxf(m, f[EPL - 1]);
+    const float M = wave_max(m);
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; i += 2) { s0 = s0 + f[i]; s1 = s1 + f[i + 1]; }
+    const float sum = s0 + s1;
+    const bool nan = __ballot(sum != sum) != 0ull;
+    int bi = -1;
+    if (M != neg_inf()) {                         // uniform
+        int bo = -1;
+#pragma unroll
+        for (int i = EPL - 1; i >= 0; --i) bo = (f[i] == M) ? i : bo;
+        bi = wave_min_i((bo >= 0) ? chunk_index<ES, AL>(beg, lane, bo) : INT_MAX);
     }
-    wave_argmax(best, bi, nan);
     if (lane == 0)
         st_coherent(partials(a, jb.b) + size_t(jb.k) * a.nc1 + jb.c,
-                    uint64_t(__float_as_uint(best)) | (uint64_t(uint32_t((nan ? kNanIdx : bi) + 2) | kValid) << 32));
+                    uint64_t(__float_as_uint(M)) | (uint64_t(uint32_t((nan ? kNanIdx : bi) + 2) | kValid) << 32));
 }
 
 // ---------------------------------------------------------- draw sub-tiles
@@ -670,20 +669,51 @@ __device__ bool merge_rows_sampled(const VerifyArgs &a, int b, int n, Smem &sh) 
     return bad;
 }
 
+constexpr int kRowBad = 1;
 // Rows 0..n's chunk partials (greedy): lowest index of the maximum into
-// sh.A[r].  Returns true in some thread if a row is bad or incomplete.
-__device__ bool merge_rows_greedy(const VerifyArgs &a, int b, int n, Smem &sh) {
-    bool bad = false;
+// sh.A[r], 16 lanes per row.  The partials are written by row waves of the
+// same launch: they are loaded in one batch per attempt (up to 8 per lane,
+// every vocabulary up to 2^18 bf16 or 2^17 fp32), and the batch repeats
+// (bounded) until all are written.  Returns kRowBad in some thread for a bad
+// row or a wait that expired.
+__device__ int merge_rows_greedy(const VerifyArgs &a, int b, int n, Smem &sh) {
+    constexpr int kRegs = 8;
     const uint64_t *part = partials(a, b);
     const int l = threadIdx.x & 15, g = threadIdx.x >> 4;
+    int flags = 0;
     for (int r0 = 0; r0 <= n; r0 += kWG / 16) {
         const int r = r0 + g;
+        const bool live = r <= n;
+        const uint64_t *pp = part + size_t(live ? r : 0) * a.nc1;
         float best = neg_inf();
         int bi = -1, nan = 0, ok = 1;
-        if (r <= n) {
-            const uint64_t *pp = part + size_t(r) * a.nc1;
+        if (a.nc1 <= 16 * kRegs) {
+            uint64_t v[kRegs];
+            for (uint32_t spins = 0;; ++spins) {
+                ok = 1;
+#pragma unroll
+                for (int i = 0; i < kRegs; ++i) {
+                    const int cc = l + 16 * i;
+                    v[i] = (live && cc < a.nc1) ? ld_coherent(pp + cc) : (uint64_t(1) << 32 | uint64_t(kValid) << 32);
+                }
+#pragma unroll
+                for (int i = 0; i < kRegs; ++i) ok &= int(valid(v[i]));
+                if (__syncthreads_and(ok) || spins >= a.spin_limit) break;
+                __builtin_amdgcn_s_sleep(4);
+            }
+#pragma unroll
+            for (int i = 0; i < kRegs; ++i) {          // ascending chunks: the first maximum wins
+                const int vi = int(hi_u(v[i]) & ~kValid) - 2;
+                if (vi == kNanIdx) nan = 1;
+                else merge_am(best, bi, lo_f(v[i]), vi);
+            }
+        } else if (live) {
             for (int cc = l; cc < a.nc1; cc += 16) {
-                const uint64_t v = ld_coherent(pp + cc);
+                uint64_t v = ld_coherent(pp + cc);
+                for (uint32_t spins = 0; !valid(v) && spins < a.spin_limit; ++spins) {
+                    __builtin_amdgcn_s_sleep(4);
+                    v = ld_coherent(pp + cc);
+                }
                 ok &= int(valid(v));
                 const int vi = int(hi_u(v) & ~kValid) - 2;
                 if (vi == kNanIdx) nan = 1;
@@ -692,12 +722,12 @@ __device__ bool merge_rows_greedy(const VerifyArgs &a, int b, int n, Smem &sh) {
         }
         row16_argmax(best, bi, nan);
         ok = row16_and(ok);
-        if (l == 0 && r <= n) {
-            bad |= !ok || nan || bi < 0 || best == __builtin_inff();
+        if (l == 0 && live) {
+            if (!ok || nan || bi < 0 || best == __builtin_inff()) flags |= kRowBad;
             sh.A[r] = bi;
         }
     }
-    return bad;
+    return flags;
 }
 
 // Unnormalised target probability 2^(z*c - R) of a value z in a row with
@@ -983,8 +1013,16 @@ __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
     const int k = threadIdx.x;
     int xk = 0;
     if (k < n) xk = a.x[size_t(b) * G + k];
-    if (!wait_partials(a, b, n)) { write_error(a, b); return; }
-    bool bad = merge_rows_greedy(a, b, n, sh);
+    // One lane first waits (bounded) for the request's last-dispatched row
+    // wave, so the workgroup does not poll every partial while the row pass
+    // is still streaming.
+    if (threadIdx.x == 0) {
+        const uint64_t *last = partials(a, b) + size_t(n + 1) * a.nc1 - 1;
+        for (uint32_t spins = 0; spins < a.spin_limit && !valid(ld_coherent(last)); ++spins)
+            __builtin_amdgcn_s_sleep(8);
+    }
+    __syncthreads();
+    bool bad = merge_rows_greedy(a, b, n, sh) != 0;
     bad |= k < n && (xk < 0 || xk >= a.V);
     if (__syncthreads_or(bad)) {
         write_error(a, b);
