@@ -93,9 +93,8 @@ typedef struct {
  * Bytes of device workspace spec_verify needs for this shape (0 on invalid
  * arguments).  The same workspace serves every shape whose query is not larger.
  *
- * The workspace holds a fixed 1 MiB region of per-request counters (the same
- * offsets for every shape), the per-row chunk partials and the per-request
- * sub-tile masses.  It must be zero-filled once before its first use (e.g.
+ * The workspace holds the per-row partial sums, the per-draft gathers and the
+ * per-request sub-tile masses.  It must be zero-filled once before its first use (e.g.
  * allocated with a zeroing allocator); every completed call leaves it
  * zero-filled again, so one workspace can serve later calls of any shape
  * without clearing.  Calls that share one workspace must not overlap in time

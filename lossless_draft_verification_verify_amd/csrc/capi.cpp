@@ -10,7 +10,7 @@
 #include "spec_verify.h"
 #include "sv_plan.h"
 
-static_assert(SPEC_MAX_BATCH == sv::kMaxBatch, "batch limit matches the counter region");
+static_assert(SPEC_MAX_BATCH == sv::kMaxBatch, "one batch limit for the header and the kernels");
 
 namespace {
 
@@ -158,13 +158,17 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
     a.spin_limit = 1u << 20;
     const bool az = aligned(target_logits, 16) && (size_t(V) * es) % 16 == 0;
     const bool aq = aligned(draft_probs, 16) && V % 4 == 0;
-    const long row_wgs = (long(B) * (G + 1) * a.nc1 + sv::kWaves - 1) / sv::kWaves;   // one wave per chunk
+    const long row_wgs = (long(B) * (G + 1) * a.nc1 + sv::kWaves - 1) / sv::kWaves;   // greedy: one wave per chunk
 
     if (sampled) {
-        // Row pass, then request pass: nothing waits, each launch sized freely.
+        // Row pass, then request pass (the kernel boundary orders every row
+        // partial before the per-request work, across all XCDs).  One row
+        // workgroup per (request, row, group of kWaves chunks).
+        a.np1 = (a.nc1 + sv::kWaves - 1) / sv::kWaves;
+        const long row_groups = long(B) * (G + 1) * a.np1;
         a.spw = sv::kSubBatch;
         a.nc2 = (a.nsub + a.spw - 1) / a.spw;
-        if (sv::launch_rows_sampled(a, az, es, int(row_wgs), stream) != 0) return SPEC_ERR_DEVICE;
+        if (sv::launch_rows_sampled(a, az, es, int(row_groups), stream) != 0) return SPEC_ERR_DEVICE;
         if (row_event && hipEventRecord(row_event, static_cast<hipStream_t>(stream)) != hipSuccess)
             return SPEC_ERR_DEVICE;
         return sv::launch_requests_sampled(a, az, aq, es, int(long(B) * a.nc2), stream) == 0 ? SPEC_OK
@@ -176,6 +180,7 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
     if (hipGetDevice(&dev) != hipSuccess) return SPEC_ERR_DEVICE;
     const int one = greedy_one_launch(dev, az, es, B);
     if (one < 0) return SPEC_ERR_DEVICE;
+    a.np1 = a.nc1;
     a.nc2 = 1;
     if (one) {
         a.mode = 0;

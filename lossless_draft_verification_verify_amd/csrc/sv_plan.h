@@ -19,23 +19,23 @@ constexpr int kNanIdx = -2;         // greedy partial: chunk holds a NaN
 // bytes (2048 bf16 or 1024 fp32 values).
 inline int chunk_elems(int esize) { return 64 * kRowVec * (16 / esize); }
 
-// Workspace.  Between calls every byte the kernels use is zero: each slot is
-// reset by the last workgroup that reads it, so one zero-filled workspace stays
+// Workspace.  Between calls every byte the kernels use is zero: each word is
+// reset by the last workgroup that reads it, and every word carries its own
+// written mark (nothing is a counter), so one zero-filled workspace stays
 // valid across calls of any shape.
-//   counters [kMaxBatch] 16-byte slots at fixed offsets: word 2 counts the
-//            request's workgroups of the request pass;
-//   part     [B*(G+1)*nc1] u64 chunk partials, bit 63 set once written
-//            (sampled: low = max bits, high = sum bits | 1<<31;
-//             greedy:  low = max bits, high = (argmax + 2) | 1<<31);
-//   mass     [B*nsub] 2 u64: fp64 (residual mass, target mass) per sub-tile;
-//   gx       [B*G] u64: the row pass's gather of draft k (sampled only):
-//            low = fp32 bits of z[b,k,x_k], high = bits of q[b,k,x_k];
 //   zero     256 bytes never written: the draft row a bonus draw reads in
-//            place of q (so the draw loads need no branch).
+//            place of q (so the draw loads need no branch);
+//   part     [B*(G+1)*np1] u64 partials, bit 63 set once written
+//            (sampled, one per row workgroup of kWaves chunks: low = max
+//             bits, high = sum bits | 1<<31;
+//             greedy, one per chunk: low = max bits, high = (argmax + 2) | 1<<31);
+//            the region is sized for the greedy count (np1 = nc1);
+//   mass     [B*nsub] 2 u64: fp64 (residual mass, target mass) per sub-tile,
+//            bit 63 set once written;
+//   gx       [B*G] u64: the row pass's gather of draft k (sampled only):
+//            low = fp32 bits of z[b,k,x_k], high = bits of q[b,k,x_k].
 
 constexpr int kMaxBatch = 65536;
-constexpr size_t kSlotBytes = 16;
-constexpr size_t kCounterBytes = size_t(kMaxBatch) * kSlotBytes;
 constexpr uint32_t kValid = 0x80000000u;
 
 struct Layout {
@@ -52,7 +52,7 @@ inline Layout make_layout(int64_t B, int64_t G, int64_t V, int esize) {
     const int64_t nc1 = (V + chunk_elems(esize) - 1) / chunk_elems(esize);
     const int64_t nsub = (V + kSub - 1) / kSub;
     Layout L;
-    size_t o = kCounterBytes;
+    size_t o = 0;
     L.zero = o; o += 256;
     L.part = o; o += align256(size_t(B) * size_t(G + 1) * size_t(nc1) * 8);
     L.mass = o; o += align256(size_t(B) * size_t(nsub) * 16);
@@ -76,6 +76,7 @@ struct VerifyArgs {
     float T;          // temperature
     float c32;        // log2(e) / T, the fp32 exponent scale
     int32_t nc1, ch1; // row-pass chunks (waves) per row, elements per chunk
+    int32_t np1;      // partials per row: sampled ceil(nc1 / kWaves), greedy nc1
     int32_t nsub;     // draw sub-tiles per row
     int32_t nc2, spw; // request workgroups per request, sub-tiles per workgroup
     int32_t mode;     // greedy kernel: 0 row items then request items; 1 row items only; 2 request items only

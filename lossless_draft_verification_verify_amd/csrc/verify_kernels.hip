@@ -14,34 +14,37 @@
 // The work is a bandwidth-bound streaming reduction (no contraction, so no
 // MFMA).  Temperature > 0 runs as two launches on the caller's stream:
 //
-//   row pass       one wave per (request, row, 2048-element chunk): four
-//                  16-byte streaming loads per lane, the chunk maximum, then
-//                  the sum of 2^((z - m) * log2(e)/T), both reduced across the
-//                  wave with DPP (no LDS, no barrier); lane 0 stores the
-//                  (max, sum) partial as one 64-bit word.  The wave whose chunk
-//                  holds draft token x_k also records z(x_k) and q(x_k), so the
-//                  request pass has no dependent gathers.
+//   row pass       one workgroup per (request, row, 8192-element group), one
+//                  wave per 2048-element chunk: four 16-byte streaming loads
+//                  per lane, the chunk maximum, then the sum of
+//                  2^((z - m) * log2(e)/T), both reduced across the wave with
+//                  DPP; the four waves' (max, sum) pairs merge in LDS into one
+//                  64-bit partial per group.  The wave whose chunk holds draft
+//                  token x_k also records z(x_k) and q(x_k), so the request
+//                  pass has no dependent gathers.
 //   request pass   nc2 workgroups per request, one per pair of 2048-element
-//                  sub-tiles of the draw row.  Each merges the request's chunk
+//                  sub-tiles of the draw row.  Each merges the request's
 //                  partials per row (16 lanes per row, fp64 sums), runs the
 //                  accept tests and finds the first rejection j (every
 //                  workgroup of the request computes the same result), then
 //                  streams its sub-tiles of the one row the final token is drawn
 //                  from (target row j, plus draft row j on a rejection) and
-//                  writes fp64 sub-tile masses.  The last of the request's
-//                  workgroups to arrive (a counter) locates u * R by a parallel
-//                  prefix over the masses, re-scans that one sub-tile, writes
-//                  the token, and zeroes every workspace word the request used.
+//                  writes fp64 sub-tile masses, each word marked as written.
+//                  The request's last workgroup in grid order polls the masses,
+//                  locates u * R by a parallel prefix over them, re-scans that
+//                  one sub-tile, writes the token, and zeroes every workspace
+//                  word the request used.
 //
-// Nothing waits on anything inside a launch except the arrival counter, so
-// there are no spin loops on this path.  Temperature 0 (argmax) is one launch:
-// row waves, then one workgroup per request that polls its rows' partials
-// (bounded wait) — the host keeps those below half the resident capacity, else
-// it splits them into a second launch.
+// The only wait inside a sampled launch is that last workgroup's (bounded)
+// poll, which depends only on workgroups dispatched before it.  Temperature 0
+// (argmax) is one launch: row waves, then one workgroup per request that polls
+// its rows' partials (bounded wait) — the host keeps those below half the
+// resident capacity, else it splits them into a second launch.
 //
 // Words handed between workgroups of one launch (sub-tile masses, the greedy
 // partials) use coherent device-scope stores and loads instead of device-scope
-// fences, which on this chip write back or invalidate the whole L2.
+// fences, which on this chip write back or invalidate the whole L2; each such
+// word carries its own written bit, so none needs ordering.
 //
 // Determinism: no floating-point atomics; every reduction has a fixed order.
 // A sub-tile mass is the butterfly sum of its wave totals, which is bitwise the
@@ -109,19 +112,13 @@ __device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
 // Words one workgroup hands to another inside a launch are written with
 // coherent device-scope stores and read with coherent device-scope loads (no
 // whole-cache write-back or invalidation, which a generic device-scope fence
-// performs on every L2).  A greedy chunk partial carries its own valid bit, so
-// it needs no ordering at all.  Sub-tile masses are ordered before the arrival
-// that publishes them by waiting for the stores to complete.
+// performs on every L2).  Greedy chunk partials and sub-tile masses carry
+// their own written bits, so they need no ordering at all.
 __device__ __forceinline__ void st_coherent(void *p, uint64_t v) {
     __hip_atomic_store(static_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t ld_coherent(const void *p) {
     return __hip_atomic_load(static_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void stores_complete() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);          // vmcnt = expcnt = lgkmcnt = 0
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 // Output words that a later workgroup may overwrite are written through to
 // the coherence point, so the last write in time is the one that lands.
@@ -318,29 +315,8 @@ __device__ void wg_scan(const double (&v)[NS], double (&excl)[NS], double (&incl
 
 // ------------------------------------------------------------- workspace
 
-// Every thread's published stores complete, then one counted arrival.
-// Returns true in every thread of the workgroup that arrives last; that
-// workgroup resets the counter.
-__device__ bool arrive_last(unsigned *ctr, unsigned target, Smem &sh) {
-    stores_complete();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int last = (old + 1 == target);
-        if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sh.last = last;
-    }
-    __syncthreads();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    return sh.last != 0;
-}
-
-// Draw-workgroup counter of request b (fixed offset for every shape).
-__device__ __forceinline__ unsigned *draw_counter(const VerifyArgs &a, int b) {
-    return reinterpret_cast<unsigned *>(a.ws + size_t(b) * kSlotBytes) + 2;
-}
 __device__ __forceinline__ uint64_t *partials(const VerifyArgs &a, int b) {
-    return reinterpret_cast<uint64_t *>(a.ws + a.lay.part) + size_t(b) * (a.G + 1) * a.nc1;
+    return reinterpret_cast<uint64_t *>(a.ws + a.lay.part) + size_t(b) * (a.G + 1) * a.np1;
 }
 __device__ __forceinline__ uint64_t *masses(const VerifyArgs &a, int b) {
     return reinterpret_cast<uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
@@ -348,6 +324,10 @@ __device__ __forceinline__ uint64_t *masses(const VerifyArgs &a, int b) {
 __device__ __forceinline__ uint64_t *gathered(const VerifyArgs &a, int b) {
     return reinterpret_cast<uint64_t *>(a.ws + a.lay.gx) + size_t(b) * a.G;
 }
+// A sub-tile mass word: the fp64 mass (>= 0) with bit 63 set once written.
+constexpr uint64_t kMassWritten = uint64_t(1) << 63;
+__device__ __forceinline__ uint64_t mass_word(double m) { return uint64_t(__double_as_longlong(m)) | kMassWritten; }
+__device__ __forceinline__ double mass_value(uint64_t w) { return __longlong_as_double((long long)(w & ~kMassWritten)); }
 
 // A request with a data error: every output word -1 (diagnostics NaN).
 __device__ void write_error(const VerifyArgs &a, int b) {
@@ -417,7 +397,7 @@ __device__ __forceinline__ int chunk_index(int beg, int lane, int i) {
     return AL ? beg + (lane + 64 * (i / EPV)) * EPV + (i % EPV) : beg + lane + 64 * i;
 }
 
-// Row-pass job -> (request, row, chunk); false if that row is not read.
+// Greedy row-pass job -> (request, row, chunk); false if that row is not read.
 struct RowJob {
     int b, k, c, n;
 };
@@ -431,25 +411,27 @@ __device__ __forceinline__ bool row_job(const VerifyArgs &a, int job, RowJob &j)
     return j.n >= 0 && j.n <= a.G && j.k <= j.n;
 }
 
-// Sampled row pass, one wave: (max, sum of 2^((z - max) * c)) of its chunk.
+// Sampled row pass, one wave: (max M, sum S of 2^((z - M) * c)) of chunk c
+// of row k of request b (n = the request's verify length), uniform across
+// the wave.  The chunk holding draft token x_k also stores z(x_k) and q(x_k)
+// for the request pass's accept test.
 template <int ES, bool AL>
-__device__ void row_wave_sampled(const VerifyArgs &a, int job, int lane) {
-    RowJob jb;
-    if (!row_job(a, job, jb)) return;
+__device__ void row_chunk_sampled(const VerifyArgs &a, int b, int k, int chunk, int n, int lane, float &M_out,
+                                  float &S_out) {
     constexpr int EPL = kEPL<ES>;
     const int G1 = a.G + 1;
-    const void *row = static_cast<const char *>(a.logits) + (size_t(jb.b) * G1 + jb.k) * size_t(a.V) * ES;
-    const int beg = jb.c * a.ch1;
+    const void *row = static_cast<const char *>(a.logits) + (size_t(b) * G1 + k) * size_t(a.V) * ES;
+    const int beg = chunk * a.ch1;
     float f[EPL];
     load_chunk<ES, AL>(row, beg, a.V, lane, f);
     // The chunk holding draft token x_k gathers z(x_k) and q(x_k) for the
-    // request pass's accept test (an x_k out of range is never gathered).
-    const int xk = (jb.k < jb.n) ? ld_const(a.x, size_t(jb.b) * a.G + jb.k) : -1;
+    // accept test (an x_k out of range is never gathered).
+    const int xk = (k < n) ? ld_const(a.x, size_t(b) * a.G + k) : -1;
     const bool gather = xk >= beg && xk < beg + a.ch1 && xk < a.V;
     float gz = 0.0f, gq = 0.0f;
     if (gather && lane == 0) {
         gz = load_elem<ES>(row, size_t(xk));
-        gq = a.q[(size_t(jb.b) * a.G + jb.k) * size_t(a.V) + size_t(xk)];
+        gq = a.q[(size_t(b) * a.G + k) * size_t(a.V) + size_t(xk)];
     }
     const float c = a.c32;
     float m = f[0];
@@ -481,13 +463,10 @@ __device__ void row_wave_sampled(const VerifyArgs &a, int job, int lane) {
             s3 = s3 + exp2_fast((f[i + 3] - M) * c);
         }
     }
-    const float S = wave_sum((s0 + s1) + (s2 + s3));
-    if (lane == 0) {
-        partials(a, jb.b)[size_t(jb.k) * a.nc1 + jb.c] =
-            uint64_t(__float_as_uint(M)) | (uint64_t(__float_as_uint(S) | kValid) << 32);
-        if (gather)
-            gathered(a, jb.b)[jb.k] = uint64_t(__float_as_uint(gz)) | (uint64_t(__float_as_uint(gq)) << 32);
-    }
+    M_out = M;
+    S_out = wave_sum((s0 + s1) + (s2 + s3));
+    if (gather && lane == 0)
+        gathered(a, b)[k] = uint64_t(__float_as_uint(gz)) | (uint64_t(__float_as_uint(gq)) << 32);
 }
 
 // Greedy row pass, one wave: (max, lowest index of the max, any NaN) of its
@@ -523,7 +502,7 @@ __device__ void row_wave_greedy(const VerifyArgs &a, int job, int lane) {
         bi = wave_min_i((bo >= 0) ? chunk_index<ES, AL>(beg, lane, bo) : INT_MAX);
     }
     if (lane == 0)
-        st_coherent(partials(a, jb.b) + size_t(jb.k) * a.nc1 + jb.c,
+        st_coherent(partials(a, jb.b) + size_t(jb.k) * a.np1 + jb.c,
                     uint64_t(__float_as_uint(M)) | (uint64_t(uint32_t((nan ? kNanIdx : bi) + 2) | kValid) << 32));
 }
 
@@ -608,32 +587,32 @@ struct Decision {
     float u_final;    // u[b, G], the final draw's uniform
 };
 
-// Merge each read row's chunk partials into sh.M[r] (max) and sh.S[r] (fp64
-// sum against the reference of sh.M[r]): 16 lanes per row, each lane's
-// partials rescaled once, then a fixed 16-lane tree.  Returns true in some
-// thread if a read row is bad or has a partial that was never written.  Rows
-// up to G are loaded whatever n is, so these loads need not wait for the
-// verify length.
+// Merge each read row's partials into sh.M[r] (max) and sh.S[r] (fp64 sum
+// against the reference of sh.M[r]): 16 lanes per row, each lane's partials
+// rescaled once, then a fixed 16-lane tree.  The partials were written by the
+// previous launch.  Returns true in some thread if a read row is bad or has a
+// partial that was never written.
+constexpr int kRowBad = 1;
 __device__ bool merge_rows_sampled(const VerifyArgs &a, int b, int n, Smem &sh) {
     bool bad = false;
-    constexpr int kRegs = 4;   // partials held per lane when nc1 <= 64
+    constexpr int kRegs = 4;   // partials held per lane when np1 <= 64
     const uint64_t *part = partials(a, b);
     const int l = threadIdx.x & 15, g = threadIdx.x >> 4;
     const float c = a.c32;
     const uint64_t empty = uint64_t(0xff800000u) | (uint64_t(kValid) << 32);   // (-inf, 0), written
-    for (int r0 = 0; r0 <= a.G; r0 += kWG / 16) {
+    for (int r0 = 0; r0 <= n; r0 += kWG / 16) {
         const int r = r0 + g;
-        const bool live = r <= a.G;
-        const uint64_t *pp = part + size_t(live ? r : 0) * a.nc1;
+        const bool live = r <= n;
+        const uint64_t *pp = part + size_t(live ? r : 0) * a.np1;
         float M = neg_inf();
         double S = 0.0;
         int ok = 1;
-        if (a.nc1 <= 16 * kRegs) {
+        if (a.np1 <= 16 * kRegs) {
             uint64_t v[kRegs];
 #pragma unroll
             for (int i = 0; i < kRegs; ++i) {
                 const int cc = l + 16 * i;
-                v[i] = (live && cc < a.nc1) ? pp[cc] : empty;
+                v[i] = (live && cc < a.np1) ? pp[cc] : empty;
             }
 #pragma unroll
             for (int i = 0; i < kRegs; ++i) {
@@ -646,21 +625,21 @@ __device__ bool merge_rows_sampled(const VerifyArgs &a, int b, int n, Smem &sh) 
                 S = S + double(__uint_as_float(hi_u(v[i]) & ~kValid)) * double(rescale(lo_f(v[i]), M, c));
         } else {
             if (live)
-                for (int cc = l; cc < a.nc1; cc += 16) {
+                for (int cc = l; cc < a.np1; cc += 16) {
                     const uint64_t v = pp[cc];
                     ok &= int(valid(v));
                     M = fmaxf(M, lo_f(v));
                 }
             M = row16_max(M);
             if (live)
-                for (int cc = l; cc < a.nc1; cc += 16) {
+                for (int cc = l; cc < a.np1; cc += 16) {
                     const uint64_t v = pp[cc];
                     S = S + double(__uint_as_float(hi_u(v) & ~kValid)) * double(rescale(lo_f(v), M, c));
                 }
         }
         S = row16_sum_d(S);
         ok = row16_and(ok);
-        if (l == 0 && r <= n) {
+        if (l == 0 && live) {
             bad |= !ok || !(S > 0.0 && S < INFINITY) || !(M > neg_inf() && M < __builtin_inff());
             sh.M[r] = M;
             sh.S[r] = S;
@@ -669,7 +648,7 @@ __device__ bool merge_rows_sampled(const VerifyArgs &a, int b, int n, Smem &sh) 
     return bad;
 }
 
-constexpr int kRowBad = 1;
+
 // Rows 0..n's chunk partials (greedy): lowest index of the maximum into
 // sh.A[r], 16 lanes per row.  The partials are written by row waves of the
 // same launch: they are loaded in one batch per attempt (up to 8 per lane,
@@ -684,17 +663,17 @@ __device__ int merge_rows_greedy(const VerifyArgs &a, int b, int n, Smem &sh) {
     for (int r0 = 0; r0 <= n; r0 += kWG / 16) {
         const int r = r0 + g;
         const bool live = r <= n;
-        const uint64_t *pp = part + size_t(live ? r : 0) * a.nc1;
+        const uint64_t *pp = part + size_t(live ? r : 0) * a.np1;
         float best = neg_inf();
         int bi = -1, nan = 0, ok = 1;
-        if (a.nc1 <= 16 * kRegs) {
+        if (a.np1 <= 16 * kRegs) {
             uint64_t v[kRegs];
             for (uint32_t spins = 0;; ++spins) {
                 ok = 1;
 #pragma unroll
                 for (int i = 0; i < kRegs; ++i) {
                     const int cc = l + 16 * i;
-                    v[i] = (live && cc < a.nc1) ? ld_coherent(pp + cc) : (uint64_t(1) << 32 | uint64_t(kValid) << 32);
+                    v[i] = (live && cc < a.np1) ? ld_coherent(pp + cc) : (uint64_t(1) << 32 | uint64_t(kValid) << 32);
                 }
 #pragma unroll
                 for (int i = 0; i < kRegs; ++i) ok &= int(valid(v[i]));
@@ -708,7 +687,7 @@ __device__ int merge_rows_greedy(const VerifyArgs &a, int b, int n, Smem &sh) {
                 else merge_am(best, bi, lo_f(v[i]), vi);
             }
         } else if (live) {
-            for (int cc = l; cc < a.nc1; cc += 16) {
+            for (int cc = l; cc < a.np1; cc += 16) {
                 uint64_t v = ld_coherent(pp + cc);
                 for (uint32_t spins = 0; !valid(v) && spins < a.spin_limit; ++spins) {
                     __builtin_amdgcn_s_sleep(4);
@@ -735,68 +714,6 @@ __device__ int merge_rows_greedy(const VerifyArgs &a, int b, int n, Smem &sh) {
 __device__ __forceinline__ double target_prob(float z, float m, float c) {
     const float R = m * c;
     return finitef(R) ? exp2(double(z) * double(c) - double(R)) : exp2((double(z) - double(m)) * double(c));
-}
-
-// All chunk partials and gathers of the request are complete (written by the
-// previous launch): merge every row, run the accept tests, find the first
-// rejection.  Returns false (outputs reported by workgroup 0) for a data error
-// or an invalid verify length (then *arrive is false: no workgroup counts
-// itself).  Every load is issued before the first barrier (a barrier waits for
-// outstanding loads), so the whole decision costs one memory round trip.
-template <int ES>
-__device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, bool &arrive, Smem &sh) {
-    const int G = a.G, G1 = G + 1;
-    const int k = threadIdx.x;
-    const int n = verify_len(a, b);
-    int xk = 0;
-    uint64_t gk = 0;
-    float uk = 0.0f;
-    if (k < G) {
-        xk = a.x[size_t(b) * G + k];
-        gk = gathered(a, b)[k];
-        uk = a.u[size_t(b) * G1 + k];
-    }
-    d.u_final = a.u[size_t(b) * G1 + G];
-    bool bad = merge_rows_sampled(a, b, n, sh);
-    // Keep the uses of the per-draft loads below the partials' loads (the
-    // compiler would otherwise wait for them before issuing the partials).
-    asm volatile("" : "+v"(xk), "+v"(uk), "+v"(gk));
-    bad |= k < n && (xk < 0 || xk >= a.V);
-    const bool any_bad = __syncthreads_or(bad);
-    d.n = n;
-    arrive = false;
-    if (n < 0 || n > G) {
-        if (w == 0) write_error(a, b);
-        return false;
-    }
-    arrive = true;
-    if (any_bad) {
-        if (w == 0) write_error(a, b);
-        return false;
-    }
-    bool rej = false;
-    if (k < n) {
-        const float zx = lo_f(gk), qx = __uint_as_float(hi_u(gk));
-        const double pk = target_prob(zx, sh.M[k], a.c32) / sh.S[k];
-        const bool acc = (qx > 0.0f) ? (double(uk) < pk / double(qx)) : (pk > 0.0);
-        rej = !acc;
-    }
-    post_first(rej, 0, sh);
-    __syncthreads();
-    const int jf = wg_first(0, sh);
-    const int j = (jf == INT_MAX) ? n : jf;
-    d.j = j;
-    d.resid = j < n;
-    d.m = sh.M[j];
-    d.inv_s = float(1.0 / sh.S[j]);
-    if (w == 0) {
-        for (int t = threadIdx.x; t < G1; t += kWG) {
-            if (t < j) a.out_tok[size_t(b) * G1 + t] = a.x[size_t(b) * G + t];
-            else if (t > j) a.out_tok[size_t(b) * G1 + t] = -1;
-        }
-        if (threadIdx.x == 0) a.out_acc[b] = j;
-    }
-    return true;
 }
 
 // Diagnostics of request b (only when requested), from the merged rows.  In
@@ -828,6 +745,100 @@ __device__ void write_diag(const VerifyArgs &a, int b, bool ok, int n, Smem &sh)
     if (!ok && threadIdx.x == 0 && a.d_r) a.d_r[b] = qnan;
 }
 
+// All partials and gathers of the request are complete (written by the
+// previous launch): merge every read row, run the accept tests, find the first
+// rejection.  Returns false (outputs reported by workgroup 0) for a data error
+// or an invalid verify length (then *proceed is false: the request's
+// workgroups do nothing more, since the row pass read none of its rows).
+// Every load is issued before the first barrier (a barrier waits for
+// outstanding loads), so the whole decision costs one memory round trip.
+template <int ES>
+__device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, bool &proceed, Smem &sh) {
+    const int G = a.G, G1 = G + 1;
+    const int k = threadIdx.x;
+    const int n = verify_len(a, b);
+    d.n = n;
+    d.j = 0;
+    d.resid = false;
+    d.m = 0.0f;
+    d.inv_s = 0.0f;
+    d.u_final = 0.0f;
+    proceed = false;
+    if (n < 0 || n > G) {
+        if (w == 0) write_error(a, b);
+        return false;
+    }
+    proceed = true;
+    int xk = 0;
+    uint64_t gk = 0;
+    float uk = 0.0f;
+    if (k < n) {
+        xk = a.x[size_t(b) * G + k];
+        gk = gathered(a, b)[k];
+        uk = a.u[size_t(b) * G1 + k];
+    }
+    d.u_final = a.u[size_t(b) * G1 + G];
+    bool bad = merge_rows_sampled(a, b, n, sh);
+    // Keep the uses of the per-draft loads below the partials' loads (the
+    // compiler would otherwise wait for them before issuing the partials).
+    asm volatile("" : "+v"(xk), "+v"(uk), "+v"(gk));
+    bad |= k < n && (xk < 0 || xk >= a.V);
+    if (__syncthreads_or(bad)) {
+        if (w == 0) write_error(a, b);
+        return false;
+    }
+    bool rej = false;
+    if (k < n) {
+        const float zx = lo_f(gk), qx = __uint_as_float(hi_u(gk));
+        const double pk = target_prob(zx, sh.M[k], a.c32) / sh.S[k];
+        const bool acc = (qx > 0.0f) ? (double(uk) < pk / double(qx)) : (pk > 0.0);
+        rej = !acc;
+    }
+    post_first(rej, 0, sh);
+    __syncthreads();
+    const int jf = wg_first(0, sh);
+    const int j = (jf == INT_MAX) ? n : jf;
+    d.j = j;
+    d.resid = j < n;
+    d.m = sh.M[j];
+    d.inv_s = float(1.0 / sh.S[j]);
+    if (w == 0) {
+        for (int t = threadIdx.x; t < G1; t += kWG) {
+            if (t < j) st_out(a.out_tok + size_t(b) * G1 + t, a.x[size_t(b) * G + t]);
+            else if (t > j) st_out(a.out_tok + size_t(b) * G1 + t, -1);
+        }
+        if (threadIdx.x == 0) st_out(a.out_acc + b, j);
+    }
+    return true;
+}
+
+// Wait until every sub-tile mass word of request b is written.  With at most
+// kWG sub-tiles thread s returns sub-tile s's (residual, target) masses in v
+// (zeros past the end).  False if the bounded wait expired.
+__device__ bool wait_masses(const VerifyArgs &a, int b, double (&v)[2]) {
+    const uint64_t *mass = masses(a, b);
+    const int nsub = a.nsub;
+    for (uint32_t spins = 0;; ++spins) {
+        bool ready = true;
+        if (nsub <= kWG) {
+            const int s = threadIdx.x;
+            uint64_t w0 = kMassWritten, w1 = kMassWritten;
+            if (s < nsub) {
+                w0 = ld_coherent(mass + 2 * s);
+                w1 = ld_coherent(mass + 2 * s + 1);
+            }
+            ready = (w0 & w1 & kMassWritten) != 0;
+            v[0] = mass_value(w0);
+            v[1] = mass_value(w1);
+        } else {
+            for (int i = threadIdx.x; i < 2 * nsub; i += kWG) ready &= (ld_coherent(mass + i) & kMassWritten) != 0;
+        }
+        if (__syncthreads_and(ready)) return true;
+        if (spins >= a.spin_limit) return false;
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 // Last workgroup of request b: locate u * R and write the token.
 //
 // The draw follows the inverse-CDF definition: y is the first index whose
@@ -840,33 +851,47 @@ __device__ void write_diag(const VerifyArgs &a, int b, bool ok, int n, Smem &sh)
 // draw only when u * R lies within rounding of a cumulative sum.
 template <int ES, bool ALZ, bool ALQ>
 __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, const void *zrow, const float *qrow,
-                             Smem &sh) {
+                             const double (&polled)[2], Smem &sh) {
     const int G1 = a.G + 1;
     const bool resid = d.resid;
     const uint64_t *mass = masses(a, b);
     const int nsub = a.nsub;
     // Pass 1: totals of both mass arrays (residual, target), and the last
     // sub-tile of each with positive mass.  With at most kWG sub-tiles (every
-    // vocabulary up to 2^19) the masses stay in registers for pass 2.
+    // vocabulary up to 2^19) the masses are the polled ones, kept in
+    // registers for pass 2.
     const bool one = nsub <= kWG;
     double v[2] = {0.0, 0.0}, ex[2] = {0.0, 0.0}, in[2], tot[2];
     double R = 0.0, Rp = 0.0;
     int lr = -1, lp_s = -1;
-    for (int blk = 0; blk < nsub; blk += kWG) {
-        const int s = blk + int(threadIdx.x);
-        v[0] = 0.0; v[1] = 0.0;
-        if (s < nsub) {
-            v[0] = __longlong_as_double((long long)ld_coherent(mass + 2 * s));
-            v[1] = __longlong_as_double((long long)ld_coherent(mass + 2 * s + 1));
-        }
+    if (one) {
+        v[0] = polled[0];
+        v[1] = polled[1];
         wg_scan<2>(v, ex, in, tot, sh);
         post_last(v[0] > 0.0, 1, sh);
         post_last(v[1] > 0.0, 2, sh);
         __syncthreads();
-        if (wg_last(1, sh) >= 0) lr = blk + wg_last(1, sh);
-        if (wg_last(2, sh) >= 0) lp_s = blk + wg_last(2, sh);
-        R = R + tot[0];
-        Rp = Rp + tot[1];
+        lr = wg_last(1, sh);
+        lp_s = wg_last(2, sh);
+        R = tot[0];
+        Rp = tot[1];
+    } else {
+        for (int blk = 0; blk < nsub; blk += kWG) {
+            const int s = blk + int(threadIdx.x);
+            v[0] = 0.0; v[1] = 0.0;
+            if (s < nsub) {
+                v[0] = mass_value(ld_coherent(mass + 2 * s));
+                v[1] = mass_value(ld_coherent(mass + 2 * s + 1));
+            }
+            wg_scan<2>(v, ex, in, tot, sh);
+            post_last(v[0] > 0.0, 1, sh);
+            post_last(v[1] > 0.0, 2, sh);
+            __syncthreads();
+            if (wg_last(1, sh) >= 0) lr = blk + wg_last(1, sh);
+            if (wg_last(2, sh) >= 0) lp_s = blk + wg_last(2, sh);
+            R = R + tot[0];
+            Rp = Rp + tot[1];
+        }
     }
     // The draw is from the residual when it has mass; a rejection whose
     // residual is zero draws from p_j, a bonus draw from p_n (whose residual
@@ -888,7 +913,7 @@ __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, cons
         for (int blk = 0; blk < nsub; blk += kWG) {
             const int s = blk + int(threadIdx.x);
             double w1[1] = {0.0}, ex1[1], in1[1], tot1[1];
-            if (s < nsub) w1[0] = __longlong_as_double((long long)ld_coherent(mass + 2 * s + sel));
+            if (s < nsub) w1[0] = mass_value(ld_coherent(mass + 2 * s + sel));
             wg_scan<1>(w1, ex1, in1, tot1, sh);
             const double bs = P + ex1[0];
             post_first(s < nsub && w1[0] > 0.0 && bs + w1[0] > target, 3, sh);
@@ -936,31 +961,36 @@ __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, cons
         y = (yc >= 0) ? yc : lp;
     }
     if (y != -2) {
-        a.out_tok[size_t(b) * G1 + d.j] = y;
+        st_out(a.out_tok + size_t(b) * G1 + d.j, y);
         if (a.d_r) a.d_r[b] = resid ? float(R) : -1.0f;
     }
 }
 
 // Request pass (after the row pass has completed): workgroup w of request b
-// decides the request, streams sub-tiles [w*spw, (w+1)*spw) of the draw row,
-// and the last of the request's nc2 workgroups selects the token and zeroes
-// the request's partials, gathers and masses.
+// decides the request, streams sub-tiles [w*spw, (w+1)*spw) of the draw row
+// and writes their masses (on a data error, marks them done); the request's
+// last workgroup (w = nc2 - 1) waits for every mass word, selects the token,
+// writes the diagnostics and zeroes the request's partials, gathers and
+// masses.
 template <int ES, bool ALZ, bool ALQ>
 __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh) {
     Decision d;
-    bool arrive;
-    const bool ok = decide<ES>(a, b, w, d, arrive, sh);
-    if (!arrive) return;
+    bool proceed;
+    const bool ok = decide<ES>(a, b, w, d, proceed, sh);
+    if (!proceed) {
+        if (w == 0 && (a.d_lse || a.d_p || a.d_q || a.d_r)) write_diag<ES>(a, b, false, d.n, sh);
+        return;
+    }
     const int G1 = a.G + 1;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const bool diag = a.d_lse || a.d_p || a.d_q || a.d_r;
-    const void *zrow = nullptr;
-    const float *qrow = nullptr;
     uint64_t *mass = masses(a, b);
-    if (ok) {
-        zrow = static_cast<const char *>(a.logits) + (size_t(b) * G1 + d.j) * size_t(a.V) * ES;
-        qrow = d.resid ? a.q + (size_t(b) * a.G + d.j) * size_t(a.V)
-                       : reinterpret_cast<const float *>(a.ws + a.lay.zero);
+    const void *zrow = static_cast<const char *>(a.logits) + (size_t(b) * G1 + d.j) * size_t(a.V) * ES;
+    const float *qrow = d.resid ? a.q + (size_t(b) * a.G + d.j) * size_t(a.V)
+                                : reinterpret_cast<const float *>(a.ws + a.lay.zero);
+    if (!ok) {
+        const int s_beg = w * a.spw, s_end = min(a.nsub, (w + 1) * a.spw);
+        for (int i = 2 * s_beg + int(threadIdx.x); i < 2 * s_end; i += kWG) st_coherent(mass + i, kMassWritten);
+    } else {
         const int s_end = min(a.nsub, (w + 1) * a.spw);
         for (int s0 = w * a.spw; s0 < s_end; s0 += kSubBatch) {
             double rs[kSubBatch], ps[kSubBatch];
@@ -988,18 +1018,25 @@ __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh
             if (int(threadIdx.x) < 2 * kSubBatch) {
                 const int q = threadIdx.x, i = q % kSubBatch, which = q / kSubBatch;   // which: 0 residual, 1 target
                 const double m4 = ((sh.r.wt[0][q] + sh.r.wt[1][q]) + sh.r.wt[2][q]) + sh.r.wt[3][q];
-                if (s0 + i < s_end) st_coherent(mass + 2 * (s0 + i) + which, uint64_t(__double_as_longlong(m4)));
+                if (s0 + i < s_end) st_coherent(mass + 2 * (s0 + i) + which, mass_word(m4));
             }
         }
     }
-    if (!arrive_last(draw_counter(a, b), unsigned(a.nc2), sh)) return;
-    if (ok) {
-        final_select<ES, ALZ, ALQ>(a, b, d, zrow, qrow, sh);
-        for (int i = threadIdx.x; i < 2 * a.nsub; i += kWG) st_coherent(mass + i, 0ull);
-    }
-    if (diag) write_diag<ES>(a, b, ok, d.n, sh);
+    // The request's last workgroup in grid order selects the token: it waits
+    // only for workgroups dispatched before it, which never wait themselves.
+    // A mass word is written after its workgroup's decision, so once all are
+    // written no workgroup of the request reads the partials any more.
+    if (w != a.nc2 - 1) return;
+    // The diagnostics need only the merged rows, so they go out before the wait.
+    if (a.d_lse || a.d_p || a.d_q || a.d_r) write_diag<ES>(a, b, ok, d.n, sh);
+    double polled[2];
+    const bool all = wait_masses(a, b, polled);
+    if (ok && all) final_select<ES, ALZ, ALQ>(a, b, d, zrow, qrow, polled, sh);
+    else if (ok) write_error(a, b);              // an expired wait
+    __syncthreads();
+    for (int i = threadIdx.x; i < 2 * a.nsub; i += kWG) st_coherent(mass + i, 0ull);
     uint64_t *part = partials(a, b);
-    for (int i = threadIdx.x; i < (d.n + 1) * a.nc1; i += kWG) part[i] = 0ull;
+    for (int i = threadIdx.x; i < (d.n + 1) * a.np1; i += kWG) part[i] = 0ull;
     uint64_t *gx = gathered(a, b);
     for (int i = threadIdx.x; i < d.n; i += kWG) gx[i] = 0ull;
 }
@@ -1017,7 +1054,7 @@ __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
     // wave, so the workgroup does not poll every partial while the row pass
     // is still streaming.
     if (threadIdx.x == 0) {
-        const uint64_t *last = partials(a, b) + size_t(n + 1) * a.nc1 - 1;
+        const uint64_t *last = partials(a, b) + size_t(n + 1) * a.np1 - 1;
         for (uint32_t spins = 0; spins < a.spin_limit && !valid(ld_coherent(last)); ++spins)
             __builtin_amdgcn_s_sleep(8);
     }
@@ -1041,7 +1078,7 @@ __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
     }
     __syncthreads();
     uint64_t *pw = partials(a, b);
-    for (int i = threadIdx.x; i < (n + 1) * a.nc1; i += kWG) st_coherent(pw + i, 0ull);
+    for (int i = threadIdx.x; i < (n + 1) * a.np1; i += kWG) st_coherent(pw + i, 0ull);
 }
 
 // ------------------------------------------------------------- kernels
@@ -1049,11 +1086,35 @@ __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6); }
 __device__ __forceinline__ int row_jobs(const VerifyArgs &a) { return a.B * (a.G + 1) * a.nc1; }
 
-// Row pass of a sampled verify: one wave per (request, row, chunk).
+// Row pass of a sampled verify: one workgroup per (request b, row k, group g
+// of kWaves consecutive chunks), one wave per chunk.  The group's partial
+// merges its waves' (max, sum) pairs in wave order, so the request pass reads
+// a quarter as many partials.
 template <int ES, bool AL>
 __global__ __launch_bounds__(kWG) void k_rows_sampled(VerifyArgs a) {
-    const int job = int(blockIdx.x) * kWaves + wave_id();
-    if (job < row_jobs(a)) row_wave_sampled<ES, AL>(a, job, int(threadIdx.x) & 63);
+    __shared__ float gm[kWaves], gs[kWaves];
+    const int per = (a.G + 1) * a.np1;
+    const int i = blockIdx.x;
+    const int b = i / per, rem = i - b * per;
+    const int k = rem / a.np1, g = rem - k * a.np1;
+    const int n = verify_len(a, b);
+    if (n < 0 || n > a.G || k > n) return;           // row not read: the whole workgroup leaves
+    const int w = wave_id(), lane = int(threadIdx.x) & 63;
+    const int c = g * kWaves + w;
+    float M = neg_inf(), S = 0.0f;
+    if (c < a.nc1) row_chunk_sampled<ES, AL>(a, b, k, c, n, lane, M, S);
+    if (lane == 0) {
+        gm[w] = M;
+        gs[w] = S;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float m = fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3]));
+        float t = 0.0f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) t = t + gs[v] * rescale(gm[v], m, a.c32);
+        partials(a, b)[size_t(k) * a.np1 + g] = uint64_t(__float_as_uint(m)) | (uint64_t(__float_as_uint(t) | kValid) << 32);
+    }
 }
 
 // Request pass of a sampled verify: nc2 workgroups per request.

@@ -35,18 +35,21 @@ def to_device(w, device="cuda"):
     return z, q, x, u, vl
 
 
-def run_gpu(w, diag=True, verify_len=None):
+def run_gpu(w, diag=True, verify_len=None, with_event=False):
+    """The HIP path on w.  with_event: pass a row-pass event (recorded between
+    the row launch and the request launch)."""
     z, q, x, u, vl = to_device(w)
     if verify_len is not None:
         vl = verify_len
     T = np.float32(w["T"])
+    ev = torch.cuda.Event() if with_event else None
     if float(T) == 0.0:
-        acc, tok = sv.verify(z, None, x, None, 0.0, vl)
+        acc, tok = sv.verify(z, None, x, None, 0.0, vl, row_pass_event=ev)
         dg = None
     elif diag:
-        acc, tok, dg = sv.verify(z, q, x, u, float(T), vl, diag=True)
+        acc, tok, dg = sv.verify(z, q, x, u, float(T), vl, diag=True, row_pass_event=ev)
     else:
-        acc, tok = sv.verify(z, q, x, u, float(T), vl)
+        acc, tok = sv.verify(z, q, x, u, float(T), vl, row_pass_event=ev)
         dg = None
     torch.cuda.synchronize()
     out = {"accepted": acc.cpu().numpy().astype(np.int64), "tokens": tok.cpu().numpy().astype(np.int64)}

@@ -44,11 +44,11 @@ def test_status_strings():
 
 def test_workspace_query():
     w = _capi.verify_workspace_bytes(64, 15, 129280, _capi.SPEC_DTYPE_BF16)
-    # fixed 1 MiB counter region + a 256-byte zero block + partials 64*16 rows*64 chunks*8 B
-    # + masses 64*64 sub-tiles*16 B + gathers 64*15*8 B
-    assert w == (1 << 20) + 256 + 64 * 16 * 64 * 8 + 65536 + 64 * 15 * 8
-    # the counter region does not move with the shape
-    assert _capi.verify_workspace_bytes(1, 0, 1, _capi.SPEC_DTYPE_BF16) == (1 << 20) + 3 * 256
+    # a 256-byte zero block + partials 64*16 rows*64 chunks*8 B (sized for the
+    # greedy per-chunk count) + masses 64*64 sub-tiles*16 B + gathers 64*15*8 B
+    assert w == 256 + 64 * 16 * 64 * 8 + 65536 + 64 * 15 * 8
+    # every region is 256-byte aligned, the smallest shape included
+    assert _capi.verify_workspace_bytes(1, 0, 1, _capi.SPEC_DTYPE_BF16) == 3 * 256
     assert _capi.verify_workspace_bytes(64, 15, 129280, _capi.SPEC_DTYPE_F32) >= w
     assert _capi.verify_workspace_bytes(0, 15, 100, 1) == 0
     assert _capi.verify_workspace_bytes(1, -1, 100, 1) == 0

@@ -290,12 +290,42 @@ def test_data_errors():
     assert g["accepted"][7] >= 0
 
 
-def test_many_requests_fused_and_split_launch():
-    # 700 requests still fit one fused launch (all draw items after all row
-    # items); 1500 exceed half the resident capacity, so the draw pass runs as
-    # a second launch.
-    check(_rand_workload("many_fused", 700, 1, 300, seed=10))
-    check(_rand_workload("many_split", 1500, 1, 64, seed=13))
+def test_many_requests():
+    # Many small requests (T > 0): each request's draw workgroups trail its
+    # rows by a lag of many requests in the one launch.
+    check(_rand_workload("many_small", 700, 1, 300, seed=10))
+    check(_rand_workload("many_tiny", 1500, 1, 64, seed=13))
+    # T = 0: 700 requests share the row launch, 1500 exceed half the resident
+    # capacity and run as a second launch.
+    g0 = np.random.default_rng(14)
+    for B, V in ((700, 300), (1500, 64)):
+        bits = W.f32_to_bf16_bits((2.0 * g0.normal(size=(B, 2, V))).astype(np.float32))
+        a = W.bf16_bits_to_f32(bits).argmax(2)
+        x = np.where(g0.random((B, 1)) < 0.5, a[:, :1], g0.integers(0, V, (B, 1))).astype(np.int32)
+        w = W.Workload(name=f"many_greedy_{B}", B=B, G=1, V=V, T=0.0, dtype="bf16", logits=bits,
+                       draft_probs=None, draft_tokens=x, uniforms=None, verify_len=None)
+        say(f"[parity] {w['name']}")
+        g = run_gpu(w)
+        o = run_oracle(w)
+        np.testing.assert_array_equal(g["accepted"], o["accepted"])
+        np.testing.assert_array_equal(g["tokens"], o["tokens"])
+
+
+def test_row_pass_event_changes_nothing():
+    # Asking for the row-pass event (a timing aid) leaves every output and
+    # diagnostic bitwise unchanged, and both calls match the oracle.
+    cases = [W.block(B=8, G=15, V=20000), W.tiny(seed=1240), _rand_workload("split_fp32", 5, 4, 3000, dtype="f32", seed=4)]
+    w = _rand_workload("split_vlen", 6, 5, 5000, seed=21)
+    w["verify_len"] = np.array([0, 5, 2, 3, 1, 4], np.int32)
+    cases.append(w)
+    for w in cases:
+        say(f"[parity] with row-pass event: {w['name']} B={w['B']} G={w['G']} V={w['V']}")
+        g1 = run_gpu(w)
+        g2 = run_gpu(w, with_event=True)
+        for k in g1:
+            np.testing.assert_array_equal(np.nan_to_num(g1[k], nan=-7.0), np.nan_to_num(g2[k], nan=-7.0), err_msg=k)
+        o = run_oracle(w)
+        say("   ", compare(w, g2, o, w.get("verify_len")))
 
 
 def test_launch_plan_query():
@@ -333,9 +363,10 @@ def test_workspace_left_zero():
 def test_workspace_shared_across_shapes():
     """One workspace for calls whose shapes (and so data layouts) differ.
 
-    Regression: the counters once sat at offsets that moved with B, so a larger
-    batch read an earlier call's partial sums as counters.  They now sit at
-    fixed offsets in a region no data ever occupies.
+    Regression: counters once sat at offsets that moved with B, so a larger
+    batch read an earlier call's partial sums as counters.  No workspace word is
+    a counter now: every word carries its own written mark and is zeroed by its
+    last reader.
     """
     big = W.block(B=64, G=15, V=20000, seed=21)
     wide = _rand_workload("wide", 700, 1, 300, seed=22)
