@@ -15,10 +15,15 @@
 //
 //   1. every confidence and every cost entry the scan can reach is loaded into
 //      LDS at once (one memory round trip);
-//   2. one thread per request: fp64 CumProd in place; detect whether survival
-//      is non-increasing along each request (always true for c in [0, 1]);
-//   3. bitonic sort of (s, k*B + b) keys in LDS, candidates first (the key's
-//      second half orders equal survivals by k, then b, with no division);
+//   2. one thread per request: the fp64 running product of its confidences
+//      (the sequential loop's order), and whether survival is non-increasing
+//      along every request (always true for c in [0, 1]);
+//   3. bitonic sort of (s, k*B + b) keys, candidates first (the key's second
+//      half orders equal survivals by k, then b, with no division).  With at
+//      most 1024 slots each thread holds one in registers and the network is
+//      unrolled: partners closer than a wave are read across lanes with DPP
+//      (strides 1, 2, 4, 8) and the row-swap permutes (16, 32), farther ones
+//      through LDS;
 //   4. contiguity (only when some survival increases): a candidate can be kept
 //      only if all shallower positions of its request are candidates placed
 //      before it;
@@ -43,13 +48,18 @@ constexpr int kRegSort = 1024;     // at most this many slots: one per thread, s
 constexpr int kPad = 0x7fffffff;
 
 struct SchedSmem {
-    double key[kMaxCand];      // confidence, then survival (slot = b * G + k), then sorted survival
+    double key[kMaxCand];      // survival (slot = b * G + k), then sorted survival
     int id[kMaxCand];          // k * B + b, or kPad for padding / non-candidates
-    int pos[kMaxCand];         // sorted position of each candidate (slot b * G + k), or -1
+    union {
+        double conf[kMaxCand]; // the confidences (slot = b * G + k)
+        int pos[kMaxCand];     // contiguity: sorted position of each candidate (slot b * G + k), or -1
+        struct {
+            double xk[2][kRegSort];   // register sort: exchange buffers for strides >= 64
+            int xi[2][kRegSort];
+        } reg;
+    } u;
     int len[kMaxCand];         // per request kept length (B <= kMaxCand)
     float cost[kMaxCand + 1];  // cost[B + m] for m = 0..min(B*G, budget - B)
-    double xk[2][kRegSort];    // register sort: exchange buffers for strides >= 64
-    int xi[2][kRegSort];
     int nvalid, mstar;
     double taustar;            // tau_{m*}
 };
@@ -58,6 +68,59 @@ struct SchedSmem {
 // (the id k * B + b compares in exactly that order; padding sorts last).
 __device__ __forceinline__ bool before(double s1, int id1, double s2, int id2) {
     return s1 > s2 || (s1 == s2 && id1 < id2);
+}
+// The same order without branches (for the sorting network).
+__device__ __forceinline__ bool before_nb(double s1, int id1, double s2, int id2) {
+    return (int(s1 > s2) | (int(s1 == s2) & int(id1 < id2))) != 0;
+}
+
+// Value of lane (lane ^ S) of the wave, S < 64.
+template <int CTRL> __device__ __forceinline__ int dpp(int x) {
+    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+}
+template <int S> __device__ __forceinline__ int xor_lane(int x, int lane) {
+    if constexpr (S == 1) return dpp<0xB1>(x);                 // quad_perm [1, 0, 3, 2]
+    else if constexpr (S == 2) return dpp<0x4E>(x);            // quad_perm [2, 3, 0, 1]
+    else if constexpr (S == 4) return dpp<0x1B>(dpp<0x141>(x));   // row_half_mirror (^7), then quad_perm [3, 2, 1, 0] (^3)
+    else if constexpr (S == 8) return dpp<0x128>(x);           // row_ror:8
+    else if constexpr (S == 16) {
+        // Row swap: result 0 holds the even row's lanes, result 1 the odd row's.
+        const auto r = __builtin_amdgcn_permlane16_swap(unsigned(x), unsigned(x), false, false);
+        return int((lane & 16) ? r[0] : r[1]);
+    } else {
+        static_assert(S == 32, "in-wave stride");
+        const auto r = __builtin_amdgcn_permlane32_swap(unsigned(x), unsigned(x), false, false);
+        return int((lane & 32) ? r[0] : r[1]);
+    }
+}
+template <int S> __device__ __forceinline__ double xor_lane_d(double x, int lane) {
+    const long long v = __double_as_longlong(x);
+    const int lo = xor_lane<S>(int(uint32_t(v)), lane), hi = xor_lane<S>(int(uint32_t(uint64_t(v) >> 32)), lane);
+    return __longlong_as_double((long long)((uint64_t(uint32_t(hi)) << 32) | uint32_t(lo)));
+}
+
+// One compare-exchange step of the bitonic network at (size, stride): the
+// thread keeps the first or the second of its pair in the merge direction.
+__device__ __forceinline__ void cx_step(double &s, int &id, double s2, int id2, int tid, int size, int stride) {
+    const bool keep_first = ((tid & stride) == 0) == ((tid & size) == 0);
+    const bool mine_first = before_nb(s, id, s2, id2);
+    if (keep_first != mine_first) {
+        s = s2;
+        id = id2;
+    }
+}
+template <int S>
+__device__ __forceinline__ void cx_wave(double &s, int &id, int tid, int lane, int size) {
+    cx_step(s, id, xor_lane_d<S>(s, lane), xor_lane<S>(id, lane), tid, size, S);
+}
+// The in-wave strides of a merge stage of `size`, largest first.
+__device__ __forceinline__ void cx_in_wave(double &s, int &id, int tid, int lane, int size, int top) {
+    if (top >= 32) cx_wave<32>(s, id, tid, lane, size);
+    if (top >= 16) cx_wave<16>(s, id, tid, lane, size);
+    if (top >= 8) cx_wave<8>(s, id, tid, lane, size);
+    if (top >= 4) cx_wave<4>(s, id, tid, lane, size);
+    if (top >= 2) cx_wave<2>(s, id, tid, lane, size);
+    cx_wave<1>(s, id, tid, lane, size);
 }
 
 __device__ __forceinline__ double lane_d(double x, int l) {
@@ -91,34 +154,37 @@ __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
     while (Np < N) Np <<= 1;
 
     // 1. every input the scan can read, in one round trip.
-    for (int i = tid; i < N; i += nth) sh.key[i] = double(a.conf[i]);
+    for (int i = tid; i < N; i += nth) sh.u.conf[i] = double(a.conf[i]);
     for (int i = tid; i <= mt_max; i += nth) sh.cost[i] = a.cost[B + i];
     __syncthreads();
 
-    // 2. survival, sequential product per request, in place (LDS reads issued
-    //    together for up to 16 drafts).
+    // 2. survival s[b, k] = ((c[b,0] * c[b,1]) * ...) * c[b,k], the
+    //    sequential product, one thread per request (for G <= 16 its reads are
+    //    issued together: clamped in bounds, the ones past G unused).
     bool mono = true;
     for (int b = tid; b < B; b += nth) {
-        double acc = 1.0, prev = 1.0;
+        const double *c = sh.u.conf + b * G;
+        double *sv = sh.key + b * G;
+        double acc = 1.0;
         if (G <= 16) {
-            double c[16];
+            double cv[16];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) c[k] = (k < G) ? sh.key[b * G + k] : 1.0;
+            for (int k = 0; k < 16; ++k) cv[k] = sh.u.conf[min(b * G + k, N - 1)];
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 if (k < G) {
-                    acc = acc * c[k];
-                    if (k > 0 && !(acc <= prev)) mono = false;
-                    prev = acc;
-                    sh.key[b * G + k] = acc;
+                    const double nx = acc * cv[k];
+                    if (k > 0 && !(nx <= acc)) mono = false;
+                    acc = nx;
+                    sv[k] = acc;
                 }
             }
         } else {
             for (int k = 0; k < G; ++k) {
-                acc = acc * sh.key[b * G + k];
-                if (k > 0 && !(acc <= prev)) mono = false;
-                prev = acc;
-                sh.key[b * G + k] = acc;
+                const double nx = acc * c[k];
+                if (k > 0 && !(nx <= acc)) mono = false;
+                acc = nx;
+                sv[k] = acc;
             }
         }
         sh.len[b] = 0;
@@ -128,32 +194,24 @@ __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
     // 3. sort the candidates (s desc, k asc, b asc); padding last.
     int ncand;
     if (Np <= kRegSort) {
-        // One slot per thread, bitonic network in registers: partners closer
-        // than a wave exchange by shuffles, farther ones through LDS (two
-        // buffers, so one barrier per stage).
+        // One slot per thread, bitonic network in registers: partners in the
+        // wave by cross-lane reads (the in-wave strides of a stage unrolled),
+        // farther ones through LDS (two buffers, so one barrier per step).
         double s;
         int id;
         slot_key(sh, tid, N, B, G, eps, s, id);
         int buf = 0;
         for (int size = 2; size <= Np; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                double s2;
-                int id2;
-                if (stride < 64) {
-                    s2 = __shfl_xor(s, stride);
-                    id2 = __shfl_xor(id, stride);
-                } else {
-                    sh.xk[buf][tid] = s;
-                    sh.xi[buf][tid] = id;
-                    __syncthreads();
-                    s2 = sh.xk[buf][tid ^ stride];
-                    id2 = sh.xi[buf][tid ^ stride];
-                    buf ^= 1;
-                }
-                const bool keep_first = ((tid & stride) == 0) == ((tid & size) == 0);
-                const bool mine_first = before(s, id, s2, id2);
-                if (keep_first != mine_first) { s = s2; id = id2; }
+            for (int stride = size >> 1; stride >= 64; stride >>= 1) {
+                sh.u.reg.xk[buf][tid] = s;
+                sh.u.reg.xi[buf][tid] = id;
+                __syncthreads();
+                const double s2 = sh.u.reg.xk[buf][tid ^ stride];
+                const int id2 = sh.u.reg.xi[buf][tid ^ stride];
+                buf ^= 1;
+                cx_step(s, id, s2, id2, tid, size, stride);
             }
+            cx_in_wave(s, id, tid, lane, size, min(size >> 1, 32));
         }
         ncand = __syncthreads_count(tid < Np && id != kPad);
         if (tid < Np) { sh.key[tid] = s; sh.id[tid] = id; }
@@ -194,12 +252,12 @@ __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
 
     // 4. contiguity: only when some survival increases along a request.
     if (!nonincr) {
-        for (int i = tid; i < N; i += nth) sh.pos[i] = -1;
+        for (int i = tid; i < N; i += nth) sh.u.pos[i] = -1;
         __syncthreads();
         for (int p = tid; p < ncand; p += nth) {
             const int id = sh.id[p];
             const int k = id / B, b = id - k * B;
-            sh.pos[b * G + k] = p;
+            sh.u.pos[b * G + k] = p;
         }
         __syncthreads();
         for (int p = tid; p < ncand; p += nth) {
@@ -208,7 +266,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
             bool valid = true;
             int prevp = -1;
             for (int kk = 0; kk <= k; ++kk) {
-                const int pp = sh.pos[b * G + kk];
+                const int pp = sh.u.pos[b * G + kk];
                 if (pp < 0 || pp <= prevp) { valid = false; break; }
                 prevp = pp;
             }
