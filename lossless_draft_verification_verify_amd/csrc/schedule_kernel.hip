@@ -304,12 +304,21 @@ __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
             const double sm = (m < mt) ? sh.key[m] : 0.0;
             double tau0 = 0.0, tau1 = 0.0;
             const int cnt = min(64, mt - base);
+            if (cnt == 64) {                      // a full block: no per-step bound
 #pragma unroll
-            for (int j = 0; j < 64; ++j) {
-                if (j < cnt) {
+                for (int j = 0; j < 64; ++j) {
                     if (lane == j) tau0 = t;
                     t = t + lane_d(sm, j);
                     if (lane == j) tau1 = t;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 64; ++j) {
+                    if (j < cnt) {
+                        if (lane == j) tau0 = t;
+                        t = t + lane_d(sm, j);
+                        if (lane == j) tau1 = t;
+                    }
                 }
             }
             bool fail = false;
