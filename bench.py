@@ -121,9 +121,9 @@ def _oracle_slice(args):
 _CPU_W = None
 
 
-def cpu_baseline(w, workers, reqs, reps=6):
+def cpu_baseline(w, workers, reqs, reps=9):
     """Time the float64 oracle on host cores: the first `reqs` requests of the
-    workload, verified `reps` times over (about 10 s of summed CPU work)."""
+    workload, verified `reps` times over (10-15 s of summed CPU work)."""
     global _CPU_W
     import multiprocessing as mp
     _CPU_W = w
