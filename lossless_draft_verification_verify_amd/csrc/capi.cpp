@@ -166,7 +166,15 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
         // workgroup per (request, row, group of kWaves chunks).
         a.np1 = (a.nc1 + sv::kWaves - 1) / sv::kWaves;
         const long row_groups = long(B) * (G + 1) * a.np1;
-        a.spw = sv::kSubBatch;
+        // Sub-tiles per draw workgroup: about 1024 draw workgroups in all (each
+        // one repeats the request's decision, so fewer and longer ones keep
+        // that traffic from queueing behind the draw streams).
+        {
+            const long want = (long(B) * a.nsub + 1023) / 1024;
+            int spw = 1;
+            while (spw < want && spw < 8) spw <<= 1;
+            a.spw = spw;
+        }
         a.nc2 = (a.nsub + a.spw - 1) / a.spw;
         if (sv::launch_rows_sampled(a, az, es, int(row_groups), stream) != 0) return SPEC_ERR_DEVICE;
         if (row_event && hipEventRecord(row_event, static_cast<hipStream_t>(stream)) != hipSuccess)
