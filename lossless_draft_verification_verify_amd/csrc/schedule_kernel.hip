@@ -23,7 +23,7 @@
 //      most 1024 slots each thread holds one in registers and the network is
 //      unrolled: partners closer than a wave are read across lanes with DPP
 //      (strides 1, 2, 4, 8) and the row-swap permutes (16, 32), farther ones
-//      through LDS;
+//      through LDS, two strides per barrier where two remain;
 //   4. contiguity (only when some survival increases): a candidate can be kept
 //      only if all shallower positions of its request are candidates placed
 //      before it;
@@ -74,9 +74,10 @@ __device__ __forceinline__ bool before_nb(double s1, int id1, double s2, int id2
     return (int(s1 > s2) | (int(s1 == s2) & int(id1 < id2))) != 0;
 }
 
-// Value of lane (lane ^ S) of the wave, S < 64.
+// Value of lane (lane ^ S) of the wave, S < 64.  (Every DPP pattern used
+// reads an active lane inside its row, so no lane needs an old value.)
 template <int CTRL> __device__ __forceinline__ int dpp(int x) {
-    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
 }
 template <int S> __device__ __forceinline__ int xor_lane(int x, int lane) {
     if constexpr (S == 1) return dpp<0xB1>(x);                 // quad_perm [1, 0, 3, 2]
@@ -109,9 +110,49 @@ __device__ __forceinline__ void cx_step(double &s, int &id, double s2, int id2, 
         id = id2;
     }
 }
+// The value position pos keeps after the step (size, stride) of a pair whose
+// values are (s1, id1) at pos and (s2, id2) at its partner.
+__device__ __forceinline__ void cx_value(double s1, int id1, double s2, int id2, int pos, int size, int stride,
+                                         double &so, int &ido) {
+    const bool keep_first = ((pos & stride) == 0) == ((pos & size) == 0);
+    const bool mine = keep_first == before_nb(s1, id1, s2, id2);
+    so = mine ? s1 : s2;
+    ido = mine ? id1 : id2;
+}
+// The row-swap permutes leave every lane both members of its pair: result 0
+// holds the lower lane's value, result 1 the upper one's.
+template <int S> __device__ __forceinline__ void pair_of(int x, int &lo, int &hi) {
+    if constexpr (S == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(unsigned(x), unsigned(x), false, false);
+        lo = int(r[0]);
+        hi = int(r[1]);
+    } else {
+        static_assert(S == 32, "row-swap stride");
+        const auto r = __builtin_amdgcn_permlane32_swap(unsigned(x), unsigned(x), false, false);
+        lo = int(r[0]);
+        hi = int(r[1]);
+    }
+}
 template <int S>
 __device__ __forceinline__ void cx_wave(double &s, int &id, int tid, int lane, int size) {
-    cx_step(s, id, xor_lane_d<S>(s, lane), xor_lane<S>(id, lane), tid, size, S);
+    if constexpr (S == 16 || S == 32) {
+        // The lane keeps the pair's first element (in the sort order) when it
+        // keeps "first", else the second.
+        const long long v = __double_as_longlong(s);
+        int l0, h0, l1, h1, il, ih;
+        pair_of<S>(int(uint32_t(v)), l0, h0);
+        pair_of<S>(int(uint32_t(uint64_t(v) >> 32)), l1, h1);
+        pair_of<S>(id, il, ih);
+        const double sl = __longlong_as_double((long long)((uint64_t(uint32_t(l1)) << 32) | uint32_t(l0)));
+        const double shv = __longlong_as_double((long long)((uint64_t(uint32_t(h1)) << 32) | uint32_t(h0)));
+        const bool keep_first = ((tid & S) == 0) == ((tid & size) == 0);
+        const bool lo_first = before_nb(sl, il, shv, ih);
+        const bool take_lo = keep_first == lo_first;
+        s = take_lo ? sl : shv;
+        id = take_lo ? il : ih;
+    } else {
+        cx_step(s, id, xor_lane_d<S>(s, lane), xor_lane<S>(id, lane), tid, size, S);
+    }
 }
 // The in-wave strides of a merge stage of `size`, largest first.
 __device__ __forceinline__ void cx_in_wave(double &s, int &id, int tid, int lane, int size, int top) {
@@ -202,14 +243,31 @@ __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
         slot_key(sh, tid, N, B, G, eps, s, id);
         int buf = 0;
         for (int size = 2; size <= Np; size <<= 1) {
-            for (int stride = size >> 1; stride >= 64; stride >>= 1) {
+            int stride = size >> 1;
+            while (stride >= 64) {
                 sh.u.reg.xk[buf][tid] = s;
                 sh.u.reg.xi[buf][tid] = id;
                 __syncthreads();
-                const double s2 = sh.u.reg.xk[buf][tid ^ stride];
-                const int id2 = sh.u.reg.xi[buf][tid ^ stride];
+                if (stride >= 128) {
+                    // Two steps per barrier: strides (stride, h) over the four
+                    // positions t, t^stride, t^h, t^stride^h.
+                    const int h = stride >> 1;
+                    const double sa = sh.u.reg.xk[buf][tid ^ stride], sb = sh.u.reg.xk[buf][tid ^ h],
+                                 sc = sh.u.reg.xk[buf][tid ^ stride ^ h];
+                    const int ia = sh.u.reg.xi[buf][tid ^ stride], ib = sh.u.reg.xi[buf][tid ^ h], ic = sh.u.reg.xi[buf][tid ^ stride ^ h];
+                    double s1t, s1h;
+                    int i1t, i1h;
+                    cx_value(s, id, sa, ia, tid, size, stride, s1t, i1t);
+                    cx_value(sb, ib, sc, ic, tid ^ h, size, stride, s1h, i1h);
+                    cx_value(s1t, i1t, s1h, i1h, tid, size, h, s, id);
+                    stride >>= 2;
+                } else {
+                    const double s2 = sh.u.reg.xk[buf][tid ^ stride];
+                    const int id2 = sh.u.reg.xi[buf][tid ^ stride];
+                    cx_step(s, id, s2, id2, tid, size, stride);
+                    stride >>= 1;
+                }
                 buf ^= 1;
-                cx_step(s, id, s2, id2, tid, size, stride);
             }
             cx_in_wave(s, id, tid, lane, size, min(size >> 1, 32));
         }
