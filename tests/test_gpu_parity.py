@@ -234,6 +234,41 @@ def test_unaligned_vocab_sizes():
         check(_rand_workload(f"V{V}_{dt}", 6, 4, V, dtype=dt, seed=V))
 
 
+def test_maximum_drafts():
+    # G = 255, the most draft positions a request may carry.
+    check(_rand_workload("G255_bf16", 2, 255, 700, seed=31))
+    check(_rand_workload("G255_f32", 2, 255, 300, dtype="f32", seed=32))
+
+
+def test_large_vocabulary():
+    # V = 2^22 + 7: 2049 chunks per row give 513 partials per row (past the
+    # merge that holds a row's partials in registers) and 2049 draw sub-tiles
+    # (past the one-block mass scan and selection).
+    check(_rand_workload("V4M", 2, 2, (1 << 22) + 7, seed=33, zscale=3.0))
+
+
+def test_large_vocabulary_greedy():
+    # V = 2^22 + 3 at T = 0: 2049 chunk partials per row, past the greedy
+    # merge's one-batch path.
+    g0 = np.random.default_rng(34)
+    B, G, V = 3, 2, (1 << 22) + 3
+    bits = W.f32_to_bf16_bits((2.0 * g0.normal(size=(B, G + 1, V))).astype(np.float32))
+    a = W.bf16_bits_to_f32(bits).argmax(2)
+    x = np.where(g0.random((B, G)) < 0.7, a[:, :G], g0.integers(0, V, (B, G))).astype(np.int32)
+    w = W.Workload(name="greedy_V4M", B=B, G=G, V=V, T=0.0, dtype="bf16", logits=bits,
+                   draft_probs=None, draft_tokens=x, uniforms=None, verify_len=None)
+    say(f"[parity] {w['name']}")
+    g = run_gpu(w)
+    o = run_oracle(w)
+    np.testing.assert_array_equal(g["accepted"], o["accepted"])
+    np.testing.assert_array_equal(g["tokens"], o["tokens"])
+
+
+def test_maximum_batch():
+    # B = 65536 requests (the batch limit), a tiny vocabulary.
+    check(_rand_workload("B65536", 65536, 1, 16, seed=35))
+
+
 def test_q_equal_p_accepts_all():
     B, G, V = 12, 5, 4096
     z = np.zeros((B, G + 1, V), np.float32)                  # uniform rows: p = 1/V exactly
