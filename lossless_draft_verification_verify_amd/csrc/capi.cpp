@@ -158,7 +158,6 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
     a.spin_limit = 1u << 20;
     const bool az = aligned(target_logits, 16) && (size_t(V) * es) % 16 == 0;
     const bool aq = aligned(draft_probs, 16) && V % 4 == 0;
-    const long row_wgs = (long(B) * (G + 1) * a.nc1 + sv::kWaves - 1) / sv::kWaves;   // greedy: one wave per chunk
 
     if (sampled) {
         // Row pass, then request pass (the kernel boundary orders every row
@@ -188,7 +187,9 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
     if (hipGetDevice(&dev) != hipSuccess) return SPEC_ERR_DEVICE;
     const int one = greedy_one_launch(dev, az, es, B);
     if (one < 0) return SPEC_ERR_DEVICE;
-    a.np1 = a.nc1;
+    // One row workgroup per (request, row, group of kWaves chunks).
+    a.np1 = (a.nc1 + sv::kWaves - 1) / sv::kWaves;
+    const long row_wgs = long(B) * (G + 1) * a.np1;
     a.nc2 = 1;
     if (one) {
         a.mode = 0;

@@ -26,10 +26,10 @@ inline int chunk_elems(int esize) { return 64 * kRowVec * (16 / esize); }
 //   zero     256 bytes never written: the draft row a bonus draw reads in
 //            place of q (so the draw loads need no branch);
 //   part     [B*(G+1)*np1] u64 partials, bit 63 set once written
-//            (sampled, one per row workgroup of kWaves chunks: low = max
-//             bits, high = sum bits | 1<<31;
-//             greedy, one per chunk: low = max bits, high = (argmax + 2) | 1<<31);
-//            the region is sized for the greedy count (np1 = nc1);
+//            one per row workgroup of kWaves chunks (np1 = ceil(nc1 / kWaves)
+//            per row; the region is sized for nc1): sampled, low = max bits,
+//            high = sum bits | 1<<31; greedy, low = max bits, high =
+//            (argmax + 2) | 1<<31 (argmax -2: a NaN, -1: none);
 //   mass     [B*nsub] 2 u64: fp64 (residual mass, target mass) per sub-tile,
 //            bit 63 set once written;
 //   gx       [B*G] u64: the row pass's gather of draft k (sampled only):
@@ -76,7 +76,7 @@ struct VerifyArgs {
     float T;          // temperature
     float c32;        // log2(e) / T, the fp32 exponent scale
     int32_t nc1, ch1; // row-pass chunks (waves) per row, elements per chunk
-    int32_t np1;      // partials per row: sampled ceil(nc1 / kWaves), greedy nc1
+    int32_t np1;      // partials per row: ceil(nc1 / kWaves), one per row workgroup
     int32_t nsub;     // draw sub-tiles per row
     int32_t nc2, spw; // request workgroups per request, sub-tiles per workgroup
     int32_t mode;     // greedy kernel: 0 row items then request items; 1 row items only; 2 request items only

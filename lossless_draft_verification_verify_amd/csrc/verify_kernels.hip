@@ -237,6 +237,8 @@ struct __align__(16) Smem {
     int last;
     int q[6][kWaves];                             // per-wave results of ballot searches
     double base, R, Rp;
+    float gm[kWaves];                             // greedy row group: the waves' (max, index, NaN)
+    int gi[kWaves], gn[kWaves];
 };
 
 // ---------------------------------------------------------------- merges
@@ -397,20 +399,6 @@ __device__ __forceinline__ int chunk_index(int beg, int lane, int i) {
     return AL ? beg + (lane + 64 * (i / EPV)) * EPV + (i % EPV) : beg + lane + 64 * i;
 }
 
-// Greedy row-pass job -> (request, row, chunk); false if that row is not read.
-struct RowJob {
-    int b, k, c, n;
-};
-__device__ __forceinline__ bool row_job(const VerifyArgs &a, int job, RowJob &j) {
-    const int per = (a.G + 1) * a.nc1;
-    j.b = job / per;
-    const int local = job - j.b * per;
-    j.k = local / a.nc1;
-    j.c = local - j.k * a.nc1;
-    j.n = verify_len(a, j.b);
-    return j.n >= 0 && j.n <= a.G && j.k <= j.n;
-}
-
 // Sampled row pass, one wave: (max M, sum S of 2^((z - M) * c)) of chunk c
 // of row k of request b (n = the request's verify length), uniform across
 // the wave.  The chunk holding draft token x_k also stores z(x_k) and q(x_k)
@@ -469,19 +457,19 @@ __device__ void row_chunk_sampled(const VerifyArgs &a, int b, int k, int chunk, 
         gathered(a, b)[k] = uint64_t(__float_as_uint(gz)) | (uint64_t(__float_as_uint(gq)) << 32);
 }
 
-// Greedy row pass, one wave: (max, lowest index of the max, any NaN) of its
-// chunk.  The maximum comes first (v_max3, which drops NaN); a NaN anywhere
-// shows in a running fp32 sum of the chunk (which also turns NaN when +inf
-// meets -inf, a row whose maximum is +inf and so bad anyway); then each lane
-// finds its lowest position holding the maximum and the wave takes the lowest
-// such index.  An all -inf chunk has no argmax (index -1).
+// Greedy row pass, one wave: (max M, lowest index of the max, any NaN) of
+// chunk `chunk` of row k of request b, uniform across the wave.  The maximum
+// comes first (v_max3, which drops NaN); a NaN anywhere shows in a running
+// fp32 sum of the chunk (which also turns NaN when +inf meets -inf, a row
+// whose maximum is +inf and so bad anyway); then each lane finds its lowest
+// position holding the maximum and the wave takes the lowest such index.  An
+// all -inf chunk has no argmax (index -1).
 template <int ES, bool AL>
-__device__ void row_wave_greedy(const VerifyArgs &a, int job, int lane) {
-    RowJob jb;
-    if (!row_job(a, job, jb)) return;
+__device__ void row_chunk_greedy(const VerifyArgs &a, int b, int k, int chunk, int lane, float &M_out, int &idx_out,
+                                 bool &nan_out) {
     constexpr int EPL = kEPL<ES>;
-    const void *row = static_cast<const char *>(a.logits) + (size_t(jb.b) * (a.G + 1) + jb.k) * size_t(a.V) * ES;
-    const int beg = jb.c * a.ch1;
+    const void *row = static_cast<const char *>(a.logits) + (size_t(b) * (a.G + 1) + k) * size_t(a.V) * ES;
+    const int beg = chunk * a.ch1;
     float f[EPL];
     load_chunk<ES, AL>(row, beg, a.V, lane, f);
     float m = f[0];
@@ -493,7 +481,7 @@ __device__ void row_wave_greedy(const VerifyArgs &a, int job, int lane) {
 #pragma unroll
     for (int i = 0; i < EPL; i += 2) { s0 = s0 + f[i]; s1 = s1 + f[i + 1]; }
     const float sum = s0 + s1;
-    const bool nan = __ballot(sum != sum) != 0ull;
+    nan_out = __ballot(sum != sum) != 0ull;
     int bi = -1;
     if (M != neg_inf()) {                         // uniform
         int bo = -1;
@@ -501,9 +489,8 @@ __device__ void row_wave_greedy(const VerifyArgs &a, int job, int lane) {
         for (int i = EPL - 1; i >= 0; --i) bo = (f[i] == M) ? i : bo;
         bi = wave_min_i((bo >= 0) ? chunk_index<ES, AL>(beg, lane, bo) : INT_MAX);
     }
-    if (lane == 0)
-        st_coherent(partials(a, jb.b) + size_t(jb.k) * a.np1 + jb.c,
-                    uint64_t(__float_as_uint(M)) | (uint64_t(uint32_t((nan ? kNanIdx : bi) + 2) | kValid) << 32));
+    M_out = M;
+    idx_out = bi;
 }
 
 // ---------------------------------------------------------- draw sub-tiles
@@ -1084,7 +1071,6 @@ __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
 // ------------------------------------------------------------- kernels
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6); }
-__device__ __forceinline__ int row_jobs(const VerifyArgs &a) { return a.B * (a.G + 1) * a.nc1; }
 
 // Row pass of a sampled verify: one workgroup per (request b, row k, group g
 // of kWaves consecutive chunks), one wave per chunk.  The group's partial
@@ -1125,21 +1111,57 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     request_item_sampled<ES, ALZ, ALQ>(a, b, int(blockIdx.x) - b * a.nc2, sh);
 }
 
-// Greedy verify: row workgroups (4 row waves each, request-major), then one
-// request workgroup per request (mode 0); or only the row workgroups (mode 1)
-// / request workgroups (mode 2).
+// Greedy row workgroup gi: (request b, row k, group g of kWaves consecutive
+// chunks), one wave per chunk.  The group's partial is the largest of the
+// waves' maxima with the lowest index holding it (waves in chunk order, so the
+// first wave to reach the maximum holds the lowest index), and whether any
+// wave saw a NaN.  Stored coherently: the request items of the same launch
+// read it.
+template <int ES, bool AL>
+__device__ void row_group_greedy(const VerifyArgs &a, int gi, Smem &sh) {
+    const int per = (a.G + 1) * a.np1;
+    const int b = gi / per, rem = gi - b * per;
+    const int k = rem / a.np1, g = rem - k * a.np1;
+    const int n = verify_len(a, b);
+    if (n < 0 || n > a.G || k > n) return;           // row not read: the whole workgroup leaves
+    const int w = wave_id(), lane = int(threadIdx.x) & 63;
+    const int c = g * kWaves + w;
+    float M = neg_inf();
+    int idx = -1;
+    bool nan = false;
+    if (c < a.nc1) row_chunk_greedy<ES, AL>(a, b, k, c, lane, M, idx, nan);
+    if (lane == 0) {
+        sh.gm[w] = M;
+        sh.gi[w] = idx;
+        sh.gn[w] = int(nan);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float m = neg_inf();
+        int bi = -1, any_nan = 0;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            any_nan |= sh.gn[v];
+            if (sh.gi[v] >= 0 && (bi < 0 || sh.gm[v] > m)) {
+                m = sh.gm[v];
+                bi = sh.gi[v];
+            }
+        }
+        st_coherent(partials(a, b) + size_t(k) * a.np1 + g,
+                    uint64_t(__float_as_uint(m)) | (uint64_t(uint32_t((any_nan ? kNanIdx : bi) + 2) | kValid) << 32));
+    }
+}
+
+// Greedy verify: row workgroups (request-major), then one request workgroup
+// per request (mode 0); or only the row workgroups (mode 1) / request
+// workgroups (mode 2).
 template <int ES, bool AL>
 __global__ __launch_bounds__(kWG) void k_verify_greedy(VerifyArgs a) {
     __shared__ Smem sh;
-    const int jobs = row_jobs(a);
-    const int row_wgs = (jobs + kWaves - 1) / kWaves;
+    const int groups = a.B * (a.G + 1) * a.np1;
     const int i = blockIdx.x;
-    if (a.mode == 2 || (a.mode == 0 && i >= row_wgs)) {
-        request_item_greedy(a, a.mode == 2 ? i : i - row_wgs, sh);
-    } else {
-        const int job = i * kWaves + wave_id();
-        if (job < jobs) row_wave_greedy<ES, AL>(a, job, int(threadIdx.x) & 63);
-    }
+    if (a.mode == 2 || (a.mode == 0 && i >= groups)) request_item_greedy(a, a.mode == 2 ? i : i - groups, sh);
+    else row_group_greedy<ES, AL>(a, i, sh);
 }
 
 template <typename K>
