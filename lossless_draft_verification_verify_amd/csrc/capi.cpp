@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -159,6 +160,8 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
     const bool az = aligned(target_logits, 16) && (size_t(V) * es) % 16 == 0;
     const bool aq = aligned(draft_probs, 16) && V % 4 == 0;
 
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SPEC_ERR_DEVICE;
     if (sampled) {
         // Row pass, then request pass (the kernel boundary orders every row
         // partial before the per-request work, across all XCDs).  One row
@@ -175,7 +178,16 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
             a.spw = spw;
         }
         a.nc2 = (a.nsub + a.spw - 1) / a.spw;
-        if (sv::launch_rows_sampled(a, az, es, int(row_groups), stream) != 0) return SPEC_ERR_DEVICE;
+        if (verify_len && B <= sv::kWG) {
+            // Verify lengths leave rows unread: a grid of one resident load of
+            // workgroups whose workgroups visit only the read row groups.
+            const long cap = resident_capacity(dev, az, es);
+            if (cap <= 0) return SPEC_ERR_DEVICE;
+            if (sv::launch_rows_sampled_vl(a, az, es, int(std::min(row_groups, cap)), stream) != 0)
+                return SPEC_ERR_DEVICE;
+        } else if (sv::launch_rows_sampled(a, az, es, int(row_groups), stream) != 0) {
+            return SPEC_ERR_DEVICE;
+        }
         if (row_event && hipEventRecord(row_event, static_cast<hipStream_t>(stream)) != hipSuccess)
             return SPEC_ERR_DEVICE;
         return sv::launch_requests_sampled(a, az, aq, es, int(long(B) * a.nc2), stream) == 0 ? SPEC_OK
@@ -183,8 +195,6 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
     }
     // Greedy: the per-request items are cheap and wait for their rows, so they
     // share the row launch while they stay below half the resident capacity.
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return SPEC_ERR_DEVICE;
     const int one = greedy_one_launch(dev, az, es, B);
     if (one < 0) return SPEC_ERR_DEVICE;
     // One row workgroup per (request, row, group of kWaves chunks).

@@ -85,6 +85,7 @@ struct VerifyArgs {
 
 // Launchers (verify_kernels.hip).  Return a hipError_t as int.
 int launch_rows_sampled(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
+int launch_rows_sampled_vl(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
 int launch_requests_sampled(const VerifyArgs &a, bool aligned_z, bool aligned_q, int esize, int grid,
                             void *stream);
 int launch_verify_greedy(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);

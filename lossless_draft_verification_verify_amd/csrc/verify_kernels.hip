@@ -226,6 +226,17 @@ __device__ __forceinline__ double wave_scan_d(double x) {
     return x;
 }
 
+// Inclusive prefix sum of an int over the wave (same DPP pattern).
+__device__ __forceinline__ int wave_scan_i(int x) {
+    x = x + dpp_i<kRowShr1>(x);
+    x = x + dpp_i<kRowShr2>(x);
+    x = x + dpp_i<kRowShr4>(x);
+    x = x + dpp_i<kRowShr8>(x);
+    x = x + dpp_i<kRowBcast15, 0xA>(x);
+    x = x + dpp_i<kRowBcast31, 0xC>(x);
+    return x;
+}
+
 struct __align__(16) Smem {
     union {
         double sc[kWaves][2];                     // scan: wave totals
@@ -1072,19 +1083,13 @@ __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6); }
 
-// Row pass of a sampled verify: one workgroup per (request b, row k, group g
-// of kWaves consecutive chunks), one wave per chunk.  The group's partial
-// merges its waves' (max, sum) pairs in wave order, so the request pass reads
-// a quarter as many partials.
+// Row group (request b, row k <= n, group g of kWaves consecutive chunks) of
+// a sampled verify, one wave per chunk.  The group's partial merges its
+// waves' (max, sum) pairs in wave order, so the request pass reads a quarter
+// as many partials.
 template <int ES, bool AL>
-__global__ __launch_bounds__(kWG) void k_rows_sampled(VerifyArgs a) {
-    __shared__ float gm[kWaves], gs[kWaves];
-    const int per = (a.G + 1) * a.np1;
-    const int i = blockIdx.x;
-    const int b = i / per, rem = i - b * per;
-    const int k = rem / a.np1, g = rem - k * a.np1;
-    const int n = verify_len(a, b);
-    if (n < 0 || n > a.G || k > n) return;           // row not read: the whole workgroup leaves
+__device__ __forceinline__ void row_group_sampled(const VerifyArgs &a, int b, int k, int g, int n, float *gm,
+                                                  float *gs) {
     const int w = wave_id(), lane = int(threadIdx.x) & 63;
     const int c = g * kWaves + w;
     float M = neg_inf(), S = 0.0f;
@@ -1100,6 +1105,62 @@ __global__ __launch_bounds__(kWG) void k_rows_sampled(VerifyArgs a) {
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) t = t + gs[v] * rescale(gm[v], m, a.c32);
         partials(a, b)[size_t(k) * a.np1 + g] = uint64_t(__float_as_uint(m)) | (uint64_t(__float_as_uint(t) | kValid) << 32);
+    }
+}
+
+// Row pass of a sampled verify: one workgroup per (request, row, group).
+template <int ES, bool AL>
+__global__ __launch_bounds__(kWG) void k_rows_sampled(VerifyArgs a) {
+    __shared__ float gm[kWaves], gs[kWaves];
+    const int per = (a.G + 1) * a.np1;
+    const int i = blockIdx.x;
+    const int b = i / per, rem = i - b * per;
+    const int k = rem / a.np1, g = rem - k * a.np1;
+    const int n = verify_len(a, b);
+    if (n < 0 || n > a.G || k > n) return;           // row not read: the whole workgroup leaves
+    row_group_sampled<ES, AL>(a, b, k, g, n, gm, gs);
+}
+
+// Row pass with verify lengths and at most kWG requests, where most rows may
+// be unread: a grid sized to the device whose workgroups visit only the read
+// row groups.  Each workgroup first forms, in LDS, the prefix over requests of
+// their read row groups ((n_b + 1) * np1; none for an invalid length), then
+// takes jobs blockIdx, blockIdx + gridDim, ... of that list and finds each
+// job's request by binary search.
+template <int ES, bool AL>
+__global__ __launch_bounds__(kWG) void k_rows_sampled_vl(VerifyArgs a) {
+    __shared__ float gm[kWaves], gs[kWaves];
+    __shared__ int off[kWG + 1];
+    __shared__ int wtot[kWaves];
+    const int t = int(threadIdx.x), lane = t & 63, w = wave_id();
+    int cnt = 0;
+    if (t < a.B) {
+        const int n = a.vlen[t];
+        cnt = (n >= 0 && n <= a.G) ? (n + 1) * a.np1 : 0;
+    }
+    const int x = wave_scan_i(cnt);
+    if (lane == 63) wtot[w] = x;
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        base += (v < w) ? wtot[v] : 0;
+        total += wtot[v];
+    }
+    off[t] = base + x - cnt;                          // exclusive: first job of request t
+    if (t == 0) off[kWG] = total;
+    __syncthreads();
+    for (int job = int(blockIdx.x); job < total; job += int(gridDim.x)) {
+        int lo = 0, hi = a.B - 1;                     // the last request whose first job is <= job
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (off[mid] <= job) lo = mid;
+            else hi = mid - 1;
+        }
+        const int b = lo, local = job - off[b];
+        const int k = local / a.np1, g = local - k * a.np1;
+        row_group_sampled<ES, AL>(a, b, k, g, verify_len(a, b), gm, gs);
+        __syncthreads();                              // gm / gs are reused by the next job
     }
 }
 
@@ -1179,6 +1240,18 @@ int launch_rows_sampled(const VerifyArgs &a, bool az, int esize, int grid, void 
     } else {
         if (az) hipLaunchKernelGGL((k_rows_sampled<4, true>), dim3(grid), dim3(kWG), 0, st, a);
         else hipLaunchKernelGGL((k_rows_sampled<4, false>), dim3(grid), dim3(kWG), 0, st, a);
+    }
+    return int(hipGetLastError());
+}
+
+int launch_rows_sampled_vl(const VerifyArgs &a, bool az, int esize, int grid, void *stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (esize == 2) {
+        if (az) hipLaunchKernelGGL((k_rows_sampled_vl<2, true>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_rows_sampled_vl<2, false>), dim3(grid), dim3(kWG), 0, st, a);
+    } else {
+        if (az) hipLaunchKernelGGL((k_rows_sampled_vl<4, true>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_rows_sampled_vl<4, false>), dim3(grid), dim3(kWG), 0, st, a);
     }
     return int(hipGetLastError());
 }
