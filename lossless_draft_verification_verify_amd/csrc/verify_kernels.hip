@@ -21,9 +21,12 @@
 //                  DPP; the four waves' (max, sum) pairs merge in LDS into one
 //                  64-bit partial per group.  The wave whose chunk holds draft
 //                  token x_k also records z(x_k) and q(x_k), so the request
-//                  pass has no dependent gathers.
-//   request pass   nc2 workgroups per request, one per pair of 2048-element
-//                  sub-tiles of the draw row.  Each merges the request's
+//                  pass has no dependent gathers.  With verify lengths (at most
+//                  256 requests) a device-sized grid visits only the read row
+//                  groups instead.
+//   request pass   nc2 draw workgroups per request, each streaming spw
+//                  2048-element sub-tiles of the draw row (spw sized for about
+//                  1024 draw workgroups in all).  Each merges the request's
 //                  partials per row (16 lanes per row, fp64 sums), runs the
 //                  accept tests and finds the first rejection j (every
 //                  workgroup of the request computes the same result), then
@@ -37,9 +40,10 @@
 //
 // The only wait inside a sampled launch is that last workgroup's (bounded)
 // poll, which depends only on workgroups dispatched before it.  Temperature 0
-// (argmax) is one launch: row waves, then one workgroup per request that polls
-// its rows' partials (bounded wait) — the host keeps those below half the
-// resident capacity, else it splits them into a second launch.
+// (argmax) is one launch: row workgroups of four chunks, then one workgroup
+// per request that polls its rows' partials (bounded wait) — the host keeps
+// those below half the resident capacity, else it splits them into a second
+// launch.
 //
 // Words handed between workgroups of one launch (sub-tile masses, the greedy
 // partials) use coherent device-scope stores and loads instead of device-scope
