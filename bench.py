@@ -48,8 +48,15 @@ def row_pass_bytes(V, lens, esize=2):
 
 
 def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and blank lines removed, so
+    that only a change to the code itself makes recorded counters stale."""
+    import re
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    code = "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def measured_traffic():
