@@ -156,10 +156,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated in HBM")
-    ap.add_argument("--workload", choices=("block", "greedy", "scheduled"), default="block",
+    ap.add_argument("--workload", choices=("block", "greedy", "scheduled", "dcut"), default="block",
                     help="block: B=64 gamma=15 V=129280 T=1 (default); greedy: B=64 gamma=7 "
-                         "V=152064 T=0; scheduled: spec_schedule then spec_verify, gamma=15 V=129280")
-    ap.add_argument("--batch", type=int, default=64, help="B of the scheduled workload")
+                         "V=152064 T=0; scheduled: spec_schedule then spec_verify, gamma=15 V=129280; "
+                         "dcut: spec_dcut then spec_verify_packed over the packed rows, gamma=15 V=129280")
+    ap.add_argument("--batch", type=int, default=64, help="B of the scheduled and dcut workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=0)
     ap.add_argument("--cpu-requests", type=int, default=64)
@@ -187,8 +188,10 @@ def main():
         w = W.block()
     elif args.workload == "greedy":
         w = W.greedy()
-    else:
+    elif args.workload == "scheduled":
         w = W.scheduled(args.batch)
+    else:
+        w = W.ratio_budgeted(args.batch)
     B, G, V = w["B"], w["G"], w["V"]
     T = float(w["T"])
 
@@ -220,10 +223,38 @@ def main():
         tot = torch.empty(1, dtype=torch.int32, device=dev)
         tau = torch.empty(1, dtype=torch.float32, device=dev)
         sched = (conf, cost, w["budget"], vlen, tot, tau)
+    dcut = None
+    if args.workload == "dcut":
+        conf = to_dev(w["confidence"])
+        vlen = torch.empty(B, dtype=torch.int32, device=dev)
+        offs = torch.empty(B + 1, dtype=torch.int32, device=dev)
+        ridx = torch.empty(1, dtype=torch.int32, device=dev)
+        rows = torch.empty(1, dtype=torch.int32, device=dev)
+        sv.dcut(conf, w["ratios"], w["ratio_cost"], out_verify_len=vlen, out_row_offsets=offs, out_ratio=ridx,
+                out_rows=rows, utility=False)
+        torch.cuda.synchronize()
+        # The target's logits of the packed batch: the kept rows of each set,
+        # gathered once before timing (buffer sized for full depth).
+        off_h = offs.cpu().numpy()
+        idx = torch.tensor([b * (G + 1) + k for b in range(B) for k in range(int(off_h[b + 1] - off_h[b]))],
+                           dtype=torch.long, device=dev)
+        packed = []
+        for zz, _, _, _ in sets:
+            zp = torch.zeros(B * (G + 1), V, dtype=zz.dtype, device=dev)
+            zp[: idx.numel()] = zz.reshape(B * (G + 1), V)[idx]
+            packed.append(zp)
+        dcut = (conf, vlen, offs, ridx, rows, packed)
 
     def step(i, row_event=None):
         zz, qq, xx, uu = sets[i % len(sets)]
         vl = None
+        if dcut is not None:
+            conf, vlen, offs, ridx, rows, packed = dcut
+            sv.dcut(conf, w["ratios"], w["ratio_cost"], out_verify_len=vlen, out_row_offsets=offs, out_ratio=ridx,
+                    out_rows=rows, utility=False)
+            sv.verify_packed(packed[i % len(packed)], offs, qq, xx, uu, T, out_accepted=acc, out_tokens=tok,
+                             row_pass_event=row_event)
+            return
         if sched is not None:
             conf, cost, budget, vlen, tot, tau = sched
             sv.schedule(conf, cost, budget, out_verify_len=vlen, out_total=tot, out_expected=tau)
@@ -234,7 +265,12 @@ def main():
     step(0)
     torch.cuda.synchronize()
     a = acc.cpu().numpy()
-    lens = sched[3].cpu().numpy().astype(np.int64) if sched is not None else np.full(B, G)
+    if sched is not None:
+        lens = sched[3].cpu().numpy().astype(np.int64)
+    elif dcut is not None:
+        lens = dcut[1].cpu().numpy().astype(np.int64)
+    else:
+        lens = np.full(B, G)
     n_rej = int((a < lens).sum()) if T > 0 else 0
     esize = 2
     algo = algorithmic_bytes(B, G, V, lens, n_rej, esize)
@@ -287,10 +323,16 @@ def main():
     elif args.workload == "greedy":
         desc = "greedy draft verification: B=64, gamma=7, V=152064, bf16 logits N(0,4), T=0"
         kname = "k_verify_greedy (one launch: argmax row waves, then one workgroup per request)"
-    else:
+    elif args.workload == "scheduled":
         desc = (f"confidence-scheduled verification: spec_schedule (token budget {w['budget']}, "
                 f"cost 1 + 0.02 T) then spec_verify, B={B}, gamma=15, V=129280, bf16, T=1")
         kname = "spec_schedule + k_rows_sampled (time up to the row-pass event includes the scheduler)"
+    else:
+        r_idx = int(dcut[3].item())
+        desc = (f"ratio-budgeted verification: spec_dcut (ratios {list(w['ratios'])}, cost 1 + 0.02 rho B (G+1); "
+                f"chosen ratio {w['ratios'][r_idx]}, {int(dcut[4].item())} packed rows) then "
+                f"spec_verify_packed, B={B}, gamma=15, V=129280, bf16, T=1")
+        kname = "spec_dcut + k_rows_sampled_vl (time up to the row-pass event includes the ratio choice)"
     out = {
         "metric": "verified draft positions/sec and achieved HBM GB/s (% peak), B=64 gamma=15 V=129k",
         "value": round(value, 1),

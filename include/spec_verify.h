@@ -2,12 +2,18 @@
  * spec_verify.h -- C ABI of the MI355X (gfx950) batched lossless draft
  * verification library, libspecverify.so.
  *
- * Two operations:
+ * Operations:
  *
- *   spec_verify    speculative-sampling verification of a batch of draft
- *                  blocks against the target's logits.
- *   spec_schedule  confidence-scheduled verification depth: how many drafts
- *                  of each request to verify under a batch token budget.
+ *   spec_verify         speculative-sampling verification of a batch of draft
+ *                       blocks against the target's logits.
+ *   spec_verify_packed  the same over densely packed target rows (each
+ *                       request's kept positions only).
+ *   spec_schedule       confidence-scheduled verification depth: how many
+ *                       drafts of each request to verify under a batch token
+ *                       budget.
+ *   spec_dcut           ratio-budgeted verification depth: the budget ratio
+ *                       with the best estimated progress per profiled cost,
+ *                       its keep depths and the packed row offsets.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -59,7 +65,8 @@ typedef void *spec_stream_t;
 #define SPEC_MAX_BATCH 65536          /* B <= 65536 for spec_verify                      */
 #define SPEC_MAX_DRAFTS 255           /* G <= 255                                        */
 #define SPEC_MAX_VOCAB (1 << 30)      /* V <= 2^30                                       */
-#define SPEC_MAX_SCHEDULE_CANDIDATES 4096 /* B * G <= 4096 for spec_schedule              */
+#define SPEC_MAX_SCHEDULE_CANDIDATES 4096 /* B, B * G <= 4096 for spec_schedule, spec_dcut */
+#define SPEC_MAX_RATIOS 8             /* budget ratios per spec_dcut call                */
 
 /*
  * Optional diagnostics of spec_verify.  Each field may be NULL.
@@ -153,6 +160,35 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype,
                           void *workspace, size_t workspace_bytes, spec_stream_t stream);
 
 /*
+ * spec_verify_packed -- spec_verify over densely packed target rows.
+ *
+ * Operation ("AngelSpec", section 4.2, "Packing and correctness"): the kept
+ * prefixes of all requests form one dense batch of target positions, and each
+ * kept token is verified exactly as by spec_verify.  Request b's target rows
+ * are packed rows row_offsets[b] .. row_offsets[b+1]-1, its positions 0..n_b in
+ * order, so its verify length is n_b = row_offsets[b+1] - row_offsets[b] - 1.
+ * The result equals spec_verify on the unpacked rows with verify_len = n.
+ *
+ * Arguments as for spec_verify, except:
+ *   target_logits  [rows, V] of target_dtype; rows >= 1 is the number of rows
+ *                  the buffer holds (rows past the last request are not read).
+ *   row_offsets    [B+1] int32, device (e.g. spec_dcut's out_row_offsets).
+ *   There is no verify_len.  Workspace: spec_verify_workspace_bytes(B, G, V, dtype).
+ *   Diagnostics are indexed by (request, position) as for spec_verify.
+ *
+ * Data errors (outputs of that request all -1): row_offsets[b] < 0,
+ * row_offsets[b+1] > rows, or n_b outside [0, G]; and the data errors of
+ * spec_verify.
+ */
+spec_status_t spec_verify_packed(const void *target_logits, spec_dtype_t target_dtype, int32_t rows,
+                                 const int32_t *row_offsets, const float *draft_probs,
+                                 const int32_t *draft_tokens, const float *uniforms,
+                                 int32_t B, int32_t G, int32_t V, float temperature,
+                                 int32_t *out_accepted, int32_t *out_tokens,
+                                 const spec_verify_diag_t *diag,
+                                 void *workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/*
  * Number of kernel launches spec_verify makes for this shape on the current
  * device, with 16-byte-aligned target_logits: 2 for T > 0 (the pass over the
  * target rows, then the per-request pass); for T == 0, 1 when the per-request
@@ -197,6 +233,47 @@ spec_status_t spec_schedule(const float *confidence, const float *cost_table, in
                             int32_t *out_verify_len, int32_t *out_total_tokens,
                             float *out_expected_tokens,
                             void *workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/*
+ * spec_dcut -- ratio-budgeted verification depth (D-cut).
+ *
+ * Operation ("AngelSpec", section 4.2, Eq. 20-24), in float64:
+ *   score of request b's position k: s[b,0] = 1 (the bonus position) and
+ *   s[b,k] = prod_{t<k} c[b,t], k = 1..G, with each confidence clamped into
+ *   [0, 1] (NaN as 0);
+ *   for each ratio rho_r: K_r = max(B, ceil(rho_r * B * (G+1))) (rho_r * B(G+1)
+ *   formed exactly in double); the K_r best scores of the batch, equal scores
+ *   ranked shallower position first, then lower b, are kept: a prefix of
+ *   n_b^r + 1 positions of every request;
+ *   U_r = sum_b sum_{k<=n_b^r} s[b,k], the estimated progress;
+ *   the chosen ratio r* is the first with the largest U_r / cost_r;
+ *   out_verify_len[b] = n_b^{r*}; out_row_offsets = the exclusive prefix of
+ *   n_b + 1 (row_offsets[B] = K_{r*}), the packed layout spec_verify_packed reads.
+ * Keep depths, offsets and K are exact.  U_r is summed per request in position
+ * order, then over requests in a fixed tree order, so it can differ from a
+ * sequential sum in the last bits; r* can then differ only between ratios
+ * whose U / cost agree to about 1e-15 relative.
+ *
+ * Arguments:
+ *   confidence       [B, G] float, device (may be NULL when G == 0).
+ *   ratios           [num_ratios] float, host, each in (0, 1], e.g.
+ *                    {0.25, 0.5, 0.75, 1}.
+ *   ratio_cost       [num_ratios] float, host, each finite and > 0: the
+ *                    profiled cost of one step at this batch size and ratio.
+ *   1 <= num_ratios <= SPEC_MAX_RATIOS; B >= 1, G >= 0,
+ *   B, B*G <= SPEC_MAX_SCHEDULE_CANDIDATES.
+ *   out_verify_len   [B] int32, device: n_b in [0, G].
+ *   out_row_offsets  [B+1] int32, device.
+ *   out_ratio_index  [1] int32, device: r*.
+ *   out_total_rows   [1] int32, device: K_{r*} = sum_b (n_b + 1).
+ *   out_utility      [num_ratios] double, device, or NULL: U_r.
+ * Needs no workspace.
+ */
+spec_status_t spec_dcut(const float *confidence, int32_t B, int32_t G,
+                        const float *ratios, const float *ratio_cost, int32_t num_ratios,
+                        int32_t *out_verify_len, int32_t *out_row_offsets,
+                        int32_t *out_ratio_index, int32_t *out_total_rows,
+                        double *out_utility, spec_stream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *spec_status_string(spec_status_t status);

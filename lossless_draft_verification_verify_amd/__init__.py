@@ -8,6 +8,8 @@ the computation runs in the library's HIP kernels; there is no fallback.
     acc, tok = verify(target_logits, draft_probs, draft_tokens, uniforms, temperature)
     vlen, T, tau = schedule(confidence, cost_table, token_budget)
     acc, tok = verify(..., verify_len=vlen)
+    vlen, offsets, r, K, U = dcut(confidence, (0.25, 0.5, 0.75, 1.0), ratio_cost)
+    acc, tok = verify_packed(packed_logits, offsets, draft_probs, draft_tokens, uniforms, temperature)
 """
 
 import torch
@@ -15,7 +17,7 @@ import torch
 from . import _capi
 from ._capi import SpecError, SPEC_DTYPE_BF16, SPEC_DTYPE_F32  # noqa: F401
 
-__all__ = ["verify", "schedule", "verify_workspace_bytes", "SpecError", "load"]
+__all__ = ["verify", "verify_packed", "schedule", "dcut", "verify_workspace_bytes", "SpecError", "load"]
 
 _workspaces = {}
 
@@ -152,3 +154,105 @@ def schedule(confidence, cost_table, token_budget, eps=0.0, *, out_verify_len=No
     if st != _capi.SPEC_OK:
         raise SpecError(st, "spec_schedule")
     return out_verify_len, out_total, out_expected
+
+
+def verify_packed(packed_logits, row_offsets, draft_probs, draft_tokens, uniforms, temperature, *,
+                  out_accepted=None, out_tokens=None, diag=False, workspace=None, row_pass_event=None):
+    """Verify over packed target rows: request b's rows are packed_logits[off[b]:off[b+1]].
+
+    packed_logits [rows, V] bf16/fp32; row_offsets [B+1] int32 (device);
+    draft_probs [B, G, V]; draft_tokens [B, G]; uniforms [B, G+1] as for verify().
+    Returns what verify() returns.
+    """
+    z = packed_logits
+    if not isinstance(z, torch.Tensor) or z.dim() != 2:
+        raise ValueError("packed_logits must be a [rows, V] tensor")
+    dev = z.device
+    if dev.type != "cuda":
+        raise ValueError("packed_logits must be on a GPU")
+    rows, V = z.shape
+    if not isinstance(draft_tokens, torch.Tensor) or draft_tokens.dim() != 2:
+        raise ValueError("draft_tokens must be a [B, G] tensor")
+    B, G = draft_tokens.shape
+    G1 = G + 1
+    code = _dtype_code(z)
+    T = float(temperature)
+    i32, f32 = torch.int32, torch.float32
+    if out_accepted is None:
+        out_accepted = torch.empty(B, dtype=i32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty(B, G1, dtype=i32, device=dev)
+    for t, shape, name in ((draft_probs, (B, G, V), "draft_probs"), (uniforms, (B, G1), "uniforms"),
+                           (row_offsets, (B + 1,), "row_offsets"), (out_accepted, (B,), "out_accepted"),
+                           (out_tokens, (B, G1), "out_tokens")):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    d, dg, ev = None, None, 0
+    if isinstance(row_pass_event, int):
+        ev = row_pass_event
+    elif row_pass_event is not None:
+        if row_pass_event.cuda_event == 0:
+            row_pass_event.record(torch.cuda.current_stream(dev))
+        ev = row_pass_event.cuda_event
+    if diag:
+        dg = {"target_lse": torch.empty(B, G1, dtype=f32, device=dev),
+              "p_draft": torch.empty(B, G, dtype=f32, device=dev),
+              "q_draft": torch.empty(B, G, dtype=f32, device=dev),
+              "resid_mass": torch.empty(B, dtype=f32, device=dev)}
+        d = _capi.DiagT(*(dg[k].data_ptr() for k in ("target_lse", "p_draft", "q_draft", "resid_mass")), ev)
+    elif ev:
+        d = _capi.DiagT(0, 0, 0, 0, ev)
+    nbytes = _capi.verify_workspace_bytes(B, G, V, code)
+    ws = workspace if workspace is not None else _workspace(dev, stream, nbytes)
+    st = _capi.spec_verify_packed(
+        z.data_ptr(), code, rows, _ptr(row_offsets, i32, dev, "row_offsets"),
+        _ptr(draft_probs, f32, dev, "draft_probs"), _ptr(draft_tokens, i32, dev, "draft_tokens"),
+        _ptr(uniforms, f32, dev, "uniforms"), B, G, V, T,
+        _ptr(out_accepted, i32, dev, "out_accepted"), _ptr(out_tokens, i32, dev, "out_tokens"), d,
+        ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    if st != _capi.SPEC_OK:
+        raise SpecError(st, "spec_verify_packed")
+    if diag:
+        return out_accepted, out_tokens, dg
+    return out_accepted, out_tokens
+
+
+def dcut(confidence, ratios, ratio_cost, *, out_verify_len=None, out_row_offsets=None, out_ratio=None,
+         out_rows=None, out_utility=None, utility=True):
+    """Ratio-budgeted depth.  ratios, ratio_cost: host sequences of floats (the
+    profiled cost of each ratio at this batch size).  Returns device tensors
+    (verify_len [B], row_offsets [B+1], ratio_index [1], total_rows [1],
+    utility [R] float64 or None).
+    """
+    c = confidence
+    if not isinstance(c, torch.Tensor) or c.dim() != 2:
+        raise ValueError("confidence must be a [B, G] tensor")
+    dev = c.device
+    B, G = c.shape
+    ratios = [float(r) for r in ratios]
+    ratio_cost = [float(v) for v in ratio_cost]
+    if len(ratios) != len(ratio_cost):
+        raise ValueError("ratios and ratio_cost differ in length")
+    R = len(ratios)
+    i32 = torch.int32
+    if out_verify_len is None:
+        out_verify_len = torch.empty(B, dtype=i32, device=dev)
+    if out_row_offsets is None:
+        out_row_offsets = torch.empty(B + 1, dtype=i32, device=dev)
+    if out_ratio is None:
+        out_ratio = torch.empty(1, dtype=i32, device=dev)
+    if out_rows is None:
+        out_rows = torch.empty(1, dtype=i32, device=dev)
+    if out_utility is None and utility:
+        out_utility = torch.empty(max(R, 1), dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = _capi.spec_dcut(_ptr(c, torch.float32, dev, "confidence"), B, G, ratios, ratio_cost,
+                         _ptr(out_verify_len, i32, dev, "out_verify_len"),
+                         _ptr(out_row_offsets, i32, dev, "out_row_offsets"), _ptr(out_ratio, i32, dev, "out_ratio"),
+                         _ptr(out_rows, i32, dev, "out_rows"),
+                         _ptr(out_utility, torch.float64, dev, "out_utility") if out_utility is not None else 0,
+                         stream)
+    if st != _capi.SPEC_OK:
+        raise SpecError(st, "spec_dcut")
+    return out_verify_len, out_row_offsets, out_ratio, out_rows, out_utility

@@ -32,8 +32,11 @@ EXPORTS = (
     "spec_verify_launches",
     "spec_schedule_workspace_bytes",
     "spec_schedule",
+    "spec_verify_packed",
+    "spec_dcut",
     "spec_status_string",
 )
+MAX_RATIOS = 8
 
 
 class DiagT(ctypes.Structure):
@@ -77,6 +80,11 @@ def load():
     lib.spec_schedule_workspace_bytes.restype = sz
     lib.spec_schedule.argtypes = [vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
     lib.spec_schedule.restype = ctypes.c_int
+    lib.spec_verify_packed.argtypes = [vp, ctypes.c_int, i32, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp,
+                                       ctypes.POINTER(DiagT), vp, sz, vp]
+    lib.spec_verify_packed.restype = ctypes.c_int
+    lib.spec_dcut.argtypes = [vp, i32, i32, ctypes.POINTER(f32), ctypes.POINTER(f32), i32, vp, vp, vp, vp, vp, vp]
+    lib.spec_dcut.restype = ctypes.c_int
     lib.spec_status_string.argtypes = [ctypes.c_int]
     lib.spec_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -111,3 +119,23 @@ def spec_schedule(conf, cost, table_len, B, G, budget, eps, out_len, out_T, out_
     return int(load().spec_schedule(conf or None, cost or None, table_len, B, G, budget, ctypes.c_float(eps),
                                     out_len or None, out_T or None, out_tau or None, ws or None, ws_bytes,
                                     stream or None))
+
+
+def spec_verify_packed(logits, dtype_code, rows, roff, q, x, u, B, G, V, T, out_acc, out_tok, diag, ws, ws_bytes,
+                       stream):
+    """Raw call; pointers are ints (0 = NULL), `diag` a DiagT or None.  Returns the status."""
+    d = ctypes.byref(diag) if diag is not None else None
+    return int(load().spec_verify_packed(logits or None, dtype_code, rows, roff or None, q or None, x or None,
+                                         u or None, B, G, V, ctypes.c_float(T), out_acc or None, out_tok or None, d,
+                                         ws or None, ws_bytes, stream or None))
+
+
+def spec_dcut(conf, B, G, ratios, costs, out_len, out_off, out_ratio, out_rows, out_util, stream):
+    """Raw call; `ratios` and `costs` are host sequences of floats (None = NULL)."""
+    def arr(v):
+        if v is None:
+            return None
+        return (ctypes.c_float * max(1, len(v)))(*[float(t) for t in v])
+    n = len(ratios) if ratios is not None else (len(costs) if costs is not None else 0)
+    return int(load().spec_dcut(conf or None, B, G, arr(ratios), arr(costs), n, out_len or None, out_off or None,
+                                out_ratio or None, out_rows or None, out_util or None, stream or None))

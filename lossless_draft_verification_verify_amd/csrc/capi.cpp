@@ -12,6 +12,7 @@
 #include "sv_plan.h"
 
 static_assert(SPEC_MAX_BATCH == sv::kMaxBatch, "one batch limit for the header and the kernels");
+static_assert(SPEC_MAX_RATIOS == sv::kMaxRatios, "one ratio limit for the header and the kernels");
 
 namespace {
 
@@ -84,7 +85,7 @@ const char *spec_status_string(spec_status_t s) {
     switch (s) {
     case SPEC_OK: return "ok";
     case SPEC_ERR_NULL_POINTER: return "a required pointer is NULL";
-    case SPEC_ERR_BAD_SHAPE: return "shape, table, budget or eps out of range";
+    case SPEC_ERR_BAD_SHAPE: return "shape, table, budget, eps, ratio or cost out of range";
     case SPEC_ERR_BAD_TEMPERATURE: return "temperature must be 0 or a finite value >= 2^-126";
     case SPEC_ERR_BAD_DTYPE: return "unknown dtype";
     case SPEC_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the workspace-size query";
@@ -101,16 +102,28 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t G, int32_t V, spec_dtype_t
     return sv::make_layout(B, G, V, es).total;
 }
 
-spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, const float *draft_probs,
-                          const int32_t *draft_tokens, const float *uniforms, const int32_t *verify_len,
-                          int32_t B, int32_t G, int32_t V, float temperature, int32_t *out_accepted,
-                          int32_t *out_tokens, const spec_verify_diag_t *diag, void *workspace,
-                          size_t workspace_bytes, spec_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// spec_verify and spec_verify_packed: the target rows are [B, G+1, V]
+// (row_offsets NULL) or `rows` packed rows addressed through row_offsets.
+spec_status_t verify_impl(const void *target_logits, spec_dtype_t target_dtype, const int32_t *row_offsets,
+                          int32_t rows, const float *draft_probs, const int32_t *draft_tokens,
+                          const float *uniforms, const int32_t *verify_len, int32_t B, int32_t G, int32_t V,
+                          float temperature, int32_t *out_accepted, int32_t *out_tokens,
+                          const spec_verify_diag_t *diag, void *workspace, size_t workspace_bytes,
+                          spec_stream_t stream) {
     // ---- host-checkable errors, before anything touches the device
     const int es = esize_of(int(target_dtype));
     if (es == 0) return SPEC_ERR_BAD_DTYPE;
     const spec_status_t sh = check_verify_shape(B, G, V, es);
     if (sh != SPEC_OK) return sh;
+    if (row_offsets) {
+        if (rows < 1) return SPEC_ERR_BAD_SHAPE;
+        if (int64_t(rows) > (int64_t(1) << 40) / V) return SPEC_ERR_UNSUPPORTED;
+        if (!aligned(row_offsets, 4)) return SPEC_ERR_MISALIGNED;
+    }
     const float T = temperature;
     if (!std::isfinite(T) || T < 0.0f || (T > 0.0f && T < 1.17549435e-38f)) return SPEC_ERR_BAD_TEMPERATURE;
     const bool sampled = T > 0.0f;
@@ -140,6 +153,8 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
     a.x = draft_tokens;
     a.u = uniforms;
     a.vlen = verify_len;
+    a.roff = row_offsets;
+    a.rows = rows;
     a.out_acc = out_accepted;
     a.out_tok = out_tokens;
     a.d_lse = dg.target_lse;
@@ -178,7 +193,7 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
             a.spw = spw;
         }
         a.nc2 = (a.nsub + a.spw - 1) / a.spw;
-        if (verify_len && B <= sv::kWG) {
+        if ((verify_len || row_offsets) && B <= sv::kWG) {
             // Verify lengths leave rows unread: a grid of one resident load of
             // workgroups whose workgroups visit only the read row groups.
             const long cap = resident_capacity(dev, az, es);
@@ -214,6 +229,31 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
         return SPEC_ERR_DEVICE;
     a.mode = 2;
     return sv::launch_verify_greedy(a, az, es, B, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, const float *draft_probs,
+                          const int32_t *draft_tokens, const float *uniforms, const int32_t *verify_len,
+                          int32_t B, int32_t G, int32_t V, float temperature, int32_t *out_accepted,
+                          int32_t *out_tokens, const spec_verify_diag_t *diag, void *workspace,
+                          size_t workspace_bytes, spec_stream_t stream) {
+    return verify_impl(target_logits, target_dtype, nullptr, 0, draft_probs, draft_tokens, uniforms, verify_len,
+                       B, G, V, temperature, out_accepted, out_tokens, diag, workspace, workspace_bytes, stream);
+}
+
+spec_status_t spec_verify_packed(const void *target_logits, spec_dtype_t target_dtype, int32_t rows,
+                                 const int32_t *row_offsets, const float *draft_probs,
+                                 const int32_t *draft_tokens, const float *uniforms, int32_t B, int32_t G,
+                                 int32_t V, float temperature, int32_t *out_accepted, int32_t *out_tokens,
+                                 const spec_verify_diag_t *diag, void *workspace, size_t workspace_bytes,
+                                 spec_stream_t stream) {
+    if (!row_offsets) return SPEC_ERR_NULL_POINTER;
+    return verify_impl(target_logits, target_dtype, row_offsets, rows, draft_probs, draft_tokens, uniforms,
+                       nullptr, B, G, V, temperature, out_accepted, out_tokens, diag, workspace,
+                       workspace_bytes, stream);
 }
 
 int32_t spec_verify_launches(int32_t B, int32_t G, int32_t V, spec_dtype_t dt, float temperature) {
@@ -255,6 +295,42 @@ spec_status_t spec_schedule(const float *confidence, const float *cost_table, in
     a.out_T = out_total_tokens;
     a.out_tau = out_expected_tokens;
     return sv::launch_schedule(a, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+}
+
+spec_status_t spec_dcut(const float *confidence, int32_t B, int32_t G, const float *ratios,
+                        const float *ratio_cost, int32_t num_ratios, int32_t *out_verify_len,
+                        int32_t *out_row_offsets, int32_t *out_ratio_index, int32_t *out_total_rows,
+                        double *out_utility, spec_stream_t stream) {
+    if (B < 1 || G < 0) return SPEC_ERR_BAD_SHAPE;
+    if (int64_t(B) * G > SPEC_MAX_SCHEDULE_CANDIDATES || B > SPEC_MAX_SCHEDULE_CANDIDATES)
+        return SPEC_ERR_UNSUPPORTED;
+    if (num_ratios < 1 || num_ratios > SPEC_MAX_RATIOS) return SPEC_ERR_BAD_SHAPE;
+    if (!ratios || !ratio_cost) return SPEC_ERR_NULL_POINTER;
+    sv::DcutArgs a = {};
+    for (int r = 0; r < num_ratios; ++r) {
+        const float rho = ratios[r], c = ratio_cost[r];
+        if (!std::isfinite(rho) || !(rho > 0.0f) || rho > 1.0f) return SPEC_ERR_BAD_SHAPE;
+        if (!std::isfinite(c) || !(c > 0.0f)) return SPEC_ERR_BAD_SHAPE;
+        // K_rho = max(B, ceil(rho * B * (G + 1))); the product is exact in double.
+        const int64_t K = std::max<int64_t>(B, int64_t(std::ceil(double(rho) * double(int64_t(B) * (G + 1)))));
+        a.keep[r] = int32_t(K - B);
+        a.cost[r] = c;
+    }
+    if ((G > 0 && !confidence) || !out_verify_len || !out_row_offsets || !out_ratio_index || !out_total_rows)
+        return SPEC_ERR_NULL_POINTER;
+    if (!aligned(confidence, 4) || !aligned(out_verify_len, 4) || !aligned(out_row_offsets, 4) ||
+        !aligned(out_ratio_index, 4) || !aligned(out_total_rows, 4) || !aligned(out_utility, 8))
+        return SPEC_ERR_MISALIGNED;
+    a.conf = confidence;
+    a.B = B;
+    a.G = G;
+    a.R = num_ratios;
+    a.out_len = out_verify_len;
+    a.out_off = out_row_offsets;
+    a.out_ratio = out_ratio_index;
+    a.out_rows = out_total_rows;
+    a.out_utility = out_utility;
+    return sv::launch_dcut(a, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
 }
 
 }  // extern "C"

@@ -62,6 +62,8 @@ struct SchedSmem {
     float cost[kMaxCand + 1];  // cost[B + m] for m = 0..min(B*G, budget - B)
     int nvalid, mstar;
     double taustar;            // tau_{m*}
+    double red[kMaxThreads / 64][kMaxRatios];   // ratio budgets: per-wave progress sums
+    int wsum[kMaxThreads / 64];                 // per-wave totals of a block scan
 };
 
 // Order: larger survival first; equal survival -> smaller k, then smaller b
@@ -183,31 +185,18 @@ __device__ __forceinline__ void slot_key(const SchedSmem &sh, int i, int N, int 
     }
 }
 
-// One block of the grid; blockDim.x = max(64, Np) when Np <= kRegSort (the
-// register sort), else kMaxThreads.
-__global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
-    __shared__ SchedSmem sh;
-    const int tid = threadIdx.x, lane = tid & 63, nth = blockDim.x;
-    const int B = a.B, G = a.G, N = B * G;
-    const double eps = double(a.eps);
-    const int mt_max = min(N, a.budget - B);          // kept drafts never exceed this
-    int Np = 1;
-    while (Np < N) Np <<= 1;
-
-    // 1. every input the scan can read, in one round trip.
-    for (int i = tid; i < N; i += nth) sh.u.conf[i] = double(a.conf[i]);
-    for (int i = tid; i <= mt_max; i += nth) sh.cost[i] = a.cost[B + i];
-    __syncthreads();
-
-    // 2. survival s[b, k] = ((c[b,0] * c[b,1]) * ...) * c[b,k], the
-    //    sequential product, one thread per request (for G <= 16 its reads are
-    //    issued together: clamped in bounds, the ones past G unused).
+// 2. Survival s[b, k] = ((c[b,0] * c[b,1]) * ...) * c[b,k] (confidences in
+//    sh.u.conf), the sequential product, one thread per request (for G <= 16
+//    its reads are issued together: clamped in bounds, the ones past G
+//    unused).  Returns whether survival is non-increasing along every request.
+__device__ __forceinline__ bool survivals(SchedSmem &sh, int B, int G, int tid, int nth) {
+    const int N = B * G;
     bool mono = true;
     for (int b = tid; b < B; b += nth) {
         const double *c = sh.u.conf + b * G;
         double *sv = sh.key + b * G;
         double acc = 1.0;
-        if (G <= 16) {
+        if (G > 0 && G <= 16) {
             double cv[16];
 #pragma unroll
             for (int k = 0; k < 16; ++k) cv[k] = sh.u.conf[min(b * G + k, N - 1)];
@@ -230,9 +219,16 @@ __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
         }
         sh.len[b] = 0;
     }
-    const bool nonincr = __syncthreads_and(mono);
+    return __syncthreads_and(mono);
+}
 
-    // 3. sort the candidates (s desc, k asc, b asc); padding last.
+// 3. Sort the candidates (survival in sh.key above eps) in the order (s desc,
+//    k asc, b asc), padding last: sh.key / sh.id hold the sorted survivals and
+//    ids k * B + b.  Returns the number of candidates.
+__device__ __forceinline__ int sort_candidates(SchedSmem &sh, int B, int G, double eps, int tid, int lane, int nth) {
+    const int N = B * G;
+    int Np = 1;
+    while (Np < N) Np <<= 1;
     int ncand;
     if (Np <= kRegSort) {
         // One slot per thread, bitonic network in registers: partners in the
@@ -307,6 +303,26 @@ __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
         ncand = sh.nvalid;
         __syncthreads();
     }
+
+    return ncand;
+}
+
+// One block of the grid; blockDim.x = max(64, Np) when Np <= kRegSort (the
+// register sort), else kMaxThreads.
+__global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
+    __shared__ SchedSmem sh;
+    const int tid = threadIdx.x, lane = tid & 63, nth = blockDim.x;
+    const int B = a.B, G = a.G, N = B * G;
+    const double eps = double(a.eps);
+    const int mt_max = min(N, a.budget - B);          // kept drafts never exceed this
+
+    // 1. every input the scan can read, in one round trip.
+    for (int i = tid; i < N; i += nth) sh.u.conf[i] = double(a.conf[i]);
+    for (int i = tid; i <= mt_max; i += nth) sh.cost[i] = a.cost[B + i];
+    __syncthreads();
+
+    const bool nonincr = survivals(sh, B, G, tid, nth);
+    int ncand = sort_candidates(sh, B, G, eps, tid, lane, nth);
 
     // 4. contiguity: only when some survival increases along a request.
     if (!nonincr) {
@@ -411,6 +427,143 @@ __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
     }
 }
 
+// Sum over the wave (butterfly: every lane adds the same tree, so every lane
+// holds the same bits).
+__device__ __forceinline__ double wave_sum_fixed(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = v + __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Ratio-budgeted depth ("AngelSpec", section 4.2, Eq. 20-24): one block,
+// blockDim.x as for k_schedule.  Every draft is ranked once (the sort above,
+// with every draft a candidate); the budget of ratio r keeps the drafts of
+// sorted position < keep[r] = K_r - B, which is a contiguous prefix of every
+// request because survival never rises (confidences clamped into [0, 1]) and
+// equal survivals rank shallower first.  Then, per ratio, the estimated
+// progress U_r = sum_b (1 + kept survivals of b), the ratio with the largest
+// U_r / C_r (the first on ties), its keep depths and the packed row offsets.
+__global__ __launch_bounds__(kMaxThreads) void k_dcut(DcutArgs a) {
+    __shared__ SchedSmem sh;
+    const int tid = threadIdx.x, lane = tid & 63, nth = blockDim.x, wv = tid >> 6;
+    const int B = a.B, G = a.G, N = B * G;
+
+    for (int i = tid; i < N; i += nth) {
+        const double c = double(a.conf[i]);
+        sh.u.conf[i] = (c > 0.0) ? fmin(c, 1.0) : 0.0;   // NaN -> 0
+    }
+    __syncthreads();
+    survivals(sh, B, G, tid, nth);
+    sort_candidates(sh, B, G, -__builtin_inf(), tid, lane, nth);
+    for (int p = tid; p < N; p += nth) {                  // sorted position of each draft
+        const int id = sh.id[p];
+        const int k = id / B, b = id - k * B;
+        sh.u.pos[b * G + k] = p;
+    }
+    __syncthreads();
+
+    // Progress of request b at each ratio's depth, in position order:
+    // A_b = 1 + s_0 + ... + s_{n-1}; summed per thread, per wave, then over
+    // waves in order.
+    double U[kMaxRatios];
+#pragma unroll
+    for (int r = 0; r < kMaxRatios; ++r) U[r] = 0.0;
+    for (int b = tid; b < B; b += nth) {
+        double A = 1.0, Ab[kMaxRatios];
+#pragma unroll
+        for (int r = 0; r < kMaxRatios; ++r) Ab[r] = 1.0;
+        if (G > 0 && G <= 16) {
+            // positions, then survivals, each batch issued together
+            int pp[16];
+            double sv[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) pp[k] = sh.u.pos[min(b * G + k, N - 1)];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) sv[k] = sh.key[pp[k]];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                if (k < G) {
+                    A = A + sv[k];
+#pragma unroll
+                    for (int r = 0; r < kMaxRatios; ++r)
+                        if (pp[k] < a.keep[r]) Ab[r] = A;
+                }
+            }
+        } else {
+            for (int k = 0; k < G; ++k) {
+                const int p = sh.u.pos[b * G + k];
+                A = A + sh.key[p];
+#pragma unroll
+                for (int r = 0; r < kMaxRatios; ++r)
+                    if (p < a.keep[r]) Ab[r] = A;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kMaxRatios; ++r) U[r] = U[r] + Ab[r];
+    }
+#pragma unroll
+    for (int r = 0; r < kMaxRatios; ++r) {
+        const double w = wave_sum_fixed(U[r]);
+        if (lane == 0) sh.red[wv][r] = w;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const int nw = nth >> 6;
+        int best = 0;
+        double bv = 0.0;
+        for (int r = 0; r < a.R; ++r) {
+            double u = 0.0;
+            for (int v = 0; v < nw; ++v) u = u + sh.red[v][r];
+            const double th = u / double(a.cost[r]);
+            if (r == 0 || th > bv) {
+                bv = th;
+                best = r;
+            }
+            if (a.out_utility) a.out_utility[r] = u;
+        }
+        sh.nvalid = best;
+        sh.mstar = a.keep[best];
+        a.out_ratio[0] = best;
+        a.out_rows[0] = B + a.keep[best];
+    }
+    __syncthreads();
+
+    // Keep depths at the chosen ratio (a request's positions rise with k).
+    const int keep = sh.mstar;
+    for (int b = tid; b < B; b += nth) {
+        int n = 0;
+        for (int k = 0; k < G; ++k) n += int(sh.u.pos[b * G + k] < keep);
+        sh.len[b] = n;
+        a.out_len[b] = n;
+    }
+    __syncthreads();
+
+    // Packed row offsets: exclusive prefix of n_b + 1, each thread a
+    // contiguous run of requests.
+    const int per = (B + nth - 1) / nth;
+    const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
+    int local = 0;
+    for (int b = b0; b < b1; ++b) local += sh.len[b] + 1;
+    const int incl = wave_incl_scan(local, lane);
+    if (lane == 63) sh.wsum[wv] = incl;
+    __syncthreads();
+    int o = incl - local;
+    for (int v = 0; v < wv; ++v) o += sh.wsum[v];
+    for (int b = b0; b < b1; ++b) {
+        a.out_off[b] = o;
+        o += sh.len[b] + 1;
+    }
+    if (tid == 0) a.out_off[B] = B + keep;
+}
+
 }  // namespace
 
 int launch_schedule(const ScheduleArgs &a, void *stream) {
@@ -418,6 +571,14 @@ int launch_schedule(const ScheduleArgs &a, void *stream) {
     while (Np < a.B * a.G) Np <<= 1;
     const int threads = (Np <= kRegSort) ? (Np < 64 ? 64 : Np) : kMaxThreads;
     hipLaunchKernelGGL(k_schedule, dim3(1), dim3(threads), 0, static_cast<hipStream_t>(stream), a);
+    return int(hipGetLastError());
+}
+
+int launch_dcut(const DcutArgs &a, void *stream) {
+    int Np = 1;
+    while (Np < a.B * a.G) Np <<= 1;
+    const int threads = (Np <= kRegSort) ? (Np < 64 ? 64 : Np) : kMaxThreads;
+    hipLaunchKernelGGL(k_dcut, dim3(1), dim3(threads), 0, static_cast<hipStream_t>(stream), a);
     return int(hipGetLastError());
 }
 

@@ -67,6 +67,8 @@ struct VerifyArgs {
     const int32_t *x;
     const float *u;
     const int32_t *vlen;
+    const int32_t *roff;  // packed target rows: [B+1] row offsets (NULL: [B, G+1, V] rows)
+    int32_t rows;         // rows of a packed target buffer
     int32_t *out_acc;
     int32_t *out_tok;
     float *d_lse, *d_p, *d_q, *d_r;
@@ -101,5 +103,19 @@ struct ScheduleArgs {
     float *out_tau;
 };
 int launch_schedule(const ScheduleArgs &a, void *stream);
+
+constexpr int kMaxRatios = 8;
+struct DcutArgs {
+    const float *conf;
+    int32_t B, G, R;
+    float cost[kMaxRatios];   // profiled cost of each ratio at this batch size, in the caller's order
+    int32_t keep[kMaxRatios]; // drafts kept by each ratio: K_rho - B
+    int32_t *out_len;         // [B]
+    int32_t *out_off;         // [B+1]
+    int32_t *out_ratio;       // [1]
+    int32_t *out_rows;        // [1]
+    double *out_utility;      // [R] or NULL
+};
+int launch_dcut(const DcutArgs &a, void *stream);
 
 }  // namespace sv

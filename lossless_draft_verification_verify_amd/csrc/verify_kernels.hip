@@ -359,7 +359,21 @@ typedef const __attribute__((address_space(4))) int32_t ci32;
 __device__ __forceinline__ int32_t ld_const(const int32_t *p, size_t i) {
     return reinterpret_cast<ci32 *>(reinterpret_cast<uintptr_t>(p))[i];
 }
-__device__ __forceinline__ int verify_len(const VerifyArgs &a, int b) { return a.vlen ? ld_const(a.vlen, b) : a.G; }
+// Verify length of request b (-1 when its packed rows are invalid).  Packed
+// target rows: request b owns rows roff[b] .. roff[b+1]-1 of a buffer of
+// `rows` rows, its positions 0..n in order.
+__device__ __forceinline__ int verify_len(const VerifyArgs &a, int b) {
+    if (a.roff) {
+        const int lo = ld_const(a.roff, b), hi = ld_const(a.roff, size_t(b) + 1);
+        return (lo >= 0 && hi > lo && hi <= a.rows && hi - lo - 1 <= a.G) ? hi - lo - 1 : -1;
+    }
+    return a.vlen ? ld_const(a.vlen, b) : a.G;
+}
+// Element offset of target row k of request b ([B, G+1, V], or packed rows).
+__device__ __forceinline__ size_t row_elem(const VerifyArgs &a, int b, int k) {
+    const size_t r = a.roff ? size_t(ld_const(a.roff, b)) + size_t(k) : size_t(b) * size_t(a.G + 1) + size_t(k);
+    return r * size_t(a.V);
+}
 
 // ------------------------------------------------------------- row waves
 
@@ -422,8 +436,7 @@ template <int ES, bool AL>
 __device__ void row_chunk_sampled(const VerifyArgs &a, int b, int k, int chunk, int n, int lane, float &M_out,
                                   float &S_out) {
     constexpr int EPL = kEPL<ES>;
-    const int G1 = a.G + 1;
-    const void *row = static_cast<const char *>(a.logits) + (size_t(b) * G1 + k) * size_t(a.V) * ES;
+    const void *row = static_cast<const char *>(a.logits) + row_elem(a, b, k) * ES;
     const int beg = chunk * a.ch1;
     float f[EPL];
     load_chunk<ES, AL>(row, beg, a.V, lane, f);
@@ -483,7 +496,7 @@ template <int ES, bool AL>
 __device__ void row_chunk_greedy(const VerifyArgs &a, int b, int k, int chunk, int lane, float &M_out, int &idx_out,
                                  bool &nan_out) {
     constexpr int EPL = kEPL<ES>;
-    const void *row = static_cast<const char *>(a.logits) + (size_t(b) * (a.G + 1) + k) * size_t(a.V) * ES;
+    const void *row = static_cast<const char *>(a.logits) + row_elem(a, b, k) * ES;
     const int beg = chunk * a.ch1;
     float f[EPL];
     load_chunk<ES, AL>(row, beg, a.V, lane, f);
@@ -732,7 +745,7 @@ __device__ void write_diag(const VerifyArgs &a, int b, bool ok, int n, Smem &sh)
             lse = finitef(R) ? R * 0.6931471805599453f + logf(S) : m / a.T + logf(S);
             if (t < n) {
                 const int xt = a.x[size_t(b) * G + t];
-                const float zt = load_elem<ES>(a.logits, (size_t(b) * G1 + t) * size_t(a.V) + size_t(xt));
+                const float zt = load_elem<ES>(a.logits, row_elem(a, b, t) + size_t(xt));
                 qv = a.q[(size_t(b) * G + t) * size_t(a.V) + size_t(xt)];
                 const float e = finitef(R) ? exp2_fast(__builtin_fmaf(zt, a.c32, -R)) : exp2_fast((zt - m) * a.c32);
                 pv = e / S;
@@ -983,10 +996,9 @@ __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh
         if (w == 0 && (a.d_lse || a.d_p || a.d_q || a.d_r)) write_diag<ES>(a, b, false, d.n, sh);
         return;
     }
-    const int G1 = a.G + 1;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     uint64_t *mass = masses(a, b);
-    const void *zrow = static_cast<const char *>(a.logits) + (size_t(b) * G1 + d.j) * size_t(a.V) * ES;
+    const void *zrow = static_cast<const char *>(a.logits) + row_elem(a, b, d.j) * ES;
     const float *qrow = d.resid ? a.q + (size_t(b) * a.G + d.j) * size_t(a.V)
                                 : reinterpret_cast<const float *>(a.ws + a.lay.zero);
     if (!ok) {
@@ -1139,7 +1151,7 @@ __global__ __launch_bounds__(kWG) void k_rows_sampled_vl(VerifyArgs a) {
     const int t = int(threadIdx.x), lane = t & 63, w = wave_id();
     int cnt = 0;
     if (t < a.B) {
-        const int n = a.vlen[t];
+        const int n = verify_len(a, t);
         cnt = (n >= 0 && n <= a.G) ? (n + 1) * a.np1 : 0;
     }
     const int x = wave_scan_i(cnt);

@@ -117,3 +117,50 @@ def _sched(**kw):
 ])
 def test_schedule_rejects_bad_arguments(kw, status):
     assert _sched(**kw) == status
+
+
+def _packed(**kw):
+    args = dict(logits=Z, dtype_code=1, rows=40, roff=VL, q=Q, x=X, u=U, B=4, G=3, V=1000, T=1.0, out_acc=OA,
+                out_tok=OT, diag=None, ws=WS, ws_bytes=1 << 20, stream=0)
+    args.update(kw)
+    return _capi.spec_verify_packed(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(roff=0), 1), (dict(rows=0), 2), (dict(rows=-3), 2),
+    (dict(rows=1 << 30, V=1 << 20), 6),
+    (dict(roff=VL + 2), 8), (dict(logits=Z + 1), 8),
+    (dict(dtype_code=5), 4), (dict(B=0), 2), (dict(T=-1.0), 3), (dict(ws_bytes=100), 5),
+    (dict(q=0), 1), (dict(u=0), 1), (dict(x=0), 1),
+])
+def test_verify_packed_rejects_bad_arguments(kw, status):
+    assert _packed(**kw) == status
+
+
+def test_verify_packed_passes_validation_with_a_small_workspace_only():
+    # Valid packed arguments fail only on the workspace size, never as NULL.
+    assert _packed(T=0.0, q=0, u=0, ws_bytes=100) == 5
+    assert _packed(G=0, q=0, x=0, ws_bytes=100) == 5
+
+
+def _dcut(**kw):
+    args = dict(conf=Q, B=64, G=15, ratios=[0.25, 0.5, 0.75, 1.0], costs=[1.0, 1.1, 1.2, 1.3], out_len=OA,
+                out_off=OT, out_ratio=X, out_rows=U, out_util=WS, stream=0)
+    args.update(kw)
+    return _capi.spec_dcut(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 2), (dict(G=-1), 2),
+    (dict(B=300, G=15), 6), (dict(B=5000, G=0), 6),
+    (dict(ratios=[], costs=[]), 2), (dict(ratios=[0.5] * 9, costs=[1.0] * 9), 2),
+    (dict(ratios=[0.0, 0.5, 0.75, 1.0]), 2), (dict(ratios=[0.25, 0.5, 0.75, 1.5]), 2),
+    (dict(ratios=[0.25, float("nan"), 0.75, 1.0]), 2), (dict(ratios=[-0.25, 0.5, 0.75, 1.0]), 2),
+    (dict(costs=[1.0, 0.0, 1.0, 1.0]), 2), (dict(costs=[1.0, float("inf"), 1.0, 1.0]), 2),
+    (dict(costs=[1.0, -1.0, 1.0, 1.0]), 2),
+    (dict(ratios=None), 1), (dict(costs=None), 1),
+    (dict(conf=0), 1), (dict(out_len=0), 1), (dict(out_off=0), 1), (dict(out_ratio=0), 1), (dict(out_rows=0), 1),
+    (dict(conf=Q + 2), 8), (dict(out_off=OT + 1), 8), (dict(out_util=WS + 4), 8),
+])
+def test_dcut_rejects_bad_arguments(kw, status):
+    assert _dcut(**kw) == status

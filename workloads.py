@@ -25,6 +25,11 @@ the design doc lists them):
   scheduled  block logits at B in {4, 16, 64}; confidence c[b,k] =
              sigmoid(N(1.5, 1) - 0.08 k); cost[T] = 1 + 0.02 T for T = 0..512;
              token budget 512.
+  ratio_budgeted
+             block logits and the scheduled confidences at B in {4, 16, 64};
+             budget ratios (0.25, 0.5, 0.75, 1); the profiled cost of ratio rho
+             is the affine stand-in 1 + 0.02 * rho * B * (G + 1) (the scheduled
+             cost per target position, at the ratio's share of full depth).
 
 Draft probabilities q = softmax(draft_logits / T) (float32) and
 the draft tokens are sampled from q, as a sampling drafter does.  Uniforms are
@@ -187,4 +192,21 @@ def scheduled(B, seed=BASE_SEED + 5, G=15, V=129280, T=1.0, budget=512):
     w["confidence"] = confidences(seed, B, G)
     w["cost_table"] = linear_cost(table_len=budget + 1)
     w["budget"] = budget
+    return w
+
+
+RATIOS = (0.25, 0.5, 0.75, 1.0)
+
+
+def ratio_costs(B, G, ratios=RATIOS, a=1.0, b=0.02):
+    """Stand-in profiled step cost of each budget ratio at batch size B (float32)."""
+    return [float(v) for v in (a + b * np.asarray(ratios, np.float64) * B * (G + 1)).astype(np.float32)]
+
+
+def ratio_budgeted(B, seed=BASE_SEED + 6, G=15, V=129280, T=1.0):
+    w = block(seed=seed, B=B, G=G, V=V, T=T)
+    w["name"] = "ratio_budgeted"
+    w["confidence"] = confidences(seed, B, G)
+    w["ratios"] = RATIOS
+    w["ratio_cost"] = ratio_costs(B, G)
     return w
