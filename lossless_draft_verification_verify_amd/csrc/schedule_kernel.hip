@@ -38,6 +38,7 @@
 #include <stdint.h>
 
 #include "sv_plan.h"
+#include "sv_wave.h"
 
 namespace sv {
 namespace {
@@ -78,14 +79,11 @@ __device__ __forceinline__ bool before_nb(double s1, int id1, double s2, int id2
 
 // Value of lane (lane ^ S) of the wave, S < 64.  (Every DPP pattern used
 // reads an active lane inside its row, so no lane needs an old value.)
-template <int CTRL> __device__ __forceinline__ int dpp(int x) {
-    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
-}
 template <int S> __device__ __forceinline__ int xor_lane(int x, int lane) {
-    if constexpr (S == 1) return dpp<0xB1>(x);                 // quad_perm [1, 0, 3, 2]
-    else if constexpr (S == 2) return dpp<0x4E>(x);            // quad_perm [2, 3, 0, 1]
-    else if constexpr (S == 4) return dpp<0x1B>(dpp<0x141>(x));   // row_half_mirror (^7), then quad_perm [3, 2, 1, 0] (^3)
-    else if constexpr (S == 8) return dpp<0x128>(x);           // row_ror:8
+    if constexpr (S == 1) return dpp_i<0xB1>(x);               // quad_perm [1, 0, 3, 2]
+    else if constexpr (S == 2) return dpp_i<0x4E>(x);          // quad_perm [2, 3, 0, 1]
+    else if constexpr (S == 4) return dpp_i<0x1B>(dpp_i<0x141>(x));   // row_half_mirror (^7), then quad_perm [3, 2, 1, 0] (^3)
+    else if constexpr (S == 8) return dpp_i<0x128>(x);         // row_ror:8
     else if constexpr (S == 16) {
         // Row swap: result 0 holds the even row's lanes, result 1 the odd row's.
         const auto r = __builtin_amdgcn_permlane16_swap(unsigned(x), unsigned(x), false, false);
@@ -164,13 +162,6 @@ __device__ __forceinline__ void cx_in_wave(double &s, int &id, int tid, int lane
     if (top >= 4) cx_wave<4>(s, id, tid, lane, size);
     if (top >= 2) cx_wave<2>(s, id, tid, lane, size);
     cx_wave<1>(s, id, tid, lane, size);
-}
-
-__device__ __forceinline__ double lane_d(double x, int l) {
-    const uint64_t v = uint64_t(__double_as_longlong(x));
-    const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), l));
-    const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), l));
-    return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
 }
 
 // Sorting slot i of Np: its survival when it is a candidate, else -inf padding.
@@ -427,22 +418,6 @@ __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
     }
 }
 
-// Sum over the wave (butterfly: every lane adds the same tree, so every lane
-// holds the same bits).
-__device__ __forceinline__ double wave_sum_fixed(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = v + __shfl_xor(v, o);
-    return v;
-}
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(v, o);
-        if (lane >= o) v += t;
-    }
-    return v;
-}
-
 // Ratio-budgeted depth ("AngelSpec", section 4.2, Eq. 20-24): one block,
 // blockDim.x as for k_schedule.  Every draft is ranked once (the sort above,
 // with every draft a candidate); the budget of ratio r keeps the drafts of
@@ -471,15 +446,24 @@ __global__ __launch_bounds__(kMaxThreads) void k_dcut(DcutArgs a) {
     __syncthreads();
 
     // Progress of request b at each ratio's depth, in position order:
-    // A_b = 1 + s_0 + ... + s_{n-1}; summed per thread, per wave, then over
-    // waves in order.
+    // A_b = 1 + s_0 + ... + s_{n-1}, and the depth n itself; summed per
+    // thread, then per wave (DPP), then over the waves that hold requests,
+    // in order.
+    const int R = a.R;
     double U[kMaxRatios];
+    int nr[kMaxRatios];                                // depths of this thread's (last) request
 #pragma unroll
-    for (int r = 0; r < kMaxRatios; ++r) U[r] = 0.0;
+    for (int r = 0; r < kMaxRatios; ++r) {
+        U[r] = 0.0;
+        nr[r] = 0;
+    }
     for (int b = tid; b < B; b += nth) {
         double A = 1.0, Ab[kMaxRatios];
 #pragma unroll
-        for (int r = 0; r < kMaxRatios; ++r) Ab[r] = 1.0;
+        for (int r = 0; r < kMaxRatios; ++r) {
+            Ab[r] = 1.0;
+            nr[r] = 0;
+        }
         if (G > 0 && G <= 16) {
             // positions, then survivals, each batch issued together
             int pp[16];
@@ -494,7 +478,10 @@ __global__ __launch_bounds__(kMaxThreads) void k_dcut(DcutArgs a) {
                     A = A + sv[k];
 #pragma unroll
                     for (int r = 0; r < kMaxRatios; ++r)
-                        if (pp[k] < a.keep[r]) Ab[r] = A;
+                        if (pp[k] < a.keep[r]) {
+                            Ab[r] = A;
+                            nr[r] = k + 1;
+                        }
                 }
             }
         } else {
@@ -503,23 +490,30 @@ __global__ __launch_bounds__(kMaxThreads) void k_dcut(DcutArgs a) {
                 A = A + sh.key[p];
 #pragma unroll
                 for (int r = 0; r < kMaxRatios; ++r)
-                    if (p < a.keep[r]) Ab[r] = A;
+                    if (p < a.keep[r]) {
+                        Ab[r] = A;
+                        nr[r] = k + 1;
+                    }
             }
         }
 #pragma unroll
         for (int r = 0; r < kMaxRatios; ++r) U[r] = U[r] + Ab[r];
     }
+    const int nw = (min(B, nth) + 63) >> 6;            // waves holding requests
+    if (wv < nw) {
 #pragma unroll
-    for (int r = 0; r < kMaxRatios; ++r) {
-        const double w = wave_sum_fixed(U[r]);
-        if (lane == 0) sh.red[wv][r] = w;
+        for (int r = 0; r < kMaxRatios; ++r) {
+            if (r < R) {
+                const double w = wave_sum_d(U[r]);
+                if (lane == 0) sh.red[wv][r] = w;
+            }
+        }
     }
     __syncthreads();
     if (tid == 0) {
-        const int nw = nth >> 6;
         int best = 0;
         double bv = 0.0;
-        for (int r = 0; r < a.R; ++r) {
+        for (int r = 0; r < R; ++r) {
             double u = 0.0;
             for (int v = 0; v < nw; ++v) u = u + sh.red[v][r];
             const double th = u / double(a.cost[r]);
@@ -535,31 +529,46 @@ __global__ __launch_bounds__(kMaxThreads) void k_dcut(DcutArgs a) {
         a.out_rows[0] = B + a.keep[best];
     }
     __syncthreads();
+    const int best = sh.nvalid, keep = sh.mstar;
 
-    // Keep depths at the chosen ratio (a request's positions rise with k).
-    const int keep = sh.mstar;
-    for (int b = tid; b < B; b += nth) {
+    // Keep depths at the chosen ratio and the packed row offsets (exclusive
+    // prefix of n_b + 1).
+    if (B <= nth) {
+        // One request per thread: the depth is in registers, and the prefix
+        // is a DPP wave scan plus the totals of the waves before.
         int n = 0;
-        for (int k = 0; k < G; ++k) n += int(sh.u.pos[b * G + k] < keep);
-        sh.len[b] = n;
-        a.out_len[b] = n;
-    }
-    __syncthreads();
-
-    // Packed row offsets: exclusive prefix of n_b + 1, each thread a
-    // contiguous run of requests.
-    const int per = (B + nth - 1) / nth;
-    const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
-    int local = 0;
-    for (int b = b0; b < b1; ++b) local += sh.len[b] + 1;
-    const int incl = wave_incl_scan(local, lane);
-    if (lane == 63) sh.wsum[wv] = incl;
-    __syncthreads();
-    int o = incl - local;
-    for (int v = 0; v < wv; ++v) o += sh.wsum[v];
-    for (int b = b0; b < b1; ++b) {
-        a.out_off[b] = o;
-        o += sh.len[b] + 1;
+#pragma unroll
+        for (int r = 0; r < kMaxRatios; ++r) n = (r == best) ? nr[r] : n;
+        const int cnt = (tid < B) ? n + 1 : 0;
+        const int incl = wave_scan_i(cnt);
+        if (lane == 63) sh.wsum[wv] = incl;
+        if (tid < B) a.out_len[tid] = n;
+        __syncthreads();
+        int o = incl - cnt;
+        for (int v = 0; v < wv; ++v) o += sh.wsum[v];
+        if (tid < B) a.out_off[tid] = o;
+    } else {
+        for (int b = tid; b < B; b += nth) {
+            int n = 0;
+            for (int k = 0; k < G; ++k) n += int(sh.u.pos[b * G + k] < keep);
+            sh.len[b] = n;
+            a.out_len[b] = n;
+        }
+        __syncthreads();
+        // each thread a contiguous run of requests
+        const int per = (B + nth - 1) / nth;
+        const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
+        int local = 0;
+        for (int b = b0; b < b1; ++b) local += sh.len[b] + 1;
+        const int incl = wave_scan_i(local);
+        if (lane == 63) sh.wsum[wv] = incl;
+        __syncthreads();
+        int o = incl - local;
+        for (int v = 0; v < wv; ++v) o += sh.wsum[v];
+        for (int b = b0; b < b1; ++b) {
+            a.out_off[b] = o;
+            o += sh.len[b] + 1;
+        }
     }
     if (tid == 0) a.out_off[B] = B + keep;
 }
