@@ -13,12 +13,14 @@ verify    speculative-sampling verification (temperature softmax, accept test,
           (temperature 0) limit.
 schedule  confidence-scheduled verification depth (CumProd survival, greedy
           throughput-improving prefix extension under a token budget).
+acceptance  per-position acceptance overlap alpha = sum min(p, q) = 1 - TV,
+          and verification with the draft distribution given as logits.
 dcut      ratio-budgeted depth (top-K scores for each ratio budget, the ratio
           that maximises estimated progress over profiled cost) and
           verification over densely packed target rows.
 
 Every function is pinned by a ``-m "not gpu"`` test (tests/test_oracle_pins.py,
-tests/test_oracle_dcut.py) against what the pages and the mathematics fix;
+tests/test_oracle_dcut.py, tests/test_oracle_acceptance.py) against what the pages and the mathematics fix;
 none is "parity unpinned".
 """
 
@@ -34,3 +36,4 @@ from .verify import (  # noqa: F401
 )
 from .schedule import survival, schedule, schedule_value, brute_force  # noqa: F401
 from . import dcut  # noqa: F401  (module: oracle.dcut.dcut, oracle.dcut.verify_packed, ...)
+from . import acceptance  # noqa: F401,E402
