@@ -24,15 +24,17 @@ Readings (also in DESIGN.md):
   verified at); with draft probabilities given instead, q is used as given.
 * A verified draft row (k < n_b) that holds a NaN, whose maximum is +inf, or
   which is entirely -inf is a data error of its request, like a target row.
-* The diagnostics cover the tested positions k < n_b; other entries, and every
-  entry of a request with a data error, are NaN.  TV and c* are 1 - alpha and
-  alpha; only alpha is returned.
+* The diagnostics cover the tested positions k < n_b.  alpha_k depends only on
+  target row k and draft row k, so it is NaN when either of those rows is bad
+  (NaN, maximum +inf, or all -inf), for k >= n_b, and for every position of a
+  request whose verify length is outside [0, G].  TV and c* are 1 - alpha and
+  alpha; only alpha is returned.  Draft ids play no part.
 * Diagnostics are defined for T > 0 (at T = 0 p and q are one-hot).
 """
 
 import numpy as np
 
-from .verify import _as_f64, _prepare, row_is_bad, target_probs, verify, verify_greedy
+from .verify import _as_f64, row_is_bad, target_probs, verify, verify_greedy
 
 
 def draft_probs_from_logits(draft_logits, temperature):
@@ -64,23 +66,24 @@ def acceptance(target_logits, draft, temperature, verify_len=None, draft_is_logi
     target_logits [B, G+1, V] (float or uint16 bfloat16 bits); draft [B, G, V]:
     draft probabilities, or draft logits when draft_is_logits (softmax at T).
     """
-    # verify's row checks; token ids are not part of this computation (all 0)
-    zero_ids = np.zeros(np.shape(target_logits)[:2], np.int64)[:, 1:]
-    z, _, n, pos_used, bad = _prepare(target_logits, zero_ids, verify_len)
+    z = _as_f64(target_logits)
     B, G1, V = z.shape
     G = G1 - 1
     T = float(temperature)
     if not T > 0.0:
         raise ValueError("acceptance diagnostics need T > 0")
+    n = np.full(B, G, np.int64) if verify_len is None else np.asarray(verify_len, np.int64).reshape(B)
+    tested = (np.arange(G)[None, :] < n[:, None]) & ((n >= 0) & (n <= G))[:, None]
+    bad_pos = row_is_bad(z[:, :G])
     if draft_is_logits:
         d = _as_f64(draft).reshape(B, G, V)
-        bad = bad | _draft_rows_bad(d, n)
-    p, _ = target_probs(z, T)
-    q = draft_probs_from_logits(d, T) if draft_is_logits else np.asarray(draft, np.float64).reshape(B, G, V)
-    alpha = overlap(p[:, :G], q)
-    alpha = np.where(pos_used, alpha, np.nan)
-    alpha[bad] = np.nan
-    return alpha
+        bad_pos = bad_pos | row_is_bad(d)
+        q = draft_probs_from_logits(d, T)
+    else:
+        q = np.asarray(draft, np.float64).reshape(B, G, V)
+    p, _ = target_probs(z[:, :G], T)
+    alpha = overlap(p, q)
+    return np.where(tested & ~bad_pos, alpha, np.nan)
 
 
 def verify_logits(target_logits, draft_logits, draft_tokens, uniforms, temperature, verify_len=None):

@@ -83,16 +83,19 @@ def test_acceptance_masks_untested_positions_and_bad_requests():
     z = g.normal(size=(B, G + 1, V))
     q = softmax(g.normal(size=(B, G, V)), axis=-1)
     n = np.array([3, 1, 0, 2])
-    z[3, 1, 5] = np.nan                                # request 3 reads row 1: a data error
+    z[3, 1, 5] = np.nan                                # request 3, row 1: only alpha[3, 1] is lost
+    z[1, 2, :] = -np.inf                               # request 1 tests row 0 only: no effect
     alpha = A.acceptance(z, q, 1.0, verify_len=n)
     p = softmax(z, axis=-1)
-    for b in range(3):
+    for b in range(B):
         for k in range(G):
-            if k < n[b]:
+            if k < n[b] and not (b == 3 and k == 1):
                 assert abs(alpha[b, k] - np.minimum(p[b, k], q[b, k]).sum()) < 1e-12
             else:
                 assert np.isnan(alpha[b, k])
-    assert np.isnan(alpha[3]).all()
+    # an invalid verify length: the whole request
+    alpha = A.acceptance(z, q, 1.0, verify_len=np.array([4, 1, -1, 2]))
+    assert np.isnan(alpha[0]).all() and np.isnan(alpha[2]).all() and not np.isnan(alpha[1, 0])
     with pytest.raises(ValueError):
         A.acceptance(z, q, 0.0)
 
@@ -129,7 +132,10 @@ def test_bad_draft_rows_are_data_errors():
     out = A.verify_logits(z, d, x, u, 1.0, verify_len=n)
     assert out["accepted"][0] == -1 and out["accepted"][2] == -1 and out["accepted"][1] >= 0
     alpha = A.acceptance(z, d, 1.0, n, draft_is_logits=True)
-    assert np.isnan(alpha[0]).all() and np.isnan(alpha[2]).all() and not np.isnan(alpha[1, :2]).any()
+    # per position: the bad draft rows' positions only
+    assert np.isnan(alpha[0, 1]) and np.isnan(alpha[2, 0])
+    assert not np.isnan(alpha[0, [0, 2]]).any() and not np.isnan(alpha[2, 1:]).any()
+    assert not np.isnan(alpha[1, :2]).any() and np.isnan(alpha[1, 2])
     # greedy ignores the draft logits
     g0 = A.verify_logits(z, d, x, u, 0.0, verify_len=n)
     ref = oracle.verify_greedy(z, x, n)
