@@ -14,6 +14,8 @@
  *   spec_dcut           ratio-budgeted verification depth: the budget ratio
  *                       with the best estimated progress per profiled cost,
  *                       its keep depths and the packed row offsets.
+ *   spec_acceptance     per-position acceptance overlap alpha = sum min(p, q)
+ *                       (= 1 - TV), the expected acceptance of each draft.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -57,6 +59,11 @@ typedef enum {
 } spec_status_t;
 
 typedef enum { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 } spec_dtype_t;
+
+/* How the draft distribution is given: float32 probabilities, or logits of
+ * the target's dtype whose softmax at the call's temperature is the draft
+ * distribution. */
+typedef enum { SPEC_DRAFT_PROBS = 0, SPEC_DRAFT_LOGITS = 1 } spec_draft_kind_t;
 
 /* A hipStream_t, passed opaquely so that this header needs no HIP include. */
 typedef void *spec_stream_t;
@@ -274,6 +281,31 @@ spec_status_t spec_dcut(const float *confidence, int32_t B, int32_t G,
                         int32_t *out_verify_len, int32_t *out_row_offsets,
                         int32_t *out_ratio_index, int32_t *out_total_rows,
                         double *out_utility, spec_stream_t stream);
+
+/*
+ * spec_acceptance -- per-position acceptance diagnostics.
+ *
+ * Operation ("AngelSpec", section 2, Eq. 2, 4 and 5; "UraionSpec", the
+ * confidence head's training target): for every tested position k < len_b,
+ *   alpha[b,k] = sum_v min(p_k(v), q_k(v)),  p_k = softmax(z[b,k,:] / T),
+ * where q_k is draft[b,k,:] as given (SPEC_DRAFT_PROBS) or
+ * softmax(draft[b,k,:] / T) (SPEC_DRAFT_LOGITS).  alpha is the expected
+ * probability that draft k is accepted; TV(p_k, q_k) = 1 - alpha and the
+ * confidence target c*_k = alpha.
+ * NaN where k >= len_b, for every position of a request whose verify length is
+ * outside [0, G], and where target row k or draft row k (logits) holds a NaN,
+ * has maximum +inf or is entirely -inf.  Sums are fp32 per eight elements and
+ * fp64 beyond (about 1e-6 absolute).
+ *
+ * Arguments (device pointers): target_logits [B, G+1, V] of target_dtype (rows
+ * k < len_b are read); draft [B, G, V]: float32 probabilities, or logits of
+ * target_dtype; verify_len [B] or NULL (= G); T finite, >= 2^-126;
+ * out_alpha [B, G] float.  Shape limits as spec_verify.  Needs no workspace.
+ */
+spec_status_t spec_acceptance(const void *target_logits, spec_dtype_t target_dtype,
+                              const void *draft, spec_draft_kind_t draft_kind,
+                              const int32_t *verify_len, int32_t B, int32_t G, int32_t V,
+                              float temperature, float *out_alpha, spec_stream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *spec_status_string(spec_status_t status);

@@ -17,7 +17,7 @@ import torch
 from . import _capi
 from ._capi import SpecError, SPEC_DTYPE_BF16, SPEC_DTYPE_F32  # noqa: F401
 
-__all__ = ["verify", "verify_packed", "schedule", "dcut", "verify_workspace_bytes", "SpecError", "load"]
+__all__ = ["verify", "verify_packed", "schedule", "dcut", "acceptance", "verify_workspace_bytes", "SpecError", "load"]
 
 _workspaces = {}
 
@@ -256,3 +256,31 @@ def dcut(confidence, ratios, ratio_cost, *, out_verify_len=None, out_row_offsets
     if st != _capi.SPEC_OK:
         raise SpecError(st, "spec_dcut")
     return out_verify_len, out_row_offsets, out_ratio, out_rows, out_utility
+
+
+def acceptance(target_logits, draft, temperature, verify_len=None, *, draft_is_logits=False, out_alpha=None):
+    """Per-position acceptance overlap alpha[b, k] = sum_v min(p_k, q_k) (NaN where untested).
+
+    target_logits [B, G+1, V] bf16/fp32; draft [B, G, V]: fp32 probabilities, or
+    logits of the target's dtype when draft_is_logits (softmax at temperature).
+    """
+    z = target_logits
+    if not isinstance(z, torch.Tensor) or z.dim() != 3:
+        raise ValueError("target_logits must be a [B, G+1, V] tensor")
+    dev = z.device
+    B, G1, V = z.shape
+    G = G1 - 1
+    code = _dtype_code(z)
+    ddt = z.dtype if draft_is_logits else torch.float32
+    if tuple(draft.shape) != (B, G, V):
+        raise ValueError(f"draft has shape {tuple(draft.shape)}, expected {(B, G, V)}")
+    if out_alpha is None:
+        out_alpha = torch.empty(B, G, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = _capi.spec_acceptance(z.data_ptr(), code, _ptr(draft, ddt, dev, "draft"),
+                               _capi.SPEC_DRAFT_LOGITS if draft_is_logits else _capi.SPEC_DRAFT_PROBS,
+                               _ptr(verify_len, torch.int32, dev, "verify_len"), B, G, V, float(temperature),
+                               _ptr(out_alpha, torch.float32, dev, "out_alpha"), stream)
+    if st != _capi.SPEC_OK:
+        raise SpecError(st, "spec_acceptance")
+    return out_alpha

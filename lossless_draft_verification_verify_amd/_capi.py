@@ -24,6 +24,8 @@ STATUS_NAMES = {
 }
 SPEC_DTYPE_F32 = 0
 SPEC_DTYPE_BF16 = 1
+SPEC_DRAFT_PROBS = 0
+SPEC_DRAFT_LOGITS = 1
 
 # Every symbol the header declares.
 EXPORTS = (
@@ -34,6 +36,7 @@ EXPORTS = (
     "spec_schedule",
     "spec_verify_packed",
     "spec_dcut",
+    "spec_acceptance",
     "spec_status_string",
 )
 MAX_RATIOS = 8
@@ -85,6 +88,8 @@ def load():
     lib.spec_verify_packed.restype = ctypes.c_int
     lib.spec_dcut.argtypes = [vp, i32, i32, ctypes.POINTER(f32), ctypes.POINTER(f32), i32, vp, vp, vp, vp, vp, vp]
     lib.spec_dcut.restype = ctypes.c_int
+    lib.spec_acceptance.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, i32, i32, i32, f32, vp, vp]
+    lib.spec_acceptance.restype = ctypes.c_int
     lib.spec_status_string.argtypes = [ctypes.c_int]
     lib.spec_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -139,3 +144,8 @@ def spec_dcut(conf, B, G, ratios, costs, out_len, out_off, out_ratio, out_rows, 
     n = len(ratios) if ratios is not None else (len(costs) if costs is not None else 0)
     return int(load().spec_dcut(conf or None, B, G, arr(ratios), arr(costs), n, out_len or None, out_off or None,
                                 out_ratio or None, out_rows or None, out_util or None, stream or None))
+
+
+def spec_acceptance(logits, dtype_code, draft, draft_kind, vlen, B, G, V, T, out_alpha, stream):
+    return int(load().spec_acceptance(logits or None, dtype_code, draft or None, draft_kind, vlen or None, B, G, V,
+                                      ctypes.c_float(T), out_alpha or None, stream or None))

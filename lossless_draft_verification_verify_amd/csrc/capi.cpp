@@ -297,6 +297,37 @@ spec_status_t spec_schedule(const float *confidence, const float *cost_table, in
     return sv::launch_schedule(a, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
 }
 
+spec_status_t spec_acceptance(const void *target_logits, spec_dtype_t target_dtype, const void *draft,
+                              spec_draft_kind_t draft_kind, const int32_t *verify_len, int32_t B, int32_t G,
+                              int32_t V, float temperature, float *out_alpha, spec_stream_t stream) {
+    const int es = esize_of(int(target_dtype));
+    if (es == 0) return SPEC_ERR_BAD_DTYPE;
+    if (draft_kind != SPEC_DRAFT_PROBS && draft_kind != SPEC_DRAFT_LOGITS) return SPEC_ERR_BAD_DTYPE;
+    const spec_status_t sh = check_verify_shape(B, G, V, es);
+    if (sh != SPEC_OK) return sh;
+    if (int64_t(B) * G >= (int64_t(1) << 31)) return SPEC_ERR_UNSUPPORTED;
+    const float T = temperature;
+    if (!std::isfinite(T) || !(T >= 1.17549435e-38f)) return SPEC_ERR_BAD_TEMPERATURE;
+    if (!target_logits || (G > 0 && (!draft || !out_alpha))) return SPEC_ERR_NULL_POINTER;
+    const int ds = draft_kind == SPEC_DRAFT_LOGITS ? es : 4;
+    if (!aligned(target_logits, es) || !aligned(draft, ds) || !aligned(verify_len, 4) || !aligned(out_alpha, 4))
+        return SPEC_ERR_MISALIGNED;
+    if (G == 0) return SPEC_OK;
+    sv::AcceptArgs a = {};
+    a.z = target_logits;
+    a.d = draft;
+    a.vlen = verify_len;
+    a.out = out_alpha;
+    a.B = B;
+    a.G = G;
+    a.V = V;
+    a.c32 = float(1.4426950408889634 / double(T));
+    const bool al = aligned(target_logits, 16) && aligned(draft, 16) && (size_t(V) * es) % 16 == 0 &&
+                    (size_t(V) * ds) % 16 == 0;
+    return sv::launch_acceptance(a, al, es, draft_kind == SPEC_DRAFT_LOGITS, stream) == 0 ? SPEC_OK
+                                                                                        : SPEC_ERR_DEVICE;
+}
+
 spec_status_t spec_dcut(const float *confidence, int32_t B, int32_t G, const float *ratios,
                         const float *ratio_cost, int32_t num_ratios, int32_t *out_verify_len,
                         int32_t *out_row_offsets, int32_t *out_ratio_index, int32_t *out_total_rows,

@@ -118,4 +118,14 @@ struct DcutArgs {
 };
 int launch_dcut(const DcutArgs &a, void *stream);
 
+struct AcceptArgs {
+    const void *z;            // [B, G+1, V] target logits
+    const void *d;            // [B, G, V] draft probabilities (fp32) or draft logits (target dtype)
+    const int32_t *vlen;      // [B] or NULL
+    float *out;               // [B, G] alpha
+    int32_t B, G, V;
+    float c32;                // log2(e) / T
+};
+int launch_acceptance(const AcceptArgs &a, bool aligned, int esize, bool draft_logits, void *stream);
+
 }  // namespace sv

@@ -164,3 +164,27 @@ def _dcut(**kw):
 ])
 def test_dcut_rejects_bad_arguments(kw, status):
     assert _dcut(**kw) == status
+
+
+def _acc(**kw):
+    args = dict(logits=Z, dtype_code=1, draft=Q, draft_kind=1, vlen=0, B=4, G=3, V=1000, T=1.0, out_alpha=OA,
+                stream=0)
+    args.update(kw)
+    return _capi.spec_acceptance(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype_code=5), 4), (dict(draft_kind=2), 4),
+    (dict(B=0), 2), (dict(G=-1), 2), (dict(V=0), 2), (dict(G=256), 6),
+    (dict(T=0.0), 3), (dict(T=-1.0), 3), (dict(T=float("nan")), 3), (dict(T=float("inf")), 3),
+    (dict(logits=0), 1), (dict(draft=0), 1), (dict(out_alpha=0), 1),
+    (dict(logits=Z + 1), 8), (dict(draft=Q + 1), 8), (dict(draft=Q + 2, draft_kind=0), 8),
+    (dict(vlen=VL + 2), 8), (dict(out_alpha=OA + 2), 8),
+])
+def test_acceptance_rejects_bad_arguments(kw, status):
+    assert _acc(**kw) == status
+
+
+def test_acceptance_without_drafts_enqueues_nothing():
+    # G == 0: nothing to compute, valid without draft or output pointers.
+    assert _acc(G=0, draft=0, out_alpha=0) == 0

@@ -25,6 +25,11 @@ the design doc lists them):
   scheduled  block logits at B in {4, 16, 64}; confidence c[b,k] =
              sigmoid(N(1.5, 1) - 0.08 k); cost[T] = 1 + 0.02 T for T = 0..512;
              token budget 512.
+  block_logits
+             block target logits; the drafter emits bf16 draft logits
+             d = bf16(z + N(0, 0.75 * 1.05**k)) and samples x ~ softmax(d / T)
+             (float64 from the stored bf16 values), so the draft distribution
+             is exactly the softmax of the logits passed on.
   ratio_budgeted
              block logits and the scheduled confidences at B in {4, 16, 64};
              budget ratios (0.25, 0.5, 0.75, 1); the profiled cost of ratio rho
@@ -102,6 +107,25 @@ def _drafter(target_f32, G, T, noise_std, seed):
     return q, x
 
 
+def _logit_drafter(target_f32, G, T, noise_std, seed):
+    """Logits drafter: d = bf16(target + noise) per position, x ~ softmax(d / T)."""
+    B, G1, V = target_f32.shape
+    g_noise = rng(seed, "draft_noise")
+    g_samp = rng(seed, "draft_sample")
+    bits = np.empty((B, G, V), dtype=np.uint16)
+    x = np.empty((B, G), dtype=np.int32)
+    for k in range(G):
+        sd = noise_std(k)
+        d = target_f32[:, k, :] + np.float32(sd) * g_noise.standard_normal((B, V), dtype=np.float32)
+        bits[:, k, :] = f32_to_bf16_bits(d)
+        dd = bf16_bits_to_f32(bits[:, k, :]).astype(np.float64) / float(T)
+        dd -= dd.max(axis=1, keepdims=True)
+        e = np.exp(dd)
+        for b in range(B):
+            x[b, k] = g_samp.choice(V, p=e[b] / e[b].sum())
+    return bits, x
+
+
 def _uniforms(B, G, seed):
     return rng(seed, "verify_u").random((B, G + 1), dtype=np.float32)
 
@@ -160,6 +184,15 @@ def block(seed=BASE_SEED + 3, B=64, G=15, V=129280, T=1.0):
     q, x = _drafter(zf, G, T, lambda k: 0.75 * 1.05 ** k, seed)
     return Workload(name="block", B=B, G=G, V=V, T=T, dtype="bf16", logits=bits,
                     draft_probs=q, draft_tokens=x, uniforms=_uniforms(B, G, seed),
+                    verify_len=None, seed=seed)
+
+
+def block_logits(seed=BASE_SEED + 7, B=64, G=15, V=129280, T=1.0):
+    bits = zipf_logits(seed, B, G + 1, V)
+    zf = bf16_bits_to_f32(bits)
+    d, x = _logit_drafter(zf, G, T, lambda k: 0.75 * 1.05 ** k, seed)
+    return Workload(name="block_logits", B=B, G=G, V=V, T=T, dtype="bf16", logits=bits,
+                    draft_probs=None, draft_logits=d, draft_tokens=x, uniforms=_uniforms(B, G, seed),
                     verify_len=None, seed=seed)
 
 
