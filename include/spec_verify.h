@@ -8,6 +8,8 @@
  *                       blocks against the target's logits.
  *   spec_verify_packed  the same over densely packed target rows (each
  *                       request's kept positions only).
+ *   spec_verify_logits  the same with the draft distribution given as logits
+ *                       (its softmax at the call's temperature).
  *   spec_schedule       confidence-scheduled verification depth: how many
  *                       drafts of each request to verify under a batch token
  *                       budget.
@@ -107,8 +109,9 @@ typedef struct {
  * Bytes of device workspace spec_verify needs for this shape (0 on invalid
  * arguments).  The same workspace serves every shape whose query is not larger.
  *
- * The workspace holds the per-row partial sums, the per-draft gathers and the
- * per-request sub-tile masses.  It must be zero-filled once before its first use (e.g.
+ * The workspace holds the per-row partial sums (target rows, and draft rows
+ * for spec_verify_logits), the per-draft gathers and the per-request sub-tile
+ * masses; every verify entry point takes it.  It must be zero-filled once before its first use (e.g.
  * allocated with a zeroing allocator); every completed call leaves it
  * zero-filled again, so one workspace can serve later calls of any shape
  * without clearing.  Calls that share one workspace must not overlap in time
@@ -190,6 +193,33 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype,
 spec_status_t spec_verify_packed(const void *target_logits, spec_dtype_t target_dtype, int32_t rows,
                                  const int32_t *row_offsets, const float *draft_probs,
                                  const int32_t *draft_tokens, const float *uniforms,
+                                 int32_t B, int32_t G, int32_t V, float temperature,
+                                 int32_t *out_accepted, int32_t *out_tokens,
+                                 const spec_verify_diag_t *diag,
+                                 void *workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/*
+ * spec_verify_logits -- spec_verify with draft logits instead of draft
+ * probabilities.
+ *
+ * Operation ("AngelSpec", section 2, Eq. 2; the verification rule as for
+ * spec_verify): the draft distribution of position k is
+ * q_k = softmax(draft_logits[b,k,:] / T) at the call's temperature, formed on
+ * the device: the row pass also reduces every verified draft row (max and
+ * exp-sum), the accept test uses q_k(x_k) from that normaliser, and the
+ * residual max(p_j - q_j, 0) reads draft row j's logits.
+ *
+ * Arguments as for spec_verify, except draft_logits [B, G, V] of target_dtype
+ * (rows k < len_b are read; may be NULL if T == 0 or G == 0) in place of
+ * draft_probs.  Workspace: spec_verify_workspace_bytes.  diag->q_draft returns
+ * q_k(x_k) computed from the logits.
+ *
+ * Data errors: those of spec_verify, and a verified draft row (k < len_b) that
+ * holds a NaN, whose maximum is +inf, or which is entirely -inf.
+ */
+spec_status_t spec_verify_logits(const void *target_logits, spec_dtype_t target_dtype,
+                                 const void *draft_logits, const int32_t *draft_tokens,
+                                 const float *uniforms, const int32_t *verify_len,
                                  int32_t B, int32_t G, int32_t V, float temperature,
                                  int32_t *out_accepted, int32_t *out_tokens,
                                  const spec_verify_diag_t *diag,

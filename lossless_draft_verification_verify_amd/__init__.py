@@ -65,7 +65,7 @@ def _workspace(device, stream_handle, nbytes):
 
 
 def verify(target_logits, draft_probs, draft_tokens, uniforms, temperature, verify_len=None, *,
-           out_accepted=None, out_tokens=None, diag=False, workspace=None, row_pass_event=None):
+           out_accepted=None, out_tokens=None, diag=False, workspace=None, row_pass_event=None, draft_logits=None):
     """Verify a batch of draft blocks on the current stream of target_logits' device.
 
     target_logits [B, G+1, V] bf16/fp32; draft_probs [B, G, V] fp32 (None at T=0);
@@ -75,6 +75,8 @@ def verify(target_logits, draft_probs, draft_tokens, uniforms, temperature, veri
     row_pass_event: a torch.cuda.Event, or a raw hipEvent_t handle (int), that
     the library records right after the launch of the row pass (for timing
     that kernel alone).
+    draft_logits: [B, G, V] of the target's dtype in place of draft_probs
+    (which must then be None): q = softmax(draft_logits / temperature).
     """
     z = target_logits
     if not isinstance(z, torch.Tensor) or z.dim() != 3:
@@ -91,7 +93,10 @@ def verify(target_logits, draft_probs, draft_tokens, uniforms, temperature, veri
         out_accepted = torch.empty(B, dtype=i32, device=dev)
     if out_tokens is None:
         out_tokens = torch.empty(B, G1, dtype=i32, device=dev)
-    for t, shape, name in ((draft_probs, (B, G, V), "draft_probs"), (draft_tokens, (B, G), "draft_tokens"),
+    if draft_logits is not None and draft_probs is not None:
+        raise ValueError("pass draft_probs or draft_logits, not both")
+    for t, shape, name in ((draft_probs, (B, G, V), "draft_probs"), (draft_logits, (B, G, V), "draft_logits"),
+                           (draft_tokens, (B, G), "draft_tokens"),
                            (uniforms, (B, G1), "uniforms"), (verify_len, (B,), "verify_len"),
                            (out_accepted, (B,), "out_accepted"), (out_tokens, (B, G1), "out_tokens")):
         if t is not None and tuple(t.shape) != shape:
@@ -116,13 +121,24 @@ def verify(target_logits, draft_probs, draft_tokens, uniforms, temperature, veri
         d = _capi.DiagT(0, 0, 0, 0, ev)
     nbytes = _capi.verify_workspace_bytes(B, G, V, code)
     ws = workspace if workspace is not None else _workspace(dev, stream, nbytes)
-    st = _capi.spec_verify(
-        z.data_ptr(), code, _ptr(draft_probs, f32, dev, "draft_probs"), _ptr(draft_tokens, i32, dev, "draft_tokens"),
-        _ptr(uniforms, f32, dev, "uniforms"), _ptr(verify_len, i32, dev, "verify_len"), B, G, V, T,
-        _ptr(out_accepted, i32, dev, "out_accepted"), _ptr(out_tokens, i32, dev, "out_tokens"), d,
-        ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    if draft_logits is not None:
+        st = _capi.spec_verify_logits(
+            z.data_ptr(), code, _ptr(draft_logits, z.dtype, dev, "draft_logits"),
+            _ptr(draft_tokens, i32, dev, "draft_tokens"), _ptr(uniforms, f32, dev, "uniforms"),
+            _ptr(verify_len, i32, dev, "verify_len"), B, G, V, T,
+            _ptr(out_accepted, i32, dev, "out_accepted"), _ptr(out_tokens, i32, dev, "out_tokens"), d,
+            ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+        where = "spec_verify_logits"
+    else:
+        st = _capi.spec_verify(
+            z.data_ptr(), code, _ptr(draft_probs, f32, dev, "draft_probs"),
+            _ptr(draft_tokens, i32, dev, "draft_tokens"), _ptr(uniforms, f32, dev, "uniforms"),
+            _ptr(verify_len, i32, dev, "verify_len"), B, G, V, T,
+            _ptr(out_accepted, i32, dev, "out_accepted"), _ptr(out_tokens, i32, dev, "out_tokens"), d,
+            ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+        where = "spec_verify"
     if st != _capi.SPEC_OK:
-        raise SpecError(st, "spec_verify")
+        raise SpecError(st, where)
     if diag:
         return out_accepted, out_tokens, dg
     return out_accepted, out_tokens

@@ -35,6 +35,7 @@ EXPORTS = (
     "spec_schedule_workspace_bytes",
     "spec_schedule",
     "spec_verify_packed",
+    "spec_verify_logits",
     "spec_dcut",
     "spec_acceptance",
     "spec_status_string",
@@ -86,6 +87,9 @@ def load():
     lib.spec_verify_packed.argtypes = [vp, ctypes.c_int, i32, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp,
                                        ctypes.POINTER(DiagT), vp, sz, vp]
     lib.spec_verify_packed.restype = ctypes.c_int
+    lib.spec_verify_logits.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp,
+                                       ctypes.POINTER(DiagT), vp, sz, vp]
+    lib.spec_verify_logits.restype = ctypes.c_int
     lib.spec_dcut.argtypes = [vp, i32, i32, ctypes.POINTER(f32), ctypes.POINTER(f32), i32, vp, vp, vp, vp, vp, vp]
     lib.spec_dcut.restype = ctypes.c_int
     lib.spec_acceptance.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, i32, i32, i32, f32, vp, vp]
@@ -149,3 +153,10 @@ def spec_dcut(conf, B, G, ratios, costs, out_len, out_off, out_ratio, out_rows, 
 def spec_acceptance(logits, dtype_code, draft, draft_kind, vlen, B, G, V, T, out_alpha, stream):
     return int(load().spec_acceptance(logits or None, dtype_code, draft or None, draft_kind, vlen or None, B, G, V,
                                       ctypes.c_float(T), out_alpha or None, stream or None))
+
+
+def spec_verify_logits(logits, dtype_code, dl, x, u, vlen, B, G, V, T, out_acc, out_tok, diag, ws, ws_bytes, stream):
+    d = ctypes.byref(diag) if diag is not None else None
+    return int(load().spec_verify_logits(logits or None, dtype_code, dl or None, x or None, u or None, vlen or None,
+                                         B, G, V, ctypes.c_float(T), out_acc or None, out_tok or None, d,
+                                         ws or None, ws_bytes, stream or None))

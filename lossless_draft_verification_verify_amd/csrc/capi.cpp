@@ -33,7 +33,7 @@ spec_status_t check_verify_shape(int64_t B, int64_t G, int64_t V, int es) {
     if (B > SPEC_MAX_BATCH || G > SPEC_MAX_DRAFTS || V > SPEC_MAX_VOCAB) return SPEC_ERR_UNSUPPORTED;
     const int64_t nc1 = (V + sv::chunk_elems(es) - 1) / sv::chunk_elems(es);
     const int64_t nsub = (V + sv::kSub - 1) / sv::kSub;
-    const int64_t items = B * ((G + 1) * nc1 + nsub);   // row waves + request workgroups
+    const int64_t items = B * ((2 * G + 1) * nc1 + nsub);   // row waves (target and draft rows) + request workgroups
     if (items >= (int64_t(1) << 31)) return SPEC_ERR_UNSUPPORTED;
     if (B * (G + 1) > (int64_t(1) << 40) / V) return SPEC_ERR_UNSUPPORTED;
     return SPEC_OK;
@@ -109,7 +109,8 @@ namespace {
 // spec_verify and spec_verify_packed: the target rows are [B, G+1, V]
 // (row_offsets NULL) or `rows` packed rows addressed through row_offsets.
 spec_status_t verify_impl(const void *target_logits, spec_dtype_t target_dtype, const int32_t *row_offsets,
-                          int32_t rows, const float *draft_probs, const int32_t *draft_tokens,
+                          int32_t rows, const float *draft_probs, const void *draft_logits,
+                          const int32_t *draft_tokens,
                           const float *uniforms, const int32_t *verify_len, int32_t B, int32_t G, int32_t V,
                           float temperature, int32_t *out_accepted, int32_t *out_tokens,
                           const spec_verify_diag_t *diag, void *workspace, size_t workspace_bytes,
@@ -129,7 +130,8 @@ spec_status_t verify_impl(const void *target_logits, spec_dtype_t target_dtype, 
     const bool sampled = T > 0.0f;
     if (!target_logits || !out_accepted || !out_tokens) return SPEC_ERR_NULL_POINTER;
     if (G > 0 && !draft_tokens) return SPEC_ERR_NULL_POINTER;
-    if (sampled && G > 0 && !draft_probs) return SPEC_ERR_NULL_POINTER;
+    if (sampled && G > 0 && !draft_probs && !draft_logits) return SPEC_ERR_NULL_POINTER;
+    if (!aligned(draft_logits, es)) return SPEC_ERR_MISALIGNED;
     if (sampled && !uniforms) return SPEC_ERR_NULL_POINTER;
     if (!aligned(target_logits, es) || !aligned(draft_probs, 4) || !aligned(draft_tokens, 4) ||
         !aligned(uniforms, 4) || !aligned(verify_len, 4) || !aligned(out_accepted, 4) ||
@@ -150,6 +152,7 @@ spec_status_t verify_impl(const void *target_logits, spec_dtype_t target_dtype, 
     sv::VerifyArgs a = {};
     a.logits = target_logits;
     a.q = draft_probs;
+    a.dl = (sampled && G > 0) ? draft_logits : nullptr;   // the greedy limit never reads the draft
     a.x = draft_tokens;
     a.u = uniforms;
     a.vlen = verify_len;
@@ -173,7 +176,7 @@ spec_status_t verify_impl(const void *target_logits, spec_dtype_t target_dtype, 
     a.nsub = (V + sv::kSub - 1) / sv::kSub;
     a.spin_limit = 1u << 20;
     const bool az = aligned(target_logits, 16) && (size_t(V) * es) % 16 == 0;
-    const bool aq = aligned(draft_probs, 16) && V % 4 == 0;
+    const bool aq = a.dl ? aligned(a.dl, 16) && (size_t(V) * es) % 16 == 0 : aligned(draft_probs, 16) && V % 4 == 0;
 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SPEC_ERR_DEVICE;
@@ -182,7 +185,7 @@ spec_status_t verify_impl(const void *target_logits, spec_dtype_t target_dtype, 
         // partial before the per-request work, across all XCDs).  One row
         // workgroup per (request, row, group of kWaves chunks).
         a.np1 = (a.nc1 + sv::kWaves - 1) / sv::kWaves;
-        const long row_groups = long(B) * (G + 1) * a.np1;
+        const long row_groups = long(B) * ((G + 1) + (a.dl ? G : 0)) * a.np1;   // target rows, draft rows
         // Sub-tiles per draw workgroup: about 1024 draw workgroups in all (each
         // one repeats the request's decision, so fewer and longer ones keep
         // that traffic from queueing behind the draw streams).
@@ -240,8 +243,20 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
                           int32_t B, int32_t G, int32_t V, float temperature, int32_t *out_accepted,
                           int32_t *out_tokens, const spec_verify_diag_t *diag, void *workspace,
                           size_t workspace_bytes, spec_stream_t stream) {
-    return verify_impl(target_logits, target_dtype, nullptr, 0, draft_probs, draft_tokens, uniforms, verify_len,
-                       B, G, V, temperature, out_accepted, out_tokens, diag, workspace, workspace_bytes, stream);
+    return verify_impl(target_logits, target_dtype, nullptr, 0, draft_probs, nullptr, draft_tokens, uniforms,
+                       verify_len, B, G, V, temperature, out_accepted, out_tokens, diag, workspace, workspace_bytes,
+                       stream);
+}
+
+spec_status_t spec_verify_logits(const void *target_logits, spec_dtype_t target_dtype, const void *draft_logits,
+                                 const int32_t *draft_tokens, const float *uniforms, const int32_t *verify_len,
+                                 int32_t B, int32_t G, int32_t V, float temperature, int32_t *out_accepted,
+                                 int32_t *out_tokens, const spec_verify_diag_t *diag, void *workspace,
+                                 size_t workspace_bytes, spec_stream_t stream) {
+    if (G > 0 && temperature > 0.0f && !draft_logits) return SPEC_ERR_NULL_POINTER;
+    return verify_impl(target_logits, target_dtype, nullptr, 0, nullptr, draft_logits, draft_tokens, uniforms,
+                       verify_len, B, G, V, temperature, out_accepted, out_tokens, diag, workspace, workspace_bytes,
+                       stream);
 }
 
 spec_status_t spec_verify_packed(const void *target_logits, spec_dtype_t target_dtype, int32_t rows,
@@ -251,7 +266,7 @@ spec_status_t spec_verify_packed(const void *target_logits, spec_dtype_t target_
                                  const spec_verify_diag_t *diag, void *workspace, size_t workspace_bytes,
                                  spec_stream_t stream) {
     if (!row_offsets) return SPEC_ERR_NULL_POINTER;
-    return verify_impl(target_logits, target_dtype, row_offsets, rows, draft_probs, draft_tokens, uniforms,
+    return verify_impl(target_logits, target_dtype, row_offsets, rows, draft_probs, nullptr, draft_tokens, uniforms,
                        nullptr, B, G, V, temperature, out_accepted, out_tokens, diag, workspace,
                        workspace_bytes, stream);
 }

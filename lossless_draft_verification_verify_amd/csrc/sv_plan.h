@@ -25,6 +25,8 @@ inline int chunk_elems(int esize) { return 64 * kRowVec * (16 / esize); }
 // valid across calls of any shape.
 //   zero     256 bytes never written: the draft row a bonus draw reads in
 //            place of q (so the draw loads need no branch);
+//   partd    [B*G*np1] u64 partials of the draft rows, same format (draft
+//            logits only);
 //   part     [B*(G+1)*np1] u64 partials, bit 63 set once written
 //            one per row workgroup of kWaves chunks (np1 = ceil(nc1 / kWaves)
 //            per row; the region is sized for nc1): sampled, low = max bits,
@@ -33,7 +35,8 @@ inline int chunk_elems(int esize) { return 64 * kRowVec * (16 / esize); }
 //   mass     [B*nsub] 2 u64: fp64 (residual mass, target mass) per sub-tile,
 //            bit 63 set once written;
 //   gx       [B*G] u64: the row pass's gather of draft k (sampled only):
-//            low = fp32 bits of z[b,k,x_k], high = bits of q[b,k,x_k].
+//            low = fp32 bits of z[b,k,x_k], high = bits of q[b,k,x_k] (with
+//            draft logits: of d[b,k,x_k], stored by the draft row's pass).
 
 constexpr int kMaxBatch = 65536;
 constexpr uint32_t kValid = 0x80000000u;
@@ -41,6 +44,7 @@ constexpr uint32_t kValid = 0x80000000u;
 struct Layout {
     size_t zero;
     size_t part;
+    size_t partd;
     size_t mass;
     size_t gx;
     size_t total;
@@ -55,6 +59,7 @@ inline Layout make_layout(int64_t B, int64_t G, int64_t V, int esize) {
     size_t o = 0;
     L.zero = o; o += 256;
     L.part = o; o += align256(size_t(B) * size_t(G + 1) * size_t(nc1) * 8);
+    L.partd = o; o += align256(size_t(B) * size_t(G) * size_t(nc1) * 8);
     L.mass = o; o += align256(size_t(B) * size_t(nsub) * 16);
     L.gx = o; o += align256(size_t(B) * size_t(G) * 8);
     L.total = o;
@@ -64,6 +69,7 @@ inline Layout make_layout(int64_t B, int64_t G, int64_t V, int esize) {
 struct VerifyArgs {
     const void *logits;
     const float *q;
+    const void *dl;       // draft logits [B, G, V] of the target dtype (NULL: draft probabilities q)
     const int32_t *x;
     const float *u;
     const int32_t *vlen;
@@ -89,7 +95,7 @@ struct VerifyArgs {
 int launch_rows_sampled(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
 int launch_rows_sampled_vl(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
 int launch_requests_sampled(const VerifyArgs &a, bool aligned_z, bool aligned_q, int esize, int grid,
-                            void *stream);
+                            void *stream);   // draft logits when a.dl is set
 int launch_verify_greedy(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
 int greedy_occupancy(bool aligned_z, int esize, int *blocks_per_cu);
 

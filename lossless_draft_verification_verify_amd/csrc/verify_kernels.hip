@@ -142,6 +142,8 @@ struct __align__(16) Smem {
     } r;
     double S[kWG];                                // fp64 row sums
     float M[kWG];                                 // row maxima
+    double Sq[kWG];                               // draft logits: the draft rows' sums and maxima
+    float Mq[kWG];
     int A[kWG];                                   // greedy row argmax
     int last;
     int q[6][kWaves];                             // per-wave results of ballot searches
@@ -228,6 +230,9 @@ __device__ void wg_scan(const double (&v)[NS], double (&excl)[NS], double (&incl
 
 __device__ __forceinline__ uint64_t *partials(const VerifyArgs &a, int b) {
     return reinterpret_cast<uint64_t *>(a.ws + a.lay.part) + size_t(b) * (a.G + 1) * a.np1;
+}
+__device__ __forceinline__ uint64_t *partials_d(const VerifyArgs &a, int b) {
+    return reinterpret_cast<uint64_t *>(a.ws + a.lay.partd) + size_t(b) * a.G * a.np1;
 }
 __device__ __forceinline__ uint64_t *masses(const VerifyArgs &a, int b) {
     return reinterpret_cast<uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
@@ -324,13 +329,17 @@ __device__ __forceinline__ int chunk_index(int beg, int lane, int i) {
 
 // Sampled row pass, one wave: (max M, sum S of 2^((z - M) * c)) of chunk c
 // of row k of request b (n = the request's verify length), uniform across
-// the wave.  The chunk holding draft token x_k also stores z(x_k) and q(x_k)
-// for the request pass's accept test.
+// the wave; of draft row k when `draft` (draft logits).  The chunk holding
+// draft token x_k also stores z(x_k) and q(x_k) for the request pass's accept
+// test (with draft logits: z(x_k) from the target row, d(x_k) from the draft
+// row, each into its half of the gather word).
 template <int ES, bool AL>
-__device__ void row_chunk_sampled(const VerifyArgs &a, int b, int k, int chunk, int n, int lane, float &M_out,
-                                  float &S_out) {
+__device__ void row_chunk_sampled(const VerifyArgs &a, int b, int k, int chunk, int n, bool draft, int lane,
+                                  float &M_out, float &S_out) {
     constexpr int EPL = kEPL<ES>;
-    const void *row = static_cast<const char *>(a.logits) + row_elem(a, b, k) * ES;
+    const void *row = draft ? static_cast<const void *>(static_cast<const char *>(a.dl) +
+                                                        (size_t(b) * a.G + k) * size_t(a.V) * ES)
+                            : static_cast<const void *>(static_cast<const char *>(a.logits) + row_elem(a, b, k) * ES);
     const int beg = chunk * a.ch1;
     float f[EPL];
     load_chunk<ES, AL>(row, beg, a.V, lane, f);
@@ -341,7 +350,7 @@ __device__ void row_chunk_sampled(const VerifyArgs &a, int b, int k, int chunk, 
     float gz = 0.0f, gq = 0.0f;
     if (gather && lane == 0) {
         gz = load_elem<ES>(row, size_t(xk));
-        gq = a.q[(size_t(b) * a.G + k) * size_t(a.V) + size_t(xk)];
+        if (!a.dl) gq = a.q[(size_t(b) * a.G + k) * size_t(a.V) + size_t(xk)];
     }
     const float c = a.c32;
     float m = f[0];
@@ -375,8 +384,10 @@ __device__ void row_chunk_sampled(const VerifyArgs &a, int b, int k, int chunk, 
     }
     M_out = M;
     S_out = wave_sum((s0 + s1) + (s2 + s3));
-    if (gather && lane == 0)
-        gathered(a, b)[k] = uint64_t(__float_as_uint(gz)) | (uint64_t(__float_as_uint(gq)) << 32);
+    if (gather && lane == 0) {
+        if (!a.dl) gathered(a, b)[k] = uint64_t(__float_as_uint(gz)) | (uint64_t(__float_as_uint(gq)) << 32);
+        else reinterpret_cast<uint32_t *>(gathered(a, b) + k)[draft ? 1 : 0] = __float_as_uint(gz);
+    }
 }
 
 // Greedy row pass, one wave: (max M, lowest index of the max, any NaN) of
@@ -427,16 +438,31 @@ __device__ __forceinline__ void draw_term(float z, float q, float m, float c, fl
     r = resid ? fmaxf(p - q, 0.0f) : p;
 }
 
+// Eight values from one (bf16) or two (fp32) 16-byte words.
+template <int ES> __device__ __forceinline__ void unpack8(const uint4 (&w)[ES == 2 ? 1 : 2], float (&f)[kSubPerThread]) {
+    if constexpr (ES == 2) {
+        f[0] = bf16_lo(w[0].x); f[1] = bf16_hi(w[0].x); f[2] = bf16_lo(w[0].y); f[3] = bf16_hi(w[0].y);
+        f[4] = bf16_lo(w[0].z); f[5] = bf16_hi(w[0].z); f[6] = bf16_lo(w[0].w); f[7] = bf16_hi(w[0].w);
+    } else {
+        f[0] = __uint_as_float(w[0].x); f[1] = __uint_as_float(w[0].y);
+        f[2] = __uint_as_float(w[0].z); f[3] = __uint_as_float(w[0].w);
+        f[4] = __uint_as_float(w[1].x); f[5] = __uint_as_float(w[1].y);
+        f[6] = __uint_as_float(w[1].z); f[7] = __uint_as_float(w[1].w);
+    }
+}
+
 // One thread's 8 contiguous elements of sub-tile `sub` of a draw row: the
 // residual (or target) mass `rs` and the target mass `ps`, fp64 in index
 // order, and the terms t (residual if use_r, else target; 0 past the row end).
 // qrow is the draft row (resid) or a block of zeros (bonus draw), so the z
-// and q loads are all issued before any is waited for.  The mass pass and the
-// final re-scan both call this, so their sums agree bitwise.
-template <int ES, bool ALZ, bool ALQ>
-__device__ __forceinline__ void sub_tile(const void *zrow, const float *qrow, int V, int sub, float m, float c,
-                                         float inv_s, bool resid, bool use_r, float (&t)[kSubPerThread],
-                                         double &rs, double &ps) {
+// and q loads are all issued before any is waited for.  With draft logits
+// (DL) qrow holds logits of the target's element size, and q is their
+// softmax from the draft row's maximum mq and 1 / sum inv_sq.  The mass pass
+// and the final re-scan both call this, so their sums agree bitwise.
+template <int ES, bool ALZ, bool ALQ, bool DL>
+__device__ __forceinline__ void sub_tile(const void *zrow, const void *qrow, int V, int sub, float m, float c,
+                                         float inv_s, float mq, float inv_sq, bool resid, bool use_r,
+                                         float (&t)[kSubPerThread], double &rs, double &ps) {
     rs = 0.0; ps = 0.0;
 #pragma unroll
     for (int i = 0; i < kSubPerThread; ++i) t[i] = 0.0f;
@@ -444,26 +470,17 @@ __device__ __forceinline__ void sub_tile(const void *zrow, const float *qrow, in
     if (e0 >= V) return;
     const int qo = resid ? e0 : 0;          // the zero block is read from its start
     float z[kSubPerThread], q[kSubPerThread];
+    constexpr int QS = DL ? ES : 4;          // element size of the draft row
     if (ALZ && (!resid || ALQ) && e0 + kSubPerThread <= V) {
         const uint4 *zp = reinterpret_cast<const uint4 *>(static_cast<const char *>(zrow) + size_t(e0) * ES);
-        const uint4 *qp = reinterpret_cast<const uint4 *>(qrow + qo);
-        uint4 zw[ES == 2 ? 1 : 2];
+        const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const char *>(qrow) + size_t(qo) * QS);
+        uint4 zw[ES == 2 ? 1 : 2], qw[QS == 2 ? 1 : 2];
         zw[0] = zp[0];
         if constexpr (ES == 4) zw[1] = zp[1];
-        const uint4 q0 = qp[0], q1 = qp[1];
-        if constexpr (ES == 2) {
-            z[0] = bf16_lo(zw[0].x); z[1] = bf16_hi(zw[0].x); z[2] = bf16_lo(zw[0].y); z[3] = bf16_hi(zw[0].y);
-            z[4] = bf16_lo(zw[0].z); z[5] = bf16_hi(zw[0].z); z[6] = bf16_lo(zw[0].w); z[7] = bf16_hi(zw[0].w);
-        } else {
-            z[0] = __uint_as_float(zw[0].x); z[1] = __uint_as_float(zw[0].y);
-            z[2] = __uint_as_float(zw[0].z); z[3] = __uint_as_float(zw[0].w);
-            z[4] = __uint_as_float(zw[1].x); z[5] = __uint_as_float(zw[1].y);
-            z[6] = __uint_as_float(zw[1].z); z[7] = __uint_as_float(zw[1].w);
-        }
-        q[0] = __uint_as_float(q0.x); q[1] = __uint_as_float(q0.y);
-        q[2] = __uint_as_float(q0.z); q[3] = __uint_as_float(q0.w);
-        q[4] = __uint_as_float(q1.x); q[5] = __uint_as_float(q1.y);
-        q[6] = __uint_as_float(q1.z); q[7] = __uint_as_float(q1.w);
+        qw[0] = qp[0];
+        if constexpr (QS == 4) qw[1] = qp[1];
+        unpack8<ES>(zw, z);
+        unpack8<QS>(qw, q);
     } else {
         // Element loads at clamped indices (all in bounds, all issued at once);
         // positions past the row end are dropped below.
@@ -471,8 +488,15 @@ __device__ __forceinline__ void sub_tile(const void *zrow, const float *qrow, in
         for (int i = 0; i < kSubPerThread; ++i) {
             const int e = min(e0 + i, V - 1);
             z[i] = load_elem<ES>(zrow, size_t(e));
-            q[i] = qrow[resid ? e : 0];
+            q[i] = load_elem<QS>(qrow, size_t(resid ? e : 0));
         }
+    }
+    if constexpr (DL) {
+        // q from the draft logits (its reference as in the row pass: fl(mq * c) when finite)
+        const float Rq = mq * c;
+#pragma unroll
+        for (int i = 0; i < kSubPerThread; ++i)
+            q[i] = (finitef(Rq) ? exp2_fast(__builtin_fmaf(q[i], c, -Rq)) : exp2_fast((q[i] - mq) * c)) * inv_sq;
     }
 #pragma unroll
     for (int i = 0; i < kSubPerThread; ++i) {
@@ -493,6 +517,7 @@ struct Decision {
     int n, j;
     bool resid;
     float m, inv_s;
+    float mq, inv_sq;  // draft logits: the draft row j's maximum and 1 / sum
     float u_final;    // u[b, G], the final draw's uniform
 };
 
@@ -502,10 +527,12 @@ struct Decision {
 // previous launch.  Returns true in some thread if a read row is bad or has a
 // partial that was never written.
 constexpr int kRowBad = 1;
-__device__ bool merge_rows_sampled(const VerifyArgs &a, int b, int n, Smem &sh) {
+// Rows 0..nrows-1 of `part` (np1 partials each): fp32 maximum and fp64 sum
+// per row into Mo / So.  Returns whether any row is bad or not yet written.
+__device__ bool merge_rows_sampled(const VerifyArgs &a, const uint64_t *part, int nrows, float *Mo, double *So) {
     bool bad = false;
     constexpr int kRegs = 4;   // partials held per lane when np1 <= 64
-    const uint64_t *part = partials(a, b);
+    const int n = nrows - 1;
     const int l = threadIdx.x & 15, g = threadIdx.x >> 4;
     const float c = a.c32;
     const uint64_t empty = uint64_t(0xff800000u) | (uint64_t(kValid) << 32);   // (-inf, 0), written
@@ -550,8 +577,8 @@ __device__ bool merge_rows_sampled(const VerifyArgs &a, int b, int n, Smem &sh) 
         ok = row16_and(ok);
         if (l == 0 && live) {
             bad |= !ok || !(S > 0.0 && S < INFINITY) || !(M > neg_inf() && M < __builtin_inff());
-            sh.M[r] = M;
-            sh.S[r] = S;
+            Mo[r] = M;
+            So[r] = S;
         }
     }
     return bad;
@@ -640,7 +667,15 @@ __device__ void write_diag(const VerifyArgs &a, int b, bool ok, int n, Smem &sh)
             if (t < n) {
                 const int xt = a.x[size_t(b) * G + t];
                 const float zt = load_elem<ES>(a.logits, row_elem(a, b, t) + size_t(xt));
-                qv = a.q[(size_t(b) * G + t) * size_t(a.V) + size_t(xt)];
+                if (a.dl) {
+                    // the draft probability from the draft row's logits and normaliser
+                    const float dt = load_elem<ES>(a.dl, (size_t(b) * G + t) * size_t(a.V) + size_t(xt));
+                    const float mq = sh.Mq[t], Rq = mq * a.c32;
+                    const float eq = finitef(Rq) ? exp2_fast(__builtin_fmaf(dt, a.c32, -Rq)) : exp2_fast((dt - mq) * a.c32);
+                    qv = eq / float(sh.Sq[t]);
+                } else {
+                    qv = a.q[(size_t(b) * G + t) * size_t(a.V) + size_t(xt)];
+                }
                 const float e = finitef(R) ? exp2_fast(__builtin_fmaf(zt, a.c32, -R)) : exp2_fast((zt - m) * a.c32);
                 pv = e / S;
             }
@@ -671,6 +706,8 @@ __device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, bool &pro
     d.resid = false;
     d.m = 0.0f;
     d.inv_s = 0.0f;
+    d.mq = 0.0f;
+    d.inv_sq = 0.0f;
     d.u_final = 0.0f;
     proceed = false;
     if (n < 0 || n > G) {
@@ -687,7 +724,8 @@ __device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, bool &pro
         uk = a.u[size_t(b) * G1 + k];
     }
     d.u_final = a.u[size_t(b) * G1 + G];
-    bool bad = merge_rows_sampled(a, b, n, sh);
+    bool bad = merge_rows_sampled(a, partials(a, b), n + 1, sh.M, sh.S);
+    if (a.dl) bad |= merge_rows_sampled(a, partials_d(a, b), n, sh.Mq, sh.Sq);
     // Keep the uses of the per-draft loads below the partials' loads (the
     // compiler would otherwise wait for them before issuing the partials).
     asm volatile("" : "+v"(xk), "+v"(uk), "+v"(gk));
@@ -698,9 +736,11 @@ __device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, bool &pro
     }
     bool rej = false;
     if (k < n) {
-        const float zx = lo_f(gk), qx = __uint_as_float(hi_u(gk));
+        const float zx = lo_f(gk), hx = __uint_as_float(hi_u(gk));
         const double pk = target_prob(zx, sh.M[k], a.c32) / sh.S[k];
-        const bool acc = (qx > 0.0f) ? (double(uk) < pk / double(qx)) : (pk > 0.0);
+        // q(x_k): as read, or from the draft row's normaliser (draft logits)
+        const double qx = a.dl ? target_prob(hx, sh.Mq[k], a.c32) / sh.Sq[k] : double(hx);
+        const bool acc = (qx > 0.0) ? (double(uk) < pk / qx) : (pk > 0.0);
         rej = !acc;
     }
     post_first(rej, 0, sh);
@@ -711,6 +751,10 @@ __device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, bool &pro
     d.resid = j < n;
     d.m = sh.M[j];
     d.inv_s = float(1.0 / sh.S[j]);
+    if (a.dl && j < n) {
+        d.mq = sh.Mq[j];
+        d.inv_sq = float(1.0 / sh.Sq[j]);
+    }
     if (w == 0) {
         for (int t = threadIdx.x; t < G1; t += kWG) {
             if (t < j) st_out(a.out_tok + size_t(b) * G1 + t, a.x[size_t(b) * G + t]);
@@ -758,8 +802,8 @@ __device__ bool wait_masses(const VerifyArgs &a, int b, double (&v)[2]) {
 // positive mass.  Where rounding between the levels leaves no crossing, the
 // last positive term before the target is taken, which differs from the exact
 // draw only when u * R lies within rounding of a cumulative sum.
-template <int ES, bool ALZ, bool ALQ>
-__device__ void final_select(const VerifyArgs &a, int b, const Decision &d, const void *zrow, const float *qrow,
+template <int ES, bool ALZ, bool ALQ, bool DL>
+__device__ void final_select(const VerifyArgs &a, int b, const Decision &d, const void *zrow, const void *qrow,
                              const double (&polled)[2], Smem &sh) {
     const int G1 = a.G + 1;
     const bool resid = d.resid;
@@ -842,7 +886,7 @@ __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, cons
     const double base = lastpos ? 0.0 : sh.base;
     float t[kSubPerThread];
     double rs, ps;
-    sub_tile<ES, ALZ, ALQ>(zrow, qrow, a.V, sstar, d.m, a.c32, d.inv_s, resid, use_r, t, rs, ps);
+    sub_tile<ES, ALZ, ALQ, DL>(zrow, qrow, a.V, sstar, d.m, a.c32, d.inv_s, d.mq, d.inv_sq, resid, use_r, t, rs, ps);
     const double v1[1] = {sel ? ps : rs};
     double ex1[1], in1[1], tot1[1];
     wg_scan<1>(v1, ex1, in1, tot1, sh);
@@ -881,7 +925,7 @@ __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, cons
 // last workgroup (w = nc2 - 1) waits for every mass word, selects the token,
 // writes the diagnostics and zeroes the request's partials, gathers and
 // masses.
-template <int ES, bool ALZ, bool ALQ>
+template <int ES, bool ALZ, bool ALQ, bool DL>
 __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh) {
     Decision d;
     bool proceed;
@@ -893,8 +937,11 @@ __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     uint64_t *mass = masses(a, b);
     const void *zrow = static_cast<const char *>(a.logits) + row_elem(a, b, d.j) * ES;
-    const float *qrow = d.resid ? a.q + (size_t(b) * a.G + d.j) * size_t(a.V)
-                                : reinterpret_cast<const float *>(a.ws + a.lay.zero);
+    // the draft row j (probabilities, or logits with DL) on a rejection, else the zero block
+    const size_t qe = (size_t(b) * a.G + d.j) * size_t(a.V);
+    const void *qrow = !d.resid ? static_cast<const void *>(a.ws + a.lay.zero)
+                       : DL    ? static_cast<const void *>(static_cast<const char *>(a.dl) + qe * ES)
+                               : static_cast<const void *>(a.q + qe);
     if (!ok) {
         const int s_beg = w * a.spw, s_end = min(a.nsub, (w + 1) * a.spw);
         for (int i = 2 * s_beg + int(threadIdx.x); i < 2 * s_end; i += kWG) st_coherent(mass + i, kMassWritten);
@@ -907,7 +954,8 @@ __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh
                 float t[kSubPerThread];
                 rs[i] = 0.0; ps[i] = 0.0;
                 if (s0 + i < s_end)
-                    sub_tile<ES, ALZ, ALQ>(zrow, qrow, a.V, s0 + i, d.m, a.c32, d.inv_s, d.resid, true, t, rs[i], ps[i]);
+                    sub_tile<ES, ALZ, ALQ, DL>(zrow, qrow, a.V, s0 + i, d.m, a.c32, d.inv_s, d.mq, d.inv_sq, d.resid,
+                                               true, t, rs[i], ps[i]);
             }
 #pragma unroll
             for (int i = 0; i < kSubBatch; ++i) {
@@ -939,12 +987,16 @@ __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh
     if (a.d_lse || a.d_p || a.d_q || a.d_r) write_diag<ES>(a, b, ok, d.n, sh);
     double polled[2];
     const bool all = wait_masses(a, b, polled);
-    if (ok && all) final_select<ES, ALZ, ALQ>(a, b, d, zrow, qrow, polled, sh);
+    if (ok && all) final_select<ES, ALZ, ALQ, DL>(a, b, d, zrow, qrow, polled, sh);
     else if (ok) write_error(a, b);              // an expired wait
     __syncthreads();
     for (int i = threadIdx.x; i < 2 * a.nsub; i += kWG) st_coherent(mass + i, 0ull);
     uint64_t *part = partials(a, b);
     for (int i = threadIdx.x; i < (d.n + 1) * a.np1; i += kWG) part[i] = 0ull;
+    if (DL) {
+        uint64_t *pd = partials_d(a, b);
+        for (int i = threadIdx.x; i < d.n * a.np1; i += kWG) pd[i] = 0ull;
+    }
     uint64_t *gx = gathered(a, b);
     for (int i = threadIdx.x; i < d.n; i += kWG) gx[i] = 0ull;
 }
@@ -998,12 +1050,12 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // waves' (max, sum) pairs in wave order, so the request pass reads a quarter
 // as many partials.
 template <int ES, bool AL>
-__device__ __forceinline__ void row_group_sampled(const VerifyArgs &a, int b, int k, int g, int n, float *gm,
-                                                  float *gs) {
+__device__ __forceinline__ void row_group_sampled(const VerifyArgs &a, int b, int k, int g, int n, bool draft,
+                                                  float *gm, float *gs) {
     const int w = wave_id(), lane = int(threadIdx.x) & 63;
     const int c = g * kWaves + w;
     float M = neg_inf(), S = 0.0f;
-    if (c < a.nc1) row_chunk_sampled<ES, AL>(a, b, k, c, n, lane, M, S);
+    if (c < a.nc1) row_chunk_sampled<ES, AL>(a, b, k, c, n, draft, lane, M, S);
     if (lane == 0) {
         gm[w] = M;
         gs[w] = S;
@@ -1014,7 +1066,8 @@ __device__ __forceinline__ void row_group_sampled(const VerifyArgs &a, int b, in
         float t = 0.0f;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) t = t + gs[v] * rescale(gm[v], m, a.c32);
-        partials(a, b)[size_t(k) * a.np1 + g] = uint64_t(__float_as_uint(m)) | (uint64_t(__float_as_uint(t) | kValid) << 32);
+        (draft ? partials_d(a, b) : partials(a, b))[size_t(k) * a.np1 + g] =
+            uint64_t(__float_as_uint(m)) | (uint64_t(__float_as_uint(t) | kValid) << 32);
     }
 }
 
@@ -1022,13 +1075,16 @@ __device__ __forceinline__ void row_group_sampled(const VerifyArgs &a, int b, in
 template <int ES, bool AL>
 __global__ __launch_bounds__(kWG) void k_rows_sampled(VerifyArgs a) {
     __shared__ float gm[kWaves], gs[kWaves];
-    const int per = (a.G + 1) * a.np1;
+    // Rows of a request: target rows 0..G, then (draft logits) draft rows 0..G-1.
+    const int per = ((a.G + 1) + (a.dl ? a.G : 0)) * a.np1;
     const int i = blockIdx.x;
     const int b = i / per, rem = i - b * per;
-    const int k = rem / a.np1, g = rem - k * a.np1;
+    const int rr = rem / a.np1, g = rem - rr * a.np1;
+    const bool draft = rr > a.G;
+    const int k = draft ? rr - a.G - 1 : rr;
     const int n = verify_len(a, b);
-    if (n < 0 || n > a.G || k > n) return;           // row not read: the whole workgroup leaves
-    row_group_sampled<ES, AL>(a, b, k, g, n, gm, gs);
+    if (n < 0 || n > a.G || (draft ? k >= n : k > n)) return;   // row not read: the whole workgroup leaves
+    row_group_sampled<ES, AL>(a, b, k, g, n, draft, gm, gs);
 }
 
 // Row pass with verify lengths and at most kWG requests, where most rows may
@@ -1046,7 +1102,7 @@ __global__ __launch_bounds__(kWG) void k_rows_sampled_vl(VerifyArgs a) {
     int cnt = 0;
     if (t < a.B) {
         const int n = verify_len(a, t);
-        cnt = (n >= 0 && n <= a.G) ? (n + 1) * a.np1 : 0;
+        cnt = (n >= 0 && n <= a.G) ? ((n + 1) + (a.dl ? n : 0)) * a.np1 : 0;   // target rows, then draft rows
     }
     const int x = wave_scan_i(cnt);
     if (lane == 63) wtot[w] = x;
@@ -1068,18 +1124,22 @@ __global__ __launch_bounds__(kWG) void k_rows_sampled_vl(VerifyArgs a) {
             else hi = mid - 1;
         }
         const int b = lo, local = job - off[b];
-        const int k = local / a.np1, g = local - k * a.np1;
-        row_group_sampled<ES, AL>(a, b, k, g, verify_len(a, b), gm, gs);
+        const int n = verify_len(a, b);
+        const int rr = local / a.np1, g = local - rr * a.np1;
+        const bool draft = rr > n;
+        row_group_sampled<ES, AL>(a, b, draft ? rr - n - 1 : rr, g, n, draft, gm, gs);
         __syncthreads();                              // gm / gs are reused by the next job
     }
 }
 
 // Request pass of a sampled verify: nc2 workgroups per request.
-template <int ES, bool ALZ, bool ALQ>
-__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_requests_sampled(VerifyArgs a) {
+template <int ES, bool ALZ, bool ALQ, bool DL>
+// Draft logits need more registers (the draft normalisers and the logit
+// conversion); 4 waves per SIMD still hold 1024 draw workgroups at once.
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(DL ? 4 : 8, DL ? 4 : 8))) void k_requests_sampled(VerifyArgs a) {
     __shared__ Smem sh;
     const int b = int(blockIdx.x) / a.nc2;
-    request_item_sampled<ES, ALZ, ALQ>(a, b, int(blockIdx.x) - b * a.nc2, sh);
+    request_item_sampled<ES, ALZ, ALQ, DL>(a, b, int(blockIdx.x) - b * a.nc2, sh);
 }
 
 // Greedy row workgroup gi: (request b, row k, group g of kWaves consecutive
@@ -1166,17 +1226,23 @@ int launch_rows_sampled_vl(const VerifyArgs &a, bool az, int esize, int grid, vo
     return int(hipGetLastError());
 }
 
+template <bool DL>
+void launch_requests_dl(const VerifyArgs &a, bool az, bool aq, int esize, int grid, hipStream_t st) {
+    if (esize == 2) {
+        if (az && aq) hipLaunchKernelGGL((k_requests_sampled<2, true, true, DL>), dim3(grid), dim3(kWG), 0, st, a);
+        else if (az) hipLaunchKernelGGL((k_requests_sampled<2, true, false, DL>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_requests_sampled<2, false, false, DL>), dim3(grid), dim3(kWG), 0, st, a);
+    } else {
+        if (az && aq) hipLaunchKernelGGL((k_requests_sampled<4, true, true, DL>), dim3(grid), dim3(kWG), 0, st, a);
+        else if (az) hipLaunchKernelGGL((k_requests_sampled<4, true, false, DL>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_requests_sampled<4, false, false, DL>), dim3(grid), dim3(kWG), 0, st, a);
+    }
+}
+
 int launch_requests_sampled(const VerifyArgs &a, bool az, bool aq, int esize, int grid, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (esize == 2) {
-        if (az && aq) hipLaunchKernelGGL((k_requests_sampled<2, true, true>), dim3(grid), dim3(kWG), 0, st, a);
-        else if (az) hipLaunchKernelGGL((k_requests_sampled<2, true, false>), dim3(grid), dim3(kWG), 0, st, a);
-        else hipLaunchKernelGGL((k_requests_sampled<2, false, false>), dim3(grid), dim3(kWG), 0, st, a);
-    } else {
-        if (az && aq) hipLaunchKernelGGL((k_requests_sampled<4, true, true>), dim3(grid), dim3(kWG), 0, st, a);
-        else if (az) hipLaunchKernelGGL((k_requests_sampled<4, true, false>), dim3(grid), dim3(kWG), 0, st, a);
-        else hipLaunchKernelGGL((k_requests_sampled<4, false, false>), dim3(grid), dim3(kWG), 0, st, a);
-    }
+    if (a.dl) launch_requests_dl<true>(a, az, aq, esize, grid, st);
+    else launch_requests_dl<false>(a, az, aq, esize, grid, st);
     return int(hipGetLastError());
 }
 

@@ -45,8 +45,9 @@ def test_status_strings():
 def test_workspace_query():
     w = _capi.verify_workspace_bytes(64, 15, 129280, _capi.SPEC_DTYPE_BF16)
     # a 256-byte zero block + partials 64*16 rows*64 chunks*8 B (sized for the
-    # greedy per-chunk count) + masses 64*64 sub-tiles*16 B + gathers 64*15*8 B
-    assert w == 256 + 64 * 16 * 64 * 8 + 65536 + 64 * 15 * 8
+    # greedy per-chunk count) + draft-row partials 64*15*64*8 B (draft logits)
+    # + masses 64*64 sub-tiles*16 B + gathers 64*15*8 B
+    assert w == 256 + 64 * 16 * 64 * 8 + 64 * 15 * 64 * 8 + 65536 + 64 * 15 * 8
     # every region is 256-byte aligned, the smallest shape included
     assert _capi.verify_workspace_bytes(1, 0, 1, _capi.SPEC_DTYPE_BF16) == 3 * 256
     assert _capi.verify_workspace_bytes(64, 15, 129280, _capi.SPEC_DTYPE_F32) >= w
@@ -188,3 +189,25 @@ def test_acceptance_rejects_bad_arguments(kw, status):
 def test_acceptance_without_drafts_enqueues_nothing():
     # G == 0: nothing to compute, valid without draft or output pointers.
     assert _acc(G=0, draft=0, out_alpha=0) == 0
+
+
+def _logits(**kw):
+    args = dict(logits=Z, dtype_code=1, dl=Q, x=X, u=U, vlen=0, B=4, G=3, V=1000, T=1.0, out_acc=OA, out_tok=OT,
+                diag=None, ws=WS, ws_bytes=1 << 20, stream=0)
+    args.update(kw)
+    return _capi.spec_verify_logits(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dl=0), 1), (dict(dl=Q + 1), 8), (dict(x=0), 1), (dict(u=0), 1), (dict(logits=0), 1),
+    (dict(dtype_code=5), 4), (dict(B=0), 2), (dict(T=-1.0), 3), (dict(ws_bytes=100), 5),
+    (dict(B=65536, G=255, V=1 << 20), 6),
+])
+def test_verify_logits_rejects_bad_arguments(kw, status):
+    assert _logits(**kw) == status
+
+
+def test_verify_logits_nullable_draft():
+    # T == 0 (greedy) and G == 0 read no draft logits.
+    assert _logits(T=0.0, dl=0, u=0, ws_bytes=100) == 5
+    assert _logits(G=0, dl=0, x=0, ws_bytes=100) == 5
