@@ -156,10 +156,13 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated in HBM")
-    ap.add_argument("--workload", choices=("block", "greedy", "scheduled", "dcut"), default="block",
+    ap.add_argument("--workload", choices=("block", "greedy", "scheduled", "dcut", "logits", "acceptance"),
+                    default="block",
                     help="block: B=64 gamma=15 V=129280 T=1 (default); greedy: B=64 gamma=7 "
                          "V=152064 T=0; scheduled: spec_schedule then spec_verify, gamma=15 V=129280; "
-                         "dcut: spec_dcut then spec_verify_packed over the packed rows, gamma=15 V=129280")
+                         "dcut: spec_dcut then spec_verify_packed over the packed rows, gamma=15 V=129280; "
+                         "logits: spec_verify_logits with bf16 draft logits, B=64 gamma=15 V=129280 T=1; "
+                         "acceptance: spec_acceptance (alpha per position) on the same draft-logits workload")
     ap.add_argument("--batch", type=int, default=64, help="B of the scheduled and dcut workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=0)
@@ -190,6 +193,8 @@ def main():
         w = W.greedy()
     elif args.workload == "scheduled":
         w = W.scheduled(args.batch)
+    elif args.workload in ("logits", "acceptance"):
+        w = W.block_logits()
     else:
         w = W.ratio_budgeted(args.batch)
     B, G, V = w["B"], w["G"], w["V"]
@@ -212,6 +217,8 @@ def main():
 
     z0 = torch.from_numpy(w["logits"].view(np.int16)).to(dev).view(torch.bfloat16)
     q0, x0, u0 = to_dev(w["draft_probs"]), to_dev(w["draft_tokens"]), to_dev(w["uniforms"])
+    if w.get("draft_logits") is not None:        # draft logits travel in the q slot
+        q0 = torch.from_numpy(w["draft_logits"].view(np.int16)).to(dev).view(torch.bfloat16)
     clone = (lambda t: None if t is None else t.clone())
     sets = [(z0, q0, x0, u0)] + [tuple(clone(t) for t in (z0, q0, x0, u0)) for _ in range(args.sets - 1)]
     acc = torch.empty(B, dtype=torch.int32, device=dev)
@@ -245,9 +252,18 @@ def main():
             packed.append(zp)
         dcut = (conf, vlen, offs, ridx, rows, packed)
 
+    alpha = torch.empty(B, G, dtype=torch.float32, device=dev)
+
     def step(i, row_event=None):
         zz, qq, xx, uu = sets[i % len(sets)]
         vl = None
+        if args.workload == "logits":
+            sv.verify(zz, None, xx, uu, T, None, out_accepted=acc, out_tokens=tok, row_pass_event=row_event,
+                      draft_logits=qq)
+            return
+        if args.workload == "acceptance":
+            sv.acceptance(zz, qq, T, None, draft_is_logits=True, out_alpha=alpha)
+            return
         if dcut is not None:
             conf, vlen, offs, ridx, rows, packed = dcut
             sv.dcut(conf, w["ratios"], w["ratio_cost"], out_verify_len=vlen, out_row_offsets=offs, out_ratio=ridx,
@@ -271,12 +287,20 @@ def main():
         lens = dcut[1].cpu().numpy().astype(np.int64)
     else:
         lens = np.full(B, G)
-    n_rej = int((a < lens).sum()) if T > 0 else 0
+    n_rej = int((a < lens).sum()) if T > 0 and args.workload != "acceptance" else 0
     esize = 2
     algo = algorithmic_bytes(B, G, V, lens, n_rej, esize)
     if T == 0:                                   # no q rows, no uniforms
         algo = int((lens + 1).sum()) * V * esize + int(lens.sum()) * 4 + B * (4 + 4 * (G + 1))
     row_algo = row_pass_bytes(V, lens, esize)
+    if args.workload in ("logits", "acceptance"):
+        # draft rows 0..len_b-1 are read too; every q(x) and residual comes
+        # from rows already read, so no fp32 q row is compulsory
+        drafts = int(lens.sum()) * V * esize
+        row_algo = row_algo + drafts
+        algo = int((lens + 1).sum()) * V * esize + drafts + int(lens.sum()) * 8 + B * (4 + 4 + 4 * (G + 1))
+        if args.workload == "acceptance":          # one read of target row k and draft row k per position
+            row_algo = algo = 2 * int(lens.sum()) * V * esize
 
     for i in range(args.warmup):
         step(i)
@@ -303,7 +327,11 @@ def main():
     torch.cuda.synchronize()
     for i in range(K):
         hev.record(3 * i, sh)
-        step(i, row_event=hev.ev[3 * i + 1])
+        if args.workload == "acceptance":          # a single kernel: its own interval
+            step(i)
+            hev.record(3 * i + 1, sh)
+        else:
+            step(i, row_event=hev.ev[3 * i + 1])
         hev.record(3 * i + 2, sh)
     torch.cuda.synchronize()
     call = np.array([hev.ms(3 * i, 3 * i + 2) for i in range(K)])      # ms per call
@@ -327,6 +355,14 @@ def main():
         desc = (f"confidence-scheduled verification: spec_schedule (token budget {w['budget']}, "
                 f"cost 1 + 0.02 T) then spec_verify, B={B}, gamma=15, V=129280, bf16, T=1")
         kname = "spec_schedule + k_rows_sampled (time up to the row-pass event includes the scheduler)"
+    elif args.workload == "logits":
+        desc = ("draft-logits verification: B=64, gamma=15, V=129280, bf16 target logits (Zipf(1.1) over a "
+                "per-row permutation) and bf16 draft logits, q = softmax(draft logits / T) on the device, T=1")
+        kname = "k_rows_sampled (row pass over the target rows and the draft rows)"
+    elif args.workload == "acceptance":
+        desc = ("acceptance diagnostics: alpha = sum min(p, q) per position, B=64, gamma=15, V=129280, bf16 target "
+                "and draft logits, T=1 (two passes over each row pair)")
+        kname = "k_acceptance (one workgroup per position; algorithmic bytes = one read of each row pair)"
     else:
         r_idx = int(dcut[3].item())
         desc = (f"ratio-budgeted verification: spec_dcut (ratios {list(w['ratios'])}, cost 1 + 0.02 rho B (G+1); "
