@@ -15,12 +15,16 @@ schedule  confidence-scheduled verification depth (CumProd survival, greedy
           throughput-improving prefix extension under a token budget).
 acceptance  per-position acceptance overlap alpha = sum min(p, q) = 1 - TV,
           and verification with the draft distribution given as logits.
+calibration  Sequential Temperature Scaling (apply c^(1/T_k); the left-to-right
+          grid fit on the cumulative survival's 15-bin ECE) and the static
+          scheduler's fixed-length and threshold modes.
 dcut      ratio-budgeted depth (top-K scores for each ratio budget, the ratio
           that maximises estimated progress over profiled cost) and
           verification over densely packed target rows.
 
 Every function is pinned by a ``-m "not gpu"`` test (tests/test_oracle_pins.py,
-tests/test_oracle_dcut.py, tests/test_oracle_acceptance.py) against what the pages and the mathematics fix;
+tests/test_oracle_dcut.py, tests/test_oracle_acceptance.py,
+tests/test_oracle_calibration.py) against what the pages and the mathematics fix;
 none is "parity unpinned".
 """
 
@@ -37,3 +41,4 @@ from .verify import (  # noqa: F401
 from .schedule import survival, schedule, schedule_value, brute_force  # noqa: F401
 from . import dcut  # noqa: F401  (module: oracle.dcut.dcut, oracle.dcut.verify_packed, ...)
 from . import acceptance  # noqa: F401,E402
+from . import calibration  # noqa: F401,E402

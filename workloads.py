@@ -30,6 +30,11 @@ the design doc lists them):
              d = bf16(z + N(0, 0.75 * 1.05**k)) and samples x ~ softmax(d / T)
              (float64 from the stored bf16 values), so the draft distribution
              is exactly the softmax of the logits passed on.
+  calibration
+             N samples of the scheduled confidences and an acceptance length per
+             sample: draft k (given the earlier ones) is accepted when a uniform
+             falls below c^(1/T*_k), for a known per-position temperature T*
+             (the confidences are miscalibrated by T*, which a fit recovers).
   ratio_budgeted
              block logits and the scheduled confidences at B in {4, 16, 64};
              budget ratios (0.25, 0.5, 0.75, 1); the profiled cost of ratio rho
@@ -51,6 +56,7 @@ _STREAMS = {
     "verify_u": 4,
     "confidence": 5,
     "peaks": 6,
+    "labels": 7,
 }
 
 
@@ -243,3 +249,15 @@ def ratio_budgeted(B, seed=BASE_SEED + 6, G=15, V=129280, T=1.0):
     w["ratios"] = RATIOS
     w["ratio_cost"] = ratio_costs(B, G)
     return w
+
+
+def calibration(N, G=15, true_temps=None, seed=BASE_SEED + 8):
+    """(conf [N, G] float32, acc_len [N] int32, true_temps [G]): synthetic STS fitting data."""
+    if true_temps is None:
+        true_temps = np.array([1.0, 0.6, 1.5, 0.8, 2.0, 1.2, 0.5, 1.0, 1.8, 0.7, 1.4, 0.9, 1.6, 1.1, 0.8])[:G]
+    T = np.asarray(true_temps, np.float64)
+    conf = confidences(seed, N, G)
+    u = rng(seed, "labels").random((N, G))
+    ok = u < np.exp2(np.log2(conf.astype(np.float64)) / T[None, :])
+    acc_len = np.where(ok.all(axis=1), G, np.argmin(ok, axis=1)).astype(np.int32)
+    return conf, acc_len, T
