@@ -18,6 +18,12 @@
  *                       its keep depths and the packed row offsets.
  *   spec_acceptance     per-position acceptance overlap alpha = sum min(p, q)
  *                       (= 1 - TV), the expected acceptance of each draft.
+ *   spec_schedule_static  the static scheduler: a fixed length, or the leading
+ *                       drafts whose confidence exceeds a threshold.
+ *   spec_sts_fit        Sequential Temperature Scaling: per-position
+ *                       temperatures fitted left to right on acceptance data;
+ *                       spec_schedule, spec_dcut and spec_schedule_static
+ *                       apply them (calib_temps) as they load confidences.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -66,6 +72,17 @@ typedef enum { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 } spec_dtype_t;
  * the target's dtype whose softmax at the call's temperature is the draft
  * distribution. */
 typedef enum { SPEC_DRAFT_PROBS = 0, SPEC_DRAFT_LOGITS = 1 } spec_draft_kind_t;
+
+/* Modes of spec_schedule_static. */
+typedef enum { SPEC_STATIC_FIXED = 0, SPEC_STATIC_THRESHOLD = 1 } spec_static_mode_t;
+
+/*
+ * Calibration (every scheduler's calib_temps argument): NULL, or a host array
+ * of G finite, positive per-position temperatures T_k ("UraionSpec", section
+ * "Sequential Temperature Scaling").  Confidence c[b,k] is then read as
+ * c~ = float32(c^(1/T_k)), formed in double as 2^(log2(c) / T_k), before any
+ * other use.  Validated on the host (SPEC_ERR_BAD_SHAPE) and passed by value.
+ */
 
 /* A hipStream_t, passed opaquely so that this header needs no HIP include. */
 typedef void *spec_stream_t;
@@ -252,6 +269,7 @@ size_t spec_schedule_workspace_bytes(int32_t B, int32_t G);
  *   T + 1 > token_budget; theta = (tau + s[b,k]) / cost[T+1]; if theta > best
  *   keep it (len_b = k+1, T += 1, tau += s[b,k], best = theta), else stop.
  * The result is bit-identical to that sequential loop in float64.
+ * calib_temps: see "Calibration" above (NULL: confidences as given).
  *
  * Arguments (device pointers unless stated):
  *   confidence          [B, G] float, per-draft acceptance estimates in [0, 1].
@@ -267,6 +285,7 @@ size_t spec_schedule_workspace_bytes(int32_t B, int32_t G);
  */
 spec_status_t spec_schedule(const float *confidence, const float *cost_table, int32_t table_len,
                             int32_t B, int32_t G, int32_t token_budget, float eps,
+                            const float *calib_temps,
                             int32_t *out_verify_len, int32_t *out_total_tokens,
                             float *out_expected_tokens,
                             void *workspace, size_t workspace_bytes, spec_stream_t stream);
@@ -304,11 +323,12 @@ spec_status_t spec_schedule(const float *confidence, const float *cost_table, in
  *   out_ratio_index  [1] int32, device: r*.
  *   out_total_rows   [1] int32, device: K_{r*} = sum_b (n_b + 1).
  *   out_utility      [num_ratios] double, device, or NULL: U_r.
+ *   calib_temps      see "Calibration" above (applied before the clamp).
  * Needs no workspace.
  */
 spec_status_t spec_dcut(const float *confidence, int32_t B, int32_t G,
                         const float *ratios, const float *ratio_cost, int32_t num_ratios,
-                        int32_t *out_verify_len, int32_t *out_row_offsets,
+                        const float *calib_temps, int32_t *out_verify_len, int32_t *out_row_offsets,
                         int32_t *out_ratio_index, int32_t *out_total_rows,
                         double *out_utility, spec_stream_t stream);
 
@@ -336,6 +356,52 @@ spec_status_t spec_acceptance(const void *target_logits, spec_dtype_t target_dty
                               const void *draft, spec_draft_kind_t draft_kind,
                               const int32_t *verify_len, int32_t B, int32_t G, int32_t V,
                               float temperature, float *out_alpha, spec_stream_t stream);
+
+/*
+ * spec_schedule_static -- the static scheduler ("UraionSpec", the fallback
+ * scheduler's fixed-length and static-threshold modes; "breaking down dspark
+ * and its lineage", section "Verify smarter, not longer": threshold 0 is
+ * fixed-length verification).
+ *   SPEC_STATIC_FIXED:     len_b = min(max(fixed_len, 0), G) (confidence unused,
+ *                          may be NULL);
+ *   SPEC_STATIC_THRESHOLD: len_b = the number of leading drafts whose
+ *                          (calibrated) confidence exceeds threshold, i.e. the
+ *                          first k with c~[b,k] <= threshold, else G.
+ * Outputs (device): out_verify_len [B]; out_total_tokens [1] = sum (len_b + 1)
+ * or NULL; out_row_offsets [B+1] (the packed layout of spec_verify_packed) or
+ * NULL.  1 <= B <= SPEC_MAX_BATCH, 0 <= G <= SPEC_MAX_DRAFTS; threshold not NaN.
+ */
+spec_status_t spec_schedule_static(const float *confidence, int32_t B, int32_t G, spec_static_mode_t mode,
+                                   int32_t fixed_len, float threshold, const float *calib_temps,
+                                   int32_t *out_verify_len, int32_t *out_total_tokens,
+                                   int32_t *out_row_offsets, spec_stream_t stream);
+
+/*
+ * spec_sts_fit -- Sequential Temperature Scaling fit ("UraionSpec", section
+ * "Sequential Temperature Scaling"): for k = 0..G-1 in order, over the grid
+ * temps[0..num_temps-1], the expected calibration error with `bins`
+ * equal-width bins on [0, 1] of a_n(T) = prefix_n * c[n,k]^(1/T) against the
+ * cumulative labels y_n = [acc_len[n] > k] is
+ *   ECE(T) = (1/N) sum_bins |sum_{n in bin} a_n - sum_{n in bin} y_n|,
+ *   bin = min(floor(bins * a), bins - 1);
+ * out_temps[k] = the first grid point with the least ECE, and prefix_n gains
+ * c[n,k]^(1/T_k) (prefix starts at 1; powers in double as 2^(log2(c)/T)).
+ * Confidences are clamped into [0, 1] (NaN as 0).  Prediction sums are exact
+ * in 2^-40 fixed point, so the result does not depend on the order of
+ * accumulation.  The usual grid is 100 points, linspace(0.1, 10, 100), with
+ * 15 bins.
+ *
+ * Arguments: confidence [N, G] float and acc_len [N] int32 (accepted drafts per
+ * sample), device; temps host, each finite and > 0; 1 <= N < 2^23,
+ * 1 <= num_temps <= 128, 1 <= bins <= 32, num_temps * bins <= 2730;
+ * out_temps [G] float, device; workspace device, 256-byte aligned, at least
+ * spec_sts_fit_workspace_bytes(N, G, num_temps, bins) (0 on invalid shapes).
+ * 2 launches per position.
+ */
+size_t spec_sts_fit_workspace_bytes(int32_t N, int32_t G, int32_t num_temps, int32_t bins);
+spec_status_t spec_sts_fit(const float *confidence, const int32_t *acc_len, int32_t N, int32_t G,
+                           const float *temps, int32_t num_temps, int32_t bins, float *out_temps,
+                           void *workspace, size_t workspace_bytes, spec_stream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *spec_status_string(spec_status_t status);

@@ -17,7 +17,8 @@ import torch
 from . import _capi
 from ._capi import SpecError, SPEC_DTYPE_BF16, SPEC_DTYPE_F32  # noqa: F401
 
-__all__ = ["verify", "verify_packed", "schedule", "dcut", "acceptance", "verify_workspace_bytes", "SpecError", "load"]
+__all__ = ["verify", "verify_packed", "schedule", "dcut", "acceptance", "schedule_static", "sts_fit",
+           "verify_workspace_bytes", "SpecError", "load"]
 
 _workspaces = {}
 
@@ -145,7 +146,7 @@ def verify(target_logits, draft_probs, draft_tokens, uniforms, temperature, veri
 
 
 def schedule(confidence, cost_table, token_budget, eps=0.0, *, out_verify_len=None, out_total=None,
-             out_expected=None):
+             out_expected=None, calib_temps=None):
     """Choose per-request verify lengths.  Returns (verify_len [B], T [1], tau [1]) device tensors."""
     c = confidence
     if not isinstance(c, torch.Tensor) or c.dim() != 2:
@@ -166,7 +167,7 @@ def schedule(confidence, cost_table, token_budget, eps=0.0, *, out_verify_len=No
     st = _capi.spec_schedule(_ptr(c, f32, dev, "confidence"), _ptr(cost_table, f32, dev, "cost_table"), L, B, G,
                              int(token_budget), float(eps), _ptr(out_verify_len, i32, dev, "out_verify_len"),
                              _ptr(out_total, i32, dev, "out_total"), _ptr(out_expected, f32, dev, "out_expected"),
-                             0, 0, stream)
+                             0, 0, stream, calib=calib_temps)
     if st != _capi.SPEC_OK:
         raise SpecError(st, "spec_schedule")
     return out_verify_len, out_total, out_expected
@@ -235,7 +236,7 @@ def verify_packed(packed_logits, row_offsets, draft_probs, draft_tokens, uniform
 
 
 def dcut(confidence, ratios, ratio_cost, *, out_verify_len=None, out_row_offsets=None, out_ratio=None,
-         out_rows=None, out_utility=None, utility=True):
+         out_rows=None, out_utility=None, utility=True, calib_temps=None):
     """Ratio-budgeted depth.  ratios, ratio_cost: host sequences of floats (the
     profiled cost of each ratio at this batch size).  Returns device tensors
     (verify_len [B], row_offsets [B+1], ratio_index [1], total_rows [1],
@@ -268,7 +269,7 @@ def dcut(confidence, ratios, ratio_cost, *, out_verify_len=None, out_row_offsets
                          _ptr(out_row_offsets, i32, dev, "out_row_offsets"), _ptr(out_ratio, i32, dev, "out_ratio"),
                          _ptr(out_rows, i32, dev, "out_rows"),
                          _ptr(out_utility, torch.float64, dev, "out_utility") if out_utility is not None else 0,
-                         stream)
+                         stream, calib=calib_temps)
     if st != _capi.SPEC_OK:
         raise SpecError(st, "spec_dcut")
     return out_verify_len, out_row_offsets, out_ratio, out_rows, out_utility
@@ -300,3 +301,48 @@ def acceptance(target_logits, draft, temperature, verify_len=None, *, draft_is_l
     if st != _capi.SPEC_OK:
         raise SpecError(st, "spec_acceptance")
     return out_alpha
+
+
+def schedule_static(confidence, B=None, G=None, *, fixed_len=None, threshold=None, calib_temps=None,
+                    row_offsets=True):
+    """Static scheduler: fixed_len (every request min(L, G) drafts) or threshold
+    (leading drafts whose confidence exceeds it).  Returns device tensors
+    (verify_len [B], total [1], row_offsets [B+1] or None)."""
+    if (fixed_len is None) == (threshold is None):
+        raise ValueError("give exactly one of fixed_len and threshold")
+    if confidence is not None:
+        dev = confidence.device
+        B, G = confidence.shape
+    else:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    i32 = torch.int32
+    out_len = torch.empty(B, dtype=i32, device=dev)
+    out_T = torch.empty(1, dtype=i32, device=dev)
+    out_off = torch.empty(B + 1, dtype=i32, device=dev) if row_offsets else None
+    mode = _capi.SPEC_STATIC_FIXED if fixed_len is not None else _capi.SPEC_STATIC_THRESHOLD
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = _capi.spec_schedule_static(_ptr(confidence, torch.float32, dev, "confidence"), B, G, mode,
+                                    int(fixed_len or 0), float(threshold or 0.0), calib_temps,
+                                    out_len.data_ptr(), out_T.data_ptr(),
+                                    out_off.data_ptr() if out_off is not None else 0, stream)
+    if st != _capi.SPEC_OK:
+        raise SpecError(st, "spec_schedule_static")
+    return out_len, out_T, out_off
+
+
+def sts_fit(confidence, acc_len, temps, bins=15):
+    """Sequential Temperature Scaling fit.  confidence [N, G] fp32, acc_len [N]
+    int32 (device); temps: host sequence (the grid).  Returns out_temps [G] fp32."""
+    dev = confidence.device
+    N, G = confidence.shape
+    temps = [float(t) for t in temps]
+    nbytes = _capi.sts_fit_workspace_bytes(N, G, len(temps), bins)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty(G, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = _capi.spec_sts_fit(_ptr(confidence, torch.float32, dev, "confidence"),
+                            _ptr(acc_len, torch.int32, dev, "acc_len"), N, G, temps, bins, out.data_ptr(),
+                            ws.data_ptr(), ws.numel(), stream)
+    if st != _capi.SPEC_OK:
+        raise SpecError(st, "spec_sts_fit")
+    return out

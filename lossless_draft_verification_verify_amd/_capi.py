@@ -26,6 +26,8 @@ SPEC_DTYPE_F32 = 0
 SPEC_DTYPE_BF16 = 1
 SPEC_DRAFT_PROBS = 0
 SPEC_DRAFT_LOGITS = 1
+SPEC_STATIC_FIXED = 0
+SPEC_STATIC_THRESHOLD = 1
 
 # Every symbol the header declares.
 EXPORTS = (
@@ -38,6 +40,9 @@ EXPORTS = (
     "spec_verify_logits",
     "spec_dcut",
     "spec_acceptance",
+    "spec_schedule_static",
+    "spec_sts_fit_workspace_bytes",
+    "spec_sts_fit",
     "spec_status_string",
 )
 MAX_RATIOS = 8
@@ -82,7 +87,8 @@ def load():
     lib.spec_verify_launches.restype = i32
     lib.spec_schedule_workspace_bytes.argtypes = [i32, i32]
     lib.spec_schedule_workspace_bytes.restype = sz
-    lib.spec_schedule.argtypes = [vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
+    fp = ctypes.POINTER(f32)
+    lib.spec_schedule.argtypes = [vp, vp, i32, i32, i32, i32, f32, fp, vp, vp, vp, vp, sz, vp]
     lib.spec_schedule.restype = ctypes.c_int
     lib.spec_verify_packed.argtypes = [vp, ctypes.c_int, i32, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp,
                                        ctypes.POINTER(DiagT), vp, sz, vp]
@@ -90,10 +96,16 @@ def load():
     lib.spec_verify_logits.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp,
                                        ctypes.POINTER(DiagT), vp, sz, vp]
     lib.spec_verify_logits.restype = ctypes.c_int
-    lib.spec_dcut.argtypes = [vp, i32, i32, ctypes.POINTER(f32), ctypes.POINTER(f32), i32, vp, vp, vp, vp, vp, vp]
+    lib.spec_dcut.argtypes = [vp, i32, i32, fp, fp, i32, fp, vp, vp, vp, vp, vp, vp]
     lib.spec_dcut.restype = ctypes.c_int
     lib.spec_acceptance.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, i32, i32, i32, f32, vp, vp]
     lib.spec_acceptance.restype = ctypes.c_int
+    lib.spec_schedule_static.argtypes = [vp, i32, i32, ctypes.c_int, i32, f32, fp, vp, vp, vp, vp]
+    lib.spec_schedule_static.restype = ctypes.c_int
+    lib.spec_sts_fit_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.spec_sts_fit_workspace_bytes.restype = sz
+    lib.spec_sts_fit.argtypes = [vp, vp, i32, i32, fp, i32, i32, vp, vp, sz, vp]
+    lib.spec_sts_fit.restype = ctypes.c_int
     lib.spec_status_string.argtypes = [ctypes.c_int]
     lib.spec_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -124,10 +136,18 @@ def spec_verify(logits, dtype_code, q, x, u, vlen, B, G, V, T, out_acc, out_tok,
                                   ws or None, ws_bytes, stream or None))
 
 
-def spec_schedule(conf, cost, table_len, B, G, budget, eps, out_len, out_T, out_tau, ws, ws_bytes, stream):
+def _floats(v):
+    """A host float array for the C ABI (None = NULL)."""
+    if v is None:
+        return None
+    return (ctypes.c_float * max(1, len(v)))(*[float(t) for t in v])
+
+
+def spec_schedule(conf, cost, table_len, B, G, budget, eps, out_len, out_T, out_tau, ws, ws_bytes, stream,
+                  calib=None):
     return int(load().spec_schedule(conf or None, cost or None, table_len, B, G, budget, ctypes.c_float(eps),
-                                    out_len or None, out_T or None, out_tau or None, ws or None, ws_bytes,
-                                    stream or None))
+                                    _floats(calib), out_len or None, out_T or None, out_tau or None, ws or None,
+                                    ws_bytes, stream or None))
 
 
 def spec_verify_packed(logits, dtype_code, rows, roff, q, x, u, B, G, V, T, out_acc, out_tok, diag, ws, ws_bytes,
@@ -139,15 +159,12 @@ def spec_verify_packed(logits, dtype_code, rows, roff, q, x, u, B, G, V, T, out_
                                          ws or None, ws_bytes, stream or None))
 
 
-def spec_dcut(conf, B, G, ratios, costs, out_len, out_off, out_ratio, out_rows, out_util, stream):
-    """Raw call; `ratios` and `costs` are host sequences of floats (None = NULL)."""
-    def arr(v):
-        if v is None:
-            return None
-        return (ctypes.c_float * max(1, len(v)))(*[float(t) for t in v])
+def spec_dcut(conf, B, G, ratios, costs, out_len, out_off, out_ratio, out_rows, out_util, stream, calib=None):
+    """Raw call; `ratios`, `costs` and `calib` are host sequences of floats (None = NULL)."""
     n = len(ratios) if ratios is not None else (len(costs) if costs is not None else 0)
-    return int(load().spec_dcut(conf or None, B, G, arr(ratios), arr(costs), n, out_len or None, out_off or None,
-                                out_ratio or None, out_rows or None, out_util or None, stream or None))
+    return int(load().spec_dcut(conf or None, B, G, _floats(ratios), _floats(costs), n, _floats(calib),
+                                out_len or None, out_off or None, out_ratio or None, out_rows or None,
+                                out_util or None, stream or None))
 
 
 def spec_acceptance(logits, dtype_code, draft, draft_kind, vlen, B, G, V, T, out_alpha, stream):
@@ -160,3 +177,18 @@ def spec_verify_logits(logits, dtype_code, dl, x, u, vlen, B, G, V, T, out_acc, 
     return int(load().spec_verify_logits(logits or None, dtype_code, dl or None, x or None, u or None, vlen or None,
                                          B, G, V, ctypes.c_float(T), out_acc or None, out_tok or None, d,
                                          ws or None, ws_bytes, stream or None))
+
+
+def spec_schedule_static(conf, B, G, mode, fixed_len, tau, calib, out_len, out_T, out_off, stream):
+    return int(load().spec_schedule_static(conf or None, B, G, mode, fixed_len, ctypes.c_float(tau), _floats(calib),
+                                           out_len or None, out_T or None, out_off or None, stream or None))
+
+
+def sts_fit_workspace_bytes(N, G, nt, bins):
+    return int(load().spec_sts_fit_workspace_bytes(N, G, nt, bins))
+
+
+def spec_sts_fit(conf, acc_len, N, G, temps, bins, out_temps, ws, ws_bytes, stream):
+    n = len(temps) if temps is not None else 0
+    return int(load().spec_sts_fit(conf or None, acc_len or None, N, G, _floats(temps), n, bins, out_temps or None,
+                                   ws or None, ws_bytes, stream or None))

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = ["capi.cpp", "verify_kernels.hip", "schedule_kernel.hip", "acceptance_kernel.hip"]
+SOURCES = ["capi.cpp", "verify_kernels.hip", "schedule_kernel.hip", "acceptance_kernel.hip",
+           "calibration_kernel.hip"]
 ARCH = "gfx950"
 
 # -ffp-contract=off: every fp expression is evaluated as written (the final

@@ -68,6 +68,19 @@ long resident_capacity(int dev, bool az, int es) {
     return long(o) * d.cus;
 }
 
+// Host-validated STS temperatures (NULL: none) into the kernel arguments.
+spec_status_t set_calib(sv::Calib &cal, const float *temps, int32_t G) {
+    cal.on = 0;
+    if (!temps) return SPEC_OK;
+    if (G > sv::kMaxDrafts) return SPEC_ERR_UNSUPPORTED;
+    for (int k = 0; k < G; ++k) {
+        if (!std::isfinite(temps[k]) || !(temps[k] > 0.0f)) return SPEC_ERR_BAD_SHAPE;
+        cal.temp[k] = temps[k];
+    }
+    cal.on = 1;
+    return SPEC_OK;
+}
+
 // Greedy launch plan: whether the per-request workgroups share the row
 // launch (they wait for their rows, so they stay below half the resident
 // capacity).  -1 on a device query failure.
@@ -285,9 +298,9 @@ int32_t spec_verify_launches(int32_t B, int32_t G, int32_t V, spec_dtype_t dt, f
 size_t spec_schedule_workspace_bytes(int32_t, int32_t) { return 0; }
 
 spec_status_t spec_schedule(const float *confidence, const float *cost_table, int32_t table_len, int32_t B,
-                            int32_t G, int32_t token_budget, float eps, int32_t *out_verify_len,
-                            int32_t *out_total_tokens, float *out_expected_tokens, void *workspace,
-                            size_t workspace_bytes, spec_stream_t stream) {
+                            int32_t G, int32_t token_budget, float eps, const float *calib_temps,
+                            int32_t *out_verify_len, int32_t *out_total_tokens, float *out_expected_tokens,
+                            void *workspace, size_t workspace_bytes, spec_stream_t stream) {
     (void)workspace;
     (void)workspace_bytes;
     if (B < 1 || G < 0 || table_len < 1) return SPEC_ERR_BAD_SHAPE;
@@ -300,6 +313,7 @@ spec_status_t spec_schedule(const float *confidence, const float *cost_table, in
         !aligned(out_total_tokens, 4) || !aligned(out_expected_tokens, 4))
         return SPEC_ERR_MISALIGNED;
     sv::ScheduleArgs a = {};
+    if (const spec_status_t cs = set_calib(a.cal, calib_temps, G); cs != SPEC_OK) return cs;
     a.conf = confidence;
     a.cost = cost_table;
     a.B = B;
@@ -310,6 +324,80 @@ spec_status_t spec_schedule(const float *confidence, const float *cost_table, in
     a.out_T = out_total_tokens;
     a.out_tau = out_expected_tokens;
     return sv::launch_schedule(a, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+}
+
+spec_status_t spec_schedule_static(const float *confidence, int32_t B, int32_t G, spec_static_mode_t mode,
+                                   int32_t fixed_len, float threshold, const float *calib_temps,
+                                   int32_t *out_verify_len, int32_t *out_total_tokens,
+                                   int32_t *out_row_offsets, spec_stream_t stream) {
+    if (B < 1 || G < 0) return SPEC_ERR_BAD_SHAPE;
+    if (B > SPEC_MAX_BATCH || G > SPEC_MAX_DRAFTS) return SPEC_ERR_UNSUPPORTED;
+    if (mode != SPEC_STATIC_FIXED && mode != SPEC_STATIC_THRESHOLD) return SPEC_ERR_BAD_SHAPE;
+    if (mode == SPEC_STATIC_THRESHOLD && std::isnan(threshold)) return SPEC_ERR_BAD_SHAPE;
+    if (!out_verify_len || (mode == SPEC_STATIC_THRESHOLD && G > 0 && !confidence)) return SPEC_ERR_NULL_POINTER;
+    if (!aligned(confidence, 4) || !aligned(out_verify_len, 4) || !aligned(out_total_tokens, 4) ||
+        !aligned(out_row_offsets, 4))
+        return SPEC_ERR_MISALIGNED;
+    sv::StaticArgs a = {};
+    if (const spec_status_t cs = set_calib(a.cal, calib_temps, G); cs != SPEC_OK) return cs;
+    a.conf = confidence;
+    a.B = B;
+    a.G = G;
+    a.mode = int32_t(mode);
+    a.len = fixed_len;
+    a.tau = threshold;
+    a.out_len = out_verify_len;
+    a.out_T = out_total_tokens;
+    a.out_off = out_row_offsets;
+    return sv::launch_static(a, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+}
+
+namespace {
+int fit_groups(int32_t N) { return int(std::min<int64_t>(256, (int64_t(N) + sv::kFitThreads - 1) / sv::kFitThreads)); }
+bool fit_shape_ok(int32_t N, int32_t G, int32_t nt, int32_t bins) {
+    return N >= 1 && N < (1 << 23) && G >= 0 && G <= SPEC_MAX_DRAFTS && nt >= 1 && nt <= sv::kFitMaxTemps &&
+           bins >= 1 && bins <= sv::kFitMaxBins && size_t(nt) * bins * 3 * 8 <= 65536;
+}
+}  // namespace
+
+size_t spec_sts_fit_workspace_bytes(int32_t N, int32_t G, int32_t num_temps, int32_t bins) {
+    if (!fit_shape_ok(N, G, num_temps, bins)) return 0;
+    return sv::align256(size_t(N) * 8) + size_t(fit_groups(N)) * num_temps * bins * 3 * 8;
+}
+
+spec_status_t spec_sts_fit(const float *confidence, const int32_t *acc_len, int32_t N, int32_t G,
+                           const float *temps, int32_t num_temps, int32_t bins, float *out_temps, void *workspace,
+                           size_t workspace_bytes, spec_stream_t stream) {
+    if (!fit_shape_ok(N, G, num_temps, bins)) {
+        if (N >= (1 << 23) || G > SPEC_MAX_DRAFTS) return SPEC_ERR_UNSUPPORTED;
+        return SPEC_ERR_BAD_SHAPE;
+    }
+    if (!temps) return SPEC_ERR_NULL_POINTER;
+    sv::FitArgs a = {};
+    for (int t = 0; t < num_temps; ++t) {
+        if (!std::isfinite(temps[t]) || !(temps[t] > 0.0f)) return SPEC_ERR_BAD_SHAPE;
+        a.temps[t] = temps[t];
+    }
+    if (G == 0) return SPEC_OK;
+    if (!confidence || !acc_len || !out_temps || !workspace) return SPEC_ERR_NULL_POINTER;
+    if (!aligned(confidence, 4) || !aligned(acc_len, 4) || !aligned(out_temps, 4) || !aligned(workspace, 256))
+        return SPEC_ERR_MISALIGNED;
+    if (workspace_bytes < spec_sts_fit_workspace_bytes(N, G, num_temps, bins)) return SPEC_ERR_WORKSPACE_TOO_SMALL;
+    a.conf = confidence;
+    a.acc_len = acc_len;
+    a.out_temps = out_temps;
+    a.prefix = static_cast<double *>(workspace);
+    a.part = reinterpret_cast<int64_t *>(static_cast<unsigned char *>(workspace) + sv::align256(size_t(N) * 8));
+    a.N = N;
+    a.G = G;
+    a.nt = num_temps;
+    a.bins = bins;
+    a.nwg = fit_groups(N);
+    for (int k = 0; k < G; ++k) {
+        a.k = k;
+        if (sv::launch_fit_accumulate(a, stream) != 0 || sv::launch_fit_choose(a, stream) != 0) return SPEC_ERR_DEVICE;
+    }
+    return SPEC_OK;
 }
 
 spec_status_t spec_acceptance(const void *target_logits, spec_dtype_t target_dtype, const void *draft,
@@ -344,7 +432,8 @@ spec_status_t spec_acceptance(const void *target_logits, spec_dtype_t target_dty
 }
 
 spec_status_t spec_dcut(const float *confidence, int32_t B, int32_t G, const float *ratios,
-                        const float *ratio_cost, int32_t num_ratios, int32_t *out_verify_len,
+                        const float *ratio_cost, int32_t num_ratios, const float *calib_temps,
+                        int32_t *out_verify_len,
                         int32_t *out_row_offsets, int32_t *out_ratio_index, int32_t *out_total_rows,
                         double *out_utility, spec_stream_t stream) {
     if (B < 1 || G < 0) return SPEC_ERR_BAD_SHAPE;
@@ -353,6 +442,7 @@ spec_status_t spec_dcut(const float *confidence, int32_t B, int32_t G, const flo
     if (num_ratios < 1 || num_ratios > SPEC_MAX_RATIOS) return SPEC_ERR_BAD_SHAPE;
     if (!ratios || !ratio_cost) return SPEC_ERR_NULL_POINTER;
     sv::DcutArgs a = {};
+    if (const spec_status_t cs = set_calib(a.cal, calib_temps, G); cs != SPEC_OK) return cs;
     for (int r = 0; r < num_ratios; ++r) {
         const float rho = ratios[r], c = ratio_cost[r];
         if (!std::isfinite(rho) || !(rho > 0.0f) || rho > 1.0f) return SPEC_ERR_BAD_SHAPE;

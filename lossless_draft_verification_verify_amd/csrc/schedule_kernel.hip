@@ -164,6 +164,16 @@ __device__ __forceinline__ void cx_in_wave(double &s, int &id, int tid, int lane
     cx_wave<1>(s, id, tid, lane, size);
 }
 
+// Calibrated confidence ("UraionSpec", Sequential Temperature Scaling):
+// float32(c^(1/T)) formed as 2^(log2(c) / T) in double (0 -> 0, 1 -> 1).
+__device__ __forceinline__ float calibrate(float c, float T) {
+    return float(exp2(log2(double(c)) / double(T)));
+}
+__device__ __forceinline__ float conf_at(const float *conf, const Calib &cal, int i, int G) {
+    const float c = conf[i];
+    return cal.on ? calibrate(c, cal.temp[i % G]) : c;
+}
+
 // Sorting slot i of Np: its survival when it is a candidate, else -inf padding.
 __device__ __forceinline__ void slot_key(const SchedSmem &sh, int i, int N, int B, int G, double eps, double &s,
                                          int &id) {
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
     const int mt_max = min(N, a.budget - B);          // kept drafts never exceed this
 
     // 1. every input the scan can read, in one round trip.
-    for (int i = tid; i < N; i += nth) sh.u.conf[i] = double(a.conf[i]);
+    for (int i = tid; i < N; i += nth) sh.u.conf[i] = double(conf_at(a.conf, a.cal, i, G));
     for (int i = tid; i <= mt_max; i += nth) sh.cost[i] = a.cost[B + i];
     __syncthreads();
 
@@ -432,7 +442,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_dcut(DcutArgs a) {
     const int B = a.B, G = a.G, N = B * G;
 
     for (int i = tid; i < N; i += nth) {
-        const double c = double(a.conf[i]);
+        const double c = double(conf_at(a.conf, a.cal, i, G));
         sh.u.conf[i] = (c > 0.0) ? fmin(c, 1.0) : 0.0;   // NaN -> 0
     }
     __syncthreads();
@@ -580,6 +590,50 @@ int launch_schedule(const ScheduleArgs &a, void *stream) {
     while (Np < a.B * a.G) Np <<= 1;
     const int threads = (Np <= kRegSort) ? (Np < 64 ? 64 : Np) : kMaxThreads;
     hipLaunchKernelGGL(k_schedule, dim3(1), dim3(threads), 0, static_cast<hipStream_t>(stream), a);
+    return int(hipGetLastError());
+}
+
+// Static scheduler (one workgroup): each thread a contiguous run of
+// requests; fixed length, or the leading (calibrated) confidences above tau;
+// then the total and the packed row offsets by a block scan.
+__global__ __launch_bounds__(kMaxThreads) void k_static(StaticArgs a) {
+    __shared__ int wsum[kMaxThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nth = blockDim.x;
+    const int B = a.B, G = a.G;
+    const int per = (B + nth - 1) / nth;
+    const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
+    const int fixed = min(max(a.len, 0), G);
+    int local = 0;
+    for (int b = b0; b < b1; ++b) {
+        int n = fixed;
+        if (a.mode == 1) {
+            n = 0;
+            while (n < G && conf_at(a.conf, a.cal, b * G + n, G) > a.tau) ++n;
+        }
+        a.out_len[b] = n;
+        local += n + 1;
+    }
+    const int incl = wave_scan_i(local);
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int o = incl - local;
+    for (int v = 0; v < wv; ++v) o += wsum[v];
+    if (a.out_off) {
+        for (int b = b0; b < b1; ++b) {
+            a.out_off[b] = o;
+            o += a.out_len[b] + 1;     // this thread's own store, read back
+        }
+    }
+    if (tid == nth - 1) {
+        int tot = 0;
+        for (int v = 0; v < (nth >> 6); ++v) tot += wsum[v];
+        if (a.out_T) a.out_T[0] = tot;
+        if (a.out_off) a.out_off[B] = tot;
+    }
+}
+
+int launch_static(const StaticArgs &a, void *stream) {
+    hipLaunchKernelGGL(k_static, dim3(1), dim3(kMaxThreads), 0, static_cast<hipStream_t>(stream), a);
     return int(hipGetLastError());
 }
 

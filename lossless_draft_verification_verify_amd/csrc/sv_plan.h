@@ -99,11 +99,20 @@ int launch_requests_sampled(const VerifyArgs &a, bool aligned_z, bool aligned_q,
 int launch_verify_greedy(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
 int greedy_occupancy(bool aligned_z, int esize, int *blocks_per_cu);
 
+constexpr int kMaxDrafts = 255;
+// Sequential Temperature Scaling, applied as confidences are loaded:
+// c~ = float32(2^(log2(c) / T_k)) in double, when calib is set.
+struct Calib {
+    int32_t on;
+    float temp[kMaxDrafts];
+};
+
 struct ScheduleArgs {
     const float *conf;
     const float *cost;
     int32_t B, G, budget;
     float eps;
+    Calib cal;
     int32_t *out_len;
     int32_t *out_T;
     float *out_tau;
@@ -114,6 +123,7 @@ constexpr int kMaxRatios = 8;
 struct DcutArgs {
     const float *conf;
     int32_t B, G, R;
+    Calib cal;
     float cost[kMaxRatios];   // profiled cost of each ratio at this batch size, in the caller's order
     int32_t keep[kMaxRatios]; // drafts kept by each ratio: K_rho - B
     int32_t *out_len;         // [B]
@@ -123,6 +133,33 @@ struct DcutArgs {
     double *out_utility;      // [R] or NULL
 };
 int launch_dcut(const DcutArgs &a, void *stream);
+
+// Static scheduler: fixed length (mode 0) or leading confidences above tau (mode 1).
+struct StaticArgs {
+    const float *conf;
+    int32_t B, G, mode, len;
+    float tau;
+    Calib cal;
+    int32_t *out_len;         // [B]
+    int32_t *out_T;           // [1] sum of (len + 1), or NULL
+    int32_t *out_off;         // [B+1] packed row offsets, or NULL
+};
+int launch_static(const StaticArgs &a, void *stream);
+
+// Sequential Temperature Scaling fit, one position per pair of launches.
+struct FitArgs {
+    const float *conf;        // [N, G]
+    const int32_t *acc_len;   // [N]
+    float *out_temps;         // [G]
+    double *prefix;           // workspace [N]: calibrated survival of the positions fitted so far
+    int64_t *part;            // workspace [nwg][nt][bins][3]: count, labels, fixed-point predictions
+    int32_t N, G, nt, bins, nwg, k;
+    float temps[128];         // the grid
+};
+constexpr int kFitMaxTemps = 128, kFitMaxBins = 32, kFitThreads = 1024;
+constexpr double kFitScale = 1099511627776.0;   // 2^40: fixed-point unit of the prediction sums
+int launch_fit_accumulate(const FitArgs &a, void *stream);
+int launch_fit_choose(const FitArgs &a, void *stream);
 
 struct AcceptArgs {
     const void *z;            // [B, G+1, V] target logits

@@ -23,13 +23,15 @@ Readings (also in DESIGN.md):
   cumulative label is 1 when at least k+1 drafts were accepted (acc_len > k).
 * c~ = float32(2^(log2(c) / T)), the power formed in float64 and rounded to
   the float32 that the schedulers read.  c = 0 gives 0, c = 1 gives 1.
-* The grid is numpy.linspace(0.1, 10.0, 100), step 0.1 with T = 1 on it.
-  Equal ECE keeps the first (smallest) T.
+* The grid is numpy.linspace(0.1, 10.0, 100), step 0.1 with T = 1 on it, each
+  point taken as the float32 the library is given.  Equal ECE keeps the first
+  (smallest) T.
 * ECE over 15 equal-width bins on [0, 1]: bin = min(floor(15 a), 14).
   ECE = (1/N) sum_bins |sum_{i in bin} a_i - sum_{i in bin} y_i|, the
   count-weighted gap between mean prediction and mean label.  The survival
   used for later positions is the float64 product of the fitted powers, not
   rounded to float32.
+* The fit takes confidences clamped into [0, 1] (NaN as 0).
 * Static threshold: a request keeps its leading drafts whose (calibrated)
   confidence exceeds tau.  len_b = the first k with c~[b, k] <= tau, else G.
 * Fixed length: len_b = min(L, G) for every request.
@@ -80,9 +82,10 @@ def sts_fit(conf, acc_len, temps=None, bins=15, return_ece=False):
     position if return_ece.
     """
     c = np.asarray(conf, np.float32).astype(np.float64)
+    c = np.clip(np.where(np.isnan(c), 0.0, c), 0.0, 1.0)
     L = np.asarray(acc_len, np.int64)
     N, G = c.shape
-    temps = grid() if temps is None else np.asarray(temps, np.float64)
+    temps = np.asarray(grid() if temps is None else temps, np.float32).astype(np.float64)
     prefix = np.ones(N, np.float64)
     fitted = np.empty(G, np.float64)
     table = np.empty((G, len(temps)), np.float64)

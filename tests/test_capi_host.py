@@ -211,3 +211,58 @@ def test_verify_logits_nullable_draft():
     # T == 0 (greedy) and G == 0 read no draft logits.
     assert _logits(T=0.0, dl=0, u=0, ws_bytes=100) == 5
     assert _logits(G=0, dl=0, x=0, ws_bytes=100) == 5
+
+
+@pytest.mark.parametrize("calib", [[1.0, 0.0, 1.0], [1.0, -2.0, 1.0], [float("nan"), 1.0, 1.0],
+                                   [1.0, float("inf"), 1.0]])
+def test_calibration_temperatures_validated(calib):
+    assert _sched(G=3, calib=calib) == 2
+    assert _dcut(G=3, calib=calib) == 2
+    assert _capi.spec_schedule_static(Q, 4, 3, 1, 0, 0.5, calib, OA, OT, 0, 0) == 2
+
+
+def _static(**kw):
+    args = dict(conf=Q, B=4, G=15, mode=1, fixed_len=0, tau=0.5, calib=None, out_len=OA, out_T=OT, out_off=X,
+                stream=0)
+    args.update(kw)
+    return _capi.spec_schedule_static(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 2), (dict(G=-1), 2), (dict(mode=2), 2), (dict(tau=float("nan")), 2),
+    (dict(B=65537), 6), (dict(G=256), 6),
+    (dict(out_len=0), 1), (dict(conf=0), 1),
+    (dict(conf=Q + 2), 8), (dict(out_off=X + 1), 8),
+])
+def test_static_rejects_bad_arguments(kw, status):
+    assert _static(**kw) == status
+
+
+def test_static_fixed_needs_no_confidence():
+    # passes validation; the launch itself fails only for lack of a device, never as NULL (1)
+    assert _static(mode=0, conf=0, fixed_len=3) != 1
+
+
+def _fit(**kw):
+    args = dict(conf=Q, acc_len=X, N=1000, G=4, temps=[0.5, 1.0, 2.0], bins=15, out_temps=OA, ws=WS,
+                ws_bytes=1 << 24, stream=0)
+    args.update(kw)
+    return _capi.spec_sts_fit(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), 2), (dict(G=-1), 2), (dict(bins=0), 2), (dict(bins=33), 2), (dict(temps=[]), 2),
+    (dict(temps=[1.0] * 129), 2), (dict(temps=[1.0, 0.0]), 2), (dict(temps=[float("nan")]), 2),
+    (dict(N=1 << 23), 6), (dict(G=256), 6),
+    (dict(conf=0), 1), (dict(acc_len=0), 1), (dict(out_temps=0), 1), (dict(ws=0), 1), (dict(temps=None), 2),
+    (dict(ws=WS + 8), 8), (dict(ws_bytes=100), 5),
+])
+def test_sts_fit_rejects_bad_arguments(kw, status):
+    assert _fit(**kw) == status
+
+
+def test_sts_fit_workspace_query():
+    assert _capi.sts_fit_workspace_bytes(1000, 4, 100, 15) == 8192 + 1 * 100 * 15 * 3 * 8
+    assert _capi.sts_fit_workspace_bytes(1 << 20, 4, 100, 15) == (1 << 23) + 256 * 100 * 15 * 3 * 8
+    assert _capi.sts_fit_workspace_bytes(0, 4, 100, 15) == 0
+    assert _capi.sts_fit_workspace_bytes(10, 4, 128, 32) == 0       # LDS bound: 128 * 32 * 24 > 64 KiB
