@@ -150,19 +150,60 @@ def cpu_baseline(w, workers, reqs, reps=9):
                       f"over a {procs}-process pool; wall {wall:.2f} s, summed worker time {sum(busy):.2f} s"}
 
 
+def sts_fit_bench(args):
+    """spec_sts_fit on the calibration recipe: 2^20 samples x 15 positions,
+    the 100-point grid linspace(0.1, 10, 100), 15 bins (2 launches per position)."""
+    import torch
+    import lossless_draft_verification_verify_amd as sv
+    sv.load()
+    dev = torch.device("cuda:0")
+    N, G = 1 << 20, 15
+    conf, L, _ = W.calibration(N, G=G)
+    c, l = torch.from_numpy(conf).to(dev), torch.from_numpy(L).to(dev)
+    temps = [float(np.float32(t)) for t in np.linspace(0.1, 10.0, 100)]
+    for _ in range(args.warmup):
+        sv.sts_fit(c, l, temps)
+    torch.cuda.synchronize()
+    K = max(1, min(args.steps, 20))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        sv.sts_fit(c, l, temps)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    evals = N * G * len(temps)
+    print(json.dumps({
+        "metric": "STS fit: sample-positions per second", "value": round(N * G / (ms * 1e-3), 1),
+        "unit": "sample-positions/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"Sequential Temperature Scaling fit: N={N} samples, G={G} positions, "
+                               "100-point grid, 15 bins, 30 launches", "N": N, "G": G, "grid": len(temps)},
+        "roofline": {"bound": "alu", "achieved": round(evals / (ms * 1e-3) / 1e9, 3), "unit": "G grid evaluations/s",
+                     "peak": None, "frac": None, "traffic": None,
+                     "kernel": "k_fit_accumulate (one fp64 exp2, a bin and three LDS atomics per sample, position "
+                               "and grid point)"},
+        "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated in HBM")
-    ap.add_argument("--workload", choices=("block", "greedy", "scheduled", "dcut", "logits", "acceptance"),
+    ap.add_argument("--workload", choices=("block", "greedy", "scheduled", "dcut", "logits", "acceptance", "static",
+                                           "sts_fit"),
                     default="block",
                     help="block: B=64 gamma=15 V=129280 T=1 (default); greedy: B=64 gamma=7 "
                          "V=152064 T=0; scheduled: spec_schedule then spec_verify, gamma=15 V=129280; "
                          "dcut: spec_dcut then spec_verify_packed over the packed rows, gamma=15 V=129280; "
                          "logits: spec_verify_logits with bf16 draft logits, B=64 gamma=15 V=129280 T=1; "
-                         "acceptance: spec_acceptance (alpha per position) on the same draft-logits workload")
+                         "acceptance: spec_acceptance (alpha per position) on the same draft-logits workload; "
+                         "static: spec_schedule_static (threshold 0.5) then spec_verify, gamma=15 V=129280; "
+                         "sts_fit: spec_sts_fit on 2^20 samples x 15 positions, 100-point grid, 15 bins")
+    ap.add_argument("--calibrated", action="store_true",
+                    help="scheduled / dcut / static: apply per-position STS temperatures as confidences load")
     ap.add_argument("--batch", type=int, default=64, help="B of the scheduled and dcut workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=0)
@@ -175,6 +216,9 @@ def main():
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(requests shard across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "sts_fit":
+        return sts_fit_bench(args)
 
     if args.copy_probe:
         import torch
@@ -191,7 +235,7 @@ def main():
         w = W.block()
     elif args.workload == "greedy":
         w = W.greedy()
-    elif args.workload == "scheduled":
+    elif args.workload in ("scheduled", "static"):
         w = W.scheduled(args.batch)
     elif args.workload in ("logits", "acceptance"):
         w = W.block_logits()
@@ -223,6 +267,12 @@ def main():
     sets = [(z0, q0, x0, u0)] + [tuple(clone(t) for t in (z0, q0, x0, u0)) for _ in range(args.sets - 1)]
     acc = torch.empty(B, dtype=torch.int32, device=dev)
     tok = torch.empty(B, G + 1, dtype=torch.int32, device=dev)
+    # stand-in fitted temperatures (the calibration recipe's per-position values)
+    calib = W.calibration(2, G=G)[2].astype(np.float32).tolist() if args.calibrated else None
+    static = None
+    if args.workload == "static":
+        static = (to_dev(w["confidence"]), 0.5, torch.empty(B, dtype=torch.int32, device=dev),
+                  torch.empty(1, dtype=torch.int32, device=dev))
     sched = None
     if args.workload == "scheduled":
         conf, cost = to_dev(w["confidence"]), to_dev(w["cost_table"])
@@ -238,7 +288,7 @@ def main():
         ridx = torch.empty(1, dtype=torch.int32, device=dev)
         rows = torch.empty(1, dtype=torch.int32, device=dev)
         sv.dcut(conf, w["ratios"], w["ratio_cost"], out_verify_len=vlen, out_row_offsets=offs, out_ratio=ridx,
-                out_rows=rows, utility=False)
+                out_rows=rows, utility=False, calib_temps=calib)
         torch.cuda.synchronize()
         # The target's logits of the packed batch: the kept rows of each set,
         # gathered once before timing (buffer sized for full depth).
@@ -267,13 +317,16 @@ def main():
         if dcut is not None:
             conf, vlen, offs, ridx, rows, packed = dcut
             sv.dcut(conf, w["ratios"], w["ratio_cost"], out_verify_len=vlen, out_row_offsets=offs, out_ratio=ridx,
-                    out_rows=rows, utility=False)
+                    out_rows=rows, utility=False, calib_temps=calib)
             sv.verify_packed(packed[i % len(packed)], offs, qq, xx, uu, T, out_accepted=acc, out_tokens=tok,
                              row_pass_event=row_event)
             return
+        if static is not None:
+            vl, _, _ = sv.schedule_static(static[0], threshold=static[1], calib_temps=calib, row_offsets=False,
+                                          out_verify_len=static[2], out_total=static[3])
         if sched is not None:
             conf, cost, budget, vlen, tot, tau = sched
-            sv.schedule(conf, cost, budget, out_verify_len=vlen, out_total=tot, out_expected=tau)
+            sv.schedule(conf, cost, budget, out_verify_len=vlen, out_total=tot, out_expected=tau, calib_temps=calib)
             vl = vlen
         sv.verify(zz, qq, xx, uu, T, vl, out_accepted=acc, out_tokens=tok, row_pass_event=row_event)
 
@@ -283,6 +336,8 @@ def main():
     a = acc.cpu().numpy()
     if sched is not None:
         lens = sched[3].cpu().numpy().astype(np.int64)
+    elif static is not None:
+        lens = static[2].cpu().numpy().astype(np.int64)
     elif dcut is not None:
         lens = dcut[1].cpu().numpy().astype(np.int64)
     else:
@@ -353,8 +408,13 @@ def main():
         kname = "k_verify_greedy (one launch: argmax row waves, then one workgroup per request)"
     elif args.workload == "scheduled":
         desc = (f"confidence-scheduled verification: spec_schedule (token budget {w['budget']}, "
-                f"cost 1 + 0.02 T) then spec_verify, B={B}, gamma=15, V=129280, bf16, T=1")
+                f"cost 1 + 0.02 T{', STS-calibrated' if calib else ''}) then spec_verify, B={B}, gamma=15, "
+                f"V=129280, bf16, T=1")
         kname = "spec_schedule + k_rows_sampled (time up to the row-pass event includes the scheduler)"
+    elif args.workload == "static":
+        desc = (f"static-threshold verification: spec_schedule_static (confidence > 0.5"
+                f"{', STS-calibrated' if calib else ''}) then spec_verify, B={B}, gamma=15, V=129280, bf16, T=1")
+        kname = "spec_schedule_static + k_rows_sampled_vl (time up to the row-pass event includes the scheduler)"
     elif args.workload == "logits":
         desc = ("draft-logits verification: B=64, gamma=15, V=129280, bf16 target logits (Zipf(1.1) over a "
                 "per-row permutation) and bf16 draft logits, q = softmax(draft logits / T) on the device, T=1")
@@ -365,8 +425,9 @@ def main():
         kname = "k_acceptance (one workgroup per position; algorithmic bytes = one read of each row pair)"
     else:
         r_idx = int(dcut[3].item())
+        desc_cal = ", STS-calibrated" if calib else ""
         desc = (f"ratio-budgeted verification: spec_dcut (ratios {list(w['ratios'])}, cost 1 + 0.02 rho B (G+1); "
-                f"chosen ratio {w['ratios'][r_idx]}, {int(dcut[4].item())} packed rows) then "
+                f"chosen ratio {w['ratios'][r_idx]}, {int(dcut[4].item())} packed rows{desc_cal}) then "
                 f"spec_verify_packed, B={B}, gamma=15, V=129280, bf16, T=1")
         kname = "spec_dcut + k_rows_sampled_vl (time up to the row-pass event includes the ratio choice)"
     out = {

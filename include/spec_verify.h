@@ -385,7 +385,7 @@ spec_status_t spec_schedule_static(const float *confidence, int32_t B, int32_t G
  *   ECE(T) = (1/N) sum_bins |sum_{n in bin} a_n - sum_{n in bin} y_n|,
  *   bin = min(floor(bins * a), bins - 1);
  * out_temps[k] = the first grid point with the least ECE, and prefix_n gains
- * c[n,k]^(1/T_k) (prefix starts at 1; powers in double as 2^(log2(c)/T)).
+ * c[n,k]^(1/T_k) (prefix starts at 1; powers in double as 2^(log2(c) * (1/T))).
  * Confidences are clamped into [0, 1] (NaN as 0).  Prediction sums are exact
  * in 2^-40 fixed point, so the result does not depend on the order of
  * accumulation.  The usual grid is 100 points, linspace(0.1, 10, 100), with
@@ -393,10 +393,10 @@ spec_status_t spec_schedule_static(const float *confidence, int32_t B, int32_t G
  *
  * Arguments: confidence [N, G] float and acc_len [N] int32 (accepted drafts per
  * sample), device; temps host, each finite and > 0; 1 <= N < 2^23,
- * 1 <= num_temps <= 128, 1 <= bins <= 32, num_temps * bins <= 2730;
+ * 1 <= num_temps <= 128, 1 <= bins <= 32 (so num_temps * bins <= 4096);
  * out_temps [G] float, device; workspace device, 256-byte aligned, at least
  * spec_sts_fit_workspace_bytes(N, G, num_temps, bins) (0 on invalid shapes).
- * 2 launches per position.
+ * 3 launches per position.
  */
 size_t spec_sts_fit_workspace_bytes(int32_t N, int32_t G, int32_t num_temps, int32_t bins);
 spec_status_t spec_sts_fit(const float *confidence, const int32_t *acc_len, int32_t N, int32_t G,

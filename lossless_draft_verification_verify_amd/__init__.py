@@ -304,7 +304,7 @@ def acceptance(target_logits, draft, temperature, verify_len=None, *, draft_is_l
 
 
 def schedule_static(confidence, B=None, G=None, *, fixed_len=None, threshold=None, calib_temps=None,
-                    row_offsets=True):
+                    row_offsets=True, out_verify_len=None, out_total=None, out_row_offsets=None):
     """Static scheduler: fixed_len (every request min(L, G) drafts) or threshold
     (leading drafts whose confidence exceeds it).  Returns device tensors
     (verify_len [B], total [1], row_offsets [B+1] or None)."""
@@ -316,9 +316,11 @@ def schedule_static(confidence, B=None, G=None, *, fixed_len=None, threshold=Non
     else:
         dev = torch.device("cuda", torch.cuda.current_device())
     i32 = torch.int32
-    out_len = torch.empty(B, dtype=i32, device=dev)
-    out_T = torch.empty(1, dtype=i32, device=dev)
-    out_off = torch.empty(B + 1, dtype=i32, device=dev) if row_offsets else None
+    out_len = out_verify_len if out_verify_len is not None else torch.empty(B, dtype=i32, device=dev)
+    out_T = out_total if out_total is not None else torch.empty(1, dtype=i32, device=dev)
+    out_off = out_row_offsets
+    if out_off is None and row_offsets:
+        out_off = torch.empty(B + 1, dtype=i32, device=dev)
     mode = _capi.SPEC_STATIC_FIXED if fixed_len is not None else _capi.SPEC_STATIC_THRESHOLD
     stream = torch.cuda.current_stream(dev).cuda_stream
     st = _capi.spec_schedule_static(_ptr(confidence, torch.float32, dev, "confidence"), B, G, mode,

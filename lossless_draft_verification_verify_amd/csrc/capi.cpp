@@ -356,13 +356,14 @@ namespace {
 int fit_groups(int32_t N) { return int(std::min<int64_t>(256, (int64_t(N) + sv::kFitThreads - 1) / sv::kFitThreads)); }
 bool fit_shape_ok(int32_t N, int32_t G, int32_t nt, int32_t bins) {
     return N >= 1 && N < (1 << 23) && G >= 0 && G <= SPEC_MAX_DRAFTS && nt >= 1 && nt <= sv::kFitMaxTemps &&
-           bins >= 1 && bins <= sv::kFitMaxBins && size_t(nt) * bins * 3 * 8 <= 65536;
+           bins >= 1 && bins <= sv::kFitMaxBins && size_t(nt) * bins * 2 * 8 <= 65536;
 }
 }  // namespace
 
 size_t spec_sts_fit_workspace_bytes(int32_t N, int32_t G, int32_t num_temps, int32_t bins) {
     if (!fit_shape_ok(N, G, num_temps, bins)) return 0;
-    return sv::align256(size_t(N) * 8) + size_t(fit_groups(N)) * num_temps * bins * 3 * 8;
+    return sv::align256(size_t(N) * 8) + sv::align256(size_t(num_temps) * 8) +
+           size_t(fit_groups(N)) * num_temps * bins * 2 * 8;
 }
 
 spec_status_t spec_sts_fit(const float *confidence, const int32_t *acc_len, int32_t N, int32_t G,
@@ -387,7 +388,9 @@ spec_status_t spec_sts_fit(const float *confidence, const int32_t *acc_len, int3
     a.acc_len = acc_len;
     a.out_temps = out_temps;
     a.prefix = static_cast<double *>(workspace);
-    a.part = reinterpret_cast<int64_t *>(static_cast<unsigned char *>(workspace) + sv::align256(size_t(N) * 8));
+    a.err = reinterpret_cast<double *>(static_cast<unsigned char *>(workspace) + sv::align256(size_t(N) * 8));
+    a.part = reinterpret_cast<int64_t *>(static_cast<unsigned char *>(workspace) + sv::align256(size_t(N) * 8) +
+                                         sv::align256(size_t(num_temps) * 8));
     a.N = N;
     a.G = G;
     a.nt = num_temps;

@@ -607,8 +607,19 @@ __global__ __launch_bounds__(kMaxThreads) void k_static(StaticArgs a) {
     for (int b = b0; b < b1; ++b) {
         int n = fixed;
         if (a.mode == 1) {
+            // 16 confidences at a time, all loaded before any is tested
             n = 0;
-            while (n < G && conf_at(a.conf, a.cal, b * G + n, G) > a.tau) ++n;
+            for (int k0 = 0; k0 < G && n == k0; k0 += 16) {
+                float cv[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) cv[i] = a.conf[size_t(b) * G + min(k0 + i, G - 1)];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int k = k0 + i;
+                    const float c = a.cal.on ? calibrate(cv[i], a.cal.temp[min(k, G - 1)]) : cv[i];
+                    if (n == k && k < G && c > a.tau) n = k + 1;
+                }
+            }
         }
         a.out_len[b] = n;
         local += n + 1;

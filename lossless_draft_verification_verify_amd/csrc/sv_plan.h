@@ -152,14 +152,15 @@ struct FitArgs {
     const int32_t *acc_len;   // [N]
     float *out_temps;         // [G]
     double *prefix;           // workspace [N]: calibrated survival of the positions fitted so far
-    int64_t *part;            // workspace [nwg][nt][bins][3]: count, labels, fixed-point predictions
+    int64_t *part;            // workspace [nwg][nt][bins][2]: labels, fixed-point predictions
+    double *err;              // workspace [nt]: the calibration error of each grid point
     int32_t N, G, nt, bins, nwg, k;
     float temps[128];         // the grid
 };
 constexpr int kFitMaxTemps = 128, kFitMaxBins = 32, kFitThreads = 1024;
 constexpr double kFitScale = 1099511627776.0;   // 2^40: fixed-point unit of the prediction sums
 int launch_fit_accumulate(const FitArgs &a, void *stream);
-int launch_fit_choose(const FitArgs &a, void *stream);
+int launch_fit_choose(const FitArgs &a, void *stream);   // two launches: per-temperature error, then the argmin
 
 struct AcceptArgs {
     const void *z;            // [B, G+1, V] target logits

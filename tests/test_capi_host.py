@@ -262,7 +262,7 @@ def test_sts_fit_rejects_bad_arguments(kw, status):
 
 
 def test_sts_fit_workspace_query():
-    assert _capi.sts_fit_workspace_bytes(1000, 4, 100, 15) == 8192 + 1 * 100 * 15 * 3 * 8
-    assert _capi.sts_fit_workspace_bytes(1 << 20, 4, 100, 15) == (1 << 23) + 256 * 100 * 15 * 3 * 8
+    assert _capi.sts_fit_workspace_bytes(1000, 4, 100, 15) == 8192 + 1024 + 1 * 100 * 15 * 2 * 8
+    assert _capi.sts_fit_workspace_bytes(1 << 20, 4, 100, 15) == (1 << 23) + 1024 + 256 * 100 * 15 * 2 * 8
     assert _capi.sts_fit_workspace_bytes(0, 4, 100, 15) == 0
-    assert _capi.sts_fit_workspace_bytes(10, 4, 128, 32) == 0       # LDS bound: 128 * 32 * 24 > 64 KiB
+    assert _capi.sts_fit_workspace_bytes(10, 4, 128, 32) > 0        # 128 * 32 * 16 B of LDS fits
