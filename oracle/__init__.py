@@ -18,13 +18,15 @@ acceptance  per-position acceptance overlap alpha = sum min(p, q) = 1 - TV,
 calibration  Sequential Temperature Scaling (apply c^(1/T_k); the left-to-right
           grid fit on the cumulative survival's 15-bin ECE) and the static
           scheduler's fixed-length and threshold modes.
+tree      greedy verification of a candidate tree (the acceptance walk after
+          the target's ancestor-masked pass).
 dcut      ratio-budgeted depth (top-K scores for each ratio budget, the ratio
           that maximises estimated progress over profiled cost) and
           verification over densely packed target rows.
 
 Every function is pinned by a ``-m "not gpu"`` test (tests/test_oracle_pins.py,
 tests/test_oracle_dcut.py, tests/test_oracle_acceptance.py,
-tests/test_oracle_calibration.py) against what the pages and the mathematics fix;
+tests/test_oracle_calibration.py, tests/test_oracle_tree.py) against what the pages and the mathematics fix;
 none is "parity unpinned".
 """
 
@@ -42,3 +44,4 @@ from .schedule import survival, schedule, schedule_value, brute_force  # noqa: F
 from . import dcut  # noqa: F401  (module: oracle.dcut.dcut, oracle.dcut.verify_packed, ...)
 from . import acceptance  # noqa: F401,E402
 from . import calibration  # noqa: F401,E402
+from . import tree  # noqa: F401,E402
