@@ -10,6 +10,9 @@
  *                       request's kept positions only).
  *   spec_verify_logits  the same with the draft distribution given as logits
  *                       (its softmax at the call's temperature).
+ *   spec_verify_tree    greedy verification of a candidate tree (the
+ *                       acceptance walk after the target's ancestor-masked
+ *                       pass over the flattened tree).
  *   spec_schedule       confidence-scheduled verification depth: how many
  *                       drafts of each request to verify under a batch token
  *                       budget.
@@ -241,6 +244,44 @@ spec_status_t spec_verify_logits(const void *target_logits, spec_dtype_t target_
                                  int32_t *out_accepted, int32_t *out_tokens,
                                  const spec_verify_diag_t *diag,
                                  void *workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/*
+ * spec_verify_tree -- greedy (temperature 0) verification of a candidate tree.
+ *
+ * Operation ("breaking down dspark and its lineage", section "Tree
+ * attention"): the candidates of request b form a tree of M nodes; node 0 is
+ * the root (the last committed token), node i >= 1 carries token
+ * node_tokens[b,i] and parent parents[b,i] < i.  target_logits[b,i,:] is the
+ * target's next-token distribution after the path root..i (one target pass over
+ * the flattened tree with an ancestor-only mask).  From the root, the walk
+ * moves to the child of the current node whose token equals the lowest-index
+ * argmax of the current node's row (the lowest-numbered child if several
+ * carry it) and stops when none does.  This emits exactly what greedy
+ * decoding of the target would.
+ *   out_accepted[b] = accepted path length;
+ *   out_tokens[b,:] = the accepted tokens, then the argmax at the last node
+ *                     (the bonus), then -1;
+ *   out_path[b,:]   = the accepted node indices after the root, then -1.
+ * Sampled acceptance over several candidates is not defined on the pages and
+ * not provided.
+ *
+ * Arguments (device pointers): target_logits [B, M, V] of target_dtype;
+ * parents, node_tokens [B, M] int32 (entry 0 ignored; may be NULL if M == 1);
+ * 1 <= M <= SPEC_MAX_DRAFTS + 1; out_accepted [B], out_tokens [B, M],
+ * out_path [B, M] int32; workspace of spec_verify_workspace_bytes(B, M - 1, V,
+ * target_dtype).  Two launches: the greedy row pass over every node row, then
+ * one workgroup per request.
+ *
+ * Data errors (that request's outputs all -1): a parent outside [0, i) or a
+ * token outside [0, V) at some node i >= 1; a visited row (the root or a node
+ * on the accepted path) that holds a NaN, whose maximum is +inf, or which is
+ * entirely -inf.
+ */
+spec_status_t spec_verify_tree(const void *target_logits, spec_dtype_t target_dtype,
+                               const int32_t *parents, const int32_t *node_tokens,
+                               int32_t B, int32_t M, int32_t V,
+                               int32_t *out_accepted, int32_t *out_tokens, int32_t *out_path,
+                               void *workspace, size_t workspace_bytes, spec_stream_t stream);
 
 /*
  * Number of kernel launches spec_verify makes for this shape on the current

@@ -17,7 +17,7 @@ import torch
 from . import _capi
 from ._capi import SpecError, SPEC_DTYPE_BF16, SPEC_DTYPE_F32  # noqa: F401
 
-__all__ = ["verify", "verify_packed", "schedule", "dcut", "acceptance", "schedule_static", "sts_fit",
+__all__ = ["verify", "verify_packed", "verify_tree", "schedule", "dcut", "acceptance", "schedule_static", "sts_fit",
            "verify_workspace_bytes", "SpecError", "load"]
 
 _workspaces = {}
@@ -348,3 +348,34 @@ def sts_fit(confidence, acc_len, temps, bins=15):
     if st != _capi.SPEC_OK:
         raise SpecError(st, "spec_sts_fit")
     return out
+
+
+def verify_tree(target_logits, parents, node_tokens, *, workspace=None):
+    """Greedy verification of a candidate tree per request.
+
+    target_logits [B, M, V] bf16/fp32 (row i: the target after the path to node i);
+    parents, node_tokens [B, M] int32 (entry 0 is the root).  Returns device
+    tensors (accepted [B], tokens [B, M], path [B, M]).
+    """
+    z = target_logits
+    if not isinstance(z, torch.Tensor) or z.dim() != 3:
+        raise ValueError("target_logits must be a [B, M, V] tensor")
+    dev = z.device
+    B, M, V = z.shape
+    code = _dtype_code(z)
+    i32 = torch.int32
+    for t, name in ((parents, "parents"), (node_tokens, "node_tokens")):
+        if t is not None and tuple(t.shape) != (B, M):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(B, M)}")
+    acc = torch.empty(B, dtype=i32, device=dev)
+    tok = torch.empty(B, M, dtype=i32, device=dev)
+    path = torch.empty(B, M, dtype=i32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = _capi.verify_workspace_bytes(B, M - 1, V, code)
+    ws = workspace if workspace is not None else _workspace(dev, stream, nbytes)
+    st = _capi.spec_verify_tree(z.data_ptr(), code, _ptr(parents, i32, dev, "parents"),
+                                _ptr(node_tokens, i32, dev, "node_tokens"), B, M, V, acc.data_ptr(), tok.data_ptr(),
+                                path.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    if st != _capi.SPEC_OK:
+        raise SpecError(st, "spec_verify_tree")
+    return acc, tok, path

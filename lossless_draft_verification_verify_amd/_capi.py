@@ -38,6 +38,7 @@ EXPORTS = (
     "spec_schedule",
     "spec_verify_packed",
     "spec_verify_logits",
+    "spec_verify_tree",
     "spec_dcut",
     "spec_acceptance",
     "spec_schedule_static",
@@ -96,6 +97,8 @@ def load():
     lib.spec_verify_logits.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp,
                                        ctypes.POINTER(DiagT), vp, sz, vp]
     lib.spec_verify_logits.restype = ctypes.c_int
+    lib.spec_verify_tree.argtypes = [vp, ctypes.c_int, vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_tree.restype = ctypes.c_int
     lib.spec_dcut.argtypes = [vp, i32, i32, fp, fp, i32, fp, vp, vp, vp, vp, vp, vp]
     lib.spec_dcut.restype = ctypes.c_int
     lib.spec_acceptance.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, i32, i32, i32, f32, vp, vp]
@@ -192,3 +195,9 @@ def spec_sts_fit(conf, acc_len, N, G, temps, bins, out_temps, ws, ws_bytes, stre
     n = len(temps) if temps is not None else 0
     return int(load().spec_sts_fit(conf or None, acc_len or None, N, G, _floats(temps), n, bins, out_temps or None,
                                    ws or None, ws_bytes, stream or None))
+
+
+def spec_verify_tree(logits, dtype_code, par, tok, B, M, V, out_acc, out_tok, out_path, ws, ws_bytes, stream):
+    return int(load().spec_verify_tree(logits or None, dtype_code, par or None, tok or None, B, M, V,
+                                       out_acc or None, out_tok or None, out_path or None, ws or None, ws_bytes,
+                                       stream or None))

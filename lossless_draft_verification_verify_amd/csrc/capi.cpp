@@ -284,6 +284,48 @@ spec_status_t spec_verify_packed(const void *target_logits, spec_dtype_t target_
                        workspace_bytes, stream);
 }
 
+spec_status_t spec_verify_tree(const void *target_logits, spec_dtype_t target_dtype, const int32_t *parents,
+                               const int32_t *node_tokens, int32_t B, int32_t M, int32_t V, int32_t *out_accepted,
+                               int32_t *out_tokens, int32_t *out_path, void *workspace, size_t workspace_bytes,
+                               spec_stream_t stream) {
+    const int es = esize_of(int(target_dtype));
+    if (es == 0) return SPEC_ERR_BAD_DTYPE;
+    if (M < 1) return SPEC_ERR_BAD_SHAPE;
+    if (M > SPEC_MAX_DRAFTS + 1) return SPEC_ERR_UNSUPPORTED;
+    const int32_t G = M - 1;
+    const spec_status_t sh = check_verify_shape(B, G, V, es);
+    if (sh != SPEC_OK) return sh;
+    if (!target_logits || !out_accepted || !out_tokens || !out_path || !workspace) return SPEC_ERR_NULL_POINTER;
+    if (M > 1 && (!parents || !node_tokens)) return SPEC_ERR_NULL_POINTER;
+    if (!aligned(target_logits, es) || !aligned(parents, 4) || !aligned(node_tokens, 4) ||
+        !aligned(out_accepted, 4) || !aligned(out_tokens, 4) || !aligned(out_path, 4) || !aligned(workspace, 256))
+        return SPEC_ERR_MISALIGNED;
+    const Layout lay = sv::make_layout(B, G, V, es);
+    if (workspace_bytes < lay.total) return SPEC_ERR_WORKSPACE_TOO_SMALL;
+    sv::VerifyArgs a = {};
+    a.logits = target_logits;
+    a.out_acc = out_accepted;
+    a.out_tok = out_tokens;
+    a.out_path = out_path;
+    a.tpar = parents;
+    a.ttok = node_tokens;
+    a.ws = static_cast<unsigned char *>(workspace);
+    a.lay = lay;
+    a.B = B;
+    a.G = G;
+    a.V = V;
+    a.ch1 = sv::chunk_elems(es);
+    a.nc1 = (V + a.ch1 - 1) / a.ch1;
+    a.np1 = (a.nc1 + sv::kWaves - 1) / sv::kWaves;
+    a.nsub = (V + sv::kSub - 1) / sv::kSub;
+    a.nc2 = 1;
+    a.spin_limit = 1u << 20;
+    a.mode = 1;                                        // the greedy row workgroups only: every node row
+    const bool az = aligned(target_logits, 16) && (size_t(V) * es) % 16 == 0;
+    if (sv::launch_verify_greedy(a, az, es, int(long(B) * M * a.np1), stream) != 0) return SPEC_ERR_DEVICE;
+    return sv::launch_tree_walk(a, B, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+}
+
 int32_t spec_verify_launches(int32_t B, int32_t G, int32_t V, spec_dtype_t dt, float temperature) {
     const int es = esize_of(int(dt));
     if (es == 0 || check_verify_shape(B, G, V, es) != SPEC_OK) return -1;

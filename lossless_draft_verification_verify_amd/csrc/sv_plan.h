@@ -88,6 +88,8 @@ struct VerifyArgs {
     int32_t nsub;     // draw sub-tiles per row
     int32_t nc2, spw; // request workgroups per request, sub-tiles per workgroup
     int32_t mode;     // greedy kernel: 0 row items then request items; 1 row items only; 2 request items only
+    const int32_t *tpar, *ttok;   // tree walk: [B, G+1] parents and tokens of the candidate nodes
+    int32_t *out_path;            // tree walk: [B, G+1] accepted nodes, then -1
     uint32_t spin_limit;
 };
 
@@ -98,6 +100,7 @@ int launch_requests_sampled(const VerifyArgs &a, bool aligned_z, bool aligned_q,
                             void *stream);   // draft logits when a.dl is set
 int launch_verify_greedy(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
 int greedy_occupancy(bool aligned_z, int esize, int *blocks_per_cu);
+int launch_tree_walk(const VerifyArgs &a, int grid, void *stream);
 
 constexpr int kMaxDrafts = 255;
 // Sequential Temperature Scaling, applied as confidences are loaded:

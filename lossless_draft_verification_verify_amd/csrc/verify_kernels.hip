@@ -591,6 +591,9 @@ __device__ bool merge_rows_sampled(const VerifyArgs &a, const uint64_t *part, in
 // every vocabulary up to 2^18 bf16 or 2^17 fp32), and the batch repeats
 // (bounded) until all are written.  Returns kRowBad in some thread for a bad
 // row or a wait that expired.
+// Merged argmax of rows 0..n into sh.A (kBadRowArgmax for a bad row: a NaN,
+// maximum +inf, all -inf, or a partial never written); returns kRowBad if any.
+constexpr int kBadRowArgmax = -3;
 __device__ int merge_rows_greedy(const VerifyArgs &a, int b, int n, Smem &sh) {
     constexpr int kRegs = 8;
     const uint64_t *part = partials(a, b);
@@ -638,8 +641,9 @@ __device__ int merge_rows_greedy(const VerifyArgs &a, int b, int n, Smem &sh) {
         row16_argmax(best, bi, nan);
         ok = row16_and(ok);
         if (l == 0 && live) {
-            if (!ok || nan || bi < 0 || best == __builtin_inff()) flags |= kRowBad;
-            sh.A[r] = bi;
+            const bool rb = !ok || nan || bi < 0 || best == __builtin_inff();
+            if (rb) flags |= kRowBad;
+            sh.A[r] = rb ? kBadRowArgmax : bi;
         }
     }
     return flags;
@@ -1195,6 +1199,64 @@ __global__ __launch_bounds__(kWG) void k_verify_greedy(VerifyArgs a) {
     else row_group_greedy<ES, AL>(a, i, sh);
 }
 
+// Greedy tree walk ("breaking down dspark and its lineage", section "Tree
+// attention"): one workgroup per request, after the greedy row pass over its
+// G + 1 node rows.  Every row's argmax is merged; each node that carries its
+// parent's argmax offers itself to the parent (LDS minimum: the lowest such
+// child); the walk from the root is then a pointer chase in LDS.  A visited
+// bad row, a parent outside [0, i) or a token outside [0, V) is a data error.
+__global__ __launch_bounds__(kWG) void k_tree_walk(VerifyArgs a) {
+    __shared__ Smem sh;
+    __shared__ int match[kWG];
+    __shared__ int emit[kWG + 1], path[kWG];
+    __shared__ int acc_n;
+    const int b = int(blockIdx.x), t = int(threadIdx.x), M = a.G + 1;
+    const int32_t *par = a.tpar + size_t(b) * M, *tok = a.ttok + size_t(b) * M;
+    bool bad = false;
+    int p = 0, tk = 0;
+    if (t < M) {
+        match[t] = INT_MAX;
+        if (t >= 1) {
+            p = par[t];
+            tk = tok[t];
+            bad = !(p >= 0 && p < t) || !(tk >= 0 && tk < a.V);
+        }
+    }
+    merge_rows_greedy(a, b, a.G, sh);
+    bad = __syncthreads_or(bad);
+    if (!bad && t >= 1 && t < M && tk == sh.A[p]) atomicMin(&match[p], t);
+    __syncthreads();
+    if (t == 0) {
+        int n = -1;
+        if (!bad) {
+            int cur = 0;
+            n = 0;
+            for (;;) {
+                const int am = sh.A[cur];
+                if (am < 0) {                             // a visited bad row
+                    n = -1;
+                    break;
+                }
+                emit[n] = am;
+                const int nx = match[cur];
+                if (nx == INT_MAX) break;
+                path[n++] = nx;
+                cur = nx;
+            }
+        }
+        acc_n = n;
+    }
+    __syncthreads();
+    const int n = acc_n;
+    for (int i = t; i < M; i += kWG) {
+        a.out_tok[size_t(b) * M + i] = (n >= 0 && i <= n) ? emit[i] : -1;
+        a.out_path[size_t(b) * M + i] = (n >= 0 && i < n) ? path[i] : -1;
+    }
+    if (t == 0) a.out_acc[b] = n;
+    uint64_t *pw = partials(a, b);
+    for (int i = t; i < M * a.np1; i += kWG) st_coherent(pw + i, 0ull);
+}
+
 template <typename K>
 int occ(K kernel, int *n) {
     return int(hipOccupancyMaxActiveBlocksPerMultiprocessor(n, kernel, kWG, 0));
@@ -1255,6 +1317,11 @@ int launch_verify_greedy(const VerifyArgs &a, bool az, int esize, int grid, void
         if (az) hipLaunchKernelGGL((k_verify_greedy<4, true>), dim3(grid), dim3(kWG), 0, st, a);
         else hipLaunchKernelGGL((k_verify_greedy<4, false>), dim3(grid), dim3(kWG), 0, st, a);
     }
+    return int(hipGetLastError());
+}
+
+int launch_tree_walk(const VerifyArgs &a, int grid, void *stream) {
+    hipLaunchKernelGGL(k_tree_walk, dim3(grid), dim3(kWG), 0, static_cast<hipStream_t>(stream), a);
     return int(hipGetLastError());
 }
 

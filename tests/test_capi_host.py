@@ -266,3 +266,24 @@ def test_sts_fit_workspace_query():
     assert _capi.sts_fit_workspace_bytes(1 << 20, 4, 100, 15) == (1 << 23) + 1024 + 256 * 100 * 15 * 2 * 8
     assert _capi.sts_fit_workspace_bytes(0, 4, 100, 15) == 0
     assert _capi.sts_fit_workspace_bytes(10, 4, 128, 32) > 0        # 128 * 32 * 16 B of LDS fits
+
+
+def _tree(**kw):
+    args = dict(logits=Z, dtype_code=1, par=Q, tok=X, B=4, M=8, V=1000, out_acc=OA, out_tok=OT, out_path=U, ws=WS,
+                ws_bytes=1 << 20, stream=0)
+    args.update(kw)
+    return _capi.spec_verify_tree(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype_code=5), 4), (dict(M=0), 2), (dict(B=0), 2), (dict(V=0), 2), (dict(M=257), 6),
+    (dict(logits=0), 1), (dict(par=0), 1), (dict(tok=0), 1), (dict(out_acc=0), 1), (dict(out_tok=0), 1),
+    (dict(out_path=0), 1), (dict(ws=0), 1),
+    (dict(logits=Z + 1), 8), (dict(par=Q + 2), 8), (dict(ws=WS + 8), 8), (dict(ws_bytes=100), 5),
+])
+def test_verify_tree_rejects_bad_arguments(kw, status):
+    assert _tree(**kw) == status
+
+
+def test_verify_tree_root_only_needs_no_tree():
+    assert _tree(M=1, par=0, tok=0, ws_bytes=10) == 5

@@ -1,0 +1,128 @@
+"""GPU parity of greedy tree verification (spec_verify_tree) against the
+float64 oracle, through the C ABI.  Integer results: bit-exact, no allowance.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import tree as TR
+import workloads as W
+import lossless_draft_verification_verify_amd as sv
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sv.load()
+    yield
+
+
+def dev_logits(arr, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
+
+
+def run(z, dtype, par, tok):
+    acc, out, path = sv.verify_tree(dev_logits(z, dtype), torch.from_numpy(np.asarray(par, np.int32)).cuda(),
+                                    torch.from_numpy(np.asarray(tok, np.int32)).cuda())
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), out.cpu().numpy(), path.cpu().numpy()
+
+
+def check(z, dtype, par, tok, tag="", sel=None):
+    acc, out, path = run(z, dtype, par, tok)
+    if sel is None:
+        sel = np.arange(len(acc))
+    o = TR.tree_verify_greedy(np.asarray(z)[sel], np.asarray(par)[sel], np.asarray(tok)[sel])
+    np.testing.assert_array_equal(acc[sel], o["accepted"], err_msg=tag)
+    np.testing.assert_array_equal(out[sel], o["tokens"], err_msg=tag)
+    np.testing.assert_array_equal(path[sel], o["path"], err_msg=tag)
+    say(f"    {tag}: accepted {acc[sel].tolist()[:16]}")
+    return acc, out, path
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 152064), ("f32", 4099), ("bf16", 1023)])
+def test_chain_tree_is_greedy_verification(dtype, V):
+    g = np.random.default_rng(V)
+    B, G = 12, 7
+    z = (4.0 * g.normal(size=(B, G + 1, V))).astype(np.float32)
+    zb = W.f32_to_bf16_bits(z) if dtype == "bf16" else z
+    zf = W.bf16_bits_to_f32(zb) if dtype == "bf16" else z
+    a = zf.argmax(axis=2)
+    x = np.where(g.random((B, G)) < 0.75, a[:, :G], g.integers(0, V, (B, G))).astype(np.int32)
+    par = np.tile(TR.chain(G), (B, 1))
+    tok = np.concatenate([np.zeros((B, 1), np.int32), x], axis=1)
+    acc, out, _ = check(zb, dtype, par, tok, tag=f"chain {dtype} V={V}")
+    ref = oracle.verify_greedy(zb, x)
+    np.testing.assert_array_equal(acc, ref["accepted"])
+    np.testing.assert_array_equal(out, ref["tokens"])
+
+
+def test_medusa_style_tree():
+    """The 64-node layered tree at V = 152064 (bf16); the oracle on every request."""
+    w = W.tree(B=8)
+    say(f"[parity] tree B={w['B']} M={w['M']} V={w['V']}")
+    acc, _, _ = check(w["logits"], "bf16", w["parents"], w["node_tokens"], tag="64-node tree")
+    assert acc.max() >= 2                  # the noisy drafter reaches depth
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_trees(seed):
+    g = np.random.default_rng(50 + seed)
+    B, M, V = 16, int(g.integers(1, 40)), 257
+    z = (2.0 * g.normal(size=(B, M, V))).astype(np.float32)
+    a = z.argmax(axis=2)
+    par = np.array([[-1] + [int(g.integers(0, i)) for i in range(1, M)] for _ in range(B)], np.int32)
+    tok = g.integers(0, V, (B, M)).astype(np.int32)
+    hit = g.random((B, M)) < 0.6                      # many nodes carry their parent's argmax
+    for b in range(B):
+        for i in range(1, M):
+            if hit[b, i]:
+                tok[b, i] = a[b, par[b, i]]
+    check(z, "f32", par, tok, tag=f"random M={M}")
+
+
+def test_root_only_and_data_errors():
+    g = np.random.default_rng(9)
+    B, M, V = 6, 5, 300
+    z = (2.0 * g.normal(size=(B, M, V))).astype(np.float32)
+    a = z.argmax(axis=2)
+    par = np.tile(np.array([-1, 0, 1, 2, 0], np.int32), (B, 1))
+    tok = np.zeros((B, M), np.int32)
+    tok[:, 1], tok[:, 2], tok[:, 3] = a[:, 0], a[:, 1], a[:, 2]       # the walk goes 0 -> 1 -> 2 -> 3
+    tok[:, 4] = (a[:, 0] + 1) % V
+    z[0, 4, 7] = np.nan                  # node 4 is never visited: fine
+    z[1, 2, :] = -np.inf                 # node 2 is visited: error
+    par[2, 3] = 3                        # parent not before the node: error
+    tok[3, 4] = V                        # token out of range: error
+    z[4, 0, 11] = np.inf                 # root maximum +inf: error
+    acc, out, path = check(z, "f32", par, tok, tag="data errors")
+    assert acc.tolist()[:5] == [3, -1, -1, -1, -1] and acc[5] == 3
+    # a root-only tree emits the root argmax
+    acc, out, path = run(z[:, :1].copy(), "f32", par[:, :1].copy(), tok[:, :1].copy())
+    assert (acc[[0, 1, 2, 3, 5]] == 0).all() and acc[4] == -1
+    np.testing.assert_array_equal(out[[0, 1, 2, 3, 5], 0], a[[0, 1, 2, 3, 5], 0])
+
+
+def test_workspace_left_zero_for_verify():
+    """The tree walk zeroes every partial it used: a later spec_verify on the same workspace is unaffected."""
+    w = W.tree(B=8, V=20000, seed=3)
+    z = dev_logits(w["logits"], "bf16")
+    M = w["M"]
+    ws = torch.zeros(sv.verify_workspace_bytes(8, M - 1, 20000), dtype=torch.uint8, device="cuda")
+    sv.verify_tree(z, torch.from_numpy(w["parents"]).cuda(), torch.from_numpy(w["node_tokens"]).cuda(), workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero().item()) == 0

@@ -30,6 +30,12 @@ the design doc lists them):
              d = bf16(z + N(0, 0.75 * 1.05**k)) and samples x ~ softmax(d / T)
              (float64 from the stored bf16 values), so the draft distribution
              is exactly the softmax of the logits passed on.
+  tree       a candidate tree per request (64 nodes: the root, 8 children, 4
+             children on each of the first 4, 3 on each of the first 8 of
+             those, 1 on each of the first 15 of those); bf16 node rows
+             z ~ N(0, 4); a node's children are the top-k tokens of its parent
+             row plus N(0, 0.2) noise (k = its number of children), so
+             siblings are distinct and the best guess is often the argmax.
   calibration
              N samples of the scheduled confidences and an acceptance length per
              sample: draft k (given the earlier ones) is accepted when a uniform
@@ -261,3 +267,38 @@ def calibration(N, G=15, true_temps=None, seed=BASE_SEED + 8):
     ok = u < np.exp2(np.log2(conf.astype(np.float64)) / T[None, :])
     acc_len = np.where(ok.all(axis=1), G, np.argmin(ok, axis=1)).astype(np.int32)
     return conf, acc_len, T
+
+
+def tree_topology(levels=((0, 8), (4, 4), (8, 3), (15, 1))):
+    """Parents of a layered candidate tree.  Each level (w, k): the first w nodes
+    of the previous level (all of them when w == 0) get k children each."""
+    parents = [-1]
+    prev = [0]
+    for w, k in levels:
+        take = prev if w == 0 else prev[:w]
+        cur = []
+        for p in take:
+            for _ in range(k):
+                parents.append(p)
+                cur.append(len(parents) - 1)
+        prev = cur
+    return np.asarray(parents, np.int64)
+
+
+def tree(seed=BASE_SEED + 9, B=8, V=152064, parents=None, noise=0.2):
+    par = tree_topology() if parents is None else np.asarray(parents, np.int64)
+    M = len(par)
+    z = (4.0 * rng(seed, "target").standard_normal((B, M, V))).astype(np.float32)
+    bits = f32_to_bf16_bits(z)
+    zf = bf16_bits_to_f32(bits)
+    gn = rng(seed, "draft_noise")
+    tok = np.zeros((B, M), np.int64)
+    for p in range(M):
+        kids = np.nonzero(par == p)[0]
+        if len(kids) == 0:
+            continue
+        d = zf[:, p, :] + (noise * gn.standard_normal((B, V))).astype(np.float32)
+        top = np.argsort(-d, axis=1, kind="stable")[:, : len(kids)]
+        tok[:, kids] = top
+    return Workload(name="tree", B=B, M=M, V=V, T=0.0, dtype="bf16", logits=bits,
+                    parents=np.tile(par, (B, 1)).astype(np.int32), node_tokens=tok.astype(np.int32), seed=seed)
