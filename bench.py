@@ -186,6 +186,61 @@ def sts_fit_bench(args):
         "cpu_baseline": None}), flush=True)
 
 
+def tree_bench(args):
+    """spec_verify_tree on the layered 64-node tree: B=8, V=152064, bf16 (512 node rows per call, the bytes of
+    the greedy workload).  Rotating input copies; HIP events around each call."""
+    import torch
+    import lossless_draft_verification_verify_amd as sv
+    sv.load()
+    dev = torch.device("cuda:0")
+    w = W.tree()
+    B, M, V = w["B"], w["M"], w["V"]
+    z0 = torch.from_numpy(w["logits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    par = torch.from_numpy(w["parents"]).to(dev)
+    tok = torch.from_numpy(w["node_tokens"]).to(dev)
+    sets = [z0] + [z0.clone() for _ in range(args.sets - 1)]
+    acc = None
+    for i in range(args.warmup):
+        acc, _, _ = sv.verify_tree(sets[i % len(sets)], par, tok)
+    torch.cuda.synchronize()
+    K = args.steps
+    stream = torch.cuda.current_stream(dev)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(K):
+        acc, _, _ = sv.verify_tree(sets[i % len(sets)], par, tok)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / K
+    hev = HipEvents(2 * K)
+    sh = stream.cuda_stream
+    for i in range(K):
+        hev.record(2 * i, sh)
+        sv.verify_tree(sets[i % len(sets)], par, tok)
+        hev.record(2 * i + 1, sh)
+    torch.cuda.synchronize()
+    call = np.array([hev.ms(2 * i, 2 * i + 1) for i in range(K)])
+    hev.close()
+    a = acc.cpu().numpy()
+    algo = B * M * V * 2 + B * M * 8 + B * (4 + 8 * M)
+    kern_ms = float(call.mean())
+    nodes = B * (M - 1)
+    print(json.dumps({
+        "metric": "verified draft positions/sec and achieved HBM GB/s (% peak), B=64 gamma=15 V=129k",
+        "value": round(nodes / (ms_step * 1e-3), 1), "unit": "verified candidate nodes/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"greedy tree verification: B={B} requests, a {M}-node layered candidate tree "
+                               f"(8/16/24/15 nodes per level), V={V}, bf16 logits N(0,4), T=0",
+                   "B": B, "nodes": M, "V": V, "rotating_sets": len(sets), "mean_accepted": float(a.mean())},
+        "roofline": {"bound": "hbm", "achieved": round(algo / (kern_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(algo / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "traffic": None,
+                     "kernel": "whole call: k_verify_greedy row workgroups over every node row + k_tree_walk",
+                     "algorithmic_bytes_per_launch": algo, "launch_ms_mean": round(kern_ms, 5)},
+        "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,7 +248,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated in HBM")
     ap.add_argument("--workload", choices=("block", "greedy", "scheduled", "dcut", "logits", "acceptance", "static",
-                                           "sts_fit"),
+                                           "sts_fit", "tree"),
                     default="block",
                     help="block: B=64 gamma=15 V=129280 T=1 (default); greedy: B=64 gamma=7 "
                          "V=152064 T=0; scheduled: spec_schedule then spec_verify, gamma=15 V=129280; "
@@ -201,7 +256,8 @@ def main():
                          "logits: spec_verify_logits with bf16 draft logits, B=64 gamma=15 V=129280 T=1; "
                          "acceptance: spec_acceptance (alpha per position) on the same draft-logits workload; "
                          "static: spec_schedule_static (threshold 0.5) then spec_verify, gamma=15 V=129280; "
-                         "sts_fit: spec_sts_fit on 2^20 samples x 15 positions, 100-point grid, 15 bins")
+                         "sts_fit: spec_sts_fit on 2^20 samples x 15 positions, 100-point grid, 15 bins; "
+                         "tree: spec_verify_tree, B=8 requests x a 64-node candidate tree, V=152064, T=0")
     ap.add_argument("--calibrated", action="store_true",
                     help="scheduled / dcut / static: apply per-position STS temperatures as confidences load")
     ap.add_argument("--batch", type=int, default=64, help="B of the scheduled and dcut workloads")
@@ -219,6 +275,8 @@ def main():
 
     if args.workload == "sts_fit":
         return sts_fit_bench(args)
+    if args.workload == "tree":
+        return tree_bench(args)
 
     if args.copy_probe:
         import torch

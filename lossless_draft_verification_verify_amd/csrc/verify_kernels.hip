@@ -1199,6 +1199,55 @@ __global__ __launch_bounds__(kWG) void k_verify_greedy(VerifyArgs a) {
     else row_group_greedy<ES, AL>(a, i, sh);
 }
 
+// Merged argmax of rows 0..n into sh.A for the tree walk: four lanes per row
+// (a row's partials interleaved over them, all loads issued together), so 64
+// rows per pass.  The partials are complete (written by the previous launch).
+// No barrier inside; the caller synchronises.
+__device__ void merge_rows_greedy4(const VerifyArgs &a, int b, int n, Smem &sh) {
+    constexpr int kR = 8;                  // partials per lane when np1 <= 32
+    const uint64_t *part = partials(a, b);
+    const int l = threadIdx.x & 3, g = threadIdx.x >> 2;
+    const uint64_t empty = uint64_t(1) << 32 | uint64_t(kValid) << 32;   // (0.0, index -1), written
+    for (int r0 = 0; r0 <= n; r0 += kWG / 4) {
+        const int r = r0 + g;
+        const bool live = r <= n;
+        const uint64_t *pp = part + size_t(live ? r : 0) * a.np1;
+        float best = neg_inf();
+        int bi = -1, nan = 0, ok = 1;
+        if (a.np1 <= 4 * kR) {
+            uint64_t v[kR];
+#pragma unroll
+            for (int i = 0; i < kR; ++i) {
+                const int cc = l + 4 * i;
+                v[i] = (live && cc < a.np1) ? pp[cc] : empty;
+            }
+#pragma unroll
+            for (int i = 0; i < kR; ++i) {
+                ok &= int(valid(v[i]));
+                const int vi = int(hi_u(v[i]) & ~kValid) - 2;
+                if (vi == kNanIdx) nan = 1;
+                else merge_am(best, bi, lo_f(v[i]), vi);
+            }
+        } else if (live) {
+            for (int cc = l; cc < a.np1; cc += 4) {
+                const uint64_t v = pp[cc];
+                ok &= int(valid(v));
+                const int vi = int(hi_u(v) & ~kValid) - 2;
+                if (vi == kNanIdx) nan = 1;
+                else merge_am(best, bi, lo_f(v), vi);
+            }
+        }
+        am_step<kXor1>(best, bi, nan);
+        am_step<kXor2>(best, bi, nan);
+        ok = ok & dpp_i<kXor1>(ok);
+        ok = ok & dpp_i<kXor2>(ok);
+        if (l == 0 && live) {
+            const bool rb = !ok || nan || bi < 0 || best == __builtin_inff();
+            sh.A[r] = rb ? kBadRowArgmax : bi;
+        }
+    }
+}
+
 // Greedy tree walk ("breaking down dspark and its lineage", section "Tree
 // attention"): one workgroup per request, after the greedy row pass over its
 // G + 1 node rows.  Every row's argmax is merged; each node that carries its
@@ -1222,7 +1271,7 @@ __global__ __launch_bounds__(kWG) void k_tree_walk(VerifyArgs a) {
             bad = !(p >= 0 && p < t) || !(tk >= 0 && tk < a.V);
         }
     }
-    merge_rows_greedy(a, b, a.G, sh);
+    merge_rows_greedy4(a, b, a.G, sh);
     bad = __syncthreads_or(bad);
     if (!bad && t >= 1 && t < M && tk == sh.A[p]) atomicMin(&match[p], t);
     __syncthreads();
