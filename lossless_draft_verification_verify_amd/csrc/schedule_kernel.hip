@@ -174,14 +174,30 @@ __device__ __forceinline__ float conf_at(const float *conf, const Calib &cal, in
     return cal.on ? calibrate(c, cal.temp[i % G]) : c;
 }
 
-// Sorting slot i of Np: its survival when it is a candidate, else -inf padding.
-__device__ __forceinline__ void slot_key(const SchedSmem &sh, int i, int N, int B, int G, double eps, double &s,
-                                         int &id) {
+// Sorting slot i: its survival when it is a candidate, else -inf padding.
+// L = 0: slot i is draft i = b * G + k.  L > 0 (survival never rises along a
+// request): request b owns the run of L slots from b * L, its drafts in order
+// (reversed for odd b), padding after them, so every run is already sorted
+// and consecutive runs alternate direction: the bitonic network can start at
+// stage 2L.
+__device__ __forceinline__ void slot_key(const SchedSmem &sh, int i, int N, int B, int G, int L, double eps,
+                                         double &s, int &id) {
     s = -__builtin_inf();
     id = kPad;
-    if (i < N && sh.key[i] > eps) {
-        const int b = i / G, k = i - b * G;
-        s = sh.key[i];
+    int b, k;
+    if (L > 0) {
+        b = i / L;
+        const int j = i - b * L;
+        k = (b & 1) ? L - 1 - j : j;
+        if (b >= B || k >= G) return;
+    } else {
+        if (i >= N) return;
+        b = i / G;
+        k = i - b * G;
+    }
+    const double v = sh.key[b * G + k];
+    if (v > eps) {
+        s = v;
         id = k * B + b;
     }
 }
@@ -225,11 +241,25 @@ __device__ __forceinline__ bool survivals(SchedSmem &sh, int B, int G, int tid, 
 
 // 3. Sort the candidates (survival in sh.key above eps) in the order (s desc,
 //    k asc, b asc), padding last: sh.key / sh.id hold the sorted survivals and
-//    ids k * B + b.  Returns the number of candidates.
-__device__ __forceinline__ int sort_candidates(SchedSmem &sh, int B, int G, double eps, int tid, int lane, int nth) {
+//    ids k * B + b.  Returns the number of candidates.  presorted: survival
+//    never rises along any request, so the run layout of slot_key applies when
+//    it needs no more slots than the workgroup has threads.
+__device__ __forceinline__ int sort_candidates(SchedSmem &sh, int B, int G, double eps, int tid, int lane, int nth,
+                                               bool presorted = false) {
     const int N = B * G;
     int Np = 1;
     while (Np < N) Np <<= 1;
+    int L = 0;
+    if (presorted && G >= 2) {
+        int l = 1;
+        while (l < G) l <<= 1;
+        int np = 1;
+        while (np < B * l) np <<= 1;
+        if (np <= nth && np <= kRegSort) {
+            L = l;
+            Np = np;
+        }
+    }
     int ncand;
     if (Np <= kRegSort) {
         // One slot per thread, bitonic network in registers: partners in the
@@ -237,9 +267,9 @@ __device__ __forceinline__ int sort_candidates(SchedSmem &sh, int B, int G, doub
         // farther ones through LDS (two buffers, so one barrier per step).
         double s;
         int id;
-        slot_key(sh, tid, N, B, G, eps, s, id);
+        slot_key(sh, tid, N, B, G, L, eps, s, id);
         int buf = 0;
-        for (int size = 2; size <= Np; size <<= 1) {
+        for (int size = (L > 0) ? 2 * L : 2; size <= Np; size <<= 1) {
             int stride = size >> 1;
             while (stride >= 64) {
                 sh.u.reg.xk[buf][tid] = s;
@@ -275,7 +305,7 @@ __device__ __forceinline__ int sort_candidates(SchedSmem &sh, int B, int G, doub
         for (int i = tid; i < Np; i += nth) {
             double v;
             int id;
-            slot_key(sh, i, N, B, G, eps, v, id);
+            slot_key(sh, i, N, B, G, 0, eps, v, id);
             sh.key[i] = v;          // slot i is read only by its own thread here
             sh.id[i] = id;
         }
@@ -323,7 +353,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
     __syncthreads();
 
     const bool nonincr = survivals(sh, B, G, tid, nth);
-    int ncand = sort_candidates(sh, B, G, eps, tid, lane, nth);
+    int ncand = sort_candidates(sh, B, G, eps, tid, lane, nth, nonincr);
 
     // 4. contiguity: only when some survival increases along a request.
     if (!nonincr) {
@@ -447,7 +477,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_dcut(DcutArgs a) {
     }
     __syncthreads();
     survivals(sh, B, G, tid, nth);
-    sort_candidates(sh, B, G, -__builtin_inf(), tid, lane, nth);
+    sort_candidates(sh, B, G, -__builtin_inf(), tid, lane, nth, true);   // clamped: survival never rises
     for (int p = tid; p < N; p += nth) {                  // sorted position of each draft
         const int id = sh.id[p];
         const int k = id / B, b = id - k * B;
