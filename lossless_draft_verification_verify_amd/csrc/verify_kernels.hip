@@ -148,6 +148,7 @@ struct __align__(16) Smem {
     int last;
     int q[6][kWaves];                             // per-wave results of ballot searches
     double base, R, Rp;
+    int fsel[2];                                  // final select: first sub-tile, flags
     float gm[kWaves];                             // greedy row group: the waves' (max, index, NaN)
     int gi[kWaves], gn[kWaves];
 };
@@ -813,81 +814,120 @@ __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, cons
     const bool resid = d.resid;
     const uint64_t *mass = masses(a, b);
     const int nsub = a.nsub;
-    // Pass 1: totals of both mass arrays (residual, target), and the last
-    // sub-tile of each with positive mass.  With at most kWG sub-tiles (every
-    // vocabulary up to 2^19) the masses are the polled ones, kept in
-    // registers for pass 2.
-    const bool one = nsub <= kWG;
-    double v[2] = {0.0, 0.0}, ex[2] = {0.0, 0.0}, in[2], tot[2];
-    double R = 0.0, Rp = 0.0;
-    int lr = -1, lp_s = -1;
-    if (one) {
-        v[0] = polled[0];
-        v[1] = polled[1];
-        wg_scan<2>(v, ex, in, tot, sh);
-        post_last(v[0] > 0.0, 1, sh);
-        post_last(v[1] > 0.0, 2, sh);
-        __syncthreads();
-        lr = wg_last(1, sh);
-        lp_s = wg_last(2, sh);
-        R = tot[0];
-        Rp = tot[1];
-    } else {
-        for (int blk = 0; blk < nsub; blk += kWG) {
-            const int s = blk + int(threadIdx.x);
-            v[0] = 0.0; v[1] = 0.0;
-            if (s < nsub) {
-                v[0] = mass_value(ld_coherent(mass + 2 * s));
-                v[1] = mass_value(ld_coherent(mass + 2 * s + 1));
+    double R = 0.0, Rp = 0.0, target = 0.0, base = 0.0;
+    int sstar = INT_MAX, sel = 0;
+    bool use_r = false, lastpos = false;
+    if (nsub <= 64) {
+        // Wave 0 holds every sub-tile's masses (the polled values): both
+        // prefixes, the last positive sub-tiles and the first sub-tile past
+        // u * R come from DPP scans and ballots, with one barrier to share
+        // them.  The prefixes are bitwise those of the workgroup scan below,
+        // to which waves 1..3 would only add zeros.
+        if (threadIdx.x < 64) {
+            const int s = threadIdx.x;
+            const double x0 = wave_scan_d(polled[0]), x1 = wave_scan_d(polled[1]);
+            const double tR = lane_d(x0, 63), tRp = lane_d(x1, 63);
+            const bool ur = resid && tR > 0.0;
+            const int sl = (resid && !ur) ? 1 : 0;
+            const double tg = double(d.u_final) * (sl ? tRp : tR);
+            const double vs = sl ? polled[1] : polled[0], xs = sl ? x1 : x0;
+            const double ps = dpp_d<kWaveShr1>(xs), bs = (s == 0) ? 0.0 : ps;
+            const uint64_t mp = __ballot(vs > 0.0);
+            const uint64_t mf = __ballot(s < nsub && vs > 0.0 && bs + vs > tg);
+            const int ss = mf ? __builtin_ctzll(mf) : (mp ? 63 - __builtin_clzll(mp) : 0);
+            const double bb = mf ? lane_d(bs, ss) : 0.0;
+            if (s == 0) {
+                sh.R = tR;
+                sh.Rp = tRp;
+                sh.base = bb;
+                sh.fsel[0] = ss;
+                sh.fsel[1] = int(mf == 0) | (int(ur) << 1) | (sl << 2);
             }
+        }
+        __syncthreads();
+        R = sh.R;
+        Rp = sh.Rp;
+        base = sh.base;
+        sstar = sh.fsel[0];
+        lastpos = (sh.fsel[1] & 1) != 0;
+        use_r = (sh.fsel[1] & 2) != 0;
+        sel = sh.fsel[1] >> 2;
+        target = double(d.u_final) * (sel ? Rp : R);
+    } else {
+        // Pass 1: totals of both mass arrays (residual, target), and the last
+        // sub-tile of each with positive mass.  With at most kWG sub-tiles (every
+        // vocabulary up to 2^19) the masses are the polled ones, kept in
+        // registers for pass 2.
+        const bool one = nsub <= kWG;
+        double v[2] = {0.0, 0.0}, ex[2] = {0.0, 0.0}, in[2], tot[2];
+        int lr = -1, lp_s = -1;
+        if (one) {
+            v[0] = polled[0];
+            v[1] = polled[1];
             wg_scan<2>(v, ex, in, tot, sh);
             post_last(v[0] > 0.0, 1, sh);
             post_last(v[1] > 0.0, 2, sh);
             __syncthreads();
-            if (wg_last(1, sh) >= 0) lr = blk + wg_last(1, sh);
-            if (wg_last(2, sh) >= 0) lp_s = blk + wg_last(2, sh);
-            R = R + tot[0];
-            Rp = Rp + tot[1];
-        }
-    }
-    // The draw is from the residual when it has mass; a rejection whose
-    // residual is zero draws from p_j, a bonus draw from p_n (whose residual
-    // terms are p itself).
-    const bool use_r = resid && R > 0.0;
-    const int sel = (resid && !use_r) ? 1 : 0;
-    const double target = double(d.u_final) * (sel ? Rp : R);
-    // Pass 2: the first sub-tile s with positive mass and base(s) + mass(s) > target.
-    int sstar = INT_MAX;
-    if (one) {
-        const int s = int(threadIdx.x);
-        const double vs = sel ? v[1] : v[0], bs = sel ? ex[1] : ex[0];
-        post_first(s < nsub && vs > 0.0 && bs + vs > target, 3, sh);
-        __syncthreads();
-        sstar = wg_first(3, sh);
-        if (s == sstar) sh.base = bs;
-    } else {
-        double P = 0.0;
-        for (int blk = 0; blk < nsub; blk += kWG) {
-            const int s = blk + int(threadIdx.x);
-            double w1[1] = {0.0}, ex1[1], in1[1], tot1[1];
-            if (s < nsub) w1[0] = mass_value(ld_coherent(mass + 2 * s + sel));
-            wg_scan<1>(w1, ex1, in1, tot1, sh);
-            const double bs = P + ex1[0];
-            post_first(s < nsub && w1[0] > 0.0 && bs + w1[0] > target, 3, sh);
-            __syncthreads();
-            const int f = wg_first(3, sh);
-            if (f != INT_MAX) {
-                sstar = blk + f;
-                if (s == sstar) sh.base = bs;
-                break;
+            lr = wg_last(1, sh);
+            lp_s = wg_last(2, sh);
+            R = tot[0];
+            Rp = tot[1];
+        } else {
+            for (int blk = 0; blk < nsub; blk += kWG) {
+                const int s = blk + int(threadIdx.x);
+                v[0] = 0.0; v[1] = 0.0;
+                if (s < nsub) {
+                    v[0] = mass_value(ld_coherent(mass + 2 * s));
+                    v[1] = mass_value(ld_coherent(mass + 2 * s + 1));
+                }
+                wg_scan<2>(v, ex, in, tot, sh);
+                post_last(v[0] > 0.0, 1, sh);
+                post_last(v[1] > 0.0, 2, sh);
+                __syncthreads();
+                if (wg_last(1, sh) >= 0) lr = blk + wg_last(1, sh);
+                if (wg_last(2, sh) >= 0) lp_s = blk + wg_last(2, sh);
+                R = R + tot[0];
+                Rp = Rp + tot[1];
             }
-            P = P + tot1[0];
         }
+        // The draw is from the residual when it has mass; a rejection whose
+        // residual is zero draws from p_j, a bonus draw from p_n (whose residual
+        // terms are p itself).
+        use_r = resid && R > 0.0;
+        sel = (resid && !use_r) ? 1 : 0;
+        target = double(d.u_final) * (sel ? Rp : R);
+        // Pass 2: the first sub-tile s with positive mass and base(s) + mass(s) > target.
+        if (one) {
+            const int s = int(threadIdx.x);
+            const double vs = sel ? v[1] : v[0], bs = sel ? ex[1] : ex[0];
+            post_first(s < nsub && vs > 0.0 && bs + vs > target, 3, sh);
+            __syncthreads();
+            sstar = wg_first(3, sh);
+            if (s == sstar) sh.base = bs;
+        } else {
+            double P = 0.0;
+            for (int blk = 0; blk < nsub; blk += kWG) {
+                const int s = blk + int(threadIdx.x);
+                double w1[1] = {0.0}, ex1[1], in1[1], tot1[1];
+                if (s < nsub) w1[0] = mass_value(ld_coherent(mass + 2 * s + sel));
+                wg_scan<1>(w1, ex1, in1, tot1, sh);
+                const double bs = P + ex1[0];
+                post_first(s < nsub && w1[0] > 0.0 && bs + w1[0] > target, 3, sh);
+                __syncthreads();
+                const int f = wg_first(3, sh);
+                if (f != INT_MAX) {
+                    sstar = blk + f;
+                    if (s == sstar) sh.base = bs;
+                    break;
+                }
+                P = P + tot1[0];
+            }
+        }
+        __syncthreads();
+        lastpos = sstar == INT_MAX;               // u * R at or beyond the top: last positive term
+        if (lastpos) sstar = max(0, sel ? lp_s : lr);
+        base = lastpos ? 0.0 : sh.base;
     }
-    __syncthreads();
-    const bool lastpos = sstar == INT_MAX;         // u * R at or beyond the top: last positive term
-    if (lastpos) sstar = max(0, sel ? lp_s : lr);
-    const double base = lastpos ? 0.0 : sh.base;
     float t[kSubPerThread];
     double rs, ps;
     sub_tile<ES, ALZ, ALQ, DL>(zrow, qrow, a.V, sstar, d.m, a.c32, d.inv_s, d.mq, d.inv_sq, resid, use_r, t, rs, ps);
