@@ -618,7 +618,7 @@ __device__ int merge_rows_greedy(const VerifyArgs &a, int b, int n, Smem &sh) {
 #pragma unroll
                 for (int i = 0; i < kRegs; ++i) ok &= int(valid(v[i]));
                 if (__syncthreads_and(ok) || spins >= a.spin_limit) break;
-                __builtin_amdgcn_s_sleep(4);
+                __builtin_amdgcn_s_sleep(1);
             }
 #pragma unroll
             for (int i = 0; i < kRegs; ++i) {          // ascending chunks: the first maximum wins
@@ -1054,15 +1054,10 @@ __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
     const int k = threadIdx.x;
     int xk = 0;
     if (k < n) xk = a.x[size_t(b) * G + k];
-    // One lane first waits (bounded) for the request's last-dispatched row
-    // wave, so the workgroup does not poll every partial while the row pass
-    // is still streaming.
-    if (threadIdx.x == 0) {
-        const uint64_t *last = partials(a, b) + size_t(n + 1) * a.np1 - 1;
-        for (uint32_t spins = 0; spins < a.spin_limit && !valid(ld_coherent(last)); ++spins)
-            __builtin_amdgcn_s_sleep(8);
-    }
-    __syncthreads();
+    // Every lane polls its partials directly (a batch per attempt): request
+    // workgroups are dispatched after the last row workgroup, so this polling
+    // overlaps only the row pass's final workgroups, and the last partial is
+    // seen one round trip earlier than behind a one-lane wait on it.
     bool bad = merge_rows_greedy(a, b, n, sh) != 0;
     bad |= k < n && (xk < 0 || xk >= a.V);
     if (__syncthreads_or(bad)) {
