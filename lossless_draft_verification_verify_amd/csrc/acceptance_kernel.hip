@@ -13,10 +13,14 @@
 //   pass 1  per thread an online (max, sum of 2^((z - m) log2(e)/T)) over
 //           16-byte loads (eight elements per load, four loads in flight per
 //           row), merged across the wave with DPP and across the four waves in
-//           LDS; the draft row too in draft-logits mode;
+//           LDS; the draft row too in draft-logits mode.  These loads are
+//           ordinary (cache-allocating) ones, so part of the row pair is still
+//           cached when pass 2 reads it (7.7% faster than streaming loads at
+//           B = 64, gamma = 15, V = 129280 with draft logits);
 //   pass 2  sum of min(p, q) per thread (fp32 per eight elements, fp64 across
 //           them), then a DPP and LDS sum in fp64; each term is one fma and
-//           one v_exp_f32, p = 2^(fma(z, c, -(fl(m c) + log2 S))).
+//           one v_exp_f32, p = 2^(fma(z, c, -(fl(m c) + log2 S))).  The row
+//           pair is not read again, so these loads are nontemporal.
 // Both passes are bound by the two reads of the row pair once the terms cost
 // two instructions each.
 // A row holding a NaN, whose maximum is +inf, or which is entirely -inf gives
@@ -43,7 +47,7 @@ __device__ __forceinline__ float exp2n(float x) { return __builtin_amdgcn_exp2f(
 __device__ __forceinline__ bool fin(float x) { return __builtin_isfinite(x); }
 
 typedef uint32_t au32x4 __attribute__((ext_vector_type(4)));
-// A 16-byte load for data read once (nontemporal).
+// A 16-byte load for data read for the last time (nontemporal).
 __device__ __forceinline__ uint4 ld_once(const uint4 *p) {
     const au32x4 v = __builtin_nontemporal_load(reinterpret_cast<const au32x4 *>(p));
     return make_uint4(v[0], v[1], v[2], v[3]);
@@ -59,13 +63,15 @@ template <int ES> __device__ __forceinline__ float elem(const void *row, size_t 
 }
 
 // Eight consecutive elements e0 .. e0+7 of a row (positions >= V read as
-// `fill`).  Aligned rows take one (bf16) or two (fp32) 16-byte loads.
-template <int ES, bool AL>
+// `fill`).  Aligned rows take one (bf16) or two (fp32) 16-byte loads,
+// nontemporal (NT) or ordinary.
+template <bool NT> __device__ __forceinline__ uint4 ld16(const uint4 *p) { return NT ? ld_once(p) : *p; }
+template <int ES, bool AL, bool NT>
 __device__ __forceinline__ void load8(const void *row, int e0, int V, float fill, float (&f)[kAE]) {
     if (AL && e0 + kAE <= V) {
         const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const char *>(row) + size_t(e0) * ES);
         if constexpr (ES == 2) {
-            const uint4 w = ld_once(p);
+            const uint4 w = ld16<NT>(p);
             const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -73,7 +79,7 @@ __device__ __forceinline__ void load8(const void *row, int e0, int V, float fill
                 f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
             }
         } else {
-            const uint4 w0 = ld_once(p), w1 = ld_once(p + 1);
+            const uint4 w0 = ld16<NT>(p), w1 = ld16<NT>(p + 1);
             f[0] = __uint_as_float(w0.x); f[1] = __uint_as_float(w0.y);
             f[2] = __uint_as_float(w0.z); f[3] = __uint_as_float(w0.w);
             f[4] = __uint_as_float(w1.x); f[5] = __uint_as_float(w1.y);
@@ -182,9 +188,9 @@ __device__ double overlap_rows(const void *zrow, const void *drow, int V, int t,
 #pragma unroll
         for (int u = 0; u < kAU; ++u) {
             const int e0 = base + u * kAStep + t * kAE;
-            load8<ES, AL>(zrow, e0, V, ninf(), fz[u]);
-            if constexpr (QL) load8<ES, AL>(drow, e0, V, ninf(), fd[u]);
-            else load8<4, AL>(drow, e0, V, 0.0f, fd[u]);
+            load8<ES, AL, true>(zrow, e0, V, ninf(), fz[u]);
+            if constexpr (QL) load8<ES, AL, true>(drow, e0, V, ninf(), fd[u]);
+            else load8<4, AL, true>(drow, e0, V, 0.0f, fd[u]);
         }
 #pragma unroll
         for (int u = 0; u < kAU; ++u) {
@@ -227,8 +233,8 @@ __global__ __launch_bounds__(kAT) void k_acceptance(AcceptArgs a) {
 #pragma unroll
         for (int u = 0; u < kAU; ++u) {
             const int e0 = base + u * kAStep + t * kAE;
-            load8<ES, AL>(zrow, e0, V, ninf(), fz[u]);
-            if constexpr (QL) load8<ES, AL>(drow, e0, V, ninf(), fd[u]);
+            load8<ES, AL, false>(zrow, e0, V, ninf(), fz[u]);
+            if constexpr (QL) load8<ES, AL, false>(drow, e0, V, ninf(), fd[u]);
         }
 #pragma unroll
         for (int u = 0; u < kAU; ++u) {
