@@ -23,7 +23,10 @@
 //      most 1024 slots each thread holds one in registers and the network is
 //      unrolled: partners closer than a wave are read across lanes with DPP
 //      (strides 1, 2, 4, 8) and the row-swap permutes (16, 32), farther ones
-//      through LDS, two strides per barrier where two remain;
+//      through LDS, two strides per barrier where two remain.  The network
+//      compares one 64-bit key (fp32-rounded survival above the id); runs of
+//      equal fp32 survival are then re-ranked exactly, so the order is the
+//      exact one;
 //   4. contiguity (only when some survival increases): a candidate can be kept
 //      only if all shallower positions of its request are candidates placed
 //      before it;
@@ -55,8 +58,9 @@ struct SchedSmem {
         double conf[kMaxCand]; // the confidences (slot = b * G + k)
         int pos[kMaxCand];     // contiguity: sorted position of each candidate (slot b * G + k), or -1
         struct {
-            double xk[2][kRegSort];   // register sort: exchange buffers for strides >= 64
-            int xi[2][kRegSort];
+            uint64_t xq[2][kRegSort]; // register sort: exchange buffers for strides >= 64
+            double fs[kRegSort];      // then the sorted exact survivals and ids (run fix-up)
+            int fi[kRegSort];
         } reg;
     } u;
     int len[kMaxCand];         // per request kept length (B <= kMaxCand)
@@ -72,10 +76,19 @@ struct SchedSmem {
 __device__ __forceinline__ bool before(double s1, int id1, double s2, int id2) {
     return s1 > s2 || (s1 == s2 && id1 < id2);
 }
-// The same order without branches (for the sorting network).
-__device__ __forceinline__ bool before_nb(double s1, int id1, double s2, int id2) {
-    return (int(s1 > s2) | (int(s1 == s2) & int(id1 < id2))) != 0;
+// Sorting-network key: the survival rounded to fp32 (larger first) above the
+// id k * B + b; padding sorts last.  Rounding is monotone, so the key order
+// equals the exact order except inside runs of equal fp32 survival, which the
+// sort then re-ranks exactly.  One 64-bit unsigned compare per network step.
+constexpr uint64_t kPadKey = ~0ull;
+__device__ __forceinline__ uint64_t pack_key(double s, int id) {
+    if (id == kPad) return kPadKey;
+    const uint32_t u = __float_as_uint(float(s + 0.0));                 // -0 -> +0
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);    // ascending with the value
+    return (uint64_t(~ord) << 32) | uint32_t(id);
 }
+__device__ __forceinline__ uint32_t key_run(uint64_t k) { return uint32_t(k >> 32); }
+__device__ __forceinline__ int key_id(uint64_t k) { return k == kPadKey ? kPad : int(uint32_t(k)); }
 
 // Value of lane (lane ^ S) of the wave, S < 64.  (Every DPP pattern used
 // reads an active lane inside its row, so no lane needs an old value.)
@@ -94,30 +107,17 @@ template <int S> __device__ __forceinline__ int xor_lane(int x, int lane) {
         return int((lane & 32) ? r[0] : r[1]);
     }
 }
-template <int S> __device__ __forceinline__ double xor_lane_d(double x, int lane) {
-    const long long v = __double_as_longlong(x);
-    const int lo = xor_lane<S>(int(uint32_t(v)), lane), hi = xor_lane<S>(int(uint32_t(uint64_t(v) >> 32)), lane);
-    return __longlong_as_double((long long)((uint64_t(uint32_t(hi)) << 32) | uint32_t(lo)));
+__device__ __forceinline__ uint64_t join64(int lo, int hi) { return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo); }
+template <int S> __device__ __forceinline__ uint64_t xor_lane_k(uint64_t x, int lane) {
+    return join64(xor_lane<S>(int(uint32_t(x)), lane), xor_lane<S>(int(uint32_t(x >> 32)), lane));
 }
 
-// One compare-exchange step of the bitonic network at (size, stride): the
-// thread keeps the first or the second of its pair in the merge direction.
-__device__ __forceinline__ void cx_step(double &s, int &id, double s2, int id2, int tid, int size, int stride) {
-    const bool keep_first = ((tid & stride) == 0) == ((tid & size) == 0);
-    const bool mine_first = before_nb(s, id, s2, id2);
-    if (keep_first != mine_first) {
-        s = s2;
-        id = id2;
-    }
-}
-// The value position pos keeps after the step (size, stride) of a pair whose
-// values are (s1, id1) at pos and (s2, id2) at its partner.
-__device__ __forceinline__ void cx_value(double s1, int id1, double s2, int id2, int pos, int size, int stride,
-                                         double &so, int &ido) {
+// The key position pos keeps after the step (size, stride) of a pair whose
+// keys are k1 at pos and k2 at its partner: the first in order when pos keeps
+// "first" (its bit `stride` agrees with its bit `size`), else the second.
+__device__ __forceinline__ uint64_t cx_keep(uint64_t k1, uint64_t k2, int pos, int size, int stride) {
     const bool keep_first = ((pos & stride) == 0) == ((pos & size) == 0);
-    const bool mine = keep_first == before_nb(s1, id1, s2, id2);
-    so = mine ? s1 : s2;
-    ido = mine ? id1 : id2;
+    return (keep_first == (k1 < k2)) ? k1 : k2;
 }
 // The row-swap permutes leave every lane both members of its pair: result 0
 // holds the lower lane's value, result 1 the upper one's.
@@ -134,34 +134,26 @@ template <int S> __device__ __forceinline__ void pair_of(int x, int &lo, int &hi
     }
 }
 template <int S>
-__device__ __forceinline__ void cx_wave(double &s, int &id, int tid, int lane, int size) {
+__device__ __forceinline__ void cx_wave(uint64_t &k, int tid, int lane, int size) {
     if constexpr (S == 16 || S == 32) {
-        // The lane keeps the pair's first element (in the sort order) when it
-        // keeps "first", else the second.
-        const long long v = __double_as_longlong(s);
-        int l0, h0, l1, h1, il, ih;
-        pair_of<S>(int(uint32_t(v)), l0, h0);
-        pair_of<S>(int(uint32_t(uint64_t(v) >> 32)), l1, h1);
-        pair_of<S>(id, il, ih);
-        const double sl = __longlong_as_double((long long)((uint64_t(uint32_t(l1)) << 32) | uint32_t(l0)));
-        const double shv = __longlong_as_double((long long)((uint64_t(uint32_t(h1)) << 32) | uint32_t(h0)));
+        int l0, h0, l1, h1;
+        pair_of<S>(int(uint32_t(k)), l0, h0);
+        pair_of<S>(int(uint32_t(k >> 32)), l1, h1);
+        const uint64_t kl = join64(l0, l1), kh = join64(h0, h1);
         const bool keep_first = ((tid & S) == 0) == ((tid & size) == 0);
-        const bool lo_first = before_nb(sl, il, shv, ih);
-        const bool take_lo = keep_first == lo_first;
-        s = take_lo ? sl : shv;
-        id = take_lo ? il : ih;
+        k = (keep_first == (kl < kh)) ? kl : kh;
     } else {
-        cx_step(s, id, xor_lane_d<S>(s, lane), xor_lane<S>(id, lane), tid, size, S);
+        k = cx_keep(k, xor_lane_k<S>(k, lane), tid, size, S);
     }
 }
 // The in-wave strides of a merge stage of `size`, largest first.
-__device__ __forceinline__ void cx_in_wave(double &s, int &id, int tid, int lane, int size, int top) {
-    if (top >= 32) cx_wave<32>(s, id, tid, lane, size);
-    if (top >= 16) cx_wave<16>(s, id, tid, lane, size);
-    if (top >= 8) cx_wave<8>(s, id, tid, lane, size);
-    if (top >= 4) cx_wave<4>(s, id, tid, lane, size);
-    if (top >= 2) cx_wave<2>(s, id, tid, lane, size);
-    cx_wave<1>(s, id, tid, lane, size);
+__device__ __forceinline__ void cx_in_wave(uint64_t &k, int tid, int lane, int size, int top) {
+    if (top >= 32) cx_wave<32>(k, tid, lane, size);
+    if (top >= 16) cx_wave<16>(k, tid, lane, size);
+    if (top >= 8) cx_wave<8>(k, tid, lane, size);
+    if (top >= 4) cx_wave<4>(k, tid, lane, size);
+    if (top >= 2) cx_wave<2>(k, tid, lane, size);
+    cx_wave<1>(k, tid, lane, size);
 }
 
 // Calibrated confidence ("UraionSpec", Sequential Temperature Scaling):
@@ -262,44 +254,64 @@ __device__ __forceinline__ int sort_candidates(SchedSmem &sh, int B, int G, doub
     }
     int ncand;
     if (Np <= kRegSort) {
-        // One slot per thread, bitonic network in registers: partners in the
-        // wave by cross-lane reads (the in-wave strides of a stage unrolled),
-        // farther ones through LDS (two buffers, so one barrier per step).
-        double s;
-        int id;
-        slot_key(sh, tid, N, B, G, L, eps, s, id);
+        // One slot per thread, bitonic network in registers on the packed
+        // keys: partners in the wave by cross-lane reads (the in-wave strides
+        // of a stage unrolled), farther ones through LDS (two buffers, so one
+        // barrier per step).
+        double s0;
+        int id0;
+        slot_key(sh, tid, N, B, G, L, eps, s0, id0);
+        uint64_t k = pack_key(s0, id0);
         int buf = 0;
         for (int size = (L > 0) ? 2 * L : 2; size <= Np; size <<= 1) {
             int stride = size >> 1;
             while (stride >= 64) {
-                sh.u.reg.xk[buf][tid] = s;
-                sh.u.reg.xi[buf][tid] = id;
+                sh.u.reg.xq[buf][tid] = k;
                 __syncthreads();
                 if (stride >= 128) {
                     // Two steps per barrier: strides (stride, h) over the four
                     // positions t, t^stride, t^h, t^stride^h.
                     const int h = stride >> 1;
-                    const double sa = sh.u.reg.xk[buf][tid ^ stride], sb = sh.u.reg.xk[buf][tid ^ h],
-                                 sc = sh.u.reg.xk[buf][tid ^ stride ^ h];
-                    const int ia = sh.u.reg.xi[buf][tid ^ stride], ib = sh.u.reg.xi[buf][tid ^ h], ic = sh.u.reg.xi[buf][tid ^ stride ^ h];
-                    double s1t, s1h;
-                    int i1t, i1h;
-                    cx_value(s, id, sa, ia, tid, size, stride, s1t, i1t);
-                    cx_value(sb, ib, sc, ic, tid ^ h, size, stride, s1h, i1h);
-                    cx_value(s1t, i1t, s1h, i1h, tid, size, h, s, id);
+                    const uint64_t ka = sh.u.reg.xq[buf][tid ^ stride], kb = sh.u.reg.xq[buf][tid ^ h],
+                                   kc = sh.u.reg.xq[buf][tid ^ stride ^ h];
+                    const uint64_t k1t = cx_keep(k, ka, tid, size, stride);
+                    const uint64_t k1h = cx_keep(kb, kc, tid ^ h, size, stride);
+                    k = cx_keep(k1t, k1h, tid, size, h);
                     stride >>= 2;
                 } else {
-                    const double s2 = sh.u.reg.xk[buf][tid ^ stride];
-                    const int id2 = sh.u.reg.xi[buf][tid ^ stride];
-                    cx_step(s, id, s2, id2, tid, size, stride);
+                    k = cx_keep(k, sh.u.reg.xq[buf][tid ^ stride], tid, size, stride);
                     stride >>= 1;
                 }
                 buf ^= 1;
             }
-            cx_in_wave(s, id, tid, lane, size, min(size >> 1, 32));
+            cx_in_wave(k, tid, lane, size, min(size >> 1, 32));
         }
+        // Runs of equal key_run (equal fp32 survival) are in id order; rank
+        // each element exactly inside its run (usually a run of one).
+        const int id = key_id(k);
+        double s = -__builtin_inf();
+        if (id != kPad) {
+            const int kk = id / B, b = id - kk * B;
+            s = sh.key[b * G + kk];
+        }
+        __syncthreads();                           // the last exchange buffer is read
+        sh.u.reg.xq[0][tid] = k;
+        sh.u.reg.fs[tid] = s;
+        sh.u.reg.fi[tid] = id;
         ncand = __syncthreads_count(tid < Np && id != kPad);
-        if (tid < Np) { sh.key[tid] = s; sh.id[tid] = id; }
+        int rank = tid;
+        if (id != kPad) {
+            const uint32_t run = key_run(k);
+            int lo = tid, hi = tid;
+            while (lo > 0 && key_run(sh.u.reg.xq[0][lo - 1]) == run) --lo;
+            while (hi + 1 < Np && key_run(sh.u.reg.xq[0][hi + 1]) == run) ++hi;
+            if (hi > lo) {
+                rank = lo;
+                for (int p = lo; p <= hi; ++p)
+                    if (p != tid && before(sh.u.reg.fs[p], sh.u.reg.fi[p], s, id)) ++rank;
+            }
+        }
+        if (tid < Np) { sh.key[rank] = s; sh.id[rank] = id; }
         __syncthreads();
     } else {
         for (int i = tid; i < Np; i += nth) {
