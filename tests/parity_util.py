@@ -142,3 +142,20 @@ def compare(w, gpu, orc, verify_len=None, check_diag=True):
         assert rel <= 1e-5, ("lse", rel)
         rep["lse_maxrel"] = float(rel)
     return rep
+
+
+def sub_fp32_run_confidences(B=48, A=32):
+    """Confidences whose depth-2 survivals s = c0 * c1 all round to one fp32
+    value but differ (or tie exactly) in fp64, ordered against the request
+    index.  c0 = 1 - a u, c1 = 1 - (2A - a) u with u = 2^-24 and a = b + 1, so
+    s = 1 - 2A u + a (2A - a) u^2 exactly; the last term is far below half an
+    fp32 ulp.  The exact order within the run is a (2A - a) descending, then
+    b ascending on exact ties (a and 2A - a)."""
+    u = 2.0 ** -24
+    a = np.arange(1, B + 1, dtype=np.float64)
+    conf = np.stack([1.0 - a * u, 1.0 - (2 * A - a) * u], axis=1).astype(np.float32)
+    assert np.all(conf.astype(np.float64) == np.stack([1.0 - a * u, 1.0 - (2 * A - a) * u], axis=1))
+    s1 = conf[:, 0].astype(np.float64) * conf[:, 1].astype(np.float64)
+    assert len(set(s1.astype(np.float32).tolist())) == 1 and len(set(s1.tolist())) > B // 2
+    return conf
+

@@ -19,7 +19,7 @@ import oracle
 from oracle import dcut as OD
 import workloads as W
 import lossless_draft_verification_verify_amd as sv
-from parity_util import compare, to_device
+from parity_util import compare, sub_fp32_run_confidences, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -283,3 +283,16 @@ def test_packed_equals_unpacked_with_lengths():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(g["accepted"], acc.cpu().numpy())
         np.testing.assert_array_equal(g["tokens"], tok.cpu().numpy())
+
+
+def test_dcut_run_of_equal_fp32_survivals():
+    """Ratio budgets whose cut falls inside a run of depth-2 survivals that
+    differ only below fp32 precision (the exact order decides who is kept)."""
+    conf = sub_fp32_run_confidences()
+    B, G = conf.shape
+    for rho in (0.70, 0.72, 0.75, 0.8, 0.9):
+        keep = OD.ratio_budget(rho, B, G) - B
+        assert B < keep < 2 * B, rho                 # inside the depth-2 run
+        g, o = check_dcut(conf, [rho], [1.0], tag=f"rho {rho}")
+        deep = sorted(np.flatnonzero(o["lengths"][0] == 2).tolist())
+        assert deep != list(range(keep - B)), rho     # not the request-index order

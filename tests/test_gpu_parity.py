@@ -14,7 +14,7 @@ import torch
 import oracle
 import workloads as W
 import lossless_draft_verification_verify_amd as sv
-from parity_util import compare, run_gpu, run_oracle, to_device
+from parity_util import compare, run_gpu, run_oracle, sub_fp32_run_confidences, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -416,3 +416,22 @@ def test_workspace_shared_across_shapes():
         g = {"accepted": acc.cpu().numpy().astype(np.int64), "tokens": tok.cpu().numpy().astype(np.int64)}
         compare(w, g, o, check_diag=False)
     assert not ws.cpu().numpy().any()
+
+
+def test_schedule_run_of_equal_fp32_survivals():
+    """The budget cuts through a run of depth-2 candidates that differ only
+    below fp32 precision: the kept ones must be the exact order's first."""
+    conf = sub_fp32_run_confidences()
+    B = conf.shape[0]
+    L = B * 3 + 2
+    cost = np.ones(L, np.float32)                  # theta always improves: the budget stops the walk
+    for extra in (1, 2, 5, 7, 13, 20, 31, 47):
+        budget = 2 * B + extra
+        lo, To, tauo = oracle.schedule(conf, cost, budget)
+        assert sorted(np.flatnonzero(lo == 2).tolist()) != list(range(extra))   # not the index order
+        say(f"[parity] schedule, equal-fp32 run, budget {budget}")
+        vl, T, tau = sv.schedule(torch.from_numpy(conf).cuda(), torch.from_numpy(cost).cuda(), budget)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(vl.cpu().numpy(), lo, err_msg=f"budget {budget}")
+        assert int(T.item()) == To == budget
+        assert float(tau.item()) == np.float32(tauo), budget      # tau summed in the same order
