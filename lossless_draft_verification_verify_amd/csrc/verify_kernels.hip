@@ -36,7 +36,10 @@
 //                  The request's last workgroup in grid order polls the masses,
 //                  locates u * R by a parallel prefix over them, re-scans that
 //                  one sub-tile, writes the token, and zeroes every workspace
-//                  word the request used.
+//                  word the request used.  With B a multiple of 8 a request's
+//                  workgroups all sit on one XCD (workgroup i runs on XCD
+//                  i mod 8), so the repeated decision loads and the re-scan
+//                  hit that XCD's L2.
 //
 // The only wait inside a sampled launch is that last workgroup's (bounded)
 // poll, which depends only on workgroups dispatched before it.  Temperature 0
@@ -1177,8 +1180,20 @@ template <int ES, bool ALZ, bool ALQ, bool DL>
 // conversion); 4 waves per SIMD still hold 1024 draw workgroups at once.
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(DL ? 4 : 8, DL ? 4 : 8))) void k_requests_sampled(VerifyArgs a) {
     __shared__ Smem sh;
-    const int b = int(blockIdx.x) / a.nc2;
-    request_item_sampled<ES, ALZ, ALQ, DL>(a, b, int(blockIdx.x) - b * a.nc2, sh);
+    // With B a multiple of the XCD count, workgroup i (placed on XCD i mod 8)
+    // serves request ((i / 8) / nc2) * 8 + i mod 8: a request's workgroups
+    // share one XCD and its L2, in increasing grid order.
+    const int i = int(blockIdx.x);
+    int b, w;
+    if ((a.B & 7) == 0) {
+        const int x = i & 7, j = i >> 3;
+        b = (j / a.nc2) * 8 + x;
+        w = j - (j / a.nc2) * a.nc2;
+    } else {
+        b = i / a.nc2;
+        w = i - b * a.nc2;
+    }
+    request_item_sampled<ES, ALZ, ALQ, DL>(a, b, w, sh);
 }
 
 // Greedy row workgroup gi: (request b, row k, group g of kWaves consecutive
