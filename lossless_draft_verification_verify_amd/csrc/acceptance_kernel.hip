@@ -6,13 +6,17 @@
 // and q_k the draft distribution (given, or softmax(d_k / T) of draft logits).
 // alpha is the expected acceptance probability of the position, 1 - TV(p, q).
 //
-// One workgroup of 256 threads per position (1024-thread workgroups measured
-// slower: 228 against 208 us at B = 64, gamma = 15, V = 129280).  The exact overlap needs both
-// rows' normalisers before any min(p, q), so the workgroup reads its row pair
-// twice:
+// One workgroup of 512 threads per position, two 16-byte loads in flight per
+// row per thread.  At B = 64, gamma = 15, V = 129280 (draft logits) this shape
+// left the most of each row pair cached for its second read:
+//   256 threads: 188 us with two loads in flight, 185 us with four;
+//   512 threads: 155.5 us with two, 155.6 us with one, 185.5 us with four;
+//   1024 threads: 198 us with two, 202 us with one.
+// The exact overlap needs both rows' normalisers before any min(p, q), so the
+// workgroup reads its row pair twice:
 //   pass 1  per thread an online (max, sum of 2^((z - m) log2(e)/T)) over
-//           16-byte loads (eight elements per load, four loads in flight per
-//           row), merged across the wave with DPP and across the four waves in
+//           16-byte loads (eight elements per load, two loads in flight per
+//           row), merged across the wave with DPP and across the eight waves in
 //           LDS; the draft row too in draft-logits mode.  These loads are
 //           ordinary (cache-allocating) ones, so part of the row pair is still
 //           cached when pass 2 reads it (7.7% faster than streaming loads at
@@ -36,11 +40,11 @@
 namespace sv {
 namespace {
 
-constexpr int kAT = 256;                 // threads per workgroup
+constexpr int kAT = 512;                 // threads per workgroup
 constexpr int kAW = kAT / 64;            // waves
 constexpr int kAE = 8;                   // elements per thread per load
-constexpr int kAU = 4;                   // loads in flight per row per thread
-constexpr int kAStep = kAT * kAE;        // elements per workgroup step (2048)
+constexpr int kAU = 2;                   // loads in flight per row per thread
+constexpr int kAStep = kAT * kAE;        // elements per workgroup step (4096)
 
 __device__ __forceinline__ float ninf() { return -__builtin_inff(); }
 __device__ __forceinline__ float exp2n(float x) { return __builtin_amdgcn_exp2f(x); }   // v_exp_f32
