@@ -339,11 +339,13 @@ __device__ __forceinline__ int chunk_index(int beg, int lane, int i) {
 // row, each into its half of the gather word).
 template <int ES, bool AL>
 __device__ void row_chunk_sampled(const VerifyArgs &a, int b, int k, int chunk, int n, bool draft, int lane,
-                                  float &M_out, float &S_out) {
+                                  float &M_out, float &S_out, long trow = -1) {
     constexpr int EPL = kEPL<ES>;
+    // trow: the target row's index when the caller already holds it
+    const size_t zoff = (trow >= 0) ? size_t(trow) * size_t(a.V) : row_elem(a, b, k);
     const void *row = draft ? static_cast<const void *>(static_cast<const char *>(a.dl) +
                                                         (size_t(b) * a.G + k) * size_t(a.V) * ES)
-                            : static_cast<const void *>(static_cast<const char *>(a.logits) + row_elem(a, b, k) * ES);
+                            : static_cast<const void *>(static_cast<const char *>(a.logits) + zoff * ES);
     const int beg = chunk * a.ch1;
     float f[EPL];
     load_chunk<ES, AL>(row, beg, a.V, lane, f);
@@ -1093,11 +1095,11 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // as many partials.
 template <int ES, bool AL>
 __device__ __forceinline__ void row_group_sampled(const VerifyArgs &a, int b, int k, int g, int n, bool draft,
-                                                  float *gm, float *gs) {
+                                                  float *gm, float *gs, long trow = -1) {
     const int w = wave_id(), lane = int(threadIdx.x) & 63;
     const int c = g * kWaves + w;
     float M = neg_inf(), S = 0.0f;
-    if (c < a.nc1) row_chunk_sampled<ES, AL>(a, b, k, c, n, draft, lane, M, S);
+    if (c < a.nc1) row_chunk_sampled<ES, AL>(a, b, k, c, n, draft, lane, M, S, trow);
     if (lane == 0) {
         gm[w] = M;
         gs[w] = S;
@@ -1140,11 +1142,14 @@ __global__ __launch_bounds__(kWG) void k_rows_sampled_vl(VerifyArgs a) {
     __shared__ float gm[kWaves], gs[kWaves];
     __shared__ int off[kWG + 1];
     __shared__ int wtot[kWaves];
+    __shared__ int nlen[kWG], row0[kWG];     // each request's length and first target row
     const int t = int(threadIdx.x), lane = t & 63, w = wave_id();
     int cnt = 0;
     if (t < a.B) {
         const int n = verify_len(a, t);
         cnt = (n >= 0 && n <= a.G) ? ((n + 1) + (a.dl ? n : 0)) * a.np1 : 0;   // target rows, then draft rows
+        nlen[t] = n;
+        row0[t] = a.roff ? ld_const(a.roff, t) : t * (a.G + 1);
     }
     const int x = wave_scan_i(cnt);
     if (lane == 63) wtot[w] = x;
@@ -1166,10 +1171,11 @@ __global__ __launch_bounds__(kWG) void k_rows_sampled_vl(VerifyArgs a) {
             else hi = mid - 1;
         }
         const int b = lo, local = job - off[b];
-        const int n = verify_len(a, b);
+        const int n = nlen[b];
         const int rr = local / a.np1, g = local - rr * a.np1;
         const bool draft = rr > n;
-        row_group_sampled<ES, AL>(a, b, draft ? rr - n - 1 : rr, g, n, draft, gm, gs);
+        const int k = draft ? rr - n - 1 : rr;
+        row_group_sampled<ES, AL>(a, b, k, g, n, draft, gm, gs, long(row0[b]) + k);
         __syncthreads();                              // gm / gs are reused by the next job
     }
 }
