@@ -22,8 +22,8 @@
 //                  64-bit partial per group.  The wave whose chunk holds draft
 //                  token x_k also records z(x_k) and q(x_k), so the request
 //                  pass has no dependent gathers.  With verify lengths (at most
-//                  256 requests) a device-sized grid visits only the read row
-//                  groups instead.
+//                  256 requests) a grid of twice the resident workgroups
+//                  visits only the read row groups instead.
 //   request pass   nc2 draw workgroups per request, each streaming spw
 //                  2048-element sub-tiles of the draw row (spw sized for about
 //                  1024 draw workgroups in all).  Each merges the request's
