@@ -27,7 +27,11 @@ import workloads as W  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 KERNEL_SRC = os.path.join(ROOT, "lossless_draft_verification_verify_amd", "csrc", "verify_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_rows_sampled_block_traffic.md")
+# rocprofv3 counter summaries of each workload's dominant kernel
+TRAFFIC_FILES = {
+    "block": os.path.join(ROOT, "profiles", "k_rows_sampled_block_traffic.md"),
+    "greedy": os.path.join(ROOT, "profiles", "k_verify_greedy_traffic.md"),
+}
 
 
 def algorithmic_bytes(B, G, V, lens, n_rej, esize=2):
@@ -59,12 +63,16 @@ def kernel_sha():
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the row pass from the committed rocprofv3
-    counter runs (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known
-    size), if they were taken on the current kernel source; else None."""
+def measured_traffic(workload="block"):
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE, scaled by a
+    plain copy of known size), if they were taken on the current kernel
+    source; else None."""
+    path = TRAFFIC_FILES.get(workload)
+    if path is None:
+        return None
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             lines = f.read().splitlines()
     except OSError:
         return None
@@ -456,7 +464,7 @@ def main():
     positions = int(lens.sum())
     value = positions / (ms_step * 1e-3)
     achieved = row_algo / (kern_ms * 1e-3) / 1e9
-    traffic = measured_traffic() if args.workload == "block" else None
+    traffic = measured_traffic(args.workload)
     if args.workload == "block":
         desc = ("block-diffusion draft verification: B=64, gamma=15, V=129280, bf16 logits "
                 "(Zipf(1.1) over a per-row permutation), fp32 draft probabilities, T=1")
