@@ -26,11 +26,16 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
-KERNEL_SRC = os.path.join(ROOT, "lossless_draft_verification_verify_amd", "csrc", "verify_kernels.hip")
-# rocprofv3 counter summaries of each workload's dominant kernel
+CSRC = os.path.join(ROOT, "lossless_draft_verification_verify_amd", "csrc")
+KERNEL_SRC = os.path.join(CSRC, "verify_kernels.hip")
+# rocprofv3 counter summaries of each workload's dominant kernel, and the
+# source file that kernel is built from
 TRAFFIC_FILES = {
-    "block": os.path.join(ROOT, "profiles", "k_rows_sampled_block_traffic.md"),
-    "greedy": os.path.join(ROOT, "profiles", "k_verify_greedy_traffic.md"),
+    "block": (os.path.join(ROOT, "profiles", "k_rows_sampled_block_traffic.md"), KERNEL_SRC),
+    "greedy": (os.path.join(ROOT, "profiles", "k_verify_greedy_traffic.md"), KERNEL_SRC),
+    "logits": (os.path.join(ROOT, "profiles", "k_rows_sampled_logits_traffic.md"), KERNEL_SRC),
+    "acceptance": (os.path.join(ROOT, "profiles", "k_acceptance_traffic.md"),
+                   os.path.join(CSRC, "acceptance_kernel.hip")),
 }
 
 
@@ -51,11 +56,11 @@ def row_pass_bytes(V, lens, esize=2):
     return int((lens + 1).sum()) * V * esize + int(lens.sum()) * 8
 
 
-def kernel_sha():
-    """Hash of the kernel source's code: comments and blank lines removed, so
+def kernel_sha(src=KERNEL_SRC):
+    """Hash of a kernel source's code: comments and blank lines removed, so
     that only a change to the code itself makes recorded counters stale."""
     import re
-    with open(KERNEL_SRC) as f:
+    with open(src) as f:
         src = f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
@@ -68,9 +73,9 @@ def measured_traffic(workload="block"):
     committed rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE, scaled by a
     plain copy of known size), if they were taken on the current kernel
     source; else None."""
-    path = TRAFFIC_FILES.get(workload)
-    if path is None:
+    if workload not in TRAFFIC_FILES:
         return None
+    path, src = TRAFFIC_FILES[workload]
     try:
         with open(path) as f:
             lines = f.read().splitlines()
@@ -81,7 +86,7 @@ def measured_traffic(workload="block"):
         key, sep, val = line.strip().partition(": ")
         if sep and key in ("kernel_sha", "kernel", "bytes_per_launch"):
             kv[key] = val.strip()
-    if kv.get("kernel_sha") != kernel_sha() or "bytes_per_launch" not in kv:
+    if kv.get("kernel_sha") != kernel_sha(src) or "bytes_per_launch" not in kv:
         return None
     return int(kv["bytes_per_launch"])
 
