@@ -435,3 +435,28 @@ def test_schedule_run_of_equal_fp32_survivals():
         np.testing.assert_array_equal(vl.cpu().numpy(), lo, err_msg=f"budget {budget}")
         assert int(T.item()) == To == budget
         assert float(tau.item()) == np.float32(tauo), budget      # tau summed in the same order
+
+
+def _subset(w, n):
+    """The first n requests of workload w (requests are independent)."""
+    out = dict(w, B=n)
+    for key in ("logits", "draft_probs", "draft_tokens", "uniforms", "verify_len"):
+        if out.get(key) is not None:
+            out[key] = np.ascontiguousarray(w[key][:n])
+    return out
+
+
+@pytest.mark.parametrize("make", [lambda: W.block(B=64, G=5, V=5000, seed=91),
+                                  lambda: W.greedy(B=64, G=5, V=5000, seed=92)], ids=["sampled", "greedy"])
+def test_batch_independence_across_placements(make):
+    """Requests are verified independently: the first n requests give the same
+    outputs, bit for bit, whether n is a multiple of 8 (a request's draw
+    workgroups grouped on one XCD) or not (workgroups in request order)."""
+    w = make()
+    say(f"[parity] batch independence T={w['T']}")
+    full = run_gpu(w, diag=False)
+    for n in (1, 7, 8, 9, 24, 63):
+        part = run_gpu(_subset(w, n), diag=False)
+        np.testing.assert_array_equal(part["accepted"], full["accepted"][:n], err_msg=f"n={n}")
+        np.testing.assert_array_equal(part["tokens"], full["tokens"][:n], err_msg=f"n={n}")
+    compare(w, full, run_oracle(w), check_diag=False)
