@@ -460,3 +460,22 @@ def test_batch_independence_across_placements(make):
         np.testing.assert_array_equal(part["accepted"], full["accepted"][:n], err_msg=f"n={n}")
         np.testing.assert_array_equal(part["tokens"], full["tokens"][:n], err_msg=f"n={n}")
     compare(w, full, run_oracle(w), check_diag=False)
+
+
+def test_full_lengths_through_the_length_pass_many_jobs():
+    """B = 256 (the largest batch that takes the verify-length row pass), every
+    length G: each workgroup of that pass runs several row jobs, and the
+    outputs must equal the full-grid row pass's bit for bit."""
+    B, G, V = 256, 15, 32768
+    say(f"[parity] verify-length pass, B={B} G={G} V={V}")
+    gen = torch.Generator(device="cuda").manual_seed(1717)
+    z = (torch.randn(B, G + 1, V, device="cuda", generator=gen) * 2).to(torch.bfloat16)
+    q = torch.softmax(z[:, :G].float() + 0.5 * torch.randn(B, G, V, device="cuda", generator=gen), dim=-1).contiguous()
+    x = torch.randint(0, V, (B, G), device="cuda", dtype=torch.int32, generator=gen)
+    u = torch.rand(B, G + 1, device="cuda", generator=gen)
+    acc0, tok0 = sv.verify(z, q, x, u, 1.0)
+    full = torch.full((B,), G, dtype=torch.int32, device="cuda")
+    acc1, tok1 = sv.verify(z, q, x, u, 1.0, full)
+    torch.cuda.synchronize()
+    assert torch.equal(acc0, acc1) and torch.equal(tok0, tok1)
+    assert int((acc0 < 0).sum()) == 0
