@@ -1122,7 +1122,19 @@ __global__ __launch_bounds__(kWG) void k_rows_sampled(VerifyArgs a) {
     // Rows of a request: target rows 0..G, then (draft logits) draft rows 0..G-1.
     const int per = ((a.G + 1) + (a.dl ? a.G : 0)) * a.np1;
     const int i = blockIdx.x;
-    const int b = i / per, rem = i - b * per;
+    // With B a multiple of 8, workgroup i (on XCD i mod 8) serves request
+    // ((i / 8) / per) * 8 + i mod 8: each XCD streams whole requests, a
+    // contiguous block of rows (faster than interleaving every request's row
+    // groups over all eight XCDs).
+    int b, rem;
+    if ((a.B & 7) == 0) {
+        const int x = i & 7, j = i >> 3;
+        b = (j / per) * 8 + x;
+        rem = j - (j / per) * per;
+    } else {
+        b = i / per;
+        rem = i - b * per;
+    }
     const int rr = rem / a.np1, g = rem - rr * a.np1;
     const bool draft = rr > a.G;
     const int k = draft ? rr - a.G - 1 : rr;
@@ -1211,7 +1223,16 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(DL ? 4 : 8,
 template <int ES, bool AL>
 __device__ void row_group_greedy(const VerifyArgs &a, int gi, Smem &sh) {
     const int per = (a.G + 1) * a.np1;
-    const int b = gi / per, rem = gi - b * per;
+    // Request-per-XCD placement as in the sampled row pass (B a multiple of 8).
+    int b, rem;
+    if ((a.B & 7) == 0) {
+        const int x = gi & 7, j = gi >> 3;
+        b = (j / per) * 8 + x;
+        rem = j - (j / per) * per;
+    } else {
+        b = gi / per;
+        rem = gi - b * per;
+    }
     const int k = rem / a.np1, g = rem - k * a.np1;
     const int n = verify_len(a, b);
     if (n < 0 || n > a.G || k > n) return;           // row not read: the whole workgroup leaves
