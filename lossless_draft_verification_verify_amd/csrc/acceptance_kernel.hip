@@ -216,7 +216,12 @@ __device__ double overlap_rows(const void *zrow, const void *drow, int V, int t,
 template <int ES, bool AL, bool QL>
 __global__ __launch_bounds__(kAT) void k_acceptance(AcceptArgs a) {
     __shared__ ASmem sh;
-    const int b = int(blockIdx.x) / a.G, k = int(blockIdx.x) - b * a.G;
+    // With B * G a multiple of 8, the workgroups on XCD x (= blockIdx mod 8)
+    // take the x-th eighth of the positions: contiguous row pairs per XCD.
+    const int npos = a.B * a.G;
+    int pos = int(blockIdx.x);
+    if ((npos & 7) == 0) pos = (pos & 7) * (npos >> 3) + (pos >> 3);
+    const int b = pos / a.G, k = pos - b * a.G;
     const int n = a.vlen ? a.vlen[b] : a.G;
     float *out = a.out + size_t(b) * a.G + k;
     if (n < 0 || n > a.G || k >= n) {
