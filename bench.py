@@ -6,9 +6,10 @@ gamma=15 draft positions, V=129280, bf16 target logits, T=1 (every request
 verifies all 15 drafts, so a step verifies 960 draft positions).  Inputs are
 seeded synthetic arrays resident in HBM before the timed region; several
 independent copies rotate so that HBM, not the 256 MB last-level cache, serves
-the reads.  Prints one JSON line.
+the reads.  Prints one JSON line, with the roofline of the whole call and the
+float64 oracle timed on host cores beside it.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--no-cpu-baseline]
 """
 
 import argparse
@@ -127,53 +128,129 @@ class HipEvents:
             self.hip.hipEventDestroy(h)
 
 
-def _oracle_slice(args):
-    import oracle
-    lo, hi = args
-    w = _CPU_W
-    sl = slice(lo, hi)
+_CPU = {}
+
+
+def _cpu_job(part):
+    lo, hi = part
     t0 = time.perf_counter()
-    oracle.verify(w["logits"][sl], w["draft_probs"][sl], w["draft_tokens"][sl], w["uniforms"][sl],
-                  np.float32(w["T"]))
-    return time.perf_counter() - t0
+    units = _CPU["fn"](lo, hi)
+    return time.perf_counter() - t0, units
 
 
-_CPU_W = None
+def cpu_baseline(fn, n_items, unit, what, budget_s=12.0, max_workers=16):
+    """Time the float64 oracle, as it stands, on host cores.
 
-
-def cpu_baseline(w, workers, reqs, reps=9):
-    """Time the float64 oracle on host cores: the first `reqs` requests of the
-    workload, verified `reps` times over (10-15 s of summed CPU work)."""
-    global _CPU_W
+    fn(lo, hi) runs the oracle on items [lo, hi) of the workload (requests, or
+    sample chunks) and returns the units of work done (verified positions,
+    ...).  First one core runs slices in turn for about 2 s (the 1-core
+    figure); then a fork pool of min(max_workers, affinity cores) workers runs
+    slices that cover the workload, repeated to about budget_s seconds of
+    summed worker time.  Must run before anything initialises the GPU."""
     import multiprocessing as mp
-    _CPU_W = w
-    chunk = max(1, reqs // workers)
-    parts = [(i, min(reqs, i + chunk)) for i in range(0, reqs, chunk)] * reps
-    procs = min(workers, len(parts))
+    _CPU["fn"] = fn
+    per = max(1, n_items // 16)
+    slices = [(lo, min(n_items, lo + per)) for lo in range(0, n_items, per)]
+    t0 = time.perf_counter()
+    units1, done = 0, 0
+    while True:
+        lo, hi = slices[done % len(slices)]
+        units1 += fn(lo, hi)
+        done += 1
+        if time.perf_counter() - t0 >= 2.0:
+            break
+    t1 = time.perf_counter() - t0
+    affinity = len(os.sched_getaffinity(0))
+    workers = min(max_workers, affinity)
+    nparts = max(workers, int(round(budget_s / (t1 / done))))
+    parts = [slices[k % len(slices)] for k in range(nparts)]
     ctx = mp.get_context("fork")                 # before any GPU initialisation
     t0 = time.perf_counter()
-    with ctx.Pool(processes=procs) as pool:
-        busy = pool.map(_oracle_slice, parts)
+    with ctx.Pool(processes=workers) as pool:
+        res = pool.map(_cpu_job, parts, chunksize=1)
     wall = time.perf_counter() - t0
-    positions = reqs * w["G"] * reps
-    return {"value": positions / wall, "unit": "verified draft positions/s", "cores": procs,
-            "kind": "oracle",
-            "sample": f"{reqs} of {w['B']} requests of the same workload (all {w['G']} positions each), "
-                      f"verified {reps} times over by the float64 numpy oracle in {len(parts)} slices "
-                      f"over a {procs}-process pool; wall {wall:.2f} s, summed worker time {sum(busy):.2f} s"}
+    units = sum(u for _, u in res)
+    return {"value": round(units / wall, 2), "unit": unit, "cores": workers, "kind": "oracle",
+            "one_core_value": round(units1 / t1, 2), "affinity_cores": affinity,
+            "sample": f"{what}: {len(parts)} slices of up to {per} of {n_items} items over a {workers}-process "
+                      f"fork pool, wall {wall:.2f} s, summed worker time {sum(t for t, _ in res):.2f} s; "
+                      f"one core: {done} slices in {t1:.2f} s"}
+
+
+def oracle_fn(kind, w, lens=None):
+    """The oracle's work for requests [lo, hi) of workload w, and its unit count."""
+    import oracle
+    T = np.float32(w.get("T", 0.0))
+    G = w.get("G", 0)
+    if kind in ("block", "tiny", "mtp", "greedy"):
+        def fn(lo, hi):
+            oracle.verify(w["logits"][lo:hi], w.get("draft_probs")[lo:hi] if w.get("draft_probs") is not None
+                          else None, w["draft_tokens"][lo:hi],
+                          None if w.get("uniforms") is None else w["uniforms"][lo:hi], T)
+            return (hi - lo) * G
+        return fn
+    if kind in ("scheduled", "static", "dcut"):
+        def fn(lo, hi):
+            if lo == 0:                           # the batch-wide length choice, once per pass over the batch
+                if kind == "scheduled":
+                    oracle.schedule(w["confidence"], w["cost_table"], w["budget"])
+                elif kind == "static":
+                    from oracle import calibration as C
+                    C.static_threshold(w["confidence"], 0.5)
+                else:
+                    from oracle import dcut as OD
+                    OD.dcut(w["confidence"], w["ratios"], w["ratio_cost"])
+            oracle.verify(w["logits"][lo:hi], w["draft_probs"][lo:hi], w["draft_tokens"][lo:hi],
+                          w["uniforms"][lo:hi], T, lens[lo:hi])
+            return int(np.sum(lens[lo:hi]))
+        return fn
+    if kind == "logits":
+        from oracle import acceptance as OA
+
+        def fn(lo, hi):
+            OA.verify_logits(w["logits"][lo:hi], w["draft_logits"][lo:hi], w["draft_tokens"][lo:hi],
+                             w["uniforms"][lo:hi], T)
+            return (hi - lo) * G
+        return fn
+    if kind == "acceptance":
+        from oracle import acceptance as OA
+
+        def fn(lo, hi):
+            OA.acceptance(w["logits"][lo:hi], w["draft_logits"][lo:hi], T, draft_is_logits=True)
+            return (hi - lo) * G
+        return fn
+    if kind == "tree":
+        from oracle import tree as OT
+
+        def fn(lo, hi):
+            OT.tree_verify_greedy(w["logits"][lo:hi], w["parents"][lo:hi], w["node_tokens"][lo:hi])
+            return (hi - lo) * (w["M"] - 1)
+        return fn
+    raise ValueError(kind)
 
 
 def sts_fit_bench(args):
     """spec_sts_fit on the calibration recipe: 2^20 samples x 15 positions,
-    the 100-point grid linspace(0.1, 10, 100), 15 bins (2 launches per position)."""
+    the 100-point grid linspace(0.1, 10, 100), 15 bins (3 launches per position)."""
+    N, G = 1 << 20, 15
+    conf, L, _ = W.calibration(N, G=G)
+    temps = [float(np.float32(t)) for t in np.linspace(0.1, 10.0, 100)]
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import calibration as C
+        chunk = 1 << 12
+
+        def fn(lo, hi):
+            C.sts_fit(conf[lo * chunk:hi * chunk], L[lo * chunk:hi * chunk], temps)
+            return (hi - lo) * chunk * G
+        cpu = cpu_baseline(fn, N // chunk, "sample-positions/s",
+                           f"the float64 oracle's fit on chunks of {chunk} of the {N} samples (all {G} positions, "
+                           "the same grid and bins)")
     import torch
     import lossless_draft_verification_verify_amd as sv
     sv.load()
     dev = torch.device("cuda:0")
-    N, G = 1 << 20, 15
-    conf, L, _ = W.calibration(N, G=G)
     c, l = torch.from_numpy(conf).to(dev), torch.from_numpy(L).to(dev)
-    temps = [float(np.float32(t)) for t in np.linspace(0.1, 10.0, 100)]
     for _ in range(args.warmup):
         sv.sts_fit(c, l, temps)
     torch.cuda.synchronize()
@@ -186,28 +263,38 @@ def sts_fit_bench(args):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
     evals = N * G * len(temps)
+    # ALU peak of the accumulate kernel's inner step: one fp64 exp2 per grid evaluation is
+    # the costliest op; the chip's fp64 vector rate is 78.6 TFLOP/s and an fp64 exp2 is about
+    # 20 fp64 operations, so at most ~3.9 T evaluations/s.
+    alu_peak = 78.6e12 / 20 / 1e9
     print(json.dumps({
         "metric": "STS fit: sample-positions per second", "value": round(N * G / (ms * 1e-3), 1),
         "unit": "sample-positions/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
         "config": {"workload": f"Sequential Temperature Scaling fit: N={N} samples, G={G} positions, "
-                               "100-point grid, 15 bins, 30 launches", "N": N, "G": G, "grid": len(temps)},
+                               "100-point grid, 15 bins, 45 launches", "N": N, "G": G, "grid": len(temps)},
         "roofline": {"bound": "alu", "achieved": round(evals / (ms * 1e-3) / 1e9, 3), "unit": "G grid evaluations/s",
-                     "peak": None, "frac": None, "traffic": None,
+                     "peak": round(alu_peak, 1), "frac": round(evals / (ms * 1e-3) / 1e9 / alu_peak, 4),
+                     "traffic": None,
+                     "peak_derivation": "fp64 vector peak 78.6 TFLOP/s / ~20 fp64 operations per exp2 evaluation",
                      "kernel": "k_fit_accumulate (one fp64 exp2, a bin and three LDS atomics per sample, position "
                                "and grid point)"},
-        "cpu_baseline": None}), flush=True)
+        "cpu_baseline": cpu}), flush=True)
 
 
 def tree_bench(args):
     """spec_verify_tree on the layered 64-node tree: B=8, V=152064, bf16 (512 node rows per call, the bytes of
     the greedy workload).  Rotating input copies; HIP events around each call."""
+    w = W.tree()
+    B, M, V = w["B"], w["M"], w["V"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(oracle_fn("tree", w), B, "verified candidate nodes/s",
+                           f"the float64 oracle's greedy tree walk on the {B} requests of the same workload")
     import torch
     import lossless_draft_verification_verify_amd as sv
     sv.load()
     dev = torch.device("cuda:0")
-    w = W.tree()
-    B, M, V = w["B"], w["M"], w["V"]
     z0 = torch.from_numpy(w["logits"].view(np.int16)).to(dev).view(torch.bfloat16)
     par = torch.from_numpy(w["parents"]).to(dev)
     tok = torch.from_numpy(w["node_tokens"]).to(dev)
@@ -225,18 +312,8 @@ def tree_bench(args):
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / K
-    hev = HipEvents(2 * K)
-    sh = stream.cuda_stream
-    for i in range(K):
-        hev.record(2 * i, sh)
-        sv.verify_tree(sets[i % len(sets)], par, tok)
-        hev.record(2 * i + 1, sh)
-    torch.cuda.synchronize()
-    call = np.array([hev.ms(2 * i, 2 * i + 1) for i in range(K)])
-    hev.close()
     a = acc.cpu().numpy()
     algo = B * M * V * 2 + B * M * 8 + B * (4 + 8 * M)
-    kern_ms = float(call.mean())
     nodes = B * (M - 1)
     print(json.dumps({
         "metric": "verified draft positions/sec and achieved HBM GB/s (% peak), B=64 gamma=15 V=129k",
@@ -246,12 +323,42 @@ def tree_bench(args):
         "config": {"workload": f"greedy tree verification: B={B} requests, a {M}-node layered candidate tree "
                                f"(8/16/24/15 nodes per level), V={V}, bf16 logits N(0,4), T=0",
                    "B": B, "nodes": M, "V": V, "rotating_sets": len(sets), "mean_accepted": float(a.mean())},
-        "roofline": {"bound": "hbm", "achieved": round(algo / (kern_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(algo / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(algo / (ms_step * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(algo / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                      "traffic": None,
-                     "kernel": "whole call: k_verify_greedy row workgroups over every node row + k_tree_walk",
-                     "algorithmic_bytes_per_launch": algo, "launch_ms_mean": round(kern_ms, 5)},
-        "cpu_baseline": None}), flush=True)
+                     "kernel": "whole spec_verify_tree call: k_verify_greedy row workgroups over every node row, "
+                               "then k_tree_walk",
+                     "algorithmic_bytes_per_launch": algo, "launch_ms_mean": round(ms_step, 5)},
+        "cpu_baseline": cpu}), flush=True)
+
+
+def acceptance_stats(acc, lens):
+    """Mean accepted drafts, mean tokens per request (accepted + 1), and the
+    acceptance rate at each draft position: the share of the requests that
+    reached and verified position k whose draft k was accepted."""
+    acc, lens = np.asarray(acc, np.int64), np.asarray(lens, np.int64)
+    ok = acc >= 0
+    acc, lens = acc[ok], lens[ok]
+    rate = []
+    for k in range(int(lens.max()) if lens.size else 0):
+        tested = (acc >= k) & (lens > k)
+        rate.append(round(float((acc[tested] > k).mean()), 4) if tested.any() else None)
+    return {"mean_accepted": round(float(acc.mean()), 4), "mean_tokens_per_request": round(float((acc + 1).mean()), 4),
+            "acceptance_by_position": rate}
+
+
+DESCRIPTIONS = {
+    "block": ("block-diffusion draft verification: B=64, gamma=15, V=129280, bf16 logits "
+              "(Zipf(1.1) over a per-row permutation), fp32 draft probabilities, T=1"),
+    "tiny": "tiny verification: B=4, gamma=4, V=1024, fp32 logits N(0,2), fp32 draft probabilities, T=1",
+    "mtp": ("MTP-style short drafts: B=16, gamma=3, V=32000, bf16 logits N(0,3) with a 1-in-8 peaked token (+8), "
+            "fp32 draft probabilities, T=0.7"),
+    "greedy": "greedy draft verification: B=64, gamma=7, V=152064, bf16 logits N(0,4), T=0",
+    "logits": ("draft-logits verification: B=64, gamma=15, V=129280, bf16 target logits (Zipf(1.1) over a "
+               "per-row permutation) and bf16 draft logits, q = softmax(draft logits / T) on the device, T=1"),
+    "acceptance": ("acceptance diagnostics: alpha = sum min(p, q) per position, B=64, gamma=15, V=129280, bf16 target "
+                   "and draft logits, T=1 (two passes over each row pair)"),
+}
 
 
 def main():
@@ -260,10 +367,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="independent input copies rotated in HBM")
-    ap.add_argument("--workload", choices=("block", "greedy", "scheduled", "dcut", "logits", "acceptance", "static",
-                                           "sts_fit", "tree"),
+    ap.add_argument("--workload", choices=("block", "tiny", "mtp", "greedy", "scheduled", "dcut", "logits",
+                                           "acceptance", "static", "sts_fit", "tree"),
                     default="block",
-                    help="block: B=64 gamma=15 V=129280 T=1 (default); greedy: B=64 gamma=7 "
+                    help="block: B=64 gamma=15 V=129280 T=1 (default); tiny: B=4 gamma=4 V=1024 fp32 T=1; "
+                         "mtp: B=16 gamma=3 V=32000 T=0.7; greedy: B=64 gamma=7 "
                          "V=152064 T=0; scheduled: spec_schedule then spec_verify, gamma=15 V=129280; "
                          "dcut: spec_dcut then spec_verify_packed over the packed rows, gamma=15 V=129280; "
                          "logits: spec_verify_logits with bf16 draft logits, B=64 gamma=15 V=129280 T=1; "
@@ -273,10 +381,8 @@ def main():
                          "tree: spec_verify_tree, B=8 requests x a 64-node candidate tree, V=152064, T=0")
     ap.add_argument("--calibrated", action="store_true",
                     help="scheduled / dcut / static: apply per-position STS temperatures as confidences load")
-    ap.add_argument("--batch", type=int, default=64, help="B of the scheduled and dcut workloads")
+    ap.add_argument("--batch", type=int, default=64, help="B of the scheduled, static and dcut workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-workers", type=int, default=0)
-    ap.add_argument("--cpu-requests", type=int, default=64)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 20 plain device-to-device copies of MIB MiB (a known-size kernel "
                          "for scaling the HBM byte counters), then exit")
@@ -302,23 +408,50 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "copies": 20}), flush=True)
         return
 
-    if args.workload == "block":
+    kind = args.workload
+    if kind == "block":
         w = W.block()
-    elif args.workload == "greedy":
+    elif kind == "tiny":
+        w = W.tiny()
+    elif kind == "mtp":
+        w = W.mtp()
+    elif kind == "greedy":
         w = W.greedy()
-    elif args.workload in ("scheduled", "static"):
+    elif kind in ("scheduled", "static"):
         w = W.scheduled(args.batch)
-    elif args.workload in ("logits", "acceptance"):
+    elif kind in ("logits", "acceptance"):
         w = W.block_logits()
     else:
         w = W.ratio_budgeted(args.batch)
     B, G, V = w["B"], w["G"], w["V"]
     T = float(w["T"])
+    esize = 2 if w["dtype"] == "bf16" else 4
+    # stand-in fitted temperatures (the calibration recipe's per-position values)
+    calib = W.calibration(2, G=G)[2].astype(np.float32).tolist() if args.calibrated else None
+
+    # The oracle's lengths for the scheduled workloads (the GPU's are checked equal below).
+    lens_o = None
+    if kind == "scheduled":
+        import oracle
+        from oracle import calibration as C
+        conf_o = w["confidence"] if calib is None else C.sts_apply(w["confidence"], calib)
+        lens_o = np.asarray(oracle.schedule(conf_o, w["cost_table"], w["budget"])[0], np.int64)
+    elif kind == "static":
+        from oracle import calibration as C
+        lens_o = C.static_threshold(w["confidence"] if calib is None else C.sts_apply(w["confidence"], calib), 0.5)
+    elif kind == "dcut":
+        from oracle import calibration as C
+        from oracle import dcut as OD
+        lens_o = np.asarray(OD.dcut(w["confidence"] if calib is None else C.sts_apply(w["confidence"], calib),
+                                    w["ratios"], w["ratio_cost"])["verify_len"], np.int64)
 
     cpu = None
-    if not args.no_cpu_baseline and args.workload == "block":
-        workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
-        cpu = cpu_baseline(w, workers, min(args.cpu_requests, B))
+    if not args.no_cpu_baseline:
+        unit = "alpha positions/s" if kind == "acceptance" else "verified draft positions/s"
+        cpu = cpu_baseline(oracle_fn(kind, w, lens_o), B, unit,
+                           f"the float64 oracle on the {B} requests of the same workload"
+                           + (" (its own length choice once per pass over the batch, then verification)"
+                              if lens_o is not None else ""))
 
     import torch
     import lossless_draft_verification_verify_amd as sv
@@ -330,7 +463,10 @@ def main():
     def to_dev(a):
         return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    z0 = torch.from_numpy(w["logits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    if w["dtype"] == "bf16":
+        z0 = torch.from_numpy(w["logits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        z0 = to_dev(w["logits"])
     q0, x0, u0 = to_dev(w["draft_probs"]), to_dev(w["draft_tokens"]), to_dev(w["uniforms"])
     if w.get("draft_logits") is not None:        # draft logits travel in the q slot
         q0 = torch.from_numpy(w["draft_logits"].view(np.int16)).to(dev).view(torch.bfloat16)
@@ -338,21 +474,19 @@ def main():
     sets = [(z0, q0, x0, u0)] + [tuple(clone(t) for t in (z0, q0, x0, u0)) for _ in range(args.sets - 1)]
     acc = torch.empty(B, dtype=torch.int32, device=dev)
     tok = torch.empty(B, G + 1, dtype=torch.int32, device=dev)
-    # stand-in fitted temperatures (the calibration recipe's per-position values)
-    calib = W.calibration(2, G=G)[2].astype(np.float32).tolist() if args.calibrated else None
     static = None
-    if args.workload == "static":
+    if kind == "static":
         static = (to_dev(w["confidence"]), 0.5, torch.empty(B, dtype=torch.int32, device=dev),
                   torch.empty(1, dtype=torch.int32, device=dev))
     sched = None
-    if args.workload == "scheduled":
+    if kind == "scheduled":
         conf, cost = to_dev(w["confidence"]), to_dev(w["cost_table"])
         vlen = torch.empty(B, dtype=torch.int32, device=dev)
         tot = torch.empty(1, dtype=torch.int32, device=dev)
         tau = torch.empty(1, dtype=torch.float32, device=dev)
         sched = (conf, cost, w["budget"], vlen, tot, tau)
     dcut = None
-    if args.workload == "dcut":
+    if kind == "dcut":
         conf = to_dev(w["confidence"])
         vlen = torch.empty(B, dtype=torch.int32, device=dev)
         offs = torch.empty(B + 1, dtype=torch.int32, device=dev)
@@ -378,11 +512,11 @@ def main():
     def step(i, row_event=None):
         zz, qq, xx, uu = sets[i % len(sets)]
         vl = None
-        if args.workload == "logits":
+        if kind == "logits":
             sv.verify(zz, None, xx, uu, T, None, out_accepted=acc, out_tokens=tok, row_pass_event=row_event,
                       draft_logits=qq)
             return
-        if args.workload == "acceptance":
+        if kind == "acceptance":
             sv.acceptance(zz, qq, T, None, draft_is_logits=True, out_alpha=alpha)
             return
         if dcut is not None:
@@ -412,20 +546,21 @@ def main():
     elif dcut is not None:
         lens = dcut[1].cpu().numpy().astype(np.int64)
     else:
-        lens = np.full(B, G)
-    n_rej = int((a < lens).sum()) if T > 0 and args.workload != "acceptance" else 0
-    esize = 2
+        lens = np.full(B, G, np.int64)
+    if lens_o is not None and not np.array_equal(lens, lens_o):
+        raise RuntimeError("the device's verify lengths differ from the oracle's")
+    n_rej = int((a < lens).sum()) if T > 0 and kind != "acceptance" else 0
     algo = algorithmic_bytes(B, G, V, lens, n_rej, esize)
     if T == 0:                                   # no q rows, no uniforms
         algo = int((lens + 1).sum()) * V * esize + int(lens.sum()) * 4 + B * (4 + 4 * (G + 1))
     row_algo = row_pass_bytes(V, lens, esize)
-    if args.workload in ("logits", "acceptance"):
+    if kind in ("logits", "acceptance"):
         # draft rows 0..len_b-1 are read too; every q(x) and residual comes
         # from rows already read, so no fp32 q row is compulsory
         drafts = int(lens.sum()) * V * esize
         row_algo = row_algo + drafts
         algo = int((lens + 1).sum()) * V * esize + drafts + int(lens.sum()) * 8 + B * (4 + 4 + 4 * (G + 1))
-        if args.workload == "acceptance":          # one read of target row k and draft row k per position
+        if kind == "acceptance":                   # one read of target row k and draft row k per position
             row_algo = algo = 2 * int(lens.sum()) * V * esize
 
     for i in range(args.warmup):
@@ -433,7 +568,7 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    stream = torch.cuda.current_stream(dev)       # the stream spec_verify launches on
+    stream = torch.cuda.current_stream(dev)       # the stream the library launches on
     sh = stream.cuda_stream
 
     # Throughput: exactly K calls back to back, nothing else on the stream.
@@ -447,13 +582,14 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
 
-    # Kernel durations: K more calls, each bracketed by events on the same
-    # stream, plus the event the library records right after the row-pass launch.
+    # Per-call spread and the row pass alone: K more calls, each bracketed by
+    # events on the same stream, plus the event the library records right
+    # after the row-pass launch.
     hev = HipEvents(3 * K)
     torch.cuda.synchronize()
     for i in range(K):
         hev.record(3 * i, sh)
-        if args.workload == "acceptance":          # a single kernel: its own interval
+        if kind == "acceptance":                 # a single kernel: its own interval
             step(i)
             hev.record(3 * i + 1, sh)
         else:
@@ -465,46 +601,34 @@ def main():
     req_ms = np.array([hev.ms(3 * i + 1, 3 * i + 2) for i in range(K)])  # ms after it
     hev.close()
     ms_step = total_ms / K
-    kern_ms = float(rows_ms.mean())
     positions = int(lens.sum())
     value = positions / (ms_step * 1e-3)
-    achieved = row_algo / (kern_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload)
-    if args.workload == "block":
-        desc = ("block-diffusion draft verification: B=64, gamma=15, V=129280, bf16 logits "
-                "(Zipf(1.1) over a per-row permutation), fp32 draft probabilities, T=1")
-        kname = "k_rows_sampled (row pass: max and exp-sum of every read target row)"
-    elif args.workload == "greedy":
-        desc = "greedy draft verification: B=64, gamma=7, V=152064, bf16 logits N(0,4), T=0"
-        kname = "k_verify_greedy (one launch: argmax row waves, then one workgroup per request)"
-    elif args.workload == "scheduled":
-        desc = (f"confidence-scheduled verification: spec_schedule (token budget {w['budget']}, "
-                f"cost 1 + 0.02 T{', STS-calibrated' if calib else ''}) then spec_verify, B={B}, gamma=15, "
-                f"V=129280, bf16, T=1")
-        kname = "spec_schedule + k_rows_sampled (time up to the row-pass event includes the scheduler)"
-    elif args.workload == "static":
+    call_gbps = algo / (ms_step * 1e-3) / 1e9
+    row_gbps = row_algo / (float(rows_ms.mean()) * 1e-3) / 1e9
+    traffic = measured_traffic(kind)
+    if kind in DESCRIPTIONS:
+        desc = DESCRIPTIONS[kind]
+    elif kind == "scheduled":
+        desc = (f"confidence-scheduled verification: spec_schedule{'_calibrated' if calib else ''} (token budget "
+                f"{w['budget']}, cost 1 + 0.02 T) then spec_verify, B={B}, gamma=15, V=129280, bf16, T=1")
+    elif kind == "static":
         desc = (f"static-threshold verification: spec_schedule_static (confidence > 0.5"
                 f"{', STS-calibrated' if calib else ''}) then spec_verify, B={B}, gamma=15, V=129280, bf16, T=1")
-        kname = "spec_schedule_static + k_rows_sampled_vl (time up to the row-pass event includes the scheduler)"
-    elif args.workload == "logits":
-        desc = ("draft-logits verification: B=64, gamma=15, V=129280, bf16 target logits (Zipf(1.1) over a "
-                "per-row permutation) and bf16 draft logits, q = softmax(draft logits / T) on the device, T=1")
-        kname = "k_rows_sampled (row pass over the target rows and the draft rows)"
-    elif args.workload == "acceptance":
-        desc = ("acceptance diagnostics: alpha = sum min(p, q) per position, B=64, gamma=15, V=129280, bf16 target "
-                "and draft logits, T=1 (two passes over each row pair)")
-        kname = "k_acceptance (one workgroup per position; algorithmic bytes = one read of each row pair)"
     else:
         r_idx = int(dcut[3].item())
         desc_cal = ", STS-calibrated" if calib else ""
         desc = (f"ratio-budgeted verification: spec_dcut (ratios {list(w['ratios'])}, cost 1 + 0.02 rho B (G+1); "
                 f"chosen ratio {w['ratios'][r_idx]}, {int(dcut[4].item())} packed rows{desc_cal}) then "
                 f"spec_verify_packed, B={B}, gamma=15, V=129280, bf16, T=1")
-        kname = "spec_dcut + k_rows_sampled_vl (time up to the row-pass event includes the ratio choice)"
+    launches = {"acceptance": "k_acceptance (one launch)",
+                "greedy": "k_verify_greedy (one launch: argmax row workgroups, then one workgroup per request)"}
+    call_kernels = launches.get(kind, "the whole call: row pass (k_rows_sampled" +
+                                ("_vl" if lens_o is not None else "") + "), then request pass (k_requests_sampled)" +
+                                (", after the length choice" if lens_o is not None else ""))
     out = {
         "metric": "verified draft positions/sec and achieved HBM GB/s (% peak), B=64 gamma=15 V=129k",
         "value": round(value, 1),
-        "unit": "verified draft positions/s",
+        "unit": "alpha positions/s" if kind == "acceptance" else "verified draft positions/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
@@ -514,24 +638,28 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": desc, "B": B, "gamma": G, "V": V, "temperature": T, "logits": "bf16",
+        "config": {"workload": desc, "B": B, "gamma": G, "V": V, "temperature": T, "logits": w["dtype"],
                    "rotating_sets": len(sets), "verified_positions_per_step": positions,
                    "rejecting_requests": n_rej},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+        # The roofline of the verify call as a whole (every launch it makes):
+        # its algorithmic bytes over its time per call in the throughput loop.
+        "roofline": {"bound": "hbm", "achieved": round(call_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(call_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": kname,
-                     "algorithmic_bytes_per_launch": row_algo,
-                     "launch_ms_mean": round(kern_ms, 5),
-                     "launch_ms_p10_p50_p90": [round(float(np.percentile(rows_ms, p)), 5) for p in (10, 50, 90)]},
-        "call": {"algorithmic_bytes": algo,
-                 "achieved_GBps": round(algo / (ms_step * 1e-3) / 1e9, 1),
-                 "frac": round(algo / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                 "ms_p10_p50_p90": [round(float(np.percentile(call, p)), 5) for p in (10, 50, 90)],
-                 "after_row_pass_ms_mean": round(float(req_ms.mean()), 5)},
+                     "kernel": call_kernels,
+                     "algorithmic_bytes_per_launch": algo,
+                     "launch_ms_mean": round(ms_step, 5),
+                     "call_ms_p10_p50_p90_event_timed": [round(float(np.percentile(call, p)), 5)
+                                                         for p in (10, 50, 90)]},
+        "row_pass": {"algorithmic_bytes": row_algo, "ms_mean_event_timed": round(float(rows_ms.mean()), 5),
+                     "achieved_GBps": round(row_gbps, 1), "frac": round(row_gbps / PEAK_HBM_GBPS, 4),
+                     "after_row_pass_ms_mean": round(float(req_ms.mean()), 5),
+                     "note": "interval from the call's start to the library's event after the row-pass launch"},
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
+    if kind != "acceptance":
+        out["acceptance"] = acceptance_stats(a, lens)
     print(json.dumps(out), flush=True)
 
 

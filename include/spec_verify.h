@@ -16,6 +16,7 @@
  *   spec_schedule       confidence-scheduled verification depth: how many
  *                       drafts of each request to verify under a batch token
  *                       budget.
+ *   spec_schedule_calibrated  the same on temperature-calibrated confidences.
  *   spec_dcut           ratio-budgeted verification depth: the budget ratio
  *                       with the best estimated progress per profiled cost,
  *                       its keep depths and the packed row offsets.
@@ -25,8 +26,9 @@
  *                       drafts whose confidence exceeds a threshold.
  *   spec_sts_fit        Sequential Temperature Scaling: per-position
  *                       temperatures fitted left to right on acceptance data;
- *                       spec_schedule, spec_dcut and spec_schedule_static
- *                       apply them (calib_temps) as they load confidences.
+ *                       spec_schedule_calibrated, spec_dcut and
+ *                       spec_schedule_static apply them (calib_temps) as they
+ *                       load confidences.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -80,7 +82,8 @@ typedef enum { SPEC_DRAFT_PROBS = 0, SPEC_DRAFT_LOGITS = 1 } spec_draft_kind_t;
 typedef enum { SPEC_STATIC_FIXED = 0, SPEC_STATIC_THRESHOLD = 1 } spec_static_mode_t;
 
 /*
- * Calibration (every scheduler's calib_temps argument): NULL, or a host array
+ * Calibration (the calib_temps argument of spec_schedule_calibrated, spec_dcut
+ * and spec_schedule_static): NULL, or a host array
  * of G finite, positive per-position temperatures T_k ("UraionSpec", section
  * "Sequential Temperature Scaling").  Confidence c[b,k] is then read as
  * c~ = float32(c^(1/T_k)), formed in double as 2^(log2(c) / T_k), before any
@@ -310,7 +313,8 @@ size_t spec_schedule_workspace_bytes(int32_t B, int32_t G);
  *   T + 1 > token_budget; theta = (tau + s[b,k]) / cost[T+1]; if theta > best
  *   keep it (len_b = k+1, T += 1, tau += s[b,k], best = theta), else stop.
  * The result is bit-identical to that sequential loop in float64.
- * calib_temps: see "Calibration" above (NULL: confidences as given).
+ * Confidences are used as given; spec_schedule_calibrated applies per-position
+ * temperatures first.
  *
  * Arguments (device pointers unless stated):
  *   confidence          [B, G] float, per-draft acceptance estimates in [0, 1].
@@ -326,10 +330,28 @@ size_t spec_schedule_workspace_bytes(int32_t B, int32_t G);
  */
 spec_status_t spec_schedule(const float *confidence, const float *cost_table, int32_t table_len,
                             int32_t B, int32_t G, int32_t token_budget, float eps,
-                            const float *calib_temps,
                             int32_t *out_verify_len, int32_t *out_total_tokens,
                             float *out_expected_tokens,
                             void *workspace, size_t workspace_bytes, spec_stream_t stream);
+
+/*
+ * spec_schedule_calibrated -- spec_schedule on calibrated confidences
+ * ("UraionSpec", section "Sequential Temperature Scaling", applied before the
+ * prefix scheduler of section "Hardware-Aware Prefix Scheduler").
+ *
+ * Exactly spec_schedule with every confidence c[b,k] replaced by
+ * c~ = float32(c^(1/T_k)) (see "Calibration" above), where calib_temps is a
+ * host array of G finite, positive temperatures (e.g. spec_sts_fit's output,
+ * copied to the host).  calib_temps == NULL is spec_schedule itself.  The
+ * other arguments, outputs and errors are those of spec_schedule; an invalid
+ * temperature returns SPEC_ERR_BAD_SHAPE before anything is enqueued.
+ */
+spec_status_t spec_schedule_calibrated(const float *confidence, const float *calib_temps,
+                                       const float *cost_table, int32_t table_len,
+                                       int32_t B, int32_t G, int32_t token_budget, float eps,
+                                       int32_t *out_verify_len, int32_t *out_total_tokens,
+                                       float *out_expected_tokens,
+                                       void *workspace, size_t workspace_bytes, spec_stream_t stream);
 
 /*
  * spec_dcut -- ratio-budgeted verification depth (D-cut).

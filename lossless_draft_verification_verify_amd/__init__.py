@@ -147,7 +147,8 @@ def verify(target_logits, draft_probs, draft_tokens, uniforms, temperature, veri
 
 def schedule(confidence, cost_table, token_budget, eps=0.0, *, out_verify_len=None, out_total=None,
              out_expected=None, calib_temps=None):
-    """Choose per-request verify lengths.  Returns (verify_len [B], T [1], tau [1]) device tensors."""
+    """Choose per-request verify lengths.  Returns (verify_len [B], T [1], tau [1]) device tensors.
+    calib_temps: a host sequence of G temperatures (spec_schedule_calibrated), or None (spec_schedule)."""
     c = confidence
     if not isinstance(c, torch.Tensor) or c.dim() != 2:
         raise ValueError("confidence must be a [B, G] tensor")
@@ -164,12 +165,16 @@ def schedule(confidence, cost_table, token_budget, eps=0.0, *, out_verify_len=No
     if out_expected is None:
         out_expected = torch.empty(1, dtype=f32, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    st = _capi.spec_schedule(_ptr(c, f32, dev, "confidence"), _ptr(cost_table, f32, dev, "cost_table"), L, B, G,
-                             int(token_budget), float(eps), _ptr(out_verify_len, i32, dev, "out_verify_len"),
-                             _ptr(out_total, i32, dev, "out_total"), _ptr(out_expected, f32, dev, "out_expected"),
-                             0, 0, stream, calib=calib_temps)
+    args = (_ptr(cost_table, f32, dev, "cost_table"), L, B, G, int(token_budget), float(eps),
+            _ptr(out_verify_len, i32, dev, "out_verify_len"), _ptr(out_total, i32, dev, "out_total"),
+            _ptr(out_expected, f32, dev, "out_expected"), 0, 0, stream)
+    if calib_temps is None:
+        st, where = _capi.spec_schedule(_ptr(c, f32, dev, "confidence"), *args), "spec_schedule"
+    else:
+        st = _capi.spec_schedule_calibrated(_ptr(c, f32, dev, "confidence"), calib_temps, *args)
+        where = "spec_schedule_calibrated"
     if st != _capi.SPEC_OK:
-        raise SpecError(st, "spec_schedule")
+        raise SpecError(st, where)
     return out_verify_len, out_total, out_expected
 
 

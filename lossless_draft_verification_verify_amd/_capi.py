@@ -36,6 +36,7 @@ EXPORTS = (
     "spec_verify_launches",
     "spec_schedule_workspace_bytes",
     "spec_schedule",
+    "spec_schedule_calibrated",
     "spec_verify_packed",
     "spec_verify_logits",
     "spec_verify_tree",
@@ -89,8 +90,10 @@ def load():
     lib.spec_schedule_workspace_bytes.argtypes = [i32, i32]
     lib.spec_schedule_workspace_bytes.restype = sz
     fp = ctypes.POINTER(f32)
-    lib.spec_schedule.argtypes = [vp, vp, i32, i32, i32, i32, f32, fp, vp, vp, vp, vp, sz, vp]
+    lib.spec_schedule.argtypes = [vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
     lib.spec_schedule.restype = ctypes.c_int
+    lib.spec_schedule_calibrated.argtypes = [vp, fp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
+    lib.spec_schedule_calibrated.restype = ctypes.c_int
     lib.spec_verify_packed.argtypes = [vp, ctypes.c_int, i32, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp,
                                        ctypes.POINTER(DiagT), vp, sz, vp]
     lib.spec_verify_packed.restype = ctypes.c_int
@@ -146,11 +149,18 @@ def _floats(v):
     return (ctypes.c_float * max(1, len(v)))(*[float(t) for t in v])
 
 
-def spec_schedule(conf, cost, table_len, B, G, budget, eps, out_len, out_T, out_tau, ws, ws_bytes, stream,
-                  calib=None):
+def spec_schedule(conf, cost, table_len, B, G, budget, eps, out_len, out_T, out_tau, ws, ws_bytes, stream):
     return int(load().spec_schedule(conf or None, cost or None, table_len, B, G, budget, ctypes.c_float(eps),
-                                    _floats(calib), out_len or None, out_T or None, out_tau or None, ws or None,
+                                    out_len or None, out_T or None, out_tau or None, ws or None,
                                     ws_bytes, stream or None))
+
+
+def spec_schedule_calibrated(conf, calib, cost, table_len, B, G, budget, eps, out_len, out_T, out_tau, ws, ws_bytes,
+                             stream):
+    """`calib`: a host sequence of G temperatures (None = NULL)."""
+    return int(load().spec_schedule_calibrated(conf or None, _floats(calib), cost or None, table_len, B, G, budget,
+                                               ctypes.c_float(eps), out_len or None, out_T or None, out_tau or None,
+                                               ws or None, ws_bytes, stream or None))
 
 
 def spec_verify_packed(logits, dtype_code, rows, roff, q, x, u, B, G, V, T, out_acc, out_tok, diag, ws, ws_bytes,

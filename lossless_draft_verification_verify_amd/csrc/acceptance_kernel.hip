@@ -22,9 +22,10 @@
 //           cached when pass 2 reads it (7.7% faster than streaming loads at
 //           B = 64, gamma = 15, V = 129280 with draft logits);
 //   pass 2  sum of min(p, q) per thread (fp32 per eight elements, fp64 across
-//           them), then a DPP and LDS sum in fp64; each term is one fma and
-//           one v_exp_f32, p = 2^(fma(z, c, -(fl(m c) + log2 S))).  The row
-//           pair is not read again, so these loads are nontemporal.
+//           them), then a DPP and LDS sum in fp64; each term's exponent is
+//           fma(z, c, -fl(m c)) - log2 S, and with draft logits a term is
+//           2^min(a, b), one v_exp_f32.  The row pair is not read again, so
+//           these loads are nontemporal.
 // Both passes are bound by the two reads of the row pair once the terms cost
 // two instructions each.
 // A row holding a NaN, whose maximum is +inf, or which is entirely -inf gives
@@ -100,8 +101,15 @@ struct MS {
     float m, s;
     bool nan;
 };
+// s, a sum taken against reference m_from, rescaled to reference m_to >=
+// m_from.  Sums use the rounded reference R = fl(m c) (see ms_add8), so the
+// factor is 2^(fl(m_from c) - fl(m_to c)) (an exact difference of the two
+// references), which makes the references' rounding cancel; where m c
+// overflows, 2^((m_from - m_to) c).
 __device__ __forceinline__ float rescale(float s, float m_from, float m_to, float c) {
-    return (m_from == ninf()) ? 0.0f : s * exp2n((m_from - m_to) * c);
+    if (m_from == ninf()) return 0.0f;
+    const float r_from = m_from * c, r_to = m_to * c;
+    return s * ((fin(r_from) && fin(r_to)) ? exp2n(r_from - r_to) : exp2n((m_from - m_to) * c));
 }
 __device__ __forceinline__ void ms_add8(MS &a, const float (&f)[kAE], float c) {
     float cm = f[0];
@@ -179,13 +187,16 @@ __device__ void ms_block(MS (&v)[2], int nrow, float c, ASmem &sh) {
     }
 }
 
-// Pass 2 over the row pair: sum of min(p, q) per thread.  FAST: p = 2^(fma(z,
-// c, -Lp)) with Lp = fl(mp c) + log2 Sp (likewise q); else 2^((z - mp) c -
-// log2 Sp), for temperatures so small that m c overflows.
+// Pass 2 over the row pair: sum of min(p, q) per thread.  The exponent of p
+// is a = fma(z, c, -fl(mp c)) - log2 Sp: the reference is subtracted before
+// log2 Sp, so the exponent's rounding is relative to |a| (small for the terms
+// that carry the mass), not to |mp c|.  With draft logits b is formed the same
+// way and min(p, q) = 2^min(a, b) (2^x is monotone), one exp per term.  Where
+// m c overflows (a tiny T), a = (z - mp) c - log2 Sp (FAST false).
 template <int ES, bool AL, bool QL, bool FAST>
 __device__ double overlap_rows(const void *zrow, const void *drow, int V, int t, float c, float mp, float lsp,
                                float mq, float lsq) {
-    const float Lp = mp * c + lsp, Lq = mq * c + lsq;
+    const float Rp = mp * c, Rq = mq * c;
     double acc = 0.0;
     for (int base = 0; base < V; base += kAStep * kAU) {
         float fz[kAU][kAE], fd[kAU][kAE];
@@ -201,10 +212,13 @@ __device__ double overlap_rows(const void *zrow, const void *drow, int V, int t,
             float s = 0.0f;
 #pragma unroll
             for (int i = 0; i < kAE; ++i) {
-                const float p = FAST ? exp2n(__builtin_fmaf(fz[u][i], c, -Lp)) : exp2n((fz[u][i] - mp) * c - lsp);
-                float q = fd[u][i];
-                if constexpr (QL) q = FAST ? exp2n(__builtin_fmaf(q, c, -Lq)) : exp2n((q - mq) * c - lsq);
-                s = s + fminf(p, q);
+                const float ea = (FAST ? __builtin_fmaf(fz[u][i], c, -Rp) : (fz[u][i] - mp) * c) - lsp;
+                if constexpr (QL) {
+                    const float eb = (FAST ? __builtin_fmaf(fd[u][i], c, -Rq) : (fd[u][i] - mq) * c) - lsq;
+                    s = s + exp2n(fminf(ea, eb));
+                } else {
+                    s = s + fminf(exp2n(ea), fd[u][i]);
+                }
             }
             acc = acc + double(s);
         }
@@ -259,8 +273,9 @@ __global__ __launch_bounds__(kAT) void k_acceptance(AcceptArgs a) {
         if (t == 0) *out = __builtin_nanf("");
         return;
     }
-    const float mp = v[0].m, lsp = __log2f(v[0].s);
-    const float mq = QL ? v[1].m : 0.0f, lsq = QL ? __log2f(v[1].s) : 0.0f;
+    // log2 of the sums, correctly rounded (once per workgroup)
+    const float mp = v[0].m, lsp = float(log2(double(v[0].s)));
+    const float mq = QL ? v[1].m : 0.0f, lsq = QL ? float(log2(double(v[1].s))) : 0.0f;
 
     // Pass 2: sum of min(p, q).
     const bool fast = fin(mp * c) && (!QL || fin(mq * c));

@@ -343,12 +343,15 @@ int32_t spec_verify_launches(int32_t B, int32_t G, int32_t V, spec_dtype_t dt, f
 
 size_t spec_schedule_workspace_bytes(int32_t, int32_t) { return 0; }
 
-spec_status_t spec_schedule(const float *confidence, const float *cost_table, int32_t table_len, int32_t B,
-                            int32_t G, int32_t token_budget, float eps, const float *calib_temps,
+}  // extern "C"
+
+namespace {
+
+// spec_schedule and spec_schedule_calibrated (calib_temps NULL: as given).
+spec_status_t schedule_impl(const float *confidence, const float *calib_temps, const float *cost_table,
+                            int32_t table_len, int32_t B, int32_t G, int32_t token_budget, float eps,
                             int32_t *out_verify_len, int32_t *out_total_tokens, float *out_expected_tokens,
-                            void *workspace, size_t workspace_bytes, spec_stream_t stream) {
-    (void)workspace;
-    (void)workspace_bytes;
+                            spec_stream_t stream) {
     if (B < 1 || G < 0 || table_len < 1) return SPEC_ERR_BAD_SHAPE;
     if (int64_t(B) * G > SPEC_MAX_SCHEDULE_CANDIDATES || B > SPEC_MAX_SCHEDULE_CANDIDATES)
         return SPEC_ERR_UNSUPPORTED;
@@ -370,6 +373,31 @@ spec_status_t spec_schedule(const float *confidence, const float *cost_table, in
     a.out_T = out_total_tokens;
     a.out_tau = out_expected_tokens;
     return sv::launch_schedule(a, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+spec_status_t spec_schedule(const float *confidence, const float *cost_table, int32_t table_len, int32_t B,
+                            int32_t G, int32_t token_budget, float eps, int32_t *out_verify_len,
+                            int32_t *out_total_tokens, float *out_expected_tokens, void *workspace,
+                            size_t workspace_bytes, spec_stream_t stream) {
+    (void)workspace;            // spec_schedule_workspace_bytes is 0: the scheduler works in LDS
+    (void)workspace_bytes;
+    return schedule_impl(confidence, nullptr, cost_table, table_len, B, G, token_budget, eps, out_verify_len,
+                         out_total_tokens, out_expected_tokens, stream);
+}
+
+spec_status_t spec_schedule_calibrated(const float *confidence, const float *calib_temps, const float *cost_table,
+                                       int32_t table_len, int32_t B, int32_t G, int32_t token_budget, float eps,
+                                       int32_t *out_verify_len, int32_t *out_total_tokens,
+                                       float *out_expected_tokens, void *workspace, size_t workspace_bytes,
+                                       spec_stream_t stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return schedule_impl(confidence, calib_temps, cost_table, table_len, B, G, token_budget, eps, out_verify_len,
+                         out_total_tokens, out_expected_tokens, stream);
 }
 
 spec_status_t spec_schedule_static(const float *confidence, int32_t B, int32_t G, spec_static_mode_t mode,

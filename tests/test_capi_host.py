@@ -102,11 +102,63 @@ def test_verify_diag_alignment_checked():
     assert _verify(diag=d) == 8
 
 
-def _sched(**kw):
+def _sched(calib=None, **kw):
     args = dict(conf=Q, cost=U, table_len=513, B=4, G=15, budget=512, eps=0.0, out_len=OA, out_T=OT,
                 out_tau=X, ws=0, ws_bytes=0, stream=0)
     args.update(kw)
-    return _capi.spec_schedule(**args)
+    if calib is None:
+        return _capi.spec_schedule(**args)
+    return _capi.spec_schedule_calibrated(calib=calib, **args)
+
+
+def _declaration(name):
+    """(type, name) pairs of a function's parameters as include/spec_verify.h declares it."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    out = []
+    for p in m.group(1).split(","):
+        p = " ".join(p.replace("*", " * ").split())
+        typ, _, nm = p.rpartition(" ")
+        out.append((typ.replace(" *", "*"), nm))
+    return out
+
+
+# The scheduler's boundary as the hot-path scope fixes it: confidences, cost
+# table and budget in, lengths and totals out, then the workspace and stream.
+SCHEDULE_PROTOTYPE = [
+    ("const float*", "confidence"), ("const float*", "cost_table"), ("int32_t", "table_len"),
+    ("int32_t", "B"), ("int32_t", "G"), ("int32_t", "token_budget"), ("float", "eps"),
+    ("int32_t*", "out_verify_len"), ("int32_t*", "out_total_tokens"), ("float*", "out_expected_tokens"),
+    ("void*", "workspace"), ("size_t", "workspace_bytes"), ("spec_stream_t", "stream"),
+]
+VERIFY_PROTOTYPE = [
+    ("const void*", "target_logits"), ("spec_dtype_t", "target_dtype"), ("const float*", "draft_probs"),
+    ("const int32_t*", "draft_tokens"), ("const float*", "uniforms"), ("const int32_t*", "verify_len"),
+    ("int32_t", "B"), ("int32_t", "G"), ("int32_t", "V"), ("float", "temperature"),
+    ("int32_t*", "out_accepted"), ("int32_t*", "out_tokens"), ("const spec_verify_diag_t*", "diag"),
+    ("void*", "workspace"), ("size_t", "workspace_bytes"), ("spec_stream_t", "stream"),
+]
+
+
+def test_boundary_prototypes_are_pinned():
+    assert _declaration("spec_schedule") == SCHEDULE_PROTOTYPE
+    assert _declaration("spec_verify") == VERIFY_PROTOTYPE
+    # the calibrated scheduler is spec_schedule with the host temperatures after the confidences
+    cal = _declaration("spec_schedule_calibrated")
+    assert cal == SCHEDULE_PROTOTYPE[:1] + [("const float*", "calib_temps")] + SCHEDULE_PROTOTYPE[1:]
+    # the binding's ctypes prototype has as many arguments as the declaration
+    lib = _capi.load()
+    assert len(lib.spec_schedule.argtypes) == len(SCHEDULE_PROTOTYPE)
+    assert len(lib.spec_schedule_calibrated.argtypes) == len(cal)
+    assert len(lib.spec_verify.argtypes) == len(VERIFY_PROTOTYPE)
+
+
+def test_calibrated_schedule_validates_like_schedule():
+    # every argument error of spec_schedule is reported the same way by the calibrated entry point
+    for kw, status in [(dict(B=0), 2), (dict(budget=513), 2), (dict(conf=0), 1), (dict(out_len=0), 1),
+                       (dict(conf=Q + 1), 8), (dict(B=300, G=15, budget=400), 6)]:
+        assert _sched(calib=[1.0] * kw.get("G", 15), **kw) == status, kw
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -165,3 +165,27 @@ def test_fit_then_calibrated_schedule():
     lo, To, _ = oracle.schedule(C.sts_apply(c64, temps), cost, 512)
     np.testing.assert_array_equal(vl.cpu().numpy(), lo)
     say(f"    calibrated schedule T={To} (uncalibrated {oracle.schedule(c64, cost, 512)[1]})")
+
+
+@pytest.mark.parametrize("calibrated", [False, True])
+def test_static_threshold_then_verify_full_size(calibrated):
+    """spec_schedule_static (threshold 0.5) feeding spec_verify on the device at
+    the full vocabulary (B = 64, G = 15, V = 129280): the verify-length row
+    pass runs about two row jobs per workgroup.  Lengths exact against the
+    oracle's static threshold; lengths, tokens and diagnostics of the verify
+    against the oracle's verification with those lengths."""
+    from parity_util import compare, run_gpu, run_oracle
+    w = W.scheduled(64)
+    conf = w["confidence"]
+    temps = W.calibration(2, G=15)[2].astype(np.float32).tolist() if calibrated else None
+    say(f"[parity] static threshold 0.5 then verify, B=64 V=129280 calibrated={calibrated}")
+    vl, T, _ = sv.schedule_static(torch.from_numpy(conf).cuda(), threshold=0.5, calib_temps=temps,
+                                  row_offsets=False)
+    torch.cuda.synchronize()
+    n = C.static_threshold(conf if temps is None else C.sts_apply(conf, temps), 0.5)
+    np.testing.assert_array_equal(vl.cpu().numpy(), n)
+    assert int(T.item()) == int((n + 1).sum())
+    g = run_gpu(w, verify_len=vl)
+    o = run_oracle(w, n)
+    rep = compare(w, g, o, n)
+    say("   ", rep, "positions", int(n.sum()))

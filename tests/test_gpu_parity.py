@@ -479,3 +479,22 @@ def test_full_lengths_through_the_length_pass_many_jobs():
     torch.cuda.synchronize()
     assert torch.equal(acc0, acc1) and torch.equal(tok0, tok1)
     assert int((acc0 < 0).sum()) == 0
+
+
+@pytest.mark.parametrize("lengths", ["random", "full"])
+def test_verify_length_pass_many_jobs_against_oracle(lengths):
+    """B = 256, G = 15, V = 32768 through the verify-length row pass (the
+    largest batch that takes it): each workgroup runs two to four row jobs.
+    Random lengths in [0, 15] (zeros and full lengths included) and every
+    length G, against the oracle: lengths and tokens under the verify rule,
+    p(x_k), q(x_k), R and the row log-sum-exp within their tolerances."""
+    B, G, V = 256, 15, 32768
+    w = W.block(B=B, G=G, V=V, seed=1718)
+    if lengths == "random":
+        vl = np.random.default_rng(1718).integers(0, G + 1, size=B).astype(np.int32)
+        vl[:8] = [0, G, 0, G, 1, G - 1, 7, G]
+    else:
+        vl = np.full(B, G, np.int32)
+    w["verify_len"] = vl
+    rep = check(w, vl)
+    assert rep["requests"] == B
