@@ -496,5 +496,5 @@ def test_verify_length_pass_many_jobs_against_oracle(lengths):
     else:
         vl = np.full(B, G, np.int32)
     w["verify_len"] = vl
-    rep = check(w, vl)
-    assert rep["requests"] == B
+    _, _, rep = check(w, vl)
+    assert rep["requests"] == B and rep["exact"] + rep["flagged_and_differ"] == B
