@@ -67,8 +67,10 @@ typedef enum {
     SPEC_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < the *_workspace_bytes query   */
     SPEC_ERR_UNSUPPORTED = 6,         /* valid but beyond this build's limits            */
     SPEC_ERR_DEVICE = 7,              /* HIP error while querying the device or launching */
-    SPEC_ERR_MISALIGNED = 8           /* a pointer is not aligned to its element type /
+    SPEC_ERR_MISALIGNED = 8,          /* a pointer is not aligned to its element type /
                                          the workspace is not 256-byte aligned           */
+    SPEC_ERR_SCRATCH_TOO_SMALL = 9    /* spec_verify_noalloc: the shape needs more than
+                                         SPEC_NOALLOC_SCRATCH_BYTES of workspace          */
 } spec_status_t;
 
 typedef enum { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 } spec_dtype_t;
@@ -294,6 +296,35 @@ spec_status_t spec_verify_tree(const void *target_logits, spec_dtype_t target_dt
  * invalid arguments or a failed device query.  Host-only; enqueues nothing.
  */
 int32_t spec_verify_launches(int32_t B, int32_t G, int32_t V, spec_dtype_t target_dtype, float temperature);
+
+/* Workspace bytes held by spec_verify_noalloc's static scratch (per GPU). */
+#define SPEC_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * spec_verify_noalloc -- spec_verify for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same operation, arguments, outputs and errors as
+ * spec_verify, without the workspace arguments.
+ *
+ * The workspace is a static device array of SPEC_NOALLOC_SCRATCH_BYTES inside
+ * the library; each GPU the library runs on holds its own copy until the
+ * process ends.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine); on its first use on a device it looks up that device's
+ * address of the array.  Each call clears the part of the array it uses (a
+ * fill kernel on `stream`) and then launches exactly what spec_verify does.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (on two streams, or from two host threads) race and must not be
+ * made.  A shape whose spec_verify_workspace_bytes exceeds
+ * SPEC_NOALLOC_SCRATCH_BYTES (about B = 490 requests at G = 15, V = 129280,
+ * bf16) returns SPEC_ERR_SCRATCH_TOO_SMALL before anything is enqueued.
+ */
+spec_status_t spec_verify_noalloc(const void *target_logits, spec_dtype_t target_dtype,
+                                  const float *draft_probs, const int32_t *draft_tokens,
+                                  const float *uniforms, const int32_t *verify_len,
+                                  int32_t B, int32_t G, int32_t V, float temperature,
+                                  int32_t *out_accepted, int32_t *out_tokens,
+                                  const spec_verify_diag_t *diag, spec_stream_t stream);
 
 /* Bytes of device workspace spec_schedule needs (currently 0: it works in LDS). */
 size_t spec_schedule_workspace_bytes(int32_t B, int32_t G);

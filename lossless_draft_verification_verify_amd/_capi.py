@@ -21,7 +21,9 @@ STATUS_NAMES = {
     6: "SPEC_ERR_UNSUPPORTED",
     7: "SPEC_ERR_DEVICE",
     8: "SPEC_ERR_MISALIGNED",
+    9: "SPEC_ERR_SCRATCH_TOO_SMALL",
 }
+NOALLOC_SCRATCH_BYTES = 8 << 20
 SPEC_DTYPE_F32 = 0
 SPEC_DTYPE_BF16 = 1
 SPEC_DRAFT_PROBS = 0
@@ -34,6 +36,7 @@ EXPORTS = (
     "spec_verify_workspace_bytes",
     "spec_verify",
     "spec_verify_launches",
+    "spec_verify_noalloc",
     "spec_schedule_workspace_bytes",
     "spec_schedule",
     "spec_schedule_calibrated",
@@ -85,6 +88,9 @@ def load():
     lib.spec_verify.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp,
                                 ctypes.POINTER(DiagT), vp, sz, vp]
     lib.spec_verify.restype = ctypes.c_int
+    lib.spec_verify_noalloc.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp,
+                                        ctypes.POINTER(DiagT), vp]
+    lib.spec_verify_noalloc.restype = ctypes.c_int
     lib.spec_verify_launches.argtypes = [i32, i32, i32, ctypes.c_int, f32]
     lib.spec_verify_launches.restype = i32
     lib.spec_schedule_workspace_bytes.argtypes = [i32, i32]
@@ -140,6 +146,14 @@ def spec_verify(logits, dtype_code, q, x, u, vlen, B, G, V, T, out_acc, out_tok,
     return int(load().spec_verify(logits or None, dtype_code, q or None, x or None, u or None, vlen or None,
                                   B, G, V, ctypes.c_float(T), out_acc or None, out_tok or None, d,
                                   ws or None, ws_bytes, stream or None))
+
+
+def spec_verify_noalloc(logits, dtype_code, q, x, u, vlen, B, G, V, T, out_acc, out_tok, diag, stream):
+    """Raw call of the no-allocation variant (static scratch); returns the status."""
+    d = ctypes.byref(diag) if diag is not None else None
+    return int(load().spec_verify_noalloc(logits or None, dtype_code, q or None, x or None, u or None,
+                                          vlen or None, B, G, V, ctypes.c_float(T), out_acc or None,
+                                          out_tok or None, d, stream or None))
 
 
 def _floats(v):

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libspecverify.so")
 SOURCES = ["capi.cpp", "verify_kernels.hip", "schedule_kernel.hip", "acceptance_kernel.hip",
-           "calibration_kernel.hip"]
+           "calibration_kernel.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 # -ffp-contract=off: every fp expression is evaluated as written (the final

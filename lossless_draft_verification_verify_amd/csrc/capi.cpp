@@ -13,6 +13,7 @@
 
 static_assert(SPEC_MAX_BATCH == sv::kMaxBatch, "one batch limit for the header and the kernels");
 static_assert(SPEC_MAX_RATIOS == sv::kMaxRatios, "one ratio limit for the header and the kernels");
+static_assert(SPEC_NOALLOC_SCRATCH_BYTES == sv::kNoAllocScratchBytes, "one scratch size for the header and the library");
 
 namespace {
 
@@ -105,6 +106,9 @@ const char *spec_status_string(spec_status_t s) {
     case SPEC_ERR_UNSUPPORTED: return "shape beyond this build's limits";
     case SPEC_ERR_DEVICE: return "HIP error while querying the device or launching";
     case SPEC_ERR_MISALIGNED: return "pointer misaligned for its element type (workspace: 256 bytes)";
+    case SPEC_ERR_SCRATCH_TOO_SMALL:
+        return "spec_verify_noalloc: the shape needs more workspace than the static scratch holds "
+               "(SPEC_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }
@@ -127,7 +131,7 @@ spec_status_t verify_impl(const void *target_logits, spec_dtype_t target_dtype, 
                           const float *uniforms, const int32_t *verify_len, int32_t B, int32_t G, int32_t V,
                           float temperature, int32_t *out_accepted, int32_t *out_tokens,
                           const spec_verify_diag_t *diag, void *workspace, size_t workspace_bytes,
-                          spec_stream_t stream) {
+                          spec_stream_t stream, bool noalloc = false) {
     // ---- host-checkable errors, before anything touches the device
     const int es = esize_of(int(target_dtype));
     if (es == 0) return SPEC_ERR_BAD_DTYPE;
@@ -157,9 +161,21 @@ spec_status_t verify_impl(const void *target_logits, spec_dtype_t target_dtype, 
         !aligned(dg.resid_mass, 4))
         return SPEC_ERR_MISALIGNED;
     const Layout lay = sv::make_layout(B, G, V, es);
-    if (!workspace) return SPEC_ERR_NULL_POINTER;
-    if (!aligned(workspace, 256)) return SPEC_ERR_MISALIGNED;
-    if (workspace_bytes < lay.total) return SPEC_ERR_WORKSPACE_TOO_SMALL;
+    if (noalloc) {
+        // the static scratch stands in for the workspace
+        if (lay.total > sv::kNoAllocScratchBytes) return SPEC_ERR_SCRATCH_TOO_SMALL;
+    } else {
+        if (!workspace) return SPEC_ERR_NULL_POINTER;
+        if (!aligned(workspace, 256)) return SPEC_ERR_MISALIGNED;
+        if (workspace_bytes < lay.total) return SPEC_ERR_WORKSPACE_TOO_SMALL;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SPEC_ERR_DEVICE;
+    if (noalloc) {
+        // this device's address of the scratch, then clear what the call uses
+        if (sv::noalloc_scratch(dev, &workspace) != 0) return SPEC_ERR_DEVICE;
+        if (sv::launch_zero(workspace, lay.total, stream) != 0) return SPEC_ERR_DEVICE;
+    }
 
     // ---- launch plan
     sv::VerifyArgs a = {};
@@ -191,8 +207,6 @@ spec_status_t verify_impl(const void *target_logits, spec_dtype_t target_dtype, 
     const bool az = aligned(target_logits, 16) && (size_t(V) * es) % 16 == 0;
     const bool aq = a.dl ? aligned(a.dl, 16) && (size_t(V) * es) % 16 == 0 : aligned(draft_probs, 16) && V % 4 == 0;
 
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return SPEC_ERR_DEVICE;
     if (sampled) {
         // Row pass, then request pass (the kernel boundary orders every row
         // partial before the per-request work, across all XCDs).  One row
@@ -263,6 +277,15 @@ spec_status_t spec_verify(const void *target_logits, spec_dtype_t target_dtype, 
     return verify_impl(target_logits, target_dtype, nullptr, 0, draft_probs, nullptr, draft_tokens, uniforms,
                        verify_len, B, G, V, temperature, out_accepted, out_tokens, diag, workspace, workspace_bytes,
                        stream);
+}
+
+spec_status_t spec_verify_noalloc(const void *target_logits, spec_dtype_t target_dtype, const float *draft_probs,
+                                  const int32_t *draft_tokens, const float *uniforms, const int32_t *verify_len,
+                                  int32_t B, int32_t G, int32_t V, float temperature, int32_t *out_accepted,
+                                  int32_t *out_tokens, const spec_verify_diag_t *diag, spec_stream_t stream) {
+    return verify_impl(target_logits, target_dtype, nullptr, 0, draft_probs, nullptr, draft_tokens, uniforms,
+                       verify_len, B, G, V, temperature, out_accepted, out_tokens, diag, nullptr, 0, stream,
+                       /*noalloc=*/true);
 }
 
 spec_status_t spec_verify_logits(const void *target_logits, spec_dtype_t target_dtype, const void *draft_logits,

@@ -102,6 +102,13 @@ int launch_verify_greedy(const VerifyArgs &a, bool aligned_z, int esize, int gri
 int greedy_occupancy(bool aligned_z, int esize, int *blocks_per_cu);
 int launch_tree_walk(const VerifyArgs &a, int grid, void *stream);
 
+// Static scratch of spec_verify_noalloc (noalloc.hip): its size, this
+// device's address of it (asked once per device), and a fill kernel that
+// clears its first `bytes` (a multiple of 256) on `stream`.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+int noalloc_scratch(int dev, void **out);
+int launch_zero(void *p, size_t bytes, void *stream);
+
 constexpr int kMaxDrafts = 255;
 // Sequential Temperature Scaling, applied as confidences are loaded:
 // c~ = float32(2^(log2(c) / T_k)) in double, when calib is set.

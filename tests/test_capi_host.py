@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for code in range(9):
+    for code in range(10):
         s = _capi.status_string(code)
         assert isinstance(s, str) and s and s != "unknown status"
     assert _capi.status_string(99) == "unknown status"
@@ -339,3 +339,29 @@ def test_verify_tree_rejects_bad_arguments(kw, status):
 
 def test_verify_tree_root_only_needs_no_tree():
     assert _tree(M=1, par=0, tok=0, ws_bytes=10) == 5
+
+
+def _noalloc(**kw):
+    args = dict(logits=Z, dtype_code=1, q=Q, x=X, u=U, vlen=0, B=4, G=3, V=1000, T=1.0, out_acc=OA, out_tok=OT,
+                diag=None, stream=0)
+    args.update(kw)
+    return _capi.spec_verify_noalloc(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype_code=5), 4), (dict(B=0), 2), (dict(G=256), 6), (dict(T=-1.0), 3),
+    (dict(logits=0), 1), (dict(q=0), 1), (dict(u=0), 1), (dict(out_acc=0), 1),
+    (dict(logits=Z + 1), 8), (dict(vlen=VL + 2), 8),
+    # beyond the static scratch: refused before any device call
+    (dict(B=1000, G=15, V=129280), 9), (dict(B=65536, G=3, V=8192), 9),
+])
+def test_noalloc_rejects_bad_arguments(kw, status):
+    assert _noalloc(**kw) == status
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define SPEC_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _capi.NOALLOC_SCRATCH_BYTES
+    # the headline shape fits, with room for several times its batch
+    assert _capi.verify_workspace_bytes(64, 15, 129280, _capi.SPEC_DTYPE_BF16) * 7 < _capi.NOALLOC_SCRATCH_BYTES
