@@ -117,10 +117,9 @@ typedef void *spec_stream_t;
  *                        row j; -1 when every verified draft was accepted
  *
  * row_pass_event is a hipEvent_t (opaque) created by the caller, for timing:
- * spec_verify records it on `stream` right after the launch of the pass over
- * the target rows (T > 0 always; T == 0 after the row launch when the call is
- * split in two launches, else after its single launch).  It costs one event
- * record and no extra memory traffic.
+ * the call records it on `stream` right after the launch that reads the target
+ * rows: after the row launch when the call makes two launches, else after its
+ * single launch.  It costs one event record and no extra memory traffic.
  */
 typedef struct {
     float *target_lse;
@@ -290,10 +289,13 @@ spec_status_t spec_verify_tree(const void *target_logits, spec_dtype_t target_dt
 
 /*
  * Number of kernel launches spec_verify makes for this shape on the current
- * device, with 16-byte-aligned target_logits: 2 for T > 0 (the pass over the
- * target rows, then the per-request pass); for T == 0, 1 when the per-request
- * work shares the row launch and 2 when it runs as a second launch.  -1 on
- * invalid arguments or a failed device query.  Host-only; enqueues nothing.
+ * device, with 16-byte-aligned target_logits and verify_len NULL: for T > 0,
+ * 1 (the row workgroups, a decision workgroup per request and the request
+ * workgroups share one grid; with verify lengths and B <= 256, or with draft
+ * logits, spec_verify and spec_verify_logits make 2: the pass over the read
+ * rows, then the per-request pass); for T == 0, 1 when the per-request work
+ * shares the row launch and 2 when it runs as a second launch.  -1 on invalid
+ * arguments or a failed device query.  Host-only; enqueues nothing.
  */
 int32_t spec_verify_launches(int32_t B, int32_t G, int32_t V, spec_dtype_t target_dtype, float temperature);
 

@@ -34,7 +34,7 @@ spec_status_t check_verify_shape(int64_t B, int64_t G, int64_t V, int es) {
     if (B > SPEC_MAX_BATCH || G > SPEC_MAX_DRAFTS || V > SPEC_MAX_VOCAB) return SPEC_ERR_UNSUPPORTED;
     const int64_t nc1 = (V + sv::chunk_elems(es) - 1) / sv::chunk_elems(es);
     const int64_t nsub = (V + sv::kSub - 1) / sv::kSub;
-    const int64_t items = B * ((2 * G + 1) * nc1 + nsub);   // row waves (target and draft rows) + request workgroups
+    const int64_t items = B * ((2 * G + 1) * nc1 + nsub + 1);   // row groups (target, draft rows) + decision + request workgroups
     if (items >= (int64_t(1) << 31)) return SPEC_ERR_UNSUPPORTED;
     if (B * (G + 1) > (int64_t(1) << 40) / V) return SPEC_ERR_UNSUPPORTED;
     return SPEC_OK;
@@ -223,7 +223,27 @@ spec_status_t verify_impl(const void *target_logits, spec_dtype_t target_dtype, 
             a.spw = spw;
         }
         a.nc2 = (a.nsub + a.spw - 1) / a.spw;
-        if ((verify_len || row_offsets) && B <= sv::kWG) {
+        const bool vl_pass = (verify_len || row_offsets) && B <= sv::kWG;
+        if (!a.dl && !vl_pass) {
+            // One launch (draft probabilities, full-grid row layout): the row
+            // workgroups, one decision workgroup per request (in grid order one
+            // request after its rows), then the request workgroups, which only
+            // poll the request's decision record: about 2048 of them in all
+            // (B = 64: 2048 at 55.0 us per call, against 1024 at 55.9 and 4096
+            // at 55.4).  Each waits only on workgroups before it in grid order.
+            const long want = (long(B) * a.nsub + 2047) / 2048;
+            int spw = 1;
+            while (spw < want && spw < 8) spw <<= 1;
+            a.spw = spw;
+            a.nc2 = (a.nsub + a.spw - 1) / a.spw;
+            a.lag = 1;
+            if (sv::launch_verify_sampled(a, az, aq, es, int(row_groups + long(B) * (1 + a.nc2)), stream) != 0)
+                return SPEC_ERR_DEVICE;
+            if (row_event && hipEventRecord(row_event, static_cast<hipStream_t>(stream)) != hipSuccess)
+                return SPEC_ERR_DEVICE;
+            return SPEC_OK;
+        }
+        if (vl_pass) {
             // Verify lengths leave rows unread: a grid of two resident loads of
             // workgroups (no workgroup waits on another) whose workgroups visit
             // only the read row groups.  Two loads measured best: one leaves
@@ -357,7 +377,7 @@ int32_t spec_verify_launches(int32_t B, int32_t G, int32_t V, spec_dtype_t dt, f
     const int es = esize_of(int(dt));
     if (es == 0 || check_verify_shape(B, G, V, es) != SPEC_OK) return -1;
     if (!std::isfinite(temperature) || temperature < 0.0f) return -1;
-    if (temperature > 0.0f) return 2;                 // row pass, then request pass
+    if (temperature > 0.0f) return 1;                 // one launch (verify_len NULL: the full-grid row layout)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return -1;
     const int one = greedy_one_launch(dev, (size_t(V) * es) % 16 == 0, es, B);

@@ -36,7 +36,12 @@ inline int chunk_elems(int esize) { return 64 * kRowVec * (16 / esize); }
 //            bit 63 set once written;
 //   gx       [B*G] u64: the row pass's gather of draft k (sampled only):
 //            low = fp32 bits of z[b,k,x_k], high = bits of q[b,k,x_k] (with
-//            draft logits: of d[b,k,x_k], stored by the draft row's pass).
+//            draft logits: of d[b,k,x_k], stored by the draft row's pass;
+//            in the one-launch verify, max(q, 0) with bit 63 set once written);
+//   dec      [B] 2 u64: the one-launch verify's decision record of request b,
+//            each word with bit 63 set once written: word 0 low = fp32 bits
+//            of m_j, high = j | resid << 15 | ok << 16; word 1 low = fp32
+//            bits of 1 / S_j.
 
 constexpr int kMaxBatch = 65536;
 constexpr uint32_t kValid = 0x80000000u;
@@ -47,6 +52,7 @@ struct Layout {
     size_t partd;
     size_t mass;
     size_t gx;
+    size_t dec;
     size_t total;
 };
 
@@ -62,6 +68,7 @@ inline Layout make_layout(int64_t B, int64_t G, int64_t V, int esize) {
     L.partd = o; o += align256(size_t(B) * size_t(G) * size_t(nc1) * 8);
     L.mass = o; o += align256(size_t(B) * size_t(nsub) * 16);
     L.gx = o; o += align256(size_t(B) * size_t(G) * 8);
+    L.dec = o; o += align256(size_t(B) * 16);
     L.total = o;
     return L;
 }
@@ -91,6 +98,7 @@ struct VerifyArgs {
     const int32_t *tpar, *ttok;   // tree walk: [B, G+1] parents and tokens of the candidate nodes
     int32_t *out_path;            // tree walk: [B, G+1] accepted nodes, then -1
     uint32_t spin_limit;
+    int32_t lag;                  // one-launch verify: requests between a request's rows and its decision workgroup
 };
 
 // Launchers (verify_kernels.hip).  Return a hipError_t as int.
@@ -98,6 +106,8 @@ int launch_rows_sampled(const VerifyArgs &a, bool aligned_z, int esize, int grid
 int launch_rows_sampled_vl(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
 int launch_requests_sampled(const VerifyArgs &a, bool aligned_z, bool aligned_q, int esize, int grid,
                             void *stream);   // draft logits when a.dl is set
+// One launch: the row workgroups, then the request workgroups (draft probabilities only).
+int launch_verify_sampled(const VerifyArgs &a, bool aligned_z, bool aligned_q, int esize, int grid, void *stream);
 int launch_verify_greedy(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
 int greedy_occupancy(bool aligned_z, int esize, int *blocks_per_cu);
 int launch_tree_walk(const VerifyArgs &a, int grid, void *stream);

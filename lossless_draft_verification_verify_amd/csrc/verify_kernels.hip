@@ -12,43 +12,49 @@
 // How it maps to the chip
 // -----------------------
 // The work is a bandwidth-bound streaming reduction (no contraction, so no
-// MFMA).  Temperature > 0 runs as two launches on the caller's stream:
+// MFMA).  With draft probabilities and the full [B, G+1, V] row layout a
+// temperature > 0 call is one launch, k_verify_sampled, whose grid holds three
+// kinds of workgroup:
 //
-//   row pass       one workgroup per (request, row, 8192-element group), one
-//                  wave per 2048-element chunk: four 16-byte streaming loads
-//                  per lane, the chunk maximum, then the sum of
-//                  2^((z - m) * log2(e)/T), both reduced across the wave with
-//                  DPP; the four waves' (max, sum) pairs merge in LDS into one
-//                  64-bit partial per group.  The wave whose chunk holds draft
-//                  token x_k also records z(x_k) and q(x_k), so the request
-//                  pass has no dependent gathers.  With verify lengths (at most
-//                  256 requests) a grid of twice the resident workgroups
-//                  visits only the read row groups instead.
-//   request pass   nc2 draw workgroups per request, each streaming spw
-//                  2048-element sub-tiles of the draw row (spw sized for about
-//                  1024 draw workgroups in all).  Each merges the request's
-//                  partials per row (16 lanes per row, fp64 sums), runs the
-//                  accept tests and finds the first rejection j (every
-//                  workgroup of the request computes the same result), then
-//                  streams its sub-tiles of the one row the final token is drawn
-//                  from (target row j, plus draft row j on a rejection) and
-//                  writes fp64 sub-tile masses, each word marked as written.
+//   row groups     one per (request, row, 8192-element group), one wave per
+//                  2048-element chunk: four 16-byte streaming loads per lane,
+//                  the chunk maximum, then the sum of 2^((z - m) * log2(e)/T),
+//                  both reduced across the wave with DPP; the four waves'
+//                  (max, sum) pairs merge in LDS into one 64-bit partial per
+//                  group, published with its written bit.  The wave whose chunk
+//                  holds draft token x_k also publishes z(x_k) and q(x_k).
+//   decisions      one per request, placed in grid order one request after its
+//                  row groups (on the same XCD): polls the request's partials
+//                  and gathers, merges each row (fp64), runs the accept tests,
+//                  takes the first rejection j, writes the accepted prefix and
+//                  publishes a decision record (j, m_j, 1/S_j).
+//   request pass   after every row group and decision: nc2 workgroups per
+//                  request (about 2048 in all), each polling the record and
+//                  streaming its sub-tiles of the one row the final token is
+//                  drawn from (target row j, plus draft row j on a rejection),
+//                  writing fp64 sub-tile masses, each word marked as written.
 //                  The request's last workgroup in grid order polls the masses,
 //                  locates u * R by a parallel prefix over them, re-scans that
-//                  one sub-tile, writes the token, and zeroes every workspace
-//                  word the request used.  With B a multiple of 8 a request's
-//                  workgroups all sit on one XCD (workgroup i runs on XCD
-//                  i mod 8), so the repeated decision loads and the re-scan
-//                  hit that XCD's L2.
+//                  one sub-tile, writes the token, and zeroes the words the
+//                  request used.
 //
-// The only wait inside a sampled launch is that last workgroup's (bounded)
-// poll, which depends only on workgroups dispatched before it.  Temperature 0
-// (argmax) is one launch: row workgroups of four chunks, then one workgroup
-// per request that polls its rows' partials (bounded wait) — the host keeps
-// those below half the resident capacity, else it splits them into a second
-// launch.
+// Every wait is on workgroups earlier in grid order that never wait on later
+// ones, so the launch completes whatever the device holds at once.  With B a
+// multiple of 8 each XCD (workgroup i runs on XCD i mod 8) serves whole
+// requests: their row groups as a contiguous stream, their decisions while
+// it streams the next request, their request workgroups at the end.
+// With verify lengths at B <= 256, or with draft logits, the call is two
+// launches instead: a row pass (k_rows_sampled_vl visits only the read row
+// groups; k_rows_sampled otherwise), then k_requests_sampled, whose every
+// workgroup makes the decision itself from the completed partials.
 //
-// Words handed between workgroups of one launch (sub-tile masses, the greedy
+// Temperature 0 (argmax) is one launch: row workgroups of four chunks, then
+// one workgroup per request that polls its rows' partials (bounded wait) --
+// the host keeps those below half the resident capacity, else it splits them
+// into a second launch.
+//
+// Words handed between workgroups of one launch (row partials, gathers and
+// decision records of the one-launch verify, sub-tile masses, the greedy
 // partials) use coherent device-scope stores and loads instead of device-scope
 // fences, which on this chip write back or invalidate the whole L2; each such
 // word carries its own written bit, so none needs ordering.
@@ -336,10 +342,14 @@ __device__ __forceinline__ int chunk_index(int beg, int lane, int i) {
 // the wave; of draft row k when `draft` (draft logits).  The chunk holding
 // draft token x_k also stores z(x_k) and q(x_k) for the request pass's accept
 // test (with draft logits: z(x_k) from the target row, d(x_k) from the draft
-// row, each into its half of the gather word).
+// row, each into its half of the gather word).  With `published` (the
+// one-launch verify, draft probabilities) the gather word is stored
+// coherently and carries its own written bit in place of q's sign: q(x_k) is
+// stored as max(q, 0) (NaN as 0), which the accept test treats alike (a q
+// that is not positive accepts iff p(x_k) > 0).
 template <int ES, bool AL>
 __device__ void row_chunk_sampled(const VerifyArgs &a, int b, int k, int chunk, int n, bool draft, int lane,
-                                  float &M_out, float &S_out, long trow = -1) {
+                                  float &M_out, float &S_out, long trow = -1, bool published = false) {
     constexpr int EPL = kEPL<ES>;
     // trow: the target row's index when the caller already holds it
     const size_t zoff = (trow >= 0) ? size_t(trow) * size_t(a.V) : row_elem(a, b, k);
@@ -391,8 +401,14 @@ __device__ void row_chunk_sampled(const VerifyArgs &a, int b, int k, int chunk, 
     M_out = M;
     S_out = wave_sum((s0 + s1) + (s2 + s3));
     if (gather && lane == 0) {
-        if (!a.dl) gathered(a, b)[k] = uint64_t(__float_as_uint(gz)) | (uint64_t(__float_as_uint(gq)) << 32);
-        else reinterpret_cast<uint32_t *>(gathered(a, b) + k)[draft ? 1 : 0] = __float_as_uint(gz);
+        if (published) {
+            const uint32_t qb = (gq > 0.0f) ? __float_as_uint(gq) : 0u;
+            st_coherent(gathered(a, b) + k, uint64_t(__float_as_uint(gz)) | (uint64_t(qb | kValid) << 32));
+        } else if (!a.dl) {
+            gathered(a, b)[k] = uint64_t(__float_as_uint(gz)) | (uint64_t(__float_as_uint(gq)) << 32);
+        } else {
+            reinterpret_cast<uint32_t *>(gathered(a, b) + k)[draft ? 1 : 0] = __float_as_uint(gz);
+        }
     }
 }
 
@@ -590,6 +606,84 @@ __device__ bool merge_rows_sampled(const VerifyArgs &a, const uint64_t *part, in
     return bad;
 }
 
+// merge_rows_sampled for partials that row workgroups of the same launch are
+// still writing (the one-launch verify): each row batch's coherent loads
+// repeat, with a short sleep, until every word carries its written bit (a
+// bounded wait; an expired one reports the request as bad).  The merge itself
+// is merge_rows_sampled's, in the same order, so its results are bitwise the
+// same.  `extra` issues the caller's own polled loads with every attempt and
+// reports whether they are complete; the attempt succeeds when both are.
+template <typename F>
+__device__ bool merge_rows_sampled_poll(const VerifyArgs &a, const uint64_t *part, int nrows, float *Mo,
+                                        double *So, F extra) {
+    bool bad = false;
+    constexpr int kRegs = 4;
+    const int n = nrows - 1;
+    const int l = threadIdx.x & 15, g = threadIdx.x >> 4;
+    const float c = a.c32;
+    const uint64_t empty = uint64_t(0xff800000u) | (uint64_t(kValid) << 32);   // (-inf, 0), written
+    for (int r0 = 0; r0 <= n; r0 += kWG / 16) {
+        const int r = r0 + g;
+        const bool live = r <= n;
+        const uint64_t *pp = part + size_t(live ? r : 0) * a.np1;
+        float M = neg_inf();
+        double S = 0.0;
+        int ok = 1;
+        if (a.np1 <= 16 * kRegs) {
+            uint64_t v[kRegs];
+            for (uint32_t spins = 0;; ++spins) {
+                ok = 1;
+#pragma unroll
+                for (int i = 0; i < kRegs; ++i) {
+                    const int cc = l + 16 * i;
+                    v[i] = (live && cc < a.np1) ? ld_coherent(pp + cc) : empty;
+                }
+                ok = int(extra());
+#pragma unroll
+                for (int i = 0; i < kRegs; ++i) ok &= int(valid(v[i]));
+                if (__syncthreads_and(ok) || spins >= a.spin_limit) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+#pragma unroll
+            for (int i = 0; i < kRegs; ++i) M = fmaxf(M, lo_f(v[i]));
+            M = row16_max(M);
+#pragma unroll
+            for (int i = 0; i < kRegs; ++i)
+                S = S + double(__uint_as_float(hi_u(v[i]) & ~kValid)) * double(rescale(lo_f(v[i]), M, c));
+        } else {
+            for (uint32_t spins = 0;; ++spins) {
+                ok = int(extra());
+                if (__syncthreads_and(ok) || spins >= a.spin_limit) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            if (live)
+                for (int cc = l; cc < a.np1; cc += 16) {
+                    uint64_t v = ld_coherent(pp + cc);
+                    for (uint32_t spins = 0; !valid(v) && spins < a.spin_limit; ++spins) {
+                        __builtin_amdgcn_s_sleep(2);
+                        v = ld_coherent(pp + cc);
+                    }
+                    ok &= int(valid(v));
+                    M = fmaxf(M, lo_f(v));
+                }
+            M = row16_max(M);
+            if (live)
+                for (int cc = l; cc < a.np1; cc += 16) {
+                    const uint64_t v = ld_coherent(pp + cc);      // written by now (or the request is bad)
+                    S = S + double(__uint_as_float(hi_u(v) & ~kValid)) * double(rescale(lo_f(v), M, c));
+                }
+        }
+        S = row16_sum_d(S);
+        ok = row16_and(ok);
+        if (l == 0 && live) {
+            bad |= !ok || !(S > 0.0 && S < INFINITY) || !(M > neg_inf() && M < __builtin_inff());
+            Mo[r] = M;
+            So[r] = S;
+        }
+    }
+    return bad;
+}
+
 
 // Rows 0..n's chunk partials (greedy): lowest index of the maximum into
 // sh.A[r], 16 lanes per row.  The partials are written by row waves of the
@@ -773,6 +867,132 @@ __device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, bool &pro
         if (threadIdx.x == 0) st_out(a.out_acc + b, j);
     }
     return true;
+}
+
+// ------------------------------------------------- one-launch decision record
+
+__device__ __forceinline__ uint64_t *decision(const VerifyArgs &a, int b) {
+    return reinterpret_cast<uint64_t *>(a.ws + a.lay.dec) + size_t(b) * 2;
+}
+constexpr uint32_t kDecResid = 1u << 15, kDecOk = 1u << 16, kDecJ = 0x7fffu;
+
+// The decision workgroup of request b in the one-launch verify, after the
+// request's row workgroups in grid order.  It polls the row partials and the
+// flagged gathers until written, then decides exactly as decide() does (the
+// same merge and accept tests); writes the accepted prefix, the -1 padding
+// and out_accepted (the token at j is left to the request workgroups), and the
+// diagnostics if asked; publishes the decision record; and clears the
+// partials and gathers, which nothing reads after it.  An invalid verify
+// length or a data error is reported here (a data error's record has ok = 0;
+// an invalid length publishes nothing: the request workgroups see the length
+// themselves).
+template <int ES>
+__device__ void decide_publish(const VerifyArgs &a, int b, Smem &sh) {
+    const int G = a.G, G1 = G + 1;
+    const int k = threadIdx.x;
+    const int n = verify_len(a, b);
+    const bool diag = a.d_lse || a.d_p || a.d_q || a.d_r;
+    if (n < 0 || n > G) {
+        write_error(a, b);
+        if (diag) write_diag<ES>(a, b, false, n, sh);
+        return;
+    }
+    int xk = 0;
+    float uk = 0.0f;
+    uint64_t gk = 0;
+    if (k < n) {
+        xk = a.x[size_t(b) * G + k];
+        uk = a.u[size_t(b) * G1 + k];
+    }
+    // The gather word of draft k is written (its bit set) by the row
+    // workgroup whose chunk holds x_k; an id out of range is never gathered
+    // and is a data error.  It is polled with the partials.
+    bool gready = !(k < n);
+    const uint64_t *gxp = gathered(a, b) + (k < n ? k : 0);
+    bool bad = merge_rows_sampled_poll(a, partials(a, b), n + 1, sh.M, sh.S, [&]() -> bool {
+        if (!gready) {
+            gk = ld_coherent(gxp);
+            gready = (hi_u(gk) & kValid) != 0u || xk < 0 || xk >= a.V;
+        }
+        return gready;
+    });
+    bad |= k < n && (xk < 0 || xk >= a.V);
+    const bool err = __syncthreads_or(bad);
+    int j = n;
+    float m = 0.0f, inv_s = 0.0f;
+    if (!err) {
+        bool rej = false;
+        if (k < n) {
+            const float zx = lo_f(gk), qx32 = __uint_as_float(hi_u(gk) & ~kValid);
+            const double pk = target_prob(zx, sh.M[k], a.c32) / sh.S[k];
+            const double qx = double(qx32);
+            const bool acc = (qx > 0.0) ? (double(uk) < pk / qx) : (pk > 0.0);
+            rej = !acc;
+        }
+        post_first(rej, 0, sh);
+        __syncthreads();
+        const int jf = wg_first(0, sh);
+        j = (jf == INT_MAX) ? n : jf;
+        m = sh.M[j];
+        inv_s = float(1.0 / sh.S[j]);
+        for (int t = threadIdx.x; t < G1; t += kWG) {
+            if (t < j) st_out(a.out_tok + size_t(b) * G1 + t, a.x[size_t(b) * G + t]);
+            else if (t > j) st_out(a.out_tok + size_t(b) * G1 + t, -1);
+        }
+        if (threadIdx.x == 0) st_out(a.out_acc + b, j);
+    } else {
+        write_error(a, b);
+    }
+    if (diag) write_diag<ES>(a, b, !err, n, sh);
+    if (threadIdx.x == 0) {
+        uint64_t *rec = decision(a, b);
+        const uint32_t h = uint32_t(j) | (j < n ? kDecResid : 0u) | (err ? 0u : kDecOk) | kValid;
+        st_coherent(rec + 1, uint64_t(__float_as_uint(inv_s)) | (uint64_t(kValid) << 32));
+        st_coherent(rec, uint64_t(__float_as_uint(m)) | (uint64_t(h) << 32));
+    }
+    uint64_t *part = partials(a, b);
+    for (int i = threadIdx.x; i < (n + 1) * a.np1; i += kWG) st_coherent(part + i, 0ull);
+    for (int i = threadIdx.x; i < n; i += kWG) st_coherent(gathered(a, b) + i, 0ull);
+}
+
+// A request workgroup of the one-launch verify: request b's decision, from its
+// record (a bounded wait, uniform across the workgroup).  Returns false for a
+// data error; *proceed is false for an invalid verify length (the decision
+// workgroup reports it).  An expired wait reports the request as bad (the
+// request's last workgroup writes the error).
+__device__ bool await_decision(const VerifyArgs &a, int b, int w, Decision &d, bool &proceed) {
+    const int G = a.G, G1 = G + 1;
+    const int n = verify_len(a, b);
+    d.n = n;
+    d.j = 0;
+    d.resid = false;
+    d.m = 0.0f;
+    d.inv_s = 0.0f;
+    d.mq = 0.0f;
+    d.inv_sq = 0.0f;
+    proceed = n >= 0 && n <= G;
+    if (!proceed) return false;
+    d.u_final = a.u[size_t(b) * G1 + G];
+    const uint64_t *rec = decision(a, b);
+    uint64_t w0 = 0, w1 = 0;
+    bool ready = false;
+    for (uint32_t spins = 0;; ++spins) {
+        w0 = ld_coherent(rec);
+        w1 = ld_coherent(rec + 1);
+        ready = __syncthreads_and(((w0 & w1) >> 63) != 0);
+        if (ready || spins >= a.spin_limit) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    if (!ready) {
+        if (w == a.nc2 - 1) write_error(a, b);
+        return false;
+    }
+    const uint32_t h = hi_u(w0);
+    d.j = int(h & kDecJ);
+    d.resid = (h & kDecResid) != 0u;
+    d.m = lo_f(w0);
+    d.inv_s = lo_f(w1);
+    return (h & kDecOk) != 0u;
 }
 
 // Wait until every sub-tile mass word of request b is written.  With at most
@@ -973,14 +1193,16 @@ __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, cons
 // and writes their masses (on a data error, marks them done); the request's
 // last workgroup (w = nc2 - 1) waits for every mass word, selects the token,
 // writes the diagnostics and zeroes the request's partials, gathers and
-// masses.
-template <int ES, bool ALZ, bool ALQ, bool DL>
+// masses.  FUSED: the same, in the launch that also runs the row workgroups
+// (the decision polls the partials; nothing was gathered).
+template <int ES, bool ALZ, bool ALQ, bool DL, bool FUSED = false>
 __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh) {
+    static_assert(!(FUSED && DL), "the one-launch verify reads draft probabilities");
     Decision d;
     bool proceed;
-    const bool ok = decide<ES>(a, b, w, d, proceed, sh);
+    const bool ok = FUSED ? await_decision(a, b, w, d, proceed) : decide<ES>(a, b, w, d, proceed, sh);
     if (!proceed) {
-        if (w == 0 && (a.d_lse || a.d_p || a.d_q || a.d_r)) write_diag<ES>(a, b, false, d.n, sh);
+        if (!FUSED && w == 0 && (a.d_lse || a.d_p || a.d_q || a.d_r)) write_diag<ES>(a, b, false, d.n, sh);
         return;
     }
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -1032,14 +1254,20 @@ __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh
     // A mass word is written after its workgroup's decision, so once all are
     // written no workgroup of the request reads the partials any more.
     if (w != a.nc2 - 1) return;
-    // The diagnostics need only the merged rows, so they go out before the wait.
-    if (a.d_lse || a.d_p || a.d_q || a.d_r) write_diag<ES>(a, b, ok, d.n, sh);
+    // The diagnostics need only the merged rows, so they go out before the wait
+    // (in the one-launch verify the decision workgroup writes them).
+    if (!FUSED && (a.d_lse || a.d_p || a.d_q || a.d_r)) write_diag<ES>(a, b, ok, d.n, sh);
     double polled[2];
     const bool all = wait_masses(a, b, polled);
     if (ok && all) final_select<ES, ALZ, ALQ, DL>(a, b, d, zrow, qrow, polled, sh);
     else if (ok) write_error(a, b);              // an expired wait
     __syncthreads();
     for (int i = threadIdx.x; i < 2 * a.nsub; i += kWG) st_coherent(mass + i, 0ull);
+    if constexpr (FUSED) {
+        // every request workgroup has read the record before writing its masses
+        if (threadIdx.x < 2) st_coherent(decision(a, b) + threadIdx.x, 0ull);
+        return;
+    }
     uint64_t *part = partials(a, b);
     for (int i = threadIdx.x; i < (d.n + 1) * a.np1; i += kWG) part[i] = 0ull;
     if (DL) {
@@ -1093,13 +1321,15 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // a sampled verify, one wave per chunk.  The group's partial merges its
 // waves' (max, sum) pairs in wave order, so the request pass reads a quarter
 // as many partials.
+// With `published` (the one-launch verify) the partial and the gather are
+// stored coherently, for request workgroups of the same launch that poll them.
 template <int ES, bool AL>
 __device__ __forceinline__ void row_group_sampled(const VerifyArgs &a, int b, int k, int g, int n, bool draft,
-                                                  float *gm, float *gs, long trow = -1) {
+                                                  float *gm, float *gs, long trow = -1, bool published = false) {
     const int w = wave_id(), lane = int(threadIdx.x) & 63;
     const int c = g * kWaves + w;
     float M = neg_inf(), S = 0.0f;
-    if (c < a.nc1) row_chunk_sampled<ES, AL>(a, b, k, c, n, draft, lane, M, S, trow);
+    if (c < a.nc1) row_chunk_sampled<ES, AL>(a, b, k, c, n, draft, lane, M, S, trow, published);
     if (lane == 0) {
         gm[w] = M;
         gs[w] = S;
@@ -1110,8 +1340,10 @@ __device__ __forceinline__ void row_group_sampled(const VerifyArgs &a, int b, in
         float t = 0.0f;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) t = t + gs[v] * rescale(gm[v], m, a.c32);
-        (draft ? partials_d(a, b) : partials(a, b))[size_t(k) * a.np1 + g] =
-            uint64_t(__float_as_uint(m)) | (uint64_t(__float_as_uint(t) | kValid) << 32);
+        uint64_t *dst = (draft ? partials_d(a, b) : partials(a, b)) + size_t(k) * a.np1 + g;
+        const uint64_t word = uint64_t(__float_as_uint(m)) | (uint64_t(__float_as_uint(t) | kValid) << 32);
+        if (published) st_coherent(dst, word);
+        else *dst = word;
     }
 }
 
@@ -1212,6 +1444,91 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(DL ? 4 : 8,
         w = i - b * a.nc2;
     }
     request_item_sampled<ES, ALZ, ALQ, DL>(a, b, w, sh);
+}
+
+// One-launch sampled verify (draft probabilities).  Three kinds of workgroup
+// share one grid:
+//   rows(b)    request b's row workgroups (k_rows_sampled's, with partials and
+//              gathers published coherently, each word with its written bit);
+//   dec(b)     one decision workgroup (decide_publish): polls rows(b)'s words,
+//              decides, writes the accepted prefix and a decision record;
+//   draws(b)   request b's nc2 request workgroups (k_requests_sampled's),
+//              which poll the record instead of the partials, stream the draw
+//              row and select the token.
+// Every wait is on workgroups earlier in grid order that never wait on later
+// ones (dec(b) on rows(b), draws(b) on dec(b) and, for the last of them, on
+// draws(b)'s earlier ones), so the launch completes whatever the device holds
+// at once.
+//
+// Grid order.  With B a multiple of 8, workgroup i runs on XCD x = i mod 8 and
+// is the (i / 8)-th of that XCD's sequence, which serves requests b = 8t + x,
+// t = 0..R-1 (R = B / 8):
+//   rows(0) .. rows(lag-1), then rows(t) followed by dec(t - lag) for
+//   t = lag..R-1, then dec(R-lag) .. dec(R-1), then draws(0) .. draws(R-1).
+// A request is decided while the XCD streams the next request's rows, so when
+// the request workgroups are dispatched (after every row workgroup) all but
+// the last requests' records are ready and their draw streams start at once,
+// filling the row pass's drain.  Otherwise: every rows(b), then every dec(b),
+// then every draws(b).
+template <int ES, bool ALZ, bool ALQ>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_verify_sampled(VerifyArgs a) {
+    __shared__ Smem sh;
+    __shared__ float gm[kWaves], gs[kWaves];
+    const int per = (a.G + 1) * a.np1, nc2 = a.nc2;
+    const int i = int(blockIdx.x);
+    int kind, b, loc;                                 // kind: 0 rows, 1 decision, 2 draws
+    if ((a.B & 7) == 0) {
+        const int x = i & 7;
+        int s = i >> 3;
+        const int R = a.B >> 3, L = min(a.lag, R);
+        int t;
+        if (s < L * per) {                            // rows(0) .. rows(L-1)
+            t = s / per;
+            kind = 0;
+            loc = s - t * per;
+        } else if ((s -= L * per) < (R - L) * (per + 1)) {   // rows(t), dec(t - L)
+            const int q = s / (per + 1), o = s - q * (per + 1);
+            kind = (o < per) ? 0 : 1;
+            t = (o < per) ? L + q : q;
+            loc = o;
+        } else if ((s -= (R - L) * (per + 1)) < L) {  // dec(R-L) .. dec(R-1)
+            kind = 1;
+            t = R - L + s;
+            loc = 0;
+        } else {                                      // draws(0) .. draws(R-1)
+            s -= L;
+            kind = 2;
+            t = s / nc2;
+            loc = s - t * nc2;
+        }
+        b = 8 * t + x;
+    } else {
+        const int groups = a.B * per;
+        if (i < groups) {
+            kind = 0;
+            b = i / per;
+            loc = i - b * per;
+        } else if (i < groups + a.B) {
+            kind = 1;
+            b = i - groups;
+            loc = 0;
+        } else {
+            const int j = i - groups - a.B;
+            kind = 2;
+            b = j / nc2;
+            loc = j - b * nc2;
+        }
+    }
+    if (kind == 0) {
+        const int k = loc / a.np1, g = loc - k * a.np1;
+        const int n = verify_len(a, b);
+        if (n < 0 || n > a.G || k > n) return;        // row not read: the whole workgroup leaves
+        row_group_sampled<ES, ALZ>(a, b, k, g, n, false, gm, gs, -1, /*published=*/true);
+    } else if (kind == 1) {
+        decide_publish<ES>(a, b, sh);
+    } else {
+        request_item_sampled<ES, ALZ, ALQ, false, true>(a, b, loc, sh);
+    }
 }
 
 // Greedy row workgroup gi: (request b, row k, group g of kWaves consecutive
@@ -1431,6 +1748,20 @@ int launch_requests_sampled(const VerifyArgs &a, bool az, bool aq, int esize, in
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (a.dl) launch_requests_dl<true>(a, az, aq, esize, grid, st);
     else launch_requests_dl<false>(a, az, aq, esize, grid, st);
+    return int(hipGetLastError());
+}
+
+int launch_verify_sampled(const VerifyArgs &a, bool az, bool aq, int esize, int grid, void *stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (esize == 2) {
+        if (az && aq) hipLaunchKernelGGL((k_verify_sampled<2, true, true>), dim3(grid), dim3(kWG), 0, st, a);
+        else if (az) hipLaunchKernelGGL((k_verify_sampled<2, true, false>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_verify_sampled<2, false, false>), dim3(grid), dim3(kWG), 0, st, a);
+    } else {
+        if (az && aq) hipLaunchKernelGGL((k_verify_sampled<4, true, true>), dim3(grid), dim3(kWG), 0, st, a);
+        else if (az) hipLaunchKernelGGL((k_verify_sampled<4, true, false>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_verify_sampled<4, false, false>), dim3(grid), dim3(kWG), 0, st, a);
+    }
     return int(hipGetLastError());
 }
 

@@ -366,7 +366,8 @@ def test_row_pass_event_changes_nothing():
 def test_launch_plan_query():
     from lossless_draft_verification_verify_amd import _capi
     torch.cuda.init()
-    assert _capi.verify_launches(64, 15, 129280, _capi.SPEC_DTYPE_BF16, 1.0) == 2
+    # sampled with draft probabilities and no verify lengths: one launch
+    assert _capi.verify_launches(64, 15, 129280, _capi.SPEC_DTYPE_BF16, 1.0) == 1
     assert _capi.verify_launches(64, 7, 152064, _capi.SPEC_DTYPE_BF16, 0.0) == 1
     # far more requests than half the resident workgroups: the greedy call splits
     assert _capi.verify_launches(60000, 1, 64, _capi.SPEC_DTYPE_BF16, 0.0) == 2
