@@ -194,7 +194,7 @@ spec_status_t verify_impl(const void *target_logits, spec_dtype_t target_dtype, 
     a.d_q = dg.q_draft;
     a.d_r = dg.resid_mass;
     a.ws = static_cast<unsigned char *>(workspace);
-    a.lay = lay;
+    a.lay = sv::to_units(lay);
     a.B = B;
     a.G = G;
     a.V = V;
@@ -357,7 +357,7 @@ spec_status_t spec_verify_tree(const void *target_logits, spec_dtype_t target_dt
     a.tpar = parents;
     a.ttok = node_tokens;
     a.ws = static_cast<unsigned char *>(workspace);
-    a.lay = lay;
+    a.lay = sv::to_units(lay);
     a.B = B;
     a.G = G;
     a.V = V;

@@ -73,6 +73,17 @@ inline Layout make_layout(int64_t B, int64_t G, int64_t V, int esize) {
     return L;
 }
 
+// The layout as the kernels take it: each region's offset in units of 256
+// bytes (every region is 256-byte aligned), so that the kernel arguments stay
+// small.
+struct LayoutUnits {
+    uint32_t zero, part, partd, mass, gx, dec;
+};
+inline LayoutUnits to_units(const Layout &L) {
+    return {uint32_t(L.zero >> 8), uint32_t(L.part >> 8), uint32_t(L.partd >> 8), uint32_t(L.mass >> 8),
+            uint32_t(L.gx >> 8), uint32_t(L.dec >> 8)};
+}
+
 struct VerifyArgs {
     const void *logits;
     const float *q;
@@ -86,7 +97,7 @@ struct VerifyArgs {
     int32_t *out_tok;
     float *d_lse, *d_p, *d_q, *d_r;
     unsigned char *ws;
-    Layout lay;
+    LayoutUnits lay;
     int32_t B, G, V;
     float T;          // temperature
     float c32;        // log2(e) / T, the fp32 exponent scale

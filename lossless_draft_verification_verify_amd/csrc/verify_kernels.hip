@@ -239,16 +239,16 @@ __device__ void wg_scan(const double (&v)[NS], double (&excl)[NS], double (&incl
 // ------------------------------------------------------------- workspace
 
 __device__ __forceinline__ uint64_t *partials(const VerifyArgs &a, int b) {
-    return reinterpret_cast<uint64_t *>(a.ws + a.lay.part) + size_t(b) * (a.G + 1) * a.np1;
+    return reinterpret_cast<uint64_t *>(a.ws + size_t(a.lay.part) * 256) + size_t(b) * (a.G + 1) * a.np1;
 }
 __device__ __forceinline__ uint64_t *partials_d(const VerifyArgs &a, int b) {
-    return reinterpret_cast<uint64_t *>(a.ws + a.lay.partd) + size_t(b) * a.G * a.np1;
+    return reinterpret_cast<uint64_t *>(a.ws + size_t(a.lay.partd) * 256) + size_t(b) * a.G * a.np1;
 }
 __device__ __forceinline__ uint64_t *masses(const VerifyArgs &a, int b) {
-    return reinterpret_cast<uint64_t *>(a.ws + a.lay.mass) + size_t(b) * a.nsub * 2;
+    return reinterpret_cast<uint64_t *>(a.ws + size_t(a.lay.mass) * 256) + size_t(b) * a.nsub * 2;
 }
 __device__ __forceinline__ uint64_t *gathered(const VerifyArgs &a, int b) {
-    return reinterpret_cast<uint64_t *>(a.ws + a.lay.gx) + size_t(b) * a.G;
+    return reinterpret_cast<uint64_t *>(a.ws + size_t(a.lay.gx) * 256) + size_t(b) * a.G;
 }
 // A sub-tile mass word: the fp64 mass (>= 0) with bit 63 set once written.
 constexpr uint64_t kMassWritten = uint64_t(1) << 63;
@@ -872,7 +872,7 @@ __device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, bool &pro
 // ------------------------------------------------- one-launch decision record
 
 __device__ __forceinline__ uint64_t *decision(const VerifyArgs &a, int b) {
-    return reinterpret_cast<uint64_t *>(a.ws + a.lay.dec) + size_t(b) * 2;
+    return reinterpret_cast<uint64_t *>(a.ws + size_t(a.lay.dec) * 256) + size_t(b) * 2;
 }
 constexpr uint32_t kDecResid = 1u << 15, kDecOk = 1u << 16, kDecJ = 0x7fffu;
 
@@ -1079,79 +1079,67 @@ __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, cons
         sel = sh.fsel[1] >> 2;
         target = double(d.u_final) * (sel ? Rp : R);
     } else {
-        // Pass 1: totals of both mass arrays (residual, target), and the last
-        // sub-tile of each with positive mass.  With at most kWG sub-tiles (every
-        // vocabulary up to 2^19) the masses are the polled ones, kept in
-        // registers for pass 2.
-        const bool one = nsub <= kWG;
-        double v[2] = {0.0, 0.0}, ex[2] = {0.0, 0.0}, in[2], tot[2];
-        int lr = -1, lp_s = -1;
-        if (one) {
-            v[0] = polled[0];
-            v[1] = polled[1];
-            wg_scan<2>(v, ex, in, tot, sh);
-            post_last(v[0] > 0.0, 1, sh);
-            post_last(v[1] > 0.0, 2, sh);
-            __syncthreads();
-            lr = wg_last(1, sh);
-            lp_s = wg_last(2, sh);
-            R = tot[0];
-            Rp = tot[1];
-        } else {
-            for (int blk = 0; blk < nsub; blk += kWG) {
-                const int s = blk + int(threadIdx.x);
-                v[0] = 0.0; v[1] = 0.0;
+        // More than 64 sub-tiles: wave 0 walks them in blocks of 64 with the DPP
+        // scans and ballots of the path above and a running base (the words are
+        // complete: wait_masses saw every written bit).  Pass 1 forms both totals
+        // and the last positive sub-tile of each array; pass 2 finds the first
+        // sub-tile with positive mass whose running total passes u * R.  Both
+        // passes add the same block totals in the same order, so the located
+        // sub-tile is consistent with R.
+        if (threadIdx.x < 64) {
+            const int lane = threadIdx.x;
+            double tR = 0.0, tRp = 0.0;
+            int lr = -1, lp = -1;
+            for (int blk = 0; blk < nsub; blk += 64) {
+                const int s = blk + lane;
+                double v0 = 0.0, v1 = 0.0;
                 if (s < nsub) {
-                    v[0] = mass_value(ld_coherent(mass + 2 * s));
-                    v[1] = mass_value(ld_coherent(mass + 2 * s + 1));
+                    v0 = mass_value(ld_coherent(mass + 2 * s));
+                    v1 = mass_value(ld_coherent(mass + 2 * s + 1));
                 }
-                wg_scan<2>(v, ex, in, tot, sh);
-                post_last(v[0] > 0.0, 1, sh);
-                post_last(v[1] > 0.0, 2, sh);
-                __syncthreads();
-                if (wg_last(1, sh) >= 0) lr = blk + wg_last(1, sh);
-                if (wg_last(2, sh) >= 0) lp_s = blk + wg_last(2, sh);
-                R = R + tot[0];
-                Rp = Rp + tot[1];
+                const double x0 = wave_scan_d(v0), x1 = wave_scan_d(v1);
+                tR = tR + lane_d(x0, 63);
+                tRp = tRp + lane_d(x1, 63);
+                const uint64_t m0 = __ballot(v0 > 0.0), m1 = __ballot(v1 > 0.0);
+                if (m0) lr = blk + 63 - __builtin_clzll(m0);
+                if (m1) lp = blk + 63 - __builtin_clzll(m1);
             }
-        }
-        // The draw is from the residual when it has mass; a rejection whose
-        // residual is zero draws from p_j, a bonus draw from p_n (whose residual
-        // terms are p itself).
-        use_r = resid && R > 0.0;
-        sel = (resid && !use_r) ? 1 : 0;
-        target = double(d.u_final) * (sel ? Rp : R);
-        // Pass 2: the first sub-tile s with positive mass and base(s) + mass(s) > target.
-        if (one) {
-            const int s = int(threadIdx.x);
-            const double vs = sel ? v[1] : v[0], bs = sel ? ex[1] : ex[0];
-            post_first(s < nsub && vs > 0.0 && bs + vs > target, 3, sh);
-            __syncthreads();
-            sstar = wg_first(3, sh);
-            if (s == sstar) sh.base = bs;
-        } else {
-            double P = 0.0;
-            for (int blk = 0; blk < nsub; blk += kWG) {
-                const int s = blk + int(threadIdx.x);
-                double w1[1] = {0.0}, ex1[1], in1[1], tot1[1];
-                if (s < nsub) w1[0] = mass_value(ld_coherent(mass + 2 * s + sel));
-                wg_scan<1>(w1, ex1, in1, tot1, sh);
-                const double bs = P + ex1[0];
-                post_first(s < nsub && w1[0] > 0.0 && bs + w1[0] > target, 3, sh);
-                __syncthreads();
-                const int f = wg_first(3, sh);
-                if (f != INT_MAX) {
-                    sstar = blk + f;
-                    if (s == sstar) sh.base = bs;
+            const bool ur = resid && tR > 0.0;
+            const int sl = (resid && !ur) ? 1 : 0;
+            const double tg = double(d.u_final) * (sl ? tRp : tR);
+            double P = 0.0, bb = 0.0;
+            int ss = INT_MAX;
+            for (int blk = 0; blk < nsub; blk += 64) {
+                const int s = blk + lane;
+                const double vs = (s < nsub) ? mass_value(ld_coherent(mass + 2 * s + sl)) : 0.0;
+                const double xs = wave_scan_d(vs);
+                const double ps = dpp_d<kWaveShr1>(xs), bs = P + ((lane == 0) ? 0.0 : ps);
+                const uint64_t mf = __ballot(s < nsub && vs > 0.0 && bs + vs > tg);
+                if (mf) {
+                    const int f = __builtin_ctzll(mf);
+                    ss = blk + f;
+                    bb = lane_d(bs, f);
                     break;
                 }
-                P = P + tot1[0];
+                P = P + lane_d(xs, 63);
+            }
+            if (lane == 0) {
+                sh.R = tR;
+                sh.Rp = tRp;
+                sh.base = bb;
+                sh.fsel[0] = (ss == INT_MAX) ? max(0, sl ? lp : lr) : ss;
+                sh.fsel[1] = int(ss == INT_MAX) | (int(ur) << 1) | (sl << 2);
             }
         }
         __syncthreads();
-        lastpos = sstar == INT_MAX;               // u * R at or beyond the top: last positive term
-        if (lastpos) sstar = max(0, sel ? lp_s : lr);
-        base = lastpos ? 0.0 : sh.base;
+        R = sh.R;
+        Rp = sh.Rp;
+        base = sh.base;
+        sstar = sh.fsel[0];
+        lastpos = (sh.fsel[1] & 1) != 0;
+        use_r = (sh.fsel[1] & 2) != 0;
+        sel = sh.fsel[1] >> 2;
+        target = double(d.u_final) * (sel ? Rp : R);
     }
     float t[kSubPerThread];
     double rs, ps;
@@ -1210,7 +1198,7 @@ __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh
     const void *zrow = static_cast<const char *>(a.logits) + row_elem(a, b, d.j) * ES;
     // the draft row j (probabilities, or logits with DL) on a rejection, else the zero block
     const size_t qe = (size_t(b) * a.G + d.j) * size_t(a.V);
-    const void *qrow = !d.resid ? static_cast<const void *>(a.ws + a.lay.zero)
+    const void *qrow = !d.resid ? static_cast<const void *>(a.ws + size_t(a.lay.zero) * 256)
                        : DL    ? static_cast<const void *>(static_cast<const char *>(a.dl) + qe * ES)
                                : static_cast<const void *>(a.q + qe);
     if (!ok) {
