@@ -22,9 +22,8 @@ Readings (also in DESIGN.md):
 * 0-based positions: conf[:, k] is the confidence of draft k+1, and its
   cumulative label is 1 when at least k+1 drafts were accepted (acc_len > k).
 * c~ = float32(2^(log2(c) / T)), the power formed in float64 and rounded to
-  the float32 that the schedulers read.  c = 0 gives 0, c = 1 gives 1.  (The
-  GPU fit forms log2(c) * (1/T); the last-bit difference only moves a sample
-  across a bin edge or the error by ~1e-16, inside the parity tolerance.)
+  float32, the precision the schedulers read confidences in.  c = 0 gives 0,
+  c = 1 gives 1.
 * The grid is numpy.linspace(0.1, 10.0, 100), step 0.1 with T = 1 on it, each
   point taken as the float32 the library is given.  Equal ECE keeps the first
   (smallest) T.

@@ -3,11 +3,13 @@
 TEST INFRASTRUCTURE ONLY -- see the package docstring.
 
 Source: "breaking down dspark and its lineage", section "Tree attention"
-(and "Prefill, decode, and trees on both sides"): the candidates form a tree
-in which each token is a node and each node's children are the continuations
-that follow it.  The target verifies the flattened tree in one pass under an
-ancestor-only mask, so every node is scored in exactly the context of its own
-root-to-node path, and the target decides which candidate path survives.
+(and "Prefill, decode, and trees on both sides"): a drafter may propose
+several continuations per step, arranged as a tree rooted at the last
+committed token, where a node's parent is the token it extends.  One target
+pass over the flattened tree, with attention restricted to each node's
+ancestors, gives every node the distribution it would get on its own
+root-to-node path; verification then keeps the one candidate path the target
+agrees with.
 "UraionSpec", "Future work", names tree verification for autoregressive
 drafters.
 
