@@ -291,9 +291,9 @@ spec_status_t spec_verify_tree(const void *target_logits, spec_dtype_t target_dt
  * Number of kernel launches spec_verify makes for this shape on the current
  * device, with 16-byte-aligned target_logits and verify_len NULL: for T > 0,
  * 1 (the row workgroups, a decision workgroup per request and the request
- * workgroups share one grid; with verify lengths and B <= 256, or with draft
- * logits, spec_verify and spec_verify_logits make 2: the pass over the read
- * rows, then the per-request pass); for T == 0, 1 when the per-request work
+ * workgroups share one grid, also with verify lengths; spec_verify_logits,
+ * with draft logits, makes 2: the pass over the read rows, then the
+ * per-request pass); for T == 0, 1 when the per-request work
  * shares the row launch and 2 when it runs as a second launch.  -1 on invalid
  * arguments or a failed device query.  Host-only; enqueues nothing.
  */

@@ -224,8 +224,8 @@ spec_status_t verify_impl(const void *target_logits, spec_dtype_t target_dtype, 
         }
         a.nc2 = (a.nsub + a.spw - 1) / a.spw;
         const bool vl_pass = (verify_len || row_offsets) && B <= sv::kWG;
-        if (!a.dl && !vl_pass) {
-            // One launch (draft probabilities, full-grid row layout): the row
+        if (!a.dl) {
+            // One launch (draft probabilities): the row
             // workgroups, one decision workgroup per request (in grid order one
             // request after its rows), then the request workgroups, which only
             // poll the request's decision record: about 2048 of them in all
@@ -237,14 +237,23 @@ spec_status_t verify_impl(const void *target_logits, spec_dtype_t target_dtype, 
             a.spw = spw;
             a.nc2 = (a.nsub + a.spw - 1) / a.spw;
             a.lag = 1;
-            if (sv::launch_verify_sampled(a, az, aq, es, int(row_groups + long(B) * (1 + a.nc2)), stream) != 0)
+            long rows = row_groups;
+            if (vl_pass) {
+                // Verify lengths leave rows unread: at most one resident load
+                // of row workgroups that visit only the read row groups.
+                const long cap = resident_capacity(dev, az, es);
+                if (cap <= 0) return SPEC_ERR_DEVICE;
+                rows = std::min(row_groups, cap);
+                a.vlrows = int32_t(rows);
+            }
+            if (sv::launch_verify_sampled(a, az, aq, es, int(rows + long(B) * (1 + a.nc2)), stream) != 0)
                 return SPEC_ERR_DEVICE;
             if (row_event && hipEventRecord(row_event, static_cast<hipStream_t>(stream)) != hipSuccess)
                 return SPEC_ERR_DEVICE;
             return SPEC_OK;
         }
         if (vl_pass) {
-            // Verify lengths leave rows unread: a grid of two resident loads of
+            // Draft logits with verify lengths: a grid of two resident loads of
             // workgroups (no workgroup waits on another) whose workgroups visit
             // only the read row groups.  Two loads measured best: one leaves
             // the last jobs of a busy workgroup queued behind its earlier ones

@@ -9,31 +9,31 @@
 //
 // The result is bit-identical to the sequential float64 loop: the survival
 // products and the running sum tau are formed in exactly that loop's order;
-// only the independent parts (sorting, the theta comparisons, the length
+// only the independent parts (ranking, the theta comparisons, the length
 // tally) run in parallel.  The work is a chain of dependent steps on one
-// workgroup, so the design minimises round trips and serial steps:
+// workgroup, so the design minimises round trips, barriers and the length of
+// each thread's instruction stream:
 //
 //   1. every confidence and every cost entry the scan can reach is loaded into
 //      LDS at once (one memory round trip);
-//   2. one thread per request: the fp64 running product of its confidences
-//      (the sequential loop's order), and whether survival is non-increasing
-//      along every request (always true for c in [0, 1]);
-//   3. bitonic sort of (s, k*B + b) keys, candidates first (the key's second
-//      half orders equal survivals by k, then b, with no division).  With at
-//      most 1024 slots each thread holds one in registers and the network is
-//      unrolled: partners closer than a wave are read across lanes with DPP
-//      (strides 1, 2, 4, 8) and the row-swap permutes (16, 32), farther ones
-//      through LDS, two strides per barrier where two remain.  The network
-//      compares one 64-bit key (fp32-rounded survival above the id); runs of
-//      equal fp32 survival are then re-ranked exactly, so the order is the
-//      exact one;
+//   2. one slot (b, k) per thread: its survival, the fp64 product of
+//      c[b,0..k] in order, and whether it exceeds the one before;
+//   3. the exact rank of every candidate without a sorting network: each
+//      candidate counts into a bin of its fp32-rounded survival (8 bins per
+//      octave, an LDS atomic that also numbers it inside the bin), a block
+//      scan of the bins gives each bin's first rank, and a candidate's rank is
+//      that plus the number of candidates of its own bin that precede it,
+//      compared exactly.  A bin with many candidates (equal survivals) sends
+//      the call to a bitonic network over packed (fp32 survival, id) keys with
+//      an exact re-rank inside runs of equal fp32 survival;
 //   4. contiguity (only when some survival increases): a candidate can be kept
 //      only if all shallower positions of its request are candidates placed
 //      before it;
-//   5. one wave walks the sorted candidates 64 at a time: tau is extended in
-//      candidate order, lane by lane, then the 64 tests theta_{m+1} > theta_m
-//      run at once; the walk stops at the block holding the first failure
-//      (or at the budget), so it visits only about m* + 64 candidates;
+//   5. one wave walks the ranked candidates 64 at a time: one lane extends
+//      tau in candidate order and stores each step in LDS, then the 64 tests
+//      theta_{m+1} > theta_m run at once; the walk stops at the block holding
+//      the first failure (or at the budget), so it visits only about m* + 64
+//      candidates;
 //   6. lengths are tallied from the first m* candidates.
 
 #include <hip/hip_runtime.h>
@@ -50,13 +50,25 @@ constexpr int kMaxThreads = 1024;
 constexpr int kMaxCand = 4096;
 constexpr int kRegSort = 1024;     // at most this many slots: one per thread, sorted in registers
 constexpr int kPad = 0x7fffffff;
+constexpr int kEpt = kMaxCand / kMaxThreads;   // slots per thread
+// Window bins: 1/64 octave of survival each, counted from the highest
+// candidate's down, kWinPer per thread (the lowest also takes everything
+// below the window).
+constexpr int kWinShift = 17;      // fp32 order key >> kWinShift: the bin scale
+constexpr int kWinPer = 4;
+constexpr int kBins = kWinPer * kMaxThreads;
+constexpr int kWinCap = 64;        // a bin ranked inside holds at most this many candidates, else the network sort
+constexpr int kTopK = 256;         // k_schedule ranks the bins that start before this place
+constexpr int kGrp = kTopK + kWinCap;
 
+// Slots: draft (b, k) is slot k * B + b, which is also its id in the order
+// (equal survivals: smaller k, then smaller b, first).
 struct SchedSmem {
-    double key[kMaxCand];      // survival (slot = b * G + k), then sorted survival
-    int id[kMaxCand];          // k * B + b, or kPad for padding / non-candidates
+    double key[kMaxCand];      // survival by slot; after the network sort, sorted survival
+    int id[kMaxCand];          // network sort: ids in order; bin ranking: ids grouped by bin (by place)
     union {
-        double conf[kMaxCand]; // the confidences (slot = b * G + k)
-        int pos[kMaxCand];     // contiguity: sorted position of each candidate (slot b * G + k), or -1
+        double conf[kMaxCand]; // the confidences by slot; bin ranking: survivals grouped by bin (by place)
+        int pos[kMaxCand];     // contiguity: sorted position of each candidate (by slot), or -1
         struct {
             uint64_t xq[2][kRegSort]; // register sort: exchange buffers for strides >= 64
             double fs[kRegSort];      // then the sorted exact survivals and ids (run fix-up)
@@ -65,10 +77,17 @@ struct SchedSmem {
     } u;
     int len[kMaxCand];         // per request kept length (B <= kMaxCand)
     float cost[kMaxCand + 1];  // cost[B + m] for m = 0..min(B*G, budget - B)
-    int nvalid, mstar;
+    int nvalid, mstar, nsel;
     double taustar;            // tau_{m*}
     double red[kMaxThreads / 64][kMaxRatios];   // ratio budgets: per-wave progress sums
     int wsum[kMaxThreads / 64];                 // per-wave totals of a block scan
+    int wmax[kMaxThreads / 64];                 // per-wave maxima
+    int wany[kMaxThreads / 64];                 // per-wave flags
+    alignas(16) int hist[kBins];                // window bins: counts, then each bin's first place
+    double rs[kGrp];           // k_schedule: the first places in order (survival, id)
+    int ri[kGrp];
+    uint8_t kept[kMaxCand];    // k_dcut: by slot, bit r set when ratio r keeps the draft
+    double tau[9];             // the walk: tau before candidates 0, 8, ..., 56 of a block, and after the last
 };
 
 // Order: larger survival first; equal survival -> smaller k, then smaller b
@@ -167,72 +186,33 @@ __device__ __forceinline__ float conf_at(const float *conf, const Calib &cal, in
 }
 
 // Sorting slot i: its survival when it is a candidate, else -inf padding.
-// L = 0: slot i is draft i = b * G + k.  L > 0 (survival never rises along a
-// request): request b owns the run of L slots from b * L, its drafts in order
-// (reversed for odd b), padding after them, so every run is already sorted
-// and consecutive runs alternate direction: the bitonic network can start at
-// stage 2L.
+// L = 0: slot i.  L > 0 (survival never rises along a request): request b
+// owns the run of L slots from b * L, its drafts in order (reversed for odd
+// b), padding after them, so every run is already sorted and consecutive runs
+// alternate direction: the bitonic network can start at stage 2L.
 __device__ __forceinline__ void slot_key(const SchedSmem &sh, int i, int N, int B, int G, int L, double eps,
                                          double &s, int &id) {
     s = -__builtin_inf();
     id = kPad;
-    int b, k;
+    int j;
     if (L > 0) {
-        b = i / L;
-        const int j = i - b * L;
-        k = (b & 1) ? L - 1 - j : j;
+        const int b = i / L, r = i - b * L;
+        const int k = (b & 1) ? L - 1 - r : r;
         if (b >= B || k >= G) return;
+        j = k * B + b;
     } else {
         if (i >= N) return;
-        b = i / G;
-        k = i - b * G;
+        j = i;
     }
-    const double v = sh.key[b * G + k];
+    const double v = sh.key[j];
     if (v > eps) {
         s = v;
-        id = k * B + b;
+        id = j;
     }
 }
 
-// 2. Survival s[b, k] = ((c[b,0] * c[b,1]) * ...) * c[b,k] (confidences in
-//    sh.u.conf), the sequential product, one thread per request (for G <= 16
-//    its reads are issued together: clamped in bounds, the ones past G
-//    unused).  Returns whether survival is non-increasing along every request.
-__device__ __forceinline__ bool survivals(SchedSmem &sh, int B, int G, int tid, int nth) {
-    const int N = B * G;
-    bool mono = true;
-    for (int b = tid; b < B; b += nth) {
-        const double *c = sh.u.conf + b * G;
-        double *sv = sh.key + b * G;
-        double acc = 1.0;
-        if (G > 0 && G <= 16) {
-            double cv[16];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) cv[k] = sh.u.conf[min(b * G + k, N - 1)];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                if (k < G) {
-                    const double nx = acc * cv[k];
-                    if (k > 0 && !(nx <= acc)) mono = false;
-                    acc = nx;
-                    sv[k] = acc;
-                }
-            }
-        } else {
-            for (int k = 0; k < G; ++k) {
-                const double nx = acc * c[k];
-                if (k > 0 && !(nx <= acc)) mono = false;
-                acc = nx;
-                sv[k] = acc;
-            }
-        }
-        sh.len[b] = 0;
-    }
-    return __syncthreads_and(mono);
-}
-
-// 3. Sort the candidates (survival in sh.key above eps) in the order (s desc,
-//    k asc, b asc), padding last: sh.key / sh.id hold the sorted survivals and
+// Network sort of the candidates (survival in sh.key above eps) in the order
+//    (s desc, k asc, b asc), padding last: sh.key / sh.id hold the sorted survivals and
 //    ids k * B + b.  Returns the number of candidates.  presorted: survival
 //    never rises along any request, so the run layout of slot_key applies when
 //    it needs no more slots than the workgroup has threads.
@@ -290,10 +270,7 @@ __device__ __forceinline__ int sort_candidates(SchedSmem &sh, int B, int G, doub
         // each element exactly inside its run (usually a run of one).
         const int id = key_id(k);
         double s = -__builtin_inf();
-        if (id != kPad) {
-            const int kk = id / B, b = id - kk * B;
-            s = sh.key[b * G + kk];
-        }
+        if (id != kPad) s = sh.key[id];
         __syncthreads();                           // the last exchange buffer is read
         sh.u.reg.xq[0][tid] = k;
         sh.u.reg.fs[tid] = s;
@@ -350,32 +327,327 @@ __device__ __forceinline__ int sort_candidates(SchedSmem &sh, int B, int G, doub
     return ncand;
 }
 
-// One block of the grid; blockDim.x = max(64, Np) when Np <= kRegSort (the
-// register sort), else kMaxThreads.
+// 5. Walk the sorted candidates key[0..mt) (wave 0): m* = the first m with
+//    !(theta_{m+1} > theta_m), or mt; tau_m = B + s_(0) + ... + s_(m-1) in
+//    candidate order and theta_m = tau_m / cost[B + m].  Per block of 64: one
+//    lane extends the running sum over the block and stores it before every
+//    8th candidate; each lane then repeats the sum from its checkpoint to its
+//    own candidate (the same additions in the same order, so the same tau),
+//    and the 64 tests run at once, one per lane; the walk stops at the block
+//    holding the first failure.  Sets sh.mstar and sh.taustar.
+__device__ __forceinline__ void walk(SchedSmem &sh, const double *key, int mt, int B, int lane) {
+    double t = double(B);
+    if (mt == 0 && lane == 0) { sh.mstar = 0; sh.taustar = t; }
+    for (int base = 0; base < mt; base += 64) {
+        const int cnt = min(64, mt - base);
+        const double *kb = key + base;
+        if (lane == 0) {
+            double u = t;
+            if (cnt == 64) {                          // a full block: no per-step bound
+#pragma unroll
+                for (int j0 = 0; j0 < 64; j0 += 32) {
+                    double v[32];
+#pragma unroll
+                    for (int j = 0; j < 32; ++j) v[j] = kb[j0 + j];
+#pragma unroll
+                    for (int j = 0; j < 32; ++j) {
+                        if (((j0 + j) & 7) == 0) sh.tau[(j0 + j) >> 3] = u;
+                        u = u + v[j];
+                    }
+                }
+            } else {
+                for (int j = 0; j < cnt; ++j) {
+                    if ((j & 7) == 0) sh.tau[j >> 3] = u;
+                    u = u + kb[j];
+                }
+            }
+            sh.tau[8] = u;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        bool fail = false;
+        double tau0 = 0.0;
+        if (lane < cnt) {
+            const int m = base + lane, r = lane & 7;
+            double v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = kb[min((lane & ~7) + q, cnt - 1)];   // those past r unused
+            double u = sh.tau[lane >> 3];
+#pragma unroll
+            for (int q = 0; q < 7; ++q)
+                if (q < r) u = u + v[q];
+            tau0 = u;
+            double sm = v[0];
+#pragma unroll
+            for (int q = 1; q < 8; ++q) sm = (q == r) ? v[q] : sm;
+            const double tau1 = u + sm;
+            const double th0 = tau0 / double(sh.cost[m]);
+            const double th1 = tau1 / double(sh.cost[m + 1]);
+            fail = !(th1 > th0);
+        }
+        t = sh.tau[8];
+        const unsigned long long f = __ballot(fail);
+        if (f) {
+            const int first = __builtin_ctzll(f);
+            if (lane == first) { sh.mstar = base + first; sh.taustar = tau0; }
+            break;
+        }
+        if (base + 64 >= mt && lane == 0) { sh.mstar = mt; sh.taustar = t; }   // no failure up to mt
+        __builtin_amdgcn_wave_barrier();                                       // tau[] is rewritten next
+    }
+}
+
+// 6. Lengths from the first m* candidates (ids[0..m*)), tau_{m*} for the caller.
+__device__ __forceinline__ void tally(SchedSmem &sh, const ScheduleArgs &a, const int *ids, int mstar, int tid,
+                                      int nth) {
+    const int B = a.B;
+    for (int m = tid; m < mstar; m += nth) {
+        const int id = ids[m];
+        const int k = id / B, b = id - k * B;
+        atomicMax(&sh.len[b], k + 1);
+    }
+    __syncthreads();
+    for (int b = tid; b < B; b += nth) a.out_len[b] = sh.len[b];
+    if (tid == 0) {
+        a.out_T[0] = B + mstar;
+        if (a.out_tau) a.out_tau[0] = float(sh.taustar);
+    }
+}
+
+// fp32 order key of a survival (ascending with the value; -0 as +0).
+__device__ __forceinline__ uint32_t ord32(double s) {
+    const uint32_t u = __float_as_uint(float(s + 0.0));
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// 2. Survivals, one thread per request b: s[b,k] = the running product of
+//    c[b,0..k] in order (sh.u.conf by slot) into sh.key.  Per thread: `up`,
+//    some survival rises; `top`, the highest candidate's bin scale
+//    (ord32 >> kWinShift; s[b,0] is a request's highest when none rises).
+__device__ __forceinline__ void survivals(SchedSmem &sh, int B, int G, double eps, int tid, int nth, bool &up,
+                                          int &top) {
+    up = false;
+    top = -1;
+    for (int b = tid; b < B && G > 0; b += nth) {
+        double acc = 1.0, s0;
+        if (G <= 16) {
+            // Branch-free: positions past G multiply by 1 (acc unchanged,
+            // never a rise) and store the same value again at G - 1.
+            double cv[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const double x = sh.u.conf[min(t, G - 1) * B + b];
+                cv[t] = (t < G) ? x : 1.0;
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const double nx = acc * cv[t];
+                up |= t > 0 && !(nx <= acc);
+                acc = nx;
+                if (t == 0) s0 = acc;
+                sh.key[min(t, G - 1) * B + b] = acc;
+            }
+        } else {
+            for (int t = 0; t < G; ++t) {
+                const double nx = acc * sh.u.conf[t * B + b];
+                if (t > 0 && !(nx <= acc)) up = true;
+                acc = nx;
+                sh.key[t * B + b] = acc;
+            }
+            s0 = sh.key[b];
+        }
+        if (s0 > eps) top = max(top, int(ord32(s0) >> kWinShift));
+    }
+}
+
+// Block-wide OR of `up` and maximum of `top` (both per thread), with the one
+// barrier the survivals need anyway.  Returns the maximum; `any` the OR.
+__device__ __forceinline__ int reduce_survival_flags(SchedSmem &sh, bool up, int top, int lane, int wv, int nw,
+                                                     bool &any) {
+    const int tw = wave_scan_max_i(top + 1);
+    const bool wu = __ballot(up) != 0ull;
+    if (lane == 63) {
+        sh.wmax[wv] = tw;
+        sh.wany[wv] = wu ? 1 : 0;
+    }
+    __syncthreads();
+    const int x = (lane < nw) ? sh.wmax[lane] : 0, f = (lane < nw) ? sh.wany[lane] : 0;
+    any = __ballot(f != 0) != 0ull;
+    return __builtin_amdgcn_readlane(wave_scan_max_i(x), 63) - 1;
+}
+
+// 3. Window bins (survival never rises; sh.key by slot; sh.hist[0, kWinPer *
+//    nth) zero).  Every candidate slot goes to bin top - (ord32(s) >>
+//    kWinShift), at most the last, and takes a number inside it (LDS atomic);
+//    a block scan turns the counts into each bin's first place (bins ascend
+//    as survival descends, and hold ordered ranges of it).  Per thread: its
+//    slots' (survival, bin or -1, number) and its own bins' counts c4 and
+//    first places s4; returns the number of candidates.  The caller's barrier
+//    publishes the first places.
+__device__ int window_bins(SchedSmem &sh, int N, double eps, int top, int tid, int lane, int nth,
+                           double (&sv)[kEpt], int (&fb)[kEpt], int (&at)[kEpt], int4 &c4, int4 &s4) {
+    const int wv = tid >> 6, nw = nth >> 6, nb = kWinPer * nth;
+#pragma unroll
+    for (int r = 0; r < kEpt; ++r) {
+        const int i = tid + r * nth;
+        fb[r] = -1;
+        sv[r] = 0.0;
+        at[r] = 0;
+        if (i < N) {
+            sv[r] = sh.key[i];
+            if (sv[r] > eps) {
+                fb[r] = min(max(top - int(ord32(sv[r]) >> kWinShift), 0), nb - 1);
+                at[r] = atomicAdd(&sh.hist[fb[r]], 1);
+            }
+        }
+    }
+    __syncthreads();
+    c4 = *reinterpret_cast<const int4 *>(&sh.hist[kWinPer * tid]);
+    const int local = (c4.x + c4.y) + (c4.z + c4.w);
+    const int incl = wave_scan_i(local);
+    if (lane == 63) sh.wsum[wv] = incl;
+    __syncthreads();
+    const int wx = wave_scan_i((lane < nw) ? sh.wsum[lane] : 0);
+    const int total = __builtin_amdgcn_readlane(wx, 63);
+    const int w = __builtin_amdgcn_readfirstlane(wv);
+    int cum = incl - local + ((w > 0) ? __builtin_amdgcn_readlane(wx, w - 1) : 0);
+    s4.x = cum;
+    cum += c4.x;
+    s4.y = cum;
+    cum += c4.y;
+    s4.z = cum;
+    cum += c4.z;
+    s4.w = cum;
+    *reinterpret_cast<int4 *>(&sh.hist[kWinPer * tid]) = s4;
+    return total;
+}
+
+// Places inside a bin: candidates in bins marked by `rank_it` are grouped by
+// place (survival in sh.u.conf, id in sh.id, at first place + number), then
+// each one's place is its bin's first place plus the candidates of its bin
+// that precede it (exact comparisons).  place[r] = -1 for the others.
+// Bins end at the next bin's first place, the last at `total`.
+template <class F>
+__device__ void place_in_bins(SchedSmem &sh, int total, int tid, int nth, const double (&sv)[kEpt],
+                              const int (&fb)[kEpt], const int (&at)[kEpt], int (&place)[kEpt], F rank_it) {
+    const int nb = kWinPer * nth;
+    int lo[kEpt], hi[kEpt];
+#pragma unroll
+    for (int r = 0; r < kEpt; ++r) {
+        place[r] = -1;
+        lo[r] = hi[r] = 0;
+        if (fb[r] >= 0) {
+            lo[r] = sh.hist[fb[r]];
+            hi[r] = (fb[r] + 1 < nb) ? sh.hist[fb[r] + 1] : total;
+            if (rank_it(lo[r], hi[r])) {
+                sh.u.conf[lo[r] + at[r]] = sv[r];
+                sh.id[lo[r] + at[r]] = tid + r * nth;
+            } else {
+                lo[r] = hi[r] = -1;                 // not ranked inside
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kEpt; ++r) {
+        if (lo[r] >= 0 && fb[r] >= 0) {             // lo = -1: not ranked; fb = -1: not a candidate
+            const int id = tid + r * nth;
+            int p = lo[r];
+            for (int q0 = lo[r]; q0 < hi[r]; q0 += 4) {     // four reads in flight
+                double gs[4];
+                int gi[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    gs[q] = sh.u.conf[min(q0 + q, hi[r] - 1)];
+                    gi[q] = sh.id[min(q0 + q, hi[r] - 1)];
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) p += (q0 + q < hi[r] && before(gs[q], gi[q], sv[r], id)) ? 1 : 0;
+            }
+            place[r] = p;
+        }
+    }
+}
+
+// One block of the grid; blockDim.x = max(64, Np) when Np <= kRegSort, else
+// kMaxThreads.  When survival never rises (the usual case): window bins, the
+// bins that start before kTopK ranked inside (they are the first S places of
+// the order exactly), and the walk over them; the walk needs only about m* +
+// 64 places, so it is decided there unless it passes S or a ranked bin is
+// too full.  Otherwise (and then): the network sort of every candidate.
 __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
     __shared__ SchedSmem sh;
-    const int tid = threadIdx.x, lane = tid & 63, nth = blockDim.x;
+    const int tid = threadIdx.x, lane = tid & 63, nth = blockDim.x, wv = tid >> 6, nw = nth >> 6;
     const int B = a.B, G = a.G, N = B * G;
     const double eps = double(a.eps);
     const int mt_max = min(N, a.budget - B);          // kept drafts never exceed this
 
-    // 1. every input the scan can read, in one round trip.
-    for (int i = tid; i < N; i += nth) sh.u.conf[i] = double(conf_at(a.conf, a.cal, i, G));
+    // 1. every input the scan can read, in one round trip (confidences by
+    //    slot); bins and lengths cleared.
+    for (int j = tid; j < N; j += nth) {
+        const int k = j / B, b = j - k * B;
+        sh.u.conf[j] = double(conf_at(a.conf, a.cal, b * G + k, G));
+    }
     for (int i = tid; i <= mt_max; i += nth) sh.cost[i] = a.cost[B + i];
+    *reinterpret_cast<int4 *>(&sh.hist[kWinPer * tid]) = make_int4(0, 0, 0, 0);
+    for (int b = tid; b < B; b += nth) sh.len[b] = 0;
     __syncthreads();
 
-    const bool nonincr = survivals(sh, B, G, tid, nth);
-    int ncand = sort_candidates(sh, B, G, eps, tid, lane, nth, nonincr);
+    bool up;
+    int top;
+    survivals(sh, B, G, eps, tid, nth, up, top);
+    bool rises;
+    const int topb = reduce_survival_flags(sh, up, top, lane, wv, nw, rises);
+
+    if (!rises) {
+        double sv[kEpt];
+        int fb[kEpt], at[kEpt], place[kEpt];
+        int4 c4, s4;
+        const int total = window_bins(sh, N, eps, topb, tid, lane, nth, sv, fb, at, c4, s4);
+        // S = the end of the bin holding place kTopK - 1 (one writer), or
+        // every candidate when there are fewer; a ranked bin over kWinCap
+        // sends the call to the network sort.
+        const int cs[4] = {c4.x, c4.y, c4.z, c4.w}, ss[4] = {s4.x, s4.y, s4.z, s4.w};
+        bool big = false;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (cs[q] > 0 && ss[q] < kTopK && ss[q] + cs[q] >= kTopK) sh.nsel = ss[q] + cs[q];
+            big |= cs[q] > kWinCap && ss[q] < kTopK;
+        }
+        const bool wb = __ballot(big) != 0ull;
+        if (lane == 63) sh.wany[wv] = wb ? 1 : 0;
+        __syncthreads();
+        if (__ballot(lane < nw && sh.wany[lane] != 0) == 0ull) {
+            const int S = (total < kTopK) ? total : sh.nsel;
+            place_in_bins(sh, total, tid, nth, sv, fb, at, place, [](int lo, int) { return lo < kTopK; });
+#pragma unroll
+            for (int r = 0; r < kEpt; ++r) {
+                if (place[r] >= 0) {
+                    sh.rs[place[r]] = sv[r];
+                    sh.ri[place[r]] = tid + r * nth;
+                }
+            }
+            __syncthreads();
+            const int mt = min(total, mt_max);
+            const int mtw = min(S, mt);
+            if (tid < 64) walk(sh, sh.rs, mtw, B, lane);
+            __syncthreads();
+            const int mstar = sh.mstar;
+            if (!(mstar == mtw && mtw < mt)) {        // decided inside the ranked places
+                tally(sh, a, sh.ri, mstar, tid, nth);
+                return;
+            }
+        }
+        __syncthreads();
+    }
+    int ncand = sort_candidates(sh, B, G, eps, tid, lane, nth, !rises);
 
     // 4. contiguity: only when some survival increases along a request.
-    if (!nonincr) {
+    if (rises) {
         for (int i = tid; i < N; i += nth) sh.u.pos[i] = -1;
         __syncthreads();
-        for (int p = tid; p < ncand; p += nth) {
-            const int id = sh.id[p];
-            const int k = id / B, b = id - k * B;
-            sh.u.pos[b * G + k] = p;
-        }
+        for (int p = tid; p < ncand; p += nth) sh.u.pos[sh.id[p]] = p;
         __syncthreads();
         for (int p = tid; p < ncand; p += nth) {
             const int id = sh.id[p];
@@ -383,7 +655,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
             bool valid = true;
             int prevp = -1;
             for (int kk = 0; kk <= k; ++kk) {
-                const int pp = sh.u.pos[b * G + kk];
+                const int pp = sh.u.pos[kk * B + b];
                 if (pp < 0 || pp <= prevp) { valid = false; break; }
                 prevp = pp;
             }
@@ -410,98 +682,98 @@ __global__ __launch_bounds__(kMaxThreads) void k_schedule(ScheduleArgs a) {
         ncand = sh.nvalid;
     }
     const int mt = min(ncand, mt_max);                // at most budget - B can be kept
-
-    // 5. walk the sorted candidates; m* = first m with !(theta_{m+1} > theta_m).
-    //    tau_m = B + s_(0) + ... + s_(m-1) in candidate order; theta_m = tau_m / cost[B + m].
-    if (tid < 64) {
-        double t = double(B);
-        if (mt == 0 && lane == 0) { sh.mstar = 0; sh.taustar = t; }
-        for (int base = 0; base < mt; base += 64) {
-            const int m = base + lane;
-            const double sm = (m < mt) ? sh.key[m] : 0.0;
-            double tau0 = 0.0, tau1 = 0.0;
-            const int cnt = min(64, mt - base);
-            if (cnt == 64) {                      // a full block: no per-step bound
-#pragma unroll
-                for (int j = 0; j < 64; ++j) {
-                    if (lane == j) tau0 = t;
-                    t = t + lane_d(sm, j);
-                    if (lane == j) tau1 = t;
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 64; ++j) {
-                    if (j < cnt) {
-                        if (lane == j) tau0 = t;
-                        t = t + lane_d(sm, j);
-                        if (lane == j) tau1 = t;
-                    }
-                }
-            }
-            bool fail = false;
-            if (m < mt) {
-                const double th0 = tau0 / double(sh.cost[m]);
-                const double th1 = tau1 / double(sh.cost[m + 1]);
-                fail = !(th1 > th0);
-            }
-            const unsigned long long f = __ballot(fail);
-            if (f) {
-                const int first = __builtin_ctzll(f);
-                if (lane == first) { sh.mstar = base + first; sh.taustar = tau0; }
-                break;
-            }
-            if (base + 64 >= mt && lane == 0) { sh.mstar = mt; sh.taustar = t; }   // no failure up to mt
-        }
-    }
+    if (tid < 64) walk(sh, sh.key, mt, B, lane);
     __syncthreads();
-    const int mstar = sh.mstar;
-
-    // 6. lengths from the first m* candidates, tau_{m*} for the caller.
-    for (int m = tid; m < mstar; m += nth) {
-        const int id = sh.id[m];
-        const int k = id / B, b = id - k * B;
-        atomicMax(&sh.len[b], k + 1);
-    }
-    __syncthreads();
-    for (int b = tid; b < B; b += nth) a.out_len[b] = sh.len[b];
-    if (tid == 0) {
-        a.out_T[0] = B + mstar;
-        if (a.out_tau) a.out_tau[0] = float(sh.taustar);
-    }
+    tally(sh, a, sh.id, sh.mstar, tid, nth);
 }
 
 // Ratio-budgeted depth ("AngelSpec", section 4.2, Eq. 20-24): one block,
-// blockDim.x as for k_schedule.  Every draft is ranked once (the sort above,
-// with every draft a candidate); the budget of ratio r keeps the drafts of
+// blockDim.x as for k_schedule.  The budget of ratio r keeps the drafts of
 // sorted position < keep[r] = K_r - B, which is a contiguous prefix of every
 // request because survival never rises (confidences clamped into [0, 1]) and
-// equal survivals rank shallower first.  Then, per ratio, the estimated
-// progress U_r = sum_b (1 + kept survivals of b), the ratio with the largest
-// U_r / C_r (the first on ties), its keep depths and the packed row offsets.
+// equal survivals rank shallower first.  Only which side of each keep[r] a
+// draft falls on matters: with window bins, a bin that ends by keep[r] is
+// kept whole and one that starts at or after it not at all; only the bins
+// holding a keep[r] strictly inside are ranked inside (the network sort when
+// one is too full).  Then, per ratio, the estimated progress U_r = sum_b
+// (1 + kept survivals of b), the ratio with the largest U_r / C_r (the first
+// on ties), its keep depths and the packed row offsets.
 __global__ __launch_bounds__(kMaxThreads) void k_dcut(DcutArgs a) {
     __shared__ SchedSmem sh;
-    const int tid = threadIdx.x, lane = tid & 63, nth = blockDim.x, wv = tid >> 6;
-    const int B = a.B, G = a.G, N = B * G;
+    const int tid = threadIdx.x, lane = tid & 63, nth = blockDim.x, wv = tid >> 6, nwt = nth >> 6;
+    const int B = a.B, G = a.G, N = B * G, R = a.R;
+    const double ninf = -__builtin_inf();
 
-    for (int i = tid; i < N; i += nth) {
-        const double c = double(conf_at(a.conf, a.cal, i, G));
-        sh.u.conf[i] = (c > 0.0) ? fmin(c, 1.0) : 0.0;   // NaN -> 0
+    for (int j = tid; j < N; j += nth) {
+        const int k = j / B, b = j - k * B;
+        const double c = double(conf_at(a.conf, a.cal, b * G + k, G));
+        sh.u.conf[j] = (c > 0.0) ? fmin(c, 1.0) : 0.0;   // NaN -> 0
     }
+    *reinterpret_cast<int4 *>(&sh.hist[kWinPer * tid]) = make_int4(0, 0, 0, 0);
     __syncthreads();
-    survivals(sh, B, G, tid, nth);
-    sort_candidates(sh, B, G, -__builtin_inf(), tid, lane, nth, true);   // clamped: survival never rises
-    for (int p = tid; p < N; p += nth) {                  // sorted position of each draft
-        const int id = sh.id[p];
-        const int k = id / B, b = id - k * B;
-        sh.u.pos[b * G + k] = p;
+    bool up;
+    int top;
+    survivals(sh, B, G, ninf, tid, nth, up, top);
+    bool rises;                                           // clamped: never
+    const int topb = reduce_survival_flags(sh, up, top, lane, wv, nwt, rises);
+
+    double sv[kEpt];
+    int fb[kEpt], at[kEpt], place[kEpt];
+    int4 c4, s4;
+    const int total = window_bins(sh, N, ninf, topb, tid, lane, nth, sv, fb, at, c4, s4);
+    // A bin holding some keep[r] strictly inside is ranked inside; too full: network sort.
+    const auto straddles = [&](int lo, int hi) {
+        bool x = false;
+#pragma unroll
+        for (int r = 0; r < kMaxRatios; ++r) x |= r < R && lo < a.keep[r] && a.keep[r] < hi;
+        return x;
+    };
+    const int cs[4] = {c4.x, c4.y, c4.z, c4.w}, ss[4] = {s4.x, s4.y, s4.z, s4.w};
+    bool big = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) big |= cs[q] > kWinCap && straddles(ss[q], ss[q] + cs[q]);
+    const bool wb = __ballot(big) != 0ull;
+    if (lane == 63) sh.wany[wv] = wb ? 1 : 0;
+    __syncthreads();
+    const double *surv = sh.key;                          // survival by slot
+    if (__ballot(lane < nwt && sh.wany[lane] != 0) == 0ull) {
+        place_in_bins(sh, total, tid, nth, sv, fb, at, place, straddles);
+#pragma unroll
+        for (int r = 0; r < kEpt; ++r) {
+            const int i = tid + r * nth;
+            if (i < N) {
+                const int lo = sh.hist[fb[r]];
+                const int hi = (fb[r] + 1 < kWinPer * nth) ? sh.hist[fb[r] + 1] : total;
+                uint32_t m = 0;
+#pragma unroll
+                for (int q = 0; q < kMaxRatios; ++q) {
+                    const int kp = a.keep[q];
+                    const bool kept = hi <= kp || (lo < kp && place[r] >= 0 && place[r] < kp);
+                    m |= (q < R && kept) ? (1u << q) : 0u;
+                }
+                sh.kept[i] = uint8_t(m);
+            }
+        }
+        __syncthreads();
+    } else {
+        __syncthreads();
+        sort_candidates(sh, B, G, ninf, tid, lane, nth, true);
+        for (int p = tid; p < N; p += nth) {              // by slot: survival and kept bits
+            const int id = sh.id[p];
+            uint32_t m = 0;
+#pragma unroll
+            for (int q = 0; q < kMaxRatios; ++q) m |= (q < R && p < a.keep[q]) ? (1u << q) : 0u;
+            sh.kept[id] = uint8_t(m);
+            sh.u.conf[id] = sh.key[p];
+        }
+        __syncthreads();
+        surv = sh.u.conf;
     }
-    __syncthreads();
 
     // Progress of request b at each ratio's depth, in position order:
     // A_b = 1 + s_0 + ... + s_{n-1}, and the depth n itself; summed per
     // thread, then per wave (DPP), then over the waves that hold requests,
     // in order.
-    const int R = a.R;
     double U[kMaxRatios];
     int nr[kMaxRatios];                                // depths of this thread's (last) request
 #pragma unroll
@@ -517,20 +789,21 @@ __global__ __launch_bounds__(kMaxThreads) void k_dcut(DcutArgs a) {
             nr[r] = 0;
         }
         if (G > 0 && G <= 16) {
-            // positions, then survivals, each batch issued together
-            int pp[16];
-            double sv[16];
+            // kept bits, then survivals, each batch issued together
+            uint32_t km[16];
+            double s[16];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) pp[k] = sh.u.pos[min(b * G + k, N - 1)];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) sv[k] = sh.key[pp[k]];
+            for (int k = 0; k < 16; ++k) {
+                km[k] = sh.kept[min(k, G - 1) * B + b];
+                s[k] = surv[min(k, G - 1) * B + b];
+            }
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 if (k < G) {
-                    A = A + sv[k];
+                    A = A + s[k];
 #pragma unroll
                     for (int r = 0; r < kMaxRatios; ++r)
-                        if (pp[k] < a.keep[r]) {
+                        if ((km[k] >> r) & 1u) {
                             Ab[r] = A;
                             nr[r] = k + 1;
                         }
@@ -538,11 +811,11 @@ __global__ __launch_bounds__(kMaxThreads) void k_dcut(DcutArgs a) {
             }
         } else {
             for (int k = 0; k < G; ++k) {
-                const int p = sh.u.pos[b * G + k];
-                A = A + sh.key[p];
+                const uint32_t m = sh.kept[k * B + b];
+                A = A + surv[k * B + b];
 #pragma unroll
                 for (int r = 0; r < kMaxRatios; ++r)
-                    if (p < a.keep[r]) {
+                    if ((m >> r) & 1u) {
                         Ab[r] = A;
                         nr[r] = k + 1;
                     }
@@ -602,7 +875,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_dcut(DcutArgs a) {
     } else {
         for (int b = tid; b < B; b += nth) {
             int n = 0;
-            for (int k = 0; k < G; ++k) n += int(sh.u.pos[b * G + k] < keep);
+            for (int k = 0; k < G; ++k) n += int((sh.kept[k * B + b] >> best) & 1u);
             sh.len[b] = n;
             a.out_len[b] = n;
         }

@@ -110,6 +110,7 @@ struct VerifyArgs {
     int32_t *out_path;            // tree walk: [B, G+1] accepted nodes, then -1
     uint32_t spin_limit;
     int32_t lag;                  // one-launch verify: requests between a request's rows and its decision workgroup
+    int32_t vlrows;               // one-launch verify with verify lengths: its row workgroups (0: full grid)
 };
 
 // Launchers (verify_kernels.hip).  Return a hipError_t as int.
@@ -117,7 +118,9 @@ int launch_rows_sampled(const VerifyArgs &a, bool aligned_z, int esize, int grid
 int launch_rows_sampled_vl(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
 int launch_requests_sampled(const VerifyArgs &a, bool aligned_z, bool aligned_q, int esize, int grid,
                             void *stream);   // draft logits when a.dl is set
-// One launch: the row workgroups, then the request workgroups (draft probabilities only).
+// One launch: the row workgroups, a decision workgroup per request, then the
+// request workgroups (draft probabilities only); a.vlrows > 0: the row
+// workgroups are a.vlrows of the verify-length kind.
 int launch_verify_sampled(const VerifyArgs &a, bool aligned_z, bool aligned_q, int esize, int grid, void *stream);
 int launch_verify_greedy(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
 int greedy_occupancy(bool aligned_z, int esize, int *blocks_per_cu);

@@ -116,5 +116,17 @@ __device__ __forceinline__ int wave_scan_i(int x) {
     return x;
 }
 
+// Inclusive prefix maximum of a non-negative int over the wave (lane 63
+// holds the wave's maximum; lanes without a source read 0, the identity).
+__device__ __forceinline__ int wave_scan_max_i(int x) {
+    x = max(x, dpp_i<kRowShr1>(x));
+    x = max(x, dpp_i<kRowShr2>(x));
+    x = max(x, dpp_i<kRowShr4>(x));
+    x = max(x, dpp_i<kRowShr8>(x));
+    x = max(x, dpp_i<kRowBcast15, 0xA>(x));
+    x = max(x, dpp_i<kRowBcast31, 0xC>(x));
+    return x;
+}
+
 }  // namespace
 }  // namespace sv

@@ -1367,49 +1367,57 @@ __global__ __launch_bounds__(kWG) void k_rows_sampled(VerifyArgs a) {
 // be unread: a grid sized to the device whose workgroups visit only the read
 // row groups.  Each workgroup first forms, in LDS, the prefix over requests of
 // their read row groups ((n_b + 1) * np1; none for an invalid length), then
-// takes jobs blockIdx, blockIdx + gridDim, ... of that list and finds each
-// job's request by binary search.
+// takes jobs first, first + nwg, ... of that list (first = its index among the
+// nwg row workgroups) and finds each job's request by binary search.
+// `published` as for row_group_sampled (the one-launch verify).
+struct VlSmem {
+    float gm[kWaves], gs[kWaves];
+    int off[kWG + 1];
+    int wtot[kWaves];
+    int nlen[kWG], row0[kWG];                 // each request's length and first target row
+};
 template <int ES, bool AL>
-__global__ __launch_bounds__(kWG) void k_rows_sampled_vl(VerifyArgs a) {
-    __shared__ float gm[kWaves], gs[kWaves];
-    __shared__ int off[kWG + 1];
-    __shared__ int wtot[kWaves];
-    __shared__ int nlen[kWG], row0[kWG];     // each request's length and first target row
+__device__ void rows_vl(const VerifyArgs &a, int first, int nwg, bool published, VlSmem &v) {
     const int t = int(threadIdx.x), lane = t & 63, w = wave_id();
     int cnt = 0;
     if (t < a.B) {
         const int n = verify_len(a, t);
         cnt = (n >= 0 && n <= a.G) ? ((n + 1) + (a.dl ? n : 0)) * a.np1 : 0;   // target rows, then draft rows
-        nlen[t] = n;
-        row0[t] = a.roff ? ld_const(a.roff, t) : t * (a.G + 1);
+        v.nlen[t] = n;
+        v.row0[t] = a.roff ? ld_const(a.roff, t) : t * (a.G + 1);
     }
     const int x = wave_scan_i(cnt);
-    if (lane == 63) wtot[w] = x;
+    if (lane == 63) v.wtot[w] = x;
     __syncthreads();
     int base = 0, total = 0;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-        base += (v < w) ? wtot[v] : 0;
-        total += wtot[v];
+    for (int q = 0; q < kWaves; ++q) {
+        base += (q < w) ? v.wtot[q] : 0;
+        total += v.wtot[q];
     }
-    off[t] = base + x - cnt;                          // exclusive: first job of request t
-    if (t == 0) off[kWG] = total;
+    v.off[t] = base + x - cnt;                        // exclusive: first job of request t
+    if (t == 0) v.off[kWG] = total;
     __syncthreads();
-    for (int job = int(blockIdx.x); job < total; job += int(gridDim.x)) {
+    for (int job = first; job < total; job += nwg) {
         int lo = 0, hi = a.B - 1;                     // the last request whose first job is <= job
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (off[mid] <= job) lo = mid;
+            if (v.off[mid] <= job) lo = mid;
             else hi = mid - 1;
         }
-        const int b = lo, local = job - off[b];
-        const int n = nlen[b];
+        const int b = lo, local = job - v.off[b];
+        const int n = v.nlen[b];
         const int rr = local / a.np1, g = local - rr * a.np1;
         const bool draft = rr > n;
         const int k = draft ? rr - n - 1 : rr;
-        row_group_sampled<ES, AL>(a, b, k, g, n, draft, gm, gs, long(row0[b]) + k);
+        row_group_sampled<ES, AL>(a, b, k, g, n, draft, v.gm, v.gs, long(v.row0[b]) + k, published);
         __syncthreads();                              // gm / gs are reused by the next job
     }
+}
+template <int ES, bool AL>
+__global__ __launch_bounds__(kWG) void k_rows_sampled_vl(VerifyArgs a) {
+    __shared__ VlSmem v;
+    rows_vl<ES, AL>(a, int(blockIdx.x), int(gridDim.x), false, v);
 }
 
 // Request pass of a sampled verify: nc2 workgroups per request.
@@ -1458,12 +1466,38 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(DL ? 4 : 8,
 // the last requests' records are ready and their draw streams start at once,
 // filling the row pass's drain.  Otherwise: every rows(b), then every dec(b),
 // then every draws(b).
-template <int ES, bool ALZ, bool ALQ>
+//
+// VL (verify lengths or packed rows, at most kWG requests): the first a.vlrows
+// workgroups are k_rows_sampled_vl's (visiting only the read row groups),
+// then one decision workgroup per request, then the request workgroups.
+template <int ES, bool ALZ, bool ALQ, bool VL>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_verify_sampled(VerifyArgs a) {
     __shared__ Smem sh;
     __shared__ float gm[kWaves], gs[kWaves];
     const int per = (a.G + 1) * a.np1, nc2 = a.nc2;
     const int i = int(blockIdx.x);
+    if constexpr (VL) {
+        __shared__ VlSmem v;
+        if (i < a.vlrows) {
+            rows_vl<ES, ALZ>(a, i, a.vlrows, /*published=*/true, v);
+        } else if (i < a.vlrows + a.B) {
+            decide_publish<ES>(a, i - a.vlrows, sh);
+        } else {
+            // with vlrows and B multiples of 8, request b's workgroups share an XCD
+            const int j = i - a.vlrows - a.B;
+            int b, w;
+            if ((a.B & 7) == 0 && (a.vlrows & 7) == 0) {
+                const int x = j & 7, jj = j >> 3;
+                b = (jj / nc2) * 8 + x;
+                w = jj - (jj / nc2) * nc2;
+            } else {
+                b = j / nc2;
+                w = j - b * nc2;
+            }
+            request_item_sampled<ES, ALZ, ALQ, false, true>(a, b, w, sh);
+        }
+        return;
+    }
     int kind, b, loc;                                 // kind: 0 rows, 1 decision, 2 draws
     if ((a.B & 7) == 0) {
         const int x = i & 7;
@@ -1739,17 +1773,23 @@ int launch_requests_sampled(const VerifyArgs &a, bool az, bool aq, int esize, in
     return int(hipGetLastError());
 }
 
+template <bool VL>
+void launch_verify_sampled_t(const VerifyArgs &a, bool az, bool aq, int esize, int grid, hipStream_t st) {
+    if (esize == 2) {
+        if (az && aq) hipLaunchKernelGGL((k_verify_sampled<2, true, true, VL>), dim3(grid), dim3(kWG), 0, st, a);
+        else if (az) hipLaunchKernelGGL((k_verify_sampled<2, true, false, VL>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_verify_sampled<2, false, false, VL>), dim3(grid), dim3(kWG), 0, st, a);
+    } else {
+        if (az && aq) hipLaunchKernelGGL((k_verify_sampled<4, true, true, VL>), dim3(grid), dim3(kWG), 0, st, a);
+        else if (az) hipLaunchKernelGGL((k_verify_sampled<4, true, false, VL>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_verify_sampled<4, false, false, VL>), dim3(grid), dim3(kWG), 0, st, a);
+    }
+}
+
 int launch_verify_sampled(const VerifyArgs &a, bool az, bool aq, int esize, int grid, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (esize == 2) {
-        if (az && aq) hipLaunchKernelGGL((k_verify_sampled<2, true, true>), dim3(grid), dim3(kWG), 0, st, a);
-        else if (az) hipLaunchKernelGGL((k_verify_sampled<2, true, false>), dim3(grid), dim3(kWG), 0, st, a);
-        else hipLaunchKernelGGL((k_verify_sampled<2, false, false>), dim3(grid), dim3(kWG), 0, st, a);
-    } else {
-        if (az && aq) hipLaunchKernelGGL((k_verify_sampled<4, true, true>), dim3(grid), dim3(kWG), 0, st, a);
-        else if (az) hipLaunchKernelGGL((k_verify_sampled<4, true, false>), dim3(grid), dim3(kWG), 0, st, a);
-        else hipLaunchKernelGGL((k_verify_sampled<4, false, false>), dim3(grid), dim3(kWG), 0, st, a);
-    }
+    if (a.vlrows > 0) launch_verify_sampled_t<true>(a, az, aq, esize, grid, st);
+    else launch_verify_sampled_t<false>(a, az, aq, esize, grid, st);
     return int(hipGetLastError());
 }
 

@@ -65,7 +65,13 @@ int launch_verify_sampled(const VerifyArgs &a, bool, bool, int es, int grid, voi
     CHECK(a.G == 0 || a.x);
     CHECK(!a.dl && a.u && (a.G == 0 || a.q));
     CHECK(a.spw >= 1 && a.nc2 * a.spw >= a.nsub && (a.nc2 - 1) * a.spw < a.nsub);
-    CHECK(long(grid) == long(a.B) * ((a.G + 1) * a.np1 + 1 + a.nc2));
+    if (a.vlrows == 0) {
+        CHECK(long(grid) == long(a.B) * ((a.G + 1) * a.np1 + 1 + a.nc2));
+    } else {                                        // verify lengths: at most one resident load of row workgroups
+        CHECK(a.B <= kWG && (a.vlen || a.roff));
+        CHECK(a.vlrows >= 1 && a.vlrows <= long(a.B) * (a.G + 1) * a.np1 && a.vlrows <= 8L * 256);
+        CHECK(long(grid) == a.vlrows + long(a.B) * (1 + a.nc2));
+    }
     return 0;
 }
 int launch_verify_greedy(const VerifyArgs &a, bool, int es, int grid, void *) {

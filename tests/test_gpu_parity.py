@@ -196,6 +196,53 @@ def test_schedule_large_and_block_boundaries(B, G, slope, extra):
     assert abs(float(tau.item()) - np.float32(tauo)) <= 1e-6 * max(1.0, tauo)
 
 
+def test_schedule_selective_prefix_against_oracle():
+    """Schedules whose walk stops before, at and after the first 256 candidates
+    of the order (the kernel sorts only a prefix of the order that a histogram
+    of survivals picks, and sorts everything when the walk runs past it), with
+    exact ties, zero confidences, a negative eps and many requests."""
+    g0 = np.random.default_rng(23)
+    for trial in range(40):
+        B = int(g0.choice([17, 40, 64, 100, 256, 512, 1024]))
+        G = int(g0.integers(1, 17))
+        while B * G > 4096:
+            G -= 1
+        conf = (1 / (1 + np.exp(-g0.normal(1.5, 1.2, size=(B, G))))).astype(np.float32)
+        if trial % 4 == 1:
+            conf = (np.round(conf * 8) / 8).astype(np.float32)        # large runs of equal survival
+        if trial % 6 == 2:
+            conf[g0.random((B, G)) < 0.3] = 0.0
+        L = B * (G + 1) + 2
+        slope = float(g0.choice([0.0, 0.0005, 0.002, 0.01, 0.05]))
+        cost = (1.0 + slope * np.arange(L)).astype(np.float32)
+        budget = int(g0.integers(B, L))
+        eps = float(g0.choice([-0.5, 0.0, 0.01]))
+        lo, To, tauo = oracle.schedule(conf, cost, budget, eps)
+        say(f"[parity] schedule selective trial {trial}: B={B} G={G} slope={slope} budget={budget} eps={eps} "
+            f"kept={To - B}")
+        vl, T, tau = sv.schedule(torch.from_numpy(conf).cuda(), torch.from_numpy(cost).cuda(), budget, eps)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(vl.cpu().numpy(), lo, err_msg=f"trial {trial}")
+        assert int(T.item()) == To, trial
+        assert abs(float(tau.item()) - np.float32(tauo)) <= 1e-6 * max(1.0, tauo), trial
+
+
+def test_schedule_one_survival_bin_holds_every_candidate():
+    """512 requests with equal confidence: every candidate falls in one
+    survival bin, more than the selective sort takes, so every one is sorted."""
+    B, G = 512, 1
+    conf = np.full((B, G), 0.75, np.float32)
+    cost = np.ones(B * 2 + 1, np.float32)
+    for budget in (B, B + 1, B + 300, 2 * B):
+        lo, To, tauo = oracle.schedule(conf, cost, budget)
+        say(f"[parity] schedule, one bin, budget {budget}")
+        vl, T, tau = sv.schedule(torch.from_numpy(conf).cuda(), torch.from_numpy(cost).cuda(), budget)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(vl.cpu().numpy(), lo, err_msg=f"budget {budget}")
+        assert int(T.item()) == To == budget
+        assert float(tau.item()) == np.float32(tauo), budget
+
+
 # ------------------------------------------------------------ edge cases
 
 def _rand_workload(name, B, G, V, T=1.0, dtype="bf16", seed=0, zscale=2.0):
