@@ -160,6 +160,8 @@ struct __align__(16) Smem {
     int fsel[2];                                  // final select: first sub-tile, flags
     float gm[kWaves];                             // greedy row group: the waves' (max, index, NaN)
     int gi[kWaves], gn[kWaves];
+    uint64_t pw[2];                               // a polled record, shared from one lane
+    int pok;
 };
 
 // ---------------------------------------------------------------- merges
@@ -197,12 +199,21 @@ __device__ __forceinline__ void post_last(bool pred, int q, Smem &sh) {
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) sh.q[q][w] = m ? w * 64 + 63 - __builtin_clzll(m) : -1;
 }
+// Whether any thread's predicate holds, through ballot slot q (one barrier;
+// cheaper than __syncthreads_or).  Slot q must not be posted again before
+// every thread has read it.
+__device__ __forceinline__ bool wg_any(bool pred, int q, Smem &sh);
 // Lowest thread with the posted predicate (INT_MAX if none) / highest (-1).
 __device__ __forceinline__ int wg_first(int q, const Smem &sh) {
     return min(min(sh.q[q][0], sh.q[q][1]), min(sh.q[q][2], sh.q[q][3]));
 }
 __device__ __forceinline__ int wg_last(int q, const Smem &sh) {
     return max(max(sh.q[q][0], sh.q[q][1]), max(sh.q[q][2], sh.q[q][3]));
+}
+__device__ __forceinline__ bool wg_any(bool pred, int q, Smem &sh) {
+    post_first(pred, q, sh);
+    __syncthreads();
+    return wg_first(q, sh) != INT_MAX;
 }
 
 // Inclusive prefix over the 256 threads of NS fp64 values at once: the DPP
@@ -607,12 +618,13 @@ __device__ bool merge_rows_sampled(const VerifyArgs &a, const uint64_t *part, in
 }
 
 // merge_rows_sampled for partials that row workgroups of the same launch are
-// still writing (the one-launch verify): each row batch's coherent loads
-// repeat, with a short sleep, until every word carries its written bit (a
-// bounded wait; an expired one reports the request as bad).  The merge itself
-// is merge_rows_sampled's, in the same order, so its results are bitwise the
-// same.  `extra` issues the caller's own polled loads with every attempt and
-// reports whether they are complete; the attempt succeeds when both are.
+// still writing (the one-launch verify): each lane reloads those of its words
+// that do not yet carry their written bit until all do (a bounded wait; an
+// expired one reports the request as bad), with no workgroup-wide step per
+// attempt.  The merge itself is merge_rows_sampled's, in the same order, so
+// its results are bitwise the same.  `extra` issues the lane's own polled
+// loads with every attempt and reports whether they are complete; the lane is
+// done when both are.
 template <typename F>
 __device__ bool merge_rows_sampled_poll(const VerifyArgs &a, const uint64_t *part, int nrows, float *Mo,
                                         double *So, F extra) {
@@ -631,18 +643,18 @@ __device__ bool merge_rows_sampled_poll(const VerifyArgs &a, const uint64_t *par
         int ok = 1;
         if (a.np1 <= 16 * kRegs) {
             uint64_t v[kRegs];
+#pragma unroll
+            for (int i = 0; i < kRegs; ++i) v[i] = 0ull;
             for (uint32_t spins = 0;; ++spins) {
-                ok = 1;
 #pragma unroll
                 for (int i = 0; i < kRegs; ++i) {
                     const int cc = l + 16 * i;
-                    v[i] = (live && cc < a.np1) ? ld_coherent(pp + cc) : empty;
+                    if (!valid(v[i])) v[i] = (live && cc < a.np1) ? ld_coherent(pp + cc) : empty;
                 }
                 ok = int(extra());
 #pragma unroll
                 for (int i = 0; i < kRegs; ++i) ok &= int(valid(v[i]));
-                if (__syncthreads_and(ok) || spins >= a.spin_limit) break;
-                __builtin_amdgcn_s_sleep(2);
+                if (ok || spins >= a.spin_limit) break;
             }
 #pragma unroll
             for (int i = 0; i < kRegs; ++i) M = fmaxf(M, lo_f(v[i]));
@@ -707,17 +719,19 @@ __device__ int merge_rows_greedy(const VerifyArgs &a, int b, int n, Smem &sh) {
         int bi = -1, nan = 0, ok = 1;
         if (a.np1 <= 16 * kRegs) {
             uint64_t v[kRegs];
+#pragma unroll
+            for (int i = 0; i < kRegs; ++i) v[i] = 0ull;
             for (uint32_t spins = 0;; ++spins) {
-                ok = 1;
 #pragma unroll
                 for (int i = 0; i < kRegs; ++i) {
                     const int cc = l + 16 * i;
-                    v[i] = (live && cc < a.np1) ? ld_coherent(pp + cc) : (uint64_t(1) << 32 | uint64_t(kValid) << 32);
+                    if (!valid(v[i]))
+                        v[i] = (live && cc < a.np1) ? ld_coherent(pp + cc) : (uint64_t(1) << 32 | uint64_t(kValid) << 32);
                 }
+                ok = 1;
 #pragma unroll
                 for (int i = 0; i < kRegs; ++i) ok &= int(valid(v[i]));
-                if (__syncthreads_and(ok) || spins >= a.spin_limit) break;
-                __builtin_amdgcn_s_sleep(1);
+                if (ok || spins >= a.spin_limit) break;
             }
 #pragma unroll
             for (int i = 0; i < kRegs; ++i) {          // ascending chunks: the first maximum wins
@@ -917,7 +931,7 @@ __device__ void decide_publish(const VerifyArgs &a, int b, Smem &sh) {
         return gready;
     });
     bad |= k < n && (xk < 0 || xk >= a.V);
-    const bool err = __syncthreads_or(bad);
+    const bool err = wg_any(bad, 1, sh);
     int j = n;
     float m = 0.0f, inv_s = 0.0f;
     if (!err) {
@@ -935,6 +949,15 @@ __device__ void decide_publish(const VerifyArgs &a, int b, Smem &sh) {
         j = (jf == INT_MAX) ? n : jf;
         m = sh.M[j];
         inv_s = float(1.0 / sh.S[j]);
+    }
+    // The record first (the request workgroups wait on it), then the outputs.
+    if (threadIdx.x == 0) {
+        uint64_t *rec = decision(a, b);
+        const uint32_t h = uint32_t(j) | (j < n ? kDecResid : 0u) | (err ? 0u : kDecOk) | kValid;
+        st_coherent(rec + 1, uint64_t(__float_as_uint(inv_s)) | (uint64_t(kValid) << 32));
+        st_coherent(rec, uint64_t(__float_as_uint(m)) | (uint64_t(h) << 32));
+    }
+    if (!err) {
         for (int t = threadIdx.x; t < G1; t += kWG) {
             if (t < j) st_out(a.out_tok + size_t(b) * G1 + t, a.x[size_t(b) * G + t]);
             else if (t > j) st_out(a.out_tok + size_t(b) * G1 + t, -1);
@@ -944,23 +967,18 @@ __device__ void decide_publish(const VerifyArgs &a, int b, Smem &sh) {
         write_error(a, b);
     }
     if (diag) write_diag<ES>(a, b, !err, n, sh);
-    if (threadIdx.x == 0) {
-        uint64_t *rec = decision(a, b);
-        const uint32_t h = uint32_t(j) | (j < n ? kDecResid : 0u) | (err ? 0u : kDecOk) | kValid;
-        st_coherent(rec + 1, uint64_t(__float_as_uint(inv_s)) | (uint64_t(kValid) << 32));
-        st_coherent(rec, uint64_t(__float_as_uint(m)) | (uint64_t(h) << 32));
-    }
     uint64_t *part = partials(a, b);
     for (int i = threadIdx.x; i < (n + 1) * a.np1; i += kWG) st_coherent(part + i, 0ull);
     for (int i = threadIdx.x; i < n; i += kWG) st_coherent(gathered(a, b) + i, 0ull);
 }
 
 // A request workgroup of the one-launch verify: request b's decision, from its
-// record (a bounded wait, uniform across the workgroup).  Returns false for a
+// record (a bounded wait: one lane polls, keeping its next load in flight
+// while it examines the last, and shares the record through LDS).  Returns false for a
 // data error; *proceed is false for an invalid verify length (the decision
 // workgroup reports it).  An expired wait reports the request as bad (the
 // request's last workgroup writes the error).
-__device__ bool await_decision(const VerifyArgs &a, int b, int w, Decision &d, bool &proceed) {
+__device__ bool await_decision(const VerifyArgs &a, int b, int w, Decision &d, bool &proceed, Smem &sh) {
     const int G = a.G, G1 = G + 1;
     const int n = verify_len(a, b);
     d.n = n;
@@ -974,15 +992,24 @@ __device__ bool await_decision(const VerifyArgs &a, int b, int w, Decision &d, b
     if (!proceed) return false;
     d.u_final = a.u[size_t(b) * G1 + G];
     const uint64_t *rec = decision(a, b);
-    uint64_t w0 = 0, w1 = 0;
-    bool ready = false;
-    for (uint32_t spins = 0;; ++spins) {
-        w0 = ld_coherent(rec);
-        w1 = ld_coherent(rec + 1);
-        ready = __syncthreads_and(((w0 & w1) >> 63) != 0);
-        if (ready || spins >= a.spin_limit) break;
-        __builtin_amdgcn_s_sleep(2);
+    if (threadIdx.x == 0) {
+        // one lane polls, with the next poll in flight while it examines the last
+        uint64_t p0 = ld_coherent(rec), p1 = ld_coherent(rec + 1);
+        bool r = false;
+        for (uint32_t spins = 0;; ++spins) {
+            const uint64_t n0 = ld_coherent(rec), n1 = ld_coherent(rec + 1);
+            if (((p0 & p1) >> 63) != 0) { r = true; break; }
+            if (spins >= a.spin_limit) break;
+            p0 = n0;
+            p1 = n1;
+        }
+        sh.pw[0] = p0;
+        sh.pw[1] = p1;
+        sh.pok = r ? 1 : 0;
     }
+    __syncthreads();
+    const uint64_t w0 = sh.pw[0], w1 = sh.pw[1];
+    const bool ready = sh.pok != 0;
     if (!ready) {
         if (w == a.nc2 - 1) write_error(a, b);
         return false;
@@ -996,11 +1023,28 @@ __device__ bool await_decision(const VerifyArgs &a, int b, int w, Decision &d, b
 }
 
 // Wait until every sub-tile mass word of request b is written.  With at most
-// kWG sub-tiles thread s returns sub-tile s's (residual, target) masses in v
-// (zeros past the end).  False if the bounded wait expired.
+// kWG sub-tiles thread s polls sub-tile s's two words on its own and returns
+// its (residual, target) masses in v (zeros past the end), and one barrier
+// ends the wait.  False if a bounded wait expired.
 __device__ bool wait_masses(const VerifyArgs &a, int b, double (&v)[2]) {
     const uint64_t *mass = masses(a, b);
     const int nsub = a.nsub;
+    if (nsub <= kWG) {
+        const int s = threadIdx.x;
+        uint64_t w0 = kMassWritten, w1 = kMassWritten;
+        bool mine = true;
+        if (s < nsub) {
+            for (uint32_t spins = 0;; ++spins) {
+                w0 = ld_coherent(mass + 2 * s);
+                w1 = ld_coherent(mass + 2 * s + 1);
+                if ((w0 & w1 & kMassWritten) != 0) break;
+                if (spins >= a.spin_limit) { mine = false; break; }
+            }
+        }
+        v[0] = mass_value(w0);
+        v[1] = mass_value(w1);
+        return !__syncthreads_or(!mine);
+    }
     for (uint32_t spins = 0;; ++spins) {
         bool ready = true;
         if (nsub <= kWG) {
@@ -1188,7 +1232,7 @@ __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh
     static_assert(!(FUSED && DL), "the one-launch verify reads draft probabilities");
     Decision d;
     bool proceed;
-    const bool ok = FUSED ? await_decision(a, b, w, d, proceed) : decide<ES>(a, b, w, d, proceed, sh);
+    const bool ok = FUSED ? await_decision(a, b, w, d, proceed, sh) : decide<ES>(a, b, w, d, proceed, sh);
     if (!proceed) {
         if (!FUSED && w == 0 && (a.d_lse || a.d_p || a.d_q || a.d_r)) write_diag<ES>(a, b, false, d.n, sh);
         return;
@@ -1281,7 +1325,7 @@ __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
     // seen one round trip earlier than behind a one-lane wait on it.
     bool bad = merge_rows_greedy(a, b, n, sh) != 0;
     bad |= k < n && (xk < 0 || xk >= a.V);
-    if (__syncthreads_or(bad)) {
+    if (wg_any(bad, 1, sh)) {
         write_error(a, b);
     } else {
         post_first(k < n && xk != sh.A[k], 0, sh);
