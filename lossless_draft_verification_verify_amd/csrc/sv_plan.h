@@ -38,10 +38,11 @@ inline int chunk_elems(int esize) { return 64 * kRowVec * (16 / esize); }
 //            low = fp32 bits of z[b,k,x_k], high = bits of q[b,k,x_k] (with
 //            draft logits: of d[b,k,x_k], stored by the draft row's pass;
 //            in the one-launch verify, max(q, 0) with bit 63 set once written);
-//   dec      [B] 2 u64: the one-launch verify's decision record of request b,
+//   dec      [B] 4 u64: the one-launch verify's decision record of request b,
 //            each word with bit 63 set once written: word 0 low = fp32 bits
 //            of m_j, high = j | resid << 15 | ok << 16; word 1 low = fp32
-//            bits of 1 / S_j.
+//            bits of 1 / S_j; word 2 (written once every read row and gather
+//            has been checked) bit 0 = no data error; word 3 unused.
 
 constexpr int kMaxBatch = 65536;
 constexpr uint32_t kValid = 0x80000000u;
@@ -68,7 +69,7 @@ inline Layout make_layout(int64_t B, int64_t G, int64_t V, int esize) {
     L.partd = o; o += align256(size_t(B) * size_t(G) * size_t(nc1) * 8);
     L.mass = o; o += align256(size_t(B) * size_t(nsub) * 16);
     L.gx = o; o += align256(size_t(B) * size_t(G) * 8);
-    L.dec = o; o += align256(size_t(B) * 16);
+    L.dec = o; o += align256(size_t(B) * 32);
     L.total = o;
     return L;
 }

@@ -25,18 +25,20 @@
 //                  holds draft token x_k also publishes z(x_k) and q(x_k).
 //   decisions      one per request, placed in grid order one request after its
 //                  row groups (on the same XCD): polls the request's partials
-//                  and gathers, merges each row (fp64), runs the accept tests,
-//                  takes the first rejection j, writes the accepted prefix and
-//                  publishes a decision record (j, m_j, 1/S_j).
+//                  and gathers, merges each row (fp64) as it completes and runs
+//                  its accept test, and publishes a decision record (j, m_j,
+//                  1/S_j) as soon as rows 0..j settle the first rejection j;
+//                  once every row is in, it states whether the request holds
+//                  a data error anywhere and writes the accepted prefix.
 //   request pass   after every row group and decision: nc2 workgroups per
 //                  request (about 2048 in all), each polling the record and
 //                  streaming its sub-tiles of the one row the final token is
 //                  drawn from (target row j, plus draft row j on a rejection),
 //                  writing fp64 sub-tile masses, each word marked as written.
-//                  The request's last workgroup in grid order polls the masses,
-//                  locates u * R by a parallel prefix over them, re-scans that
-//                  one sub-tile, writes the token, and zeroes the words the
-//                  request used.
+//                  The request's last workgroup in grid order polls the masses
+//                  and the decision's error check, locates u * R by a parallel
+//                  prefix over the masses, re-scans that one sub-tile, writes
+//                  the token, and zeroes the words the request used.
 //
 // Every wait is on workgroups earlier in grid order that never wait on later
 // ones, so the launch completes whatever the device holds at once.  With B a
@@ -162,6 +164,8 @@ struct __align__(16) Smem {
     int gi[kWaves], gn[kWaves];
     uint64_t pw[2];                               // a polled record, shared from one lane
     int pok;
+    int rst[kWG / 16];                            // early decision: each row's status
+    int pub;                                      // early decision: the record is out
 };
 
 // ---------------------------------------------------------------- merges
@@ -886,31 +890,66 @@ __device__ bool decide(const VerifyArgs &a, int b, int w, Decision &d, bool &pro
 // ------------------------------------------------- one-launch decision record
 
 __device__ __forceinline__ uint64_t *decision(const VerifyArgs &a, int b) {
-    return reinterpret_cast<uint64_t *>(a.ws + size_t(a.lay.dec) * 256) + size_t(b) * 2;
+    return reinterpret_cast<uint64_t *>(a.ws + size_t(a.lay.dec) * 256) + size_t(b) * 4;
 }
 constexpr uint32_t kDecResid = 1u << 15, kDecOk = 1u << 16, kDecJ = 0x7fffu;
+// Word 2 of the record: every read row and gather checked; ok or a data error.
+constexpr uint64_t kFinWritten = uint64_t(kValid) << 32, kFinOk = 1ull;
 
 // The decision workgroup of request b in the one-launch verify, after the
 // request's row workgroups in grid order.  It polls the row partials and the
-// flagged gathers until written, then decides exactly as decide() does (the
-// same merge and accept tests); writes the accepted prefix, the -1 padding
-// and out_accepted (the token at j is left to the request workgroups), and the
-// diagnostics if asked; publishes the decision record; and clears the
-// partials and gathers, which nothing reads after it.  An invalid verify
-// length or a data error is reported here (a data error's record has ok = 0;
-// an invalid length publishes nothing: the request workgroups see the length
-// themselves).
+// flagged gathers until written and decides exactly as decide() does (the
+// same merge and accept tests), in two steps:
+//  - the record (words 0 and 1: j, the residual flag, m_j and 1 / S_j) goes
+//    out as soon as the rows it depends on are in: rows 0..j merged, rows
+//    0..j-1 accepted and row j rejected (or, with every draft accepted, row
+//    n merged).  Row workgroups finish roughly in row order and most
+//    requests reject early, so the request workgroups start the draw while
+//    the later rows are still being read.  A bad row, or an id out of range,
+//    among those rows publishes a record with ok = 0;
+//  - once every read row and gather is in, word 2 states whether the request
+//    holds a data error anywhere (the request's last workgroup waits for it
+//    before writing the drawn token); then the accepted prefix, the -1
+//    padding and out_accepted (or the error outputs) and the diagnostics go
+//    out, and the partials and gathers, which nothing reads after it, are
+//    cleared.
+// An invalid verify length publishes nothing: the request workgroups see the
+// length themselves.
+
+// The record of a decision (one thread).
+__device__ __forceinline__ void put_record(uint64_t *rec, int j, int n, bool err, float m, float inv_s) {
+    const uint32_t h = uint32_t(j) | (j < n ? kDecResid : 0u) | (err ? 0u : kDecOk) | kValid;
+    st_coherent(rec + 1, uint64_t(__float_as_uint(inv_s)) | (uint64_t(kValid) << 32));
+    st_coherent(rec, uint64_t(__float_as_uint(m)) | (uint64_t(h) << 32));
+}
+
+// After every read row is in: the accepted prefix, the padding and
+// out_accepted (the token at j is left to the request workgroups), or the
+// error outputs; the diagnostics; the clearing of the partials and gathers.
 template <int ES>
-__device__ void decide_publish(const VerifyArgs &a, int b, Smem &sh) {
+__device__ void decision_outputs(const VerifyArgs &a, int b, int n, int j, bool err, Smem &sh) {
+    const int G = a.G, G1 = G + 1;
+    if (!err) {
+        for (int t = threadIdx.x; t < G1; t += kWG) {
+            if (t < j) st_out(a.out_tok + size_t(b) * G1 + t, a.x[size_t(b) * G + t]);
+            else if (t > j) st_out(a.out_tok + size_t(b) * G1 + t, -1);
+        }
+        if (threadIdx.x == 0) st_out(a.out_acc + b, j);
+    } else {
+        write_error(a, b);
+    }
+    if (a.d_lse || a.d_p || a.d_q || a.d_r) write_diag<ES>(a, b, !err, n, sh);
+    uint64_t *part = partials(a, b);
+    for (int i = threadIdx.x; i < (n + 1) * a.np1; i += kWG) st_coherent(part + i, 0ull);
+    for (int i = threadIdx.x; i < n; i += kWG) st_coherent(gathered(a, b) + i, 0ull);
+}
+
+// More rows than 16-lane groups, or more partials per row than a lane holds:
+// every row merged first, then the record and word 2 together.
+template <int ES>
+__device__ void decide_publish_whole(const VerifyArgs &a, int b, int n, Smem &sh) {
     const int G = a.G, G1 = G + 1;
     const int k = threadIdx.x;
-    const int n = verify_len(a, b);
-    const bool diag = a.d_lse || a.d_p || a.d_q || a.d_r;
-    if (n < 0 || n > G) {
-        write_error(a, b);
-        if (diag) write_diag<ES>(a, b, false, n, sh);
-        return;
-    }
     int xk = 0;
     float uk = 0.0f;
     uint64_t gk = 0;
@@ -950,26 +989,159 @@ __device__ void decide_publish(const VerifyArgs &a, int b, Smem &sh) {
         m = sh.M[j];
         inv_s = float(1.0 / sh.S[j]);
     }
-    // The record first (the request workgroups wait on it), then the outputs.
     if (threadIdx.x == 0) {
         uint64_t *rec = decision(a, b);
-        const uint32_t h = uint32_t(j) | (j < n ? kDecResid : 0u) | (err ? 0u : kDecOk) | kValid;
-        st_coherent(rec + 1, uint64_t(__float_as_uint(inv_s)) | (uint64_t(kValid) << 32));
-        st_coherent(rec, uint64_t(__float_as_uint(m)) | (uint64_t(h) << 32));
+        put_record(rec, j, n, err, m, inv_s);
+        st_coherent(rec + 2, kFinWritten | (err ? 0ull : kFinOk));
     }
-    if (!err) {
-        for (int t = threadIdx.x; t < G1; t += kWG) {
-            if (t < j) st_out(a.out_tok + size_t(b) * G1 + t, a.x[size_t(b) * G + t]);
-            else if (t > j) st_out(a.out_tok + size_t(b) * G1 + t, -1);
-        }
-        if (threadIdx.x == 0) st_out(a.out_acc + b, j);
-    } else {
+    decision_outputs<ES>(a, b, n, j, err, sh);
+}
+
+// A row's status in the early decision.
+constexpr int kRowWait = 0, kRowAcc = 1, kRowRej = 2, kRowBadSt = 3;
+
+// What the statuses settle (uniform across the wave; lane r <= n holds row
+// r's status s): the first row not accepted decides (rejected: j; bad: a data
+// error; still waiting: nothing yet); with none, every draft is accepted and
+// j = n.
+struct Settled {
+    bool known, err;
+    int j;
+};
+__device__ __forceinline__ Settled settle(int n, int lane, int s) {
+    const uint64_t notacc = __ballot(lane <= n && s != kRowAcc);
+    const int f = notacc ? __builtin_ctzll(notacc) : n;
+    const int sf = notacc ? __builtin_amdgcn_readlane(s, f) : kRowAcc;
+    return Settled{sf != kRowWait, sf == kRowBadSt, f};
+}
+
+template <int ES>
+__device__ void decide_publish(const VerifyArgs &a, int b, Smem &sh) {
+    constexpr int kRegs = 4;      // partials held per lane (np1 <= 64)
+    constexpr int kRows = kWG / 16;
+    const int G = a.G, G1 = G + 1;
+    const int n = verify_len(a, b);
+    if (n < 0 || n > G) {
         write_error(a, b);
+        if (a.d_lse || a.d_p || a.d_q || a.d_r) write_diag<ES>(a, b, false, n, sh);
+        return;
     }
-    if (diag) write_diag<ES>(a, b, !err, n, sh);
-    uint64_t *part = partials(a, b);
-    for (int i = threadIdx.x; i < (n + 1) * a.np1; i += kWG) st_coherent(part + i, 0ull);
-    for (int i = threadIdx.x; i < n; i += kWG) st_coherent(gathered(a, b) + i, 0ull);
+    if (n + 1 > kRows || a.np1 > 16 * kRegs) {
+        decide_publish_whole<ES>(a, b, n, sh);
+        return;
+    }
+    // Row r = t / 16 is merged by the 16 lanes of group r; the group's lane 0
+    // also holds draft r (its id, uniform and gather word) for the accept test.
+    // The statuses are cleared before any load is issued (a barrier waits for
+    // outstanding loads), and no barrier follows until every row is in.
+    const int t = threadIdx.x, l = t & 15, r = t >> 4, lane = t & 63;
+    if (t < kRows) sh.rst[t] = kRowWait;
+    if (t == 0) sh.pub = 0;
+    __syncthreads();
+    const bool live = r <= n, drafted = r < n;
+    const bool lead = l == 0 && drafted;
+    int xr = 0;
+    float ur = 0.0f;
+    if (lead) {
+        xr = a.x[size_t(b) * G + r];
+        ur = a.u[size_t(b) * G1 + r];
+    }
+    const bool xbad = lead && (xr < 0 || xr >= a.V);
+    const uint64_t *pp = partials(a, b) + size_t(live ? r : 0) * a.np1;
+    const uint64_t *gxp = gathered(a, b) + (drafted ? r : 0);
+    const uint64_t empty = uint64_t(0xff800000u) | (uint64_t(kValid) << 32);   // (-inf, 0), written
+    const float c = a.c32;
+    uint64_t v[kRegs], gk = 0;
+#pragma unroll
+    for (int i = 0; i < kRegs; ++i) v[i] = 0ull;
+    bool gready = !lead;
+    bool merged = !live;                    // uniform in the group
+    bool settled = false;                   // uniform in the wave: the record is out
+    for (uint32_t spins = 0;; ++spins) {
+        // Each lane reloads only its words not yet written (a bounded wait:
+        // a row whose wait expires stays waiting, a data error).
+#pragma unroll
+        for (int i = 0; i < kRegs; ++i) {
+            const int cc = l + 16 * i;
+            if (!valid(v[i])) v[i] = (live && cc < a.np1) ? ld_coherent(pp + cc) : empty;
+        }
+        if (!gready) {
+            gk = ld_coherent(gxp);
+            gready = valid(gk) || xbad;     // an id out of range is never gathered
+        }
+        int ok = int(gready);
+#pragma unroll
+        for (int i = 0; i < kRegs; ++i) ok &= int(valid(v[i]));
+        ok = row16_and(ok);
+        const bool fresh = ok && !merged;
+        if (__ballot(fresh) != 0ull) {
+            // Rows complete in this attempt: merge_rows_sampled's merge (the
+            // same order, so bitwise the same M and S), the accept test, and
+            // the row's status, stored after its M and S.
+            float M = neg_inf();
+#pragma unroll
+            for (int i = 0; i < kRegs; ++i) M = fmaxf(M, lo_f(v[i]));
+            M = row16_max(M);
+            double S = 0.0;
+#pragma unroll
+            for (int i = 0; i < kRegs; ++i)
+                S = S + double(__uint_as_float(hi_u(v[i]) & ~kValid)) * double(rescale(lo_f(v[i]), M, c));
+            S = row16_sum_d(S);
+            if (fresh && l == 0) {
+                int st;
+                if (xbad || !(S > 0.0 && S < INFINITY) || !(M > neg_inf() && M < __builtin_inff())) {
+                    st = kRowBadSt;
+                } else if (!drafted) {
+                    st = kRowAcc;                   // row n: merged and good
+                } else {
+                    const float zx = lo_f(gk), qx32 = __uint_as_float(hi_u(gk) & ~kValid);
+                    const double pk = target_prob(zx, M, c) / S;
+                    const double qx = double(qx32);
+                    float u = ur;
+                    asm volatile("" : "+v"(u));     // widened here, not held widened through the wait
+                    st = ((qx > 0.0) ? (double(u) < pk / qx) : (pk > 0.0)) ? kRowAcc : kRowRej;
+                }
+                sh.M[r] = M;
+                sh.S[r] = S;
+                __hip_atomic_store(&sh.rst[r], st, __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            merged = merged || ok;
+            // Publish once the statuses settle the decision; the first wave
+            // to claim sh.pub writes the record.  (Sequentially consistent
+            // status stores and loads: of two waves completing rows at once,
+            // at least one sees both.)
+            if (!settled) {
+                const int s = (lane <= n) ? __hip_atomic_load(&sh.rst[lane], __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_WORKGROUP)
+                                          : kRowAcc;
+                const Settled d = settle(n, lane, s);
+                if (d.known) {
+                    settled = true;
+                    if (lane == 0 && atomicCAS(&sh.pub, 0, 1) == 0) {
+                        float m = 0.0f, inv_s = 0.0f;
+                        if (!d.err) {
+                            m = sh.M[d.j];
+                            inv_s = float(1.0 / sh.S[d.j]);
+                        }
+                        put_record(decision(a, b), d.j, n, d.err, m, inv_s);
+                    }
+                }
+            }
+        }
+        if (__ballot(!merged) == 0ull || spins >= a.spin_limit) break;
+    }
+    __syncthreads();
+    // Every row in (or its wait expired): a row still waiting or bad anywhere
+    // is a data error; otherwise the decision is the one already published.
+    const int s = (lane <= n) ? sh.rst[lane] : kRowAcc;
+    const bool err = __ballot(lane <= n && s != kRowAcc && s != kRowRej) != 0ull;
+    const Settled d = settle(n, lane, s);
+    const int j = err ? n : d.j;
+    if (t == 0) {
+        uint64_t *rec = decision(a, b);
+        if (sh.pub == 0) put_record(rec, j, n, err, err ? 0.0f : sh.M[j], err ? 0.0f : float(1.0 / sh.S[j]));
+        st_coherent(rec + 2, kFinWritten | (err ? 0ull : kFinOk));
+    }
+    decision_outputs<ES>(a, b, n, j, err, sh);
 }
 
 // A request workgroup of the one-launch verify: request b's decision, from its
@@ -1022,45 +1194,50 @@ __device__ bool await_decision(const VerifyArgs &a, int b, int w, Decision &d, b
     return (h & kDecOk) != 0u;
 }
 
-// Wait until every sub-tile mass word of request b is written.  With at most
-// kWG sub-tiles thread s polls sub-tile s's two words on its own and returns
-// its (residual, target) masses in v (zeros past the end), and one barrier
-// ends the wait.  False if a bounded wait expired.
-__device__ bool wait_masses(const VerifyArgs &a, int b, double (&v)[2]) {
+// Wait until every sub-tile mass word of request b is written and, with fin
+// (the one-launch verify: word 2 of the decision record), until the decision
+// workgroup has checked every read row; *fin_ok is then whether it found no
+// data error.  With at most kWG sub-tiles thread s polls sub-tile s's two
+// words on its own (thread 0 also polls fin) and returns its (residual,
+// target) masses in v (zeros past the end), and one barrier ends the wait.
+// False if a bounded wait expired.
+__device__ bool wait_masses(const VerifyArgs &a, int b, double (&v)[2], const uint64_t *fin, bool &fin_ok,
+                            Smem &sh) {
     const uint64_t *mass = masses(a, b);
     const int nsub = a.nsub;
+    const bool pf = fin != nullptr && threadIdx.x == 0;
     if (nsub <= kWG) {
         const int s = threadIdx.x;
-        uint64_t w0 = kMassWritten, w1 = kMassWritten;
+        uint64_t w0 = kMassWritten, w1 = kMassWritten, wf = kFinWritten | kFinOk;
         bool mine = true;
         if (s < nsub) {
             for (uint32_t spins = 0;; ++spins) {
                 w0 = ld_coherent(mass + 2 * s);
                 w1 = ld_coherent(mass + 2 * s + 1);
-                if ((w0 & w1 & kMassWritten) != 0) break;
+                if (pf) wf = ld_coherent(fin);
+                if ((w0 & w1 & kMassWritten) != 0 && (wf & kFinWritten) != 0) break;
                 if (spins >= a.spin_limit) { mine = false; break; }
             }
         }
+        if (pf) sh.pok = int((wf & kFinOk) != 0);
         v[0] = mass_value(w0);
         v[1] = mass_value(w1);
-        return !__syncthreads_or(!mine);
+        const bool all = !__syncthreads_or(!mine);
+        fin_ok = fin == nullptr || sh.pok != 0;
+        return all;
     }
     for (uint32_t spins = 0;; ++spins) {
         bool ready = true;
-        if (nsub <= kWG) {
-            const int s = threadIdx.x;
-            uint64_t w0 = kMassWritten, w1 = kMassWritten;
-            if (s < nsub) {
-                w0 = ld_coherent(mass + 2 * s);
-                w1 = ld_coherent(mass + 2 * s + 1);
-            }
-            ready = (w0 & w1 & kMassWritten) != 0;
-            v[0] = mass_value(w0);
-            v[1] = mass_value(w1);
-        } else {
-            for (int i = threadIdx.x; i < 2 * nsub; i += kWG) ready &= (ld_coherent(mass + i) & kMassWritten) != 0;
+        for (int i = threadIdx.x; i < 2 * nsub; i += kWG) ready &= (ld_coherent(mass + i) & kMassWritten) != 0;
+        if (pf) {
+            const uint64_t wf = ld_coherent(fin);
+            ready &= (wf & kFinWritten) != 0;
+            sh.pok = int((wf & kFinOk) != 0);
         }
-        if (__syncthreads_and(ready)) return true;
+        if (__syncthreads_and(ready)) {
+            fin_ok = fin == nullptr || sh.pok != 0;
+            return true;
+        }
         if (spins >= a.spin_limit) return false;
         __builtin_amdgcn_s_sleep(2);
     }
@@ -1289,15 +1466,20 @@ __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh
     // The diagnostics need only the merged rows, so they go out before the wait
     // (in the one-launch verify the decision workgroup writes them).
     if (!FUSED && (a.d_lse || a.d_p || a.d_q || a.d_r)) write_diag<ES>(a, b, ok, d.n, sh);
+    // In the one-launch verify the token waits also for the decision
+    // workgroup's check of every read row (word 2 of the record): on a data
+    // error that workgroup writes the error outputs instead.
     double polled[2];
-    const bool all = wait_masses(a, b, polled);
-    if (ok && all) final_select<ES, ALZ, ALQ, DL>(a, b, d, zrow, qrow, polled, sh);
-    else if (ok) write_error(a, b);              // an expired wait
+    bool fin_ok = true;
+    const bool all = wait_masses(a, b, polled, FUSED ? decision(a, b) + 2 : nullptr, fin_ok, sh);
+    if (ok && all && fin_ok) final_select<ES, ALZ, ALQ, DL>(a, b, d, zrow, qrow, polled, sh);
+    else if (ok && !all) write_error(a, b);      // an expired wait
     __syncthreads();
     for (int i = threadIdx.x; i < 2 * a.nsub; i += kWG) st_coherent(mass + i, 0ull);
     if constexpr (FUSED) {
-        // every request workgroup has read the record before writing its masses
-        if (threadIdx.x < 2) st_coherent(decision(a, b) + threadIdx.x, 0ull);
+        // every request workgroup has read the record before writing its
+        // masses, and word 2 is the decision workgroup's last write to it
+        if (threadIdx.x < 3) st_coherent(decision(a, b) + threadIdx.x, 0ull);
         return;
     }
     uint64_t *part = partials(a, b);
@@ -1491,7 +1673,8 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(DL ? 4 : 8,
 //   rows(b)    request b's row workgroups (k_rows_sampled's, with partials and
 //              gathers published coherently, each word with its written bit);
 //   dec(b)     one decision workgroup (decide_publish): polls rows(b)'s words,
-//              decides, writes the accepted prefix and a decision record;
+//              publishes a decision record once rows 0..j settle it, then,
+//              with every row in, the error check and the accepted prefix;
 //   draws(b)   request b's nc2 request workgroups (k_requests_sampled's),
 //              which poll the record instead of the partials, stream the draw
 //              row and select the token.

@@ -46,8 +46,8 @@ def test_workspace_query():
     w = _capi.verify_workspace_bytes(64, 15, 129280, _capi.SPEC_DTYPE_BF16)
     # a 256-byte zero block + partials 64*16 rows*64 chunks*8 B (sized for the
     # greedy per-chunk count) + draft-row partials 64*15*64*8 B (draft logits)
-    # + masses 64*64 sub-tiles*16 B + gathers 64*15*8 B + decision records 64*16 B
-    assert w == 256 + 64 * 16 * 64 * 8 + 64 * 15 * 64 * 8 + 65536 + 64 * 15 * 8 + 64 * 16
+    # + masses 64*64 sub-tiles*16 B + gathers 64*15*8 B + decision records 64*32 B
+    assert w == 256 + 64 * 16 * 64 * 8 + 64 * 15 * 64 * 8 + 65536 + 64 * 15 * 8 + 64 * 32
     # every region is 256-byte aligned, the smallest shape included
     assert _capi.verify_workspace_bytes(1, 0, 1, _capi.SPEC_DTYPE_BF16) == 4 * 256
     assert _capi.verify_workspace_bytes(64, 15, 129280, _capi.SPEC_DTYPE_F32) >= w
