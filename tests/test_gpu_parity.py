@@ -372,6 +372,35 @@ def test_data_errors():
     assert g["accepted"][7] >= 0
 
 
+@pytest.mark.parametrize("B,lengths", [(16, False), (13, False), (16, True)])
+def test_data_error_after_an_early_rejection(B, lengths):
+    """Requests certainly rejected at row 0 whose later rows (or ids) are bad
+    are still data errors: the decision that rows 0..j settle goes out before
+    the request's later rows are in, and the check of every read row decides
+    the outputs.  Full lengths (the grid in XCD order, or not) and verify
+    lengths; with and without diagnostics."""
+    G, V = 4, 2000
+    w = _rand_workload("late_errors", B, G, V, dtype="f32", seed=21)
+    z, q, x, u = w["logits"], w["draft_probs"], w["draft_tokens"], w["uniforms"]
+    for b in range(8):                        # p(x_0) / q(x_0) ~ e^-40: rejected at row 0
+        x[b, 0] = 5
+        q[b, 0, :] = 0.0
+        q[b, 0, 5] = 1.0
+        z[b, 0, 5] = -40.0
+        u[b, 0] = 0.5
+    z[0, 3, 11] = np.nan                      # NaN in a later row
+    z[1, G, 0] = np.inf                       # +inf maximum in the bonus row
+    x[2, 2] = V + 7                           # a later id out of range
+    z[3, 1, :] = -np.inf                      # a later row all -inf
+    x[4, 3] = -1
+    if lengths:
+        w["verify_len"] = np.full(B, G, np.int32)
+    for diag in (True, False):
+        g, o, rep = check(w, diag=diag)
+        assert g["accepted"][:8].tolist() == [-1] * 5 + [0] * 3
+        assert (g["tokens"][:5] == -1).all()
+
+
 def test_many_requests():
     # Many small requests (T > 0): each request's draw workgroups trail its
     # rows by a lag of many requests in the one launch.
