@@ -229,8 +229,8 @@ spec_status_t verify_impl(const void *target_logits, spec_dtype_t target_dtype, 
             // workgroups, one decision workgroup per request (in grid order one
             // request after its rows), then the request workgroups, which only
             // poll the request's decision record: about 2048 of them in all
-            // (B = 64: 2048 at 55.0 us per call, against 1024 at 55.9 and 4096
-            // at 55.4).  Each waits only on workgroups before it in grid order.
+            // (B = 64: 2048 at 51.4 us per call, against 1024 at 52.7 and 4096
+            // at 52.1).  Each waits only on workgroups before it in grid order.
             const long want = (long(B) * a.nsub + 2047) / 2048;
             int spw = 1;
             while (spw < want && spw < 8) spw <<= 1;
