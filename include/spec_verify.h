@@ -273,8 +273,10 @@ spec_status_t spec_verify_logits(const void *target_logits, spec_dtype_t target_
  * parents, node_tokens [B, M] int32 (entry 0 ignored; may be NULL if M == 1);
  * 1 <= M <= SPEC_MAX_DRAFTS + 1; out_accepted [B], out_tokens [B, M],
  * out_path [B, M] int32; workspace of spec_verify_workspace_bytes(B, M - 1, V,
- * target_dtype).  Two launches: the greedy row pass over every node row, then
- * one workgroup per request.
+ * target_dtype).  One launch while B is at most half the workgroups the
+ * device holds at once (the greedy row pass over every node row, then one
+ * workgroup per request that waits for its rows' partials); else two launches
+ * (the row pass, then the walks).
  *
  * Data errors (that request's outputs all -1): a parent outside [0, i) or a
  * token outside [0, V) at some node i >= 1; a visited row (the root or a node

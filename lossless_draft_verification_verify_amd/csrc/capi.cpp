@@ -376,9 +376,18 @@ spec_status_t spec_verify_tree(const void *target_logits, spec_dtype_t target_dt
     a.nsub = (V + sv::kSub - 1) / sv::kSub;
     a.nc2 = 1;
     a.spin_limit = 1u << 20;
-    a.mode = 1;                                        // the greedy row workgroups only: every node row
     const bool az = aligned(target_logits, 16) && (size_t(V) * es) % 16 == 0;
-    if (sv::launch_verify_greedy(a, az, es, int(long(B) * M * a.np1), stream) != 0) return SPEC_ERR_DEVICE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SPEC_ERR_DEVICE;
+    // One launch (rows, then one walk workgroup per request that polls its
+    // rows) while the walk workgroups stay below half the resident capacity,
+    // as for the greedy verify; else the row launch, then the walks.
+    const int one = greedy_one_launch(dev, az, es, B);
+    if (one < 0) return SPEC_ERR_DEVICE;
+    const long row_wgs = long(B) * M * a.np1;
+    if (one) return sv::launch_tree_fused(a, az, es, int(row_wgs + B), stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
+    a.mode = 1;                                        // the greedy row workgroups only: every node row
+    if (sv::launch_verify_greedy(a, az, es, int(row_wgs), stream) != 0) return SPEC_ERR_DEVICE;
     return sv::launch_tree_walk(a, B, stream) == 0 ? SPEC_OK : SPEC_ERR_DEVICE;
 }
 

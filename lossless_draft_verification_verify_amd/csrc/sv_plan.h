@@ -126,6 +126,8 @@ int launch_verify_sampled(const VerifyArgs &a, bool aligned_z, bool aligned_q, i
 int launch_verify_greedy(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
 int greedy_occupancy(bool aligned_z, int esize, int *blocks_per_cu);
 int launch_tree_walk(const VerifyArgs &a, int grid, void *stream);
+// Tree verification in one launch: B * M * np1 row workgroups, then B walks.
+int launch_tree_fused(const VerifyArgs &a, bool aligned_z, int esize, int grid, void *stream);
 
 // Static scratch of spec_verify_noalloc (noalloc.hip): its size, this
 // device's address of it (asked once per device), and a fill kernel that

@@ -1844,8 +1844,12 @@ __global__ __launch_bounds__(kWG) void k_verify_greedy(VerifyArgs a) {
 
 // Merged argmax of rows 0..n into sh.A for the tree walk: four lanes per row
 // (a row's partials interleaved over them, all loads issued together), so 64
-// rows per pass.  The partials are complete (written by the previous launch).
-// No barrier inside; the caller synchronises.
+// rows per pass.  POLL: the row workgroups of the same launch are still
+// writing the partials, so each lane reloads those of its words not yet
+// written until all are (a bounded wait; a word never written makes its row
+// bad); otherwise they are complete (written by the previous launch).  No
+// barrier inside; the caller synchronises.
+template <bool POLL>
 __device__ void merge_rows_greedy4(const VerifyArgs &a, int b, int n, Smem &sh) {
     constexpr int kR = 8;                  // partials per lane when np1 <= 32
     const uint64_t *part = partials(a, b);
@@ -1859,10 +1863,25 @@ __device__ void merge_rows_greedy4(const VerifyArgs &a, int b, int n, Smem &sh) 
         int bi = -1, nan = 0, ok = 1;
         if (a.np1 <= 4 * kR) {
             uint64_t v[kR];
+            if constexpr (POLL) {
 #pragma unroll
-            for (int i = 0; i < kR; ++i) {
-                const int cc = l + 4 * i;
-                v[i] = (live && cc < a.np1) ? pp[cc] : empty;
+                for (int i = 0; i < kR; ++i) v[i] = 0ull;
+                for (uint32_t spins = 0;; ++spins) {
+                    int all = 1;
+#pragma unroll
+                    for (int i = 0; i < kR; ++i) {
+                        const int cc = l + 4 * i;
+                        if (!valid(v[i])) v[i] = (live && cc < a.np1) ? ld_coherent(pp + cc) : empty;
+                        all &= int(valid(v[i]));
+                    }
+                    if (all || spins >= a.spin_limit) break;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kR; ++i) {
+                    const int cc = l + 4 * i;
+                    v[i] = (live && cc < a.np1) ? pp[cc] : empty;
+                }
             }
 #pragma unroll
             for (int i = 0; i < kR; ++i) {
@@ -1873,7 +1892,10 @@ __device__ void merge_rows_greedy4(const VerifyArgs &a, int b, int n, Smem &sh) 
             }
         } else if (live) {
             for (int cc = l; cc < a.np1; cc += 4) {
-                const uint64_t v = pp[cc];
+                uint64_t v = POLL ? ld_coherent(pp + cc) : pp[cc];
+                if constexpr (POLL) {
+                    for (uint32_t spins = 0; !valid(v) && spins < a.spin_limit; ++spins) v = ld_coherent(pp + cc);
+                }
                 ok &= int(valid(v));
                 const int vi = int(hi_u(v) & ~kValid) - 2;
                 if (vi == kNanIdx) nan = 1;
@@ -1897,26 +1919,30 @@ __device__ void merge_rows_greedy4(const VerifyArgs &a, int b, int n, Smem &sh) 
 // parent's argmax offers itself to the parent (LDS minimum: the lowest such
 // child); the walk from the root is then a pointer chase in LDS.  A visited
 // bad row, a parent outside [0, i) or a token outside [0, V) is a data error.
-__global__ __launch_bounds__(kWG) void k_tree_walk(VerifyArgs a) {
-    __shared__ Smem sh;
-    __shared__ int match[kWG];
-    __shared__ int emit[kWG + 1], path[kWG];
-    __shared__ int acc_n;
-    const int b = int(blockIdx.x), t = int(threadIdx.x), M = a.G + 1;
+// POLL: the row workgroups of the same launch (earlier in grid order) are
+// still writing the partials.
+struct TreeSmem {
+    int match[kWG];
+    int emit[kWG + 1], path[kWG];
+    int acc_n;
+};
+template <bool POLL>
+__device__ void tree_walk_item(const VerifyArgs &a, int b, Smem &sh, TreeSmem &ts) {
+    const int t = int(threadIdx.x), M = a.G + 1;
     const int32_t *par = a.tpar + size_t(b) * M, *tok = a.ttok + size_t(b) * M;
     bool bad = false;
     int p = 0, tk = 0;
     if (t < M) {
-        match[t] = INT_MAX;
+        ts.match[t] = INT_MAX;
         if (t >= 1) {
             p = par[t];
             tk = tok[t];
             bad = !(p >= 0 && p < t) || !(tk >= 0 && tk < a.V);
         }
     }
-    merge_rows_greedy4(a, b, a.G, sh);
+    merge_rows_greedy4<POLL>(a, b, a.G, sh);
     bad = __syncthreads_or(bad);
-    if (!bad && t >= 1 && t < M && tk == sh.A[p]) atomicMin(&match[p], t);
+    if (!bad && t >= 1 && t < M && tk == sh.A[p]) atomicMin(&ts.match[p], t);
     __syncthreads();
     if (t == 0) {
         int n = -1;
@@ -1929,24 +1955,45 @@ __global__ __launch_bounds__(kWG) void k_tree_walk(VerifyArgs a) {
                     n = -1;
                     break;
                 }
-                emit[n] = am;
-                const int nx = match[cur];
+                ts.emit[n] = am;
+                const int nx = ts.match[cur];
                 if (nx == INT_MAX) break;
-                path[n++] = nx;
+                ts.path[n++] = nx;
                 cur = nx;
             }
         }
-        acc_n = n;
+        ts.acc_n = n;
     }
     __syncthreads();
-    const int n = acc_n;
+    const int n = ts.acc_n;
     for (int i = t; i < M; i += kWG) {
-        a.out_tok[size_t(b) * M + i] = (n >= 0 && i <= n) ? emit[i] : -1;
-        a.out_path[size_t(b) * M + i] = (n >= 0 && i < n) ? path[i] : -1;
+        a.out_tok[size_t(b) * M + i] = (n >= 0 && i <= n) ? ts.emit[i] : -1;
+        a.out_path[size_t(b) * M + i] = (n >= 0 && i < n) ? ts.path[i] : -1;
     }
     if (t == 0) a.out_acc[b] = n;
     uint64_t *pw = partials(a, b);
     for (int i = t; i < M * a.np1; i += kWG) st_coherent(pw + i, 0ull);
+}
+
+// The walk after a separate row launch: one workgroup per request.
+__global__ __launch_bounds__(kWG) void k_tree_walk(VerifyArgs a) {
+    __shared__ Smem sh;
+    __shared__ TreeSmem ts;
+    tree_walk_item<false>(a, int(blockIdx.x), sh, ts);
+}
+
+// Tree verification in one launch: the greedy row workgroups over every node
+// row (row_group_greedy's placement), then one walk workgroup per request,
+// which polls its rows' partials (every wait is on workgroups earlier in grid
+// order; the host keeps the walk workgroups below half the resident capacity).
+template <int ES, bool AL>
+__global__ __launch_bounds__(kWG) void k_tree_fused(VerifyArgs a) {
+    __shared__ Smem sh;
+    __shared__ TreeSmem ts;
+    const int groups = a.B * (a.G + 1) * a.np1;
+    const int i = blockIdx.x;
+    if (i >= groups) tree_walk_item<true>(a, i - groups, sh, ts);
+    else row_group_greedy<ES, AL>(a, i, sh);
 }
 
 template <typename K>
@@ -2028,6 +2075,18 @@ int launch_verify_greedy(const VerifyArgs &a, bool az, int esize, int grid, void
     } else {
         if (az) hipLaunchKernelGGL((k_verify_greedy<4, true>), dim3(grid), dim3(kWG), 0, st, a);
         else hipLaunchKernelGGL((k_verify_greedy<4, false>), dim3(grid), dim3(kWG), 0, st, a);
+    }
+    return int(hipGetLastError());
+}
+
+int launch_tree_fused(const VerifyArgs &a, bool az, int esize, int grid, void *stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (esize == 2) {
+        if (az) hipLaunchKernelGGL((k_tree_fused<2, true>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_tree_fused<2, false>), dim3(grid), dim3(kWG), 0, st, a);
+    } else {
+        if (az) hipLaunchKernelGGL((k_tree_fused<4, true>), dim3(grid), dim3(kWG), 0, st, a);
+        else hipLaunchKernelGGL((k_tree_fused<4, false>), dim3(grid), dim3(kWG), 0, st, a);
     }
     return int(hipGetLastError());
 }

@@ -82,6 +82,12 @@ int launch_verify_greedy(const VerifyArgs &a, bool, int es, int grid, void *) {
     return 0;
 }
 int greedy_occupancy(bool, int, int *n) { *n = 8; return 0; }
+int launch_tree_fused(const VerifyArgs &a, bool, int es, int grid, void *) {
+    common(a, es, grid);
+    CHECK(a.out_path && (a.G == 0 || (a.tpar && a.ttok)));
+    CHECK(long(grid) == long(a.B) * (a.G + 1) * a.np1 + a.B);
+    return 0;
+}
 int launch_tree_walk(const VerifyArgs &a, int grid, void *) {
     CHECK(grid == a.B && a.out_path && (a.G == 0 || (a.tpar && a.ttok)));
     ++g_launches;

@@ -95,6 +95,25 @@ def test_random_trees(seed):
     check(z, "f32", par, tok, tag=f"random M={M}")
 
 
+@pytest.mark.parametrize("B", [40, 2600])
+def test_one_launch_and_two_launch_paths(B):
+    """B = 40 runs rows and walks in one launch; B = 2600, more walk
+    workgroups than half the device holds at once, runs the row launch and
+    then the walks."""
+    g = np.random.default_rng(70 + B)
+    M, V = 6, 700
+    z = (2.0 * g.normal(size=(B, M, V))).astype(np.float32)
+    a = z.argmax(axis=2)
+    par = np.array([[-1] + [int(g.integers(0, i)) for i in range(1, M)] for _ in range(B)], np.int32)
+    tok = g.integers(0, V, (B, M)).astype(np.int32)
+    hit = g.random((B, M)) < 0.7
+    for b in range(B):
+        for i in range(1, M):
+            if hit[b, i]:
+                tok[b, i] = a[b, par[b, i]]
+    check(z, "f32", par, tok, tag=f"B={B}")
+
+
 def test_root_only_and_data_errors():
     g = np.random.default_rng(9)
     B, M, V = 6, 5, 300
