@@ -542,10 +542,12 @@ def main():
             vl = vlen
         sv.verify(zz, qq, xx, uu, T, vl, out_accepted=acc, out_tokens=tok, row_pass_event=row_event)
 
-    # The plain verify workloads call the C ABI directly in the timed loops, with
-    # every argument marshalled once beforehand, so the Python binding's per-call
-    # checks (tens of microseconds) cannot starve the GPU between calls.
+    # The verify workloads, and the scheduler workloads without calibration,
+    # call the C ABI directly in the timed loops, with every argument marshalled
+    # once beforehand, so the Python binding's per-call checks (tens of
+    # microseconds) cannot starve the GPU between calls.
     fast = None
+    fast_path = kind in ("block", "tiny", "mtp", "greedy") or (kind in ("scheduled", "static", "dcut") and calib is None)
     if kind in ("block", "tiny", "mtp", "greedy"):
         import ctypes
         from lossless_draft_verification_verify_amd import _capi
@@ -563,6 +565,56 @@ def main():
             rc = fn(*fast[i % len(fast)])
             if rc != 0:
                 raise RuntimeError(f"spec_verify: {_capi.status_string(rc)}")
+    elif kind in ("scheduled", "static", "dcut") and calib is None:
+        # The scheduler, then the verify over its lengths: the same two C ABI
+        # calls the Python binding makes, marshalled once.
+        import ctypes
+        from lossless_draft_verification_verify_amd import _capi
+        lib = _capi.load()
+        code = _capi.SPEC_DTYPE_BF16 if z0.dtype == torch.bfloat16 else _capi.SPEC_DTYPE_F32
+        nbytes = _capi.verify_workspace_bytes(B, G, V, code)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        st_handle = torch.cuda.current_stream(dev).cuda_stream
+        ptr = (lambda t: None if t is None else t.data_ptr())
+        cT = ctypes.c_float(T)
+        if kind == "scheduled":
+            conf, cost, budget, vlen, tot, tau = sched
+            first = (lib.spec_schedule, "spec_schedule",
+                     (conf.data_ptr(), cost.data_ptr(), int(cost.shape[0]), B, G, int(budget), ctypes.c_float(0.0),
+                      vlen.data_ptr(), tot.data_ptr(), tau.data_ptr(), None, 0, st_handle))
+            second = (lib.spec_verify, "spec_verify",
+                      [(ptr(zz), code, ptr(qq), ptr(xx), ptr(uu), vlen.data_ptr(), B, G, V, cT, acc.data_ptr(),
+                        tok.data_ptr(), None, ws.data_ptr(), ws.numel(), st_handle) for zz, qq, xx, uu in sets])
+        elif kind == "static":
+            sconf, thr, slen, stot = static
+            first = (lib.spec_schedule_static, "spec_schedule_static",
+                     (sconf.data_ptr(), B, G, _capi.SPEC_STATIC_THRESHOLD, 0, ctypes.c_float(thr), None,
+                      slen.data_ptr(), stot.data_ptr(), None, st_handle))
+            second = (lib.spec_verify, "spec_verify",
+                      [(ptr(zz), code, ptr(qq), ptr(xx), ptr(uu), slen.data_ptr(), B, G, V, cT, acc.data_ptr(),
+                        tok.data_ptr(), None, ws.data_ptr(), ws.numel(), st_handle) for zz, qq, xx, uu in sets])
+        else:
+            dconf, dlen, doffs, dridx, drows, packed = dcut
+            nr = len(w["ratios"])
+            rat = (ctypes.c_float * nr)(*[float(r) for r in w["ratios"]])
+            rco = (ctypes.c_float * nr)(*[float(r) for r in w["ratio_cost"]])
+            first = (lib.spec_dcut, "spec_dcut",
+                     (dconf.data_ptr(), B, G, rat, rco, nr, None, dlen.data_ptr(), doffs.data_ptr(),
+                      dridx.data_ptr(), drows.data_ptr(), None, st_handle))
+            second = (lib.spec_verify_packed, "spec_verify_packed",
+                      [(zp.data_ptr(), code, int(zp.shape[0]), doffs.data_ptr(), ptr(qq), ptr(xx), ptr(uu), B, G, V,
+                        cT, acc.data_ptr(), tok.data_ptr(), None, ws.data_ptr(), ws.numel(), st_handle)
+                       for zp, (_, qq, xx, uu) in zip(packed, sets)])
+        f1, n1, a1 = first
+        f2, n2, a2 = second
+
+        def step_fast(i):
+            rc = f1(*a1)
+            if rc != 0:
+                raise RuntimeError(f"{n1}: {_capi.status_string(rc)}")
+            rc = f2(*a2[i % len(a2)])
+            if rc != 0:
+                raise RuntimeError(f"{n2}: {_capi.status_string(rc)}")
     else:
         step_fast = step
 
@@ -701,7 +753,7 @@ def main():
         "config": {"workload": desc, "B": B, "gamma": G, "V": V, "temperature": T, "logits": w["dtype"],
                    "rotating_sets": len(sets), "verified_positions_per_step": positions,
                    "rejecting_requests": n_rej, "host_enqueue_ms_per_step": round(host_ms / K, 5),
-                   "call_path": "C ABI, arguments marshalled once" if fast is not None else "Python binding"},
+                   "call_path": "C ABI, arguments marshalled once" if fast_path else "Python binding"},
         # The roofline of the verify call as a whole (every launch it makes):
         # its algorithmic bytes over its time per call in the throughput loop.
         "roofline": {"bound": "hbm", "achieved": round(call_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
