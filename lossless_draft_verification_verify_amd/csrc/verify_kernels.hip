@@ -1373,15 +1373,23 @@ __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, cons
 #pragma unroll
     for (int i = 0; i < kSubPerThread; ++i)
         if (t[i] > 0.0f) lp = e0 + i;
-    post_last(v1[0] > 0.0, 4, sh);
-    post_first(v1[0] > 0.0 && !lastpos && base + in1[0] > target, 5, sh);
-    __syncthreads();
-    const int t1 = wg_first(5, sh), tl = wg_last(4, sh);
-    // The thread holding the draw writes it.
+    // The draw lies in the first thread with positive mass whose running total
+    // passes the target.  A thread's exclusive prefix is bitwise its
+    // predecessor's inclusive one, so that thread is the one whose interval
+    // [base + excl, base + incl) holds the target: each thread tests its own,
+    // with no barrier.  Whether one does is uniform: the sub-tile was chosen
+    // with base <= target < base + its mass, which equals the scan's total
+    // bitwise; only when no sub-tile passed (lastpos) does none, and the last
+    // thread with positive mass takes its last positive term.
+    const bool none = lastpos || !(base + tot1[0] > target);
     int y = -2;
-    if (t1 == INT_MAX) {
+    if (none) {
+        post_last(v1[0] > 0.0, 4, sh);
+        __syncthreads();
+        const int tl = wg_last(4, sh);
         if (int(threadIdx.x) == max(tl, 0)) y = lp;   // tl < 0 cannot happen: p(argmax) >= 1/V
-    } else if (int(threadIdx.x) == t1) {
+    } else if (base + ex1[0] <= target && base + in1[0] > target) {
+        // The thread holding the draw writes it.
         double acc = base + ex1[0];
         int yc = -1;
 #pragma unroll
