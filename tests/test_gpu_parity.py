@@ -401,6 +401,25 @@ def test_data_error_after_an_early_rejection(B, lengths):
         assert (g["tokens"][:5] == -1).all()
 
 
+def test_random_shapes_one_launch():
+    """Seeded sweep over the one-launch verify's shapes: every depth G up to 15
+    (rows spread over one to four waves of the decision workgroup), B in and
+    out of multiples of 8, full and random verify lengths, three temperatures,
+    bf16 and fp32."""
+    g = np.random.default_rng(77)
+    for trial in range(14):
+        B = int(g.choice([1, 7, 8, 13, 24, 64]))
+        G = int(g.integers(1, 16))
+        V = int(g.choice([257, 1000, 2048, 4099]))
+        T = float(g.choice([0.5, 1.0, 2.0]))
+        dtype = "bf16" if trial % 2 == 0 else "f32"
+        w = _rand_workload(f"sweep{trial}", B, G, V, T=T, dtype=dtype, seed=100 + trial,
+                           zscale=float(g.choice([1.0, 2.0, 4.0])))
+        if trial % 3 == 1:
+            w["verify_len"] = g.integers(0, G + 1, size=B).astype(np.int32)
+        check(w, diag=(trial % 4 == 0))
+
+
 def test_many_requests():
     # Many small requests (T > 0): each request's draw workgroups trail its
     # rows by a lag of many requests in the one launch.
