@@ -1222,7 +1222,7 @@ __device__ bool wait_masses(const VerifyArgs &a, int b, double (&v)[2], const ui
         if (pf) sh.pok = int((wf & kFinOk) != 0);
         v[0] = mass_value(w0);
         v[1] = mass_value(w1);
-        const bool all = !__syncthreads_or(!mine);
+        const bool all = !wg_any(!mine, 2, sh);
         fin_ok = fin == nullptr || sh.pok != 0;
         return all;
     }
@@ -1271,10 +1271,17 @@ __device__ void final_select(const VerifyArgs &a, int b, const Decision &d, cons
         // to which waves 1..3 would only add zeros.
         if (threadIdx.x < 64) {
             const int s = threadIdx.x;
-            const double x0 = wave_scan_d(polled[0]), x1 = wave_scan_d(polled[1]);
-            const double tR = lane_d(x0, 63), tRp = lane_d(x1, 63);
+            const double x0 = wave_scan_d(polled[0]);
+            const double tR = lane_d(x0, 63);
             const bool ur = resid && tR > 0.0;
             const int sl = (resid && !ur) ? 1 : 0;
+            // the target masses' prefix only when the draw falls back to them
+            // (a residual of zero mass; uniform across the wave)
+            double x1 = 0.0, tRp = 0.0;
+            if (sl) {
+                x1 = wave_scan_d(polled[1]);
+                tRp = lane_d(x1, 63);
+            }
             const double tg = double(d.u_final) * (sl ? tRp : tR);
             const double vs = sl ? polled[1] : polled[0], xs = sl ? x1 : x0;
             const double ps = dpp_d<kWaveShr1>(xs), bs = (s == 0) ? 0.0 : ps;
