@@ -420,6 +420,28 @@ def test_random_shapes_one_launch():
         check(w, diag=(trial % 4 == 0))
 
 
+def test_two_streams_at_once():
+    """Calls on two streams (each with its own workspace) run at the same time:
+    one-launch verifies of different shapes, with and without verify lengths,
+    enqueued back to back without synchronising, each against the oracle."""
+    ws = [_rand_workload("stream_a", 16, 7, 20000, seed=61),
+          _rand_workload("stream_b", 24, 5, 8000, T=0.7, dtype="f32", seed=62)]
+    ws[1]["verify_len"] = np.random.default_rng(63).integers(0, 6, size=24).astype(np.int32)
+    orc = [run_oracle(w) for w in ws]
+    ins = [to_device(w) for w in ws]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for rnd in range(3):
+        outs = []
+        for w, (z, q, x, u, vl), st in zip(ws, ins, streams):
+            with torch.cuda.stream(st):
+                outs.append(sv.verify(z, q, x, u, float(w["T"]), vl))
+        torch.cuda.synchronize()
+        for w, o, (acc, tok) in zip(ws, orc, outs):
+            g = {"accepted": acc.cpu().numpy().astype(np.int64), "tokens": tok.cpu().numpy().astype(np.int64)}
+            say(f"    round {rnd} {w['name']}:", compare(w, g, o, check_diag=False))
+
+
 def test_many_requests():
     # Many small requests (T > 0): each request's draw workgroups trail its
     # rows by a lag of many requests in the one launch.
