@@ -1524,6 +1524,15 @@ __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
     bad |= k < n && (xk < 0 || xk >= a.V);
     if (wg_any(bad, 1, sh)) {
         write_error(a, b);
+    } else if (G1 <= 64) {
+        // every draft and output position lies in wave 0: the first mismatch
+        // by one ballot, with no further barrier
+        if (threadIdx.x < 64) {
+            const uint64_t mm = __ballot(k < n && xk != sh.A[k]);
+            const int j = mm ? __builtin_ctzll(mm) : n;
+            if (k < G1) a.out_tok[size_t(b) * G1 + k] = (k < j) ? xk : (k == j) ? sh.A[j] : -1;
+            if (k == 0) a.out_acc[b] = j;
+        }
     } else {
         post_first(k < n && xk != sh.A[k], 0, sh);
         __syncthreads();
@@ -1537,7 +1546,7 @@ __device__ void request_item_greedy(const VerifyArgs &a, int b, Smem &sh) {
         }
         if (threadIdx.x == 0) a.out_acc[b] = j;
     }
-    __syncthreads();
+    // Every lane finished reading the partials before wg_any's barrier.
     uint64_t *pw = partials(a, b);
     for (int i = threadIdx.x; i < (n + 1) * a.np1; i += kWG) st_coherent(pw + i, 0ull);
 }
