@@ -1489,7 +1489,8 @@ __device__ void request_item_sampled(const VerifyArgs &a, int b, int w, Smem &sh
     const bool all = wait_masses(a, b, polled, FUSED ? decision(a, b) + 2 : nullptr, fin_ok, sh);
     if (ok && all && fin_ok) final_select<ES, ALZ, ALQ, DL>(a, b, d, zrow, qrow, polled, sh);
     else if (ok && !all) write_error(a, b);      // an expired wait
-    __syncthreads();
+    // Every read of the mass words and of the record came before a barrier
+    // of the wait or of the select.
     for (int i = threadIdx.x; i < 2 * a.nsub; i += kWG) st_coherent(mass + i, 0ull);
     if constexpr (FUSED) {
         // every request workgroup has read the record before writing its
